@@ -1,0 +1,96 @@
+/*
+ * oracle.h -- plain, slow, fp64 CPU oracle for per-element mesh
+ * differentiation and sparse assembly.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this code.  It shares no source, header,
+ * table or helper with the GPU library, and the GPU library never loads it.
+ *
+ * What it computes follows the page "Locality-Aware Automatic Differentiation
+ * on the GPU for Mesh-Based Computations" (Mahmoud, Goel, Ragan-Kelley,
+ * Solomon), section "Method": a partially separable scalar objective
+ * F(x) = sum_j f_j(x_j), each term giving a dense local gradient g_j and
+ * Hessian H_j, assembled as g = sum_j S_j^T g_j and H = sum_j S_j^T H_j S_j.
+ * Key design 3 (CSR preallocated from topology) and key design 4 (runtime
+ * vertex-vertex pairs add off-diagonal blocks) fix the sparsity pattern.
+ *
+ * Conventions (readings of what the page leaves open):
+ *  - DOF 3*v + c is coordinate c of vertex v.
+ *  - H is block CSR with 3x3 blocks, full symmetric storage, diagonal block
+ *    always present, columns ascending within a row; block k holds
+ *    d2F / dx_{row,r} dx_{col_idx[k],c} at vals[9k + 3r + c].
+ *  - the pattern row of vertex a is {a} U {b : a, b share a face or a
+ *    spring} U {pair partners of a}.
+ *  - the Hessian is exact (no projection or clamping).
+ *
+ * Every function returns 0 on success and a negative value on bad input.
+ */
+#ifndef LAD_ORACLE_H
+#define LAD_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int32_t nv;                  /* vertices */
+    int32_t nf;                  /* triangles; faces[3*f + i] */
+    const int32_t *faces;
+    int32_t ns;                  /* springs; springs[2*s + i], 0 = none */
+    const int32_t *springs;
+    const double *rest_len;      /* [ns] */
+    double k;                    /* spring stiffness */
+    int32_t inertia;             /* 1 = add 0.5*c*|x_v - x_tilde_v|^2 per vertex */
+    double c;
+    const double *x_tilde;       /* [nv*3] */
+    int32_t face_energy;         /* 1 = symmetric Dirichlet per face */
+    const double *dm_inv;        /* [nf*4] row-major inverse rest edge matrix */
+    const double *area;          /* [nf] rest area */
+    int32_t np;                  /* vertex-vertex pairs; pairs[2*p + i] */
+    const int32_t *pairs;
+    double kappa, dhat;          /* barrier stiffness and support */
+} oracle_problem;
+
+/* Pattern: number of blocks, then the arrays (row_ptr[nv+1], col_idx[nnzb]). */
+int64_t oracle_pattern_nnzb(const oracle_problem *p);
+int oracle_pattern(const oracle_problem *p, int32_t *row_ptr, int32_t *col_idx);
+
+/* Energy, gradient g[3*nv] and block values hvals[9*nnzb] on the given
+ * pattern (which must contain every block the terms touch). */
+int oracle_eval(const oracle_problem *p, const int32_t *row_ptr,
+                const int32_t *col_idx, const double *x, double *energy,
+                double *g, double *hvals);
+
+/* y = H v with H the oracle's own assembled Hessian (block-CSR SpMV). */
+int oracle_hvp(const oracle_problem *p, const int32_t *row_ptr,
+               const int32_t *col_idx, const double *x, const double *v,
+               double *y);
+
+/* Block-CSR SpMV y = H v, exported for the tests. */
+int oracle_bsr_spmv(int32_t nv, const int32_t *row_ptr, const int32_t *col_idx,
+                    const double *hvals, const double *v, double *y);
+
+/* Element-level routines, exported so the tests can pin them alone.
+ * Local DOF order: vertex-major (vertex 0 xyz, vertex 1 xyz, ...). */
+void oracle_spring_local(const double *xa, const double *xb, double rest,
+                         double k, double *E, double *g6, double *H36);
+void oracle_barrier_local(const double *xa, const double *xb, double kappa,
+                          double dhat, double *E, double *g6, double *H36);
+void oracle_barrier_scalar(double d, double kappa, double dhat, double *b,
+                           double *db, double *ddb);
+void oracle_inertia_local(const double *xv, const double *xt, double c,
+                          double *E, double *g3, double *H9);
+void oracle_face_local(const double *x0, const double *x1, const double *x2,
+                       const double *dm_inv, double area, double *E,
+                       double *g9, double *H81);
+/* Face gradient taken from the hyper-dual evaluator instead of the closed
+ * form (for cross-checking the two). */
+void oracle_face_grad_hyperdual(const double *x0, const double *x1,
+                                const double *x2, const double *dm_inv,
+                                double area, double *g9);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
