@@ -1,0 +1,226 @@
+/*
+ * lad.h -- locality-aware per-element automatic differentiation of mesh
+ * energies on AMD Instinct MI355X (gfx950): the C ABI of liblad.so.
+ *
+ * The library evaluates a partially separable objective
+ *     F(x) = sum_j f_j(x_j)
+ * over a triangle mesh, differentiates every local term j in forward mode
+ * (second-order dual numbers in registers), and assembles on the GPU
+ *     g = sum_j S_j^T g_j         (global gradient)
+ *     H = sum_j S_j^T H_j S_j     (3x3-block CSR Hessian)
+ * together with a matrix-free Hessian-vector product and double-buffered
+ * insertion of runtime vertex-vertex contact pairs.
+ * Source: page "Locality-Aware Automatic Differentiation on the GPU for
+ * Mesh-Based Computations" (Mahmoud, Goel, Ragan-Kelley, Solomon), section
+ * "Method" and its key designs 1-4.
+ *
+ * Terms supported (each switched on in lad_mesh_desc):
+ *   spring   0.5 k (|x_a - x_b| - L_s)^2                 per spring s=(a,b)
+ *   inertia  0.5 c |x_v - xt_v|^2                          per vertex v
+ *   face     A_f (tr C + tr C / det C),  C = F^T F,        per triangle f
+ *            F = [x1 - x0, x2 - x0] Dm_f^{-1}  (symmetric Dirichlet)
+ *   pair     -kappa (d - dhat)^2 ln(d / dhat) for d < dhat, else 0,
+ *            d = |x_i - x_j|                               per inserted pair
+ *
+ * Data layout (all device arrays are caller-owned unless stated):
+ *   x, v, g, y : [nv][3] of the context dtype (float or double), DOF 3v+c.
+ *   hvals      : [capacity][3][3] of the dtype; block k of the active pattern
+ *                holds d2F / dx_{row,r} dx_{col_idx[k],c} at 9k + 3r + c.
+ *   pattern    : row_ptr int32 [nv+1], col_idx int32 [nnzb]; rows are
+ *                vertices, columns ascending, full symmetric storage, the
+ *                diagonal block always present.  Row a holds {a}, every
+ *                vertex sharing a face or a spring with a, and a's current
+ *                pair partners.
+ *
+ * Errors: every call returns lad_status; nothing throws across the ABI.
+ * Arguments are checked on the host before anything is enqueued; a failed
+ * call enqueues nothing and leaves outputs and the pattern untouched.  Pair
+ * indices live on the device and are checked there: a bad pair set leaves
+ * the previous pattern active and is reported by lad_device_status.
+ *
+ * Streams: every call enqueues on the caller's HIP stream (hipStream_t passed
+ * as void*; NULL is the null stream).  lad_eval_energy_grad_hess, lad_hvp and
+ * lad_insert_pairs never synchronise with the host.  lad_build_pattern,
+ * lad_get_pattern, lad_get_info and lad_device_status synchronise that stream.
+ *
+ * Threading: one context must not be used by two host threads at once.
+ */
+#ifndef LAD_H
+#define LAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lad_ctx lad_ctx;
+
+typedef enum {
+    LAD_OK = 0,
+    LAD_ERR_ARG = -1,       /* bad argument (null pointer, size, index)     */
+    LAD_ERR_CAPACITY = -2,  /* more pairs or blocks than reserved storage   */
+    LAD_ERR_OOM = -3,       /* device or host allocation failed             */
+    LAD_ERR_HIP = -4,       /* a HIP runtime call failed                     */
+    LAD_ERR_STATE = -5,     /* call not valid in the context's state        */
+    LAD_ERR_PAIRS = -6      /* device-side check rejected a pair set        */
+} lad_status;
+
+typedef enum { LAD_F32 = 0, LAD_F64 = 1 } lad_dtype;
+
+/* Mesh and energy terms.  All pointers are HOST pointers, read during
+ * lad_build_pattern and not retained (the library copies what it needs).
+ * Per-element constants are given in fp64 and rounded once to the dtype. */
+typedef struct {
+    int32_t nv;                 /* vertices, >= 1                              */
+    int32_t nf;                 /* triangles, >= 0                             */
+    const int32_t *faces;       /* [nf][3] vertex ids (counter-clockwise)      */
+
+    lad_dtype dtype;            /* arithmetic and storage type of x, g, H, v, y */
+    int32_t deterministic;      /* 1: fixed-order (colour-phased) assembly,     */
+                                /*    bitwise reproducible run to run           */
+    int32_t patch_lds_bytes;    /* LDS budget per patch; 0 = library default    */
+    int32_t pair_capacity;      /* max pairs per lad_insert_pairs, >= 0         */
+
+    int32_t ns;                 /* springs, >= 0 (0 = no spring term)          */
+    const int32_t *springs;     /* [ns][2] vertex ids, a != b                  */
+    const double *rest_len;     /* [ns] rest lengths L_s                       */
+    double k;                   /* spring stiffness                            */
+
+    int32_t inertia;            /* 1 = inertia term on every vertex            */
+    double c;                   /* inertia weight (mass / dt^2)                */
+    const double *x_tilde;      /* [nv][3] inertial target positions           */
+
+    int32_t face_energy;        /* 1 = symmetric-Dirichlet term on every face  */
+    const double *dm_inv;       /* [nf][4] row-major 2x2 inverse rest edge matrix */
+    const double *area;         /* [nf] rest areas                              */
+
+    double kappa;               /* pair barrier stiffness                      */
+    double dhat;                /* pair barrier support, > 0 if pair_capacity>0 */
+} lad_mesh_desc;
+
+/* Summary of a context (lad_get_info synchronises the context's stream to
+ * read the device-side active pattern size). */
+typedef struct {
+    int32_t nv;
+    int32_t dtype;
+    int64_t nnzb_base;          /* blocks of the topology pattern              */
+    int64_t nnzb_active;        /* blocks of the active pattern (base + pairs) */
+    int64_t hvals_capacity;     /* blocks an hvals buffer must hold            */
+    int32_t npairs_active;
+    int32_t npatches;
+    int32_t lds_bytes_eval;     /* dynamic LDS of the eval kernel per workgroup */
+    int32_t lds_bytes_hvp;
+    int64_t spring_records;     /* element records incl. patch-boundary copies */
+    int64_t face_records;
+    int32_t max_colors;         /* colour phases of the deterministic mode     */
+    int32_t active_buffer;      /* 0 = topology pattern, 1/2 = pair buffers    */
+} lad_info;
+
+/*
+ * Build a context: validate the mesh, derive the block pattern on the GPU
+ * (parallel row count, wave/LDS prefix scan, fill, per-row sort and
+ * de-duplication), split the vertices into LDS-sized patches on the host,
+ * and upload the per-patch element records.  Source: key design 2 (patches
+ * with ribbon vertices staged in on-chip memory) and key design 3 (pattern
+ * preallocated at initialisation from the topology with a prefix sum).
+ * Synchronises `hip_stream`.  On success *out owns device memory until
+ * lad_destroy.  Errors: LAD_ERR_ARG (bad sizes, null arrays for enabled
+ * terms, vertex ids out of range, a spring with a == b, nnzb*9 >= 2^31),
+ * LAD_ERR_OOM, LAD_ERR_HIP.
+ */
+lad_status lad_build_pattern(const lad_mesh_desc *desc, void *hip_stream,
+                             lad_ctx **out);
+
+/* Read the context summary.  Synchronises the context's build stream. */
+lad_status lad_get_info(lad_ctx *ctx, lad_info *info);
+
+/*
+ * Active pattern: *nnzb gets its block count; *d_row_ptr and *d_col_idx get
+ * library-owned DEVICE pointers, valid until the next lad_insert_pairs or
+ * lad_destroy.  Synchronises `hip_stream` (which must be the stream the
+ * context's calls run on, so that pending inserts are complete).
+ */
+lad_status lad_get_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nnzb,
+                           const int32_t **d_row_ptr, const int32_t **d_col_idx);
+
+/*
+ * Copy the active pattern into caller-owned DEVICE buffers: d_row_ptr gets
+ * nv+1 entries, d_col_idx gets nnzb entries (*nnzb, which must not exceed
+ * col_capacity).  Synchronises `hip_stream` to read the active buffer, then
+ * copies on it and synchronises again.  Errors: LAD_ERR_ARG (NULL pointer),
+ * LAD_ERR_CAPACITY (col_capacity < nnzb; nothing copied).
+ */
+lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
+                            int32_t *d_col_idx, int64_t col_capacity, int64_t *nnzb);
+
+/*
+ * Energy, gradient and block-CSR Hessian at positions d_x.
+ * Source: section "Method" (g = sum S_j^T g_j, H = sum S_j^T H_j S_j) and
+ * key design 1 (per-element forward mode; global traffic is one read of the
+ * mesh and one write of the derivatives).
+ *   d_x      device [nv][3] dtype, read only.
+ *   d_energy device double, overwritten with F(x).
+ *   d_grad   device [nv][3] dtype, fully overwritten.
+ *   d_hvals  device [hvals_capacity][3][3] dtype; the first nnzb_active
+ *            blocks are fully overwritten in the active pattern's order.
+ *   hvals_capacity_blocks must be >= lad_info.hvals_capacity.
+ * Asynchronous on `hip_stream`; no host synchronisation.  Outputs must not
+ * alias inputs.  Errors: LAD_ERR_ARG (null pointer, capacity too small).
+ */
+lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x,
+                                     double *d_energy, void *d_grad,
+                                     void *d_hvals, int64_t hvals_capacity_blocks,
+                                     void *hip_stream);
+
+/*
+ * Matrix-free Hessian-vector product y = H(x) v, H never stored.
+ * Source: section "Method" (matrix-free operations on the assembled
+ * derivatives) and the parameterisation application in "Results".
+ *   d_x, d_v device [nv][3] dtype, read only; d_y device [nv][3] dtype,
+ *   fully overwritten.  Asynchronous; no host synchronisation.
+ */
+lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y,
+                   void *hip_stream);
+
+/*
+ * Replace the runtime vertex-vertex pairs: the next pattern is
+ * topology U {(i,j),(j,i) for every pair}, sorted and de-duplicated; the
+ * previous pairs are dropped.  Built on the GPU into the inactive one of two
+ * reserved pattern buffers, then made active by a device-side swap (no host
+ * round trip).  Source: key design 4 (decoupled discovery and evaluation,
+ * double-buffered CSR with reserved storage).
+ *   d_pairs  device int32 [npairs][2]; read during the call's kernels only.
+ *   npairs   0 <= npairs <= pair_capacity (0 restores the topology pattern).
+ * Host errors: LAD_ERR_ARG, LAD_ERR_CAPACITY (npairs > pair_capacity); the
+ * pattern is then unchanged.  Device-side checks (index out of range, i == j,
+ * a patch's reserved map exceeded) keep the previous pattern and pairs
+ * active and latch an error readable with lad_device_status.
+ * Asynchronous; hvals buffers sized to lad_info.hvals_capacity stay valid.
+ */
+lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs,
+                            void *hip_stream);
+
+/*
+ * Read and clear the device-side error latch set by lad_insert_pairs.
+ * *status gets LAD_OK, LAD_ERR_PAIRS or LAD_ERR_CAPACITY.  Synchronises
+ * `hip_stream`.
+ */
+lad_status lad_device_status(lad_ctx *ctx, void *hip_stream, int32_t *status);
+
+/* Message for the last host-side error of this context ("" if none).  The
+ * string is owned by the context.  With ctx == NULL: the last error of a
+ * failed lad_build_pattern in this thread. */
+const char *lad_last_error(const lad_ctx *ctx);
+
+/* Static name of a status code. */
+const char *lad_status_string(lad_status s);
+
+/* Release the context and its device memory (synchronises the device).
+ * NULL is a no-op.  The pointer is invalid afterwards. */
+void lad_destroy(lad_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LAD_H */

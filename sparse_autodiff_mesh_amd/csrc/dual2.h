@@ -1,0 +1,216 @@
+// dual2.h -- second-order forward-mode dual numbers held in registers.
+//
+// A Dual2<T, N> carries a scalar u together with its gradient du/dz (N
+// entries) and its Hessian d2u/dz2 (N(N+1)/2 packed upper-triangle entries)
+// with respect to N seeded variables z.  Every operation propagates all three
+// by the chain rule, so evaluating a local energy on seeded inputs yields its
+// value, dense local gradient and dense local Hessian in one forward pass,
+// with no tape and no memory traffic.  Source: page "Locality-Aware Automatic
+// Differentiation on the GPU for Mesh-Based Computations", key design 1
+// (element-level forward mode; primal, directional derivatives and local
+// Hessians stay in registers or shared memory).
+//
+// Everything is fully unrolled at compile time; N is small (3 for two-vertex
+// radial terms, 6 for faces, 9 for a face seeded in world coordinates).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace lad {
+
+template <int N>
+struct Tri {
+    static constexpr int size = N * (N + 1) / 2;
+    // packed index of (i, j), i <= j, row-major upper triangle
+    __host__ __device__ static constexpr int idx(int i, int j)
+    {
+        return i * N - (i * (i - 1)) / 2 + (j - i);
+    }
+};
+
+template <typename T, int N>
+struct Dual2 {
+    static constexpr int NH = Tri<N>::size;
+    T v;
+    T g[N];
+    T h[NH];
+
+    __device__ __forceinline__ static Dual2 constant(T c)
+    {
+        Dual2 r;
+        r.v = c;
+#pragma unroll
+        for (int i = 0; i < N; ++i) r.g[i] = T(0);
+#pragma unroll
+        for (int i = 0; i < NH; ++i) r.h[i] = T(0);
+        return r;
+    }
+    // the k-th seeded variable with value c
+    __device__ __forceinline__ static Dual2 var(T c, int k)
+    {
+        Dual2 r = constant(c);
+#pragma unroll
+        for (int i = 0; i < N; ++i) r.g[i] = (i == k) ? T(1) : T(0);
+        return r;
+    }
+    __device__ __forceinline__ T hess(int i, int j) const
+    {
+        return i <= j ? h[Tri<N>::idx(i, j)] : h[Tri<N>::idx(j, i)];
+    }
+};
+
+// ---- linear operations --------------------------------------------------
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator+(const Dual2<T, N> &a, const Dual2<T, N> &b)
+{
+    Dual2<T, N> r;
+    r.v = a.v + b.v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = a.g[i] + b.g[i];
+#pragma unroll
+    for (int i = 0; i < Dual2<T, N>::NH; ++i) r.h[i] = a.h[i] + b.h[i];
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator-(const Dual2<T, N> &a, const Dual2<T, N> &b)
+{
+    Dual2<T, N> r;
+    r.v = a.v - b.v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = a.g[i] - b.g[i];
+#pragma unroll
+    for (int i = 0; i < Dual2<T, N>::NH; ++i) r.h[i] = a.h[i] - b.h[i];
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator-(const Dual2<T, N> &a)
+{
+    Dual2<T, N> r;
+    r.v = -a.v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = -a.g[i];
+#pragma unroll
+    for (int i = 0; i < Dual2<T, N>::NH; ++i) r.h[i] = -a.h[i];
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator*(T s, const Dual2<T, N> &a)
+{
+    Dual2<T, N> r;
+    r.v = s * a.v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = s * a.g[i];
+#pragma unroll
+    for (int i = 0; i < Dual2<T, N>::NH; ++i) r.h[i] = s * a.h[i];
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator+(const Dual2<T, N> &a, T s)
+{
+    Dual2<T, N> r = a;
+    r.v = a.v + s;
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator-(const Dual2<T, N> &a, T s)
+{
+    Dual2<T, N> r = a;
+    r.v = a.v - s;
+    return r;
+}
+
+// ---- product rule ---------------------------------------------------------
+// (ab)'  = a'b + ab'
+// (ab)'' = a''b + ab'' + a' b'^T + b' a'^T
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator*(const Dual2<T, N> &a, const Dual2<T, N> &b)
+{
+    Dual2<T, N> r;
+    r.v = a.v * b.v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = a.v * b.g[i] + b.v * a.g[i];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int j = i; j < N; ++j) {
+            const int k = Tri<N>::idx(i, j);
+            r.h[k] = a.v * b.h[k] + b.v * a.h[k] + (a.g[i] * b.g[j] + a.g[j] * b.g[i]);
+        }
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> sqr(const Dual2<T, N> &a)
+{
+    Dual2<T, N> r;
+    r.v = a.v * a.v;
+    const T two_v = T(2) * a.v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = two_v * a.g[i];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int j = i; j < N; ++j) {
+            const int k = Tri<N>::idx(i, j);
+            r.h[k] = two_v * a.h[k] + T(2) * (a.g[i] * a.g[j]);
+        }
+    return r;
+}
+
+// ---- scalar functions: f(a)' = f1 a',  f(a)'' = f1 a'' + f2 a' a'^T ------
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> chain(const Dual2<T, N> &a, T f0, T f1, T f2)
+{
+    Dual2<T, N> r;
+    r.v = f0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.g[i] = f1 * a.g[i];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int j = i; j < N; ++j) {
+            const int k = Tri<N>::idx(i, j);
+            r.h[k] = f1 * a.h[k] + f2 * (a.g[i] * a.g[j]);
+        }
+    return r;
+}
+
+__device__ __forceinline__ float lad_sqrt(float x) { return __builtin_sqrtf(x); }
+__device__ __forceinline__ double lad_sqrt(double x) { return __builtin_sqrt(x); }
+__device__ __forceinline__ float lad_log(float x) { return ::logf(x); }
+__device__ __forceinline__ double lad_log(double x) { return ::log(x); }
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> sqrt(const Dual2<T, N> &a)
+{
+    const T s = lad_sqrt(a.v);
+    const T inv = T(1) / s;
+    return chain(a, s, T(0.5) * inv, T(-0.25) * inv * inv * inv);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> log(const Dual2<T, N> &a)
+{
+    const T inv = T(1) / a.v;
+    return chain(a, lad_log(a.v), inv, -inv * inv);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> reciprocal(const Dual2<T, N> &a)
+{
+    const T inv = T(1) / a.v;
+    return chain(a, inv, -inv * inv, T(2) * inv * inv * inv);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Dual2<T, N> operator/(const Dual2<T, N> &a, const Dual2<T, N> &b)
+{
+    return a * reciprocal(b);
+}
+
+}  // namespace lad

@@ -1,0 +1,557 @@
+// lad_api.cpp -- the C ABI of liblad: argument checks, context lifetime and
+// the order of kernel launches.  Every argument is checked on the host
+// before anything touches the GPU; the per-step calls enqueue on the
+// caller's stream and never synchronise.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lad_internal.h"
+
+namespace lad {
+hipError_t raise_lds_limits();
+}
+
+using namespace lad;
+
+struct lad_ctx {
+    int32_t nv = 0;
+    lad_dtype dtype = LAD_F32;
+    int32_t es = 4;
+    int32_t det = 0;
+    hipStream_t stream = nullptr;
+    int64_t nnzb_base = 0, hcap = 0;
+    int32_t pair_cap = 0;
+    double k = 0, c = 0, kappa = 0, dhat = 0;
+    int32_t springs_on = 0, faces_on = 0, inertia_on = 0;
+    int32_t npatch = 0, lds_eval = 0, lds_hvp = 0, max_colors = 0;
+    int64_t nspr_rec = 0, nfac_rec = 0;
+    int32_t pair_blocks = 0;
+
+    std::vector<void *> allocs;
+    PatchHdr *d_hdr = nullptr;
+    int32_t *d_rib = nullptr;
+    SpringRec *d_spr = nullptr;
+    void *d_spr_rest = nullptr;
+    FaceRec *d_fac = nullptr;
+    void *d_fac_dm = nullptr;
+    void *d_fac_area = nullptr;
+    int32_t *d_col_bounds = nullptr;
+    uint16_t *d_diag_rel = nullptr;
+    void *d_xt = nullptr;
+    DevState *d_state = nullptr;
+    double *d_epart = nullptr;
+    PatternBufs pat{};
+    InsertBufs ins{};
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_build_error;
+
+lad_status fail(lad_ctx *ctx, lad_status s, const std::string &msg)
+{
+    if (ctx) ctx->err = msg;
+    else g_build_error = msg;
+    return s;
+}
+
+lad_status hip_fail(lad_ctx *ctx, hipError_t e, const char *what)
+{
+    return fail(ctx, LAD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename T>
+hipError_t dev_alloc(lad_ctx *ctx, T **p, size_t count)
+{
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, count > 0 ? count * sizeof(T) : 16);
+    if (e == hipSuccess) {
+        ctx->allocs.push_back(q);
+        *p = static_cast<T *>(q);
+    }
+    return e;
+}
+
+void free_all(lad_ctx *ctx)
+{
+    for (void *p : ctx->allocs) (void)hipFree(p);
+    ctx->allocs.clear();
+}
+
+std::string check_desc(const lad_mesh_desc *d)
+{
+    if (!d) return "desc is NULL";
+    if (d->nv <= 0) return "nv must be >= 1";
+    if (d->nf < 0 || d->ns < 0) return "nf and ns must be >= 0";
+    if (d->dtype != LAD_F32 && d->dtype != LAD_F64) return "dtype must be LAD_F32 or LAD_F64";
+    if (d->pair_capacity < 0) return "pair_capacity must be >= 0";
+    if (d->patch_lds_bytes < 0 || d->patch_lds_bytes > 160 * 1024)
+        return "patch_lds_bytes must be in [0, 163840]";
+    if (d->nf > 0 && !d->faces) return "faces is NULL";
+    for (int64_t f = 0; f < d->nf; ++f) {
+        const int32_t *t = d->faces + 3 * f;
+        for (int i = 0; i < 3; ++i)
+            if (t[i] < 0 || t[i] >= d->nv) return "face vertex id out of range";
+        if (t[0] == t[1] || t[1] == t[2] || t[0] == t[2]) return "face with a repeated vertex";
+    }
+    if (d->ns > 0) {
+        if (!d->springs || !d->rest_len) return "springs or rest_len is NULL";
+        for (int64_t s = 0; s < d->ns; ++s) {
+            const int32_t a = d->springs[2 * s], b = d->springs[2 * s + 1];
+            if (a < 0 || a >= d->nv || b < 0 || b >= d->nv) return "spring vertex id out of range";
+            if (a == b) return "spring with a == b";
+            if (!std::isfinite(d->rest_len[s])) return "non-finite rest length";
+        }
+        if (!std::isfinite(d->k)) return "non-finite k";
+    }
+    if (d->inertia) {
+        if (!d->x_tilde) return "x_tilde is NULL";
+        if (!std::isfinite(d->c)) return "non-finite c";
+    }
+    if (d->face_energy && d->nf > 0 && (!d->dm_inv || !d->area)) return "dm_inv or area is NULL";
+    if (d->pair_capacity > 0) {
+        if (!(d->dhat > 0) || !std::isfinite(d->dhat)) return "dhat must be > 0 with pairs";
+        if (!std::isfinite(d->kappa)) return "non-finite kappa";
+        if (int64_t(d->pair_capacity) * 2 >= (int64_t(1) << 30)) return "pair_capacity too large";
+    }
+    const int64_t raw = int64_t(d->nv) + 6 * int64_t(d->nf) + 2 * int64_t(d->ns);
+    if (raw >= (int64_t(1) << 31)) return "mesh too large for int32 pattern indices";
+    return "";
+}
+
+template <typename T>
+std::vector<T> narrow(const double *src, size_t n)
+{
+    std::vector<T> out(n);
+    for (size_t i = 0; i < n; ++i) out[i] = T(src[i]);
+    return out;
+}
+
+template <typename T>
+hipError_t upload(lad_ctx *ctx, T **dst, const std::vector<T> &src, hipStream_t s)
+{
+    hipError_t e = dev_alloc(ctx, dst, src.size());
+    if (e == hipSuccess && !src.empty())
+        e = hipMemcpyAsync(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice, s);
+    return e;
+}
+
+template <typename T>
+lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &plan, hipStream_t s)
+{
+    std::vector<T> rest(plan.spr_src.size());
+    for (size_t i = 0; i < rest.size(); ++i) rest[i] = T(d->rest_len[plan.spr_src[i]]);
+    std::vector<T> dm(plan.fac_src.size() * 4), area(plan.fac_src.size());
+    for (size_t i = 0; i < area.size(); ++i) {
+        const int64_t f = plan.fac_src[i];
+        for (int j = 0; j < 4; ++j) dm[4 * i + j] = T(d->dm_inv[4 * f + j]);
+        area[i] = T(d->area[f]);
+    }
+    T *p = nullptr;
+    hipError_t e = upload(ctx, &p, rest, s);
+    ctx->d_spr_rest = p;
+    if (e == hipSuccess) e = upload(ctx, &p, dm, s);
+    ctx->d_fac_dm = p;
+    if (e == hipSuccess) e = upload(ctx, &p, area, s);
+    ctx->d_fac_area = p;
+    if (e == hipSuccess && d->inertia) {
+        e = upload(ctx, &p, narrow<T>(d->x_tilde, size_t(d->nv) * 3), s);
+        ctx->d_xt = p;
+    }
+    // lifetime of the host vectors: synchronise before they go out of scope
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? LAD_OK : hip_fail(ctx, e, "upload of element constants");
+}
+
+template <typename T>
+PatchArgs<T> patch_args(const lad_ctx *ctx)
+{
+    PatchArgs<T> a{};
+    a.hdr = ctx->d_hdr;
+    a.npatch = ctx->npatch;
+    a.rib = ctx->d_rib;
+    a.spr = ctx->d_spr;
+    a.spr_rest = static_cast<const T *>(ctx->d_spr_rest);
+    a.fac = ctx->d_fac;
+    a.fac_dm = static_cast<const T *>(ctx->d_fac_dm);
+    a.fac_area = static_cast<const T *>(ctx->d_fac_area);
+    a.col_bounds = ctx->d_col_bounds;
+    a.diag_rel = ctx->d_diag_rel;
+    a.x_tilde = static_cast<const T *>(ctx->d_xt);
+    a.k = T(ctx->k);
+    a.c = T(ctx->c);
+    a.springs_on = ctx->springs_on;
+    a.faces_on = ctx->faces_on;
+    a.inertia_on = ctx->inertia_on;
+    a.state = ctx->d_state;
+    a.pat = ctx->pat;
+    return a;
+}
+
+template <typename T>
+hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, void *hv,
+                        hipStream_t s)
+{
+    const PatchArgs<T> a = patch_args<T>(ctx);
+    hipError_t e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g),
+                                  static_cast<T *>(hv), ctx->d_epart, ctx->det, ctx->lds_eval, s);
+    if (e == hipSuccess && ctx->pair_blocks > 0)
+        e = launch_pairs_eval<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
+                                 static_cast<T *>(g), static_cast<T *>(hv),
+                                 ctx->d_epart + ctx->npatch, ctx->pair_blocks, T(ctx->kappa),
+                                 T(ctx->dhat), s);
+    if (e == hipSuccess)
+        e = launch_energy_reduce(ctx->d_epart, ctx->npatch + ctx->pair_blocks, energy, s);
+    return e;
+}
+
+template <typename T>
+hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s)
+{
+    const PatchArgs<T> a = patch_args<T>(ctx);
+    hipError_t e = launch_hvp<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
+                                 static_cast<T *>(y), ctx->det, ctx->lds_hvp, s);
+    if (e == hipSuccess && ctx->pair_blocks > 0)
+        e = launch_pairs_hvp<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
+                                static_cast<const T *>(v), static_cast<T *>(y), ctx->pair_blocks,
+                                T(ctx->kappa), T(ctx->dhat), s);
+    return e;
+}
+
+lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
+{
+    hipError_t e;
+    const int32_t nv = d->nv;
+    ctx->nv = nv;
+    ctx->dtype = d->dtype;
+    ctx->es = d->dtype == LAD_F64 ? 8 : 4;
+    ctx->det = d->deterministic ? 1 : 0;
+    ctx->stream = s;
+    ctx->pair_cap = d->pair_capacity;
+    ctx->k = d->k;
+    ctx->c = d->c;
+    ctx->kappa = d->kappa;
+    ctx->dhat = d->dhat;
+    ctx->springs_on = d->ns > 0;
+    ctx->faces_on = d->face_energy && d->nf > 0;
+    ctx->inertia_on = d->inertia ? 1 : 0;
+
+    // ---- topology pattern on the GPU
+    std::vector<void *> temps;
+    auto tmp_alloc = [&](int32_t **p, size_t n) {
+        void *q = nullptr;
+        hipError_t r = hipMalloc(&q, (n > 0 ? n : 1) * sizeof(int32_t));
+        if (r == hipSuccess) {
+            temps.push_back(q);
+            *p = static_cast<int32_t *>(q);
+        }
+        return r;
+    };
+    auto free_temps = [&]() {
+        for (void *q : temps) (void)hipFree(q);
+        temps.clear();
+    };
+    const int64_t raw = int64_t(nv) + 6 * int64_t(d->nf) + 2 * int64_t(d->ns);
+    int32_t *d_faces = nullptr, *d_springs = nullptr;
+    PatternScratch sc{};
+    e = tmp_alloc(&d_faces, size_t(d->nf) * 3);
+    if (e == hipSuccess) e = tmp_alloc(&d_springs, size_t(d->ns) * 2);
+    if (e == hipSuccess) e = tmp_alloc(&sc.cnt, nv);
+    if (e == hipSuccess) e = tmp_alloc(&sc.off, size_t(nv) + 1);
+    if (e == hipSuccess) e = tmp_alloc(&sc.raw, size_t(raw));
+    if (e == hipSuccess) e = tmp_alloc(&sc.cur, nv);
+    if (e == hipSuccess) e = tmp_alloc(&sc.ucnt, nv);
+    if (e == hipSuccess) e = tmp_alloc(&sc.tmp, size_t(scan_tmp_size(nv)));
+    int32_t *d_rp0 = nullptr, *d_ci0 = nullptr;
+    if (e == hipSuccess) e = dev_alloc(ctx, &d_rp0, size_t(nv) + 1);
+    if (e != hipSuccess) {
+        free_temps();
+        return fail(ctx, LAD_ERR_OOM, std::string("device allocation: ") + hipGetErrorString(e));
+    }
+    if (d->nf > 0)
+        e = hipMemcpyAsync(d_faces, d->faces, size_t(d->nf) * 3 * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && d->ns > 0)
+        e = hipMemcpyAsync(d_springs, d->springs, size_t(d->ns) * 2 * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_pattern_count(nv, d->nf, d_faces, d->ns, d_springs, sc, s);
+    if (e == hipSuccess) e = launch_pattern_fill(nv, d->nf, d_faces, d->ns, d_springs, sc, s);
+    if (e == hipSuccess) e = launch_pattern_unique(nv, sc, s);
+    if (e == hipSuccess) e = launch_scan(sc.ucnt, d_rp0, nv, sc.tmp, s);
+    std::vector<int32_t> h_rp(size_t(nv) + 1);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h_rp.data(), d_rp0, h_rp.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        free_temps();
+        return hip_fail(ctx, e, "pattern build");
+    }
+    const int64_t nnzb = h_rp[nv];
+    ctx->nnzb_base = nnzb;
+    ctx->hcap = nnzb + 2 * int64_t(d->pair_capacity);
+    if (ctx->hcap * 9 >= (int64_t(1) << 31)) {
+        free_temps();
+        return fail(ctx, LAD_ERR_ARG, "pattern too large for int32 value indices");
+    }
+    e = dev_alloc(ctx, &d_ci0, size_t(nnzb));
+    if (e == hipSuccess) e = launch_pattern_compact(nv, sc, d_rp0, d_ci0, s);
+    std::vector<int32_t> h_ci(static_cast<size_t>(nnzb));
+    if (e == hipSuccess && nnzb > 0)
+        e = hipMemcpyAsync(h_ci.data(), d_ci0, h_ci.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    free_temps();
+    if (e != hipSuccess) return hip_fail(ctx, e, "pattern compaction");
+
+    // ---- patches (host)
+    PlanInput in;
+    in.nv = nv;
+    in.nf = d->nf;
+    in.faces = d->faces;
+    in.ns = d->ns;
+    in.springs = d->springs;
+    in.face_energy = ctx->faces_on;
+    in.row_ptr = h_rp.data();
+    in.col_idx = h_ci.data();
+    in.elem_size = ctx->es;
+    in.lds_budget = d->patch_lds_bytes > 0 ? d->patch_lds_bytes : 40 * 1024;
+    Plan plan;
+    std::string msg = build_plan(in, plan);
+    if (!msg.empty()) return fail(ctx, LAD_ERR_ARG, "patcher: " + msg);
+    ctx->npatch = int32_t(plan.hdr.size());
+    ctx->lds_eval = plan.lds_eval;
+    ctx->lds_hvp = plan.lds_hvp;
+    ctx->max_colors = plan.max_colors;
+    ctx->nspr_rec = int64_t(plan.spr.size());
+    ctx->nfac_rec = int64_t(plan.fac.size());
+
+    e = upload(ctx, &ctx->d_hdr, plan.hdr, s);
+    if (e == hipSuccess) e = upload(ctx, &ctx->d_rib, plan.rib, s);
+    if (e == hipSuccess) e = upload(ctx, &ctx->d_spr, plan.spr, s);
+    if (e == hipSuccess) e = upload(ctx, &ctx->d_fac, plan.fac, s);
+    if (e == hipSuccess) e = upload(ctx, &ctx->d_col_bounds, plan.col_bounds, s);
+    if (e == hipSuccess) e = upload(ctx, &ctx->d_diag_rel, plan.diag_rel, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "upload of patch tables");
+    lad_status st = ctx->dtype == LAD_F64 ? upload_constants<double>(ctx, d, plan, s)
+                                          : upload_constants<float>(ctx, d, plan, s);
+    if (st != LAD_OK) return st;
+
+    // ---- pattern buffers, device state, scratch
+    std::memset(&ctx->pat, 0, sizeof(ctx->pat));
+    std::memset(&ctx->ins, 0, sizeof(ctx->ins));
+    ctx->pat.rp[0] = d_rp0;
+    ctx->pat.ci[0] = d_ci0;
+    ctx->ins.rp[0] = d_rp0;
+    ctx->ins.ci[0] = d_ci0;
+    e = dev_alloc(ctx, &ctx->d_state, 1);
+    DevState hs{};
+    hs.nnzb[0] = int32_t(nnzb);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(ctx->d_state, &hs, sizeof(hs), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && d->pair_capacity > 0) {
+        const size_t cap2 = size_t(d->pair_capacity) * 2;
+        ctx->ins.ib_words = int32_t((ctx->hcap + 31) / 32);
+        for (int b = 1; b <= 2 && e == hipSuccess; ++b) {
+            e = dev_alloc(ctx, &ctx->ins.rp[b], size_t(nv) + 1);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.ci[b], size_t(ctx->hcap));
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.ib[b], size_t(ctx->ins.ib_words));
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pairs[b], cap2);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_ptr[b], size_t(nv) + 1);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc[b], cap2);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_row[b], cap2);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pnew[b], cap2);
+        }
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.cnt, size_t(nv));
+        if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.cnt, 0, size_t(nv) * 4, s);
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.newlen, size_t(nv));
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.tmp, size_t(scan_tmp_size(nv)));
+        for (int b = 1; b <= 2; ++b) {
+            ctx->pat.rp[b] = ctx->ins.rp[b];
+            ctx->pat.ci[b] = ctx->ins.ci[b];
+            ctx->pat.ib[b] = ctx->ins.ib[b];
+            ctx->pat.pairs[b] = ctx->ins.pairs[b];
+            ctx->pat.pinc_ptr[b] = ctx->ins.pinc_ptr[b];
+            ctx->pat.pinc[b] = ctx->ins.pinc[b];
+            ctx->pat.pinc_row[b] = ctx->ins.pinc_row[b];
+        }
+        ctx->pair_blocks = int32_t((cap2 + kThreads - 1) / kThreads);
+    }
+    if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_epart, size_t(ctx->npatch + ctx->pair_blocks));
+    if (e == hipSuccess && (ctx->lds_eval > 64 * 1024 || ctx->lds_hvp > 64 * 1024))
+        e = raise_lds_limits();
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "allocation of pattern buffers");
+    return LAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lad_status lad_build_pattern(const lad_mesh_desc *desc, void *hip_stream, lad_ctx **out)
+{
+    if (!out) return fail(nullptr, LAD_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    const std::string msg = check_desc(desc);
+    if (!msg.empty()) return fail(nullptr, LAD_ERR_ARG, msg);
+    lad_ctx *ctx = new (std::nothrow) lad_ctx();
+    if (!ctx) return fail(nullptr, LAD_ERR_OOM, "host allocation failed");
+    const lad_status s = build(desc, static_cast<hipStream_t>(hip_stream), ctx);
+    if (s != LAD_OK) {
+        g_build_error = ctx->err;
+        (void)hipStreamSynchronize(static_cast<hipStream_t>(hip_stream));
+        free_all(ctx);
+        delete ctx;
+        return s;
+    }
+    g_build_error.clear();
+    *out = ctx;
+    return LAD_OK;
+}
+
+lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
+{
+    if (!ctx || !info) return fail(ctx, LAD_ERR_ARG, "ctx or info is NULL");
+    DevState hs{};
+    hipError_t e = hipMemcpyAsync(&hs, ctx->d_state, sizeof(hs), hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lad_get_info");
+    std::memset(info, 0, sizeof(*info));
+    info->nv = ctx->nv;
+    info->dtype = ctx->dtype;
+    info->nnzb_base = ctx->nnzb_base;
+    info->nnzb_active = hs.active == 0 ? ctx->nnzb_base : hs.nnzb[hs.active];
+    info->hvals_capacity = ctx->hcap;
+    info->npairs_active = hs.active == 0 ? 0 : hs.np[hs.active];
+    info->npatches = ctx->npatch;
+    info->lds_bytes_eval = ctx->lds_eval;
+    info->lds_bytes_hvp = ctx->lds_hvp;
+    info->spring_records = ctx->nspr_rec;
+    info->face_records = ctx->nfac_rec;
+    info->max_colors = ctx->max_colors;
+    info->active_buffer = hs.active;
+    return LAD_OK;
+}
+
+lad_status lad_get_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nnzb,
+                           const int32_t **d_row_ptr, const int32_t **d_col_idx)
+{
+    if (!ctx || !nnzb || !d_row_ptr || !d_col_idx) return fail(ctx, LAD_ERR_ARG, "NULL argument");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    DevState hs{};
+    hipError_t e = hipMemcpyAsync(&hs, ctx->d_state, sizeof(hs), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lad_get_pattern");
+    const int a = hs.active;
+    if (a < 0 || a > 2) return fail(ctx, LAD_ERR_STATE, "corrupt device state");
+    *nnzb = a == 0 ? ctx->nnzb_base : hs.nnzb[a];
+    *d_row_ptr = ctx->pat.rp[a];
+    *d_col_idx = ctx->pat.ci[a];
+    return LAD_OK;
+}
+
+lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
+                            int32_t *d_col_idx, int64_t col_capacity, int64_t *nnzb)
+{
+    if (!ctx || !d_row_ptr || !d_col_idx || !nnzb) return fail(ctx, LAD_ERR_ARG, "NULL argument");
+    const int32_t *rp = nullptr, *ci = nullptr;
+    lad_status st = lad_get_pattern(ctx, hip_stream, nnzb, &rp, &ci);
+    if (st != LAD_OK) return st;
+    if (*nnzb > col_capacity) return fail(ctx, LAD_ERR_CAPACITY, "col_capacity below nnzb");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipMemcpyAsync(d_row_ptr, rp, (size_t(ctx->nv) + 1) * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && *nnzb > 0)
+        e = hipMemcpyAsync(d_col_idx, ci, size_t(*nnzb) * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lad_copy_pattern");
+    return LAD_OK;
+}
+
+lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x, double *d_energy,
+                                     void *d_grad, void *d_hvals,
+                                     int64_t hvals_capacity_blocks, void *hip_stream)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!d_x || !d_energy || !d_grad || !d_hvals) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    if (hvals_capacity_blocks < ctx->hcap)
+        return fail(ctx, LAD_ERR_ARG, "hvals capacity below " + std::to_string(ctx->hcap) + " blocks");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ctx->dtype == LAD_F64 ? enqueue_eval<double>(ctx, d_x, d_energy, d_grad, d_hvals, s)
+                                         : enqueue_eval<float>(ctx, d_x, d_energy, d_grad, d_hvals, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "eval launch");
+    return LAD_OK;
+}
+
+lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y, void *hip_stream)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!d_x || !d_v || !d_y) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ctx->dtype == LAD_F64 ? enqueue_hvp<double>(ctx, d_x, d_v, d_y, s)
+                                         : enqueue_hvp<float>(ctx, d_x, d_v, d_y, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hvp launch");
+    return LAD_OK;
+}
+
+lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs, void *hip_stream)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (npairs < 0) return fail(ctx, LAD_ERR_ARG, "npairs must be >= 0");
+    if (npairs > ctx->pair_cap)
+        return fail(ctx, LAD_ERR_CAPACITY,
+                    "npairs " + std::to_string(npairs) + " exceeds pair_capacity " +
+                        std::to_string(ctx->pair_cap));
+    if (npairs > 0 && !d_pairs) return fail(ctx, LAD_ERR_ARG, "d_pairs is NULL");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = npairs == 0 ? launch_restore_topology(ctx->d_state, s)
+                               : launch_insert(ctx->d_state, d_pairs, npairs, ctx->nv, ctx->ins,
+                                               ctx->d_hdr, ctx->npatch, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "insert launch");
+    return LAD_OK;
+}
+
+lad_status lad_device_status(lad_ctx *ctx, void *hip_stream, int32_t *status)
+{
+    if (!ctx || !status) return fail(ctx, LAD_ERR_ARG, "NULL argument");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    DevState hs{};
+    hipError_t e = hipMemcpyAsync(&hs, ctx->d_state, sizeof(hs), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    const int32_t zero = 0;
+    if (e == hipSuccess && hs.err_latched != 0)
+        e = hipMemcpyAsync(reinterpret_cast<char *>(ctx->d_state) + offsetof(DevState, err_latched),
+                           &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lad_device_status");
+    *status = (hs.err_latched & 1) ? LAD_ERR_PAIRS : (hs.err_latched & 2) ? LAD_ERR_CAPACITY : LAD_OK;
+    return LAD_OK;
+}
+
+const char *lad_last_error(const lad_ctx *ctx) { return ctx ? ctx->err.c_str() : g_build_error.c_str(); }
+
+const char *lad_status_string(lad_status s)
+{
+    switch (s) {
+    case LAD_OK: return "LAD_OK";
+    case LAD_ERR_ARG: return "LAD_ERR_ARG";
+    case LAD_ERR_CAPACITY: return "LAD_ERR_CAPACITY";
+    case LAD_ERR_OOM: return "LAD_ERR_OOM";
+    case LAD_ERR_HIP: return "LAD_ERR_HIP";
+    case LAD_ERR_STATE: return "LAD_ERR_STATE";
+    case LAD_ERR_PAIRS: return "LAD_ERR_PAIRS";
+    }
+    return "LAD_ERR_UNKNOWN";
+}
+
+void lad_destroy(lad_ctx *ctx)
+{
+    if (!ctx) return;
+    (void)hipStreamSynchronize(ctx->stream);
+    free_all(ctx);
+    delete ctx;
+}
+
+}  // extern "C"

@@ -1,0 +1,657 @@
+// lad_eval.hip -- per-patch evaluation, differentiation and assembly on
+// gfx950.
+//
+// Page "Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+// Computations":
+//   * key design 1: per-element forward-mode AD, every intermediate in
+//     registers or on-chip memory; global traffic is one read of the mesh
+//     and one write of the final sparse derivatives;
+//   * key design 2: one workgroup per patch, patch-local staging of
+//     positions (owned + ribbon vertices) in LDS;
+//   * section "Method": g = sum_j S_j^T g_j, H = sum_j S_j^T H_j S_j, plus the
+//     matrix-free Hessian-vector product.
+//
+// gfx950 design: a patch owns a contiguous range of rows, so its whole slice
+// of the block-CSR value array is accumulated in LDS (LDS atomics, or plain
+// adds in colour phases for the deterministic mode) and then streamed to HBM
+// once with 16-byte stores.  Nothing in HBM is zero-filled, read back or
+// updated atomically; the only HBM writes are the final values.
+#include "dual2.h"
+#include "energies.h"
+#include "lad_internal.h"
+
+namespace lad {
+
+namespace {
+
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Give every XCD a contiguous run of patches so neighbouring patches,
+// which share ribbon vertices, meet in the same L2.
+__device__ __forceinline__ int xcd_remap(int b, int n)
+{
+    const int q = n >> 3, r = n & 7;
+    const int x = b & 7, i = b >> 3;
+    return x * q + min(x, r) + i;
+}
+
+template <bool ATOMIC, typename T>
+__device__ __forceinline__ void lds_add(T *p, T v)
+{
+    if constexpr (ATOMIC)
+        __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+        *p += v;
+}
+
+// Add s * K (3x3 symmetric, packed in a Dual2<T,3> Hessian) into block B.
+template <bool ATOMIC, typename T>
+__device__ __forceinline__ void add_block3(T *B, const Dual2<T, 3> &e, T s)
+{
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(B + 3 * r + c, s * e.hess(r, c));
+}
+
+// Sum of `v` over the workgroup, in a fixed order; valid in thread 0.
+__device__ __forceinline__ double block_sum(double v, double *red)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0)
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) s += red[i];
+    return s;
+}
+
+template <typename T>
+struct Vec;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+template <>
+struct Vec<float> {
+    using type = f32x4;
+    static constexpr int n = 4;
+};
+template <>
+struct Vec<double> {
+    using type = f64x2;
+    static constexpr int n = 2;
+};
+
+// Copy n elements from LDS src to global dst.  The caller placed src so that
+// (src - 16B-aligned base) == (dst mod 16 bytes), hence the body moves in
+// aligned 16-byte vectors.
+template <typename T>
+__device__ __forceinline__ void stream_out(T *__restrict__ dst, const T *src, int n, int pad)
+{
+    constexpr int V = Vec<T>::n;
+    using VT = typename Vec<T>::type;
+    const int head = min(n, (V - pad) % V);
+    for (int i = threadIdx.x; i < head; i += kThreads) dst[i] = src[i];
+    const int nvec = (n - head) / V;
+    VT *dv = reinterpret_cast<VT *>(dst + head);
+    const VT *sv = reinterpret_cast<const VT *>(src + head);
+    for (int i = threadIdx.x; i < nvec; i += kThreads) __builtin_nontemporal_store(sv[i], dv + i);
+    for (int i = head + nvec * V + threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// Element bodies.  xs: staged positions (local ids); nown: owned count.
+// ---------------------------------------------------------------------------
+
+// Two-vertex spring, differentiated in z = x_a - x_b.  With K = d2f/dz2 and
+// q = df/dz the element blocks are g = [q, -q], H = [[K, -K], [-K, K]].
+template <bool ATOMIC, typename T>
+__device__ __forceinline__ void spring_eval(const SpringRec rec, T rest, T k, const T *xs,
+                                            T *H, T *gs, const uint16_t *dtab, int nown,
+                                            double &eacc)
+{
+    const int la = rec.lab & 0xFFFF, lb = rec.lab >> 16;
+    Dual2<T, 3> d[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(xs[3 * la + c] - xs[3 * lb + c], c);
+    const Dual2<T, 3> e = spring_energy(d, rest, k);
+    if (la < nown) {
+        eacc += double(e.v);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(gs + 3 * la + c, e.g[c]);
+        add_block3<ATOMIC>(H + 9 * dtab[la], e, T(1));
+        add_block3<ATOMIC>(H + 9 * (rec.blk & 0xFFFF), e, T(-1));
+    }
+    if (lb < nown) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(gs + 3 * lb + c, -e.g[c]);
+        add_block3<ATOMIC>(H + 9 * dtab[lb], e, T(1));
+        add_block3<ATOMIC>(H + 9 * (rec.blk >> 16), e, T(-1));
+    }
+}
+
+// Face: F = [x1-x0, x2-x0] M (M = Dm^-1), so dF[s][c]/dx_v[s] = w[v][c] with
+// w1 = M row 0, w2 = M row 1, w0 = -(w1 + w2).  The 3x3 block (v, u) is
+// B[s][t] = sum_{c,c'} w[v][c] w[u][c'] d2E/dF[s][c]dF[t][c'].
+template <typename T>
+struct FaceLocal {
+    Dual2<T, 6> e;
+    T w[3][2];
+};
+
+template <typename T>
+__device__ __forceinline__ void face_local(const FaceRec &rec, const T *dm, T area, const T *xs,
+                                           FaceLocal<T> &out)
+{
+    const T m00 = dm[0], m01 = dm[1], m10 = dm[2], m11 = dm[3];
+    const T *x0 = xs + 3 * rec.l[0];
+    const T *x1 = xs + 3 * rec.l[1];
+    const T *x2 = xs + 3 * rec.l[2];
+    Dual2<T, 6> F[6];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const T d0 = x1[r] - x0[r], d1 = x2[r] - x0[r];
+        F[2 * r + 0] = Dual2<T, 6>::var(d0 * m00 + d1 * m10, 2 * r + 0);
+        F[2 * r + 1] = Dual2<T, 6>::var(d0 * m01 + d1 * m11, 2 * r + 1);
+    }
+    out.e = face_energy(F, area);
+    out.w[1][0] = m00;
+    out.w[1][1] = m01;
+    out.w[2][0] = m10;
+    out.w[2][1] = m11;
+    out.w[0][0] = -(m00 + m10);
+    out.w[0][1] = -(m01 + m11);
+}
+
+template <bool ATOMIC, typename T>
+__device__ __forceinline__ void face_eval(const FaceRec rec, const T *dm, T area, const T *xs,
+                                          T *H, T *gs, int nown, double &eacc)
+{
+    FaceLocal<T> fl;
+    face_local(rec, dm, area, xs, fl);
+    const Dual2<T, 6> &e = fl.e;
+    if (rec.l[0] < nown) eacc += double(e.v);
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+        if (rec.l[v] >= nown) continue;
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+            lds_add<ATOMIC>(gs + 3 * rec.l[v] + s,
+                            fl.w[v][0] * e.g[2 * s] + fl.w[v][1] * e.g[2 * s + 1]);
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            T *B = H + 9 * rec.blk[3 * v + u];
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    // (Q w_u) with Q = d2E/dF[s][.] dF[t][.]
+                    const T q0 = e.hess(2 * s, 2 * t) * fl.w[u][0] +
+                                 e.hess(2 * s, 2 * t + 1) * fl.w[u][1];
+                    const T q1 = e.hess(2 * s + 1, 2 * t) * fl.w[u][0] +
+                                 e.hess(2 * s + 1, 2 * t + 1) * fl.w[u][1];
+                    lds_add<ATOMIC>(B + 3 * s + t, fl.w[v][0] * q0 + fl.w[v][1] * q1);
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Eval kernel: energy, gradient and Hessian block rows of one patch.
+// ---------------------------------------------------------------------------
+template <typename T, bool DET>
+__global__ void __launch_bounds__(kThreads)
+k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
+             double *__restrict__ epart)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int V = Vec<T>::n;
+    const int p = xcd_remap(blockIdx.x, gridDim.x);
+    const PatchHdr h = A.hdr[p];
+    const int tid = threadIdx.x;
+    const int act = A.state->active;
+    const int32_t *rpa = A.pat.rp[act];
+    const int32_t ra0 = rpa[h.v0];
+    const int32_t nact = rpa[h.v0 + h.nown] - ra0;
+    const bool mapped = nact != h.nblk;
+
+    // carve LDS (same order and sizes as lds_eval_bytes on the host)
+    const int nloc = h.nown + h.nrib;
+    int64_t off = 0;
+    T *Hbase = reinterpret_cast<T *>(smem + off);
+    off += align16((int64_t(h.nblk) * 9 + 4) * sizeof(T));
+    T *gbase = reinterpret_cast<T *>(smem + off);
+    off += align16((int64_t(h.nown) * 3 + 4) * sizeof(T));
+    T *xs = reinterpret_cast<T *>(smem + off);
+    off += align16(int64_t(nloc) * 3 * sizeof(T));
+    uint16_t *dtab = reinterpret_cast<uint16_t *>(smem + off);
+    off += align16(int64_t(h.nown) * 2);
+    uint16_t *amap = reinterpret_cast<uint16_t *>(smem + off);
+    off += align16(int64_t(h.amap_cap) * 2);
+    double *red = reinterpret_cast<double *>(smem + off);
+
+    const int hpad = mapped ? 0 : int((int64_t(ra0) * 9) % V);
+    T *H = Hbase + hpad;
+    const int gpad = int((int64_t(h.v0) * 3) % V);
+    T *gs = gbase + gpad;
+
+    // 1. zero the accumulators, stage positions (owned, then ribbon)
+    for (int i = tid; i < h.nblk * 9; i += kThreads) H[i] = T(0);
+    for (int i = tid; i < h.nown * 3; i += kThreads) gs[i] = T(0);
+    const T *xo = x + int64_t(h.v0) * 3;
+    for (int i = tid; i < h.nown * 3; i += kThreads) xs[i] = xo[i];
+    for (int i = tid; i < h.nrib * 3; i += kThreads) {
+        const int r = i / 3, c = i - 3 * r;
+        xs[3 * h.nown + i] = x[int64_t(A.rib[h.rib_off + r]) * 3 + c];
+    }
+    for (int i = tid; i < h.nown; i += kThreads) dtab[i] = A.diag_rel[h.v0 + i];
+    __syncthreads();
+
+    double eacc = 0.0;
+    // 2. inertia: one owned vertex per thread, first writer of its blocks
+    if (A.inertia_on) {
+        for (int i = tid; i < h.nown; i += kThreads) {
+            const T *xt = A.x_tilde + int64_t(h.v0 + i) * 3;
+            Dual2<T, 3> z[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) z[c] = Dual2<T, 3>::var(xs[3 * i + c] - xt[c], c);
+            const Dual2<T, 3> e = inertia_energy(z, A.c);
+            eacc += double(e.v);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) gs[3 * i + c] += e.g[c];
+            add_block3<false>(H + 9 * dtab[i], e, T(1));
+        }
+        __syncthreads();
+    }
+
+    // 3. springs
+    if (A.springs_on && h.nspr > 0) {
+        const SpringRec *R = A.spr + h.spr_off;
+        const T *L = A.spr_rest + h.spr_off;
+        if constexpr (DET) {
+            const int32_t *cb = A.col_bounds + h.col_off;
+            for (int c = 0; c < h.nspr_col; ++c) {
+                for (int e = cb[c] + tid; e < cb[c + 1]; e += kThreads)
+                    spring_eval<false>(R[e], L[e], A.k, xs, H, gs, dtab, h.nown, eacc);
+                __syncthreads();
+            }
+        } else {
+            for (int e = tid; e < h.nspr; e += kThreads)
+                spring_eval<true>(R[e], L[e], A.k, xs, H, gs, dtab, h.nown, eacc);
+        }
+    }
+
+    // 4. faces
+    if (A.faces_on && h.nfac > 0) {
+        const FaceRec *R = A.fac + h.fac_off;
+        const T *dm = A.fac_dm + int64_t(h.fac_off) * 4;
+        const T *ar = A.fac_area + h.fac_off;
+        if constexpr (DET) {
+            const int32_t *cb = A.col_bounds + h.col_off + (h.nspr_col ? h.nspr_col + 1 : 0);
+            for (int c = 0; c < h.nfac_col; ++c) {
+                for (int e = cb[c] + tid; e < cb[c + 1]; e += kThreads)
+                    face_eval<false>(R[e], dm + 4 * e, ar[e], xs, H, gs, h.nown, eacc);
+                __syncthreads();
+            }
+        } else {
+            for (int e = tid; e < h.nfac; e += kThreads)
+                face_eval<true>(R[e], dm + 4 * e, ar[e], xs, H, gs, h.nown, eacc);
+        }
+    }
+    __syncthreads();
+
+    // 5. write the owned slice of the active pattern's value array
+    T *dst = hv + int64_t(ra0) * 9;
+    if (!mapped) {
+        stream_out(dst, H, h.nblk * 9, hpad);
+    } else if (nact <= h.amap_cap) {
+        // pairs inserted blocks into these rows: map every active block to
+        // its base block (or to zero for an inserted one)
+        const int32_t *rp0 = A.pat.rp[0];
+        const uint32_t *ib = A.pat.ib[act];
+        for (int i = tid; i < h.nown; i += kThreads) {
+            const int32_t a0 = rpa[h.v0 + i] - ra0, a1 = rpa[h.v0 + i + 1] - ra0;
+            int32_t b = rp0[h.v0 + i] - h.blk0;
+            for (int32_t j = a0; j < a1; ++j) {
+                const int64_t gp = int64_t(ra0) + j;
+                const bool ins = (ib[gp >> 5] >> (gp & 31)) & 1u;
+                amap[j] = ins ? kNone : uint16_t(b++);
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < nact * 9; i += kThreads) {
+            const int j = i / 9, c = i - 9 * j;
+            const uint16_t m = amap[j];
+            dst[i] = (m == kNone) ? T(0) : H[9 * m + c];
+        }
+    }
+    stream_out(g + int64_t(h.v0) * 3, gs, h.nown * 3, gpad);
+
+    const double es = block_sum(eacc, red);
+    if (tid == 0) epart[p] = es;
+}
+
+// ---------------------------------------------------------------------------
+// HVP kernel: y = H(x) v for the owned rows of one patch, H never formed.
+// ---------------------------------------------------------------------------
+template <typename T, bool DET>
+__global__ void __launch_bounds__(kThreads)
+k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int p = xcd_remap(blockIdx.x, gridDim.x);
+    const PatchHdr h = A.hdr[p];
+    const int tid = threadIdx.x;
+    const int nloc = h.nown + h.nrib;
+    int64_t off = 0;
+    T *xs = reinterpret_cast<T *>(smem + off);
+    off += align16(int64_t(nloc) * 3 * sizeof(T));
+    T *vs = reinterpret_cast<T *>(smem + off);
+    off += align16(int64_t(nloc) * 3 * sizeof(T));
+    T *ys = reinterpret_cast<T *>(smem + off);
+
+    const T *xo = x + int64_t(h.v0) * 3;
+    const T *vo = v + int64_t(h.v0) * 3;
+    for (int i = tid; i < h.nown * 3; i += kThreads) {
+        xs[i] = xo[i];
+        vs[i] = vo[i];
+        ys[i] = T(0);
+    }
+    for (int i = tid; i < h.nrib * 3; i += kThreads) {
+        const int r = i / 3, c = i - 3 * r;
+        const int64_t gi = int64_t(A.rib[h.rib_off + r]) * 3 + c;
+        xs[3 * h.nown + i] = x[gi];
+        vs[3 * h.nown + i] = v[gi];
+    }
+    __syncthreads();
+
+    if (A.inertia_on) {
+        for (int i = tid; i < h.nown * 3; i += kThreads) ys[i] += A.c * vs[i];
+        __syncthreads();
+    }
+
+    auto spring_hvp = [&](const SpringRec rec, T rest, auto atomic_tag) {
+        constexpr bool AT = decltype(atomic_tag)::value;
+        const int la = rec.lab & 0xFFFF, lb = rec.lab >> 16;
+        Dual2<T, 3> d[3];
+        T dv[3];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            d[c] = Dual2<T, 3>::var(xs[3 * la + c] - xs[3 * lb + c], c);
+            dv[c] = vs[3 * la + c] - vs[3 * lb + c];
+        }
+        const Dual2<T, 3> e = spring_energy(d, rest, A.k);
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const T kv = e.hess(r, 0) * dv[0] + e.hess(r, 1) * dv[1] + e.hess(r, 2) * dv[2];
+            if (la < h.nown) lds_add<AT>(ys + 3 * la + r, kv);
+            if (lb < h.nown) lds_add<AT>(ys + 3 * lb + r, -kv);
+        }
+    };
+    auto face_hvp = [&](const FaceRec rec, const T *dm, T area, auto atomic_tag) {
+        constexpr bool AT = decltype(atomic_tag)::value;
+        FaceLocal<T> fl;
+        face_local(rec, dm, area, xs, fl);
+        // dF = B v_j, yF = (d2E/dF2) dF, y_v = B_v^T yF
+        T dF[6];
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dF[2 * s + c] = fl.w[0][c] * vs[3 * rec.l[0] + s] +
+                                fl.w[1][c] * vs[3 * rec.l[1] + s] +
+                                fl.w[2][c] * vs[3 * rec.l[2] + s];
+        T yF[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            T acc = T(0);
+#pragma unroll
+            for (int j = 0; j < 6; ++j) acc += fl.e.hess(i, j) * dF[j];
+            yF[i] = acc;
+        }
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            if (rec.l[u] >= h.nown) continue;
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+                lds_add<AT>(ys + 3 * rec.l[u] + s,
+                            fl.w[u][0] * yF[2 * s] + fl.w[u][1] * yF[2 * s + 1]);
+        }
+    };
+    using AtomicTag = std::integral_constant<bool, !DET>;
+
+    if (A.springs_on && h.nspr > 0) {
+        const SpringRec *R = A.spr + h.spr_off;
+        const T *L = A.spr_rest + h.spr_off;
+        if constexpr (DET) {
+            const int32_t *cb = A.col_bounds + h.col_off;
+            for (int c = 0; c < h.nspr_col; ++c) {
+                for (int e = cb[c] + tid; e < cb[c + 1]; e += kThreads)
+                    spring_hvp(R[e], L[e], AtomicTag{});
+                __syncthreads();
+            }
+        } else {
+            for (int e = tid; e < h.nspr; e += kThreads) spring_hvp(R[e], L[e], AtomicTag{});
+        }
+    }
+    if (A.faces_on && h.nfac > 0) {
+        const FaceRec *R = A.fac + h.fac_off;
+        const T *dm = A.fac_dm + int64_t(h.fac_off) * 4;
+        const T *ar = A.fac_area + h.fac_off;
+        if constexpr (DET) {
+            const int32_t *cb = A.col_bounds + h.col_off + (h.nspr_col ? h.nspr_col + 1 : 0);
+            for (int c = 0; c < h.nfac_col; ++c) {
+                for (int e = cb[c] + tid; e < cb[c + 1]; e += kThreads)
+                    face_hvp(R[e], dm + 4 * e, ar[e], AtomicTag{});
+                __syncthreads();
+            }
+        } else {
+            for (int e = tid; e < h.nfac; e += kThreads)
+                face_hvp(R[e], dm + 4 * e, ar[e], AtomicTag{});
+        }
+    }
+    __syncthreads();
+    T *yo = y + int64_t(h.v0) * 3;
+    for (int i = tid; i < h.nown * 3; i += kThreads) yo[i] = ys[i];
+}
+
+// ---------------------------------------------------------------------------
+// Pair terms: row gather.  One thread per row that has pairs; it evaluates
+// each of the row's pairs (in pair order) and adds the row's contributions,
+// so every block and gradient entry has a single writer and the summation
+// order is fixed.  Runs after the patch kernel on the same stream.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t find_col(const int32_t *ci, int32_t lo, int32_t hi, int32_t b)
+{
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (ci[mid] < b) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+template <typename T, bool HVP>
+__global__ void __launch_bounds__(kThreads)
+k_pairs(const DevState *__restrict__ st, PatternBufs pat, const T *__restrict__ x,
+        const T *__restrict__ v, T *__restrict__ out_vec, T *__restrict__ hv,
+        double *__restrict__ epart, T kappa, T dhat)
+{
+    __shared__ double red[kWaves];
+    const int act = st->active;
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    double eacc = 0.0;
+    if (act != 0 && t < 2 * st->np[act]) {
+        const int32_t *pp = pat.pinc_ptr[act];
+        const int32_t a = pat.pinc_row[act][t];
+        if (t == pp[a]) {
+            const int32_t *prs = pat.pairs[act];
+            const int32_t *rp = pat.rp[act], *ci = pat.ci[act];
+            const int32_t r0 = rp[a], r1 = rp[a + 1];
+            T xa[3], ga[3] = {T(0), T(0), T(0)}, Kd[9] = {};
+#pragma unroll
+            for (int c = 0; c < 3; ++c) xa[c] = x[int64_t(a) * 3 + c];
+            for (int32_t k = pp[a]; k < pp[a + 1]; ++k) {
+                const int32_t q = pat.pinc[act][k];
+                const int32_t i = prs[2 * q], j = prs[2 * q + 1];
+                const int32_t b = (i == a) ? j : i;
+                T dz[3];
+#pragma unroll
+                for (int c = 0; c < 3; ++c) dz[c] = xa[c] - x[int64_t(b) * 3 + c];
+                const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
+                if (!(l2 < dhat * dhat)) continue;
+                Dual2<T, 3> d[3];
+#pragma unroll
+                for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(dz[c], c);
+                const Dual2<T, 3> e = barrier_energy(d, kappa, dhat);
+                if (i == a) eacc += double(e.v);
+                if constexpr (HVP) {
+#pragma unroll
+                    for (int r = 0; r < 3; ++r) {
+                        T kv = T(0);
+#pragma unroll
+                        for (int c = 0; c < 3; ++c)
+                            kv += e.hess(r, c) * (v[int64_t(a) * 3 + c] - v[int64_t(b) * 3 + c]);
+                        ga[r] += kv;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) ga[c] += e.g[c];
+#pragma unroll
+                    for (int r = 0; r < 3; ++r)
+#pragma unroll
+                        for (int c = 0; c < 3; ++c) Kd[3 * r + c] += e.hess(r, c);
+                    const int32_t kb = find_col(ci, r0, r1, b);
+                    if (kb < r1 && ci[kb] == b) {
+                        T *B = hv + int64_t(kb) * 9;
+#pragma unroll
+                        for (int r = 0; r < 3; ++r)
+#pragma unroll
+                            for (int c = 0; c < 3; ++c) B[3 * r + c] -= e.hess(r, c);
+                    }
+                }
+            }
+            if constexpr (!HVP) {
+                const int32_t ka = find_col(ci, r0, r1, a);
+                if (ka < r1 && ci[ka] == a) {
+                    T *B = hv + int64_t(ka) * 9;
+#pragma unroll
+                    for (int r = 0; r < 9; ++r) B[r] += Kd[r];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 3; ++c) out_vec[int64_t(a) * 3 + c] += ga[c];
+        }
+    }
+    if constexpr (!HVP) {
+        const double es = block_sum(eacc, red);
+        if (threadIdx.x == 0) epart[blockIdx.x] = es;
+    }
+}
+
+// Sum of n partial energies in a fixed order (one workgroup).
+__global__ void __launch_bounds__(kThreads)
+k_energy_reduce(const double *__restrict__ part, int n, double *__restrict__ out)
+{
+    __shared__ double red[kWaves];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += kThreads) s += part[i];
+    const double tot = block_sum(s, red);
+    if (threadIdx.x == 0) *out = tot;
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hv, double *epart, int det,
+                       int lds_bytes, hipStream_t s)
+{
+    if (a.npatch == 0) return hipSuccess;
+    if (det)
+        hipLaunchKernelGGL((k_eval_patch<T, true>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
+                           a, x, g, hv, epart);
+    else
+        hipLaunchKernelGGL((k_eval_patch<T, false>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
+                           a, x, g, hv, epart);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y, int det, int lds_bytes,
+                      hipStream_t s)
+{
+    if (a.npatch == 0) return hipSuccess;
+    if (det)
+        hipLaunchKernelGGL((k_hvp_patch<T, true>), dim3(a.npatch), dim3(kThreads), lds_bytes, s, a,
+                           x, v, y);
+    else
+        hipLaunchKernelGGL((k_hvp_patch<T, false>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
+                           a, x, v, y);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x, T *g, T *hv,
+                             double *epart, int nblocks, T kappa, T dhat, hipStream_t s)
+{
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_pairs<T, false>), dim3(nblocks), dim3(kThreads), 0, s, st, pat, x,
+                       (const T *)nullptr, g, hv, epart, kappa, dhat);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x, const T *v, T *y,
+                            int nblocks, T kappa, T dhat, hipStream_t s)
+{
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_pairs<T, true>), dim3(nblocks), dim3(kThreads), 0, s, st, pat, x, v, y,
+                       (T *)nullptr, (double *)nullptr, kappa, dhat);
+    return hipGetLastError();
+}
+
+hipError_t launch_energy_reduce(const double *epart, int n, double *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_energy_reduce, dim3(1), dim3(kThreads), 0, s, epart, n, out);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t raise_lds_limit()
+{
+    hipError_t e = hipSuccess;
+    const int lim = 160 * 1024;
+    e = hipFuncSetAttribute((const void *)k_eval_patch<T, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lim);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)k_eval_patch<T, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lim);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)k_hvp_patch<T, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lim);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)k_hvp_patch<T, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lim);
+    return e;
+}
+
+hipError_t raise_lds_limits() { return raise_lds_limit<float>() == hipSuccess ? raise_lds_limit<double>() : hipErrorUnknown; }
+
+#define LAD_INST(T)                                                                                \
+    template hipError_t launch_eval<T>(const PatchArgs<T> &, const T *, T *, T *, double *, int,   \
+                                       int, hipStream_t);                                          \
+    template hipError_t launch_hvp<T>(const PatchArgs<T> &, const T *, const T *, T *, int, int,   \
+                                      hipStream_t);                                                \
+    template hipError_t launch_pairs_eval<T>(const DevState *, PatternBufs, const T *, T *, T *,   \
+                                             double *, int, T, T, hipStream_t);                    \
+    template hipError_t launch_pairs_hvp<T>(const DevState *, PatternBufs, const T *, const T *,   \
+                                            T *, int, T, T, hipStream_t);
+LAD_INST(float)
+LAD_INST(double)
+
+}  // namespace lad

@@ -1,0 +1,217 @@
+// lad_insert.hip -- double-buffered insertion of runtime vertex-vertex pairs.
+//
+// Page "Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+// Computations", key design 4: interaction pairs found at run time add
+// off-diagonal Hessian blocks; discovery is decoupled from evaluation, and a
+// double-buffered CSR with reserved storage takes the new non-zeros in
+// parallel on the GPU, then the buffers swap, with no CPU round trip.
+//
+// Pattern of a step = topology pattern U {(i,j), (j,i) : current pairs},
+// rows sorted and de-duplicated; the previous step's pairs are dropped.
+// Buffer 0 is the immutable topology pattern; buffers 1 and 2 alternate.
+// Every kernel below picks the back buffer from the device-side state, so
+// the host never needs to know which buffer is active.  The last kernel
+// commits (flips `active`) only if every device-side check passed.
+#include "lad_internal.h"
+
+namespace lad {
+
+hipError_t launch_scan_back(const int32_t *in, int32_t *const out[3], const DevState *st,
+                            int32_t n, int32_t *tmp, hipStream_t s);
+
+namespace {
+
+__device__ __forceinline__ int back_of(const DevState *st) { return st->active == 1 ? 2 : 1; }
+
+__global__ void k_ins_begin(DevState *st) { st->err_cur = 0; }
+
+// Validate, copy the pairs into the back buffer, count pairs per row.
+__global__ void __launch_bounds__(kThreads)
+k_ins_count(DevState *st, const int32_t *__restrict__ in, int32_t np, int32_t nv, InsertBufs b)
+{
+    const int32_t q = blockIdx.x * kThreads + threadIdx.x;
+    if (q >= np) return;
+    const int bk = back_of(st);
+    const int32_t i = in[2 * q], j = in[2 * q + 1];
+    b.pairs[bk][2 * q] = i;
+    b.pairs[bk][2 * q + 1] = j;
+    const bool ok = i >= 0 && i < nv && j >= 0 && j < nv && i != j;
+    if (!ok) {
+        atomicOr(&st->err_cur, 1);
+        return;
+    }
+    atomicAdd(&b.cnt[i], 1);
+    atomicAdd(&b.cnt[j], 1);
+}
+
+// Scatter pair ids into per-row incidence lists; cnt returns to zero.
+__global__ void __launch_bounds__(kThreads)
+k_ins_fill(const DevState *st, int32_t np, int32_t nv, InsertBufs b)
+{
+    const int32_t q = blockIdx.x * kThreads + threadIdx.x;
+    if (q >= np) return;
+    const int bk = back_of(st);
+    const int32_t i = b.pairs[bk][2 * q], j = b.pairs[bk][2 * q + 1];
+    if (!(i >= 0 && i < nv && j >= 0 && j < nv && i != j)) return;
+    const int32_t pi = b.pinc_ptr[bk][i] + atomicSub(&b.cnt[i], 1) - 1;
+    b.pinc[bk][pi] = q;
+    b.pinc_row[bk][pi] = i;
+    const int32_t pj = b.pinc_ptr[bk][j] + atomicSub(&b.cnt[j], 1) - 1;
+    b.pinc[bk][pj] = q;
+    b.pinc_row[bk][pj] = j;
+}
+
+__device__ __forceinline__ int32_t lower_bound(const int32_t *c, int32_t lo, int32_t hi, int32_t x)
+{
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (c[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Per row: order its pairs by pair id (fixed evaluation order), collect the
+// distinct partners that are not already in the topology row (sorted, into
+// pnew at the row's incidence offset) and emit the new row length.
+__global__ void __launch_bounds__(kThreads)
+k_ins_rows(const DevState *st, int32_t nv, InsertBufs b)
+{
+    const int32_t a = blockIdx.x * kThreads + threadIdx.x;
+    if (a >= nv) return;
+    const int bk = back_of(st);
+    const int32_t rb0 = b.rp[0][a], rb1 = b.rp[0][a + 1];
+    const int32_t p0 = b.pinc_ptr[bk][a], p1 = b.pinc_ptr[bk][a + 1];
+    int32_t len = rb1 - rb0;
+    if (p1 > p0) {
+        int32_t *pl = b.pinc[bk];
+        for (int32_t i = p0 + 1; i < p1; ++i) {
+            const int32_t key = pl[i];
+            int32_t j = i - 1;
+            while (j >= p0 && pl[j] > key) {
+                pl[j + 1] = pl[j];
+                --j;
+            }
+            pl[j + 1] = key;
+        }
+        const int32_t *prs = b.pairs[bk];
+        int32_t *pn = b.pnew[bk] + p0;
+        int32_t nn = 0;
+        for (int32_t k = p0; k < p1; ++k) {
+            const int32_t q = pl[k];
+            const int32_t other = prs[2 * q] == a ? prs[2 * q + 1] : prs[2 * q];
+            const int32_t pos = lower_bound(b.ci[0], rb0, rb1, other);
+            if (pos < rb1 && b.ci[0][pos] == other) continue;
+            bool dup = false;
+            for (int32_t m = 0; m < nn; ++m) dup |= pn[m] == other;
+            if (!dup) pn[nn++] = other;
+        }
+        for (int32_t i = 1; i < nn; ++i) {
+            const int32_t key = pn[i];
+            int32_t j = i - 1;
+            while (j >= 0 && pn[j] > key) {
+                pn[j + 1] = pn[j];
+                --j;
+            }
+            pn[j + 1] = key;
+        }
+        len += nn;
+    }
+    b.newlen[a] = len;
+}
+
+__global__ void __launch_bounds__(kThreads) k_ins_clearbits(const DevState *st, InsertBufs b)
+{
+    const int32_t w = blockIdx.x * kThreads + threadIdx.x;
+    if (w < b.ib_words) b.ib[back_of(st)][w] = 0u;
+}
+
+// Merge the topology row with the row's new partners into the back buffer
+// and flag the inserted positions.
+__global__ void __launch_bounds__(kThreads) k_ins_merge(const DevState *st, int32_t nv, InsertBufs b)
+{
+    const int32_t a = blockIdx.x * kThreads + threadIdx.x;
+    if (a >= nv) return;
+    const int bk = back_of(st);
+    const int32_t *cb = b.ci[0];
+    const int32_t rb0 = b.rp[0][a], rb1 = b.rp[0][a + 1];
+    const int32_t o0 = b.rp[bk][a], o1 = b.rp[bk][a + 1];
+    const int32_t nn = (o1 - o0) - (rb1 - rb0);
+    int32_t *out = b.ci[bk];
+    if (nn == 0) {
+        for (int32_t k = 0; k < rb1 - rb0; ++k) out[o0 + k] = cb[rb0 + k];
+        return;
+    }
+    const int32_t *pn = b.pnew[bk] + b.pinc_ptr[bk][a];
+    int32_t i = rb0, m = 0, o = o0;
+    while (o < o1) {
+        if (m >= nn && i >= rb1) break;
+        const bool take_new = m < nn && (i >= rb1 || pn[m] < cb[i]);
+        if (take_new) {
+            out[o] = pn[m++];
+            atomicOr(&b.ib[bk][o >> 5], 1u << (o & 31));
+        } else {
+            out[o] = cb[i++];
+        }
+        ++o;
+    }
+}
+
+// Every patch must still fit its reserved LDS block map.
+__global__ void __launch_bounds__(kThreads)
+k_ins_check(DevState *st, const PatchHdr *__restrict__ hdr, int32_t npatch, InsertBufs b)
+{
+    const int32_t p = blockIdx.x * kThreads + threadIdx.x;
+    if (p >= npatch) return;
+    const int bk = back_of(st);
+    const PatchHdr h = hdr[p];
+    const int32_t n = b.rp[bk][h.v0 + h.nown] - b.rp[bk][h.v0];
+    if (n > h.amap_cap) atomicOr(&st->err_cur, 2);
+}
+
+__global__ void k_ins_commit(DevState *st, int32_t np, int32_t nv, InsertBufs b)
+{
+    const int bk = back_of(st);
+    if (st->err_cur == 0) {
+        st->np[bk] = np;
+        st->nnzb[bk] = b.rp[bk][nv];
+        __threadfence();
+        st->active = bk;
+    } else {
+        st->err_latched |= st->err_cur;
+    }
+}
+
+__global__ void k_restore_topology(DevState *st) { st->active = 0; }
+
+inline unsigned blocks_for(int64_t n) { return unsigned((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32_t nv,
+                         InsertBufs b, const PatchHdr *hdr, int32_t npatch, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_ins_begin, dim3(1), dim3(1), 0, s, st);
+    hipLaunchKernelGGL(k_ins_count, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, d_pairs, np,
+                       nv, b);
+    hipError_t e = launch_scan_back(b.cnt, b.pinc_ptr, st, nv, b.tmp, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ins_fill, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, np, nv, b);
+    hipLaunchKernelGGL(k_ins_rows, dim3(blocks_for(nv)), dim3(kThreads), 0, s, st, nv, b);
+    e = launch_scan_back(b.newlen, b.rp, st, nv, b.tmp, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ins_clearbits, dim3(blocks_for(b.ib_words)), dim3(kThreads), 0, s, st, b);
+    hipLaunchKernelGGL(k_ins_merge, dim3(blocks_for(nv)), dim3(kThreads), 0, s, st, nv, b);
+    hipLaunchKernelGGL(k_ins_check, dim3(blocks_for(npatch)), dim3(kThreads), 0, s, st, hdr,
+                       npatch, b);
+    hipLaunchKernelGGL(k_ins_commit, dim3(1), dim3(1), 0, s, st, np, nv, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_restore_topology(DevState *st, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_restore_topology, dim3(1), dim3(1), 0, s, st);
+    return hipGetLastError();
+}
+
+}  // namespace lad

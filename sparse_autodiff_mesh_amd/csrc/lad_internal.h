@@ -1,0 +1,202 @@
+// lad_internal.h -- types shared by the host side of liblad (patcher, API)
+// and its HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+#include <string>
+#include <vector>
+
+#include "lad.h"
+
+namespace lad {
+
+constexpr int kThreads = 256;          // threads per workgroup, patch kernels
+constexpr uint16_t kNone = 0xFFFFu;    // "this row is not owned by the patch"
+constexpr int kMaxLocal = 65535;       // local vertex / block ids are uint16
+constexpr int kMaxColors = 256;        // colour phases per element kind
+
+// One two-vertex element seen from one patch.  lab = la | lb << 16 are the
+// patch-local vertex ids (owned vertices first, then ribbon vertices);
+// blk = blk_ab | blk_ba << 16 are patch-relative block indices of (a, b) in
+// row a and of (b, a) in row b (kNone when that row is not owned).
+struct SpringRec {
+    uint32_t lab;
+    uint32_t blk;
+};
+
+// One triangle seen from one patch: local vertex ids and the patch-relative
+// block index of (v_i, v_j) in row v_i for every ordered pair (kNone when
+// v_i is not owned).  24 bytes.
+struct FaceRec {
+    uint16_t l[3];
+    uint16_t blk[9];
+};
+
+// Per-patch header.  The patch owns vertices [v0, v0 + nown) and thereby
+// the contiguous block range [blk0, blk0 + nblk) of the topology pattern.
+struct PatchHdr {
+    int32_t v0, nown;        // owned vertex range
+    int32_t rib_off, nrib;   // ribbon (ghost) vertex list
+    int32_t spr_off, nspr;   // spring records
+    int32_t fac_off, nfac;   // face records
+    int32_t blk0, nblk;      // base block range of the owned rows
+    int32_t col_off;         // offset into the colour-bound list
+    int32_t nspr_col;        // spring colours (bounds at col_off .. +nspr_col)
+    int32_t nfac_col;        // face colours (bounds follow the spring bounds)
+    int32_t amap_cap;        // reserved LDS map entries for an active chunk
+    int32_t lds_eval;        // LDS bytes this patch needs in the eval kernel
+    int32_t lds_hvp;         // ... and in the HVP kernel
+};
+static_assert(sizeof(PatchHdr) == 64, "PatchHdr layout");
+
+// Device-side state of the double-buffered pattern.  Kernels read `active`
+// (0 = topology pattern, 1 or 2 = a pair buffer); only the commit kernel of
+// lad_insert_pairs writes it.
+struct DevState {
+    int32_t active;
+    int32_t err_latched;     // sticky error bits: 1 = bad pair, 2 = capacity
+    int32_t err_cur;         // error bits of the insert in flight
+    int32_t np[3];           // pairs of each buffer
+    int32_t nnzb[3];         // blocks of each buffer
+    int32_t pad[7];
+};
+
+// ---------------------------------------------------------------------------
+// Host-side patch plan (built by the patcher, uploaded by the API).
+// ---------------------------------------------------------------------------
+struct Plan {
+    int elem_size = 4;                     // sizeof(T)
+    std::vector<PatchHdr> hdr;
+    std::vector<int32_t> rib;              // ribbon vertex ids, sorted per patch
+    std::vector<SpringRec> spr;
+    std::vector<int32_t> spr_src;          // spring id behind each record
+    std::vector<FaceRec> fac;
+    std::vector<int32_t> fac_src;          // face id behind each record
+    std::vector<int32_t> col_bounds;       // colour bounds (record offsets)
+    std::vector<uint16_t> diag_rel;        // [nv] patch-relative diagonal block
+    std::vector<int32_t> vpatch;           // [nv] owning patch of each vertex
+    int32_t lds_eval = 0, lds_hvp = 0, max_colors = 0;
+};
+
+struct PlanInput {
+    int32_t nv = 0;
+    int32_t nf = 0;
+    const int32_t *faces = nullptr;
+    int32_t ns = 0;
+    const int32_t *springs = nullptr;
+    int32_t face_energy = 0;
+    const int32_t *row_ptr = nullptr;      // topology pattern (host copies)
+    const int32_t *col_idx = nullptr;
+    int32_t elem_size = 4;
+    int32_t lds_budget = 0;
+};
+
+// LDS bytes of one patch in the eval and HVP kernels (same formula the
+// kernels use to carve their dynamic LDS).
+int64_t lds_eval_bytes(int elem_size, int nblk, int nown, int nloc, int amap_cap);
+int64_t lds_hvp_bytes(int elem_size, int nown, int nloc);
+int32_t amap_capacity(int nblk);
+
+// Returns "" on success, else an error message.
+std::string build_plan(const PlanInput &in, Plan &out);
+
+// ---------------------------------------------------------------------------
+// Kernel argument bundles and launchers (defined in the .hip files).
+// ---------------------------------------------------------------------------
+struct PatternBufs {
+    const int32_t *rp[3];
+    const int32_t *ci[3];
+    const uint32_t *ib[3];       // inserted-block bits (buffers 1, 2)
+    const int32_t *pairs[3];
+    const int32_t *pinc_ptr[3];  // per-row pair incidence (buffers 1, 2)
+    const int32_t *pinc[3];
+    const int32_t *pinc_row[3];
+};
+
+template <typename T>
+struct PatchArgs {
+    const PatchHdr *hdr;
+    int32_t npatch;
+    const int32_t *rib;
+    const SpringRec *spr;
+    const T *spr_rest;
+    const FaceRec *fac;
+    const T *fac_dm;             // [records][4]
+    const T *fac_area;
+    const int32_t *col_bounds;
+    const uint16_t *diag_rel;
+    const T *x_tilde;            // null = no inertia
+    T k, c;
+    int32_t springs_on, faces_on, inertia_on;
+    const DevState *state;
+    PatternBufs pat;
+};
+
+template <typename T>
+hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hvals,
+                       double *epart, int det, int lds_bytes, hipStream_t s);
+template <typename T>
+hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y,
+                      int det, int lds_bytes, hipStream_t s);
+template <typename T>
+hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x,
+                             T *g, T *hvals, double *epart, int nblocks,
+                             T kappa, T dhat, hipStream_t s);
+template <typename T>
+hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x,
+                            const T *v, T *y, int nblocks, T kappa, T dhat,
+                            hipStream_t s);
+hipError_t raise_lds_limits();
+hipError_t launch_energy_reduce(const double *epart, int n, double *out,
+                                hipStream_t s);
+
+// Exclusive scan: out[0..n] with out[n] = total.  tmp needs
+// scan_tmp_size(n) int32 entries.
+int64_t scan_tmp_size(int64_t n);
+hipError_t launch_scan(const int32_t *in, int32_t *out, int32_t n, int32_t *tmp,
+                       hipStream_t s);
+
+// Pattern builder: topology rows from faces and springs.
+struct PatternScratch {
+    int32_t *cnt;      // [nv]
+    int32_t *off;      // [nv + 1]
+    int32_t *raw;      // [raw total]
+    int32_t *cur;      // [nv]
+    int32_t *ucnt;     // [nv]
+    int32_t *tmp;      // scan scratch
+};
+hipError_t launch_pattern_count(int32_t nv, int32_t nf, const int32_t *faces,
+                                int32_t ns, const int32_t *springs,
+                                PatternScratch sc, hipStream_t s);
+hipError_t launch_pattern_fill(int32_t nv, int32_t nf, const int32_t *faces,
+                               int32_t ns, const int32_t *springs,
+                               PatternScratch sc, hipStream_t s);
+hipError_t launch_pattern_unique(int32_t nv, PatternScratch sc, hipStream_t s);
+hipError_t launch_pattern_compact(int32_t nv, PatternScratch sc,
+                                  const int32_t *row_ptr, int32_t *col_idx,
+                                  hipStream_t s);
+
+// Pair insertion (double-buffered).  Mutable views of buffers 1 and 2.
+struct InsertBufs {
+    int32_t *rp[3];
+    int32_t *ci[3];
+    uint32_t *ib[3];
+    int32_t *pairs[3];
+    int32_t *pinc_ptr[3];
+    int32_t *pinc[3];
+    int32_t *pinc_row[3];
+    int32_t *pnew[3];            // distinct new partners per row (scratch)
+    int32_t *cnt;                // [nv], all zero between inserts
+    int32_t *newlen;             // [nv]
+    int32_t *tmp;                // scan scratch
+    int32_t ib_words;            // words of each inserted-bit array
+};
+hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np,
+                         int32_t nv, InsertBufs b, const PatchHdr *hdr,
+                         int32_t npatch, hipStream_t s);
+hipError_t launch_restore_topology(DevState *st, hipStream_t s);
+
+}  // namespace lad

@@ -1,0 +1,325 @@
+// lad_patch.cpp -- host-side mesh patcher.
+//
+// Splits the vertices into patches sized for one workgroup's LDS and emits,
+// per patch, the element records its kernel evaluates.  Source: page
+// "Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+// Computations", key design 2 (mesh cut into patches that fit the memory
+// hierarchy, one thread block per patch, ribbon/ghost elements for
+// cross-patch neighbours, patch-local staging of connectivity and
+// attributes).
+//
+// Design on gfx950 (differs from the page's RXMesh patches):
+//  * A patch owns a CONTIGUOUS range of vertex ids, so the block-CSR rows it
+//    owns form one contiguous range of the Hessian value array: the kernel
+//    accumulates that whole range in LDS and writes it back as one coalesced
+//    stream, and no block is ever zero-filled or atomically updated in HBM.
+//  * Owner computes: every element that touches an owned vertex is evaluated
+//    by that patch, and only the owned rows are written.  Elements on a patch
+//    boundary are evaluated once per patch that owns one of their vertices;
+//    ribbon vertices are the non-owned vertices of those elements.
+//  * Records inside a patch are greedily coloured so that no two elements of
+//    one colour share an owned vertex.  The deterministic mode runs the
+//    colours one after another with plain LDS read-add-write (a fixed
+//    summation order); the default mode uses LDS atomics and the same order
+//    keeps lanes of one wave off the same addresses.
+#include <algorithm>
+#include <cstring>
+
+#include "lad_internal.h"
+
+namespace lad {
+
+static int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+int32_t amap_capacity(int nblk) { return nblk + std::max(32, nblk / 8); }
+
+// Region order must match the carving in the kernels.
+int64_t lds_eval_bytes(int es, int nblk, int nown, int nloc, int amap_cap)
+{
+    int64_t b = 0;
+    b += align16((int64_t(nblk) * 9 + 4) * es);  // H chunk (+ vector pad)
+    b += align16(int64_t(nown) * 3 * es + 4 * es);  // g chunk (+ vector pad)
+    b += align16(int64_t(nloc) * 3 * es);        // staged positions
+    b += align16(int64_t(nown) * 2);             // diagonal block table
+    b += align16(int64_t(amap_cap) * 2);         // active->base block map
+    b += 64;                                     // energy reduction
+    return b;
+}
+
+int64_t lds_hvp_bytes(int es, int nown, int nloc)
+{
+    int64_t b = 0;
+    b += align16(int64_t(nloc) * 3 * es);        // x
+    b += align16(int64_t(nloc) * 3 * es);        // v
+    b += align16(int64_t(nown) * 3 * es);        // y accumulators
+    b += 64;
+    return b;
+}
+
+namespace {
+
+int32_t find_pos(const int32_t *row_ptr, const int32_t *col_idx, int32_t a, int32_t b)
+{
+    const int32_t *lo = col_idx + row_ptr[a], *hi = col_idx + row_ptr[a + 1];
+    const int32_t *it = std::lower_bound(lo, hi, b);
+    if (it == hi || *it != b) return -1;
+    return int32_t(it - lo);
+}
+
+// Greedy colouring of records that touch `m` owned vertices each.  `owned`
+// returns the owned-local ids of record r (negative = not owned).  Returns
+// the colour count, or -1 if more than kMaxColors are needed.
+template <class OwnedFn>
+int colour_records(int nrec, int nown, int m, OwnedFn owned, std::vector<int> &colour)
+{
+    constexpr int W = kMaxColors / 64;
+    std::vector<uint64_t> used(size_t(nown) * W, 0);
+    colour.assign(nrec, 0);
+    int ncol = 0;
+    int ids[3];
+    for (int r = 0; r < nrec; ++r) {
+        owned(r, ids);
+        uint64_t mask[W] = {};
+        for (int i = 0; i < m; ++i)
+            if (ids[i] >= 0)
+                for (int w = 0; w < W; ++w) mask[w] |= used[size_t(ids[i]) * W + w];
+        int c = -1;
+        for (int w = 0; w < W && c < 0; ++w)
+            if (~mask[w]) c = 64 * w + __builtin_ctzll(~mask[w]);
+        if (c < 0) return -1;
+        colour[r] = c;
+        for (int i = 0; i < m; ++i)
+            if (ids[i] >= 0) used[size_t(ids[i]) * W + c / 64] |= uint64_t(1) << (c % 64);
+        ncol = std::max(ncol, c + 1);
+    }
+    return ncol;
+}
+
+}  // namespace
+
+std::string build_plan(const PlanInput &in, Plan &out)
+{
+    const int32_t nv = in.nv;
+    const int es = in.elem_size;
+    const int32_t *rp = in.row_ptr, *ci = in.col_idx;
+    out = Plan();
+    out.elem_size = es;
+    if (nv <= 0) return "nv must be positive";
+
+    // ---- 1. patch boundaries: greedy over vertex ids under the LDS budget
+    std::vector<int32_t> stamp(nv, -1);
+    std::vector<int32_t> starts;
+    {
+        int32_t pid = 0, nown = 0, nblk = 0, nloc = 0;
+        starts.push_back(0);
+        for (int32_t v = 0; v < nv; ++v) {
+            const int32_t len = rp[v + 1] - rp[v];
+            int32_t fresh = 0;
+            for (int32_t k = rp[v]; k < rp[v + 1]; ++k) fresh += stamp[ci[k]] != pid;
+            auto fits = [&](int32_t o, int32_t b, int32_t l) {
+                return b <= kMaxLocal - 1 && l <= kMaxLocal - 1 &&
+                       amap_capacity(b) <= kMaxLocal &&
+                       lds_eval_bytes(es, b, o, l, amap_capacity(b)) <= in.lds_budget;
+            };
+            if (nown > 0 && !fits(nown + 1, nblk + len, nloc + fresh)) {
+                ++pid;
+                starts.push_back(v);
+                nown = nblk = nloc = 0;
+                fresh = len;  // nothing stamped with the new id yet
+            }
+            if (!fits(nown + 1, nblk + len, nloc + fresh))
+                return "vertex " + std::to_string(v) + " has a row too long for the LDS budget";
+            for (int32_t k = rp[v]; k < rp[v + 1]; ++k) stamp[ci[k]] = pid;
+            nown += 1;
+            nblk += len;
+            nloc += fresh;
+        }
+        starts.push_back(nv);
+    }
+    const int32_t np = int32_t(starts.size()) - 1;
+    out.vpatch.resize(nv);
+    for (int32_t p = 0; p < np; ++p)
+        for (int32_t v = starts[p]; v < starts[p + 1]; ++v) out.vpatch[v] = p;
+
+    // ---- 2. element -> patch incidence (counting sort by patch)
+    auto emit_lists = [&](int32_t ne, int m, const int32_t *ev, std::vector<int32_t> &off,
+                          std::vector<int32_t> &lst) {
+        off.assign(size_t(np) + 1, 0);
+        for (int32_t e = 0; e < ne; ++e) {
+            int32_t ps[3];
+            int cnt = 0;
+            for (int i = 0; i < m; ++i) {
+                int32_t p = out.vpatch[ev[int64_t(e) * m + i]];
+                bool dup = false;
+                for (int j = 0; j < cnt; ++j) dup |= ps[j] == p;
+                if (!dup) ps[cnt++] = p;
+            }
+            for (int j = 0; j < cnt; ++j) off[ps[j] + 1] += 1;
+        }
+        for (int32_t p = 0; p < np; ++p) off[p + 1] += off[p];
+        lst.assign(off[np], 0);
+        std::vector<int32_t> cur(off.begin(), off.end() - 1);
+        for (int32_t e = 0; e < ne; ++e) {
+            int32_t ps[3];
+            int cnt = 0;
+            for (int i = 0; i < m; ++i) {
+                int32_t p = out.vpatch[ev[int64_t(e) * m + i]];
+                bool dup = false;
+                for (int j = 0; j < cnt; ++j) dup |= ps[j] == p;
+                if (!dup) ps[cnt++] = p;
+            }
+            for (int j = 0; j < cnt; ++j) lst[cur[ps[j]]++] = e;
+        }
+    };
+    std::vector<int32_t> soff, slst, foff, flst;
+    if (in.ns > 0) emit_lists(in.ns, 2, in.springs, soff, slst);
+    else soff.assign(size_t(np) + 1, 0);
+    if (in.face_energy && in.nf > 0) emit_lists(in.nf, 3, in.faces, foff, flst);
+    else foff.assign(size_t(np) + 1, 0);
+
+    // ---- 3. per patch: local numbering, records, colours, LDS sizes
+    std::vector<int32_t> local(nv, -1);
+    std::fill(stamp.begin(), stamp.end(), -1);
+    out.hdr.resize(np);
+    out.diag_rel.assign(nv, kNone);
+    out.spr.reserve(slst.size());
+    out.spr_src.reserve(slst.size());
+    out.fac.reserve(flst.size());
+    out.fac_src.reserve(flst.size());
+    std::vector<int> colour;
+    std::vector<int32_t> order;
+    for (int32_t p = 0; p < np; ++p) {
+        PatchHdr &h = out.hdr[p];
+        std::memset(&h, 0, sizeof(h));
+        const int32_t v0 = starts[p], v1 = starts[p + 1], nown = v1 - v0;
+        h.v0 = v0;
+        h.nown = nown;
+        h.blk0 = rp[v0];
+        h.nblk = rp[v1] - rp[v0];
+        // local ids: owned first, then ribbon (ascending global id)
+        std::vector<int32_t> rib;
+        for (int32_t v = v0; v < v1; ++v) {
+            stamp[v] = p;
+            local[v] = v - v0;
+        }
+        for (int32_t v = v0; v < v1; ++v)
+            for (int32_t k = rp[v]; k < rp[v + 1]; ++k)
+                if (stamp[ci[k]] != p) {
+                    stamp[ci[k]] = p;
+                    rib.push_back(ci[k]);
+                }
+        std::sort(rib.begin(), rib.end());
+        for (size_t i = 0; i < rib.size(); ++i) local[rib[i]] = nown + int32_t(i);
+        h.rib_off = int32_t(out.rib.size());
+        h.nrib = int32_t(rib.size());
+        out.rib.insert(out.rib.end(), rib.begin(), rib.end());
+        const int32_t nloc = nown + h.nrib;
+
+        for (int32_t v = v0; v < v1; ++v) {
+            int32_t pos = find_pos(rp, ci, v, v);
+            if (pos < 0) return "diagonal block missing";
+            out.diag_rel[v] = uint16_t(rp[v] - h.blk0 + pos);
+        }
+        auto slot = [&](int32_t a, int32_t b) -> uint16_t {
+            if (a < v0 || a >= v1) return kNone;
+            int32_t pos = find_pos(rp, ci, a, b);
+            return pos < 0 ? kNone : uint16_t(rp[a] - h.blk0 + pos);
+        };
+
+        // springs
+        h.col_off = int32_t(out.col_bounds.size());
+        {
+            const int32_t n = soff[p + 1] - soff[p];
+            const int32_t *lst = slst.data() + soff[p];
+            int nc = colour_records(n, nown, 2, [&](int r, int *ids) {
+                const int32_t *s = in.springs + 2 * int64_t(lst[r]);
+                for (int i = 0; i < 2; ++i) {
+                    int32_t l = local[s[i]];
+                    ids[i] = l < nown ? l : -1;
+                }
+            }, colour);
+            if (nc < 0) return "too many spring colours in a patch";
+            order.resize(n);
+            for (int32_t r = 0; r < n; ++r) order[r] = r;
+            std::stable_sort(order.begin(), order.end(),
+                             [&](int32_t x, int32_t y) { return colour[x] < colour[y]; });
+            h.spr_off = int32_t(out.spr.size());
+            h.nspr = n;
+            h.nspr_col = nc;
+            int32_t c = -1;
+            for (int32_t i = 0; i < n; ++i) {
+                const int32_t r = order[i];
+                while (c < colour[r]) {
+                    out.col_bounds.push_back(i);
+                    ++c;
+                }
+                const int32_t s = lst[r];
+                const int32_t a = in.springs[2 * int64_t(s)], b = in.springs[2 * int64_t(s) + 1];
+                SpringRec rec;
+                rec.lab = uint32_t(local[a]) | (uint32_t(local[b]) << 16);
+                uint16_t sab = slot(a, b), sba = slot(b, a);
+                if ((a >= v0 && a < v1 && sab == kNone) || (b >= v0 && b < v1 && sba == kNone))
+                    return "spring block missing from pattern";
+                rec.blk = uint32_t(sab) | (uint32_t(sba) << 16);
+                out.spr.push_back(rec);
+                out.spr_src.push_back(s);
+            }
+            if (n > 0) out.col_bounds.push_back(n);
+            else h.nspr_col = 0;
+            out.max_colors = std::max(out.max_colors, h.nspr_col);
+        }
+        // faces
+        {
+            const int32_t n = foff[p + 1] - foff[p];
+            const int32_t *lst = flst.data() + foff[p];
+            int nc = colour_records(n, nown, 3, [&](int r, int *ids) {
+                const int32_t *t = in.faces + 3 * int64_t(lst[r]);
+                for (int i = 0; i < 3; ++i) {
+                    int32_t l = local[t[i]];
+                    ids[i] = l < nown ? l : -1;
+                }
+            }, colour);
+            if (nc < 0) return "too many face colours in a patch";
+            order.resize(n);
+            for (int32_t r = 0; r < n; ++r) order[r] = r;
+            std::stable_sort(order.begin(), order.end(),
+                             [&](int32_t x, int32_t y) { return colour[x] < colour[y]; });
+            h.fac_off = int32_t(out.fac.size());
+            h.nfac = n;
+            h.nfac_col = nc;
+            int32_t c = -1;
+            for (int32_t i = 0; i < n; ++i) {
+                const int32_t r = order[i];
+                while (c < colour[r]) {
+                    out.col_bounds.push_back(i);
+                    ++c;
+                }
+                const int32_t f = lst[r];
+                const int32_t *t = in.faces + 3 * int64_t(f);
+                FaceRec rec;
+                for (int a = 0; a < 3; ++a) {
+                    rec.l[a] = uint16_t(local[t[a]]);
+                    for (int b = 0; b < 3; ++b) {
+                        uint16_t s = slot(t[a], t[b]);
+                        if (t[a] >= v0 && t[a] < v1 && s == kNone)
+                            return "face block missing from pattern";
+                        rec.blk[3 * a + b] = s;
+                    }
+                }
+                out.fac.push_back(rec);
+                out.fac_src.push_back(f);
+            }
+            if (n > 0) out.col_bounds.push_back(n);
+            else h.nfac_col = 0;
+            out.max_colors = std::max(out.max_colors, h.nfac_col);
+        }
+        h.amap_cap = amap_capacity(h.nblk);
+        h.lds_eval = int32_t(lds_eval_bytes(es, h.nblk, nown, nloc, h.amap_cap));
+        h.lds_hvp = int32_t(lds_hvp_bytes(es, nown, nloc));
+        out.lds_eval = std::max(out.lds_eval, h.lds_eval);
+        out.lds_hvp = std::max(out.lds_hvp, h.lds_hvp);
+    }
+    return "";
+}
+
+}  // namespace lad

@@ -1,0 +1,149 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+identical seeded inputs.  Patterns must match bit for bit; values within the
+relative Frobenius tolerances in gpu_util.TOL."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_autodiff_mesh_amd import inputs
+
+from gpu_util import TOL, dev, host_input, log_case, rel
+
+pytestmark = pytest.mark.gpu
+
+
+def run_eval(lad, mesh, dtype, det=False, lds=0, springs=True, inertia=True, faces=False):
+    import torch
+    L = lad.Lad(mesh.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds,
+                **lad.mesh_terms(mesh, springs=springs, inertia=inertia, faces=faces))
+    prob = oracle.problem_from_mesh(mesh, springs=springs, inertia=inertia, faces=faces,
+                                    f32=(dtype == "f32"))
+    x_h = host_input(mesh.x, dtype)
+    E, g, H = L.eval(dev(x_h, dtype))
+    rp, ci = L.pattern()
+    torch.cuda.synchronize()
+    return L, prob, x_h, (E.cpu().numpy()[0], g.cpu().numpy(), H.cpu().numpy(),
+                          rp.cpu().numpy(), ci.cpu().numpy())
+
+
+def check_against_oracle(prob, x_h, res, dtype):
+    E, g, H, rp, ci = res
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(rp, orp), "row_ptr differs"
+    assert np.array_equal(ci, oci), "col_idx differs"
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    tol = TOL[dtype]
+    assert rel([E], [Eo]) <= tol, (E, Eo)
+    assert rel(g, go) <= tol, rel(g, go)
+    assert rel(H[: oci.size], Ho) <= tol, rel(H[: oci.size], Ho)
+    return orp, oci
+
+
+@pytest.mark.parametrize("n,dtype,det,lds", [
+    (10, "f64", False, 0), (10, "f64", True, 0), (10, "f32", False, 0),
+    (37, "f32", False, 6144), (37, "f64", True, 6144), (37, "f32", True, 6144),
+    (100, "f32", False, 0), (100, "f64", False, 0), (100, "f32", True, 0),
+])
+def test_cloth_eval(lad, n, dtype, det, lds):
+    log_case(test="cloth_eval", n=n, dtype=dtype, det=det, lds=lds)
+    m = inputs.cloth(n)
+    L, prob, x_h, res = run_eval(lad, m, dtype, det, lds)
+    info = L.get_info()
+    if lds:
+        assert info["npatches"] > 4  # several patches and ribbons
+    check_against_oracle(prob, x_h, res, dtype)
+    L.close()
+
+
+@pytest.mark.parametrize("n,dtype,det,lds", [
+    (12, "f64", False, 0), (33, "f32", False, 8192), (33, "f64", True, 8192),
+    (64, "f32", True, 0),
+])
+def test_face_eval(lad, n, dtype, det, lds):
+    log_case(test="face_eval", n=n, dtype=dtype, det=det, lds=lds)
+    m = inputs.face_grid(n)
+    L, prob, x_h, res = run_eval(lad, m, dtype, det, lds, springs=False, inertia=False,
+                                 faces=True)
+    check_against_oracle(prob, x_h, res, dtype)
+    L.close()
+
+
+@pytest.mark.parametrize("dtype,det", [("f64", False), ("f32", True)])
+def test_all_terms_eval(lad, dtype, det):
+    log_case(test="all_terms", dtype=dtype, det=det)
+    m = inputs.cloth(29)
+    L, prob, x_h, res = run_eval(lad, m, dtype, det, 7000, springs=True, inertia=True,
+                                 faces=True)
+    check_against_oracle(prob, x_h, res, dtype)
+    L.close()
+
+
+@pytest.mark.parametrize("n,dtype,det,faces,lds", [
+    (20, "f64", False, True, 0), (45, "f32", False, True, 8192), (45, "f64", True, False, 8192),
+    (64, "f32", True, True, 0),
+])
+def test_hvp(lad, n, dtype, det, faces, lds):
+    import torch
+    log_case(test="hvp", n=n, dtype=dtype, det=det, faces=faces, lds=lds)
+    m = inputs.cloth(n)
+    L = lad.Lad(m.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds,
+                **lad.mesh_terms(m, faces=faces))
+    prob = oracle.problem_from_mesh(m, faces=faces, f32=(dtype == "f32"))
+    x_h = host_input(m.x, dtype)
+    v_h = host_input(inputs.hvp_direction(m.nv), dtype)
+    y = L.hvp(dev(x_h, dtype), dev(v_h, dtype))
+    torch.cuda.synchronize()
+    orp, oci = oracle.pattern(prob)
+    yo = oracle.hvp(prob, orp, oci, x_h, v_h)
+    assert rel(y.cpu().numpy(), yo) <= TOL[dtype]
+    L.close()
+
+
+def test_single_vertex_and_isolated(lad):
+    """Degenerate meshes: one vertex with inertia only; a mesh with isolated
+    vertices (rows holding only the diagonal)."""
+    import torch
+    log_case(test="degenerate")
+    X = np.array([[0.1, 0.2, 0.3]])
+    L = lad.Lad(1, dtype="f64", x_tilde=np.zeros((1, 3)), c=4.0)
+    E, g, H = L.eval(dev(X, "f64"))
+    torch.cuda.synchronize()
+    assert abs(E.item() - 0.5 * 4.0 * 0.14) < 1e-15
+    assert np.allclose(g.cpu().numpy(), 4.0 * X)
+    assert np.allclose(H.cpu().numpy()[0], 4.0 * np.eye(3))
+    L.close()
+    faces = np.array([[0, 1, 2]], dtype=np.int32)
+    x = np.random.default_rng(3).normal(size=(6, 3))
+    springs = np.array([[0, 1], [1, 2], [0, 2], [4, 5]], dtype=np.int32)
+    rest = np.array([1.0, 1.1, 0.9, 0.5])
+    L = lad.Lad(6, dtype="f64", faces=faces, springs=springs, rest_len=rest, k=3.0,
+                x_tilde=np.zeros((6, 3)), c=2.0)
+    E, g, H = L.eval(dev(x, "f64"))
+    rp, ci = L.pattern()
+    torch.cuda.synchronize()
+    prob = oracle.Problem(nv=6, faces=faces, springs=springs, rest_len=rest, k=3.0,
+                          x_tilde=np.zeros((6, 3)), c=2.0)
+    check_against_oracle(prob, x, (E.item(), g.cpu().numpy(), H.cpu().numpy(),
+                                   rp.cpu().numpy(), ci.cpu().numpy()), "f64")
+    assert np.diff(rp.cpu().numpy())[3] == 1  # vertex 3 is isolated
+    L.close()
+
+
+def test_outputs_fully_overwritten(lad):
+    """Every call overwrites its outputs: stale buffer contents never leak."""
+    import torch
+    log_case(test="overwrite")
+    m = inputs.cloth(23)
+    L = lad.Lad(m.nv, dtype="f32", patch_lds_bytes=6144, **lad.mesh_terms(m))
+    x = dev(host_input(m.x, "f32"), "f32")
+    E1, g1, H1 = L.eval(x)
+    E2, g2, H2 = L.alloc_outputs()
+    E2.fill_(1e30)
+    g2.fill_(float("nan"))
+    H2.fill_(float("nan"))
+    L.eval(x, out=(E2, g2, H2))
+    torch.cuda.synchronize()
+    n = L.get_info()["nnzb_active"]
+    assert torch.equal(E1, E2) or abs(E1.item() - E2.item()) <= 1e-6 * abs(E1.item())
+    assert torch.isfinite(g2).all() and torch.isfinite(H2[:n]).all()
+    L.close()
