@@ -1,0 +1,382 @@
+#!/usr/bin/env python3
+"""Throughput of per-element forward-mode AD with on-GPU sparse assembly.
+
+One step is one call of lad_eval_energy_grad_hess on the mass-spring cloth
+over a 1000 x 1000 vertex grid in fp32 (2,996,001 springs + 1,000,000 inertia
+terms; gradient of 3e6 values and a 3x3-block CSR Hessian of 6,992,002
+blocks).  This is the workload of the cloth timing table on the page
+"Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+Computations" (section "Results": gradient and Hessian per step, linear solve
+excluded).  Inputs are seeded synthetic grids, resident in HBM before the
+timed region starts; the pattern build (initialisation) is not timed.
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline      the eval kernel against the HBM peak: compulsory bytes per
+                launch (one read of the mesh data, one write of g and H) over
+                the kernel's mean duration from HIP events on its stream;
+  cpu_baseline  the fp64 CPU oracle, single-threaded, on the same workload;
+  secondary     the other workloads (face-energy grid eval and matrix-free
+                HVP, cloth plus contact-pair insertion, 100 x 100 cloth).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--n 1000]
+                    [--no-cpu-baseline] [--no-secondary] [--flush-mall]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published peak
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_eval_cloth1000_f32.txt")
+KERNEL_SOURCES = ["lad_eval.hip", "dual2.h", "energies.h", "lad_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte counts (one read of the mesh data, one write of g and H)
+# ---------------------------------------------------------------------------
+def compulsory_bytes_eval(nv, ns, nf, nnzb, es, inertia=True, faces=False, npairs=0):
+    b = 3 * nv * es                       # x
+    if inertia:
+        b += 3 * nv * es                  # x_tilde
+    b += ns * (es + 8)                    # rest length + two int32 endpoints
+    if faces:
+        b += nf * (12 + 5 * es)           # three int32 vertex ids, Dm^-1 (4), area
+    b += npairs * 8                       # pair endpoints
+    b += 3 * nv * es                      # g
+    b += 9 * nnzb * es                    # H values
+    return b
+
+
+def compulsory_bytes_hvp(nv, ns, nf, es, faces=False):
+    b = 3 * 3 * nv * es                   # x, v read; y written
+    b += ns * (es + 8)
+    if faces:
+        b += nf * (12 + 5 * es)
+    return b
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_autodiff_mesh_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+class Timer:
+    """HIP events on torch's current stream, which is the stream every lad_*
+    call is enqueued on (the binding passes it explicitly)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup, flush=None):
+        t = self.torch
+        for _ in range(warmup):
+            fn()
+        t.cuda.synchronize()
+        starts = [t.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [t.cuda.Event(enable_timing=True) for _ in range(steps)]
+        total0 = t.cuda.Event(enable_timing=True)
+        total1 = t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        total0.record()
+        for i in range(steps):
+            if flush is not None:
+                flush()
+            starts[i].record()
+            fn()
+            ends[i].record()
+        total1.record()
+        t.cuda.synchronize()
+        per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+        return {
+            "mean_ms": sum(per) / len(per),
+            "median_ms": per[len(per) // 2],
+            "min_ms": per[0],
+            "region_ms": total0.elapsed_time(total1),
+        }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def cloth_ctx(binding, mesh, dtype, pair_capacity=0, dhat=0.0, kappa=0.0):
+    return binding.Lad(mesh.nv, dtype=dtype,
+                       **binding.mesh_terms(mesh, pair_capacity=pair_capacity,
+                                            kappa=kappa, dhat=dhat))
+
+
+def to_dev(torch, a, dtype):
+    import numpy as np
+    t = torch.float64 if dtype == "f64" else torch.float32
+    return torch.tensor(np.ascontiguousarray(a), dtype=t, device="cuda")
+
+
+def bench_headline(torch, binding, inputs, args, timer):
+    m = inputs.cloth(args.n)
+    L = binding.Lad(m.nv, dtype="f32", patch_lds_bytes=args.patch_lds,
+                    **binding.mesh_terms(m))
+    info = L.get_info()
+    x = to_dev(torch, m.x, "f32")
+    E, g, H = L.alloc_outputs()
+    out = (E, g, H)
+    fn = lambda: L.eval(x, out=out)  # noqa: E731
+    flush = None
+    if args.flush_mall:
+        scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        flush = lambda: scratch.fill_(1.0)  # noqa: E731
+    r = timer.run(fn, args.steps, args.warmup, flush=flush)
+    nv, ns = m.nv, m.springs.shape[0]
+    nnzb = info["nnzb_base"]
+    terms = ns + nv
+    bc = compulsory_bytes_eval(nv, ns, 0, nnzb, 4)
+    torch.cuda.synchronize()
+    energy = E.item()
+    res = {
+        "mesh": m, "info": info, "timing": r, "terms": terms, "bytes": bc,
+        "energy": energy, "nnzb": nnzb, "ns": ns, "nv": nv,
+    }
+    L.close()
+    return res
+
+
+def bench_secondary(torch, binding, inputs, args, timer):
+    import numpy as np
+    sec = {}
+    steps = max(10, min(args.steps, 50))
+    warm = 5
+    # 100 x 100 cloth, fp32 and fp64
+    m = inputs.cloth(100)
+    for dt in ("f32", "f64"):
+        L = cloth_ctx(binding, m, dt)
+        x = to_dev(torch, m.x, dt)
+        out = L.alloc_outputs()
+        r = timer.run(lambda: L.eval(x, out=out), steps, warm)
+        sec[f"cloth100_{dt}_eval_ms"] = round(r["median_ms"], 5)
+        L.close()
+    # 512 x 512 symmetric-Dirichlet face grid, fp32: explicit eval and HVP
+    f = inputs.face_grid(512)
+    L = binding.Lad(f.nv, dtype="f32",
+                    **binding.mesh_terms(f, springs=False, inertia=False, faces=True))
+    info = L.get_info()
+    x = to_dev(torch, f.x, "f32")
+    v = to_dev(torch, inputs.hvp_direction(f.nv), "f32")
+    out = L.alloc_outputs()
+    r = timer.run(lambda: L.eval(x, out=out), steps, warm)
+    nf = f.faces.shape[0]
+    bc = compulsory_bytes_eval(f.nv, 0, nf, info["nnzb_base"], 4, inertia=False, faces=True)
+    sec["faces512_eval_ms"] = round(r["median_ms"], 5)
+    sec["faces512_eval_Mfaces_per_s"] = round(nf / (r["median_ms"] * 1e-3) / 1e6, 2)
+    sec["faces512_eval_GBps"] = round(bc / (r["median_ms"] * 1e-3) / 1e9, 1)
+    y = torch.empty_like(v)
+    r = timer.run(lambda: L.hvp(x, v, out=y), steps, warm)
+    bh = compulsory_bytes_hvp(f.nv, 0, nf, 4, faces=True)
+    sec["faces512_hvp_ms"] = round(r["median_ms"], 5)
+    sec["faces512_hvp_GBps"] = round(bh / (r["median_ms"] * 1e-3) / 1e9, 1)
+    L.close()
+    # 1000 x 1000 cloth + 2 % contact pairs per step, fp32: insert + eval
+    m = inputs.cloth(args.n)
+    dhat = 0.5 * m.h
+    P = int(round(0.02 * m.nv))
+    L = cloth_ctx(binding, m, "f32", pair_capacity=P, dhat=dhat, kappa=inputs.BARRIER_KAPPA)
+    sets = []
+    for step in range(3):
+        pairs, xs = inputs.contact_pairs(m, m.x, step=step)
+        sets.append((torch.tensor(pairs, dtype=torch.int32, device="cuda"),
+                     to_dev(torch, xs, "f32")))
+    out = L.alloc_outputs()
+    state = {"i": 0}
+
+    def step_fn():
+        p, xx = sets[state["i"] % len(sets)]
+        state["i"] += 1
+        L.insert_pairs(p)
+        L.eval(xx, out=out)
+
+    r = timer.run(step_fn, steps, warm)
+    sec["cloth1000_pairs_insert_eval_ms"] = round(r["median_ms"], 5)
+    ri = timer.run(lambda: L.insert_pairs(sets[0][0]), steps, warm)
+    sec["cloth1000_pairs_insert_ms"] = round(ri["median_ms"], 5)
+    if L.device_status() != 0:
+        raise RuntimeError("pair insertion reported a device-side error")
+    L.close()
+    sec["pairs_per_step"] = P
+    return sec
+
+
+def cpu_baseline(inputs, res):
+    """The fp64 oracle, single-threaded, on the same 1000 x 1000 cloth (inputs
+    rounded to fp32 as the GPU sees them): one evaluation, the pattern built
+    beforehand and not timed."""
+    import oracle
+    m = res["mesh"]
+    prob = oracle.problem_from_mesh(m, f32=True)
+    t0 = time.perf_counter()
+    rp, ci = oracle.pattern(prob)
+    t_pat = time.perf_counter() - t0
+    x = inputs.round_f32(m.x)
+    t0 = time.perf_counter()
+    E, _, _ = oracle.evaluate(prob, rp, ci, x)
+    t_eval = time.perf_counter() - t0
+    rel_e = abs(E - res["energy"]) / abs(E)
+    return {
+        "value": round(res["terms"] / t_eval / 1e6, 4),
+        "unit": "Melem/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one full evaluation of the {m.n}x{m.n} cloth "
+                   f"({res['terms']} terms), fp64, single thread; "
+                   f"pattern build {t_pat:.2f} s untimed"),
+        "ms_per_eval": round(t_eval * 1e3, 1),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "energy_rel_diff_vs_gpu": float(f"{rel_e:.3e}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--n", type=int, default=1000, help="cloth grid side (vertices)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="write a 512 MB scratch buffer before every timed call")
+    ap.add_argument("--patch-lds", type=int, default=0,
+                    help="LDS bytes per patch (0 = library default)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a device-to-device copy of 256 MiB five times "
+                         "(reference kernel for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the multi-GPU sharding is a design, not an implementation)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        nbytes = 256 * 1024 * 1024
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": nbytes,
+                          "calibrate_copy_bytes_written": nbytes, "launches": 5}))
+        return 0
+    from sparse_autodiff_mesh_amd import binding, inputs
+    binding.lib()  # fails loudly if liblad.so is missing
+
+    timer = Timer(torch)
+    log(f"bench: cloth {args.n}x{args.n} fp32, steps={args.steps} warmup={args.warmup}")
+    res = bench_headline(torch, binding, inputs, args, timer)
+    t = res["timing"]
+    ms = t["region_ms"] / args.steps
+    kern_ms = t["mean_ms"]
+    melem = res["terms"] / (ms * 1e-3) / 1e6
+    achieved = res["bytes"] / (kern_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+    line = {
+        "metric": "grad+Hessian ms/eval & Melem/s on 1000² cloth (1 GPU); "
+                  "achieved HBM GB/s vs peak",
+        "value": round(melem, 3),
+        "unit": "Melem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"mass-spring cloth {args.n}x{args.n} vertices, fp32, "
+                        "springs k=1e3 + inertia m/dt^2=100, gradient + block-CSR Hessian",
+            "vertices": res["nv"], "springs": res["ns"], "terms": res["terms"],
+            "nnzb": res["nnzb"], "patches": res["info"]["npatches"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "k_eval_patch<float,false>",
+            "kernel_ms_mean": round(kern_ms, 5),
+            "kernel_ms_median": round(t["median_ms"], 5),
+            "algorithmic_bytes": res["bytes"],
+            "flush_mall": bool(args.flush_mall),
+        },
+        "springs_per_s_M": round(res["ns"] / (ms * 1e-3) / 1e6, 2),
+        "energy": res["energy"],
+    }
+    if not args.no_secondary:
+        log("bench: secondary workloads")
+        line["secondary"] = bench_secondary(torch, binding, inputs, args, timer)
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(inputs, res)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

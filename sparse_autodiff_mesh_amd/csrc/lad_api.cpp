@@ -45,6 +45,7 @@ struct lad_ctx {
     void *d_xt = nullptr;
     DevState *d_state = nullptr;
     double *d_epart = nullptr;
+    unsigned *d_counter = nullptr;   // last-workgroup counter, zero between launches
     PatternBufs pat{};
     InsertBufs ins{};
     std::string err;
@@ -199,15 +200,20 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
                         hipStream_t s)
 {
     const PatchArgs<T> a = patch_args<T>(ctx);
-    hipError_t e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g),
-                                  static_cast<T *>(hv), ctx->d_epart, ctx->det, ctx->lds_eval, s);
-    if (e == hipSuccess && ctx->pair_blocks > 0)
+    // The last kernel of the call sums every partial energy into *energy.
+    const int32_t nparts = ctx->npatch + ctx->pair_blocks;
+    const bool pairs = ctx->pair_blocks > 0;
+    EnergySink es{ctx->d_epart, 0, nparts, ctx->d_counter, pairs ? nullptr : energy};
+    hipError_t e = hipSuccess;
+    if (ctx->npatch > 0)
+        e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g),
+                           static_cast<T *>(hv), es, ctx->det, ctx->lds_eval, s);
+    if (e == hipSuccess && pairs) {
+        EnergySink ep{ctx->d_epart, ctx->npatch, nparts, ctx->d_counter, energy};
         e = launch_pairs_eval<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
-                                 static_cast<T *>(g), static_cast<T *>(hv),
-                                 ctx->d_epart + ctx->npatch, ctx->pair_blocks, T(ctx->kappa),
-                                 T(ctx->dhat), s);
-    if (e == hipSuccess)
-        e = launch_energy_reduce(ctx->d_epart, ctx->npatch + ctx->pair_blocks, energy, s);
+                                 static_cast<T *>(g), static_cast<T *>(hv), ep, ctx->pair_blocks,
+                                 T(ctx->kappa), T(ctx->dhat), s);
+    }
     return e;
 }
 
@@ -380,6 +386,8 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         ctx->pair_blocks = int32_t((cap2 + kThreads - 1) / kThreads);
     }
     if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_epart, size_t(ctx->npatch + ctx->pair_blocks));
+    if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_counter, 1);
+    if (e == hipSuccess) e = hipMemsetAsync(ctx->d_counter, 0, sizeof(unsigned), s);
     if (e == hipSuccess && (ctx->lds_eval > 64 * 1024 || ctx->lds_hvp > 64 * 1024))
         e = raise_lds_limits();
     if (e == hipSuccess) e = hipStreamSynchronize(s);

@@ -72,6 +72,35 @@ __device__ __forceinline__ double block_sum(double v, double *red)
     return s;
 }
 
+// Store this workgroup's partial energy; the last workgroup of the launch to
+// get here sums all partials in index order and re-arms the counter.  The
+// release fence before the counter increment and the acquire fence after it
+// order the partial stores across workgroups (and across the XCDs' L2s).
+__device__ __forceinline__ void finish_energy(const EnergySink &es, double part, double *red)
+{
+    __shared__ int last;
+    if (threadIdx.x == 0) {
+        es.parts[es.part0 + blockIdx.x] = part;
+        last = 0;
+        if (es.out) {
+            __threadfence();
+            const unsigned prev = atomicAdd(es.counter, 1u);
+            last = prev == gridDim.x - 1;
+        }
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    double s = 0.0;
+    for (int i = threadIdx.x; i < es.n; i += kThreads)
+        s += __hip_atomic_load(es.parts + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const double tot = block_sum(s, red);
+    if (threadIdx.x == 0) {
+        *es.out = tot;
+        __hip_atomic_store(es.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <typename T>
 struct Vec;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -207,7 +236,7 @@ __device__ __forceinline__ void face_eval(const FaceRec rec, const T *dm, T area
 template <typename T, bool DET>
 __global__ void __launch_bounds__(kThreads)
 k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
-             double *__restrict__ epart)
+             EnergySink esink)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int V = Vec<T>::n;
@@ -332,8 +361,7 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
     }
     stream_out(g + int64_t(h.v0) * 3, gs, h.nown * 3, gpad);
 
-    const double es = block_sum(eacc, red);
-    if (tid == 0) epart[p] = es;
+    finish_energy(esink, block_sum(eacc, red), red);
 }
 
 // ---------------------------------------------------------------------------
@@ -480,7 +508,7 @@ template <typename T, bool HVP>
 __global__ void __launch_bounds__(kThreads)
 k_pairs(const DevState *__restrict__ st, PatternBufs pat, const T *__restrict__ x,
         const T *__restrict__ v, T *__restrict__ out_vec, T *__restrict__ hv,
-        double *__restrict__ epart, T kappa, T dhat)
+        EnergySink esink, T kappa, T dhat)
 {
     __shared__ double red[kWaves];
     const int act = st->active;
@@ -548,36 +576,22 @@ k_pairs(const DevState *__restrict__ st, PatternBufs pat, const T *__restrict__ 
             for (int c = 0; c < 3; ++c) out_vec[int64_t(a) * 3 + c] += ga[c];
         }
     }
-    if constexpr (!HVP) {
-        const double es = block_sum(eacc, red);
-        if (threadIdx.x == 0) epart[blockIdx.x] = es;
-    }
-}
-
-// Sum of n partial energies in a fixed order (one workgroup).
-__global__ void __launch_bounds__(kThreads)
-k_energy_reduce(const double *__restrict__ part, int n, double *__restrict__ out)
-{
-    __shared__ double red[kWaves];
-    double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += kThreads) s += part[i];
-    const double tot = block_sum(s, red);
-    if (threadIdx.x == 0) *out = tot;
+    if constexpr (!HVP) finish_energy(esink, block_sum(eacc, red), red);
 }
 
 }  // namespace
 
 template <typename T>
-hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hv, double *epart, int det,
+hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hv, EnergySink es, int det,
                        int lds_bytes, hipStream_t s)
 {
     if (a.npatch == 0) return hipSuccess;
     if (det)
         hipLaunchKernelGGL((k_eval_patch<T, true>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
-                           a, x, g, hv, epart);
+                           a, x, g, hv, es);
     else
         hipLaunchKernelGGL((k_eval_patch<T, false>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
-                           a, x, g, hv, epart);
+                           a, x, g, hv, es);
     return hipGetLastError();
 }
 
@@ -597,11 +611,11 @@ hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y, int d
 
 template <typename T>
 hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x, T *g, T *hv,
-                             double *epart, int nblocks, T kappa, T dhat, hipStream_t s)
+                             EnergySink es, int nblocks, T kappa, T dhat, hipStream_t s)
 {
     if (nblocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((k_pairs<T, false>), dim3(nblocks), dim3(kThreads), 0, s, st, pat, x,
-                       (const T *)nullptr, g, hv, epart, kappa, dhat);
+                       (const T *)nullptr, g, hv, es, kappa, dhat);
     return hipGetLastError();
 }
 
@@ -611,13 +625,7 @@ hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x, con
 {
     if (nblocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((k_pairs<T, true>), dim3(nblocks), dim3(kThreads), 0, s, st, pat, x, v, y,
-                       (T *)nullptr, (double *)nullptr, kappa, dhat);
-    return hipGetLastError();
-}
-
-hipError_t launch_energy_reduce(const double *epart, int n, double *out, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_energy_reduce, dim3(1), dim3(kThreads), 0, s, epart, n, out);
+                       (T *)nullptr, EnergySink{}, kappa, dhat);
     return hipGetLastError();
 }
 
@@ -643,12 +651,12 @@ static hipError_t raise_lds_limit()
 hipError_t raise_lds_limits() { return raise_lds_limit<float>() == hipSuccess ? raise_lds_limit<double>() : hipErrorUnknown; }
 
 #define LAD_INST(T)                                                                                \
-    template hipError_t launch_eval<T>(const PatchArgs<T> &, const T *, T *, T *, double *, int,   \
+    template hipError_t launch_eval<T>(const PatchArgs<T> &, const T *, T *, T *, EnergySink, int, \
                                        int, hipStream_t);                                          \
     template hipError_t launch_hvp<T>(const PatchArgs<T> &, const T *, const T *, T *, int, int,   \
                                       hipStream_t);                                                \
     template hipError_t launch_pairs_eval<T>(const DevState *, PatternBufs, const T *, T *, T *,   \
-                                             double *, int, T, T, hipStream_t);                    \
+                                             EnergySink, int, T, T, hipStream_t);                  \
     template hipError_t launch_pairs_hvp<T>(const DevState *, PatternBufs, const T *, const T *,   \
                                             T *, int, T, T, hipStream_t);
 LAD_INST(float)

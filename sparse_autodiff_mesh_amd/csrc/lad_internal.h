@@ -135,23 +135,33 @@ struct PatchArgs {
     PatternBufs pat;
 };
 
+// Where a launch puts the energy.  Every workgroup stores its partial sum at
+// parts[part0 + blockIdx.x]; when `out` is non-null the workgroup that
+// finishes last sums parts[0 .. n) in index order (fixed order, independent
+// of scheduling), writes *out and re-arms *counter (zero between launches).
+struct EnergySink {
+    double *parts;
+    int32_t part0;
+    int32_t n;
+    unsigned *counter;
+    double *out;
+};
+
 template <typename T>
 hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hvals,
-                       double *epart, int det, int lds_bytes, hipStream_t s);
+                       EnergySink es, int det, int lds_bytes, hipStream_t s);
 template <typename T>
 hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y,
                       int det, int lds_bytes, hipStream_t s);
 template <typename T>
 hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x,
-                             T *g, T *hvals, double *epart, int nblocks,
+                             T *g, T *hvals, EnergySink es, int nblocks,
                              T kappa, T dhat, hipStream_t s);
 template <typename T>
 hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x,
                             const T *v, T *y, int nblocks, T kappa, T dhat,
                             hipStream_t s);
 hipError_t raise_lds_limits();
-hipError_t launch_energy_reduce(const double *epart, int n, double *out,
-                                hipStream_t s);
 
 // Exclusive scan: out[0..n] with out[n] = total.  tmp needs
 // scan_tmp_size(n) int32 entries.
