@@ -349,7 +349,9 @@ def main():
             "workload": f"mass-spring cloth {args.n}x{args.n} vertices, fp32, "
                         "springs k=1e3 + inertia m/dt^2=100, gradient + block-CSR Hessian",
             "vertices": res["nv"], "springs": res["ns"], "terms": res["terms"],
-            "nnzb": res["nnzb"], "patches": res["info"]["npatches"],
+            "nnzb": res["nnzb"], "chunks_or_patches": res["info"]["npatches"],
+            "eval_path": {1: "patch", 2: "rows"}.get(res["info"]["eval_path"], "?"),
+            "workgroups": res["info"]["grid_eval"],
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -359,7 +361,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "k_eval_patch<float,false>",
+            "kernel": ("k_eval_rows<float>" if res["info"]["eval_path"] == 2
+                       else "k_eval_patch<float,false>"),
             "kernel_ms_mean": round(kern_ms, 5),
             "kernel_ms_median": round(t["median_ms"], 5),
             "algorithmic_bytes": res["bytes"],

@@ -97,7 +97,22 @@ typedef struct {
 
     double kappa;               /* pair barrier stiffness                      */
     double dhat;                /* pair barrier support, > 0 if pair_capacity>0 */
+
+    int32_t eval_path;          /* LAD_PATH_AUTO, LAD_PATH_PATCH or LAD_PATH_ROWS */
 } lad_mesh_desc;
+
+/* Parallel decomposition of the evaluation and HVP kernels.
+ *  LAD_PATH_PATCH  element owner: one workgroup per patch of contiguous rows;
+ *                  every element touching an owned row is evaluated once per
+ *                  such patch and scattered into the patch's rows, which are
+ *                  accumulated in LDS and streamed out.  Any mix of terms.
+ *  LAD_PATH_ROWS   row owner: one lane per block row evaluates every spring,
+ *                  inertia and pair term of that row; each block is written
+ *                  once, in a fixed order, without atomics.  Requires no face
+ *                  term, rest lengths >= 0 and at most one spring per vertex
+ *                  pair.
+ *  LAD_PATH_AUTO   LAD_PATH_ROWS when its requirements hold, else PATCH.  */
+enum { LAD_PATH_AUTO = 0, LAD_PATH_PATCH = 1, LAD_PATH_ROWS = 2 };
 
 /* Summary of a context (lad_get_info synchronises the context's stream to
  * read the device-side active pattern size). */
@@ -108,13 +123,15 @@ typedef struct {
     int64_t nnzb_active;        /* blocks of the active pattern (base + pairs) */
     int64_t hvals_capacity;     /* blocks an hvals buffer must hold            */
     int32_t npairs_active;
-    int32_t npatches;
+    int32_t npatches;           /* patches, or row chunks on the row path      */
     int32_t lds_bytes_eval;     /* dynamic LDS of the eval kernel per workgroup */
     int32_t lds_bytes_hvp;
     int64_t spring_records;     /* element records incl. patch-boundary copies */
     int64_t face_records;
     int32_t max_colors;         /* colour phases of the deterministic mode     */
     int32_t active_buffer;      /* 0 = topology pattern, 1/2 = pair buffers    */
+    int32_t eval_path;          /* LAD_PATH_PATCH or LAD_PATH_ROWS in use      */
+    int32_t grid_eval;          /* workgroups of one evaluation launch         */
 } lad_info;
 
 /*

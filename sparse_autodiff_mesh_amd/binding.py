@@ -25,6 +25,10 @@ LAD_ERR_STATE = -5
 LAD_ERR_PAIRS = -6
 LAD_F32 = 0
 LAD_F64 = 1
+LAD_PATH_AUTO = 0
+LAD_PATH_PATCH = 1
+LAD_PATH_ROWS = 2
+_PATHS = {"auto": LAD_PATH_AUTO, "patch": LAD_PATH_PATCH, "rows": LAD_PATH_ROWS}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _f64p = ctypes.POINTER(ctypes.c_double)
@@ -47,6 +51,7 @@ class lad_mesh_desc(ctypes.Structure):
         ("inertia", ctypes.c_int32), ("c", ctypes.c_double), ("x_tilde", _f64p),
         ("face_energy", ctypes.c_int32), ("dm_inv", _f64p), ("area", _f64p),
         ("kappa", ctypes.c_double), ("dhat", ctypes.c_double),
+        ("eval_path", ctypes.c_int32),
     ]
 
 
@@ -58,7 +63,8 @@ class lad_info(ctypes.Structure):
         ("npatches", ctypes.c_int32), ("lds_bytes_eval", ctypes.c_int32),
         ("lds_bytes_hvp", ctypes.c_int32), ("spring_records", ctypes.c_int64),
         ("face_records", ctypes.c_int64), ("max_colors", ctypes.c_int32),
-        ("active_buffer", ctypes.c_int32),
+        ("active_buffer", ctypes.c_int32), ("eval_path", ctypes.c_int32),
+        ("grid_eval", ctypes.c_int32),
     ]
 
 
@@ -184,7 +190,7 @@ def _ptr(a, t):
 
 def make_desc(nv, faces=None, springs=None, rest_len=None, k=0.0, x_tilde=None, c=0.0,
               face_energy=False, dm_inv=None, area=None, pair_capacity=0, kappa=0.0,
-              dhat=0.0, dtype="f32", deterministic=False, patch_lds_bytes=0):
+              dhat=0.0, dtype="f32", deterministic=False, patch_lds_bytes=0, path="auto"):
     """Fill a lad_mesh_desc from numpy arrays.  Returns (desc, keepalive)."""
     keep = {
         "faces": _i32(faces if faces is not None else np.zeros((0, 3))),
@@ -214,6 +220,7 @@ def make_desc(nv, faces=None, springs=None, rest_len=None, k=0.0, x_tilde=None, 
     d.area = _ptr(keep["area"], _f64p)
     d.kappa = float(kappa)
     d.dhat = float(dhat)
+    d.eval_path = _PATHS[path] if isinstance(path, str) else int(path)
     return d, keep
 
 

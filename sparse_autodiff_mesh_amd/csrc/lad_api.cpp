@@ -12,9 +12,7 @@
 
 #include "lad_internal.h"
 
-namespace lad {
-hipError_t raise_lds_limits();
-}
+#include <algorithm>
 
 using namespace lad;
 
@@ -31,6 +29,9 @@ struct lad_ctx {
     int32_t npatch = 0, lds_eval = 0, lds_hvp = 0, max_colors = 0;
     int64_t nspr_rec = 0, nfac_rec = 0;
     int32_t pair_blocks = 0;
+    int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
+    int32_t grid_eval = 0, grid_hvp = 0;
+    void *d_slot_rest = nullptr;
 
     std::vector<void *> allocs;
     PatchHdr *d_hdr = nullptr;
@@ -92,8 +93,11 @@ std::string check_desc(const lad_mesh_desc *d)
     if (d->nf < 0 || d->ns < 0) return "nf and ns must be >= 0";
     if (d->dtype != LAD_F32 && d->dtype != LAD_F64) return "dtype must be LAD_F32 or LAD_F64";
     if (d->pair_capacity < 0) return "pair_capacity must be >= 0";
-    if (d->patch_lds_bytes < 0 || d->patch_lds_bytes > 160 * 1024)
-        return "patch_lds_bytes must be in [0, 163840]";
+    if (d->eval_path != LAD_PATH_AUTO && d->eval_path != LAD_PATH_PATCH &&
+        d->eval_path != LAD_PATH_ROWS)
+        return "eval_path must be LAD_PATH_AUTO, LAD_PATH_PATCH or LAD_PATH_ROWS";
+    if (d->patch_lds_bytes < 0 || d->patch_lds_bytes > kMaxPatchLds)
+        return "patch_lds_bytes must be in [0, " + std::to_string(kMaxPatchLds) + "]";
     if (d->nf > 0 && !d->faces) return "faces is NULL";
     for (int64_t f = 0; f < d->nf; ++f) {
         const int32_t *t = d->faces + 3 * f;
@@ -144,7 +148,8 @@ hipError_t upload(lad_ctx *ctx, T **dst, const std::vector<T> &src, hipStream_t 
 }
 
 template <typename T>
-lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &plan, hipStream_t s)
+lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &plan,
+                            const RowPlan &rplan, hipStream_t s)
 {
     std::vector<T> rest(plan.spr_src.size());
     for (size_t i = 0; i < rest.size(); ++i) rest[i] = T(d->rest_len[plan.spr_src[i]]);
@@ -164,6 +169,10 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
     if (e == hipSuccess && d->inertia) {
         e = upload(ctx, &p, narrow<T>(d->x_tilde, size_t(d->nv) * 3), s);
         ctx->d_xt = p;
+    }
+    if (e == hipSuccess && ctx->row_mode) {
+        e = upload(ctx, &p, narrow<T>(rplan.slot_rest.data(), rplan.slot_rest.size()), s);
+        ctx->d_slot_rest = p;
     }
     // lifetime of the host vectors: synchronise before they go out of scope
     if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -196,9 +205,38 @@ PatchArgs<T> patch_args(const lad_ctx *ctx)
 }
 
 template <typename T>
+RowArgs<T> row_args(const lad_ctx *ctx)
+{
+    RowArgs<T> a{};
+    a.chunk = ctx->d_hdr;
+    a.nchunk = ctx->npatch;
+    a.rp0 = ctx->pat.rp[0];
+    a.ci0 = ctx->pat.ci[0];
+    a.slot_rest = static_cast<const T *>(ctx->d_slot_rest);
+    a.x_tilde = static_cast<const T *>(ctx->d_xt);
+    a.k = T(ctx->k);
+    a.c = T(ctx->c);
+    a.kappa = T(ctx->kappa);
+    a.dhat = T(ctx->dhat);
+    a.springs_on = ctx->springs_on;
+    a.inertia_on = ctx->inertia_on;
+    a.lds_blocks = kRowLdsBlocks;
+    a.state = ctx->d_state;
+    a.pat = ctx->pat;
+    return a;
+}
+
+template <typename T>
 hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, void *hv,
                         hipStream_t s)
 {
+    if (ctx->row_mode) {
+        // one launch: springs, inertia and pairs, energy summed by the last workgroup
+        EnergySink es{ctx->d_epart, 0, ctx->grid_eval, ctx->d_counter, energy};
+        return launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
+                                   static_cast<T *>(g), static_cast<T *>(hv), es,
+                                   ctx->grid_eval, s);
+    }
     const PatchArgs<T> a = patch_args<T>(ctx);
     // The last kernel of the call sums every partial energy into *energy.
     const int32_t nparts = ctx->npatch + ctx->pair_blocks;
@@ -220,6 +258,10 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
 template <typename T>
 hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s)
 {
+    if (ctx->row_mode)
+        return launch_hvp_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
+                                  static_cast<const T *>(v), static_cast<T *>(y), ctx->grid_hvp,
+                                  s);
     const PatchArgs<T> a = patch_args<T>(ctx);
     hipError_t e = launch_hvp<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
                                  static_cast<T *>(y), ctx->det, ctx->lds_hvp, s);
@@ -323,16 +365,30 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     in.row_ptr = h_rp.data();
     in.col_idx = h_ci.data();
     in.elem_size = ctx->es;
-    in.lds_budget = d->patch_lds_bytes > 0 ? d->patch_lds_bytes : 40 * 1024;
+    in.lds_budget = d->patch_lds_bytes > 0 ? d->patch_lds_bytes : kDefaultPatchLds;
     Plan plan;
-    std::string msg = build_plan(in, plan);
-    if (!msg.empty()) return fail(ctx, LAD_ERR_ARG, "patcher: " + msg);
+    RowPlan rplan;
+    std::string why = "patch path requested";
+    if (d->eval_path != LAD_PATH_PATCH) why = build_row_plan(in, d->rest_len, rplan);
+    if (d->eval_path == LAD_PATH_ROWS && !why.empty())
+        return fail(ctx, LAD_ERR_ARG, "row path not applicable: " + why);
+    ctx->row_mode = why.empty() ? 1 : 0;
+    if (ctx->row_mode) {
+        plan.hdr = rplan.chunk;
+        ctx->lds_eval = ctx->es == 8 ? rows_lds_bytes<double>(kRowLdsBlocks)
+                                     : rows_lds_bytes<float>(kRowLdsBlocks);
+        ctx->lds_hvp = 0;
+        ctx->nspr_rec = d->ns;
+    } else {
+        std::string msg = build_plan(in, plan);
+        if (!msg.empty()) return fail(ctx, LAD_ERR_ARG, "patcher: " + msg);
+        ctx->lds_eval = plan.lds_eval;
+        ctx->lds_hvp = plan.lds_hvp;
+        ctx->max_colors = plan.max_colors;
+        ctx->nspr_rec = int64_t(plan.spr.size());
+        ctx->nfac_rec = int64_t(plan.fac.size());
+    }
     ctx->npatch = int32_t(plan.hdr.size());
-    ctx->lds_eval = plan.lds_eval;
-    ctx->lds_hvp = plan.lds_hvp;
-    ctx->max_colors = plan.max_colors;
-    ctx->nspr_rec = int64_t(plan.spr.size());
-    ctx->nfac_rec = int64_t(plan.fac.size());
 
     e = upload(ctx, &ctx->d_hdr, plan.hdr, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_rib, plan.rib, s);
@@ -341,9 +397,18 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (e == hipSuccess) e = upload(ctx, &ctx->d_col_bounds, plan.col_bounds, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_diag_rel, plan.diag_rel, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "upload of patch tables");
-    lad_status st = ctx->dtype == LAD_F64 ? upload_constants<double>(ctx, d, plan, s)
-                                          : upload_constants<float>(ctx, d, plan, s);
+    lad_status st = ctx->dtype == LAD_F64 ? upload_constants<double>(ctx, d, plan, rplan, s)
+                                          : upload_constants<float>(ctx, d, plan, rplan, s);
     if (st != LAD_OK) return st;
+    if (ctx->row_mode) {
+        e = ctx->dtype == LAD_F64
+                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, &ctx->grid_eval, &ctx->grid_hvp)
+                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, &ctx->grid_eval, &ctx->grid_hvp);
+        if (e != hipSuccess) return hip_fail(ctx, e, "occupancy query");
+    } else {
+        ctx->grid_eval = ctx->npatch;
+        ctx->grid_hvp = ctx->npatch;
+    }
 
     // ---- pattern buffers, device state, scratch
     std::memset(&ctx->pat, 0, sizeof(ctx->pat));
@@ -383,13 +448,15 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             ctx->pat.pinc[b] = ctx->ins.pinc[b];
             ctx->pat.pinc_row[b] = ctx->ins.pinc_row[b];
         }
-        ctx->pair_blocks = int32_t((cap2 + kThreads - 1) / kThreads);
+        ctx->pair_blocks = ctx->row_mode ? 0 : int32_t((cap2 + kThreads - 1) / kThreads);
     }
-    if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_epart, size_t(ctx->npatch + ctx->pair_blocks));
+    if (e == hipSuccess)
+        e = dev_alloc(ctx, &ctx->d_epart,
+                      size_t(std::max(ctx->npatch, ctx->grid_eval) + ctx->pair_blocks));
     if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_counter, 1);
     if (e == hipSuccess) e = hipMemsetAsync(ctx->d_counter, 0, sizeof(unsigned), s);
-    if (e == hipSuccess && (ctx->lds_eval > 64 * 1024 || ctx->lds_hvp > 64 * 1024))
-        e = raise_lds_limits();
+    if (e == hipSuccess && !ctx->row_mode && (ctx->lds_eval > 64 * 1024 || ctx->lds_hvp > 64 * 1024))
+        e = raise_lds_limits(std::max(ctx->lds_eval, ctx->lds_hvp));
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(ctx, e, "allocation of pattern buffers");
     return LAD_OK;
@@ -441,6 +508,8 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     info->face_records = ctx->nfac_rec;
     info->max_colors = ctx->max_colors;
     info->active_buffer = hs.active;
+    info->eval_path = ctx->row_mode ? LAD_PATH_ROWS : LAD_PATH_PATCH;
+    info->grid_eval = ctx->grid_eval;
     return LAD_OK;
 }
 

@@ -18,6 +18,7 @@
 // updated atomically; the only HBM writes are the final values.
 #include "dual2.h"
 #include "energies.h"
+#include "lad_device.h"
 #include "lad_internal.h"
 
 namespace lad {
@@ -25,18 +26,6 @@ namespace lad {
 namespace {
 
 constexpr int kWaves = kThreads / 64;
-
-__device__ __forceinline__ int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
-
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Give every XCD a contiguous run of patches so neighbouring patches,
-// which share ribbon vertices, meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int b, int n)
-{
-    const int q = n >> 3, r = n & 7;
-    const int x = b & 7, i = b >> 3;
-    return x * q + min(x, r) + i;
-}
 
 template <bool ATOMIC, typename T>
 __device__ __forceinline__ void lds_add(T *p, T v)
@@ -55,82 +44,6 @@ __device__ __forceinline__ void add_block3(T *B, const Dual2<T, 3> &e, T s)
     for (int r = 0; r < 3; ++r)
 #pragma unroll
         for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(B + 3 * r + c, s * e.hess(r, c));
-}
-
-// Sum of `v` over the workgroup, in a fixed order; valid in thread 0.
-__device__ __forceinline__ double block_sum(double v, double *red)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    double s = 0.0;
-    if (threadIdx.x == 0)
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) s += red[i];
-    return s;
-}
-
-// Store this workgroup's partial energy; the last workgroup of the launch to
-// get here sums all partials in index order and re-arms the counter.  The
-// release fence before the counter increment and the acquire fence after it
-// order the partial stores across workgroups (and across the XCDs' L2s).
-__device__ __forceinline__ void finish_energy(const EnergySink &es, double part, double *red)
-{
-    __shared__ int last;
-    if (threadIdx.x == 0) {
-        es.parts[es.part0 + blockIdx.x] = part;
-        last = 0;
-        if (es.out) {
-            __threadfence();
-            const unsigned prev = atomicAdd(es.counter, 1u);
-            last = prev == gridDim.x - 1;
-        }
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    double s = 0.0;
-    for (int i = threadIdx.x; i < es.n; i += kThreads)
-        s += __hip_atomic_load(es.parts + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const double tot = block_sum(s, red);
-    if (threadIdx.x == 0) {
-        *es.out = tot;
-        __hip_atomic_store(es.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
-template <typename T>
-struct Vec;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef double f64x2 __attribute__((ext_vector_type(2)));
-template <>
-struct Vec<float> {
-    using type = f32x4;
-    static constexpr int n = 4;
-};
-template <>
-struct Vec<double> {
-    using type = f64x2;
-    static constexpr int n = 2;
-};
-
-// Copy n elements from LDS src to global dst.  The caller placed src so that
-// (src - 16B-aligned base) == (dst mod 16 bytes), hence the body moves in
-// aligned 16-byte vectors.
-template <typename T>
-__device__ __forceinline__ void stream_out(T *__restrict__ dst, const T *src, int n, int pad)
-{
-    constexpr int V = Vec<T>::n;
-    using VT = typename Vec<T>::type;
-    const int head = min(n, (V - pad) % V);
-    for (int i = threadIdx.x; i < head; i += kThreads) dst[i] = src[i];
-    const int nvec = (n - head) / V;
-    VT *dv = reinterpret_cast<VT *>(dst + head);
-    const VT *sv = reinterpret_cast<const VT *>(src + head);
-    for (int i = threadIdx.x; i < nvec; i += kThreads) __builtin_nontemporal_store(sv[i], dv + i);
-    for (int i = head + nvec * V + threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -253,15 +166,15 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
     const int nloc = h.nown + h.nrib;
     int64_t off = 0;
     T *Hbase = reinterpret_cast<T *>(smem + off);
-    off += align16((int64_t(h.nblk) * 9 + 4) * sizeof(T));
+    off += dalign16((int64_t(h.nblk) * 9 + 4) * sizeof(T));
     T *gbase = reinterpret_cast<T *>(smem + off);
-    off += align16((int64_t(h.nown) * 3 + 4) * sizeof(T));
+    off += dalign16((int64_t(h.nown) * 3 + 4) * sizeof(T));
     T *xs = reinterpret_cast<T *>(smem + off);
-    off += align16(int64_t(nloc) * 3 * sizeof(T));
+    off += dalign16(int64_t(nloc) * 3 * sizeof(T));
     uint16_t *dtab = reinterpret_cast<uint16_t *>(smem + off);
-    off += align16(int64_t(h.nown) * 2);
+    off += dalign16(int64_t(h.nown) * 2);
     uint16_t *amap = reinterpret_cast<uint16_t *>(smem + off);
-    off += align16(int64_t(h.amap_cap) * 2);
+    off += dalign16(int64_t(h.amap_cap) * 2);
     double *red = reinterpret_cast<double *>(smem + off);
 
     const int hpad = mapped ? 0 : int((int64_t(ra0) * 9) % V);
@@ -337,7 +250,7 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
     // 5. write the owned slice of the active pattern's value array
     T *dst = hv + int64_t(ra0) * 9;
     if (!mapped) {
-        stream_out(dst, H, h.nblk * 9, hpad);
+        stream_out<kThreads>(dst, H, h.nblk * 9, hpad);
     } else if (nact <= h.amap_cap) {
         // pairs inserted blocks into these rows: map every active block to
         // its base block (or to zero for an inserted one)
@@ -359,9 +272,9 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
             dst[i] = (m == kNone) ? T(0) : H[9 * m + c];
         }
     }
-    stream_out(g + int64_t(h.v0) * 3, gs, h.nown * 3, gpad);
+    stream_out<kThreads>(g + int64_t(h.v0) * 3, gs, h.nown * 3, gpad);
 
-    finish_energy(esink, block_sum(eacc, red), red);
+    finish_energy<kThreads>(esink, block_sum<kThreads>(eacc, red), red);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,9 +291,9 @@ k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T 
     const int nloc = h.nown + h.nrib;
     int64_t off = 0;
     T *xs = reinterpret_cast<T *>(smem + off);
-    off += align16(int64_t(nloc) * 3 * sizeof(T));
+    off += dalign16(int64_t(nloc) * 3 * sizeof(T));
     T *vs = reinterpret_cast<T *>(smem + off);
-    off += align16(int64_t(nloc) * 3 * sizeof(T));
+    off += dalign16(int64_t(nloc) * 3 * sizeof(T));
     T *ys = reinterpret_cast<T *>(smem + off);
 
     const T *xo = x + int64_t(h.v0) * 3;
@@ -576,7 +489,7 @@ k_pairs(const DevState *__restrict__ st, PatternBufs pat, const T *__restrict__ 
             for (int c = 0; c < 3; ++c) out_vec[int64_t(a) * 3 + c] += ga[c];
         }
     }
-    if constexpr (!HVP) finish_energy(esink, block_sum(eacc, red), red);
+    if constexpr (!HVP) finish_energy<kThreads>(esink, block_sum<kThreads>(eacc, red), red);
 }
 
 }  // namespace
@@ -630,25 +543,23 @@ hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x, con
 }
 
 template <typename T>
-static hipError_t raise_lds_limit()
+static hipError_t raise_lds_limit(int bytes)
 {
-    hipError_t e = hipSuccess;
-    const int lim = 160 * 1024;
-    e = hipFuncSetAttribute((const void *)k_eval_patch<T, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lim);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)k_eval_patch<T, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lim);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)k_hvp_patch<T, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lim);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)k_hvp_patch<T, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lim);
-    return e;
+    const void *fns[] = {(const void *)k_eval_patch<T, false>, (const void *)k_eval_patch<T, true>,
+                         (const void *)k_hvp_patch<T, false>, (const void *)k_hvp_patch<T, true>};
+    for (const void *f : fns) {
+        const hipError_t e =
+            hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
-hipError_t raise_lds_limits() { return raise_lds_limit<float>() == hipSuccess ? raise_lds_limit<double>() : hipErrorUnknown; }
+hipError_t raise_lds_limits(int bytes)
+{
+    const hipError_t e = raise_lds_limit<float>(bytes);
+    return e == hipSuccess ? raise_lds_limit<double>(bytes) : e;
+}
 
 #define LAD_INST(T)                                                                                \
     template hipError_t launch_eval<T>(const PatchArgs<T> &, const T *, T *, T *, EnergySink, int, \

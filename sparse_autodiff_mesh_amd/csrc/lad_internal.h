@@ -17,6 +17,8 @@ constexpr int kThreads = 256;          // threads per workgroup, patch kernels
 constexpr uint16_t kNone = 0xFFFFu;    // "this row is not owned by the patch"
 constexpr int kMaxLocal = 65535;       // local vertex / block ids are uint16
 constexpr int kMaxColors = 256;        // colour phases per element kind
+constexpr int kDefaultPatchLds = 40 * 1024;   // patch LDS budget by default
+constexpr int kMaxPatchLds = 159 * 1024;      // leaves room for static LDS
 
 // One two-vertex element seen from one patch.  lab = la | lb << 16 are the
 // patch-local vertex ids (owned vertices first, then ribbon vertices);
@@ -103,6 +105,21 @@ int32_t amap_capacity(int nblk);
 // Returns "" on success, else an error message.
 std::string build_plan(const PlanInput &in, Plan &out);
 
+// Row chunks for the row-owner kernels: up to kRowsPerChunk consecutive rows
+// whose topology blocks fit kRowBaseBlocks; every chunk reserves
+// kRowLdsBlocks blocks of LDS staging (the slack takes pair insertions).
+constexpr int kRowLdsBlocks = 512;
+constexpr int kRowBaseBlocks = 456;
+
+struct RowPlan {
+    std::vector<PatchHdr> chunk;     // v0, nown (rows), blk0, nblk, amap_cap
+    std::vector<double> slot_rest;   // [nnzb] rest length behind each block, -1: none
+};
+
+// Returns "" when the row path applies (no face term, rest lengths >= 0, at
+// most one spring per vertex pair, rows short enough), else the reason.
+std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan &out);
+
 // ---------------------------------------------------------------------------
 // Kernel argument bundles and launchers (defined in the .hip files).
 // ---------------------------------------------------------------------------
@@ -153,6 +170,37 @@ hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hvals,
 template <typename T>
 hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y,
                       int det, int lds_bytes, hipStream_t s);
+
+// Row-owner kernels for two-vertex radial terms (springs, runtime pairs) and
+// vertex terms (inertia): one lane per block row, 64 rows per chunk.
+constexpr int kRowThreads = 64;
+constexpr int kRowsPerChunk = kRowThreads;
+
+template <typename T>
+struct RowArgs {
+    const PatchHdr *chunk;       // row chunks: v0, nown (rows), amap_cap (blocks)
+    int32_t nchunk;
+    const int32_t *rp0, *ci0;    // topology pattern
+    const T *slot_rest;          // [nnzb_base] rest length of the spring behind
+                                 // each block (< 0: no spring)
+    const T *x_tilde;            // null = no inertia
+    T k, c, kappa, dhat;
+    int32_t springs_on, inertia_on;
+    int32_t lds_blocks;          // staging capacity per workgroup, in blocks
+    const DevState *state;
+    PatternBufs pat;
+};
+
+template <typename T>
+int rows_lds_bytes(int lds_blocks);
+template <typename T>
+hipError_t rows_grid(int lds_blocks, int nchunk, int *grid_eval, int *grid_hvp);
+template <typename T>
+hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
+                            int grid, hipStream_t s);
+template <typename T>
+hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
+                           hipStream_t s);
 template <typename T>
 hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x,
                              T *g, T *hvals, EnergySink es, int nblocks,
@@ -161,7 +209,8 @@ template <typename T>
 hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x,
                             const T *v, T *y, int nblocks, T kappa, T dhat,
                             hipStream_t s);
-hipError_t raise_lds_limits();
+// Allow the patch kernels `bytes` of dynamic LDS (needed above 64 KiB).
+hipError_t raise_lds_limits(int bytes);
 
 // Exclusive scan: out[0..n] with out[n] = total.  tmp needs
 // scan_tmp_size(n) int32 entries.

@@ -322,4 +322,46 @@ std::string build_plan(const PlanInput &in, Plan &out)
     return "";
 }
 
+std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan &out)
+{
+    const int32_t nv = in.nv;
+    const int32_t *rp = in.row_ptr, *ci = in.col_idx;
+    out = RowPlan();
+    if (in.face_energy) return "a face term is present";
+    const int64_t nnzb = rp[nv];
+    out.slot_rest.assign(size_t(nnzb), -1.0);
+    for (int64_t s = 0; s < in.ns; ++s) {
+        const int32_t a = in.springs[2 * s], b = in.springs[2 * s + 1];
+        const double L = rest_len[s];
+        if (!(L >= 0.0)) return "a spring has a negative rest length";
+        const int32_t pab = find_pos(rp, ci, a, b), pba = find_pos(rp, ci, b, a);
+        if (pab < 0 || pba < 0) return "spring block missing from pattern";
+        double &sab = out.slot_rest[size_t(rp[a] + pab)];
+        double &sba = out.slot_rest[size_t(rp[b] + pba)];
+        if (sab >= 0.0 || sba >= 0.0) return "two springs join the same vertex pair";
+        sab = L;
+        sba = L;
+    }
+    for (int32_t v0 = 0; v0 < nv;) {
+        int32_t n = 0, blk = 0;
+        while (n < kRowsPerChunk && v0 + n < nv) {
+            const int32_t len = rp[v0 + n + 1] - rp[v0 + n];
+            if (blk + len > kRowBaseBlocks) break;
+            blk += len;
+            ++n;
+        }
+        if (n == 0) return "vertex " + std::to_string(v0) + " has a row too long for the row path";
+        PatchHdr h;
+        std::memset(&h, 0, sizeof(h));
+        h.v0 = v0;
+        h.nown = n;
+        h.blk0 = rp[v0];
+        h.nblk = blk;
+        h.amap_cap = kRowLdsBlocks;
+        out.chunk.push_back(h);
+        v0 += n;
+    }
+    return "";
+}
+
 }  // namespace lad

@@ -13,9 +13,9 @@ pytestmark = pytest.mark.gpu
 KAPPA = inputs.BARRIER_KAPPA
 
 
-def make(lad, m, dtype, cap, det=False, lds=0, faces=False):
+def make(lad, m, dtype, cap, det=False, lds=0, faces=False, path="auto"):
     dhat = 0.5 * m.h
-    L = lad.Lad(m.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds,
+    L = lad.Lad(m.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds, path=path,
                 **lad.mesh_terms(m, faces=faces, pair_capacity=cap, kappa=KAPPA, dhat=dhat))
     return L, dhat
 
@@ -44,13 +44,17 @@ def check_step(lad, L, m, dtype, pairs, x, dhat, faces=False):
     return prob, orp, oci, x_h
 
 
-@pytest.mark.parametrize("n,dtype,det,lds", [(24, "f64", False, 0), (40, "f32", False, 6144),
-                                             (40, "f64", True, 6144), (100, "f32", False, 0)])
-def test_insert_and_eval_steps(lad, n, dtype, det, lds):
-    log_case(test="pairs_steps", n=n, dtype=dtype, det=det, lds=lds)
+@pytest.mark.parametrize("n,dtype,det,lds,path", [
+    (24, "f64", False, 0, "patch"), (40, "f32", False, 6144, "patch"),
+    (40, "f64", True, 6144, "patch"), (100, "f32", False, 0, "patch"),
+    (24, "f64", False, 0, "rows"), (40, "f32", False, 0, "rows"), (100, "f32", False, 0, "rows"),
+    (100, "f64", False, 0, "rows"),
+])
+def test_insert_and_eval_steps(lad, n, dtype, det, lds, path):
+    log_case(test="pairs_steps", n=n, dtype=dtype, det=det, lds=lds, path=path)
     m = inputs.cloth(n)
     P = int(round(0.02 * m.nv))
-    L, dhat = make(lad, m, dtype, P, det, lds)
+    L, dhat = make(lad, m, dtype, P, det, lds, path=path)
     for step in range(4):
         pairs, x = inputs.contact_pairs(m, m.x, step=step)
         L.insert_pairs(pairs_dev(pairs))
@@ -66,12 +70,13 @@ def test_insert_and_eval_steps(lad, n, dtype, det, lds):
     L.close()
 
 
-def test_duplicate_adjacent_and_shared_pairs(lad):
+@pytest.mark.parametrize("path", ["patch", "rows"])
+def test_duplicate_adjacent_and_shared_pairs(lad, path):
     """Pairs that repeat, reverse, hit an existing edge, or share a vertex:
     the pattern is still the sorted union and every pair is evaluated."""
-    log_case(test="pairs_irregular")
+    log_case(test="pairs_irregular", path=path)
     m = inputs.cloth(15)
-    L, dhat = make(lad, m, "f64", 16, lds=6144)
+    L, dhat = make(lad, m, "f64", 16, lds=6144, path=path)
     rng = np.random.default_rng(5)
     x = m.x.copy()
     pairs = np.array([[3, 100], [100, 3], [3, 100], [0, 1], [0, 16], [50, 51], [50, 140],
@@ -112,11 +117,12 @@ def test_pairs_with_faces_and_hvp(lad):
     L.close()
 
 
-def test_bad_pairs_keep_previous_pattern(lad):
-    log_case(test="pairs_bad")
+@pytest.mark.parametrize("path", ["patch", "rows"])
+def test_bad_pairs_keep_previous_pattern(lad, path):
+    log_case(test="pairs_bad", path=path)
     m = inputs.cloth(20)
     P = 8
-    L, dhat = make(lad, m, "f64", P)
+    L, dhat = make(lad, m, "f64", P, path=path)
     good, x = inputs.contact_pairs(m, m.x, step=1, frac=P / m.nv)
     L.insert_pairs(pairs_dev(good))
     assert L.device_status() == 0
@@ -135,4 +141,28 @@ def test_bad_pairs_keep_previous_pattern(lad):
         L.insert_pairs(pairs_dev(np.zeros((P + 1, 2), np.int32)))
     assert ei.value.status == lad.LAD_ERR_CAPACITY
     check_step(lad, L, m, "f64", good, x, dhat)
+    L.close()
+
+
+def test_pairs_rows_eval_and_hvp(lad):
+    """Row path with springs, inertia and pairs: eval and HVP.  Each pair
+    joins vertices two grid steps apart with a barrier support of 3h, so the
+    pairs are active without moving any vertex."""
+    import torch
+    log_case(test="pairs_rows_hvp")
+    m = inputs.cloth(30)
+    n = m.n
+    src = np.arange(0, m.nv, 37)
+    src = src[(src % n) < n - 2]
+    pairs = np.stack([src, src + 2], axis=1).astype(np.int32)
+    dhat = 3.0 * m.h
+    L = lad.Lad(m.nv, dtype="f64", path="rows",
+                **lad.mesh_terms(m, pair_capacity=len(pairs), kappa=KAPPA, dhat=dhat))
+    L.insert_pairs(pairs_dev(pairs))
+    prob, orp, oci, x_h = check_step(lad, L, m, "f64", pairs, m.x, dhat)
+    v = inputs.hvp_direction(m.nv)
+    y = L.hvp(dev(x_h, "f64"), dev(v, "f64"))
+    torch.cuda.synchronize()
+    yo = oracle.hvp(prob, orp, oci, x_h, v)
+    assert rel(y.cpu().numpy(), yo) <= TOL["f64"]
     L.close()

@@ -12,9 +12,10 @@ from gpu_util import TOL, dev, host_input, log_case, rel
 pytestmark = pytest.mark.gpu
 
 
-def run_eval(lad, mesh, dtype, det=False, lds=0, springs=True, inertia=True, faces=False):
+def run_eval(lad, mesh, dtype, det=False, lds=0, springs=True, inertia=True, faces=False,
+             path="auto"):
     import torch
-    L = lad.Lad(mesh.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds,
+    L = lad.Lad(mesh.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds, path=path,
                 **lad.mesh_terms(mesh, springs=springs, inertia=inertia, faces=faces))
     prob = oracle.problem_from_mesh(mesh, springs=springs, inertia=inertia, faces=faces,
                                     f32=(dtype == "f32"))
@@ -44,15 +45,58 @@ def check_against_oracle(prob, x_h, res, dtype):
     (37, "f32", False, 6144), (37, "f64", True, 6144), (37, "f32", True, 6144),
     (100, "f32", False, 0), (100, "f64", False, 0), (100, "f32", True, 0),
 ])
-def test_cloth_eval(lad, n, dtype, det, lds):
-    log_case(test="cloth_eval", n=n, dtype=dtype, det=det, lds=lds)
+def test_cloth_eval_patch(lad, n, dtype, det, lds):
+    log_case(test="cloth_eval_patch", n=n, dtype=dtype, det=det, lds=lds)
     m = inputs.cloth(n)
-    L, prob, x_h, res = run_eval(lad, m, dtype, det, lds)
+    L, prob, x_h, res = run_eval(lad, m, dtype, det, lds, path="patch")
     info = L.get_info()
+    assert info["eval_path"] == lad.LAD_PATH_PATCH
     if lds:
         assert info["npatches"] > 4  # several patches and ribbons
     check_against_oracle(prob, x_h, res, dtype)
     L.close()
+
+
+@pytest.mark.parametrize("n,dtype", [(2, "f64"), (3, "f64"), (10, "f64"), (10, "f32"),
+                                     (37, "f32"), (37, "f64"), (100, "f32"), (100, "f64"),
+                                     (129, "f32")])
+def test_cloth_eval_rows(lad, n, dtype):
+    """Row-owner path (the default for cloth).  Sizes span one partial chunk
+    (n = 2, 3), several chunks with a ragged tail, and chunks that straddle
+    grid rows."""
+    log_case(test="cloth_eval_rows", n=n, dtype=dtype)
+    m = inputs.cloth(n)
+    L, prob, x_h, res = run_eval(lad, m, dtype)
+    info = L.get_info()
+    assert info["eval_path"] == lad.LAD_PATH_ROWS
+    check_against_oracle(prob, x_h, res, dtype)
+    L.close()
+
+
+def test_rows_bitwise_reproducible(lad):
+    """The row path writes every value once in a fixed order: repeated
+    evaluations are bitwise identical."""
+    import torch
+    log_case(test="rows_reproducible")
+    m = inputs.cloth(64)
+    L = lad.Lad(m.nv, dtype="f32", **lad.mesh_terms(m))
+    x = dev(host_input(m.x, "f32"), "f32")
+    E0, g0, H0 = L.eval(x)
+    for _ in range(5):
+        E, g, H = L.eval(x)
+        torch.cuda.synchronize()
+        assert torch.equal(E, E0) and torch.equal(g, g0) and torch.equal(H, H0)
+    L.close()
+
+
+def test_springs_only_and_inertia_only_rows(lad):
+    log_case(test="rows_single_terms")
+    m = inputs.cloth(20)
+    for springs, inertia in ((True, False), (False, True)):
+        L, prob, x_h, res = run_eval(lad, m, "f64", springs=springs, inertia=inertia)
+        assert L.get_info()["eval_path"] == lad.LAD_PATH_ROWS
+        check_against_oracle(prob, x_h, res, "f64")
+        L.close()
 
 
 @pytest.mark.parametrize("n,dtype,det,lds", [
@@ -78,15 +122,16 @@ def test_all_terms_eval(lad, dtype, det):
     L.close()
 
 
-@pytest.mark.parametrize("n,dtype,det,faces,lds", [
-    (20, "f64", False, True, 0), (45, "f32", False, True, 8192), (45, "f64", True, False, 8192),
-    (64, "f32", True, True, 0),
+@pytest.mark.parametrize("n,dtype,det,faces,lds,path", [
+    (20, "f64", False, True, 0, "auto"), (45, "f32", False, True, 8192, "auto"),
+    (45, "f64", True, False, 8192, "patch"), (64, "f32", True, True, 0, "auto"),
+    (45, "f64", False, False, 0, "rows"), (100, "f32", False, False, 0, "rows"),
 ])
-def test_hvp(lad, n, dtype, det, faces, lds):
+def test_hvp(lad, n, dtype, det, faces, lds, path):
     import torch
-    log_case(test="hvp", n=n, dtype=dtype, det=det, faces=faces, lds=lds)
+    log_case(test="hvp", n=n, dtype=dtype, det=det, faces=faces, lds=lds, path=path)
     m = inputs.cloth(n)
-    L = lad.Lad(m.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds,
+    L = lad.Lad(m.nv, dtype=dtype, deterministic=det, patch_lds_bytes=lds, path=path,
                 **lad.mesh_terms(m, faces=faces))
     prob = oracle.problem_from_mesh(m, faces=faces, f32=(dtype == "f32"))
     x_h = host_input(m.x, dtype)
