@@ -177,13 +177,18 @@ lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
  * key design 1 (per-element forward mode; global traffic is one read of the
  * mesh and one write of the derivatives).
  *   d_x      device [nv][3] dtype, read only.
- *   d_energy device double, overwritten with F(x).
+ *   d_energy device double, overwritten with F(x); or NULL, in which case the
+ *            energy is not summed (one small kernel launch is saved: the
+ *            evaluation itself is then a single launch on springs/inertia/
+ *            pair meshes).
  *   d_grad   device [nv][3] dtype, fully overwritten.
  *   d_hvals  device [hvals_capacity][3][3] dtype; the first nnzb_active
  *            blocks are fully overwritten in the active pattern's order.
  *   hvals_capacity_blocks must be >= lad_info.hvals_capacity.
  * Asynchronous on `hip_stream`; no host synchronisation.  Outputs must not
- * alias inputs.  Errors: LAD_ERR_ARG (null pointer, capacity too small).
+ * alias inputs.  Calls on one context must be ordered (one stream, or
+ * streams synchronised by the caller): they share per-context scratch.
+ * Errors: LAD_ERR_ARG (null x, grad or hvals; capacity too small).
  */
 lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x,
                                      double *d_energy, void *d_grad,

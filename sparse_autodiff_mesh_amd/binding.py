@@ -261,13 +261,14 @@ class Lad:
         H = t.empty((self.capacity, 3, 3), dtype=self.dtype, device=self.device)
         return E, g, H
 
-    def eval(self, x, out=None):
+    def eval(self, x, out=None, energy=True):
         """(energy[1] fp64, g (nv,3), hvals (capacity,3,3)); the first
-        nnzb_active blocks of hvals are valid."""
+        nnzb_active blocks of hvals are valid.  With energy=False the energy
+        is not computed (NULL is passed) and E is left untouched."""
         assert x.dtype == self.dtype and x.is_cuda and x.is_contiguous()
         E, g, H = out if out is not None else self.alloc_outputs()
-        lad_eval_energy_grad_hess(self.ctx, x.data_ptr(), E.data_ptr(), g.data_ptr(),
-                                  H.data_ptr(), H.shape[0], _stream())
+        lad_eval_energy_grad_hess(self.ctx, x.data_ptr(), E.data_ptr() if energy else None,
+                                  g.data_ptr(), H.data_ptr(), H.shape[0], _stream())
         return E, g, H
 
     def hvp(self, x, v, out=None):

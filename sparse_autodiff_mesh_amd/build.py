@@ -27,8 +27,13 @@ CXX_SOURCES = ["lad_api.cpp", "lad_patch.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-result"]
+# Device code: no packed-FP32 instructions; finite math without signed
+# zeros, so the compiler may fold the structural zeros of the dual-number
+# seeds (x * 0 -> 0, x + 0 -> x).  Neither flag reassociates or changes
+# rounding.
 DEVICE = [f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-ffinite-math-only", "-fno-signed-zeros"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -46,7 +46,6 @@ struct lad_ctx {
     void *d_xt = nullptr;
     DevState *d_state = nullptr;
     double *d_epart = nullptr;
-    unsigned *d_counter = nullptr;   // last-workgroup counter, zero between launches
     PatternBufs pat{};
     InsertBufs ins{};
     std::string err;
@@ -230,28 +229,28 @@ template <typename T>
 hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, void *hv,
                         hipStream_t s)
 {
-    if (ctx->row_mode) {
-        // one launch: springs, inertia and pairs, energy summed by the last workgroup
-        EnergySink es{ctx->d_epart, 0, ctx->grid_eval, ctx->d_counter, energy};
-        return launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
-                                   static_cast<T *>(g), static_cast<T *>(hv), es,
-                                   ctx->grid_eval, s);
-    }
-    const PatchArgs<T> a = patch_args<T>(ctx);
-    // The last kernel of the call sums every partial energy into *energy.
-    const int32_t nparts = ctx->npatch + ctx->pair_blocks;
-    const bool pairs = ctx->pair_blocks > 0;
-    EnergySink es{ctx->d_epart, 0, nparts, ctx->d_counter, pairs ? nullptr : energy};
+    // Partial energies go to d_epart; one small launch sums them when the
+    // caller asked for the energy.
     hipError_t e = hipSuccess;
-    if (ctx->npatch > 0)
-        e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g),
-                           static_cast<T *>(hv), es, ctx->det, ctx->lds_eval, s);
-    if (e == hipSuccess && pairs) {
-        EnergySink ep{ctx->d_epart, ctx->npatch, nparts, ctx->d_counter, energy};
-        e = launch_pairs_eval<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
-                                 static_cast<T *>(g), static_cast<T *>(hv), ep, ctx->pair_blocks,
-                                 T(ctx->kappa), T(ctx->dhat), s);
+    int32_t nparts = 0;
+    if (ctx->row_mode) {
+        // one launch: springs, inertia and pairs of every row
+        e = launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x), static_cast<T *>(g),
+                                static_cast<T *>(hv), EnergySink{ctx->d_epart, 0}, ctx->grid_eval,
+                                s);
+        nparts = ctx->grid_eval;
+    } else {
+        const PatchArgs<T> a = patch_args<T>(ctx);
+        e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g), static_cast<T *>(hv),
+                           EnergySink{ctx->d_epart, 0}, ctx->det, ctx->lds_eval, s);
+        if (e == hipSuccess && ctx->pair_blocks > 0)
+            e = launch_pairs_eval<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
+                                     static_cast<T *>(g), static_cast<T *>(hv),
+                                     EnergySink{ctx->d_epart, ctx->npatch}, ctx->pair_blocks,
+                                     T(ctx->kappa), T(ctx->dhat), s);
+        nparts = ctx->npatch + ctx->pair_blocks;
     }
+    if (e == hipSuccess && energy) e = launch_energy_reduce(ctx->d_epart, nparts, energy, s);
     return e;
 }
 
@@ -453,8 +452,6 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (e == hipSuccess)
         e = dev_alloc(ctx, &ctx->d_epart,
                       size_t(std::max(ctx->npatch, ctx->grid_eval) + ctx->pair_blocks));
-    if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_counter, 1);
-    if (e == hipSuccess) e = hipMemsetAsync(ctx->d_counter, 0, sizeof(unsigned), s);
     if (e == hipSuccess && !ctx->row_mode && (ctx->lds_eval > 64 * 1024 || ctx->lds_hvp > 64 * 1024))
         e = raise_lds_limits(std::max(ctx->lds_eval, ctx->lds_hvp));
     if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -552,7 +549,7 @@ lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x, double *d_en
                                      int64_t hvals_capacity_blocks, void *hip_stream)
 {
     if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
-    if (!d_x || !d_energy || !d_grad || !d_hvals) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    if (!d_x || !d_grad || !d_hvals) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
     if (hvals_capacity_blocks < ctx->hcap)
         return fail(ctx, LAD_ERR_ARG, "hvals capacity below " + std::to_string(ctx->hcap) + " blocks");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);

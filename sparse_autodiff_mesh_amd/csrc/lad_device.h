@@ -1,5 +1,5 @@
 // lad_device.h -- device helpers shared by the evaluation kernels: fixed-order
-// workgroup reductions, the last-workgroup energy sum, XCD-aware workgroup
+// workgroup reductions, per-workgroup partial energies, XCD-aware workgroup
 // numbering and the LDS -> HBM streaming store.  Not part of the public ABI.
 #pragma once
 
@@ -44,35 +44,14 @@ __device__ __forceinline__ double block_sum(double v, double *red)
     }
 }
 
-// Store this workgroup's partial energy (thread 0's `part`); the workgroup
-// that finishes last sums all partials in index order, writes *es.out and
-// re-arms the counter.  The release fence before the counter increment and
-// the acquire fence after it order the partial stores across workgroups and
-// across the XCDs' L2 caches.
-template <int NT>
-__device__ __forceinline__ void finish_energy(const EnergySink &es, double part, double *red)
+// Store this workgroup's partial energy (thread 0's `part`).  The partials
+// are summed by k_energy_reduce, a separate launch on the same stream, so no
+// workgroup waits on another and no device-wide fence is needed: on a GPU
+// whose XCDs each have their own L2, an agent-scope release fence writes the
+// whole L2 back, which costs far more than a second launch.
+__device__ __forceinline__ void store_energy(const EnergySink &es, double part)
 {
-    __shared__ int last;
-    if (threadIdx.x == 0) {
-        es.parts[es.part0 + blockIdx.x] = part;
-        last = 0;
-        if (es.out) {
-            __threadfence();
-            const unsigned prev = atomicAdd(es.counter, 1u);
-            last = prev == gridDim.x - 1;
-        }
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    double s = 0.0;
-    for (int i = threadIdx.x; i < es.n; i += NT)
-        s += __hip_atomic_load(es.parts + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const double tot = block_sum<NT>(s, red);
-    if (threadIdx.x == 0) {
-        *es.out = tot;
-        __hip_atomic_store(es.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (threadIdx.x == 0) es.parts[es.part0 + blockIdx.x] = part;
 }
 
 template <typename T>

@@ -274,7 +274,7 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
     }
     stream_out<kThreads>(g + int64_t(h.v0) * 3, gs, h.nown * 3, gpad);
 
-    finish_energy<kThreads>(esink, block_sum<kThreads>(eacc, red), red);
+    store_energy(esink, block_sum<kThreads>(eacc, red));
 }
 
 // ---------------------------------------------------------------------------
@@ -489,10 +489,27 @@ k_pairs(const DevState *__restrict__ st, PatternBufs pat, const T *__restrict__ 
             for (int c = 0; c < 3; ++c) out_vec[int64_t(a) * 3 + c] += ga[c];
         }
     }
-    if constexpr (!HVP) finish_energy<kThreads>(esink, block_sum<kThreads>(eacc, red), red);
+    if constexpr (!HVP) store_energy(esink, block_sum<kThreads>(eacc, red));
+}
+
+// Sum of n partial energies in index order (one workgroup).
+__global__ void __launch_bounds__(kThreads)
+k_energy_reduce(const double *__restrict__ parts, int32_t n, double *__restrict__ out)
+{
+    __shared__ double red[kWaves];
+    double s = 0.0;
+    for (int32_t i = threadIdx.x; i < n; i += kThreads) s += parts[i];
+    const double tot = block_sum<kThreads>(s, red);
+    if (threadIdx.x == 0) *out = tot;
 }
 
 }  // namespace
+
+hipError_t launch_energy_reduce(const double *parts, int32_t n, double *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_energy_reduce, dim3(1), dim3(kThreads), 0, s, parts, n, out);
+    return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hv, EnergySink es, int det,

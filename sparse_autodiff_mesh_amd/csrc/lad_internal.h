@@ -152,17 +152,15 @@ struct PatchArgs {
     PatternBufs pat;
 };
 
-// Where a launch puts the energy.  Every workgroup stores its partial sum at
-// parts[part0 + blockIdx.x]; when `out` is non-null the workgroup that
-// finishes last sums parts[0 .. n) in index order (fixed order, independent
-// of scheduling), writes *out and re-arms *counter (zero between launches).
+// Where a launch puts its partial energies: workgroup b stores its sum at
+// parts[part0 + b].  launch_energy_reduce then sums parts[0 .. n) in index
+// order (fixed order, independent of scheduling).
 struct EnergySink {
     double *parts;
     int32_t part0;
-    int32_t n;
-    unsigned *counter;
-    double *out;
 };
+
+hipError_t launch_energy_reduce(const double *parts, int32_t n, double *out, hipStream_t s);
 
 template <typename T>
 hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hvals,

@@ -34,6 +34,20 @@ namespace lad {
 namespace {
 
 constexpr int kBatch = 8;  // slots whose loads a lane issues together
+static_assert(kRowThreads == 64, "one wave per workgroup: LDS hand-off needs no barrier");
+
+// LDS hand-off between the lanes of one wave.  A wave's LDS instructions
+// execute in issue order, so a read issued after another lane's write sees
+// it; the wavefront-scope fences only keep the compiler from moving memory
+// operations across this point.  Unlike a workgroup barrier this does not
+// wait for outstanding global loads and stores, so a chunk's HBM stores
+// drain while the next chunk is being computed.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // This workgroup's contiguous range [c0, c1) of the n chunks.
 __device__ __forceinline__ void chunk_range(int n, int &c0, int &c1)
@@ -41,11 +55,6 @@ __device__ __forceinline__ void chunk_range(int n, int &c0, int &c1)
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     c0 = int(int64_t(n) * w / gridDim.x);
     c1 = int(int64_t(n) * (w + 1) / gridDim.x);
-}
-
-__device__ __forceinline__ bool slot_inserted(const uint32_t *ib, int32_t s)
-{
-    return (ib[s >> 5] >> (s & 31)) & 1u;
 }
 
 // Position of column b in the sorted active row [lo, hi); the caller knows
@@ -64,35 +73,78 @@ template <typename T>
 struct Row {
     int32_t a, s0, s1, kb0;   // vertex, active slot range, first base slot
     T xa[3];
+    T xt[3];                  // inertial target (when the inertia term is on)
 };
 
-// Walk the slots of row r in batches of kBatch.  For every slot s, `fn(s,
-// kb, b, L)` gets the base-pattern index kb (-1 for a slot inserted by
-// pairs), the column b and the rest length L of the spring behind the block
-// (negative: no spring).  Loads of a batch are issued before any use.
-template <typename T, typename Fn>
-__device__ __forceinline__ void for_each_slot(const RowArgs<T> &A, const Row<T> &r, int act,
-                                              const uint32_t *ib, Fn &&fn)
+// Row header loads, all independent of each other.
+template <typename T>
+__device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, const int32_t *rpa, int32_t a,
+                                           const T *__restrict__ x)
 {
-    int32_t nins = 0;  // inserted slots seen so far in this row
-    for (int32_t base = r.s0; base < r.s1; base += kBatch) {
-        int32_t kb[kBatch], b[kBatch];
-        T L[kBatch];
+    Row<T> r;
+    r.a = a;
+    r.s0 = rpa[a];
+    r.s1 = rpa[a + 1];
+    r.kb0 = A.rp0[a];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        r.xa[k] = x[int64_t(a) * 3 + k];
+        r.xt[k] = A.inertia_on ? A.x_tilde[int64_t(a) * 3 + k] : T(0);
+    }
+    return r;
+}
+
+// Operands of up to kBatch consecutive slots of one row.  kb is the slot's
+// index in the topology pattern (-1 past the row end or for a block inserted
+// by pairs), b its column, L the rest length of the spring behind the block
+// (negative: none) and xb the column vertex's position.
+template <typename T>
+struct SlotBatch {
+    int32_t kb[kBatch], b[kBatch];
+    T L[kBatch];
+    T xb[kBatch][3];
+};
+
+// Load one batch starting at active slot `base`.  Every load uses an index
+// that is valid whatever the slot (the row's first topology slot, or the
+// row's own vertex), so all loads of the batch are issued back to back and
+// only the arithmetic that consumes them is predicated.  `nins` counts the
+// inserted slots of the row before `base` and is advanced past the batch.
+template <typename T>
+__device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r, int act,
+                                           const uint32_t *ib, int32_t base, int32_t &nins,
+                                           const T *__restrict__ x, SlotBatch<T> &q)
+{
+    uint32_t insw[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) insw[j] = 0u;
+    if (act != 0) {  // wave-uniform: pairs are active
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int32_t s = base + j;
-            const bool ins = act != 0 && s < r.s1 && slot_inserted(ib, s);
-            kb[j] = (s < r.s1 && !ins) ? r.kb0 + (s - r.s0) - nins : -1;
-            nins += ins ? 1 : 0;
+            const int32_t sl = min(base + j, r.s1 - 1);
+            insw[j] = ib[sl >> 5] >> (sl & 31);
         }
+    }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            b[j] = kb[j] >= 0 ? A.ci0[kb[j]] : -1;
-            L[j] = (kb[j] >= 0 && A.springs_on) ? A.slot_rest[kb[j]] : T(-1);
-        }
+    for (int j = 0; j < kBatch; ++j) {
+        const int32_t s = base + j;
+        const bool valid = s < r.s1;
+        const bool ins = valid && (insw[j] & 1u);
+        q.kb[j] = (valid && !ins) ? r.kb0 + (s - r.s0) - nins : -1;
+        nins += ins ? 1 : 0;
+    }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-            if (base + j < r.s1) fn(base + j, kb[j], b[j], L[j]);
+    for (int j = 0; j < kBatch; ++j) {
+        const int32_t kl = q.kb[j] >= 0 ? q.kb[j] : r.kb0;
+        q.b[j] = A.ci0[kl];
+        q.L[j] = A.slot_rest[kl];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) q.xb[j][c] = x[int64_t(bl) * 3 + c];
+        if (q.kb[j] < 0 || !A.springs_on) q.L[j] = T(-1);
     }
 }
 
@@ -110,40 +162,47 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     double E = 0.0;
     int32_t dslot = r.s0;
 
-    for_each_slot(A, r, act, ib, [&](int32_t s, int32_t kb, int32_t b, T L) {
-        T *B = Hs + 9 * (s - sb);
-        if (kb >= 0 && b == r.a) {
-            dslot = s;
-            return;
-        }
-        if (!(L >= T(0))) {  // inserted by a pair, or no spring behind the block
+    int32_t nins = 0;
+    for (int32_t base = r.s0; base < r.s1; base += kBatch) {
+        SlotBatch<T> q;
+        load_batch(A, r, act, ib, base, nins, x, q);
 #pragma unroll
-            for (int i = 0; i < 9; ++i) B[i] = T(0);
-            return;
-        }
-        Dual2<T, 3> d[3];
-#pragma unroll
-        for (int c = 0; c < 3; ++c)
-            d[c] = Dual2<T, 3>::var(r.xa[c] - x[int64_t(b) * 3 + c], c);
-        const Dual2<T, 3> e = spring_energy(d, L, A.k);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            G[i] += e.g[i];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const T h = e.hess(i, j);
-                B[3 * i + j] = -h;
-                D[3 * i + j] += h;
+        for (int j = 0; j < kBatch; ++j) {
+            const int32_t s = base + j;
+            if (s >= r.s1) break;
+            T *B = Hs + 9 * (s - sb);
+            if (q.kb[j] >= 0 && q.b[j] == r.a) {
+                dslot = s;
+                continue;
             }
+            if (!(q.L[j] >= T(0))) {  // inserted by a pair, or no spring behind the block
+#pragma unroll
+                for (int i = 0; i < 9; ++i) B[i] = T(0);
+                continue;
+            }
+            Dual2<T, 3> d[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(r.xa[c] - q.xb[j][c], c);
+            const Dual2<T, 3> e = spring_energy(d, q.L[j], A.k);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                G[i] += e.g[i];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    const T h = e.hess(i, k);
+                    B[3 * i + k] = -h;
+                    D[3 * i + k] += h;
+                }
+            }
+            if (r.a < q.b[j]) E += double(e.v);
         }
-        if (r.a < b) E += double(e.v);
-    });
+    }
 
     if (A.inertia_on) {
         Dual2<T, 3> z[3];
 #pragma unroll
         for (int c = 0; c < 3; ++c)
-            z[c] = Dual2<T, 3>::var(r.xa[c] - A.x_tilde[int64_t(r.a) * 3 + c], c);
+            z[c] = Dual2<T, 3>::var(r.xa[c] - r.xt[c], c);
         const Dual2<T, 3> e = inertia_energy(z, A.c);
         E += double(e.v);
 #pragma unroll
@@ -218,20 +277,14 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         const int pad = stage_pad<T>(int64_t(sb) * 9);
         T *Hs = stage + pad;
         if (fits && int(threadIdx.x) < nrows) {
-            Row<T> r;
-            r.a = v0 + threadIdx.x;
-            r.s0 = rpa[r.a];
-            r.s1 = rpa[r.a + 1];
-            r.kb0 = A.rp0[r.a];
-#pragma unroll
-            for (int k = 0; k < 3; ++k) r.xa[k] = x[int64_t(r.a) * 3 + k];
+            const Row<T> r = load_row(A, rpa, v0 + int32_t(threadIdx.x), x);
             eacc += eval_row(A, act, cia, ib, r, sb, Hs, x, g);
         }
-        __syncthreads();
+        wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
-        __syncthreads();
+        wave_lds_sync();
     }
-    finish_energy<kRowThreads>(esink, block_sum<kRowThreads>(eacc, nullptr), nullptr);
+    store_energy(esink, block_sum<kRowThreads>(eacc, nullptr));
 }
 
 // ---------------------------------------------------------------------------
@@ -250,17 +303,10 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     for (int c = c0; c < c1; ++c) {
         const int32_t v0 = A.chunk[c].v0, nrows = A.chunk[c].nown;
         if (int(threadIdx.x) >= nrows) continue;
-        Row<T> r;
-        r.a = v0 + threadIdx.x;
-        r.s0 = rpa[r.a];
-        r.s1 = rpa[r.a + 1];
-        r.kb0 = A.rp0[r.a];
+        const Row<T> r = load_row(A, rpa, v0 + int32_t(threadIdx.x), x);
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            r.xa[k] = x[int64_t(r.a) * 3 + k];
-            va[k] = v[int64_t(r.a) * 3 + k];
-        }
+        for (int k = 0; k < 3; ++k) va[k] = v[int64_t(r.a) * 3 + k];
         // K (v_a - v_b) for the two-vertex term with local Hessian K.
         auto add_kv = [&](const Dual2<T, 3> &e, int32_t b) {
             T dv[3];
@@ -270,14 +316,31 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             for (int i = 0; i < 3; ++i)
                 Y[i] += e.hess(i, 0) * dv[0] + e.hess(i, 1) * dv[1] + e.hess(i, 2) * dv[2];
         };
-        for_each_slot(A, r, act, ib, [&](int32_t, int32_t kb, int32_t b, T L) {
-            if (kb < 0 || b == r.a || !(L >= T(0))) return;
-            Dual2<T, 3> d[3];
+        int32_t nins = 0;
+        for (int32_t base = r.s0; base < r.s1; base += kBatch) {
+            SlotBatch<T> q;
+            load_batch(A, r, act, ib, base, nins, x, q);
+            T vb[kBatch][3];
 #pragma unroll
-            for (int k = 0; k < 3; ++k)
-                d[k] = Dual2<T, 3>::var(r.xa[k] - x[int64_t(b) * 3 + k], k);
-            add_kv(spring_energy(d, L, A.k), b);
-        });
+            for (int j = 0; j < kBatch; ++j) {
+                const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) vb[j][k] = v[int64_t(bl) * 3 + k];
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (base + j >= r.s1) break;
+                if (q.b[j] == r.a || !(q.L[j] >= T(0))) continue;
+                Dual2<T, 3> d[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) d[k] = Dual2<T, 3>::var(r.xa[k] - q.xb[j][k], k);
+                const Dual2<T, 3> e = spring_energy(d, q.L[j], A.k);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    Y[i] += e.hess(i, 0) * (va[0] - vb[j][0]) + e.hess(i, 1) * (va[1] - vb[j][1]) +
+                            e.hess(i, 2) * (va[2] - vb[j][2]);
+            }
+        }
         if (A.inertia_on) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) Y[k] += A.c * va[k];

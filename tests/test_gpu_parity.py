@@ -192,3 +192,26 @@ def test_outputs_fully_overwritten(lad):
     assert torch.equal(E1, E2) or abs(E1.item() - E2.item()) <= 1e-6 * abs(E1.item())
     assert torch.isfinite(g2).all() and torch.isfinite(H2[:n]).all()
     L.close()
+
+
+@pytest.mark.parametrize("path", ["rows", "patch"])
+def test_eval_without_energy(lad, path):
+    """d_energy = NULL skips the energy sum; gradient and Hessian are the
+    same as with it, and the energy buffer is left untouched.  (The patch
+    path runs in its deterministic mode so that two calls compare bitwise;
+    its default mode sums with LDS atomics in a varying order.)"""
+    import torch
+    log_case(test="no_energy", path=path)
+    m = inputs.cloth(33)
+    L = lad.Lad(m.nv, dtype="f64", path=path, deterministic=(path == "patch"),
+                **lad.mesh_terms(m))
+    x = dev(m.x, "f64")
+    E1, g1, H1 = L.eval(x)
+    E2, g2, H2 = L.alloc_outputs()
+    E2.fill_(-7.0)
+    L.eval(x, out=(E2, g2, H2), energy=False)
+    torch.cuda.synchronize()
+    n = L.get_info()["nnzb_active"]
+    assert E2.item() == -7.0
+    assert torch.equal(g1, g2) and torch.equal(H1[:n], H2[:n])
+    L.close()
