@@ -39,7 +39,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published peak
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_eval_cloth1000_f32.txt")
-KERNEL_SOURCES = ["lad_eval.hip", "dual2.h", "energies.h", "lad_internal.h"]
+KERNEL_SOURCES = ["lad_rows.hip", "lad_eval.hip", "lad_device.h", "dual2.h", "energies.h",
+                  "lad_internal.h"]
 
 
 def log(*a):
