@@ -32,6 +32,9 @@ struct lad_ctx {
     int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
+    int32_t *d_fptr = nullptr;
+    FaceInc *d_finc = nullptr;
+    void *d_face_dm = nullptr, *d_face_area = nullptr;
 
     std::vector<void *> allocs;
     PatchHdr *d_hdr = nullptr;
@@ -173,6 +176,14 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
         e = upload(ctx, &p, narrow<T>(rplan.slot_rest.data(), rplan.slot_rest.size()), s);
         ctx->d_slot_rest = p;
     }
+    if (e == hipSuccess && ctx->row_mode && ctx->faces_on) {
+        e = upload(ctx, &p, narrow<T>(d->dm_inv, size_t(d->nf) * 4), s);
+        ctx->d_face_dm = p;
+        if (e == hipSuccess) e = upload(ctx, &p, narrow<T>(d->area, size_t(d->nf)), s);
+        ctx->d_face_area = p;
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_fptr, rplan.fptr, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_finc, rplan.finc, s);
+    }
     // lifetime of the host vectors: synchronise before they go out of scope
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e == hipSuccess ? LAD_OK : hip_fail(ctx, e, "upload of element constants");
@@ -213,12 +224,17 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.ci0 = ctx->pat.ci[0];
     a.slot_rest = static_cast<const T *>(ctx->d_slot_rest);
     a.x_tilde = static_cast<const T *>(ctx->d_xt);
+    a.fptr = ctx->d_fptr;
+    a.finc = ctx->d_finc;
+    a.face_dm = static_cast<const T *>(ctx->d_face_dm);
+    a.face_area = static_cast<const T *>(ctx->d_face_area);
     a.k = T(ctx->k);
     a.c = T(ctx->c);
     a.kappa = T(ctx->kappa);
     a.dhat = T(ctx->dhat);
     a.springs_on = ctx->springs_on;
     a.inertia_on = ctx->inertia_on;
+    a.faces_on = ctx->faces_on;
     a.lds_blocks = kRowLdsBlocks;
     a.state = ctx->d_state;
     a.pat = ctx->pat;
@@ -378,6 +394,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
                                      : rows_lds_bytes<float>(kRowLdsBlocks);
         ctx->lds_hvp = 0;
         ctx->nspr_rec = d->ns;
+        ctx->nfac_rec = ctx->faces_on ? d->nf : 0;
     } else {
         std::string msg = build_plan(in, plan);
         if (!msg.empty()) return fail(ctx, LAD_ERR_ARG, "patcher: " + msg);
@@ -401,8 +418,10 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (st != LAD_OK) return st;
     if (ctx->row_mode) {
         e = ctx->dtype == LAD_F64
-                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, &ctx->grid_eval, &ctx->grid_hvp)
-                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, &ctx->grid_eval, &ctx->grid_hvp);
+                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, &ctx->grid_eval,
+                                    &ctx->grid_hvp)
+                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, &ctx->grid_eval,
+                                   &ctx->grid_hvp);
         if (e != hipSuccess) return hip_fail(ctx, e, "occupancy query");
     } else {
         ctx->grid_eval = ctx->npatch;

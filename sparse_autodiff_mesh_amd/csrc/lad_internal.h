@@ -111,13 +111,26 @@ std::string build_plan(const PlanInput &in, Plan &out);
 constexpr int kRowLdsBlocks = 512;
 constexpr int kRowBaseBlocks = 456;
 
+// One triangle seen from the row of one of its vertices (row-owner face
+// terms).  f is the face id; with i the row vertex's position in the face,
+// o1 and o2 are the face's vertices at positions (i+1)%3 and (i+2)%3; pk
+// packs i (bits 0-1) and, for face position k = 0, 1, 2, the offset of that
+// vertex's block within the row's topology pattern (bits 8k+8 .. 8k+15).
+struct alignas(16) FaceInc {
+    int32_t f, o1, o2;
+    uint32_t pk;
+};
+constexpr int kMaxRowFaceSlots = 256;   // slot offsets fit 8 bits
+
 struct RowPlan {
     std::vector<PatchHdr> chunk;     // v0, nown (rows), blk0, nblk, amap_cap
     std::vector<double> slot_rest;   // [nnzb] rest length behind each block, -1: none
+    std::vector<int32_t> fptr;       // [nv+1] face incidence offsets (face term on)
+    std::vector<FaceInc> finc;       // incident faces of each row, by face id
 };
 
-// Returns "" when the row path applies (no face term, rest lengths >= 0, at
-// most one spring per vertex pair, rows short enough), else the reason.
+// Returns "" when the row path applies (rest lengths >= 0, at most one
+// spring per vertex pair, rows short enough), else the reason.
 std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan &out);
 
 // ---------------------------------------------------------------------------
@@ -182,8 +195,12 @@ struct RowArgs {
     const T *slot_rest;          // [nnzb_base] rest length of the spring behind
                                  // each block (< 0: no spring)
     const T *x_tilde;            // null = no inertia
+    const int32_t *fptr;         // [nv+1] face incidence offsets (faces on)
+    const FaceInc *finc;         // incident faces of each row
+    const T *face_dm;            // [nf][4] row-major Dm^-1
+    const T *face_area;          // [nf]
     T k, c, kappa, dhat;
-    int32_t springs_on, inertia_on;
+    int32_t springs_on, inertia_on, faces_on;
     int32_t lds_blocks;          // staging capacity per workgroup, in blocks
     const DevState *state;
     PatternBufs pat;
@@ -192,7 +209,7 @@ struct RowArgs {
 template <typename T>
 int rows_lds_bytes(int lds_blocks);
 template <typename T>
-hipError_t rows_grid(int lds_blocks, int nchunk, int *grid_eval, int *grid_hvp);
+hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int *grid_eval, int *grid_hvp);
 template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s);

@@ -327,7 +327,6 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
     const int32_t nv = in.nv;
     const int32_t *rp = in.row_ptr, *ci = in.col_idx;
     out = RowPlan();
-    if (in.face_energy) return "a face term is present";
     const int64_t nnzb = rp[nv];
     out.slot_rest.assign(size_t(nnzb), -1.0);
     for (int64_t s = 0; s < in.ns; ++s) {
@@ -341,6 +340,33 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         if (sab >= 0.0 || sba >= 0.0) return "two springs join the same vertex pair";
         sab = L;
         sba = L;
+    }
+    if (in.face_energy && in.nf > 0) {
+        // per-row incidence, rows in vertex order, faces by id within a row
+        out.fptr.assign(size_t(nv) + 1, 0);
+        for (int64_t f = 0; f < in.nf; ++f)
+            for (int k = 0; k < 3; ++k) out.fptr[size_t(in.faces[3 * f + k]) + 1] += 1;
+        for (int32_t v = 0; v < nv; ++v) out.fptr[v + 1] += out.fptr[v];
+        out.finc.resize(size_t(out.fptr[nv]));
+        std::vector<int32_t> cur(out.fptr.begin(), out.fptr.end() - 1);
+        for (int64_t f = 0; f < in.nf; ++f) {
+            const int32_t *t = in.faces + 3 * f;
+            for (int i = 0; i < 3; ++i) {
+                const int32_t a = t[i];
+                FaceInc e;
+                e.f = int32_t(f);
+                e.o1 = t[(i + 1) % 3];
+                e.o2 = t[(i + 2) % 3];
+                e.pk = uint32_t(i);
+                for (int k = 0; k < 3; ++k) {
+                    const int32_t pos = find_pos(rp, ci, a, t[k]);
+                    if (pos < 0) return "face block missing from pattern";
+                    if (pos >= kMaxRowFaceSlots) return "a row is too long for the row path's face terms";
+                    e.pk |= uint32_t(pos) << (8 * k + 8);
+                }
+                out.finc[size_t(cur[a]++)] = e;
+            }
+        }
     }
     for (int32_t v0 = 0; v0 < nv;) {
         int32_t n = 0, blk = 0;

@@ -72,6 +72,7 @@ __device__ __forceinline__ int32_t find_slot(const int32_t *ci, int32_t lo, int3
 template <typename T>
 struct Row {
     int32_t a, s0, s1, kb0;   // vertex, active slot range, first base slot
+    int32_t f0, f1;           // incident-face range (when the face term is on)
     T xa[3];
     T xt[3];                  // inertial target (when the inertia term is on)
 };
@@ -86,6 +87,8 @@ __device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, const int32_t *r
     r.s0 = rpa[a];
     r.s1 = rpa[a + 1];
     r.kb0 = A.rp0[a];
+    r.f0 = A.faces_on ? A.fptr[a] : 0;
+    r.f1 = A.faces_on ? A.fptr[a + 1] : 0;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         r.xa[k] = x[int64_t(a) * 3 + k];
@@ -149,9 +152,96 @@ __device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r,
 }
 
 // ---------------------------------------------------------------------------
+// Face terms seen from one row.  The symmetric-Dirichlet energy is
+// differentiated in its natural variables F = [p1 - p0, p2 - p0] M
+// (M = Dm^-1, F stored row-major F[2s + c]), a constant linear image of the
+// face's vertex positions: dF[s][c] / dp_u[s] = w[u][c] with w1 = M row 0,
+// w2 = M row 1, w0 = -(w1 + w2).  Row vertex a at face position i then gets
+//   g_a[s]       += sum_c w[i][c] dE/dF[s][c]
+//   H_(a,u)[s][t] += sum_{c,c'} w[i][c] w[u][c'] d2E/dF[s][c] dF[t][c'].
+// ---------------------------------------------------------------------------
+constexpr int kFaceBatch = 4;  // incident faces whose loads a lane issues together
+
+template <typename T>
+struct FaceBatch {
+    FaceInc e[kFaceBatch];
+    T xo[kFaceBatch][2][3];    // positions of o1, o2
+    T m[kFaceBatch][4];        // Dm^-1
+    T area[kFaceBatch];
+};
+
+// Loads of the incident faces [base, base + kFaceBatch) of row r, with
+// indices clamped into the row's range so that every load is valid.
+template <typename T>
+__device__ __forceinline__ void load_faces(const RowArgs<T> &A, const Row<T> &r, int32_t base,
+                                           const T *__restrict__ x, FaceBatch<T> &q)
+{
+#pragma unroll
+    for (int j = 0; j < kFaceBatch; ++j) q.e[j] = A.finc[min(base + j, r.f1 - 1)];
+#pragma unroll
+    for (int j = 0; j < kFaceBatch; ++j) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            q.xo[j][0][c] = x[int64_t(q.e[j].o1) * 3 + c];
+            q.xo[j][1][c] = x[int64_t(q.e[j].o2) * 3 + c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q.m[j][c] = A.face_dm[int64_t(q.e[j].f) * 4 + c];
+        q.area[j] = A.face_area[q.e[j].f];
+    }
+}
+
+// Energy of face j of the batch as a Dual2 in F, and the weights w[u][c].
+template <typename T>
+__device__ __forceinline__ Dual2<T, 6> face_eval(const Row<T> &r, const FaceBatch<T> &q, int j,
+                                                 int i, T w[3][2])
+{
+    const T *o1 = q.xo[j][0], *o2 = q.xo[j][1];
+    T d0[3], d1[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        // face positions: p_i = x_a, p_(i+1)%3 = o1, p_(i+2)%3 = o2
+        const T p0 = i == 0 ? r.xa[c] : (i == 1 ? o2[c] : o1[c]);
+        const T p1 = i == 1 ? r.xa[c] : (i == 2 ? o2[c] : o1[c]);
+        const T p2 = i == 2 ? r.xa[c] : (i == 0 ? o2[c] : o1[c]);
+        d0[c] = p1 - p0;
+        d1[c] = p2 - p0;
+    }
+    const T *m = q.m[j];
+    Dual2<T, 6> F[6];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        F[2 * c + 0] = Dual2<T, 6>::var(d0[c] * m[0] + d1[c] * m[2], 2 * c + 0);
+        F[2 * c + 1] = Dual2<T, 6>::var(d0[c] * m[1] + d1[c] * m[3], 2 * c + 1);
+    }
+    w[1][0] = m[0];
+    w[1][1] = m[1];
+    w[2][0] = m[2];
+    w[2][1] = m[3];
+    w[0][0] = -(m[0] + m[2]);
+    w[0][1] = -(m[1] + m[3]);
+    return face_energy(F, q.area[j]);
+}
+
+// wa^T (d2E/dF[s][.] dF[t][.]) wu for all s, t.
+template <typename T>
+__device__ __forceinline__ void face_block(const Dual2<T, 6> &e, const T wa[2], const T wu[2],
+                                           T B[9])
+{
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const T q0 = e.hess(2 * s, 2 * t) * wu[0] + e.hess(2 * s, 2 * t + 1) * wu[1];
+            const T q1 = e.hess(2 * s + 1, 2 * t) * wu[0] + e.hess(2 * s + 1, 2 * t + 1) * wu[1];
+            B[3 * s + t] = wa[0] * q0 + wa[1] * q1;
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Energy, gradient and Hessian rows.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool FACES>
 __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const int32_t *cia,
                                            const uint32_t *ib, const Row<T> &r, int32_t sb,
                                            T *Hs, const T *__restrict__ x, T *__restrict__ g)
@@ -195,6 +285,45 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
                 }
             }
             if (r.a < q.b[j]) E += double(e.v);
+        }
+    }
+
+    // faces: the diagonal block and g_a in registers; the two off-diagonal
+    // blocks of each face are added into this lane's own row slice in LDS
+    if constexpr (FACES)
+    for (int32_t base = r.f0; base < r.f1; base += kFaceBatch) {
+        FaceBatch<T> q;
+        load_faces(A, r, base, x, q);
+#pragma unroll
+        for (int j = 0; j < kFaceBatch; ++j) {
+            if (base + j >= r.f1) break;
+            const FaceInc fe = q.e[j];
+            const int i = int(fe.pk & 3u);
+            T w[3][2];
+            const Dual2<T, 6> e = face_eval(r, q, j, i, w);
+            const T wa[2] = {i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]),
+                             i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1])};
+            if (i == 0) E += double(e.v);
+#pragma unroll
+            for (int s = 0; s < 3; ++s) G[s] += wa[0] * e.g[2 * s] + wa[1] * e.g[2 * s + 1];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                T Bu[9];
+                face_block(e, wa, w[u], Bu);
+                if (u == i) {
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) D[k] += Bu[k];
+                } else {
+                    // block of face vertex u in this row: its topology slot,
+                    // or (pairs active) its column's position in the active row
+                    const int32_t vu = u == (i + 1) % 3 ? fe.o1 : fe.o2;
+                    const int32_t off = int32_t((fe.pk >> (8 * u + 8)) & 255u);
+                    const int32_t sl = act == 0 ? r.s0 + off : find_slot(cia, r.s0, r.s1, vu);
+                    T *B = Hs + 9 * (sl - sb);
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) B[k] += Bu[k];
+                }
+            }
         }
     }
 
@@ -253,7 +382,7 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     return E;
 }
 
-template <typename T>
+template <typename T, bool FACES>
 __global__ void __launch_bounds__(kRowThreads)
 k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
             EnergySink esink)
@@ -278,7 +407,7 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         T *Hs = stage + pad;
         if (fits && int(threadIdx.x) < nrows) {
             const Row<T> r = load_row(A, rpa, v0 + int32_t(threadIdx.x), x);
-            eacc += eval_row(A, act, cia, ib, r, sb, Hs, x, g);
+            eacc += eval_row<T, FACES>(A, act, cia, ib, r, sb, Hs, x, g);
         }
         wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
@@ -291,7 +420,7 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
 // Matrix-free Hessian-vector product, y_a = sum over the row's terms of
 // H_ab v_b, with the local Hessians formed in registers and never stored.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool FACES>
 __global__ void __launch_bounds__(kRowThreads)
 k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
 {
@@ -341,6 +470,51 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
                             e.hess(i, 2) * (va[2] - vb[j][2]);
             }
         }
+        if constexpr (FACES)
+        for (int32_t base = r.f0; base < r.f1; base += kFaceBatch) {
+            FaceBatch<T> q;
+            load_faces(A, r, base, x, q);
+            T vo[kFaceBatch][2][3];
+#pragma unroll
+            for (int j = 0; j < kFaceBatch; ++j)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    vo[j][0][k] = v[int64_t(q.e[j].o1) * 3 + k];
+                    vo[j][1][k] = v[int64_t(q.e[j].o2) * 3 + k];
+                }
+#pragma unroll
+            for (int j = 0; j < kFaceBatch; ++j) {
+                if (base + j >= r.f1) break;
+                const int i = int(q.e[j].pk & 3u);
+                T w[3][2];
+                const Dual2<T, 6> e = face_eval(r, q, j, i, w);
+                // dF = (dF/dp) v_face, yF = (d2E/dF2) dF, y_a += (dF/dp_a)^T yF
+                T dF[6];
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp) {
+                    const T v0 = i == 0 ? va[sp] : (i == 1 ? vo[j][1][sp] : vo[j][0][sp]);
+                    const T v1 = i == 1 ? va[sp] : (i == 2 ? vo[j][1][sp] : vo[j][0][sp]);
+                    const T v2 = i == 2 ? va[sp] : (i == 0 ? vo[j][1][sp] : vo[j][0][sp]);
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        dF[2 * sp + c] = w[0][c] * v0 + w[1][c] * v1 + w[2][c] * v2;
+                }
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp) {
+                    T yf[2];
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        T acc = T(0);
+#pragma unroll
+                        for (int l = 0; l < 6; ++l) acc += e.hess(2 * sp + c, l) * dF[l];
+                        yf[c] = acc;
+                    }
+                    const T wa0 = i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]);
+                    const T wa1 = i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1]);
+                    Y[sp] += wa0 * yf[0] + wa1 * yf[1];
+                }
+            }
+        }
         if (A.inertia_on) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) Y[k] += A.c * va[k];
@@ -379,16 +553,22 @@ int rows_lds_bytes(int lds_blocks)
 }
 
 template <typename T>
-hipError_t rows_grid(int lds_blocks, int nchunk, int *grid_eval, int *grid_hvp)
+hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int *grid_eval, int *grid_hvp)
 {
     int dev = 0, cus = 0, occ_e = 0, occ_h = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int lds = rows_lds_bytes<T>(lds_blocks);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_e, k_eval_rows<T>, kRowThreads,
-                                                         rows_lds_bytes<T>(lds_blocks));
+        e = faces ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_e, k_eval_rows<T, true>,
+                                                                  kRowThreads, lds)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_e, k_eval_rows<T, false>,
+                                                                  kRowThreads, lds);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_h, k_hvp_rows<T>, kRowThreads, 0);
+        e = faces ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_h, k_hvp_rows<T, true>,
+                                                                  kRowThreads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_h, k_hvp_rows<T, false>,
+                                                                  kRowThreads, 0);
     if (e != hipSuccess) return e;
     auto clamp = [&](int occ) {
         const int64_t full = int64_t(cus > 0 ? cus : 1) * (occ > 0 ? occ : 1);
@@ -404,8 +584,13 @@ template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_eval_rows<T>), dim3(grid), dim3(kRowThreads),
-                       rows_lds_bytes<T>(a.lds_blocks), s, a, x, g, hv, es);
+    const int lds = rows_lds_bytes<T>(a.lds_blocks);
+    if (a.faces_on)
+        hipLaunchKernelGGL((k_eval_rows<T, true>), dim3(grid), dim3(kRowThreads), lds, s, a, x, g,
+                           hv, es);
+    else
+        hipLaunchKernelGGL((k_eval_rows<T, false>), dim3(grid), dim3(kRowThreads), lds, s, a, x,
+                           g, hv, es);
     return hipGetLastError();
 }
 
@@ -413,13 +598,17 @@ template <typename T>
 hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
                            hipStream_t s)
 {
-    hipLaunchKernelGGL((k_hvp_rows<T>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v, y);
+    if (a.faces_on)
+        hipLaunchKernelGGL((k_hvp_rows<T, true>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v, y);
+    else
+        hipLaunchKernelGGL((k_hvp_rows<T, false>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v,
+                           y);
     return hipGetLastError();
 }
 
 #define LAD_ROWS_INST(T)                                                                          \
     template int rows_lds_bytes<T>(int);                                                          \
-    template hipError_t rows_grid<T>(int, int, int *, int *);                                     \
+    template hipError_t rows_grid<T>(int, int, int, int *, int *);                                \
     template hipError_t launch_eval_rows<T>(const RowArgs<T> &, const T *, T *, T *, EnergySink,  \
                                             int, hipStream_t);                                    \
     template hipError_t launch_hvp_rows<T>(const RowArgs<T> &, const T *, const T *, T *, int,    \

@@ -88,20 +88,21 @@ def test_duplicate_adjacent_and_shared_pairs(lad, path):
     L.close()
 
 
-def test_pairs_with_faces_and_hvp(lad):
+@pytest.mark.parametrize("path", ["patch", "rows"])
+def test_pairs_with_faces_and_hvp(lad, path):
     """Faces plus pairs.  The barrier support is widened to 3h and each pair
     joins vertices two grid steps apart (never adjacent), so the pairs are
     active without moving any vertex: faces stay well conditioned and the
     fp64 tolerance applies as elsewhere."""
     import torch
-    log_case(test="pairs_faces_hvp")
+    log_case(test="pairs_faces_hvp", path=path)
     m = inputs.cloth(30)
     n = m.n
     src = np.arange(0, m.nv, 37)
     src = src[(src % n) < n - 2]
     pairs = np.stack([src, src + 2], axis=1).astype(np.int32)
     dhat = 3.0 * m.h
-    L = lad.Lad(m.nv, dtype="f64", patch_lds_bytes=8192,
+    L = lad.Lad(m.nv, dtype="f64", patch_lds_bytes=8192, path=path,
                 **lad.mesh_terms(m, faces=True, pair_capacity=len(pairs), kappa=KAPPA,
                                  dhat=dhat))
     x = m.x

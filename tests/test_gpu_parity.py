@@ -99,33 +99,39 @@ def test_springs_only_and_inertia_only_rows(lad):
         L.close()
 
 
-@pytest.mark.parametrize("n,dtype,det,lds", [
-    (12, "f64", False, 0), (33, "f32", False, 8192), (33, "f64", True, 8192),
-    (64, "f32", True, 0),
+@pytest.mark.parametrize("n,dtype,det,lds,path", [
+    (12, "f64", False, 0, "patch"), (33, "f32", False, 8192, "patch"),
+    (33, "f64", True, 8192, "patch"), (64, "f32", True, 0, "patch"),
+    (2, "f64", False, 0, "rows"), (12, "f64", False, 0, "rows"), (33, "f32", False, 0, "rows"),
+    (64, "f32", False, 0, "rows"), (64, "f64", False, 0, "rows"), (129, "f32", False, 0, "rows"),
 ])
-def test_face_eval(lad, n, dtype, det, lds):
-    log_case(test="face_eval", n=n, dtype=dtype, det=det, lds=lds)
+def test_face_eval(lad, n, dtype, det, lds, path):
+    log_case(test="face_eval", n=n, dtype=dtype, det=det, lds=lds, path=path)
     m = inputs.face_grid(n)
     L, prob, x_h, res = run_eval(lad, m, dtype, det, lds, springs=False, inertia=False,
-                                 faces=True)
+                                 faces=True, path=path)
+    assert L.get_info()["eval_path"] == (lad.LAD_PATH_ROWS if path == "rows" else lad.LAD_PATH_PATCH)
     check_against_oracle(prob, x_h, res, dtype)
     L.close()
 
 
-@pytest.mark.parametrize("dtype,det", [("f64", False), ("f32", True)])
-def test_all_terms_eval(lad, dtype, det):
-    log_case(test="all_terms", dtype=dtype, det=det)
+@pytest.mark.parametrize("dtype,det,path", [("f64", False, "patch"), ("f32", True, "patch"),
+                                            ("f64", False, "rows"), ("f32", False, "rows")])
+def test_all_terms_eval(lad, dtype, det, path):
+    log_case(test="all_terms", dtype=dtype, det=det, path=path)
     m = inputs.cloth(29)
     L, prob, x_h, res = run_eval(lad, m, dtype, det, 7000, springs=True, inertia=True,
-                                 faces=True)
+                                 faces=True, path=path)
     check_against_oracle(prob, x_h, res, dtype)
     L.close()
 
 
 @pytest.mark.parametrize("n,dtype,det,faces,lds,path", [
-    (20, "f64", False, True, 0, "auto"), (45, "f32", False, True, 8192, "auto"),
-    (45, "f64", True, False, 8192, "patch"), (64, "f32", True, True, 0, "auto"),
+    (20, "f64", False, True, 0, "patch"), (45, "f32", False, True, 8192, "patch"),
+    (45, "f64", True, False, 8192, "patch"), (64, "f32", True, True, 0, "patch"),
     (45, "f64", False, False, 0, "rows"), (100, "f32", False, False, 0, "rows"),
+    (20, "f64", False, True, 0, "rows"), (45, "f32", False, True, 0, "rows"),
+    (64, "f64", False, True, 0, "rows"),
 ])
 def test_hvp(lad, n, dtype, det, faces, lds, path):
     import torch
