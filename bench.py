@@ -209,6 +209,17 @@ def bench_secondary(torch, binding, inputs, args, timer):
         r = timer.run(lambda: L.eval(x, out=out), steps, warm)
         sec[f"cloth100_{dt}_eval_ms"] = round(r["median_ms"], 5)
         L.close()
+    # 1000 x 1000 cloth, fp32: matrix-free HVP
+    mc = inputs.cloth(args.n)
+    L = cloth_ctx(binding, mc, "f32")
+    xc = to_dev(torch, mc.x, "f32")
+    vc = to_dev(torch, inputs.hvp_direction(mc.nv), "f32")
+    yc = torch.empty_like(vc)
+    r = timer.run(lambda: L.hvp(xc, vc, out=yc), steps, warm)
+    bh = compulsory_bytes_hvp(mc.nv, mc.springs.shape[0], 0, 4)
+    sec["cloth1000_hvp_ms"] = round(r["median_ms"], 5)
+    sec["cloth1000_hvp_GBps"] = round(bh / (r["median_ms"] * 1e-3) / 1e9, 1)
+    L.close()
     # 512 x 512 symmetric-Dirichlet face grid, fp32: explicit eval and HVP
     f = inputs.face_grid(512)
     L = binding.Lad(f.nv, dtype="f32",
@@ -240,6 +251,8 @@ def bench_secondary(torch, binding, inputs, args, timer):
         sets.append((torch.tensor(pairs, dtype=torch.int32, device="cuda"),
                      to_dev(torch, xs, "f32")))
     out = L.alloc_outputs()
+    vdir = to_dev(torch, inputs.hvp_direction(m.nv), "f32")
+    yv = torch.empty_like(vdir)
     state = {"i": 0}
 
     def step_fn():
@@ -250,6 +263,8 @@ def bench_secondary(torch, binding, inputs, args, timer):
 
     r = timer.run(step_fn, steps, warm)
     sec["cloth1000_pairs_insert_eval_ms"] = round(r["median_ms"], 5)
+    rh = timer.run(lambda: L.hvp(sets[0][1], vdir, out=yv), steps, warm)
+    sec["cloth1000_pairs_hvp_ms"] = round(rh["median_ms"], 5)
     ri = timer.run(lambda: L.insert_pairs(sets[0][0]), steps, warm)
     sec["cloth1000_pairs_insert_ms"] = round(ri["median_ms"], 5)
     if L.device_status() != 0:

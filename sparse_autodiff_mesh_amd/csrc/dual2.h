@@ -213,4 +213,175 @@ __device__ __forceinline__ Dual2<T, N> operator/(const Dual2<T, N> &a, const Dua
     return a * reciprocal(b);
 }
 
+// ---------------------------------------------------------------------------
+// Directional second-order duals for Hessian-vector products.
+//
+// A DualHv<T, N> carries u, its gradient du/dz (N entries), its derivative
+// along one fixed direction p (t = du/dz . p) and the derivative of the
+// gradient along p (gt = d2u/dz2 p, N entries).  Seeding the variables with
+// z_k = var(value, k, p_k) and evaluating a local energy once gives its
+// gradient and the product of its Hessian with p, without forming the
+// Hessian: 2 + 2N numbers per intermediate instead of the 1 + N + N(N+1)/2
+// of Dual2 (14 instead of 28 for a face seeded in its 6 deformation-gradient
+// entries).  The product and chain rules below are those of Dual2 contracted
+// with p.
+// ---------------------------------------------------------------------------
+template <typename T, int N>
+struct DualHv {
+    T v, t;
+    T g[N];
+    T gt[N];
+
+    __device__ __forceinline__ static DualHv constant(T c)
+    {
+        DualHv r;
+        r.v = c;
+        r.t = T(0);
+#pragma unroll
+        for (int i = 0; i < N; ++i) r.g[i] = r.gt[i] = T(0);
+        return r;
+    }
+    // the k-th seeded variable with value c and direction component pk
+    __device__ __forceinline__ static DualHv var(T c, int k, T pk)
+    {
+        DualHv r = constant(c);
+        r.t = pk;
+#pragma unroll
+        for (int i = 0; i < N; ++i) r.g[i] = (i == k) ? T(1) : T(0);
+        return r;
+    }
+};
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator+(const DualHv<T, N> &a, const DualHv<T, N> &b)
+{
+    DualHv<T, N> r;
+    r.v = a.v + b.v;
+    r.t = a.t + b.t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = a.g[i] + b.g[i];
+        r.gt[i] = a.gt[i] + b.gt[i];
+    }
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator-(const DualHv<T, N> &a, const DualHv<T, N> &b)
+{
+    DualHv<T, N> r;
+    r.v = a.v - b.v;
+    r.t = a.t - b.t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = a.g[i] - b.g[i];
+        r.gt[i] = a.gt[i] - b.gt[i];
+    }
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator*(T s, const DualHv<T, N> &a)
+{
+    DualHv<T, N> r;
+    r.v = s * a.v;
+    r.t = s * a.t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = s * a.g[i];
+        r.gt[i] = s * a.gt[i];
+    }
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator+(const DualHv<T, N> &a, T s)
+{
+    DualHv<T, N> r = a;
+    r.v = a.v + s;
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator-(const DualHv<T, N> &a, T s)
+{
+    DualHv<T, N> r = a;
+    r.v = a.v - s;
+    return r;
+}
+
+// (ab)' = a'b + ab';  (ab)'' p = a'' p b + a b'' p + a' (b' . p) + b' (a' . p)
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator*(const DualHv<T, N> &a, const DualHv<T, N> &b)
+{
+    DualHv<T, N> r;
+    r.v = a.v * b.v;
+    r.t = a.v * b.t + b.v * a.t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = a.v * b.g[i] + b.v * a.g[i];
+        r.gt[i] = a.v * b.gt[i] + b.v * a.gt[i] + (a.g[i] * b.t + b.g[i] * a.t);
+    }
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> sqr(const DualHv<T, N> &a)
+{
+    DualHv<T, N> r;
+    const T two_v = T(2) * a.v;
+    r.v = a.v * a.v;
+    r.t = two_v * a.t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = two_v * a.g[i];
+        r.gt[i] = two_v * a.gt[i] + T(2) * (a.g[i] * a.t);
+    }
+    return r;
+}
+
+// f(a)' = f1 a';  f(a)'' p = f1 a'' p + f2 a' (a' . p)
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> chain(const DualHv<T, N> &a, T f0, T f1, T f2)
+{
+    DualHv<T, N> r;
+    r.v = f0;
+    r.t = f1 * a.t;
+    const T f2t = f2 * a.t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = f1 * a.g[i];
+        r.gt[i] = f1 * a.gt[i] + f2t * a.g[i];
+    }
+    return r;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> sqrt(const DualHv<T, N> &a)
+{
+    const T s = lad_sqrt(a.v);
+    const T inv = T(1) / s;
+    return chain(a, s, T(0.5) * inv, T(-0.25) * inv * inv * inv);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> log(const DualHv<T, N> &a)
+{
+    const T inv = T(1) / a.v;
+    return chain(a, lad_log(a.v), inv, -inv * inv);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> reciprocal(const DualHv<T, N> &a)
+{
+    const T inv = T(1) / a.v;
+    return chain(a, inv, -inv * inv, T(2) * inv * inv * inv);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator/(const DualHv<T, N> &a, const DualHv<T, N> &b)
+{
+    return a * reciprocal(b);
+}
+
 }  // namespace lad

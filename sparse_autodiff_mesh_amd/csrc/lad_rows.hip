@@ -160,7 +160,7 @@ __device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r,
 //   g_a[s]       += sum_c w[i][c] dE/dF[s][c]
 //   H_(a,u)[s][t] += sum_{c,c'} w[i][c] w[u][c'] d2E/dF[s][c] dF[t][c'].
 // ---------------------------------------------------------------------------
-constexpr int kFaceBatch = 4;  // incident faces whose loads a lane issues together
+constexpr int kFaceBatch = 3;  // incident faces whose loads a lane issues together
 
 template <typename T>
 struct FaceBatch {
@@ -191,28 +191,23 @@ __device__ __forceinline__ void load_faces(const RowArgs<T> &A, const Row<T> &r,
     }
 }
 
-// Energy of face j of the batch as a Dual2 in F, and the weights w[u][c].
+// Values of F = [p1 - p0, p2 - p0] M for face j of the batch (row vertex at
+// face position i) and the weights w[u][c] = dF[.][c] / dp_u.
 template <typename T>
-__device__ __forceinline__ Dual2<T, 6> face_eval(const Row<T> &r, const FaceBatch<T> &q, int j,
-                                                 int i, T w[3][2])
+__device__ __forceinline__ void face_F(const Row<T> &r, const FaceBatch<T> &q, int j, int i,
+                                       T Fv[6], T w[3][2])
 {
     const T *o1 = q.xo[j][0], *o2 = q.xo[j][1];
-    T d0[3], d1[3];
+    const T *m = q.m[j];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         // face positions: p_i = x_a, p_(i+1)%3 = o1, p_(i+2)%3 = o2
         const T p0 = i == 0 ? r.xa[c] : (i == 1 ? o2[c] : o1[c]);
         const T p1 = i == 1 ? r.xa[c] : (i == 2 ? o2[c] : o1[c]);
         const T p2 = i == 2 ? r.xa[c] : (i == 0 ? o2[c] : o1[c]);
-        d0[c] = p1 - p0;
-        d1[c] = p2 - p0;
-    }
-    const T *m = q.m[j];
-    Dual2<T, 6> F[6];
-#pragma unroll
-    for (int c = 0; c < 3; ++c) {
-        F[2 * c + 0] = Dual2<T, 6>::var(d0[c] * m[0] + d1[c] * m[2], 2 * c + 0);
-        F[2 * c + 1] = Dual2<T, 6>::var(d0[c] * m[1] + d1[c] * m[3], 2 * c + 1);
+        const T d0 = p1 - p0, d1 = p2 - p0;
+        Fv[2 * c + 0] = d0 * m[0] + d1 * m[2];
+        Fv[2 * c + 1] = d0 * m[1] + d1 * m[3];
     }
     w[1][0] = m[0];
     w[1][1] = m[1];
@@ -220,6 +215,18 @@ __device__ __forceinline__ Dual2<T, 6> face_eval(const Row<T> &r, const FaceBatc
     w[2][1] = m[3];
     w[0][0] = -(m[0] + m[2]);
     w[0][1] = -(m[1] + m[3]);
+}
+
+// Energy of face j of the batch as a Dual2 in F, and the weights w[u][c].
+template <typename T>
+__device__ __forceinline__ Dual2<T, 6> face_eval(const Row<T> &r, const FaceBatch<T> &q, int j,
+                                                 int i, T w[3][2])
+{
+    T Fv[6];
+    face_F(r, q, j, i, Fv, w);
+    Dual2<T, 6> F[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) F[k] = Dual2<T, 6>::var(Fv[k], k);
     return face_energy(F, q.area[j]);
 }
 
@@ -436,15 +443,9 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
         for (int k = 0; k < 3; ++k) va[k] = v[int64_t(r.a) * 3 + k];
-        // K (v_a - v_b) for the two-vertex term with local Hessian K.
-        auto add_kv = [&](const Dual2<T, 3> &e, int32_t b) {
-            T dv[3];
-#pragma unroll
-            for (int k = 0; k < 3; ++k) dv[k] = va[k] - v[int64_t(b) * 3 + k];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-                Y[i] += e.hess(i, 0) * dv[0] + e.hess(i, 1) * dv[1] + e.hess(i, 2) * dv[2];
-        };
+        // Every term is evaluated once in DualHv numbers seeded with the
+        // term's variables and the matching components of v; the gradient's
+        // directional derivative gt is the term's Hessian applied to v.
         int32_t nins = 0;
         for (int32_t base = r.s0; base < r.s1; base += kBatch) {
             SlotBatch<T> q;
@@ -460,14 +461,13 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             for (int j = 0; j < kBatch; ++j) {
                 if (base + j >= r.s1) break;
                 if (q.b[j] == r.a || !(q.L[j] >= T(0))) continue;
-                Dual2<T, 3> d[3];
+                DualHv<T, 3> d[3];
 #pragma unroll
-                for (int k = 0; k < 3; ++k) d[k] = Dual2<T, 3>::var(r.xa[k] - q.xb[j][k], k);
-                const Dual2<T, 3> e = spring_energy(d, q.L[j], A.k);
+                for (int k = 0; k < 3; ++k)
+                    d[k] = DualHv<T, 3>::var(r.xa[k] - q.xb[j][k], k, va[k] - vb[j][k]);
+                const DualHv<T, 3> e = spring_energy(d, q.L[j], A.k);
 #pragma unroll
-                for (int i = 0; i < 3; ++i)
-                    Y[i] += e.hess(i, 0) * (va[0] - vb[j][0]) + e.hess(i, 1) * (va[1] - vb[j][1]) +
-                            e.hess(i, 2) * (va[2] - vb[j][2]);
+                for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
             }
         }
         if constexpr (FACES)
@@ -486,10 +486,10 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             for (int j = 0; j < kFaceBatch; ++j) {
                 if (base + j >= r.f1) break;
                 const int i = int(q.e[j].pk & 3u);
-                T w[3][2];
-                const Dual2<T, 6> e = face_eval(r, q, j, i, w);
-                // dF = (dF/dp) v_face, yF = (d2E/dF2) dF, y_a += (dF/dp_a)^T yF
-                T dF[6];
+                T Fv[6], w[3][2];
+                face_F(r, q, j, i, Fv, w);
+                // direction in F: dF = (dF/dp) v_face
+                DualHv<T, 6> F[6];
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) {
                     const T v0 = i == 0 ? va[sp] : (i == 1 ? vo[j][1][sp] : vo[j][0][sp]);
@@ -497,45 +497,45 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
                     const T v2 = i == 2 ? va[sp] : (i == 0 ? vo[j][1][sp] : vo[j][0][sp]);
 #pragma unroll
                     for (int c = 0; c < 2; ++c)
-                        dF[2 * sp + c] = w[0][c] * v0 + w[1][c] * v1 + w[2][c] * v2;
+                        F[2 * sp + c] = DualHv<T, 6>::var(
+                            Fv[2 * sp + c], 2 * sp + c, w[0][c] * v0 + w[1][c] * v1 + w[2][c] * v2);
                 }
+                const DualHv<T, 6> e = face_energy(F, q.area[j]);
+                // y_a += (dF/dp_a)^T (d2E/dF2 dF)
+                const T wa0 = i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]);
+                const T wa1 = i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1]);
 #pragma unroll
-                for (int sp = 0; sp < 3; ++sp) {
-                    T yf[2];
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        T acc = T(0);
-#pragma unroll
-                        for (int l = 0; l < 6; ++l) acc += e.hess(2 * sp + c, l) * dF[l];
-                        yf[c] = acc;
-                    }
-                    const T wa0 = i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]);
-                    const T wa1 = i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1]);
-                    Y[sp] += wa0 * yf[0] + wa1 * yf[1];
-                }
+                for (int sp = 0; sp < 3; ++sp) Y[sp] += wa0 * e.gt[2 * sp] + wa1 * e.gt[2 * sp + 1];
             }
         }
         if (A.inertia_on) {
+            DualHv<T, 3> z[3];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) Y[k] += A.c * va[k];
+            for (int k = 0; k < 3; ++k) z[k] = DualHv<T, 3>::var(r.xa[k] - r.xt[k], k, va[k]);
+            const DualHv<T, 3> e = inertia_energy(z, A.c);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
         }
         if (act != 0) {
             const int32_t *pp = A.pat.pinc_ptr[act];
             const int32_t *pl = A.pat.pinc[act];
             const int32_t *prs = A.pat.pairs[act];
             for (int32_t k = pp[r.a]; k < pp[r.a + 1]; ++k) {
-                const int32_t q = pl[k];
-                const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
+                const int32_t qp = pl[k];
+                const int32_t i0 = prs[2 * qp], i1 = prs[2 * qp + 1];
                 const int32_t b = i0 == r.a ? i1 : i0;
                 T dz[3];
 #pragma unroll
                 for (int cc = 0; cc < 3; ++cc) dz[cc] = r.xa[cc] - x[int64_t(b) * 3 + cc];
                 const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
                 if (!(l2 < A.dhat * A.dhat)) continue;
-                Dual2<T, 3> d[3];
+                DualHv<T, 3> d[3];
 #pragma unroll
-                for (int cc = 0; cc < 3; ++cc) d[cc] = Dual2<T, 3>::var(dz[cc], cc);
-                add_kv(barrier_energy(d, A.kappa, A.dhat), b);
+                for (int cc = 0; cc < 3; ++cc)
+                    d[cc] = DualHv<T, 3>::var(dz[cc], cc, va[cc] - v[int64_t(b) * 3 + cc]);
+                const DualHv<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
+#pragma unroll
+                for (int cc = 0; cc < 3; ++cc) Y[cc] += e.gt[cc];
             }
         }
 #pragma unroll
