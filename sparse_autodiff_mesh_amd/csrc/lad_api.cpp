@@ -235,6 +235,7 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.springs_on = ctx->springs_on;
     a.inertia_on = ctx->inertia_on;
     a.faces_on = ctx->faces_on;
+    a.pairs_on = ctx->pair_cap > 0 ? 1 : 0;
     a.lds_blocks = kRowLdsBlocks;
     a.state = ctx->d_state;
     a.pat = ctx->pat;
@@ -418,10 +419,10 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (st != LAD_OK) return st;
     if (ctx->row_mode) {
         e = ctx->dtype == LAD_F64
-                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, &ctx->grid_eval,
-                                    &ctx->grid_hvp)
-                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, &ctx->grid_eval,
-                                   &ctx->grid_hvp);
+                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, ctx->pair_cap > 0,
+                                    &ctx->grid_eval, &ctx->grid_hvp)
+                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, ctx->pair_cap > 0,
+                                   &ctx->grid_eval, &ctx->grid_hvp);
         if (e != hipSuccess) return hip_fail(ctx, e, "occupancy query");
     } else {
         ctx->grid_eval = ctx->npatch;
@@ -442,11 +443,9 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         e = hipMemcpyAsync(ctx->d_state, &hs, sizeof(hs), hipMemcpyHostToDevice, s);
     if (e == hipSuccess && d->pair_capacity > 0) {
         const size_t cap2 = size_t(d->pair_capacity) * 2;
-        ctx->ins.ib_words = int32_t((ctx->hcap + 31) / 32);
         for (int b = 1; b <= 2 && e == hipSuccess; ++b) {
             e = dev_alloc(ctx, &ctx->ins.rp[b], size_t(nv) + 1);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.ci[b], size_t(ctx->hcap));
-            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.ib[b], size_t(ctx->ins.ib_words));
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pairs[b], cap2);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_ptr[b], size_t(nv) + 1);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc[b], cap2);
@@ -460,7 +459,6 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         for (int b = 1; b <= 2; ++b) {
             ctx->pat.rp[b] = ctx->ins.rp[b];
             ctx->pat.ci[b] = ctx->ins.ci[b];
-            ctx->pat.ib[b] = ctx->ins.ib[b];
             ctx->pat.pairs[b] = ctx->ins.pairs[b];
             ctx->pat.pinc_ptr[b] = ctx->ins.pinc_ptr[b];
             ctx->pat.pinc[b] = ctx->ins.pinc[b];

@@ -253,16 +253,19 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
         stream_out<kThreads>(dst, H, h.nblk * 9, hpad);
     } else if (nact <= h.amap_cap) {
         // pairs inserted blocks into these rows: map every active block to
-        // its base block (or to zero for an inserted one)
+        // its base block, or to zero for an inserted one (a column that the
+        // topology row does not hold; both rows are sorted)
         const int32_t *rp0 = A.pat.rp[0];
-        const uint32_t *ib = A.pat.ib[act];
+        const int32_t *ci0 = A.pat.ci[0];
+        const int32_t *cia = A.pat.ci[act];
         for (int i = tid; i < h.nown; i += kThreads) {
             const int32_t a0 = rpa[h.v0 + i] - ra0, a1 = rpa[h.v0 + i + 1] - ra0;
-            int32_t b = rp0[h.v0 + i] - h.blk0;
+            int32_t b = rp0[h.v0 + i];
+            const int32_t bend = rp0[h.v0 + i + 1];
             for (int32_t j = a0; j < a1; ++j) {
-                const int64_t gp = int64_t(ra0) + j;
-                const bool ins = (ib[gp >> 5] >> (gp & 31)) & 1u;
-                amap[j] = ins ? kNone : uint16_t(b++);
+                const bool base = b < bend && ci0[b] == cia[ra0 + j];
+                amap[j] = base ? uint16_t(b - h.blk0) : kNone;
+                b += base ? 1 : 0;
             }
         }
         __syncthreads();

@@ -23,8 +23,6 @@ namespace {
 
 __device__ __forceinline__ int back_of(const DevState *st) { return st->active == 1 ? 2 : 1; }
 
-__global__ void k_ins_begin(DevState *st) { st->err_cur = 0; }
-
 // Validate, copy the pairs into the back buffer, count pairs per row.
 __global__ void __launch_bounds__(kThreads)
 k_ins_count(DevState *st, const int32_t *__restrict__ in, int32_t np, int32_t nv, InsertBufs b)
@@ -120,14 +118,7 @@ k_ins_rows(const DevState *st, int32_t nv, InsertBufs b)
     b.newlen[a] = len;
 }
 
-__global__ void __launch_bounds__(kThreads) k_ins_clearbits(const DevState *st, InsertBufs b)
-{
-    const int32_t w = blockIdx.x * kThreads + threadIdx.x;
-    if (w < b.ib_words) b.ib[back_of(st)][w] = 0u;
-}
-
-// Merge the topology row with the row's new partners into the back buffer
-// and flag the inserted positions.
+// Merge the topology row with the row's new partners into the back buffer.
 __global__ void __launch_bounds__(kThreads) k_ins_merge(const DevState *st, int32_t nv, InsertBufs b)
 {
     const int32_t a = blockIdx.x * kThreads + threadIdx.x;
@@ -147,12 +138,7 @@ __global__ void __launch_bounds__(kThreads) k_ins_merge(const DevState *st, int3
     while (o < o1) {
         if (m >= nn && i >= rb1) break;
         const bool take_new = m < nn && (i >= rb1 || pn[m] < cb[i]);
-        if (take_new) {
-            out[o] = pn[m++];
-            atomicOr(&b.ib[bk][o >> 5], 1u << (o & 31));
-        } else {
-            out[o] = cb[i++];
-        }
+        out[o] = take_new ? pn[m++] : cb[i++];
         ++o;
     }
 }
@@ -169,16 +155,19 @@ k_ins_check(DevState *st, const PatchHdr *__restrict__ hdr, int32_t npatch, Inse
     if (n > h.amap_cap) atomicOr(&st->err_cur, 2);
 }
 
+// Flip the active buffer if every check of this insert passed, else latch
+// the error; either way re-arm err_cur for the next insert.  The kernels of
+// the next call run after this one on the same stream.
 __global__ void k_ins_commit(DevState *st, int32_t np, int32_t nv, InsertBufs b)
 {
     const int bk = back_of(st);
     if (st->err_cur == 0) {
         st->np[bk] = np;
         st->nnzb[bk] = b.rp[bk][nv];
-        __threadfence();
         st->active = bk;
     } else {
         st->err_latched |= st->err_cur;
+        st->err_cur = 0;
     }
 }
 
@@ -191,7 +180,6 @@ inline unsigned blocks_for(int64_t n) { return unsigned((n + kThreads - 1) / kTh
 hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32_t nv,
                          InsertBufs b, const PatchHdr *hdr, int32_t npatch, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_ins_begin, dim3(1), dim3(1), 0, s, st);
     hipLaunchKernelGGL(k_ins_count, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, d_pairs, np,
                        nv, b);
     hipError_t e = launch_scan_back(b.cnt, b.pinc_ptr, st, nv, b.tmp, s);
@@ -200,7 +188,6 @@ hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32
     hipLaunchKernelGGL(k_ins_rows, dim3(blocks_for(nv)), dim3(kThreads), 0, s, st, nv, b);
     e = launch_scan_back(b.newlen, b.rp, st, nv, b.tmp, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ins_clearbits, dim3(blocks_for(b.ib_words)), dim3(kThreads), 0, s, st, b);
     hipLaunchKernelGGL(k_ins_merge, dim3(blocks_for(nv)), dim3(kThreads), 0, s, st, nv, b);
     hipLaunchKernelGGL(k_ins_check, dim3(blocks_for(npatch)), dim3(kThreads), 0, s, st, hdr,
                        npatch, b);

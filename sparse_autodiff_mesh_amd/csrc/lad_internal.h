@@ -60,7 +60,8 @@ static_assert(sizeof(PatchHdr) == 64, "PatchHdr layout");
 struct DevState {
     int32_t active;
     int32_t err_latched;     // sticky error bits: 1 = bad pair, 2 = capacity
-    int32_t err_cur;         // error bits of the insert in flight
+    int32_t err_cur;         // error bits of the insert in flight (zero
+                             // between inserts: the commit kernel clears it)
     int32_t np[3];           // pairs of each buffer
     int32_t nnzb[3];         // blocks of each buffer
     int32_t pad[7];
@@ -139,7 +140,6 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
 struct PatternBufs {
     const int32_t *rp[3];
     const int32_t *ci[3];
-    const uint32_t *ib[3];       // inserted-block bits (buffers 1, 2)
     const int32_t *pairs[3];
     const int32_t *pinc_ptr[3];  // per-row pair incidence (buffers 1, 2)
     const int32_t *pinc[3];
@@ -201,6 +201,7 @@ struct RowArgs {
     const T *face_area;          // [nf]
     T k, c, kappa, dhat;
     int32_t springs_on, inertia_on, faces_on;
+    int32_t pairs_on;            // pair capacity > 0 (pairs may be active)
     int32_t lds_blocks;          // staging capacity per workgroup, in blocks
     const DevState *state;
     PatternBufs pat;
@@ -209,7 +210,8 @@ struct RowArgs {
 template <typename T>
 int rows_lds_bytes(int lds_blocks);
 template <typename T>
-hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int *grid_eval, int *grid_hvp);
+hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int pairs, int *grid_eval,
+                     int *grid_hvp);
 template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s);
@@ -257,7 +259,6 @@ hipError_t launch_pattern_compact(int32_t nv, PatternScratch sc,
 struct InsertBufs {
     int32_t *rp[3];
     int32_t *ci[3];
-    uint32_t *ib[3];
     int32_t *pairs[3];
     int32_t *pinc_ptr[3];
     int32_t *pinc[3];
@@ -266,7 +267,6 @@ struct InsertBufs {
     int32_t *cnt;                // [nv], all zero between inserts
     int32_t *newlen;             // [nv]
     int32_t *tmp;                // scan scratch
-    int32_t ib_words;            // words of each inserted-bit array
 };
 hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np,
                          int32_t nv, InsertBufs b, const PatchHdr *hdr,

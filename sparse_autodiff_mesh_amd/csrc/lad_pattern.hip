@@ -60,22 +60,10 @@ __global__ void __launch_bounds__(kThreads) k_scan_reduce(const int32_t *__restr
     if (threadIdx.x == 0) tmp[blockIdx.x] = tot;
 }
 
-// Single workgroup: exclusive scan of tmp[0..nb) in place, tmp[nb] = total.
-__global__ void __launch_bounds__(kThreads) k_scan_top(int32_t *__restrict__ tmp, int32_t nb)
-{
-    __shared__ int wsum[kWaves];
-    int carry = 0;
-    for (int32_t b0 = 0; b0 < nb; b0 += kThreads) {
-        const int32_t i = b0 + threadIdx.x;
-        const int v = i < nb ? tmp[i] : 0;
-        int tot;
-        const int ex = block_exclusive_scan(v, wsum, tot);
-        if (i < nb) tmp[i] = carry + ex;
-        carry += tot;
-    }
-    if (threadIdx.x == 0) tmp[nb] = carry;
-}
-
+// Down-sweep: tile b adds the sum of tiles 0..b-1 (read from tmp, summed
+// by this workgroup in a fixed order) to its own exclusive scan.  The last
+// tile also writes the total at out[n].  The per-tile top-level scan is thus
+// folded into this launch.
 template <typename Out>
 __global__ void __launch_bounds__(kThreads) k_scan_down(const int32_t *__restrict__ in, int32_t n,
                                                         const int32_t *__restrict__ tmp, int32_t nb,
@@ -83,6 +71,13 @@ __global__ void __launch_bounds__(kThreads) k_scan_down(const int32_t *__restric
 {
     __shared__ int wsum[kWaves];
     int32_t *o = out.get();
+    int before = 0;
+    for (int32_t t0 = 0; t0 < int32_t(blockIdx.x); t0 += kThreads) {
+        const int32_t t = t0 + threadIdx.x;
+        int tot;
+        block_exclusive_scan(t < int32_t(blockIdx.x) ? tmp[t] : 0, wsum, tot);
+        before += tot;
+    }
     const int64_t base = int64_t(blockIdx.x) * kTile + int64_t(threadIdx.x) * kItems;
     int v[kItems];
     int s = 0;
@@ -92,13 +87,13 @@ __global__ void __launch_bounds__(kThreads) k_scan_down(const int32_t *__restric
         s += v[k];
     }
     int tot;
-    int run = tmp[blockIdx.x] + block_exclusive_scan(s, wsum, tot);
+    int run = before + block_exclusive_scan(s, wsum, tot);
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         if (base + k < n) o[base + k] = run;
         run += v[k];
     }
-    if (blockIdx.x == nb - 1 && threadIdx.x == 0) o[n] = tmp[nb];
+    if (blockIdx.x == nb - 1 && threadIdx.x == kThreads - 1) o[n] = run;
 }
 
 struct DirectOut {
@@ -200,7 +195,6 @@ static hipError_t scan_impl(const int32_t *in, Out out, int32_t n, int32_t *tmp,
 {
     const int32_t nb = n > 0 ? int32_t((int64_t(n) + kTile - 1) / kTile) : 1;
     hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(kThreads), 0, s, in, n, tmp);
-    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, tmp, nb);
     hipLaunchKernelGGL((k_scan_down<Out>), dim3(nb), dim3(kThreads), 0, s, in, n,
                        (const int32_t *)tmp, nb, out);
     return hipGetLastError();

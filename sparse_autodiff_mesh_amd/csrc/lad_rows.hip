@@ -71,22 +71,27 @@ __device__ __forceinline__ int32_t find_slot(const int32_t *ci, int32_t lo, int3
 
 template <typename T>
 struct Row {
-    int32_t a, s0, s1, kb0;   // vertex, active slot range, first base slot
+    int32_t a, s0, s1;        // vertex, active slot range
+    int32_t kb0, kb1;         // topology slot range
     int32_t f0, f1;           // incident-face range (when the face term is on)
+    int32_t p0, p1;           // pair-incidence range (when pairs are active)
     T xa[3];
     T xt[3];                  // inertial target (when the inertia term is on)
 };
 
 // Row header loads, all independent of each other.
 template <typename T>
-__device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, const int32_t *rpa, int32_t a,
-                                           const T *__restrict__ x)
+__device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, int act, const int32_t *rpa,
+                                           int32_t a, const T *__restrict__ x)
 {
     Row<T> r;
+    r.p0 = act != 0 ? A.pat.pinc_ptr[act][a] : 0;
+    r.p1 = act != 0 ? A.pat.pinc_ptr[act][a + 1] : 0;
     r.a = a;
     r.s0 = rpa[a];
     r.s1 = rpa[a + 1];
     r.kb0 = A.rp0[a];
+    r.kb1 = A.rp0[a + 1];
     r.f0 = A.faces_on ? A.fptr[a] : 0;
     r.f1 = A.faces_on ? A.fptr[a + 1] : 0;
 #pragma unroll
@@ -111,44 +116,112 @@ struct SlotBatch {
 // Load one batch starting at active slot `base`.  Every load uses an index
 // that is valid whatever the slot (the row's first topology slot, or the
 // row's own vertex), so all loads of the batch are issued back to back and
-// only the arithmetic that consumes them is predicated.  `nins` counts the
-// inserted slots of the row before `base` and is advanced past the batch.
+// only the arithmetic that consumes them is predicated.
+//
+// Topology pattern active (act == 0): active slot s is topology slot
+// kb0 + (s - s0).  Pairs active: the active row is the topology row with
+// the pairs' new columns merged in, both sorted, so a slot is inserted
+// exactly when its column is not in the topology row.  The batch then loads
+// the active columns and a window of kBatch topology columns starting at
+// the cursor `jb` (the active slots of the batch can only match topology
+// slots in that window) and matches them in registers; `jb` advances past
+// the matched slots.
 template <typename T>
 __device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r, int act,
-                                           const uint32_t *ib, int32_t base, int32_t &nins,
+                                           const int32_t *cia, int32_t base, int32_t &jb,
                                            const T *__restrict__ x, SlotBatch<T> &q)
 {
-    uint32_t insw[kBatch];
+    if (act == 0) {  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) insw[j] = 0u;
-    if (act != 0) {  // wave-uniform: pairs are active
+        for (int j = 0; j < kBatch; ++j) q.kb[j] = base + j < r.s1 ? r.kb0 + (base + j - r.s0) : -1;
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int32_t sl = min(base + j, r.s1 - 1);
-            insw[j] = ib[sl >> 5] >> (sl & 31);
+            const int32_t kl = q.kb[j] >= 0 ? q.kb[j] : r.kb0;
+            q.b[j] = A.ci0[kl];
+            q.L[j] = A.slot_rest[kl];
         }
+    } else {
+        int32_t ca[kBatch], cb[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            ca[j] = cia[min(base + j, r.s1 - 1)];
+            cb[j] = A.ci0[min(jb + j, r.kb1 - 1)];
+        }
+        int32_t nmatch = 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            int32_t kb = -1;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                kb = (jb + k < r.kb1 && cb[k] == ca[j]) ? jb + k : kb;
+            q.kb[j] = base + j < r.s1 ? kb : -1;
+            q.b[j] = ca[j];
+            nmatch += q.kb[j] >= 0 ? 1 : 0;
+        }
+        jb += nmatch;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) q.L[j] = A.slot_rest[q.kb[j] >= 0 ? q.kb[j] : r.kb0];
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-        const int32_t s = base + j;
-        const bool valid = s < r.s1;
-        const bool ins = valid && (insw[j] & 1u);
-        q.kb[j] = (valid && !ins) ? r.kb0 + (s - r.s0) - nins : -1;
-        nins += ins ? 1 : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-        const int32_t kl = q.kb[j] >= 0 ? q.kb[j] : r.kb0;
-        q.b[j] = A.ci0[kl];
-        q.L[j] = A.slot_rest[kl];
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-        const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
+        const int32_t bl = (base + j < r.s1) ? q.b[j] : r.a;
 #pragma unroll
         for (int c = 0; c < 3; ++c) q.xb[j][c] = x[int64_t(bl) * 3 + c];
         if (q.kb[j] < 0 || !A.springs_on) q.L[j] = T(-1);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Runtime pairs of one row.  The first kRowPairs of them (in pair order) are
+// loaded before the slot loop, so their chain of dependent loads (pair id ->
+// endpoints -> partner position) overlaps the slot loads, and the slot loop
+// finds each partner's block by comparing columns in registers.  Further
+// pairs of the same row are handled one by one afterwards.
+// ---------------------------------------------------------------------------
+constexpr int kRowPairs = 2;
+
+template <typename T>
+struct PairPre {
+    int32_t n;                 // prefetched pairs of this row (<= kRowPairs)
+    int32_t b[kRowPairs];      // partner vertex
+    int32_t first[kRowPairs];  // 1 if this row is the pair's first vertex
+    int32_t slot[kRowPairs];   // partner's block in the active row
+    T xb[kRowPairs][3];
+};
+
+// Every field is set whatever the row: with no (or fewer) pairs the unused
+// entries name the row's own vertex, so loads indexed by pp.b stay in range.
+template <typename T>
+__device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, const Row<T> &r,
+                                               const T *__restrict__ x, PairPre<T> &pp)
+{
+    pp.n = 0;
+#pragma unroll
+    for (int k = 0; k < kRowPairs; ++k) {
+        pp.b[k] = r.a;
+        pp.first[k] = 0;
+        pp.slot[k] = r.s0;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) pp.xb[k][c] = r.xa[c];
+    }
+    if (act == 0) return;  // wave-uniform
+    const int32_t *pl = A.pat.pinc[act];
+    const int32_t *prs = A.pat.pairs[act];
+    pp.n = min(r.p1 - r.p0, kRowPairs);
+    int32_t q[kRowPairs];
+#pragma unroll
+    for (int k = 0; k < kRowPairs; ++k) q[k] = pl[k < pp.n ? r.p0 + k : 0];
+#pragma unroll
+    for (int k = 0; k < kRowPairs; ++k) {
+        const int32_t i0 = prs[2 * q[k]], i1 = prs[2 * q[k] + 1];
+        pp.first[k] = i0 == r.a ? 1 : 0;
+        pp.b[k] = k < pp.n ? (i0 == r.a ? i1 : i0) : r.a;
+        pp.slot[k] = r.s0;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowPairs; ++k)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) pp.xb[k][c] = x[int64_t(pp.b[k]) * 3 + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -248,9 +321,9 @@ __device__ __forceinline__ void face_block(const Dual2<T, 6> &e, const T wa[2], 
 // ---------------------------------------------------------------------------
 // Energy, gradient and Hessian rows.
 // ---------------------------------------------------------------------------
-template <typename T, bool FACES>
+template <typename T, bool FACES, bool PAIRS>
 __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const int32_t *cia,
-                                           const uint32_t *ib, const Row<T> &r, int32_t sb,
+                                           const Row<T> &r, int32_t sb,
                                            T *Hs, const T *__restrict__ x, T *__restrict__ g)
 {
     T D[9], G[3] = {T(0), T(0), T(0)};
@@ -259,14 +332,18 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     double E = 0.0;
     int32_t dslot = r.s0;
 
-    int32_t nins = 0;
+    PairPre<T> pp;
+    prefetch_pairs(A, act, r, x, pp);
+    int32_t jb = r.kb0;
     for (int32_t base = r.s0; base < r.s1; base += kBatch) {
         SlotBatch<T> q;
-        load_batch(A, r, act, ib, base, nins, x, q);
+        load_batch(A, r, act, cia, base, jb, x, q);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int32_t s = base + j;
             if (s >= r.s1) break;
+#pragma unroll
+            for (int k = 0; k < kRowPairs; ++k) pp.slot[k] = q.b[j] == pp.b[k] ? s : pp.slot[k];
             T *B = Hs + 9 * (s - sb);
             if (q.kb[j] >= 0 && q.b[j] == r.a) {
                 dslot = s;
@@ -349,35 +426,45 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
         }
     }
 
-    if (act != 0) {  // runtime pairs of this row, in pair order
-        const int32_t *pp = A.pat.pinc_ptr[act];
+    // runtime pairs of this row, in pair order: -K into the (a, b) block,
+    // +K into the diagonal
+    auto pair_term = [&](const T xb[3], int32_t slot, bool first) {
+        T dz[3];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) dz[c] = r.xa[c] - xb[c];
+        const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
+        if (!(l2 < A.dhat * A.dhat)) return;  // outside the barrier's support
+        Dual2<T, 3> d[3];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(dz[c], c);
+        const Dual2<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
+        if (first) E += double(e.v);
+        T *B = Hs + 9 * (slot - sb);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            G[i] += e.g[i];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const T h = e.hess(i, j);
+                B[3 * i + j] -= h;
+                D[3 * i + j] += h;
+            }
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kRowPairs; ++k)
+        if (k < pp.n) pair_term(pp.xb[k], pp.slot[k], pp.first[k] != 0);
+    if (r.p1 - r.p0 > kRowPairs) {
         const int32_t *pl = A.pat.pinc[act];
         const int32_t *prs = A.pat.pairs[act];
-        for (int32_t k = pp[r.a]; k < pp[r.a + 1]; ++k) {
+        for (int32_t k = r.p0 + kRowPairs; k < r.p1; ++k) {
             const int32_t q = pl[k];
             const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
             const int32_t b = i0 == r.a ? i1 : i0;
-            T dz[3];
+            T xb[3];
 #pragma unroll
-            for (int c = 0; c < 3; ++c) dz[c] = r.xa[c] - x[int64_t(b) * 3 + c];
-            const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
-            if (!(l2 < A.dhat * A.dhat)) continue;  // outside the barrier's support
-            Dual2<T, 3> d[3];
-#pragma unroll
-            for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(dz[c], c);
-            const Dual2<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
-            if (i0 == r.a) E += double(e.v);
-            T *B = Hs + 9 * (find_slot(cia, r.s0, r.s1, b) - sb);
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                G[i] += e.g[i];
-#pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const T h = e.hess(i, j);
-                    B[3 * i + j] -= h;
-                    D[3 * i + j] += h;
-                }
-            }
+            for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
+            pair_term(xb, find_slot(cia, r.s0, r.s1, b), i0 == r.a);
         }
     }
 
@@ -389,17 +476,17 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     return E;
 }
 
-template <typename T, bool FACES>
+template <typename T, bool FACES, bool PAIRS>
 __global__ void __launch_bounds__(kRowThreads)
 k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
             EnergySink esink)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     T *stage = reinterpret_cast<T *>(smem);
-    const int act = A.state->active;
+    // without pair capacity the topology pattern is always the active one
+    const int act = PAIRS ? A.state->active : 0;
     const int32_t *rpa = A.pat.rp[act];
     const int32_t *cia = A.pat.ci[act];
-    const uint32_t *ib = A.pat.ib[act];
     int c0, c1;
     chunk_range(A.nchunk, c0, c1);
     double eacc = 0.0;
@@ -413,8 +500,8 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         const int pad = stage_pad<T>(int64_t(sb) * 9);
         T *Hs = stage + pad;
         if (fits && int(threadIdx.x) < nrows) {
-            const Row<T> r = load_row(A, rpa, v0 + int32_t(threadIdx.x), x);
-            eacc += eval_row<T, FACES>(A, act, cia, ib, r, sb, Hs, x, g);
+            const Row<T> r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
+            eacc += eval_row<T, FACES, PAIRS>(A, act, cia, r, sb, Hs, x, g);
         }
         wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
@@ -427,29 +514,31 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
 // Matrix-free Hessian-vector product, y_a = sum over the row's terms of
 // H_ab v_b, with the local Hessians formed in registers and never stored.
 // ---------------------------------------------------------------------------
-template <typename T, bool FACES>
+template <typename T, bool FACES, bool PAIRS>
 __global__ void __launch_bounds__(kRowThreads)
 k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
 {
-    const int act = A.state->active;
+    const int act = PAIRS ? A.state->active : 0;
     const int32_t *rpa = A.pat.rp[act];
-    const uint32_t *ib = A.pat.ib[act];
+    const int32_t *cia = A.pat.ci[act];
     int c0, c1;
     chunk_range(A.nchunk, c0, c1);
     for (int c = c0; c < c1; ++c) {
         const int32_t v0 = A.chunk[c].v0, nrows = A.chunk[c].nown;
         if (int(threadIdx.x) >= nrows) continue;
-        const Row<T> r = load_row(A, rpa, v0 + int32_t(threadIdx.x), x);
+        const Row<T> r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
         for (int k = 0; k < 3; ++k) va[k] = v[int64_t(r.a) * 3 + k];
+        PairPre<T> pp;
+        prefetch_pairs(A, act, r, x, pp);
         // Every term is evaluated once in DualHv numbers seeded with the
         // term's variables and the matching components of v; the gradient's
         // directional derivative gt is the term's Hessian applied to v.
-        int32_t nins = 0;
+        int32_t jb = r.kb0;
         for (int32_t base = r.s0; base < r.s1; base += kBatch) {
             SlotBatch<T> q;
-            load_batch(A, r, act, ib, base, nins, x, q);
+            load_batch(A, r, act, cia, base, jb, x, q);
             T vb[kBatch][3];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
@@ -516,26 +605,43 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
 #pragma unroll
             for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
         }
-        if (act != 0) {
-            const int32_t *pp = A.pat.pinc_ptr[act];
+        auto pair_hv = [&](const T xb[3], const T vb[3]) {
+            T dz[3];
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc) dz[cc] = r.xa[cc] - xb[cc];
+            const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
+            if (!(l2 < A.dhat * A.dhat)) return;
+            DualHv<T, 3> d[3];
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc) d[cc] = DualHv<T, 3>::var(dz[cc], cc, va[cc] - vb[cc]);
+            const DualHv<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc) Y[cc] += e.gt[cc];
+        };
+        {
+            T vp[kRowPairs][3];
+#pragma unroll
+            for (int k = 0; k < kRowPairs; ++k)
+#pragma unroll
+                for (int cc = 0; cc < 3; ++cc) vp[k][cc] = v[int64_t(pp.b[k]) * 3 + cc];
+#pragma unroll
+            for (int k = 0; k < kRowPairs; ++k)
+                if (k < pp.n) pair_hv(pp.xb[k], vp[k]);
+        }
+        if (r.p1 - r.p0 > kRowPairs) {
             const int32_t *pl = A.pat.pinc[act];
             const int32_t *prs = A.pat.pairs[act];
-            for (int32_t k = pp[r.a]; k < pp[r.a + 1]; ++k) {
+            for (int32_t k = r.p0 + kRowPairs; k < r.p1; ++k) {
                 const int32_t qp = pl[k];
                 const int32_t i0 = prs[2 * qp], i1 = prs[2 * qp + 1];
                 const int32_t b = i0 == r.a ? i1 : i0;
-                T dz[3];
+                T xb[3], vb[3];
 #pragma unroll
-                for (int cc = 0; cc < 3; ++cc) dz[cc] = r.xa[cc] - x[int64_t(b) * 3 + cc];
-                const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
-                if (!(l2 < A.dhat * A.dhat)) continue;
-                DualHv<T, 3> d[3];
-#pragma unroll
-                for (int cc = 0; cc < 3; ++cc)
-                    d[cc] = DualHv<T, 3>::var(dz[cc], cc, va[cc] - v[int64_t(b) * 3 + cc]);
-                const DualHv<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
-#pragma unroll
-                for (int cc = 0; cc < 3; ++cc) Y[cc] += e.gt[cc];
+                for (int cc = 0; cc < 3; ++cc) {
+                    xb[cc] = x[int64_t(b) * 3 + cc];
+                    vb[cc] = v[int64_t(b) * 3 + cc];
+                }
+                pair_hv(xb, vb);
             }
         }
 #pragma unroll
@@ -552,23 +658,32 @@ int rows_lds_bytes(int lds_blocks)
     return int(((int64_t(lds_blocks) * 9 * int64_t(sizeof(T)) + 16) + 15) & ~int64_t(15));
 }
 
+template <typename T, bool F, bool P>
+static hipError_t rows_occupancy(int lds, int *occ_e, int *occ_h)
+{
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_e, k_eval_rows<T, F, P>,
+                                                                kRowThreads, lds);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, P>, kRowThreads, 0);
+    return e;
+}
+
 template <typename T>
-hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int *grid_eval, int *grid_hvp)
+hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int pairs, int *grid_eval,
+                     int *grid_hvp)
 {
     int dev = 0, cus = 0, occ_e = 0, occ_h = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int lds = rows_lds_bytes<T>(lds_blocks);
-    if (e == hipSuccess)
-        e = faces ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_e, k_eval_rows<T, true>,
-                                                                  kRowThreads, lds)
-                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_e, k_eval_rows<T, false>,
-                                                                  kRowThreads, lds);
-    if (e == hipSuccess)
-        e = faces ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_h, k_hvp_rows<T, true>,
-                                                                  kRowThreads, 0)
-                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_h, k_hvp_rows<T, false>,
-                                                                  kRowThreads, 0);
+    if (e == hipSuccess) {
+        if (faces)
+            e = pairs ? rows_occupancy<T, true, true>(lds, &occ_e, &occ_h)
+                      : rows_occupancy<T, true, false>(lds, &occ_e, &occ_h);
+        else
+            e = pairs ? rows_occupancy<T, false, true>(lds, &occ_e, &occ_h)
+                      : rows_occupancy<T, false, false>(lds, &occ_e, &occ_h);
+    }
     if (e != hipSuccess) return e;
     auto clamp = [&](int occ) {
         const int64_t full = int64_t(cus > 0 ? cus : 1) * (occ > 0 ? occ : 1);
@@ -580,18 +695,33 @@ hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int *grid_eval, int 
     return hipSuccess;
 }
 
+template <typename T, bool F, bool P>
+static void launch_eval_rows_as(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
+                                int grid, int lds, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_eval_rows<T, F, P>), dim3(grid), dim3(kRowThreads), lds, s, a, x, g, hv,
+                       es);
+}
+
 template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s)
 {
     const int lds = rows_lds_bytes<T>(a.lds_blocks);
     if (a.faces_on)
-        hipLaunchKernelGGL((k_eval_rows<T, true>), dim3(grid), dim3(kRowThreads), lds, s, a, x, g,
-                           hv, es);
+        a.pairs_on ? launch_eval_rows_as<T, true, true>(a, x, g, hv, es, grid, lds, s)
+                   : launch_eval_rows_as<T, true, false>(a, x, g, hv, es, grid, lds, s);
     else
-        hipLaunchKernelGGL((k_eval_rows<T, false>), dim3(grid), dim3(kRowThreads), lds, s, a, x,
-                           g, hv, es);
+        a.pairs_on ? launch_eval_rows_as<T, false, true>(a, x, g, hv, es, grid, lds, s)
+                   : launch_eval_rows_as<T, false, false>(a, x, g, hv, es, grid, lds, s);
     return hipGetLastError();
+}
+
+template <typename T, bool F, bool P>
+static void launch_hvp_rows_as(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
+                               hipStream_t s)
+{
+    hipLaunchKernelGGL((k_hvp_rows<T, F, P>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v, y);
 }
 
 template <typename T>
@@ -599,16 +729,17 @@ hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, in
                            hipStream_t s)
 {
     if (a.faces_on)
-        hipLaunchKernelGGL((k_hvp_rows<T, true>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v, y);
+        a.pairs_on ? launch_hvp_rows_as<T, true, true>(a, x, v, y, grid, s)
+                   : launch_hvp_rows_as<T, true, false>(a, x, v, y, grid, s);
     else
-        hipLaunchKernelGGL((k_hvp_rows<T, false>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v,
-                           y);
+        a.pairs_on ? launch_hvp_rows_as<T, false, true>(a, x, v, y, grid, s)
+                   : launch_hvp_rows_as<T, false, false>(a, x, v, y, grid, s);
     return hipGetLastError();
 }
 
 #define LAD_ROWS_INST(T)                                                                          \
     template int rows_lds_bytes<T>(int);                                                          \
-    template hipError_t rows_grid<T>(int, int, int, int *, int *);                                \
+    template hipError_t rows_grid<T>(int, int, int, int, int *, int *);                           \
     template hipError_t launch_eval_rows<T>(const RowArgs<T> &, const T *, T *, T *, EnergySink,  \
                                             int, hipStream_t);                                    \
     template hipError_t launch_hvp_rows<T>(const RowArgs<T> &, const T *, const T *, T *, int,    \
