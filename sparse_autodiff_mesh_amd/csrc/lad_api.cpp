@@ -454,7 +454,8 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         }
         if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.cnt, size_t(nv));
         if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.cnt, 0, size_t(nv) * 4, s);
-        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.newlen, size_t(nv));
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.nnew, size_t(nv));
+        if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.nnew, 0, size_t(nv) * 4, s);
         if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.tmp, size_t(scan_tmp_size(nv)));
         for (int b = 1; b <= 2; ++b) {
             ctx->pat.rp[b] = ctx->ins.rp[b];

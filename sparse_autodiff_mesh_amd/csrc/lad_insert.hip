@@ -16,8 +16,8 @@
 
 namespace lad {
 
-hipError_t launch_scan_back(const int32_t *in, int32_t *const out[3], const DevState *st,
-                            int32_t n, int32_t *tmp, hipStream_t s);
+hipError_t launch_scan_back(const int32_t *in, int32_t *const out[3], const int32_t *add,
+                            const DevState *st, int32_t n, int32_t *tmp, hipStream_t s);
 
 namespace {
 
@@ -69,90 +69,121 @@ __device__ __forceinline__ int32_t lower_bound(const int32_t *c, int32_t lo, int
     return lo;
 }
 
-// Per row: order its pairs by pair id (fixed evaluation order), collect the
-// distinct partners that are not already in the topology row (sorted, into
-// pnew at the row's incidence offset) and emit the new row length.
+// Per row that has pairs (one thread per incidence entry; the row's first
+// entry does the work): order the row's pairs by pair id (fixed evaluation
+// order), collect the distinct partners that are not already in the
+// topology row (sorted, into pnew at the row's incidence offset) and store
+// their number in nnew[row].  nnew is zero for every other row.
+// Only the first pinc_ptr[nv] entries were filled (pairs that failed the
+// device check have none), so threads past that stop before reading.
 __global__ void __launch_bounds__(kThreads)
-k_ins_rows(const DevState *st, int32_t nv, InsertBufs b)
+k_ins_rows(const DevState *st, int32_t nent, int32_t nv, InsertBufs b)
 {
-    const int32_t a = blockIdx.x * kThreads + threadIdx.x;
-    if (a >= nv) return;
+    const int32_t k = blockIdx.x * kThreads + threadIdx.x;
+    if (k >= nent) return;
     const int bk = back_of(st);
-    const int32_t rb0 = b.rp[0][a], rb1 = b.rp[0][a + 1];
+    if (k >= b.pinc_ptr[bk][nv]) return;
+    const int32_t a = b.pinc_row[bk][k];
+    if (a < 0 || a >= nv) return;
     const int32_t p0 = b.pinc_ptr[bk][a], p1 = b.pinc_ptr[bk][a + 1];
-    int32_t len = rb1 - rb0;
-    if (p1 > p0) {
-        int32_t *pl = b.pinc[bk];
-        for (int32_t i = p0 + 1; i < p1; ++i) {
-            const int32_t key = pl[i];
-            int32_t j = i - 1;
-            while (j >= p0 && pl[j] > key) {
-                pl[j + 1] = pl[j];
-                --j;
-            }
-            pl[j + 1] = key;
-        }
-        const int32_t *prs = b.pairs[bk];
-        int32_t *pn = b.pnew[bk] + p0;
-        int32_t nn = 0;
-        for (int32_t k = p0; k < p1; ++k) {
-            const int32_t q = pl[k];
-            const int32_t other = prs[2 * q] == a ? prs[2 * q + 1] : prs[2 * q];
-            const int32_t pos = lower_bound(b.ci[0], rb0, rb1, other);
-            if (pos < rb1 && b.ci[0][pos] == other) continue;
-            bool dup = false;
-            for (int32_t m = 0; m < nn; ++m) dup |= pn[m] == other;
-            if (!dup) pn[nn++] = other;
-        }
-        for (int32_t i = 1; i < nn; ++i) {
-            const int32_t key = pn[i];
-            int32_t j = i - 1;
-            while (j >= 0 && pn[j] > key) {
-                pn[j + 1] = pn[j];
-                --j;
-            }
-            pn[j + 1] = key;
-        }
-        len += nn;
-    }
-    b.newlen[a] = len;
-}
-
-// Merge the topology row with the row's new partners into the back buffer.
-__global__ void __launch_bounds__(kThreads) k_ins_merge(const DevState *st, int32_t nv, InsertBufs b)
-{
-    const int32_t a = blockIdx.x * kThreads + threadIdx.x;
-    if (a >= nv) return;
-    const int bk = back_of(st);
-    const int32_t *cb = b.ci[0];
+    if (k != p0) return;
     const int32_t rb0 = b.rp[0][a], rb1 = b.rp[0][a + 1];
-    const int32_t o0 = b.rp[bk][a], o1 = b.rp[bk][a + 1];
-    const int32_t nn = (o1 - o0) - (rb1 - rb0);
-    int32_t *out = b.ci[bk];
-    if (nn == 0) {
-        for (int32_t k = 0; k < rb1 - rb0; ++k) out[o0 + k] = cb[rb0 + k];
-        return;
+    int32_t *pl = b.pinc[bk];
+    for (int32_t i = p0 + 1; i < p1; ++i) {
+        const int32_t key = pl[i];
+        int32_t j = i - 1;
+        while (j >= p0 && pl[j] > key) {
+            pl[j + 1] = pl[j];
+            --j;
+        }
+        pl[j + 1] = key;
     }
-    const int32_t *pn = b.pnew[bk] + b.pinc_ptr[bk][a];
-    int32_t i = rb0, m = 0, o = o0;
-    while (o < o1) {
-        if (m >= nn && i >= rb1) break;
-        const bool take_new = m < nn && (i >= rb1 || pn[m] < cb[i]);
+    const int32_t *prs = b.pairs[bk];
+    int32_t *pn = b.pnew[bk] + p0;
+    int32_t nn = 0;
+    for (int32_t q0 = p0; q0 < p1; ++q0) {
+        const int32_t q = pl[q0];
+        const int32_t other = prs[2 * q] == a ? prs[2 * q + 1] : prs[2 * q];
+        const int32_t pos = lower_bound(b.ci[0], rb0, rb1, other);
+        if (pos < rb1 && b.ci[0][pos] == other) continue;
+        bool dup = false;
+        for (int32_t m = 0; m < nn; ++m) dup |= pn[m] == other;
+        if (!dup) pn[nn++] = other;
+    }
+    for (int32_t i = 1; i < nn; ++i) {
+        const int32_t key = pn[i];
+        int32_t j = i - 1;
+        while (j >= 0 && pn[j] > key) {
+            pn[j + 1] = pn[j];
+            --j;
+        }
+        pn[j + 1] = key;
+    }
+    b.nnew[a] = nn;
+}
+
+// One 64-thread workgroup (one wave) per row chunk or patch, walking its
+// rows 64 at a time.  For each group of rows the wave loads the topology
+// columns of the group into LDS with coalesced loads, every lane builds its
+// row of the new pattern in a second LDS buffer (a copy, or a merge with the
+// row's new partners, which also re-zeroes nnew), and the wave stores the
+// group's new columns with coalesced stores.  A group whose rows exceed the
+// staging buffers is merged row by row straight from and to global memory.
+// Finally the chunk's new block count is checked against its reserved
+// staging capacity.
+constexpr int kMergeThreads = 64;
+constexpr int kMergeStage = 512;   // ints per staging buffer
+
+__device__ __forceinline__ void merge_row(const int32_t *cb, int32_t len, const int32_t *pn,
+                                          int32_t nn, int32_t *out)
+{
+    int32_t i = 0, m = 0;
+    for (int32_t o = 0; o < len + nn; ++o) {
+        const bool take_new = m < nn && (i >= len || pn[m] < cb[i]);
         out[o] = take_new ? pn[m++] : cb[i++];
-        ++o;
     }
 }
 
-// Every patch must still fit its reserved LDS block map.
-__global__ void __launch_bounds__(kThreads)
-k_ins_check(DevState *st, const PatchHdr *__restrict__ hdr, int32_t npatch, InsertBufs b)
+__global__ void __launch_bounds__(kMergeThreads)
+k_ins_merge(DevState *st, const PatchHdr *__restrict__ hdr, InsertBufs b)
 {
-    const int32_t p = blockIdx.x * kThreads + threadIdx.x;
-    if (p >= npatch) return;
+    __shared__ int32_t inb[kMergeStage], outb[kMergeStage];
     const int bk = back_of(st);
-    const PatchHdr h = hdr[p];
-    const int32_t n = b.rp[bk][h.v0 + h.nown] - b.rp[bk][h.v0];
-    if (n > h.amap_cap) atomicOr(&st->err_cur, 2);
+    const PatchHdr h = hdr[blockIdx.x];
+    const int32_t *cb = b.ci[0];
+    const int32_t *rp0 = b.rp[0], *rpn = b.rp[bk];
+    int32_t *out = b.ci[bk];
+    const int lane = threadIdx.x;
+    for (int32_t g0 = h.v0; g0 < h.v0 + h.nown; g0 += kMergeThreads) {
+        const int32_t g1 = min(g0 + kMergeThreads, h.v0 + h.nown);
+        const int32_t sb = rp0[g0], se = rp0[g1], ob = rpn[g0], oe = rpn[g1];
+        const int32_t a = g0 + lane;
+        const bool mine = a < g1;
+        const int32_t rb0 = mine ? rp0[a] : 0, rb1 = mine ? rp0[a + 1] : 0;
+        const int32_t o0 = mine ? rpn[a] : 0, o1 = mine ? rpn[a + 1] : 0;
+        const int32_t len = rb1 - rb0, nn = (o1 - o0) - len;
+        const int32_t *pn = (mine && nn > 0) ? b.pnew[bk] + b.pinc_ptr[bk][a] : nullptr;
+        if (se - sb <= kMergeStage && oe - ob <= kMergeStage) {  // wave-uniform
+            for (int32_t k = lane; k < se - sb; k += kMergeThreads) inb[k] = cb[sb + k];
+            __syncthreads();
+            if (mine) {
+                if (nn == 0)
+                    for (int32_t k = 0; k < len; ++k) outb[o0 - ob + k] = inb[rb0 - sb + k];
+                else
+                    merge_row(inb + (rb0 - sb), len, pn, nn, outb + (o0 - ob));
+            }
+            __syncthreads();
+            for (int32_t k = lane; k < oe - ob; k += kMergeThreads) out[ob + k] = outb[k];
+            __syncthreads();
+        } else if (mine) {
+            if (nn == 0)
+                for (int32_t k = 0; k < len; ++k) out[o0 + k] = cb[rb0 + k];
+            else
+                merge_row(cb + rb0, len, pn, nn, out + o0);
+        }
+        if (mine && nn > 0) b.nnew[a] = 0;
+    }
+    if (lane == 0 && rpn[h.v0 + h.nown] - rpn[h.v0] > h.amap_cap) atomicOr(&st->err_cur, 2);
 }
 
 // Flip the active buffer if every check of this insert passed, else latch
@@ -182,15 +213,15 @@ hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32
 {
     hipLaunchKernelGGL(k_ins_count, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, d_pairs, np,
                        nv, b);
-    hipError_t e = launch_scan_back(b.cnt, b.pinc_ptr, st, nv, b.tmp, s);
+    hipError_t e = launch_scan_back(b.cnt, b.pinc_ptr, nullptr, st, nv, b.tmp, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_ins_fill, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, np, nv, b);
-    hipLaunchKernelGGL(k_ins_rows, dim3(blocks_for(nv)), dim3(kThreads), 0, s, st, nv, b);
-    e = launch_scan_back(b.newlen, b.rp, st, nv, b.tmp, s);
+    hipLaunchKernelGGL(k_ins_rows, dim3(blocks_for(2 * int64_t(np))), dim3(kThreads), 0, s, st,
+                       2 * np, nv, b);
+    // new row_ptr = topology row_ptr + prefix of the new blocks per row
+    e = launch_scan_back(b.nnew, b.rp, b.rp[0], st, nv, b.tmp, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ins_merge, dim3(blocks_for(nv)), dim3(kThreads), 0, s, st, nv, b);
-    hipLaunchKernelGGL(k_ins_check, dim3(blocks_for(npatch)), dim3(kThreads), 0, s, st, hdr,
-                       npatch, b);
+    hipLaunchKernelGGL(k_ins_merge, dim3(npatch), dim3(kMergeThreads), 0, s, st, hdr, b);
     hipLaunchKernelGGL(k_ins_commit, dim3(1), dim3(1), 0, s, st, np, nv, b);
     return hipGetLastError();
 }

@@ -265,7 +265,7 @@ struct InsertBufs {
     int32_t *pinc_row[3];
     int32_t *pnew[3];            // distinct new partners per row (scratch)
     int32_t *cnt;                // [nv], all zero between inserts
-    int32_t *newlen;             // [nv]
+    int32_t *nnew;               // [nv] new blocks per row, all zero between inserts
     int32_t *tmp;                // scan scratch
 };
 hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np,

@@ -90,15 +90,18 @@ __global__ void __launch_bounds__(kThreads) k_scan_down(const int32_t *__restric
     int run = before + block_exclusive_scan(s, wsum, tot);
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
-        if (base + k < n) o[base + k] = run;
+        if (base + k < n) o[base + k] = run + out.add(base + k);
         run += v[k];
     }
-    if (blockIdx.x == nb - 1 && threadIdx.x == kThreads - 1) o[n] = run;
+    if (blockIdx.x == nb - 1 && threadIdx.x == kThreads - 1) o[n] = run + out.add(n);
 }
 
+// Scan destinations: where the output goes, and what is added to each
+// element of it.
 struct DirectOut {
     int32_t *p;
     __device__ int32_t *get() const { return p; }
+    __device__ int32_t add(int64_t) const { return 0; }
 };
 
 // ---------------------------------------------------------------- pattern
@@ -205,16 +208,19 @@ hipError_t launch_scan(const int32_t *in, int32_t *out, int32_t n, int32_t *tmp,
     return scan_impl(in, DirectOut{out}, n, tmp, s);
 }
 
-// Scan whose output array is picked on the device (used by pair insertion).
+// Scan whose output array is picked on the device (used by pair insertion),
+// optionally plus a per-element addend.
 struct BackOut {
     int32_t *p[3];
+    const int32_t *addend;
     const DevState *st;
     __device__ int32_t *get() const { return p[st->active == 1 ? 2 : 1]; }
+    __device__ int32_t add(int64_t i) const { return addend ? addend[i] : 0; }
 };
-hipError_t launch_scan_back(const int32_t *in, int32_t *const out[3], const DevState *st,
-                            int32_t n, int32_t *tmp, hipStream_t s)
+hipError_t launch_scan_back(const int32_t *in, int32_t *const out[3], const int32_t *add,
+                            const DevState *st, int32_t n, int32_t *tmp, hipStream_t s)
 {
-    BackOut o{{out[0], out[1], out[2]}, st};
+    BackOut o{{out[0], out[1], out[2]}, add, st};
     return scan_impl(in, o, n, tmp, s);
 }
 
