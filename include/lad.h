@@ -132,6 +132,10 @@ typedef struct {
     int32_t active_buffer;      /* 0 = topology pattern, 1/2 = pair buffers    */
     int32_t eval_path;          /* LAD_PATH_PATCH or LAD_PATH_ROWS in use      */
     int32_t grid_eval;          /* workgroups of one evaluation launch         */
+    int64_t host_syncs;         /* host synchronisations made so far for this
+                                   context, this lad_get_info call included;
+                                   lad_eval_energy_grad_hess, lad_hvp and
+                                   lad_insert_pairs never add to it          */
 } lad_info;
 
 /*

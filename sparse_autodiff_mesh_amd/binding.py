@@ -64,7 +64,7 @@ class lad_info(ctypes.Structure):
         ("lds_bytes_hvp", ctypes.c_int32), ("spring_records", ctypes.c_int64),
         ("face_records", ctypes.c_int64), ("max_colors", ctypes.c_int32),
         ("active_buffer", ctypes.c_int32), ("eval_path", ctypes.c_int32),
-        ("grid_eval", ctypes.c_int32),
+        ("grid_eval", ctypes.c_int32), ("host_syncs", ctypes.c_int64),
     ]
 
 

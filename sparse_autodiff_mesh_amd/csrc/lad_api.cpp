@@ -30,6 +30,7 @@ struct lad_ctx {
     int64_t nspr_rec = 0, nfac_rec = 0;
     int32_t pair_blocks = 0;
     int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
+    int64_t host_syncs = 0;          // host synchronisations made for this context
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
     int32_t *d_fptr = nullptr;
@@ -68,6 +69,14 @@ lad_status fail(lad_ctx *ctx, lad_status s, const std::string &msg)
 lad_status hip_fail(lad_ctx *ctx, hipError_t e, const char *what)
 {
     return fail(ctx, LAD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Every host synchronisation the library makes for a context goes through
+// here, so lad_get_info can report how many there were.
+hipError_t host_sync(lad_ctx *ctx, hipStream_t s)
+{
+    if (ctx) ++ctx->host_syncs;
+    return hipStreamSynchronize(s);
 }
 
 template <typename T>
@@ -185,7 +194,7 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
         if (e == hipSuccess) e = upload(ctx, &ctx->d_finc, rplan.finc, s);
     }
     // lifetime of the host vectors: synchronise before they go out of scope
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     return e == hipSuccess ? LAD_OK : hip_fail(ctx, e, "upload of element constants");
 }
 
@@ -349,7 +358,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     std::vector<int32_t> h_rp(size_t(nv) + 1);
     if (e == hipSuccess)
         e = hipMemcpyAsync(h_rp.data(), d_rp0, h_rp.size() * 4, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) {
         free_temps();
         return hip_fail(ctx, e, "pattern build");
@@ -366,7 +375,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     std::vector<int32_t> h_ci(static_cast<size_t>(nnzb));
     if (e == hipSuccess && nnzb > 0)
         e = hipMemcpyAsync(h_ci.data(), d_ci0, h_ci.size() * 4, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     free_temps();
     if (e != hipSuccess) return hip_fail(ctx, e, "pattern compaction");
 
@@ -472,7 +481,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
                       size_t(std::max(ctx->npatch, ctx->grid_eval) + ctx->pair_blocks));
     if (e == hipSuccess && !ctx->row_mode && (ctx->lds_eval > 64 * 1024 || ctx->lds_hvp > 64 * 1024))
         e = raise_lds_limits(std::max(ctx->lds_eval, ctx->lds_hvp));
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "allocation of pattern buffers");
     return LAD_OK;
 }
@@ -507,7 +516,7 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     if (!ctx || !info) return fail(ctx, LAD_ERR_ARG, "ctx or info is NULL");
     DevState hs{};
     hipError_t e = hipMemcpyAsync(&hs, ctx->d_state, sizeof(hs), hipMemcpyDeviceToHost, ctx->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    if (e == hipSuccess) e = host_sync(ctx, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "lad_get_info");
     std::memset(info, 0, sizeof(*info));
     info->nv = ctx->nv;
@@ -525,6 +534,7 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     info->active_buffer = hs.active;
     info->eval_path = ctx->row_mode ? LAD_PATH_ROWS : LAD_PATH_PATCH;
     info->grid_eval = ctx->grid_eval;
+    info->host_syncs = ctx->host_syncs;
     return LAD_OK;
 }
 
@@ -535,7 +545,7 @@ lad_status lad_get_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nnzb,
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     DevState hs{};
     hipError_t e = hipMemcpyAsync(&hs, ctx->d_state, sizeof(hs), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lad_get_pattern");
     const int a = hs.active;
     if (a < 0 || a > 2) return fail(ctx, LAD_ERR_STATE, "corrupt device state");
@@ -557,7 +567,7 @@ lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
     hipError_t e = hipMemcpyAsync(d_row_ptr, rp, (size_t(ctx->nv) + 1) * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && *nnzb > 0)
         e = hipMemcpyAsync(d_col_idx, ci, size_t(*nnzb) * 4, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lad_copy_pattern");
     return LAD_OK;
 }
@@ -611,12 +621,12 @@ lad_status lad_device_status(lad_ctx *ctx, void *hip_stream, int32_t *status)
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     DevState hs{};
     hipError_t e = hipMemcpyAsync(&hs, ctx->d_state, sizeof(hs), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     const int32_t zero = 0;
     if (e == hipSuccess && hs.err_latched != 0)
         e = hipMemcpyAsync(reinterpret_cast<char *>(ctx->d_state) + offsetof(DevState, err_latched),
                            &zero, sizeof(zero), hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lad_device_status");
     *status = (hs.err_latched & 1) ? LAD_ERR_PAIRS : (hs.err_latched & 2) ? LAD_ERR_CAPACITY : LAD_OK;
     return LAD_OK;

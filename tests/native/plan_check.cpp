@@ -1,0 +1,326 @@
+// Host-only checks of the two evaluation plans built by lad_patch.cpp: the
+// patch plan (contiguous-row patches with ribbon vertices, per-patch element
+// records, colours) and the row plan (row chunks, per-block rest lengths,
+// per-row face incidence).  No GPU is touched.  Prints one line per failed
+// check and exits non-zero if any failed.
+#include <algorithm>
+#include <cstdio>
+#include <map>
+#include <random>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "lad_internal.h"
+
+using namespace lad;
+
+namespace {
+
+int g_fail = 0;
+#define CHECK(cond, ...)                                     \
+    do {                                                     \
+        if (!(cond)) {                                       \
+            ++g_fail;                                        \
+            if (g_fail < 40) {                               \
+                std::printf("FAIL %s:%d: ", __FILE__, __LINE__); \
+                std::printf(__VA_ARGS__);                    \
+                std::printf("\n");                           \
+            }                                                \
+        }                                                    \
+    } while (0)
+
+struct Mesh {
+    int32_t nv = 0;
+    std::vector<int32_t> faces, springs;
+    std::vector<double> rest;
+};
+
+void add_edge_springs(Mesh &m)
+{
+    std::set<std::pair<int32_t, int32_t>> e;
+    for (size_t f = 0; f * 3 < m.faces.size(); ++f)
+        for (int i = 0; i < 3; ++i) {
+            int32_t a = m.faces[3 * f + i], b = m.faces[3 * f + (i + 1) % 3];
+            e.insert({std::min(a, b), std::max(a, b)});
+        }
+    for (auto &p : e) {
+        m.springs.push_back(p.first);
+        m.springs.push_back(p.second);
+        m.rest.push_back(0.5 + 0.001 * double((p.first * 7 + p.second) % 100));
+    }
+}
+
+Mesh grid(int n)
+{
+    Mesh m;
+    m.nv = n * n;
+    for (int j = 0; j + 1 < n; ++j)
+        for (int i = 0; i + 1 < n; ++i) {
+            const int v = j * n + i;
+            m.faces.insert(m.faces.end(), {v, v + 1, v + n + 1, v, v + n + 1, v + n});
+        }
+    add_edge_springs(m);
+    return m;
+}
+
+// Irregular mesh: random triangles over a shuffled vertex numbering (rows of
+// very different lengths, far-apart column indices).
+Mesh random_mesh(int nv, int nf, unsigned seed)
+{
+    std::mt19937 rng(seed);
+    std::uniform_int_distribution<int> U(0, nv - 1);
+    Mesh m;
+    m.nv = nv;
+    for (int f = 0; f < nf; ++f) {
+        int a = U(rng), b = U(rng), c = U(rng);
+        if (a == b || b == c || a == c) continue;
+        m.faces.insert(m.faces.end(), {a, b, c});
+    }
+    add_edge_springs(m);
+    return m;
+}
+
+void pattern(const Mesh &m, std::vector<int32_t> &rp, std::vector<int32_t> &ci)
+{
+    std::vector<std::set<int32_t>> rows(m.nv);
+    for (int32_t v = 0; v < m.nv; ++v) rows[v].insert(v);
+    for (size_t f = 0; f * 3 < m.faces.size(); ++f)
+        for (int i = 0; i < 3; ++i)
+            for (int j = 0; j < 3; ++j) rows[m.faces[3 * f + i]].insert(m.faces[3 * f + j]);
+    for (size_t s = 0; s * 2 < m.springs.size(); ++s) {
+        rows[m.springs[2 * s]].insert(m.springs[2 * s + 1]);
+        rows[m.springs[2 * s + 1]].insert(m.springs[2 * s]);
+    }
+    rp.assign(m.nv + 1, 0);
+    ci.clear();
+    for (int32_t v = 0; v < m.nv; ++v) {
+        ci.insert(ci.end(), rows[v].begin(), rows[v].end());
+        rp[v + 1] = int32_t(ci.size());
+    }
+}
+
+int32_t slot_of(const std::vector<int32_t> &rp, const std::vector<int32_t> &ci, int32_t a, int32_t b)
+{
+    for (int32_t k = rp[a]; k < rp[a + 1]; ++k)
+        if (ci[k] == b) return k;
+    return -1;
+}
+
+PlanInput make_input(const Mesh &m, const std::vector<int32_t> &rp, const std::vector<int32_t> &ci,
+                     bool faces_on, int es, int budget)
+{
+    PlanInput in;
+    in.nv = m.nv;
+    in.nf = int32_t(m.faces.size() / 3);
+    in.faces = m.faces.data();
+    in.ns = int32_t(m.springs.size() / 2);
+    in.springs = m.springs.data();
+    in.face_energy = faces_on ? 1 : 0;
+    in.row_ptr = rp.data();
+    in.col_idx = ci.data();
+    in.elem_size = es;
+    in.lds_budget = budget;
+    return in;
+}
+
+void check_patch_plan(const Mesh &m, bool faces_on, int es, int budget, const char *tag)
+{
+    std::vector<int32_t> rp, ci;
+    pattern(m, rp, ci);
+    const PlanInput in = make_input(m, rp, ci, faces_on, es, budget);
+    Plan plan;
+    const std::string err = build_plan(in, plan);
+    CHECK(err.empty(), "%s: build_plan failed: %s", tag, err.c_str());
+    if (!err.empty()) return;
+    const int32_t np = int32_t(plan.hdr.size());
+    int32_t expect_v0 = 0;
+    std::vector<int> spr_seen(in.ns, 0), fac_seen(in.nf, 0);
+    for (int32_t p = 0; p < np; ++p) {
+        const PatchHdr &h = plan.hdr[p];
+        CHECK(h.v0 == expect_v0 && h.nown > 0, "%s: patch %d does not continue the rows", tag, p);
+        expect_v0 = h.v0 + h.nown;
+        CHECK(h.blk0 == rp[h.v0] && h.nblk == rp[h.v0 + h.nown] - rp[h.v0], "%s: patch %d block range", tag, p);
+        CHECK(h.lds_eval <= budget, "%s: patch %d LDS %d over budget %d", tag, p, h.lds_eval, budget);
+        CHECK(h.amap_cap >= h.nblk, "%s: patch %d map capacity", tag, p);
+        auto owned = [&](int32_t v) { return v >= h.v0 && v < h.v0 + h.nown; };
+        // ribbon = sorted non-owned columns of the owned rows
+        std::set<int32_t> rib_expect;
+        for (int32_t v = h.v0; v < h.v0 + h.nown; ++v)
+            for (int32_t k = rp[v]; k < rp[v + 1]; ++k)
+                if (!owned(ci[k])) rib_expect.insert(ci[k]);
+        std::vector<int32_t> rib(plan.rib.begin() + h.rib_off, plan.rib.begin() + h.rib_off + h.nrib);
+        CHECK(std::vector<int32_t>(rib_expect.begin(), rib_expect.end()) == rib, "%s: patch %d ribbon", tag, p);
+        auto global_of = [&](int l) { return l < h.nown ? h.v0 + l : rib[size_t(l - h.nown)]; };
+        for (int32_t v = h.v0; v < h.v0 + h.nown; ++v)
+            CHECK(plan.diag_rel[v] == slot_of(rp, ci, v, v) - h.blk0, "%s: diagonal slot of %d", tag, v);
+        // springs: exactly those touching an owned vertex, once each
+        std::set<int32_t> expect_s;
+        for (int32_t s = 0; s < in.ns; ++s)
+            if (owned(m.springs[2 * s]) || owned(m.springs[2 * s + 1])) expect_s.insert(s);
+        std::multiset<int32_t> got_s;
+        const int32_t *cb = plan.col_bounds.data() + h.col_off;
+        for (int32_t r = 0; r < h.nspr; ++r) {
+            const int32_t s = plan.spr_src[h.spr_off + r];
+            got_s.insert(s);
+            spr_seen[s] += 1;
+            const SpringRec rec = plan.spr[h.spr_off + r];
+            const int la = rec.lab & 0xFFFF, lb = rec.lab >> 16;
+            const int32_t a = m.springs[2 * s], b = m.springs[2 * s + 1];
+            CHECK(global_of(la) == a && global_of(lb) == b, "%s: spring %d local ids", tag, s);
+            const int32_t sab = owned(a) ? slot_of(rp, ci, a, b) - h.blk0 : kNone;
+            const int32_t sba = owned(b) ? slot_of(rp, ci, b, a) - h.blk0 : kNone;
+            CHECK(int32_t(rec.blk & 0xFFFF) == sab && int32_t(rec.blk >> 16) == sba, "%s: spring %d slots", tag, s);
+        }
+        CHECK(got_s.size() == expect_s.size() &&
+                  std::equal(expect_s.begin(), expect_s.end(), std::set<int32_t>(got_s.begin(), got_s.end()).begin()),
+              "%s: patch %d spring set", tag, p);
+        // colours: bounds monotone, no two springs of a colour share an owned vertex
+        for (int c = 0; c < h.nspr_col; ++c) {
+            CHECK(cb[c] <= cb[c + 1], "%s: colour bounds", tag);
+            std::set<int32_t> used;
+            for (int32_t r = cb[c]; r < cb[c + 1]; ++r) {
+                const int32_t s = plan.spr_src[h.spr_off + r];
+                for (int i = 0; i < 2; ++i) {
+                    const int32_t v = m.springs[2 * s + i];
+                    if (!owned(v)) continue;
+                    CHECK(!used.count(v), "%s: colour %d shares vertex %d", tag, c, v);
+                    used.insert(v);
+                }
+            }
+        }
+        if (h.nspr > 0) CHECK(cb[0] == 0 && cb[h.nspr_col] == h.nspr, "%s: colour bounds span", tag);
+        // faces
+        if (faces_on) {
+            const int32_t *fb = cb + (h.nspr_col ? h.nspr_col + 1 : 0);
+            std::set<int32_t> expect_f;
+            for (int32_t f = 0; f < in.nf; ++f)
+                for (int i = 0; i < 3; ++i)
+                    if (owned(m.faces[3 * f + i])) expect_f.insert(f);
+            CHECK(int32_t(expect_f.size()) == h.nfac, "%s: patch %d face count", tag, p);
+            for (int32_t r = 0; r < h.nfac; ++r) {
+                const int32_t f = plan.fac_src[h.fac_off + r];
+                fac_seen[f] += 1;
+                CHECK(expect_f.count(f), "%s: face %d not incident", tag, f);
+                const FaceRec &rec = plan.fac[h.fac_off + r];
+                for (int i = 0; i < 3; ++i) {
+                    const int32_t a = m.faces[3 * f + i];
+                    CHECK(global_of(rec.l[i]) == a, "%s: face %d local id", tag, f);
+                    for (int j = 0; j < 3; ++j) {
+                        const int32_t want = owned(a) ? slot_of(rp, ci, a, m.faces[3 * f + j]) - h.blk0 : kNone;
+                        CHECK(int32_t(rec.blk[3 * i + j]) == want, "%s: face %d block slot", tag, f);
+                    }
+                }
+            }
+            for (int c = 0; c < h.nfac_col; ++c) {
+                std::set<int32_t> used;
+                for (int32_t r = fb[c]; r < fb[c + 1]; ++r) {
+                    const int32_t f = plan.fac_src[h.fac_off + r];
+                    for (int i = 0; i < 3; ++i) {
+                        const int32_t v = m.faces[3 * f + i];
+                        if (!owned(v)) continue;
+                        CHECK(!used.count(v), "%s: face colour %d shares vertex %d", tag, c, v);
+                        used.insert(v);
+                    }
+                }
+            }
+        }
+    }
+    CHECK(expect_v0 == m.nv, "%s: patches do not cover the rows", tag);
+    // an element is evaluated by every patch that owns one of its vertices
+    for (int32_t s = 0; s < in.ns; ++s) {
+        std::set<int32_t> ps = {plan.vpatch[m.springs[2 * s]], plan.vpatch[m.springs[2 * s + 1]]};
+        CHECK(spr_seen[s] == int(ps.size()), "%s: spring %d evaluated %d times, owners %zu", tag, s, spr_seen[s], ps.size());
+    }
+    if (faces_on)
+        for (int32_t f = 0; f < in.nf; ++f) {
+            std::set<int32_t> ps;
+            for (int i = 0; i < 3; ++i) ps.insert(plan.vpatch[m.faces[3 * f + i]]);
+            CHECK(fac_seen[f] == int(ps.size()), "%s: face %d evaluated %d times", tag, f, fac_seen[f]);
+        }
+}
+
+void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
+{
+    std::vector<int32_t> rp, ci;
+    pattern(m, rp, ci);
+    const PlanInput in = make_input(m, rp, ci, faces_on, 4, 0);
+    RowPlan plan;
+    const std::string err = build_row_plan(in, m.rest.data(), plan);
+    CHECK(err.empty(), "%s: build_row_plan failed: %s", tag, err.c_str());
+    if (!err.empty()) return;
+    int32_t expect_v0 = 0;
+    for (const PatchHdr &h : plan.chunk) {
+        CHECK(h.v0 == expect_v0 && h.nown > 0 && h.nown <= kRowsPerChunk, "%s: chunk rows", tag);
+        CHECK(h.nblk == rp[h.v0 + h.nown] - rp[h.v0] && h.nblk <= kRowBaseBlocks, "%s: chunk blocks", tag);
+        CHECK(h.amap_cap == kRowLdsBlocks, "%s: chunk capacity", tag);
+        expect_v0 = h.v0 + h.nown;
+    }
+    CHECK(expect_v0 == m.nv, "%s: chunks do not cover the rows", tag);
+    std::vector<double> want(ci.size(), -1.0);
+    for (size_t s = 0; s * 2 < m.springs.size(); ++s) {
+        want[size_t(slot_of(rp, ci, m.springs[2 * s], m.springs[2 * s + 1]))] = m.rest[s];
+        want[size_t(slot_of(rp, ci, m.springs[2 * s + 1], m.springs[2 * s]))] = m.rest[s];
+    }
+    CHECK(plan.slot_rest == want, "%s: per-block rest lengths", tag);
+    if (!faces_on) return;
+    CHECK(int32_t(plan.fptr.size()) == m.nv + 1, "%s: face offsets size", tag);
+    std::vector<std::vector<int32_t>> inc(m.nv);
+    for (size_t f = 0; f * 3 < m.faces.size(); ++f)
+        for (int i = 0; i < 3; ++i) inc[m.faces[3 * f + i]].push_back(int32_t(f));
+    for (int32_t a = 0; a < m.nv; ++a) {
+        CHECK(plan.fptr[a + 1] - plan.fptr[a] == int32_t(inc[a].size()), "%s: row %d face count", tag, a);
+        for (int32_t k = plan.fptr[a]; k < plan.fptr[a + 1] && k - plan.fptr[a] < int32_t(inc[a].size()); ++k) {
+            const FaceInc &e = plan.finc[k];
+            const int32_t f = inc[a][size_t(k - plan.fptr[a])];
+            CHECK(e.f == f, "%s: row %d faces not in id order", tag, a);
+            const int i = int(e.pk & 3u);
+            const int32_t *t = m.faces.data() + 3 * f;
+            CHECK(i < 3 && t[i] == a && e.o1 == t[(i + 1) % 3] && e.o2 == t[(i + 2) % 3], "%s: row %d face %d vertices", tag, a, f);
+            for (int u = 0; u < 3; ++u)
+                CHECK(int32_t((e.pk >> (8 * u + 8)) & 255u) == slot_of(rp, ci, a, t[u]) - rp[a], "%s: row %d face %d slot", tag, a, f);
+        }
+    }
+}
+
+void check_row_plan_rejects()
+{
+    Mesh m = grid(6);
+    std::vector<int32_t> rp, ci;
+    RowPlan plan;
+    Mesh dup = m;  // the same spring twice
+    dup.springs.push_back(dup.springs[0]);
+    dup.springs.push_back(dup.springs[1]);
+    dup.rest.push_back(1.0);
+    pattern(dup, rp, ci);
+    CHECK(!build_row_plan(make_input(dup, rp, ci, false, 4, 0), dup.rest.data(), plan).empty(), "duplicate spring accepted");
+    Mesh neg = m;
+    neg.rest[3] = -0.5;
+    pattern(neg, rp, ci);
+    CHECK(!build_row_plan(make_input(neg, rp, ci, false, 4, 0), neg.rest.data(), plan).empty(), "negative rest length accepted");
+}
+
+}  // namespace
+
+int main()
+{
+    const Mesh g10 = grid(10), g37 = grid(37), g64 = grid(64);
+    const Mesh r1 = random_mesh(300, 700, 1), r2 = random_mesh(2000, 6000, 2);
+    check_patch_plan(g10, false, 8, 40 * 1024, "grid10");
+    check_patch_plan(g37, true, 4, 6144, "grid37 faces small patches");
+    check_patch_plan(g37, false, 8, 6144, "grid37 fp64 small patches");
+    check_patch_plan(g64, true, 4, 40 * 1024, "grid64 faces");
+    check_patch_plan(r1, true, 8, 8192, "random300 faces");
+    check_patch_plan(r2, true, 4, 16384, "random2000 faces");
+    check_row_plan(g10, false, "grid10 rows");
+    check_row_plan(g64, true, "grid64 rows faces");
+    check_row_plan(r1, true, "random300 rows faces");
+    check_row_plan(r2, false, "random2000 rows");
+    check_row_plan_rejects();
+    if (g_fail) {
+        std::printf("%d checks failed\n", g_fail);
+        return 1;
+    }
+    std::printf("all plan checks passed\n");
+    return 0;
+}

@@ -221,3 +221,59 @@ def test_eval_without_energy(lad, path):
     assert E2.item() == -7.0
     assert torch.equal(g1, g2) and torch.equal(H1[:n], H2[:n])
     L.close()
+
+
+@pytest.mark.parametrize("path,faces,det", [("patch", False, True), ("patch", True, True),
+                                            ("rows", True, False), ("rows", False, False)])
+def test_bitwise_reproducible(lad, path, faces, det):
+    """The deterministic patch mode (colour phases) and the row path sum in a
+    fixed order: ten evaluations and HVPs are bitwise identical."""
+    import torch
+    log_case(test="reproducible", path=path, faces=faces, det=det)
+    m = inputs.cloth(41)
+    L = lad.Lad(m.nv, dtype="f32", path=path, deterministic=det, patch_lds_bytes=6144,
+                **lad.mesh_terms(m, faces=faces))
+    x = dev(host_input(m.x, "f32"), "f32")
+    v = dev(host_input(inputs.hvp_direction(m.nv), "f32"), "f32")
+    E0, g0, H0 = L.eval(x)
+    y0 = L.hvp(x, v)
+    torch.cuda.synchronize()
+    E0, g0, H0, y0 = E0.clone(), g0.clone(), H0.clone(), y0.clone()
+    for _ in range(10):
+        E, g, H = L.eval(x)
+        y = L.hvp(x, v)
+        torch.cuda.synchronize()
+        assert torch.equal(E, E0) and torch.equal(g, g0) and torch.equal(H, H0)
+        assert torch.equal(y, y0)
+    L.close()
+
+
+@pytest.mark.parametrize("path", ["rows", "patch"])
+def test_no_host_sync_in_step_calls(lad, path):
+    """Evaluation, HVP and pair insertion never synchronise with the host: the
+    library's own count of host synchronisations grows only by the one that
+    the second lad_get_info makes."""
+    import torch
+    log_case(test="no_host_sync", path=path)
+    m = inputs.cloth(30)
+    P = 18
+    L = lad.Lad(m.nv, dtype="f32", path=path,
+                **lad.mesh_terms(m, pair_capacity=P, kappa=inputs.BARRIER_KAPPA, dhat=0.5 * m.h))
+    x = dev(host_input(m.x, "f32"), "f32")
+    v = dev(host_input(inputs.hvp_direction(m.nv), "f32"), "f32")
+    pairs, _ = inputs.contact_pairs(m, m.x, step=0)
+    pd = torch.tensor(pairs, dtype=torch.int32, device="cuda")
+    out = L.alloc_outputs()
+    s0 = L.get_info()["host_syncs"]
+    for _ in range(3):
+        L.eval(x, out=out)
+        L.eval(x, out=out, energy=False)
+        L.hvp(x, v)
+        L.insert_pairs(pd)
+        L.eval(x, out=out)
+        L.hvp(x, v)
+        L.insert_pairs(None)
+    s1 = L.get_info()["host_syncs"]
+    assert s1 - s0 == 1
+    torch.cuda.synchronize()
+    L.close()
