@@ -229,6 +229,7 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     RowArgs<T> a{};
     a.chunk = ctx->d_hdr;
     a.nchunk = ctx->npatch;
+    a.nv = ctx->nv;
     a.rp0 = ctx->pat.rp[0];
     a.ci0 = ctx->pat.ci[0];
     a.slot_rest = static_cast<const T *>(ctx->d_slot_rest);

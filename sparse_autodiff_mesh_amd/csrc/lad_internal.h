@@ -191,6 +191,7 @@ template <typename T>
 struct RowArgs {
     const PatchHdr *chunk;       // row chunks: v0, nown (rows), amap_cap (blocks)
     int32_t nchunk;
+    int32_t nv;                  // rows
     const int32_t *rp0, *ci0;    // topology pattern
     const T *slot_rest;          // [nnzb_base] rest length of the spring behind
                                  // each block (< 0: no spring)

@@ -80,7 +80,9 @@ struct Row {
 };
 
 // Row header loads, all independent of each other.
-template <typename T>
+// With WITH_XT = false the inertial target is not loaded (the HVP needs
+// only the inertia term's Hessian, which does not depend on it).
+template <typename T, bool WITH_XT = true>
 __device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, int act, const int32_t *rpa,
                                            int32_t a, const T *__restrict__ x)
 {
@@ -97,7 +99,7 @@ __device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, int act, const i
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         r.xa[k] = x[int64_t(a) * 3 + k];
-        r.xt[k] = A.inertia_on ? A.x_tilde[int64_t(a) * 3 + k] : T(0);
+        r.xt[k] = (WITH_XT && A.inertia_on) ? A.x_tilde[int64_t(a) * 3 + k] : r.xa[k];
     }
     return r;
 }
@@ -521,15 +523,33 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     const int act = PAIRS ? A.state->active : 0;
     const int32_t *rpa = A.pat.rp[act];
     const int32_t *cia = A.pat.ci[act];
-    int c0, c1;
-    chunk_range(A.nchunk, c0, c1);
-    for (int c = c0; c < c1; ++c) {
-        const int32_t v0 = A.chunk[c].v0, nrows = A.chunk[c].nown;
-        if (int(threadIdx.x) >= nrows) continue;
-        const Row<T> r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
+    // Nothing is staged here, so a workgroup takes a contiguous row range
+    // (ranges grouped by XCD) and walks it 64 rows at a time.  The row
+    // header, position and direction of the next group are loaded while the
+    // current group is processed, which takes one dependent load level off
+    // every group.
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
+    const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
+    int32_t an = r0 + int32_t(threadIdx.x);
+    Row<T> rn;
+    T vn[3];
+    if (an < r1) {
+        rn = load_row<T, false>(A, act, rpa, an, x);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) vn[k] = v[int64_t(an) * 3 + k];
+    }
+    for (; an < r1;) {
+        const Row<T> r = rn;
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
-        for (int k = 0; k < 3; ++k) va[k] = v[int64_t(r.a) * 3 + k];
+        for (int k = 0; k < 3; ++k) va[k] = vn[k];
+        an += kRowThreads;
+        if (an < r1) {
+            rn = load_row<T, false>(A, act, rpa, an, x);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) vn[k] = v[int64_t(an) * 3 + k];
+        }
         PairPre<T> pp;
         prefetch_pairs(A, act, r, x, pp);
         // Every term is evaluated once in DualHv numbers seeded with the
@@ -598,6 +618,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             }
         }
         if (A.inertia_on) {
+            // seeded at z = 0 (x_tilde not loaded): the Hessian c I is the same
             DualHv<T, 3> z[3];
 #pragma unroll
             for (int k = 0; k < 3; ++k) z[k] = DualHv<T, 3>::var(r.xa[k] - r.xt[k], k, va[k]);
