@@ -120,8 +120,9 @@ struct SlotBatch {
 // row's own vertex), so all loads of the batch are issued back to back and
 // only the arithmetic that consumes them is predicated.
 //
-// Topology pattern active (act == 0): active slot s is topology slot
-// kb0 + (s - s0).  Pairs active: the active row is the topology row with
+// Topology pattern active (act == 0), or a row that no current pair
+// touches (its active row is its topology row): active slot s is topology
+// slot kb0 + (s - s0).  Otherwise the active row is the topology row with
 // the pairs' new columns merged in, both sorted, so a slot is inserted
 // exactly when its column is not in the topology row.  The batch then loads
 // the active columns and a window of kBatch topology columns starting at
@@ -133,7 +134,7 @@ __device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r,
                                            const int32_t *cia, int32_t base, int32_t &jb,
                                            const T *__restrict__ x, SlotBatch<T> &q)
 {
-    if (act == 0) {  // wave-uniform
+    if (act == 0 || r.p1 == r.p0) {  // uniform in a wave with no pair rows
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) q.kb[j] = base + j < r.s1 ? r.kb0 + (base + j - r.s0) : -1;
 #pragma unroll
@@ -206,7 +207,7 @@ __device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, con
 #pragma unroll
         for (int c = 0; c < 3; ++c) pp.xb[k][c] = r.xa[c];
     }
-    if (act == 0) return;  // wave-uniform
+    if (act == 0 || r.p1 == r.p0) return;
     const int32_t *pl = A.pat.pinc[act];
     const int32_t *prs = A.pat.pairs[act];
     pp.n = min(r.p1 - r.p0, kRowPairs);
@@ -401,10 +402,11 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
                     for (int k = 0; k < 9; ++k) D[k] += Bu[k];
                 } else {
                     // block of face vertex u in this row: its topology slot,
-                    // or (pairs active) its column's position in the active row
+                    // or (a row that a pair touches) its column's position in the active row
                     const int32_t vu = u == (i + 1) % 3 ? fe.o1 : fe.o2;
                     const int32_t off = int32_t((fe.pk >> (8 * u + 8)) & 255u);
-                    const int32_t sl = act == 0 ? r.s0 + off : find_slot(cia, r.s0, r.s1, vu);
+                    const int32_t sl = (act == 0 || r.p1 == r.p0) ? r.s0 + off
+                                                                  : find_slot(cia, r.s0, r.s1, vu);
                     T *B = Hs + 9 * (sl - sb);
 #pragma unroll
                     for (int k = 0; k < 9; ++k) B[k] += Bu[k];
