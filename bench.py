@@ -71,6 +71,13 @@ def compulsory_bytes_hvp(nv, ns, nf, es, faces=False):
     return b
 
 
+def compulsory_bytes_cg_iter(nv, ns, es):
+    """One Newton-CG iteration: the HVP, then p, r updated from d, y (four
+    vectors read, two written) and the new direction (two read, one
+    written); the scalar kernels move a few KB."""
+    return compulsory_bytes_hvp(nv, ns, 0, es) + 9 * 3 * nv * es
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_autodiff_mesh_amd", "csrc")
@@ -219,6 +226,26 @@ def bench_secondary(torch, binding, inputs, args, timer):
     bh = compulsory_bytes_hvp(mc.nv, mc.springs.shape[0], 0, 4)
     sec["cloth1000_hvp_ms"] = round(r["median_ms"], 5)
     sec["cloth1000_hvp_GBps"] = round(bh / (r["median_ms"] * 1e-3) / 1e9, 1)
+    # same context, cloth displaced 0.002 h from rest (H positive definite):
+    # Newton-CG direction, a fixed number of iterations per call
+    zc = inputs.gaussian_block(11, mc.X.size).reshape(mc.X.shape)
+    xs = to_dev(torch, mc.X + 0.002 * mc.h * zc, "f32")
+    _, gs, _ = L.eval(xs)
+    ps = torch.empty_like(gs)
+    its = 32
+    stats = {}
+
+    def cg_fn():
+        stats.update(L.newton_cg(xs, gs, out=ps, max_iters=its, eta=1e-12)[1])
+
+    r = timer.run(cg_fn, max(5, steps // 5), 2)
+    if stats["iterations"] != its:
+        raise RuntimeError(f"Newton-CG stopped early: {stats}")
+    bcg = compulsory_bytes_cg_iter(mc.nv, mc.springs.shape[0], 4)
+    sec["cloth1000_newton_cg_iters"] = its
+    sec["cloth1000_newton_cg_ms_per_iter"] = round(r["median_ms"] / its, 5)
+    sec["cloth1000_newton_cg_GBps"] = round(bcg * its / (r["median_ms"] * 1e-3) / 1e9, 1)
+    sec["cloth1000_newton_cg_rel_residual"] = float(f"{stats['rel_residual']:.3e}")
     L.close()
     # 512 x 512 symmetric-Dirichlet face grid, fp32: explicit eval and HVP
     f = inputs.face_grid(512)

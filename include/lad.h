@@ -209,6 +209,47 @@ lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x,
 lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y,
                    void *hip_stream);
 
+/* Why a Newton-CG solve ended (lad_cg_stats.reason). */
+enum { LAD_CG_CONVERGED = 0, LAD_CG_NEG_CURVATURE = 1, LAD_CG_MAX_ITERS = 2 };
+
+typedef struct {
+    int32_t iterations;   /* completed CG updates                                */
+    int32_t reason;       /* LAD_CG_CONVERGED, LAD_CG_NEG_CURVATURE or
+                             LAD_CG_MAX_ITERS                                    */
+    double rel_residual;  /* |r| / |g| of the last residual (r = H p + g for the
+                             returned p, except after a first-step negative
+                             curvature exit, where p = -g and this is 1)      */
+    double grad_norm;     /* |g|                                                 */
+} lad_cg_stats;
+
+/*
+ * Newton direction by truncated conjugate gradients on the matrix-free HVP:
+ * approximately solves H(x) p = -g from p = 0 (line-search Newton-CG,
+ * Nocedal and Wright, Numerical Optimization, 2nd ed., Algorithm 7.1).
+ * Stops when |r| < eps (r = H p + g), returning p; at the first CG
+ * direction d with d.H d <= 0, returning -g if that is the first direction
+ * and the current p otherwise (a descent direction either way); or after
+ * max_iters updates, returning the current p.  eps = eta |g| for eta > 0,
+ * else min(0.5, sqrt|g|) |g| (that algorithm's forcing term).  The page
+ * "Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+ * Computations" presents fast Hessian-vector products as what makes such
+ * Newton-type methods practical on large meshes; it fixes no solver.
+ *   d_x, d_g  device [nv][3] dtype, read only (g is usually the gradient
+ *             from lad_eval_energy_grad_hess at the same x).
+ *   d_p       device [nv][3] dtype, fully overwritten; must not alias d_g.
+ *   max_iters >= 0; stats: host pointer, or NULL.
+ * Dot products are accumulated in fp64 in a fixed order (bitwise
+ * reproducible); vector updates are computed in fp64 and rounded to the
+ * dtype.  The first call allocates per-context work vectors (4 [nv][3]
+ * arrays and a few KB), kept until lad_destroy.  Synchronises `hip_stream`
+ * after every 8 iterations (to stop early) and at the end.  Errors:
+ * LAD_ERR_ARG (NULL x, g or p, p == g, max_iters < 0), LAD_ERR_OOM,
+ * LAD_ERR_HIP.
+ */
+lad_status lad_newton_cg(lad_ctx *ctx, const void *d_x, const void *d_g, void *d_p,
+                         int32_t max_iters, double eta, lad_cg_stats *stats,
+                         void *hip_stream);
+
 /*
  * Replace the runtime vertex-vertex pairs: the next pattern is
  * topology U {(i,j),(j,i) for every pair}, sorted and de-duplicated; the

@@ -68,9 +68,18 @@ class lad_info(ctypes.Structure):
     ]
 
 
+class lad_cg_stats(ctypes.Structure):
+    _fields_ = [
+        ("iterations", ctypes.c_int32), ("reason", ctypes.c_int32),
+        ("rel_residual", ctypes.c_double), ("grad_norm", ctypes.c_double),
+    ]
+
+
+LAD_CG_CONVERGED, LAD_CG_NEG_CURVATURE, LAD_CG_MAX_ITERS = 0, 1, 2
+
 EXPORTS = [
     "lad_build_pattern", "lad_get_info", "lad_get_pattern", "lad_copy_pattern",
-    "lad_eval_energy_grad_hess", "lad_hvp", "lad_insert_pairs",
+    "lad_eval_energy_grad_hess", "lad_hvp", "lad_newton_cg", "lad_insert_pairs",
     "lad_device_status", "lad_last_error", "lad_status_string", "lad_destroy",
 ]
 
@@ -95,6 +104,8 @@ def lib():
         L.lad_eval_energy_grad_hess.argtypes = [_vp, _vp, _vp, _vp, _vp,
                                                 ctypes.c_int64, _vp]
         L.lad_hvp.argtypes = [_vp, _vp, _vp, _vp, _vp]
+        L.lad_newton_cg.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_double,
+                                    ctypes.POINTER(lad_cg_stats), _vp]
         L.lad_insert_pairs.argtypes = [_vp, _vp, ctypes.c_int32, _vp]
         L.lad_device_status.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]
         L.lad_last_error.argtypes = [_vp]
@@ -159,6 +170,13 @@ def lad_eval_energy_grad_hess(ctx, d_x, d_energy, d_grad, d_hvals, capacity, str
 
 def lad_hvp(ctx, d_x, d_v, d_y, stream=None):
     _check(lib().lad_hvp(ctx, _vp(d_x), _vp(d_v), _vp(d_y), _vp(stream)), ctx)
+
+
+def lad_newton_cg(ctx, d_x, d_g, d_p, max_iters, eta=0.0, stream=None) -> dict:
+    st = lad_cg_stats()
+    _check(lib().lad_newton_cg(ctx, _vp(d_x), _vp(d_g), _vp(d_p), int(max_iters), float(eta),
+                               ctypes.byref(st), _vp(stream)), ctx)
+    return {name: getattr(st, name) for name, _ in lad_cg_stats._fields_}
 
 
 def lad_insert_pairs(ctx, d_pairs, npairs, stream=None):
@@ -276,6 +294,15 @@ class Lad:
         y = out if out is not None else self.torch.empty_like(v)
         lad_hvp(self.ctx, x.data_ptr(), v.data_ptr(), y.data_ptr(), _stream())
         return y
+
+    def newton_cg(self, x, g, out=None, max_iters=100, eta=0.0):
+        """Truncated Newton-CG direction p (H(x) p ~ -g); returns (p, stats)."""
+        assert x.dtype == self.dtype and g.dtype == self.dtype
+        assert x.is_contiguous() and g.is_contiguous()
+        p = out if out is not None else self.torch.empty_like(g)
+        stats = lad_newton_cg(self.ctx, x.data_ptr(), g.data_ptr(), p.data_ptr(), max_iters,
+                              eta, _stream())
+        return p, stats
 
     def insert_pairs(self, pairs):
         """pairs: int32 cuda tensor (P, 2), or None / empty for no pairs."""

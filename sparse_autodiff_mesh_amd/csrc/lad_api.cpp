@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "lad_internal.h"
+#include "lad_solve.h"
 
 #include <algorithm>
 
@@ -52,6 +53,12 @@ struct lad_ctx {
     double *d_epart = nullptr;
     PatternBufs pat{};
     InsertBufs ins{};
+    // Newton-CG work space, allocated by the first lad_newton_cg call
+    void *cg_r = nullptr, *cg_d = nullptr, *cg_y = nullptr;
+    double *cg_parts = nullptr;
+    int32_t cg_nparts = 0;
+    CgState *d_cg = nullptr;
+    CgState *h_cg = nullptr;         // pinned host copy
     std::string err;
 };
 
@@ -95,6 +102,8 @@ void free_all(lad_ctx *ctx)
 {
     for (void *p : ctx->allocs) (void)hipFree(p);
     ctx->allocs.clear();
+    if (ctx->h_cg) (void)hipHostFree(ctx->h_cg);
+    ctx->h_cg = nullptr;
 }
 
 std::string check_desc(const lad_mesh_desc *d)
@@ -282,12 +291,8 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
 }
 
 template <typename T>
-hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s)
+hipError_t enqueue_hvp_patch(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s)
 {
-    if (ctx->row_mode)
-        return launch_hvp_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
-                                  static_cast<const T *>(v), static_cast<T *>(y), ctx->grid_hvp,
-                                  s);
     const PatchArgs<T> a = patch_args<T>(ctx);
     hipError_t e = launch_hvp<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
                                  static_cast<T *>(y), ctx->det, ctx->lds_hvp, s);
@@ -295,6 +300,105 @@ hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipS
         e = launch_pairs_hvp<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
                                 static_cast<const T *>(v), static_cast<T *>(y), ctx->pair_blocks,
                                 T(ctx->kappa), T(ctx->dhat), s);
+    return e;
+}
+
+// y = H v, optionally with per-workgroup partial sums of v.y (row path;
+// *dot_parts_used gets their number, 0 when the caller must compute v.y
+// itself) and an early exit while *skip != 0 (row path).
+template <typename T>
+hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s,
+                       double *dot_parts = nullptr, int32_t *dot_parts_used = nullptr,
+                       const int32_t *skip = nullptr)
+{
+    if (dot_parts_used) *dot_parts_used = 0;
+    if (ctx->row_mode) {
+        RowArgs<T> a = row_args<T>(ctx);
+        a.hvp_dot = dot_parts;
+        a.hvp_skip = skip;
+        if (dot_parts_used && dot_parts) *dot_parts_used = ctx->grid_hvp;
+        return launch_hvp_rows<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
+                                  static_cast<T *>(y), ctx->grid_hvp, s);
+    }
+    return enqueue_hvp_patch<T>(ctx, x, v, y, s);
+}
+
+// Iterations enqueued between two host reads of the solve's stop flag.
+constexpr int32_t kCgCheck = 8;
+
+hipError_t cg_workspace(lad_ctx *ctx)
+{
+    if (ctx->d_cg) return hipSuccess;
+    const size_t n = size_t(ctx->nv) * 3;
+    const size_t bytes = n * size_t(ctx->es);
+    char *r = nullptr, *d = nullptr, *y = nullptr;
+    hipError_t e = dev_alloc(ctx, &r, bytes);
+    if (e == hipSuccess) e = dev_alloc(ctx, &d, bytes);
+    if (e == hipSuccess) e = dev_alloc(ctx, &y, bytes);
+    const int32_t np = std::max<int32_t>(kCgMaxGrid, ctx->grid_hvp);
+    double *parts = nullptr;
+    if (e == hipSuccess) e = dev_alloc(ctx, &parts, size_t(np));
+    CgState *st = nullptr;
+    if (e == hipSuccess) e = dev_alloc(ctx, &st, 1);
+    CgState *h = nullptr;
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void **>(&h), sizeof(CgState));
+    if (e != hipSuccess) return e;
+    ctx->cg_r = r;
+    ctx->cg_d = d;
+    ctx->cg_y = y;
+    ctx->cg_parts = parts;
+    ctx->cg_nparts = np;
+    ctx->d_cg = st;
+    ctx->h_cg = h;
+    return hipSuccess;
+}
+
+// Truncated Newton-CG (line-search Newton-CG, Nocedal and Wright,
+// Algorithm 7.1): per iteration y = H d with the partial sums of d.y (fused
+// into the row HVP), alpha, p and r updates with the partial sums of r.r,
+// beta, and the new direction.  All scalars stay on the device; the host
+// reads the stop flag every kCgCheck iterations and the final state.
+template <typename T>
+hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *pv,
+                             int32_t max_iters, double eta, hipStream_t s)
+{
+    hipError_t e = cg_workspace(ctx);
+    if (e != hipSuccess) return e;
+    const int64_t n = int64_t(ctx->nv) * 3;
+    const int grid = cg_vec_grid(n);
+    const T *g = static_cast<const T *>(gv);
+    T *p = static_cast<T *>(pv);
+    T *r = static_cast<T *>(ctx->cg_r), *d = static_cast<T *>(ctx->cg_d),
+      *y = static_cast<T *>(ctx->cg_y);
+    CgState *st = ctx->d_cg;
+    const int32_t *stop = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(st) +
+                                                            offsetof(CgState, stop));
+    e = launch_cg_init<T>(g, p, r, d, n, ctx->cg_parts, grid, s);
+    if (e == hipSuccess) e = launch_cg_start(ctx->cg_parts, grid, st, eta, max_iters, s);
+    for (int32_t done = 0; e == hipSuccess && done < max_iters;) {
+        const int32_t nb = std::min(kCgCheck, max_iters - done);
+        for (int32_t it = 0; it < nb && e == hipSuccess; ++it) {
+            int32_t nparts = 0;
+            e = enqueue_hvp<T>(ctx, x, d, y, s, ctx->cg_parts, &nparts, stop);
+            if (e == hipSuccess && nparts == 0) {
+                nparts = grid;
+                e = launch_cg_dot<T>(d, y, n, ctx->cg_parts, grid, st, s);
+            }
+            if (e == hipSuccess) e = launch_cg_alpha(ctx->cg_parts, nparts, st, s);
+            if (e == hipSuccess) e = launch_cg_update<T>(p, r, d, y, n, ctx->cg_parts, grid, st, s);
+            if (e == hipSuccess) e = launch_cg_beta(ctx->cg_parts, grid, st, max_iters, s);
+            if (e == hipSuccess) e = launch_cg_dir<T>(r, d, n, grid, st, s);
+        }
+        done += nb;
+        if (e == hipSuccess && done < max_iters) {
+            e = hipMemcpyAsync(ctx->h_cg, st, sizeof(CgState), hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess) e = host_sync(ctx, s);
+            if (e == hipSuccess && ctx->h_cg->stop) break;
+        }
+    }
+    if (e == hipSuccess) e = launch_cg_final<T>(g, p, n, grid, st, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(ctx->h_cg, st, sizeof(CgState), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     return e;
 }
 
@@ -596,6 +700,32 @@ lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y, vo
     hipError_t e = ctx->dtype == LAD_F64 ? enqueue_hvp<double>(ctx, d_x, d_v, d_y, s)
                                          : enqueue_hvp<float>(ctx, d_x, d_v, d_y, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "hvp launch");
+    return LAD_OK;
+}
+
+lad_status lad_newton_cg(lad_ctx *ctx, const void *d_x, const void *d_g, void *d_p,
+                         int32_t max_iters, double eta, lad_cg_stats *stats, void *hip_stream)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!d_x || !d_g || !d_p) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    if (d_p == d_g) return fail(ctx, LAD_ERR_ARG, "d_p must not alias d_g");
+    if (max_iters < 0) return fail(ctx, LAD_ERR_ARG, "max_iters must be >= 0");
+    if (!std::isfinite(eta)) return fail(ctx, LAD_ERR_ARG, "eta must be finite");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ctx->dtype == LAD_F64
+                       ? enqueue_newton_cg<double>(ctx, d_x, d_g, d_p, max_iters, eta, s)
+                       : enqueue_newton_cg<float>(ctx, d_x, d_g, d_p, max_iters, eta, s);
+    if (e == hipErrorOutOfMemory) return fail(ctx, LAD_ERR_OOM, "Newton-CG work space");
+    if (e != hipSuccess) return hip_fail(ctx, e, "lad_newton_cg");
+    if (stats) {
+        const CgState &h = *ctx->h_cg;
+        stats->iterations = h.iter;
+        stats->reason = h.reason;
+        stats->grad_norm = h.gnorm;
+        stats->rel_residual = (h.reason == LAD_CG_NEG_CURVATURE && h.iter == 0) ? 1.0
+                              : h.gnorm > 0.0 ? std::sqrt(h.rr) / h.gnorm
+                                              : 0.0;
+    }
     return LAD_OK;
 }
 

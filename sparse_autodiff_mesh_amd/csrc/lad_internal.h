@@ -206,6 +206,10 @@ struct RowArgs {
     int32_t lds_blocks;          // staging capacity per workgroup, in blocks
     const DevState *state;
     PatternBufs pat;
+    // HVP only: per-workgroup partial sums of v.y into hvp_dot[blockIdx]
+    // (null: none), and an early exit when *hvp_skip != 0 (null: never)
+    double *hvp_dot;
+    const int32_t *hvp_skip;
 };
 
 template <typename T>

@@ -522,6 +522,7 @@ template <typename T, bool FACES, bool PAIRS>
 __global__ void __launch_bounds__(kRowThreads)
 k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
 {
+    if (A.hvp_skip && *A.hvp_skip) return;  // workgroup-uniform
     const int act = PAIRS ? A.state->active : 0;
     const int32_t *rpa = A.pat.rp[act];
     const int32_t *cia = A.pat.ci[act];
@@ -536,6 +537,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     int32_t an = r0 + int32_t(threadIdx.x);
     Row<T> rn;
     T vn[3];
+    double vy = 0.0;  // this lane's part of v.y
     if (an < r1) {
         rn = load_row<T, false>(A, act, rpa, an, x);
 #pragma unroll
@@ -668,7 +670,14 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             }
         }
 #pragma unroll
-        for (int k = 0; k < 3; ++k) y[int64_t(r.a) * 3 + k] = Y[k];
+        for (int k = 0; k < 3; ++k) {
+            y[int64_t(r.a) * 3 + k] = Y[k];
+            vy += double(va[k]) * double(Y[k]);
+        }
+    }
+    if (A.hvp_dot) {
+        const double sum = block_sum<kRowThreads>(vy, nullptr);
+        if (threadIdx.x == 0) A.hvp_dot[blockIdx.x] = sum;
     }
 }
 

@@ -107,6 +107,9 @@ def test_null_context_calls(L):
     assert L.lad_eval_energy_grad_hess(None, vp(1), vp(1), vp(1), vp(1), 10, None) == binding.LAD_ERR_ARG
     assert L.lad_hvp(None, vp(1), vp(1), vp(1), None) == binding.LAD_ERR_ARG
     assert L.lad_insert_pairs(None, None, 0, None) == binding.LAD_ERR_ARG
+    st = binding.lad_cg_stats()
+    assert L.lad_newton_cg(None, vp(1), vp(1), vp(2), 10, 0.0, ctypes.byref(st),
+                           None) == binding.LAD_ERR_ARG
     info = binding.lad_info()
     assert L.lad_get_info(None, ctypes.byref(info)) == binding.LAD_ERR_ARG
     L.lad_destroy(None)  # no-op

@@ -1,0 +1,177 @@
+"""GPU Newton-CG (lad_newton_cg through the C ABI) against the oracle's
+truncated Newton-CG (oracle/newton_cg.py) on identical inputs: the same x
+and g (g from the oracle, rounded to the working precision), the same eta
+and iteration cap.  The stopping decisions (iteration count and reason) must
+match exactly; p within the tolerances below.
+
+Tolerances.  Both sides run the same recurrences; they differ by rounding
+only (fp64: summation order of the dots and of the HVP; fp32: the HVP and
+the vectors in fp32, the dots in fp64).  CG carries such differences from
+one iteration to the next through alpha and beta; on these well-conditioned
+systems (condition number about 90) they stay near the level of one HVP,
+so p is held to the HVP's own tolerances: 1e-12 relative in fp64 and 2e-5
+in fp32 (the largest differences seen, over up to 77 iterations, were about
+1.3e-15 and 6.5e-7).
+At the full 1000 x 1000 size the fp32 run is checked through properties
+the oracle computes independently: the true residual |H p + g| / |g| in
+fp64 matches the reported one, and p is a descent direction."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import newton_cg as ncg
+from sparse_autodiff_mesh_amd import inputs
+
+from gpu_util import dev, host_input, log_case, rel
+
+pytestmark = pytest.mark.gpu
+
+TOL_P = {"f64": 1e-12, "f32": 2e-5}
+
+
+def near_rest(n, amp, seed=11):
+    """Cloth n x n displaced from rest by amp * h * N(0, 1) per coordinate.
+    At amp = 0.002 every spring stays within a fraction of a percent of its
+    rest length and H is positive definite (smallest eigenvalue about 75 on
+    grids of 20 to 300); the perturbed cloth of the benchmark is not."""
+    m = inputs.cloth(n)
+    z = inputs.gaussian_block(seed, m.X.size).reshape(m.X.shape)
+    return m, m.X + amp * m.h * z
+
+
+def setup(lad, mesh, x, dtype, path="auto", faces=False, pairs=None, kappa=0.0, dhat=0.0):
+    import torch
+    cap = 0 if pairs is None else len(pairs)
+    L = lad.Lad(mesh.nv, dtype=dtype, path=path,
+                **lad.mesh_terms(mesh, faces=faces, pair_capacity=cap, kappa=kappa, dhat=dhat))
+    prob = oracle.problem_from_mesh(mesh, faces=faces, pairs=pairs, kappa=kappa, dhat=dhat,
+                                    f32=(dtype == "f32"))
+    if pairs is not None:
+        L.insert_pairs(torch.tensor(pairs, dtype=torch.int32, device="cuda"))
+        assert L.device_status() == 0
+    rp, ci = oracle.pattern(prob)
+    x_h = host_input(x, dtype)
+    _, g, _ = oracle.evaluate(prob, rp, ci, x_h)
+    g_h = host_input(g, dtype)
+    return L, prob, rp, ci, x_h, g_h
+
+
+def compare(lad, L, prob, rp, ci, x_h, g_h, dtype, max_iters, eta):
+    p, st = L.newton_cg(dev(x_h, dtype), dev(g_h, dtype), max_iters=max_iters, eta=eta)
+    po, it, why, res = ncg.newton_cg(prob, rp, ci, x_h, g_h, max_iters, eta=eta)
+    assert (st["iterations"], st["reason"]) == (it, why), (st, it, why)
+    e = rel(p.cpu().numpy(), po)
+    assert e <= TOL_P[dtype], e
+    assert abs(st["rel_residual"] - res) <= max(TOL_P[dtype] * res, 1e-14), (st, res)
+    return p, st, po
+
+
+@pytest.mark.parametrize("dtype,path", [("f64", "rows"), ("f64", "patch"), ("f32", "rows")])
+def test_spd_converges_like_oracle(lad, dtype, path):
+    log_case(test="ncg_spd", dtype=dtype, path=path)
+    m, x = near_rest(20, 0.002)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, dtype, path=path)
+    eta = 1e-8 if dtype == "f64" else 1e-3
+    _, st, _ = compare(lad, L, prob, rp, ci, x_h, g_h, dtype, 200, eta)
+    assert st["reason"] == lad.LAD_CG_CONVERGED and st["iterations"] > 3
+    L.close()
+
+
+@pytest.mark.parametrize("dtype,path", [("f64", "rows"), ("f64", "patch")])
+def test_indefinite_stops_at_negative_curvature_like_oracle(lad, dtype, path):
+    # the perturbed 10 x 10 cloth has an indefinite Hessian
+    log_case(test="ncg_indefinite", dtype=dtype, path=path)
+    m = inputs.cloth(10)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, m.x, dtype, path=path)
+    p, st, _ = compare(lad, L, prob, rp, ci, x_h, g_h, dtype, 500, 1e-12)
+    assert st["reason"] == lad.LAD_CG_NEG_CURVATURE and st["iterations"] > 0
+    assert float(np.vdot(g_h, p.cpu().numpy())) < 0.0
+    L.close()
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_faces_and_all_terms_fixed_iterations(lad, dtype):
+    log_case(test="ncg_faces", dtype=dtype)
+    m, x = near_rest(12, 0.002)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, dtype, faces=True)
+    _, st, _ = compare(lad, L, prob, rp, ci, x_h, g_h, dtype, 10, 1e-14)
+    assert st["reason"] == lad.LAD_CG_MAX_ITERS and st["iterations"] == 10
+    L.close()
+
+
+@pytest.mark.parametrize("path", ["rows", "patch"])
+def test_with_pairs(lad, path):
+    log_case(test="ncg_pairs", path=path)
+    m, x = near_rest(16, 0.002)
+    pairs, _ = inputs.contact_pairs(m, x, step=0)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, "f64", path=path, pairs=pairs,
+                                      kappa=100.0, dhat=0.5 * m.h)
+    compare(lad, L, prob, rp, ci, x_h, g_h, "f64", 30, 1e-10)
+    L.close()
+
+
+def test_edge_cases(lad):
+    import torch
+    log_case(test="ncg_edges")
+    m, x = near_rest(6, 0.002)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, "f64")
+    xd = dev(x_h, "f64")
+    # zero gradient: p = 0 at once
+    p, st = L.newton_cg(xd, torch.zeros_like(xd), max_iters=5)
+    assert st["iterations"] == 0 and st["reason"] == lad.LAD_CG_CONVERGED
+    assert not p.any()
+    # no iterations allowed: p = 0, iteration cap
+    p, st = L.newton_cg(xd, dev(g_h, "f64"), max_iters=0)
+    assert st["iterations"] == 0 and st["reason"] == lad.LAD_CG_MAX_ITERS and not p.any()
+    # bad arguments are rejected on the host
+    g = dev(g_h, "f64")
+    with pytest.raises(lad.LadError):
+        L.newton_cg(xd, g, out=g)
+    with pytest.raises(lad.LadError):
+        L.newton_cg(xd, g, max_iters=-1)
+    L.close()
+
+
+def test_negative_curvature_on_first_step_returns_minus_g(lad):
+    # the two-vertex configuration of the oracle pin: g.Hg < 0
+    log_case(test="ncg_first_step_negcurv")
+    X = np.array([[0.0, 0.0, 0.0], [0.5, 0.0, 0.0]])
+    xt = X + np.array([[0.0, 100.0, 0.0], [0.0, -100.0, 0.0]])
+    L = lad.Lad(2, dtype="f64", springs=np.array([[0, 1]]), rest_len=np.array([1.0]),
+                k=100.0, x_tilde=xt, c=1.0, path="rows")
+    prob = oracle.Problem(nv=2, springs=np.array([[0, 1]]), rest_len=np.array([1.0]),
+                          k=100.0, x_tilde=xt, c=1.0)
+    rp, ci = oracle.pattern(prob)
+    _, g, _ = oracle.evaluate(prob, rp, ci, X)
+    p, st = L.newton_cg(dev(X, "f64"), dev(g, "f64"), max_iters=10, eta=1e-10)
+    assert st["iterations"] == 0 and st["reason"] == lad.LAD_CG_NEG_CURVATURE
+    assert np.array_equal(p.cpu().numpy(), -g)
+    L.close()
+
+
+def test_bitwise_reproducible(lad):
+    log_case(test="ncg_reproducible")
+    m, x = near_rest(100, 0.002)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, "f32")
+    xd, gd = dev(x_h, "f32"), dev(g_h, "f32")
+    p1, s1 = L.newton_cg(xd, gd, max_iters=25, eta=1e-6)
+    p2, s2 = L.newton_cg(xd, gd, max_iters=25, eta=1e-6)
+    assert s1 == s2
+    assert np.array_equal(p1.cpu().numpy(), p2.cpu().numpy())
+    L.close()
+
+
+def test_fullsize_cloth_f32_properties(lad):
+    # 1000 x 1000 cloth in fp32, 16 iterations, as timed by the benchmark
+    log_case(test="ncg_fullsize", n=1000, dtype="f32")
+    m, x = near_rest(1000, 0.002)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, "f32")
+    p, st = L.newton_cg(dev(x_h, "f32"), dev(g_h, "f32"), max_iters=16, eta=1e-6)
+    assert st["reason"] == lad.LAD_CG_MAX_ITERS and st["iterations"] == 16
+    ph = p.cpu().numpy().astype(np.float64)
+    r = oracle.hvp(prob, rp, ci, x_h, ph) + g_h
+    true_res = np.linalg.norm(r) / np.linalg.norm(g_h)
+    assert true_res < 1.0
+    assert abs(true_res - st["rel_residual"]) <= 1e-3 + 1e-2 * true_res, (true_res, st)
+    assert float(np.vdot(g_h, ph)) < 0.0
+    L.close()
