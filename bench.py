@@ -72,10 +72,11 @@ def compulsory_bytes_hvp(nv, ns, nf, es, faces=False):
 
 
 def compulsory_bytes_cg_iter(nv, ns, es):
-    """One Newton-CG iteration: the HVP, then p, r updated from d, y (four
-    vectors read, two written) and the new direction (two read, one
-    written); the scalar kernels move a few KB."""
-    return compulsory_bytes_hvp(nv, ns, 0, es) + 9 * 3 * nv * es
+    """One Newton-CG iteration on the row path: the HVP, which forms its
+    operand d = -r + beta d_prev itself (reading r and d_prev, writing d:
+    two vectors more than a plain HVP), then p and r updated from d and y
+    (four vectors read, two written); the scalar kernels move a few KB."""
+    return compulsory_bytes_hvp(nv, ns, 0, es) + 8 * 3 * nv * es
 
 
 def kernel_source_sha():

@@ -240,9 +240,9 @@ typedef struct {
  *   max_iters >= 0; stats: host pointer, or NULL.
  * Dot products are accumulated in fp64 in a fixed order (bitwise
  * reproducible); vector updates are computed in fp64 and rounded to the
- * dtype.  The first call allocates per-context work vectors (4 [nv][3]
- * arrays and a few KB), kept until lad_destroy.  Synchronises `hip_stream`
- * after every 8 iterations (to stop early) and at the end.  Errors:
+ * dtype.  The first call allocates per-context work vectors (up to four
+ * [nv][3] arrays and a few KB), kept until lad_destroy.  Synchronises `hip_stream`
+ * after every 16 iterations (to stop early) and at the end.  Errors:
  * LAD_ERR_ARG (NULL x, g or p, p == g, max_iters < 0), LAD_ERR_OOM,
  * LAD_ERR_HIP.
  */

@@ -54,7 +54,7 @@ struct lad_ctx {
     PatternBufs pat{};
     InsertBufs ins{};
     // Newton-CG work space, allocated by the first lad_newton_cg call
-    void *cg_r = nullptr, *cg_d = nullptr, *cg_y = nullptr;
+    void *cg_r = nullptr, *cg_d = nullptr, *cg_d2 = nullptr, *cg_y = nullptr;
     double *cg_parts = nullptr;
     int32_t cg_nparts = 0;
     CgState *d_cg = nullptr;
@@ -303,13 +303,14 @@ hipError_t enqueue_hvp_patch(lad_ctx *ctx, const void *x, const void *v, void *y
     return e;
 }
 
-// y = H v, optionally with per-workgroup partial sums of v.y (row path;
-// *dot_parts_used gets their number, 0 when the caller must compute v.y
-// itself) and an early exit while *skip != 0 (row path).
+// y = H v.  The row path can also produce per-workgroup partial sums of
+// v.y (into dot_parts, returning their number in *dot_parts_used; 0 means
+// the caller must compute v.y itself), return at once while *skip != 0,
+// and form v itself as a Newton-CG direction (cg.r non-null).
 template <typename T>
 hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s,
                        double *dot_parts = nullptr, int32_t *dot_parts_used = nullptr,
-                       const int32_t *skip = nullptr)
+                       const int32_t *skip = nullptr, const CgDir<T> &cg = CgDir<T>{})
 {
     if (dot_parts_used) *dot_parts_used = 0;
     if (ctx->row_mode) {
@@ -318,22 +319,23 @@ hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipS
         a.hvp_skip = skip;
         if (dot_parts_used && dot_parts) *dot_parts_used = ctx->grid_hvp;
         return launch_hvp_rows<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
-                                  static_cast<T *>(y), ctx->grid_hvp, s);
+                                  static_cast<T *>(y), ctx->grid_hvp, s, cg);
     }
     return enqueue_hvp_patch<T>(ctx, x, v, y, s);
 }
 
 // Iterations enqueued between two host reads of the solve's stop flag.
-constexpr int32_t kCgCheck = 8;
+constexpr int32_t kCgCheck = 16;
 
 hipError_t cg_workspace(lad_ctx *ctx)
 {
     if (ctx->d_cg) return hipSuccess;
     const size_t n = size_t(ctx->nv) * 3;
     const size_t bytes = n * size_t(ctx->es);
-    char *r = nullptr, *d = nullptr, *y = nullptr;
+    char *r = nullptr, *d = nullptr, *d2 = nullptr, *y = nullptr;
     hipError_t e = dev_alloc(ctx, &r, bytes);
     if (e == hipSuccess) e = dev_alloc(ctx, &d, bytes);
+    if (e == hipSuccess && ctx->row_mode) e = dev_alloc(ctx, &d2, bytes);
     if (e == hipSuccess) e = dev_alloc(ctx, &y, bytes);
     const int32_t np = std::max<int32_t>(kCgMaxGrid, ctx->grid_hvp);
     double *parts = nullptr;
@@ -345,6 +347,7 @@ hipError_t cg_workspace(lad_ctx *ctx)
     if (e != hipSuccess) return e;
     ctx->cg_r = r;
     ctx->cg_d = d;
+    ctx->cg_d2 = d2;
     ctx->cg_y = y;
     ctx->cg_parts = parts;
     ctx->cg_nparts = np;
@@ -354,10 +357,13 @@ hipError_t cg_workspace(lad_ctx *ctx)
 }
 
 // Truncated Newton-CG (line-search Newton-CG, Nocedal and Wright,
-// Algorithm 7.1): per iteration y = H d with the partial sums of d.y (fused
-// into the row HVP), alpha, p and r updates with the partial sums of r.r,
-// beta, and the new direction.  All scalars stay on the device; the host
-// reads the stop flag every kCgCheck iterations and the final state.
+// Algorithm 7.1): per iteration the new direction d = -r + beta d, y = H d
+// and the partial sums of d.y; alpha; p and r updates with the partial sums
+// of r.r; beta.  On the row path the direction update and the d.y sums are
+// fused into the HVP (d alternates between two buffers), so an iteration is
+// four launches; the patch path runs them as separate kernels.  All scalars
+// stay on the device; the host reads the stop flag every kCgCheck
+// iterations and the final state.
 template <typename T>
 hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *pv,
                              int32_t max_iters, double eta, hipStream_t s)
@@ -375,19 +381,33 @@ hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *
                                                             offsetof(CgState, stop));
     e = launch_cg_init<T>(g, p, r, d, n, ctx->cg_parts, grid, s);
     if (e == hipSuccess) e = launch_cg_start(ctx->cg_parts, grid, st, eta, max_iters, s);
+    const double *beta = reinterpret_cast<const double *>(reinterpret_cast<const char *>(st) +
+                                                          offsetof(CgState, beta));
     for (int32_t done = 0; e == hipSuccess && done < max_iters;) {
         const int32_t nb = std::min(kCgCheck, max_iters - done);
         for (int32_t it = 0; it < nb && e == hipSuccess; ++it) {
             int32_t nparts = 0;
-            e = enqueue_hvp<T>(ctx, x, d, y, s, ctx->cg_parts, &nparts, stop);
-            if (e == hipSuccess && nparts == 0) {
+            T *dj = d;  // this iteration's direction
+            if (ctx->row_mode) {
+                // d_j = -r + beta d_(j-1) inside the HVP; beta is 0 on the
+                // first iteration, where d_(-1) = -g from the init kernel
+                T *d_old = (done + it) % 2 == 0 ? d : static_cast<T *>(ctx->cg_d2);
+                dj = (done + it) % 2 == 0 ? static_cast<T *>(ctx->cg_d2) : d;
+                CgDir<T> cg;
+                cg.r = r;
+                cg.d_old = d_old;
+                cg.d_new = dj;
+                cg.beta = beta;
+                e = enqueue_hvp<T>(ctx, x, nullptr, y, s, ctx->cg_parts, &nparts, stop, cg);
+            } else {
+                if (done + it > 0) e = launch_cg_dir<T>(r, d, n, grid, st, s);
+                if (e == hipSuccess) e = enqueue_hvp<T>(ctx, x, d, y, s);
                 nparts = grid;
-                e = launch_cg_dot<T>(d, y, n, ctx->cg_parts, grid, st, s);
+                if (e == hipSuccess) e = launch_cg_dot<T>(d, y, n, ctx->cg_parts, grid, st, s);
             }
             if (e == hipSuccess) e = launch_cg_alpha(ctx->cg_parts, nparts, st, s);
-            if (e == hipSuccess) e = launch_cg_update<T>(p, r, d, y, n, ctx->cg_parts, grid, st, s);
+            if (e == hipSuccess) e = launch_cg_update<T>(p, r, dj, y, n, ctx->cg_parts, grid, st, s);
             if (e == hipSuccess) e = launch_cg_beta(ctx->cg_parts, grid, st, max_iters, s);
-            if (e == hipSuccess) e = launch_cg_dir<T>(r, d, n, grid, st, s);
         }
         done += nb;
         if (e == hipSuccess && done < max_iters) {

@@ -220,9 +220,19 @@ hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int pairs, int *grid
 template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s);
+// Newton-CG direction formed inside the row HVP: the operand is
+// v = -r + beta d_old (beta read from the device), and every row stores its
+// v into d_new.  With r null the HVP's operand is v itself.
+template <typename T>
+struct CgDir {
+    const T *r = nullptr;
+    const T *d_old = nullptr;
+    T *d_new = nullptr;
+    const double *beta = nullptr;
+};
 template <typename T>
 hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
-                           hipStream_t s);
+                           hipStream_t s, const CgDir<T> &cg = CgDir<T>{});
 template <typename T>
 hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x,
                              T *g, T *hvals, EnergySink es, int nblocks,

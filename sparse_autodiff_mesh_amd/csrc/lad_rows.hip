@@ -518,11 +518,20 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
 // Matrix-free Hessian-vector product, y_a = sum over the row's terms of
 // H_ab v_b, with the local Hessians formed in registers and never stored.
 // ---------------------------------------------------------------------------
-template <typename T, bool FACES, bool PAIRS>
+template <typename T, bool FACES, bool PAIRS, bool CG>
 __global__ void __launch_bounds__(kRowThreads)
-k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
+k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y,
+           CgDir<T> cg)
 {
-    if (A.hvp_skip && *A.hvp_skip) return;  // workgroup-uniform
+    // early exit once a Newton-CG solve has ended; the flag and beta are
+    // loaded together with the first row group's operands (below)
+    const int32_t skip = A.hvp_skip ? *A.hvp_skip : 0;
+    // operand component i: v[i], or the next Newton-CG direction -r + beta d
+    const double beta = CG ? *cg.beta : 0.0;
+    auto dir = [&](int64_t i) -> T {
+        if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
+        else return v[i];
+    };
     const int act = PAIRS ? A.state->active : 0;
     const int32_t *rpa = A.pat.rp[act];
     const int32_t *cia = A.pat.ci[act];
@@ -541,18 +550,22 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     if (an < r1) {
         rn = load_row<T, false>(A, act, rpa, an, x);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) vn[k] = v[int64_t(an) * 3 + k];
+        for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
     }
+    if (skip) return;  // workgroup-uniform
     for (; an < r1;) {
         const Row<T> r = rn;
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
-        for (int k = 0; k < 3; ++k) va[k] = vn[k];
+        for (int k = 0; k < 3; ++k) {
+            va[k] = vn[k];
+            if constexpr (CG) cg.d_new[int64_t(r.a) * 3 + k] = va[k];
+        }
         an += kRowThreads;
         if (an < r1) {
             rn = load_row<T, false>(A, act, rpa, an, x);
 #pragma unroll
-            for (int k = 0; k < 3; ++k) vn[k] = v[int64_t(an) * 3 + k];
+            for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
         }
         PairPre<T> pp;
         prefetch_pairs(A, act, r, x, pp);
@@ -568,7 +581,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             for (int j = 0; j < kBatch; ++j) {
                 const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
 #pragma unroll
-                for (int k = 0; k < 3; ++k) vb[j][k] = v[int64_t(bl) * 3 + k];
+                for (int k = 0; k < 3; ++k) vb[j][k] = dir(int64_t(bl) * 3 + k);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
@@ -592,8 +605,8 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             for (int j = 0; j < kFaceBatch; ++j)
 #pragma unroll
                 for (int k = 0; k < 3; ++k) {
-                    vo[j][0][k] = v[int64_t(q.e[j].o1) * 3 + k];
-                    vo[j][1][k] = v[int64_t(q.e[j].o2) * 3 + k];
+                    vo[j][0][k] = dir(int64_t(q.e[j].o1) * 3 + k);
+                    vo[j][1][k] = dir(int64_t(q.e[j].o2) * 3 + k);
                 }
 #pragma unroll
             for (int j = 0; j < kFaceBatch; ++j) {
@@ -648,7 +661,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
 #pragma unroll
             for (int k = 0; k < kRowPairs; ++k)
 #pragma unroll
-                for (int cc = 0; cc < 3; ++cc) vp[k][cc] = v[int64_t(pp.b[k]) * 3 + cc];
+                for (int cc = 0; cc < 3; ++cc) vp[k][cc] = dir(int64_t(pp.b[k]) * 3 + cc);
 #pragma unroll
             for (int k = 0; k < kRowPairs; ++k)
                 if (k < pp.n) pair_hv(pp.xb[k], vp[k]);
@@ -664,7 +677,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
 #pragma unroll
                 for (int cc = 0; cc < 3; ++cc) {
                     xb[cc] = x[int64_t(b) * 3 + cc];
-                    vb[cc] = v[int64_t(b) * 3 + cc];
+                    vb[cc] = dir(int64_t(b) * 3 + cc);
                 }
                 pair_hv(xb, vb);
             }
@@ -696,7 +709,8 @@ static hipError_t rows_occupancy(int lds, int *occ_e, int *occ_h)
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_e, k_eval_rows<T, F, P>,
                                                                 kRowThreads, lds);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, P>, kRowThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, P, false>,
+                                                         kRowThreads, 0);
     return e;
 }
 
@@ -751,21 +765,26 @@ hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, Energy
 
 template <typename T, bool F, bool P>
 static void launch_hvp_rows_as(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
-                               hipStream_t s)
+                               hipStream_t s, const CgDir<T> &cg)
 {
-    hipLaunchKernelGGL((k_hvp_rows<T, F, P>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v, y);
+    if (cg.r)
+        hipLaunchKernelGGL((k_hvp_rows<T, F, P, true>), dim3(grid), dim3(kRowThreads), 0, s, a,
+                           x, v, y, cg);
+    else
+        hipLaunchKernelGGL((k_hvp_rows<T, F, P, false>), dim3(grid), dim3(kRowThreads), 0, s, a,
+                           x, v, y, cg);
 }
 
 template <typename T>
 hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
-                           hipStream_t s)
+                           hipStream_t s, const CgDir<T> &cg)
 {
     if (a.faces_on)
-        a.pairs_on ? launch_hvp_rows_as<T, true, true>(a, x, v, y, grid, s)
-                   : launch_hvp_rows_as<T, true, false>(a, x, v, y, grid, s);
+        a.pairs_on ? launch_hvp_rows_as<T, true, true>(a, x, v, y, grid, s, cg)
+                   : launch_hvp_rows_as<T, true, false>(a, x, v, y, grid, s, cg);
     else
-        a.pairs_on ? launch_hvp_rows_as<T, false, true>(a, x, v, y, grid, s)
-                   : launch_hvp_rows_as<T, false, false>(a, x, v, y, grid, s);
+        a.pairs_on ? launch_hvp_rows_as<T, false, true>(a, x, v, y, grid, s, cg)
+                   : launch_hvp_rows_as<T, false, false>(a, x, v, y, grid, s, cg);
     return hipGetLastError();
 }
 
@@ -775,7 +794,7 @@ hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, in
     template hipError_t launch_eval_rows<T>(const RowArgs<T> &, const T *, T *, T *, EnergySink,  \
                                             int, hipStream_t);                                    \
     template hipError_t launch_hvp_rows<T>(const RowArgs<T> &, const T *, const T *, T *, int,    \
-                                           hipStream_t);
+                                           hipStream_t, const CgDir<T> &);
 LAD_ROWS_INST(float)
 LAD_ROWS_INST(double)
 

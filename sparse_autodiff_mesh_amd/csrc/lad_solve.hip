@@ -25,6 +25,8 @@ namespace lad {
 namespace {
 
 constexpr int NT = kCgThreads;
+constexpr int NS = 1024;            // threads of the single-workgroup kernels
+constexpr int kSumLoads = 4;        // partial sums each of their threads loads at once
 
 // This workgroup's contiguous span [i0, i1) of n elements.
 __device__ __forceinline__ void span(int64_t n, int64_t &i0, int64_t &i1)
@@ -33,13 +35,26 @@ __device__ __forceinline__ void span(int64_t n, int64_t &i0, int64_t &i1)
     i1 = n * (blockIdx.x + 1) / gridDim.x;
 }
 
-// Sum of parts[0 .. n) in a fixed order (strided per thread, then the
-// workgroup reduction); valid in thread 0.
+// Sum of parts[0 .. n) in a fixed order, by one workgroup of NS threads:
+// thread t adds parts[t], parts[t + NS], ... in that order, then the
+// workgroup reduction adds the threads' sums; valid in thread 0.  The
+// partial sums were just written by other XCDs, so every load misses this
+// XCD's L2: each thread issues kSumLoads of them before adding any, which
+// pays that latency once per group instead of once per value.
 __device__ __forceinline__ double sum_parts(const double *__restrict__ parts, int n, double *red)
 {
     double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += NT) s += parts[i];
-    return block_sum<NT>(s, red);
+    for (int i0 = 0; i0 < n; i0 += NS * kSumLoads) {
+        double v[kSumLoads];
+#pragma unroll
+        for (int k = 0; k < kSumLoads; ++k) {
+            const int i = i0 + k * NS + int(threadIdx.x);
+            v[k] = i < n ? parts[i] : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kSumLoads; ++k) s += v[k];
+    }
+    return block_sum<NS>(s, red);
 }
 
 template <typename T>
@@ -62,11 +77,11 @@ k_cg_init(const T *__restrict__ g, T *__restrict__ p, T *__restrict__ r, T *__re
     if (threadIdx.x == 0) parts[blockIdx.x] = s;
 }
 
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NS)
 k_cg_start(const double *__restrict__ parts, int nparts, CgState *st, double eta,
            int32_t max_iters)
 {
-    __shared__ double red[NT / 64];
+    __shared__ double red[NS / 64];
     const double gg = sum_parts(parts, nparts, red);
     if (threadIdx.x != 0) return;
     const double gn = sqrt(gg);
@@ -101,13 +116,14 @@ k_cg_dot(const T *__restrict__ a, const T *__restrict__ b, int64_t n, double *__
     if (threadIdx.x == 0) parts[blockIdx.x] = s;
 }
 
-__global__ void __launch_bounds__(NT) k_cg_alpha(const double *__restrict__ parts, int nparts,
+__global__ void __launch_bounds__(NS) k_cg_alpha(const double *__restrict__ parts, int nparts,
                                                  CgState *st)
 {
-    __shared__ double red[NT / 64];
-    if (st->stop) return;
+    __shared__ double red[NS / 64];
+    // the stop flag is loaded alongside the partial sums, not before them
+    const int32_t stop = st->stop;
     const double dBd = sum_parts(parts, nparts, red);
-    if (threadIdx.x != 0) return;
+    if (stop || threadIdx.x != 0) return;
     if (!(dBd > 0.0)) {
         st->stop = 1;
         st->reason = LAD_CG_NEG_CURVATURE;
@@ -137,13 +153,13 @@ k_cg_update(T *__restrict__ p, T *__restrict__ r, const T *__restrict__ d,
     if (threadIdx.x == 0) parts[blockIdx.x] = s;
 }
 
-__global__ void __launch_bounds__(NT) k_cg_beta(const double *__restrict__ parts, int nparts,
+__global__ void __launch_bounds__(NS) k_cg_beta(const double *__restrict__ parts, int nparts,
                                                 CgState *st, int32_t max_iters)
 {
-    __shared__ double red[NT / 64];
-    if (st->stop) return;
+    __shared__ double red[NS / 64];
+    const int32_t stop = st->stop;
     const double rr = sum_parts(parts, nparts, red);
-    if (threadIdx.x != 0) return;
+    if (stop || threadIdx.x != 0) return;
     const int32_t it = st->iter + 1;
     st->iter = it;
     if (rr < st->eps2) {
@@ -198,7 +214,7 @@ hipError_t launch_cg_init(const T *g, T *p, T *r, T *d, int64_t n, double *parts
 hipError_t launch_cg_start(const double *parts, int nparts, CgState *st, double eta,
                            int32_t max_iters, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cg_start, dim3(1), dim3(NT), 0, s, parts, nparts, st, eta, max_iters);
+    hipLaunchKernelGGL(k_cg_start, dim3(1), dim3(NS), 0, s, parts, nparts, st, eta, max_iters);
     return hipGetLastError();
 }
 
@@ -212,7 +228,7 @@ hipError_t launch_cg_dot(const T *a, const T *b, int64_t n, double *parts, int g
 
 hipError_t launch_cg_alpha(const double *parts, int nparts, CgState *st, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cg_alpha, dim3(1), dim3(NT), 0, s, parts, nparts, st);
+    hipLaunchKernelGGL(k_cg_alpha, dim3(1), dim3(NS), 0, s, parts, nparts, st);
     return hipGetLastError();
 }
 
@@ -227,7 +243,7 @@ hipError_t launch_cg_update(T *p, T *r, const T *d, const T *y, int64_t n, doubl
 hipError_t launch_cg_beta(const double *parts, int nparts, CgState *st, int32_t max_iters,
                           hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cg_beta, dim3(1), dim3(NT), 0, s, parts, nparts, st, max_iters);
+    hipLaunchKernelGGL(k_cg_beta, dim3(1), dim3(NS), 0, s, parts, nparts, st, max_iters);
     return hipGetLastError();
 }
 
