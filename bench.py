@@ -71,6 +71,13 @@ def compulsory_bytes_hvp(nv, ns, nf, es, faces=False):
     return b
 
 
+def compulsory_bytes_residual_jacobian(nv, ns, es):
+    """Residuals and Jacobian values of the spring + inertia vector objective:
+    x and x_tilde read, per spring two int32 ids and a rest length; R
+    (ns + 3 nv rows) and the Jacobian values (6 ns + 3 nv) written."""
+    return 2 * 3 * nv * es + ns * (8 + es) + (ns + 3 * nv) * es + (6 * ns + 3 * nv) * es
+
+
 def compulsory_bytes_cg_iter(nv, ns, es):
     """One Newton-CG iteration on the row path: the HVP, which forms its
     operand d = -r + beta d_prev itself (reading r and d_prev, writing d:
@@ -247,6 +254,16 @@ def bench_secondary(torch, binding, inputs, args, timer):
     sec["cloth1000_newton_cg_ms_per_iter"] = round(r["median_ms"] / its, 5)
     sec["cloth1000_newton_cg_GBps"] = round(bcg * its / (r["median_ms"] * 1e-3) / 1e9, 1)
     sec["cloth1000_newton_cg_rel_residual"] = float(f"{stats['rel_residual']:.3e}")
+    # vector objective on the same context: residuals + explicit sparse
+    # Jacobian, and the matrix-free Gauss-Newton product
+    R, Jv = L.residual_jacobian(xc)
+    r = timer.run(lambda: L.residual_jacobian(xc, out=(R, Jv)), steps, warm)
+    bj = compulsory_bytes_residual_jacobian(mc.nv, mc.springs.shape[0], 4)
+    sec["cloth1000_residual_jacobian_ms"] = round(r["median_ms"], 5)
+    sec["cloth1000_residual_jacobian_GBps"] = round(bj / (r["median_ms"] * 1e-3) / 1e9, 1)
+    r = timer.run(lambda: L.gauss_newton(xc, vc, out=yc), steps, warm)
+    sec["cloth1000_gauss_newton_ms"] = round(r["median_ms"], 5)
+    sec["cloth1000_gauss_newton_GBps"] = round(bh / (r["median_ms"] * 1e-3) / 1e9, 1)
     L.close()
     # 512 x 512 symmetric-Dirichlet face grid, fp32: explicit eval and HVP
     f = inputs.face_grid(512)

@@ -209,6 +209,62 @@ lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x,
 lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y,
                    void *hip_stream);
 
+/*
+ * Vector objective: the least-squares form of the spring and inertia terms,
+ *   R_s           = sqrt(k) (|x_a - x_b| - L_s)   rows 0 .. ns-1, springs in
+ *                                                  the order of the desc
+ *   R_(ns+3v+c)   = sqrt(c) (x_v - xt_v)_c        rows ns .. ns+3nv-1
+ *                                                  (inertia on)
+ * so that 0.5 |R|^2 is the spring + inertia energy, and its sparse Jacobian
+ * J = dR/dx = sum_j P_j^T J_j S_j.  Source: page "Locality-Aware Automatic
+ * Differentiation on the GPU for Mesh-Based Computations", section "Method"
+ * (vector objectives assemble a sparse Jacobian; local Jacobians by forward
+ * mode) and its closing discussion (materialising J explicitly pays off).
+ * Available on contexts without face terms and without pair capacity (those
+ * energies are not sums of squares): other contexts get LAD_ERR_STATE.
+ *
+ * Jacobian pattern: CSR, nrows = ns (+ 3 nv) rows, 3 nv columns (DOF 3v+c),
+ * nnz = 6 ns (+ 3 nv).  Spring row s holds its two vertices' six DOFs in
+ * ascending order at entries 6s .. 6s+5; inertia row ns+i holds DOF i at
+ * entry 6 ns + i.  *d_row_ptr and *d_col_idx get library-owned DEVICE
+ * pointers valid until lad_destroy; the first call allocates and builds
+ * them on the GPU and synchronises `hip_stream`.  Errors: LAD_ERR_ARG,
+ * LAD_ERR_STATE (see above, or nnz >= 2^31), LAD_ERR_OOM, LAD_ERR_HIP.
+ */
+lad_status lad_jacobian_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nrows, int64_t *nnz,
+                                const int32_t **d_row_ptr, const int32_t **d_col_idx);
+
+/*
+ * Copy the Jacobian pattern into caller-owned DEVICE buffers: d_row_ptr
+ * gets nrows+1 entries, d_col_idx gets nnz entries (*nnz, which must not
+ * exceed col_capacity).  Builds the pattern first if needed; copies on
+ * `hip_stream` and synchronises it.  Errors: as lad_jacobian_pattern, plus
+ * LAD_ERR_CAPACITY (col_capacity < nnz; nothing copied).
+ */
+lad_status lad_copy_jacobian_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
+                                     int32_t *d_col_idx, int64_t col_capacity, int64_t *nnz);
+
+/*
+ * Residuals and Jacobian values at d_x: d_r device [nrows] dtype and
+ * d_jvals device [nnz] dtype, both fully overwritten, the values in the
+ * pattern's order (the pattern itself need not have been requested).
+ * Asynchronous; no host synchronisation.  Errors: LAD_ERR_ARG,
+ * LAD_ERR_STATE, LAD_ERR_HIP.
+ */
+lad_status lad_residual_jacobian(lad_ctx *ctx, const void *d_x, void *d_r, void *d_jvals,
+                                 void *hip_stream);
+
+/*
+ * Gauss-Newton product y = J^T (J v) at d_x, matrix-free (J is formed per
+ * term in registers and never stored); the positive semi-definite
+ * counterpart of lad_hvp for the same spring + inertia energy.  d_x, d_v
+ * device [nv][3] dtype, read only; d_y device [nv][3], fully overwritten.
+ * Needs the row path (lad_info.eval_path == LAD_PATH_ROWS).  Asynchronous;
+ * no host synchronisation.  Errors: LAD_ERR_ARG, LAD_ERR_STATE, LAD_ERR_HIP.
+ */
+lad_status lad_gauss_newton_product(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y,
+                                    void *hip_stream);
+
 /* Why a Newton-CG solve ended (lad_cg_stats.reason). */
 enum { LAD_CG_CONVERGED = 0, LAD_CG_NEG_CURVATURE = 1, LAD_CG_MAX_ITERS = 2 };
 

@@ -80,6 +80,8 @@ LAD_CG_CONVERGED, LAD_CG_NEG_CURVATURE, LAD_CG_MAX_ITERS = 0, 1, 2
 EXPORTS = [
     "lad_build_pattern", "lad_get_info", "lad_get_pattern", "lad_copy_pattern",
     "lad_eval_energy_grad_hess", "lad_hvp", "lad_newton_cg", "lad_insert_pairs",
+    "lad_jacobian_pattern", "lad_copy_jacobian_pattern", "lad_residual_jacobian",
+    "lad_gauss_newton_product",
     "lad_device_status", "lad_last_error", "lad_status_string", "lad_destroy",
 ]
 
@@ -106,6 +108,13 @@ def lib():
         L.lad_hvp.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.lad_newton_cg.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_double,
                                     ctypes.POINTER(lad_cg_stats), _vp]
+        L.lad_jacobian_pattern.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_vp),
+                                           ctypes.POINTER(_vp)]
+        L.lad_copy_jacobian_pattern.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int64,
+                                                ctypes.POINTER(ctypes.c_int64)]
+        L.lad_residual_jacobian.argtypes = [_vp, _vp, _vp, _vp, _vp]
+        L.lad_gauss_newton_product.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.lad_insert_pairs.argtypes = [_vp, _vp, ctypes.c_int32, _vp]
         L.lad_device_status.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]
         L.lad_last_error.argtypes = [_vp]
@@ -177,6 +186,29 @@ def lad_newton_cg(ctx, d_x, d_g, d_p, max_iters, eta=0.0, stream=None) -> dict:
     _check(lib().lad_newton_cg(ctx, _vp(d_x), _vp(d_g), _vp(d_p), int(max_iters), float(eta),
                                ctypes.byref(st), _vp(stream)), ctx)
     return {name: getattr(st, name) for name, _ in lad_cg_stats._fields_}
+
+
+def lad_jacobian_pattern(ctx, stream=None):
+    nrows, nnz = ctypes.c_int64(), ctypes.c_int64()
+    rp, ci = _vp(), _vp()
+    _check(lib().lad_jacobian_pattern(ctx, _vp(stream), ctypes.byref(nrows), ctypes.byref(nnz),
+                                      ctypes.byref(rp), ctypes.byref(ci)), ctx)
+    return nrows.value, nnz.value, rp.value, ci.value
+
+
+def lad_copy_jacobian_pattern(ctx, stream, d_row_ptr, d_col_idx, col_capacity):
+    nnz = ctypes.c_int64()
+    _check(lib().lad_copy_jacobian_pattern(ctx, _vp(stream), _vp(d_row_ptr), _vp(d_col_idx),
+                                           int(col_capacity), ctypes.byref(nnz)), ctx)
+    return nnz.value
+
+
+def lad_residual_jacobian(ctx, d_x, d_r, d_jvals, stream=None):
+    _check(lib().lad_residual_jacobian(ctx, _vp(d_x), _vp(d_r), _vp(d_jvals), _vp(stream)), ctx)
+
+
+def lad_gauss_newton_product(ctx, d_x, d_v, d_y, stream=None):
+    _check(lib().lad_gauss_newton_product(ctx, _vp(d_x), _vp(d_v), _vp(d_y), _vp(stream)), ctx)
 
 
 def lad_insert_pairs(ctx, d_pairs, npairs, stream=None):
@@ -303,6 +335,34 @@ class Lad:
         stats = lad_newton_cg(self.ctx, x.data_ptr(), g.data_ptr(), p.data_ptr(), max_iters,
                               eta, _stream())
         return p, stats
+
+    def jacobian_pattern(self):
+        """(row_ptr, col_idx) of the vector objective's Jacobian, copied into
+        new int32 tensors."""
+        t = self.torch
+        nrows, nnz, _, _ = lad_jacobian_pattern(self.ctx, _stream())
+        row_ptr = t.empty(nrows + 1, dtype=t.int32, device=self.device)
+        col_idx = t.empty(max(nnz, 1), dtype=t.int32, device=self.device)
+        lad_copy_jacobian_pattern(self.ctx, _stream(), row_ptr.data_ptr(), col_idx.data_ptr(),
+                                  col_idx.numel())
+        return row_ptr, col_idx[:nnz]
+
+    def residual_jacobian(self, x, out=None):
+        """(R [nrows], J values [nnz]) at x."""
+        assert x.dtype == self.dtype and x.is_contiguous()
+        if out is None:
+            nrows, nnz, _, _ = lad_jacobian_pattern(self.ctx, _stream())
+            out = (self.torch.empty(nrows, dtype=self.dtype, device=self.device),
+                   self.torch.empty(max(nnz, 1), dtype=self.dtype, device=self.device))
+        R, Jv = out
+        lad_residual_jacobian(self.ctx, x.data_ptr(), R.data_ptr(), Jv.data_ptr(), _stream())
+        return R, Jv
+
+    def gauss_newton(self, x, v, out=None):
+        assert x.dtype == self.dtype and v.dtype == self.dtype
+        y = out if out is not None else self.torch.empty_like(v)
+        lad_gauss_newton_product(self.ctx, x.data_ptr(), v.data_ptr(), y.data_ptr(), _stream())
+        return y
 
     def insert_pairs(self, pairs):
         """pairs: int32 cuda tensor (P, 2), or None / empty for no pairs."""

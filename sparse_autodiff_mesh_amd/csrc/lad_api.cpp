@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "lad_internal.h"
+#include "lad_jacobian.h"
 #include "lad_solve.h"
 
 #include <algorithm>
@@ -53,6 +54,12 @@ struct lad_ctx {
     double *d_epart = nullptr;
     PatternBufs pat{};
     InsertBufs ins{};
+    // vector objective: springs in input order, their rest lengths (dtype),
+    // and the Jacobian pattern (built by the first lad_jacobian_pattern call)
+    int32_t ns = 0;
+    int32_t *d_springs = nullptr;
+    void *d_spring_rest = nullptr;
+    int32_t *d_jrp = nullptr, *d_jci = nullptr;
     // Newton-CG work space, allocated by the first lad_newton_cg call
     void *cg_r = nullptr, *cg_d = nullptr, *cg_d2 = nullptr, *cg_y = nullptr;
     double *cg_parts = nullptr;
@@ -189,6 +196,10 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
     if (e == hipSuccess && d->inertia) {
         e = upload(ctx, &p, narrow<T>(d->x_tilde, size_t(d->nv) * 3), s);
         ctx->d_xt = p;
+    }
+    if (e == hipSuccess && d->ns > 0) {
+        e = upload(ctx, &p, narrow<T>(d->rest_len, size_t(d->ns)), s);
+        ctx->d_spring_rest = p;
     }
     if (e == hipSuccess && ctx->row_mode) {
         e = upload(ctx, &p, narrow<T>(rplan.slot_rest.data(), rplan.slot_rest.size()), s);
@@ -459,7 +470,10 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     int32_t *d_faces = nullptr, *d_springs = nullptr;
     PatternScratch sc{};
     e = tmp_alloc(&d_faces, size_t(d->nf) * 3);
-    if (e == hipSuccess) e = tmp_alloc(&d_springs, size_t(d->ns) * 2);
+    // the springs stay on the device for the vector objective
+    if (e == hipSuccess) e = dev_alloc(ctx, &d_springs, size_t(d->ns) * 2);
+    ctx->d_springs = d_springs;
+    ctx->ns = d->ns;
     if (e == hipSuccess) e = tmp_alloc(&sc.cnt, nv);
     if (e == hipSuccess) e = tmp_alloc(&sc.off, size_t(nv) + 1);
     if (e == hipSuccess) e = tmp_alloc(&sc.raw, size_t(raw));
@@ -611,6 +625,39 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     return LAD_OK;
 }
 
+lad_status check_vector_objective(lad_ctx *ctx)
+{
+    if (ctx->faces_on || ctx->pair_cap > 0)
+        return fail(ctx, LAD_ERR_STATE,
+                    "the vector objective covers spring and inertia terms; this context has face "
+                    "or pair terms");
+    const int64_t nnz = 6 * int64_t(ctx->ns) + (ctx->inertia_on ? 3 * int64_t(ctx->nv) : 0);
+    if (nnz >= (int64_t(1) << 31))
+        return fail(ctx, LAD_ERR_STATE, "Jacobian too large for int32 indices");
+    return LAD_OK;
+}
+
+template <typename T>
+hipError_t enqueue_residual_jacobian(lad_ctx *ctx, const void *x, void *r, void *jv,
+                                            hipStream_t s)
+{
+    const int64_t irows = ctx->inertia_on ? 3 * int64_t(ctx->nv) : 0;
+    return launch_residual_jacobian<T>(ctx->ns, ctx->d_springs,
+                                       static_cast<const T *>(ctx->d_spring_rest),
+                                       T(std::sqrt(ctx->k)), irows, static_cast<const T *>(x),
+                                       static_cast<const T *>(ctx->d_xt), T(std::sqrt(ctx->c)),
+                                       static_cast<T *>(r), static_cast<T *>(jv), s);
+}
+
+template <typename T>
+hipError_t enqueue_gauss_newton(lad_ctx *ctx, const void *x, const void *v, void *y,
+                                       hipStream_t s)
+{
+    return launch_gauss_newton_rows<T>(row_args<T>(ctx), T(std::sqrt(ctx->k)), T(std::sqrt(ctx->c)),
+                                       static_cast<const T *>(x), static_cast<const T *>(v),
+                                       static_cast<T *>(y), ctx->grid_hvp, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -746,6 +793,85 @@ lad_status lad_newton_cg(lad_ctx *ctx, const void *d_x, const void *d_g, void *d
                               : h.gnorm > 0.0 ? std::sqrt(h.rr) / h.gnorm
                                               : 0.0;
     }
+    return LAD_OK;
+}
+
+lad_status lad_jacobian_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nrows, int64_t *nnz,
+                                const int32_t **d_row_ptr, const int32_t **d_col_idx)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!nrows || !nnz || !d_row_ptr || !d_col_idx) return fail(ctx, LAD_ERR_ARG, "NULL argument");
+    lad_status st = check_vector_objective(ctx);
+    if (st != LAD_OK) return st;
+    const int64_t irows = ctx->inertia_on ? 3 * int64_t(ctx->nv) : 0;
+    const int64_t m = int64_t(ctx->ns) + irows, n = 6 * int64_t(ctx->ns) + irows;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (!ctx->d_jrp) {
+        int32_t *rp = nullptr, *ci = nullptr;
+        hipError_t e = dev_alloc(ctx, &rp, size_t(m) + 1);
+        if (e == hipSuccess) e = dev_alloc(ctx, &ci, size_t(n));
+        if (e != hipSuccess) return fail(ctx, LAD_ERR_OOM, "Jacobian pattern");
+        e = launch_jacobian_pattern(ctx->ns, ctx->d_springs, irows, rp, ci, s);
+        if (e == hipSuccess) e = host_sync(ctx, s);
+        if (e != hipSuccess) return hip_fail(ctx, e, "Jacobian pattern");
+        ctx->d_jrp = rp;
+        ctx->d_jci = ci;
+    }
+    *nrows = m;
+    *nnz = n;
+    *d_row_ptr = ctx->d_jrp;
+    *d_col_idx = ctx->d_jci;
+    return LAD_OK;
+}
+
+lad_status lad_copy_jacobian_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
+                                     int32_t *d_col_idx, int64_t col_capacity, int64_t *nnz)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!d_row_ptr || !d_col_idx || !nnz) return fail(ctx, LAD_ERR_ARG, "NULL argument");
+    int64_t m = 0, n = 0;
+    const int32_t *rp = nullptr, *ci = nullptr;
+    lad_status st = lad_jacobian_pattern(ctx, hip_stream, &m, &n, &rp, &ci);
+    if (st != LAD_OK) return st;
+    *nnz = n;
+    if (col_capacity < n)
+        return fail(ctx, LAD_ERR_CAPACITY, "col_capacity below nnz " + std::to_string(n));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipMemcpyAsync(d_row_ptr, rp, size_t(m + 1) * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && n > 0)
+        e = hipMemcpyAsync(d_col_idx, ci, size_t(n) * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lad_copy_jacobian_pattern");
+    return LAD_OK;
+}
+
+lad_status lad_residual_jacobian(lad_ctx *ctx, const void *d_x, void *d_r, void *d_jvals,
+                                 void *hip_stream)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!d_x || !d_r || !d_jvals) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    lad_status st = check_vector_objective(ctx);
+    if (st != LAD_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ctx->dtype == LAD_F64 ? enqueue_residual_jacobian<double>(ctx, d_x, d_r, d_jvals, s)
+                                         : enqueue_residual_jacobian<float>(ctx, d_x, d_r, d_jvals, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "residual/Jacobian launch");
+    return LAD_OK;
+}
+
+lad_status lad_gauss_newton_product(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y,
+                                    void *hip_stream)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (!d_x || !d_v || !d_y) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    lad_status st = check_vector_objective(ctx);
+    if (st != LAD_OK) return st;
+    if (!ctx->row_mode)
+        return fail(ctx, LAD_ERR_STATE, "the Gauss-Newton product needs the row path");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = ctx->dtype == LAD_F64 ? enqueue_gauss_newton<double>(ctx, d_x, d_v, d_y, s)
+                                         : enqueue_gauss_newton<float>(ctx, d_x, d_v, d_y, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "Gauss-Newton launch");
     return LAD_OK;
 }
 

@@ -28,6 +28,8 @@
 #include "energies.h"
 #include "lad_device.h"
 #include "lad_internal.h"
+#include "lad_jacobian.h"
+#include "residuals.h"
 
 namespace lad {
 
@@ -694,7 +696,76 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Gauss-Newton product of the vector objective, y = J^T (J v), H's
+// positive semi-definite counterpart.  Row owner as above: each spring's
+// local Jacobian row w = dR/dz (z = x_a - x_b, from a first-order dual
+// evaluation) is formed in registers, and the row gets w (w . (v_a - v_b));
+// the inertia rows contribute sqrt(c) (sqrt(c) v_a).  J is never stored.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads)
+k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__restrict__ v,
+          T *__restrict__ y)
+{
+    const int32_t *rpa = A.rp0;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
+    const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
+    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kRowThreads) {
+        const Row<T> r = load_row<T, false>(A, 0, rpa, a, x);
+        T va[3], Y[3] = {T(0), T(0), T(0)};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) va[k] = v[int64_t(a) * 3 + k];
+        int32_t jb = r.kb0;
+        for (int32_t base = r.s0; base < r.s1; base += kBatch) {
+            SlotBatch<T> q;
+            load_batch(A, r, 0, A.ci0, base, jb, x, q);
+            T vb[kBatch][3];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) vb[j][k] = v[int64_t(bl) * 3 + k];
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (base + j >= r.s1) break;
+                if (q.b[j] == r.a || !(q.L[j] >= T(0))) continue;
+                Dual1<T, 3> z[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) z[k] = Dual1<T, 3>::var(r.xa[k] - q.xb[j][k], k);
+                const Dual1<T, 3> e = spring_residual(z, q.L[j], sqrt_k);
+                const T u = e.g[0] * (va[0] - vb[j][0]) + e.g[1] * (va[1] - vb[j][1]) +
+                            e.g[2] * (va[2] - vb[j][2]);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) Y[k] += e.g[k] * u;
+            }
+        }
+        if (A.inertia_on)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) Y[k] += sqrt_c * (sqrt_c * va[k]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) y[int64_t(a) * 3 + k] = Y[k];
+    }
+}
+
 }  // namespace
+
+template <typename T>
+hipError_t launch_gauss_newton_rows(const RowArgs<T> &a, T sqrt_k, T sqrt_c, const T *x,
+                                    const T *v, T *y, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_gn_rows<T>, dim3(grid), dim3(kRowThreads), 0, s, a, sqrt_k, sqrt_c, x, v,
+                       y);
+    return hipGetLastError();
+}
+template hipError_t launch_gauss_newton_rows<float>(const RowArgs<float> &, float, float,
+                                                    const float *, const float *, float *, int,
+                                                    hipStream_t);
+template hipError_t launch_gauss_newton_rows<double>(const RowArgs<double> &, double, double,
+                                                     const double *, const double *, double *, int,
+                                                     hipStream_t);
 
 template <typename T>
 int rows_lds_bytes(int lds_blocks)

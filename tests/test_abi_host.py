@@ -107,6 +107,11 @@ def test_null_context_calls(L):
     assert L.lad_eval_energy_grad_hess(None, vp(1), vp(1), vp(1), vp(1), 10, None) == binding.LAD_ERR_ARG
     assert L.lad_hvp(None, vp(1), vp(1), vp(1), None) == binding.LAD_ERR_ARG
     assert L.lad_insert_pairs(None, None, 0, None) == binding.LAD_ERR_ARG
+    assert L.lad_residual_jacobian(None, vp(1), vp(1), vp(1), None) == binding.LAD_ERR_ARG
+    assert L.lad_gauss_newton_product(None, vp(1), vp(1), vp(1), None) == binding.LAD_ERR_ARG
+    n64 = ctypes.c_int64()
+    assert L.lad_copy_jacobian_pattern(None, None, vp(1), vp(1), 10,
+                                       ctypes.byref(n64)) == binding.LAD_ERR_ARG
     st = binding.lad_cg_stats()
     assert L.lad_newton_cg(None, vp(1), vp(1), vp(2), 10, 0.0, ctypes.byref(st),
                            None) == binding.LAD_ERR_ARG
