@@ -32,6 +32,7 @@ struct lad_ctx {
     int64_t nspr_rec = 0, nfac_rec = 0;
     int32_t pair_blocks = 0;
     int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
+    bool cols_complete[3] = {true, true, true};  // column array of each pattern buffer complete
     int64_t host_syncs = 0;          // host synchronisations made for this context
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
@@ -722,6 +723,12 @@ lad_status lad_get_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nnzb,
     const int a = hs.active;
     if (a < 0 || a > 2) return fail(ctx, LAD_ERR_STATE, "corrupt device state");
     *nnzb = a == 0 ? ctx->nnzb_base : hs.nnzb[a];
+    if (!ctx->cols_complete[a]) {
+        e = launch_complete_cols(ctx->d_state, ctx->ins, ctx->d_hdr, ctx->npatch, s);
+        if (e == hipSuccess) e = host_sync(ctx, s);
+        if (e != hipSuccess) return hip_fail(ctx, e, "lad_get_pattern");
+        ctx->cols_complete[a] = true;
+    }
     *d_row_ptr = ctx->pat.rp[a];
     *d_col_idx = ctx->pat.ci[a];
     return LAD_OK;
@@ -887,7 +894,10 @@ lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = npairs == 0 ? launch_restore_topology(ctx->d_state, s)
                                : launch_insert(ctx->d_state, d_pairs, npairs, ctx->nv, ctx->ins,
-                                               ctx->d_hdr, ctx->npatch, s);
+                                               ctx->d_hdr, ctx->npatch, ctx->row_mode ? 0 : 1, s);
+    // the row path leaves the untouched rows' columns of the new buffer
+    // unwritten until the pattern is read
+    if (ctx->row_mode && npairs > 0) ctx->cols_complete[1] = ctx->cols_complete[2] = false;
     if (e != hipSuccess) return hip_fail(ctx, e, "insert launch");
     return LAD_OK;
 }

@@ -12,6 +12,13 @@
 // Every kernel below picks the back buffer from the device-side state, so
 // the host never needs to know which buffer is active.  The last kernel
 // commits (flips `active`) only if every device-side check passed.
+//
+// A row that no pair touches keeps its topology row, shifted to its new
+// offset.  The row-owner kernels read such rows through the topology
+// pattern, so on that path an insert writes the columns of the touched rows
+// only (a few percent of the rows) and the rest of the column array is
+// filled in when a caller asks for the pattern; the patch path reads every
+// row and gets the complete array at once.
 #include "lad_internal.h"
 
 namespace lad {
@@ -122,15 +129,6 @@ k_ins_rows(const DevState *st, int32_t nent, int32_t nv, InsertBufs b)
     b.nnew[a] = nn;
 }
 
-// One 64-thread workgroup (one wave) per row chunk or patch, walking its
-// rows 64 at a time.  For each group of rows the wave loads the topology
-// columns of the group into LDS with coalesced loads, every lane builds its
-// row of the new pattern in a second LDS buffer (a copy, or a merge with the
-// row's new partners, which also re-zeroes nnew), and the wave stores the
-// group's new columns with coalesced stores.  A group whose rows exceed the
-// staging buffers is merged row by row straight from and to global memory.
-// Finally the chunk's new block count is checked against its reserved
-// staging capacity.
 constexpr int kMergeThreads = 64;
 constexpr int kMergeStage = 512;   // ints per staging buffer
 
@@ -144,11 +142,54 @@ __device__ __forceinline__ void merge_row(const int32_t *cb, int32_t len, const 
     }
 }
 
+// Columns of the rows that pairs touch (one thread per incidence entry; the
+// row's first entry does the work): the topology row merged with the row's
+// new partners.  Each such row also checks the staging capacity of the
+// chunk or patch that holds it (the only chunks whose size changed), and
+// re-zeroes its new-block count.
+__global__ void __launch_bounds__(kThreads)
+k_ins_merge_rows(DevState *st, int32_t nent, int32_t nv, InsertBufs b,
+                 const PatchHdr *__restrict__ hdr, int32_t nchunk)
+{
+    const int32_t k = blockIdx.x * kThreads + threadIdx.x;
+    if (k >= nent) return;
+    const int bk = back_of(st);
+    if (k >= b.pinc_ptr[bk][nv]) return;
+    const int32_t a = b.pinc_row[bk][k];
+    if (a < 0 || a >= nv) return;
+    if (k != b.pinc_ptr[bk][a]) return;
+    const int32_t rb0 = b.rp[0][a], len = b.rp[0][a + 1] - rb0;
+    const int32_t o0 = b.rp[bk][a], nn = (b.rp[bk][a + 1] - o0) - len;
+    merge_row(b.ci[0] + rb0, len, b.pnew[bk] + k, nn, b.ci[bk] + o0);
+    if (nn > 0) b.nnew[a] = 0;
+    // the chunk holding row a: the last one whose first row is <= a
+    int32_t lo = 0, hi = nchunk - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (hdr[mid].v0 <= a) lo = mid;
+        else hi = mid - 1;
+    }
+    const int32_t v0 = hdr[lo].v0, v1 = v0 + hdr[lo].nown;
+    if (b.rp[bk][v1] - b.rp[bk][v0] > hdr[lo].amap_cap) atomicOr(&st->err_cur, 2);
+}
+
+// One 64-thread workgroup (one wave) per row chunk or patch, walking its
+// rows 64 at a time.  For each group of rows the wave loads the topology
+// columns of the group into LDS with coalesced loads, every lane builds its
+// row of the new pattern in a second LDS buffer (a copy, or a merge with the
+// row's new partners, which also re-zeroes nnew), and the wave stores the
+// group's new columns with coalesced stores.  A group whose rows exceed the
+// staging buffers is merged row by row straight from and to global memory.
+// Finally the chunk's new block count is checked against its reserved
+// staging capacity.  With use_active set it completes the active buffer of
+// a row-path insert instead (every row rewritten with the same result, no
+// check; nothing to do while the topology pattern is active).
 __global__ void __launch_bounds__(kMergeThreads)
-k_ins_merge(DevState *st, const PatchHdr *__restrict__ hdr, InsertBufs b)
+k_ins_merge(DevState *st, const PatchHdr *__restrict__ hdr, InsertBufs b, int use_active)
 {
     __shared__ int32_t inb[kMergeStage], outb[kMergeStage];
-    const int bk = back_of(st);
+    const int bk = use_active ? st->active : back_of(st);
+    if (bk == 0) return;
     const PatchHdr h = hdr[blockIdx.x];
     const int32_t *cb = b.ci[0];
     const int32_t *rp0 = b.rp[0], *rpn = b.rp[bk];
@@ -183,7 +224,8 @@ k_ins_merge(DevState *st, const PatchHdr *__restrict__ hdr, InsertBufs b)
         }
         if (mine && nn > 0) b.nnew[a] = 0;
     }
-    if (lane == 0 && rpn[h.v0 + h.nown] - rpn[h.v0] > h.amap_cap) atomicOr(&st->err_cur, 2);
+    if (!use_active && lane == 0 && rpn[h.v0 + h.nown] - rpn[h.v0] > h.amap_cap)
+        atomicOr(&st->err_cur, 2);
 }
 
 // Flip the active buffer if every check of this insert passed, else latch
@@ -209,7 +251,8 @@ inline unsigned blocks_for(int64_t n) { return unsigned((n + kThreads - 1) / kTh
 }  // namespace
 
 hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32_t nv,
-                         InsertBufs b, const PatchHdr *hdr, int32_t npatch, hipStream_t s)
+                         InsertBufs b, const PatchHdr *hdr, int32_t npatch, int complete_cols,
+                         hipStream_t s)
 {
     hipLaunchKernelGGL(k_ins_count, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, d_pairs, np,
                        nv, b);
@@ -221,8 +264,19 @@ hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32
     // new row_ptr = topology row_ptr + prefix of the new blocks per row
     e = launch_scan_back(b.nnew, b.rp, b.rp[0], st, nv, b.tmp, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ins_merge, dim3(npatch), dim3(kMergeThreads), 0, s, st, hdr, b);
+    if (complete_cols)
+        hipLaunchKernelGGL(k_ins_merge, dim3(npatch), dim3(kMergeThreads), 0, s, st, hdr, b, 0);
+    else
+        hipLaunchKernelGGL(k_ins_merge_rows, dim3(blocks_for(2 * int64_t(np))), dim3(kThreads), 0,
+                           s, st, 2 * np, nv, b, hdr, npatch);
     hipLaunchKernelGGL(k_ins_commit, dim3(1), dim3(1), 0, s, st, np, nv, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_complete_cols(DevState *st, InsertBufs b, const PatchHdr *hdr, int32_t npatch,
+                                hipStream_t s)
+{
+    hipLaunchKernelGGL(k_ins_merge, dim3(npatch), dim3(kMergeThreads), 0, s, st, hdr, b, 1);
     return hipGetLastError();
 }
 

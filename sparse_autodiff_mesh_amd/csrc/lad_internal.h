@@ -283,9 +283,14 @@ struct InsertBufs {
     int32_t *nnew;               // [nv] new blocks per row, all zero between inserts
     int32_t *tmp;                // scan scratch
 };
+// complete_cols = 0 writes the columns of pair-touched rows only (row
+// path); launch_complete_cols then fills in the other rows of the active
+// buffer on demand.
 hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np,
                          int32_t nv, InsertBufs b, const PatchHdr *hdr,
-                         int32_t npatch, hipStream_t s);
+                         int32_t npatch, int complete_cols, hipStream_t s);
+hipError_t launch_complete_cols(DevState *st, InsertBufs b, const PatchHdr *hdr,
+                                int32_t npatch, hipStream_t s);
 hipError_t launch_restore_topology(DevState *st, hipStream_t s);
 
 }  // namespace lad

@@ -119,6 +119,30 @@ def test_pairs_with_faces_and_hvp(lad, path):
 
 
 @pytest.mark.parametrize("path", ["patch", "rows"])
+def test_steps_without_reading_the_pattern(lad, path):
+    # on the row path an insert writes only the touched rows' columns and
+    # the pattern read fills in the rest: evaluations in between must not
+    # depend on it, and the pattern read at the end must be complete
+    log_case(test="pairs_lazy_columns", path=path)
+    m = inputs.cloth(60)
+    P = int(round(0.02 * m.nv))
+    L, dhat = make(lad, m, "f64", P, path=path)
+    for step in range(5):
+        pairs, x = inputs.contact_pairs(m, m.x, step=step)
+        L.insert_pairs(pairs_dev(pairs))
+        prob = oracle.problem_from_mesh(m, pairs=pairs, kappa=KAPPA, dhat=dhat)
+        orp, oci = oracle.pattern(prob)
+        Eo, go, Ho = oracle.evaluate(prob, orp, oci, x)
+        E, g, H = L.eval(dev(x, "f64"))
+        assert rel([E.item()], [Eo]) <= TOL["f64"]
+        assert rel(g.cpu().numpy(), go) <= TOL["f64"]
+        assert rel(H.cpu().numpy()[: oci.size], Ho) <= TOL["f64"]
+    rp, ci = L.pattern()
+    assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+    L.close()
+
+
+@pytest.mark.parametrize("path", ["patch", "rows"])
 def test_bad_pairs_keep_previous_pattern(lad, path):
     log_case(test="pairs_bad", path=path)
     m = inputs.cloth(20)
