@@ -183,8 +183,8 @@ lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
  *   d_x      device [nv][3] dtype, read only.
  *   d_energy device double, overwritten with F(x); or NULL, in which case the
  *            energy is not summed (one small kernel launch is saved: the
- *            evaluation itself is then a single launch on springs/inertia/
- *            pair meshes).
+ *            evaluation itself is then a single launch on the row path,
+ *            two with pair capacity).
  *   d_grad   device [nv][3] dtype, fully overwritten.
  *   d_hvals  device [hvals_capacity][3][3] dtype; the first nnzb_active
  *            blocks are fully overwritten in the active pattern's order.

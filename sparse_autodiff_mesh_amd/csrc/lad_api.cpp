@@ -282,11 +282,19 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
     hipError_t e = hipSuccess;
     int32_t nparts = 0;
     if (ctx->row_mode) {
-        // one launch: springs, inertia and pairs of every row
+        // every row that no pair touches, then the touched rows
         e = launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x), static_cast<T *>(g),
                                 static_cast<T *>(hv), EnergySink{ctx->d_epart, 0}, ctx->grid_eval,
                                 s);
         nparts = ctx->grid_eval;
+        // rows touched by pairs, one thread each
+        if (e == hipSuccess && ctx->pair_blocks > 0) {
+            e = launch_eval_pair_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
+                                         static_cast<T *>(g), static_cast<T *>(hv),
+                                         EnergySink{ctx->d_epart, ctx->grid_eval},
+                                         ctx->pair_blocks, s);
+            nparts += ctx->pair_blocks;
+        }
     } else {
         const PatchArgs<T> a = patch_args<T>(ctx);
         e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g), static_cast<T *>(hv),
@@ -562,6 +570,18 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (e == hipSuccess) e = upload(ctx, &ctx->d_fac, plan.fac, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_col_bounds, plan.col_bounds, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_diag_rel, plan.diag_rel, s);
+    // row path with pair capacity: the chunk of every row, for the
+    // insertion's capacity check (uploaded before the sync below)
+    // (the pointer is stored in ctx->ins after that struct is reset below)
+    std::vector<int32_t> row_chunk;
+    int32_t *d_row_chunk = nullptr;
+    if (e == hipSuccess && ctx->row_mode && d->pair_capacity > 0) {
+        row_chunk.resize(size_t(nv));
+        for (size_t c = 0; c < plan.hdr.size(); ++c)
+            for (int32_t a = plan.hdr[c].v0; a < plan.hdr[c].v0 + plan.hdr[c].nown; ++a)
+                row_chunk[size_t(a)] = int32_t(c);
+        e = upload(ctx, &d_row_chunk, row_chunk, s);
+    }
     if (e != hipSuccess) return hip_fail(ctx, e, "upload of patch tables");
     lad_status st = ctx->dtype == LAD_F64 ? upload_constants<double>(ctx, d, plan, rplan, s)
                                           : upload_constants<float>(ctx, d, plan, rplan, s);
@@ -581,6 +601,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     // ---- pattern buffers, device state, scratch
     std::memset(&ctx->pat, 0, sizeof(ctx->pat));
     std::memset(&ctx->ins, 0, sizeof(ctx->ins));
+    ctx->ins.row_chunk = d_row_chunk;
     ctx->pat.rp[0] = d_rp0;
     ctx->pat.ci[0] = d_ci0;
     ctx->ins.rp[0] = d_rp0;
@@ -600,6 +621,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc[b], cap2);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_row[b], cap2);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pnew[b], cap2);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.trow[b], cap2);
         }
         if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.cnt, size_t(nv));
         if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.cnt, 0, size_t(nv) * 4, s);
@@ -613,8 +635,9 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             ctx->pat.pinc_ptr[b] = ctx->ins.pinc_ptr[b];
             ctx->pat.pinc[b] = ctx->ins.pinc[b];
             ctx->pat.pinc_row[b] = ctx->ins.pinc_row[b];
+            ctx->pat.trow[b] = ctx->ins.trow[b];
         }
-        ctx->pair_blocks = ctx->row_mode ? 0 : int32_t((cap2 + kThreads - 1) / kThreads);
+        ctx->pair_blocks = int32_t((cap2 + kThreads - 1) / kThreads);
     }
     if (e == hipSuccess)
         e = dev_alloc(ctx, &ctx->d_epart,

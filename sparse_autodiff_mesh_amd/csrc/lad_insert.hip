@@ -80,20 +80,25 @@ __device__ __forceinline__ int32_t lower_bound(const int32_t *c, int32_t lo, int
 // entry does the work): order the row's pairs by pair id (fixed evaluation
 // order), collect the distinct partners that are not already in the
 // topology row (sorted, into pnew at the row's incidence offset) and store
-// their number in nnew[row].  nnew is zero for every other row.
+// their number in nnew[row].  nnew is zero for every other row.  Every
+// entry also records in trow whether it is its row's first (the row) or
+// not (-1): the later kernels find the touched rows there in one load.
 // Only the first pinc_ptr[nv] entries were filled (pairs that failed the
-// device check have none), so threads past that stop before reading.
+// device check have none), so threads past that read nothing else.
 __global__ void __launch_bounds__(kThreads)
 k_ins_rows(const DevState *st, int32_t nent, int32_t nv, InsertBufs b)
 {
     const int32_t k = blockIdx.x * kThreads + threadIdx.x;
     if (k >= nent) return;
     const int bk = back_of(st);
-    if (k >= b.pinc_ptr[bk][nv]) return;
-    const int32_t a = b.pinc_row[bk][k];
-    if (a < 0 || a >= nv) return;
-    const int32_t p0 = b.pinc_ptr[bk][a], p1 = b.pinc_ptr[bk][a + 1];
-    if (k != p0) return;
+    int32_t a = -1;
+    if (k < b.pinc_ptr[bk][nv]) {
+        const int32_t r = b.pinc_row[bk][k];
+        if (r >= 0 && r < nv && k == b.pinc_ptr[bk][r]) a = r;
+    }
+    b.trow[bk][k] = a;
+    if (a < 0) return;
+    const int32_t p0 = k, p1 = b.pinc_ptr[bk][a + 1];
     const int32_t rb0 = b.rp[0][a], rb1 = b.rp[0][a + 1];
     int32_t *pl = b.pinc[bk];
     for (int32_t i = p0 + 1; i < p1; ++i) {
@@ -143,34 +148,24 @@ __device__ __forceinline__ void merge_row(const int32_t *cb, int32_t len, const 
 }
 
 // Columns of the rows that pairs touch (one thread per incidence entry; the
-// row's first entry does the work): the topology row merged with the row's
-// new partners.  Each such row also checks the staging capacity of the
-// chunk or patch that holds it (the only chunks whose size changed), and
-// re-zeroes its new-block count.
+// thread of the row's first entry does the work): the topology row merged
+// with the row's new partners.  Each such row also checks the staging
+// capacity of the chunk that holds it (the only chunks whose size changed),
+// and re-zeroes its new-block count.
 __global__ void __launch_bounds__(kThreads)
-k_ins_merge_rows(DevState *st, int32_t nent, int32_t nv, InsertBufs b,
-                 const PatchHdr *__restrict__ hdr, int32_t nchunk)
+k_ins_merge_rows(DevState *st, int32_t nent, InsertBufs b, const PatchHdr *__restrict__ hdr)
 {
     const int32_t k = blockIdx.x * kThreads + threadIdx.x;
     if (k >= nent) return;
     const int bk = back_of(st);
-    if (k >= b.pinc_ptr[bk][nv]) return;
-    const int32_t a = b.pinc_row[bk][k];
-    if (a < 0 || a >= nv) return;
-    if (k != b.pinc_ptr[bk][a]) return;
+    const int32_t a = b.trow[bk][k];
+    if (a < 0) return;
     const int32_t rb0 = b.rp[0][a], len = b.rp[0][a + 1] - rb0;
     const int32_t o0 = b.rp[bk][a], nn = (b.rp[bk][a + 1] - o0) - len;
     merge_row(b.ci[0] + rb0, len, b.pnew[bk] + k, nn, b.ci[bk] + o0);
     if (nn > 0) b.nnew[a] = 0;
-    // the chunk holding row a: the last one whose first row is <= a
-    int32_t lo = 0, hi = nchunk - 1;
-    while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (hdr[mid].v0 <= a) lo = mid;
-        else hi = mid - 1;
-    }
-    const int32_t v0 = hdr[lo].v0, v1 = v0 + hdr[lo].nown;
-    if (b.rp[bk][v1] - b.rp[bk][v0] > hdr[lo].amap_cap) atomicOr(&st->err_cur, 2);
+    const PatchHdr h = hdr[b.row_chunk[a]];
+    if (b.rp[bk][h.v0 + h.nown] - b.rp[bk][h.v0] > h.amap_cap) atomicOr(&st->err_cur, 2);
 }
 
 // One 64-thread workgroup (one wave) per row chunk or patch, walking its
@@ -254,6 +249,14 @@ hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32
                          InsertBufs b, const PatchHdr *hdr, int32_t npatch, int complete_cols,
                          hipStream_t s)
 {
+    // every array a kernel below dereferences must exist
+    for (int k = 1; k <= 2; ++k)
+        if (!b.rp[k] || !b.ci[k] || !b.pairs[k] || !b.pinc_ptr[k] || !b.pinc[k] ||
+            !b.pinc_row[k] || !b.pnew[k] || !b.trow[k])
+            return hipErrorInvalidValue;
+    if (!b.rp[0] || !b.ci[0] || !b.cnt || !b.nnew || !b.tmp || !hdr ||
+        (!complete_cols && !b.row_chunk))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_ins_count, dim3(blocks_for(np)), dim3(kThreads), 0, s, st, d_pairs, np,
                        nv, b);
     hipError_t e = launch_scan_back(b.cnt, b.pinc_ptr, nullptr, st, nv, b.tmp, s);
@@ -268,7 +271,7 @@ hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, int32
         hipLaunchKernelGGL(k_ins_merge, dim3(npatch), dim3(kMergeThreads), 0, s, st, hdr, b, 0);
     else
         hipLaunchKernelGGL(k_ins_merge_rows, dim3(blocks_for(2 * int64_t(np))), dim3(kThreads), 0,
-                           s, st, 2 * np, nv, b, hdr, npatch);
+                           s, st, 2 * np, b, hdr);
     hipLaunchKernelGGL(k_ins_commit, dim3(1), dim3(1), 0, s, st, np, nv, b);
     return hipGetLastError();
 }

@@ -144,6 +144,8 @@ struct PatternBufs {
     const int32_t *pinc_ptr[3];  // per-row pair incidence (buffers 1, 2)
     const int32_t *pinc[3];
     const int32_t *pinc_row[3];
+    const int32_t *trow[3];      // per incidence entry: its row if the entry is
+                                 // the row's first, else -1 (touched rows)
 };
 
 template <typename T>
@@ -220,6 +222,10 @@ hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int pairs, int *grid
 template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s);
+// The rows that current pairs touch (after launch_eval_rows, same stream).
+template <typename T>
+hipError_t launch_eval_pair_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
+                                 int grid, hipStream_t s);
 // Newton-CG direction formed inside the row HVP: the operand is
 // v = -r + beta d_old (beta read from the device), and every row stores its
 // v into d_new.  With r null the HVP's operand is v itself.
@@ -279,6 +285,8 @@ struct InsertBufs {
     int32_t *pinc[3];
     int32_t *pinc_row[3];
     int32_t *pnew[3];            // distinct new partners per row (scratch)
+    int32_t *trow[3];            // touched-row list, see PatternBufs::trow
+    const int32_t *row_chunk;    // [nv] chunk of each row (row path)
     int32_t *cnt;                // [nv], all zero between inserts
     int32_t *nnew;               // [nv] new blocks per row, all zero between inserts
     int32_t *tmp;                // scan scratch

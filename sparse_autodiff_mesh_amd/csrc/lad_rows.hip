@@ -507,13 +507,45 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         T *Hs = stage + pad;
         if (fits && int(threadIdx.x) < nrows) {
             const Row<T> r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
-            eacc += eval_row<T, FACES, PAIRS>(A, act, cia, r, sb, Hs, x, g);
+            // A row that pairs touch is left to k_eval_pair_rows (its slice
+            // of the staging area is streamed out unwritten and overwritten
+            // there); every other row has its topology columns, so it is
+            // evaluated with act = 0, which compiles the pair code out.
+            if (!PAIRS || r.p1 == r.p0)
+                eacc += eval_row<T, FACES, false>(A, 0, cia, r, sb, Hs, x, g);
         }
         wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
         wave_lds_sync();
     }
     store_energy(esink, block_sum<kRowThreads>(eacc, nullptr));
+}
+
+// Rows that current pairs touch: one thread per row (the thread of the row's
+// first pair-incidence entry, a fixed choice, so the energy sums keep their
+// order), which runs the full row evaluation -- column matching, pair terms
+// -- and writes the row's blocks and gradient straight to HBM.  It runs
+// after k_eval_rows on the same stream.  Only a few percent of the rows are
+// touched, but nearly every 64-row wave holds one, so handling them apart
+// keeps the divergent pair code out of the main kernel.  Every workgroup
+// stores a partial energy (zero when the topology pattern is active).
+template <typename T, bool FACES>
+__global__ void __launch_bounds__(kThreads)
+k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
+                 EnergySink esink)
+{
+    __shared__ double red[kThreads / 64];
+    const int act = A.state->active;
+    const int32_t k = int32_t(blockIdx.x) * kThreads + int32_t(threadIdx.x);
+    double e = 0.0;
+    if (act != 0 && k < A.pat.pinc_ptr[act][A.nv]) {
+        const int32_t a = A.pat.trow[act][k];
+        if (a >= 0) {
+            const Row<T> r = load_row(A, act, A.pat.rp[act], a, x);
+            e = eval_row<T, FACES, true>(A, act, A.pat.ci[act], r, 0, hv, x, g);
+        }
+    }
+    store_energy(esink, block_sum<kThreads>(e, red));
 }
 
 // ---------------------------------------------------------------------------
@@ -821,6 +853,23 @@ static void launch_eval_rows_as(const RowArgs<T> &a, const T *x, T *g, T *hv, En
 }
 
 template <typename T>
+hipError_t launch_eval_pair_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
+                                 int grid, hipStream_t s)
+{
+    for (int k = 1; k <= 2; ++k)  // the pair buffers the kernel may read
+        if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pairs[k] || !a.pat.pinc_ptr[k] ||
+            !a.pat.pinc[k] || !a.pat.trow[k])
+            return hipErrorInvalidValue;
+    if (a.faces_on)
+        hipLaunchKernelGGL((k_eval_pair_rows<T, true>), dim3(grid), dim3(kThreads), 0, s, a, x, g,
+                           hv, es);
+    else
+        hipLaunchKernelGGL((k_eval_pair_rows<T, false>), dim3(grid), dim3(kThreads), 0, s, a, x, g,
+                           hv, es);
+    return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                             int grid, hipStream_t s)
 {
@@ -864,6 +913,8 @@ hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, in
     template hipError_t rows_grid<T>(int, int, int, int, int *, int *);                           \
     template hipError_t launch_eval_rows<T>(const RowArgs<T> &, const T *, T *, T *, EnergySink,  \
                                             int, hipStream_t);                                    \
+    template hipError_t launch_eval_pair_rows<T>(const RowArgs<T> &, const T *, T *, T *,         \
+                                                 EnergySink, int, hipStream_t);                   \
     template hipError_t launch_hvp_rows<T>(const RowArgs<T> &, const T *, const T *, T *, int,    \
                                            hipStream_t, const CgDir<T> &);
 LAD_ROWS_INST(float)
