@@ -32,6 +32,7 @@ class OracleProblem(ctypes.Structure):
         ("face_energy", ctypes.c_int32), ("dm_inv", _f64p), ("area", _f64p),
         ("np", ctypes.c_int32), ("pairs", _i32p),
         ("kappa", ctypes.c_double), ("dhat", ctypes.c_double),
+        ("nvf", ctypes.c_int32), ("vf", _i32p),
     ]
 
 
@@ -67,6 +68,11 @@ def lib():
         L.oracle_face_grad_hyperdual.argtypes = [_f64p, _f64p, _f64p, _f64p,
                                                  ctypes.c_double, _f64p]
         L.oracle_face_grad_hyperdual.restype = None
+        L.oracle_vf_local.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_double,
+                                      ctypes.c_double, _f64p, _f64p, _f64p]
+        L.oracle_vf_local.restype = None
+        L.oracle_vf_distance_type.argtypes = [_f64p, _f64p, _f64p, _f64p]
+        L.oracle_vf_distance_type.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -89,7 +95,7 @@ class Problem:
 
     def __init__(self, nv, faces=None, springs=None, rest_len=None, k=0.0,
                  x_tilde=None, c=0.0, face_energy=False, dm_inv=None, area=None,
-                 pairs=None, kappa=0.0, dhat=0.0):
+                 pairs=None, kappa=0.0, dhat=0.0, vf=None):
         self.nv = int(nv)
         self.faces = _i32(faces if faces is not None else np.zeros((0, 3))).reshape(-1, 3)
         self.springs = _i32(springs if springs is not None else np.zeros((0, 2))).reshape(-1, 2)
@@ -104,6 +110,7 @@ class Problem:
         self.pairs = _i32(pairs if pairs is not None else np.zeros((0, 2))).reshape(-1, 2)
         self.kappa = float(kappa)
         self.dhat = float(dhat)
+        self.vf = _i32(vf if vf is not None else np.zeros((0, 2))).reshape(-1, 2)
 
     def with_pairs(self, pairs, kappa=None, dhat=None):
         import copy
@@ -134,6 +141,8 @@ class Problem:
         s.pairs = _p(self.pairs, _i32p)
         s.kappa = self.kappa
         s.dhat = self.dhat
+        s.nvf = self.vf.shape[0]
+        s.vf = _p(self.vf, _i32p)
         return s
 
 
@@ -242,8 +251,25 @@ def face_grad_hyperdual(x0, x1, x2, dm_inv, area):
     return g
 
 
+def vf_local(p, t0, t1, t2, kappa, dhat):
+    """Vertex-face barrier: (E, g (12,), H (12, 12)), local order p, t0, t1, t2."""
+    p, t0, t1, t2 = _f64(p), _f64(t0), _f64(t1), _f64(t2)
+    E = np.zeros(1)
+    g = np.zeros(12)
+    H = np.zeros((12, 12))
+    lib().oracle_vf_local(_p(p, _f64p), _p(t0, _f64p), _p(t1, _f64p), _p(t2, _f64p),
+                          float(kappa), float(dhat), _p(E, _f64p), _p(g, _f64p), _p(H, _f64p))
+    return float(E[0]), g, H
+
+
+def vf_distance_type(p, t0, t1, t2):
+    p, t0, t1, t2 = _f64(p), _f64(t0), _f64(t1), _f64(t2)
+    return int(lib().oracle_vf_distance_type(_p(p, _f64p), _p(t0, _f64p), _p(t1, _f64p),
+                                             _p(t2, _f64p)))
+
+
 def problem_from_mesh(mesh, springs=True, inertia=True, faces=False, pairs=None,
-                      kappa=0.0, dhat=0.0, k=None, c=None, f32=False):
+                      kappa=0.0, dhat=0.0, k=None, c=None, f32=False, vf=None):
     """Build a Problem from a generated mesh bundle.  With f32=True every real
     input is rounded to fp32 first (the inputs an fp32 evaluation sees)."""
     r = (lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)) if f32 else (lambda a: a)
@@ -257,4 +283,4 @@ def problem_from_mesh(mesh, springs=True, inertia=True, faces=False, pairs=None,
         x_tilde=r(mesh.X) if inertia else None, c=rs(cc),
         face_energy=faces, dm_inv=r(mesh.dm_inv) if faces else None,
         area=r(mesh.area) if faces else None,
-        pairs=pairs, kappa=rs(kappa), dhat=rs(dhat))
+        pairs=pairs, kappa=rs(kappa), dhat=rs(dhat), vf=vf)

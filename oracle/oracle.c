@@ -10,7 +10,7 @@
  * Source: page "Locality-Aware Automatic Differentiation on the GPU for
  * Mesh-Based Computations", section "Method" (objective F(x) = sum_j f_j(x_j)
  * and assembly through selection matrices S_j), key designs 3 and 4 (pattern
- * from topology plus runtime vertex-vertex pairs).
+ * from topology plus runtime vertex-vertex and vertex-face interactions).
  */
 #include "oracle.h"
 
@@ -34,7 +34,8 @@ static int cmp_rc(const void *a, const void *b)
 
 static int check_problem(const oracle_problem *p)
 {
-    if (!p || p->nv < 0 || p->nf < 0 || p->ns < 0 || p->np < 0) return -1;
+    if (!p || p->nv < 0 || p->nf < 0 || p->ns < 0 || p->np < 0 || p->nvf < 0) return -1;
+    if (p->nvf > 0 && !p->vf) return -1;
     if (p->nf > 0 && !p->faces) return -1;
     if (p->ns > 0 && (!p->springs || !p->rest_len)) return -1;
     if (p->np > 0 && !p->pairs) return -1;
@@ -46,6 +47,12 @@ static int check_problem(const oracle_problem *p)
         if (p->springs[i] < 0 || p->springs[i] >= p->nv) return -1;
     for (int64_t i = 0; i < 2 * (int64_t)p->np; ++i)
         if (p->pairs[i] < 0 || p->pairs[i] >= p->nv) return -1;
+    for (int32_t e = 0; e < p->nvf; ++e) {
+        int32_t v = p->vf[2 * (int64_t)e], f = p->vf[2 * (int64_t)e + 1];
+        if (v < 0 || v >= p->nv || f < 0 || f >= p->nf) return -1;
+        for (int i = 0; i < 3; ++i)
+            if (p->faces[3 * (int64_t)f + i] == v) return -1;
+    }
     return 0;
 }
 
@@ -54,7 +61,7 @@ static int check_problem(const oracle_problem *p)
 static rc_pair *directed_pairs(const oracle_problem *p, int64_t *count)
 {
     int64_t n = (int64_t)p->nv + 6 * (int64_t)p->nf + 2 * (int64_t)p->ns +
-                2 * (int64_t)p->np;
+                2 * (int64_t)p->np + 6 * (int64_t)p->nvf;
     rc_pair *e = (rc_pair *)malloc((size_t)(n > 0 ? n : 1) * sizeof(rc_pair));
     if (!e) return NULL;
     int64_t m = 0;
@@ -74,6 +81,14 @@ static rc_pair *directed_pairs(const oracle_problem *p, int64_t *count)
         int32_t a = p->pairs[2 * (int64_t)q], b = p->pairs[2 * (int64_t)q + 1];
         e[m].r = a; e[m].c = b; ++m;
         e[m].r = b; e[m].c = a; ++m;
+    }
+    for (int32_t q = 0; q < p->nvf; ++q) {
+        int32_t v = p->vf[2 * (int64_t)q], f = p->vf[2 * (int64_t)q + 1];
+        for (int i = 0; i < 3; ++i) {
+            int32_t t = p->faces[3 * (int64_t)f + i];
+            e[m].r = v; e[m].c = t; ++m;
+            e[m].r = t; e[m].c = v; ++m;
+        }
     }
     qsort(e, (size_t)m, sizeof(rc_pair), cmp_rc);
     *count = m;
@@ -328,6 +343,127 @@ void oracle_face_grad_hyperdual(const double *x0, const double *x1,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Vertex-face contact: barrier of the point-triangle distance              */
+/* ------------------------------------------------------------------------ */
+
+static double dot3(const double *a, const double *b)
+{
+    return a[0] * b[0] + a[1] * b[1] + a[2] * b[2];
+}
+
+/* Region of the triangle's closest point to p, from the signs of the
+ * projections of p onto the edge directions (the Voronoi regions of the
+ * three vertices, three edges and the face). */
+int oracle_vf_distance_type(const double *p, const double *t0, const double *t1,
+                            const double *t2)
+{
+    double e01[3], e02[3], q0[3], q1[3], q2[3];
+    for (int i = 0; i < 3; ++i) {
+        e01[i] = t1[i] - t0[i];
+        e02[i] = t2[i] - t0[i];
+        q0[i] = p[i] - t0[i];
+        q1[i] = p[i] - t1[i];
+        q2[i] = p[i] - t2[i];
+    }
+    /* projections onto e01 and e02 measured from each vertex */
+    double a1 = dot3(e01, q0), a2 = dot3(e02, q0);
+    if (a1 <= 0.0 && a2 <= 0.0) return 0;
+    double b1 = dot3(e01, q1), b2 = dot3(e02, q1);
+    if (b1 >= 0.0 && b2 <= b1) return 1;
+    double c1 = dot3(e01, q2), c2 = dot3(e02, q2);
+    if (c2 >= 0.0 && c1 <= c2) return 2;
+    /* edge regions: the barycentric weight of the opposite vertex is <= 0
+     * while p projects inside the edge */
+    if (a1 * b2 - b1 * a2 <= 0.0 && a1 >= 0.0 && b1 <= 0.0) return 3;          /* (t0,t1) */
+    if (b1 * c2 - c1 * b2 <= 0.0 && b2 - b1 >= 0.0 && c1 - c2 >= 0.0) return 4; /* (t1,t2) */
+    if (c1 * a2 - a1 * c2 <= 0.0 && a2 >= 0.0 && c2 <= 0.0) return 5;          /* (t2,t0) */
+    return 6;
+}
+
+static hd hd_sqrt(hd x)
+{
+    double s = sqrt(x.a), d1 = 0.5 / s, d2 = -0.25 / (s * x.a);
+    hd r = {s, d1 * x.b, d1 * x.c, d1 * x.d + d2 * x.b * x.c};
+    return r;
+}
+
+static hd hd_log(hd x)
+{
+    double d1 = 1.0 / x.a, d2 = -d1 * d1;
+    hd r = {log(x.a), d1 * x.b, d1 * x.c, d1 * x.d + d2 * x.b * x.c};
+    return r;
+}
+
+static hd hd_dot3(const hd *a, const hd *b)
+{
+    return hd_add(hd_add(hd_mul(a[0], b[0]), hd_mul(a[1], b[1])), hd_mul(a[2], b[2]));
+}
+
+static void hd_cross3(const hd *a, const hd *b, hd *c)
+{
+    c[0] = hd_sub(hd_mul(a[1], b[2]), hd_mul(a[2], b[1]));
+    c[1] = hd_sub(hd_mul(a[2], b[0]), hd_mul(a[0], b[2]));
+    c[2] = hd_sub(hd_mul(a[0], b[1]), hd_mul(a[1], b[0]));
+}
+
+/* Barrier of the distance of the given type, at hyper-dual coordinates
+ * X[0..2] = p, X[3..5] = t0, X[6..8] = t1, X[9..11] = t2. */
+static hd vf_energy_hd(const hd *X, int type, double kappa, double dhat)
+{
+    const hd *P = X, *T[3] = {X + 3, X + 6, X + 9};
+    hd d;
+    if (type <= 2) {                       /* |p - t_i| */
+        hd q[3];
+        for (int i = 0; i < 3; ++i) q[i] = hd_sub(P[i], T[type][i]);
+        d = hd_sqrt(hd_dot3(q, q));
+    } else if (type <= 5) {                /* |(p - t_i) x (t_j - t_i)| / |t_j - t_i| */
+        int i = type - 3, j = (type - 2) % 3;
+        hd q[3], e[3], c[3];
+        for (int k = 0; k < 3; ++k) {
+            q[k] = hd_sub(P[k], T[i][k]);
+            e[k] = hd_sub(T[j][k], T[i][k]);
+        }
+        hd_cross3(q, e, c);
+        d = hd_sqrt(hd_mul(hd_dot3(c, c), hd_inv(hd_dot3(e, e))));
+    } else {                               /* |(p - t0) . n| / |n| */
+        hd e1[3], e2[3], n[3], q[3];
+        for (int k = 0; k < 3; ++k) {
+            e1[k] = hd_sub(T[1][k], T[0][k]);
+            e2[k] = hd_sub(T[2][k], T[0][k]);
+            q[k] = hd_sub(P[k], T[0][k]);
+        }
+        hd_cross3(e1, e2, n);
+        hd s = hd_dot3(q, n);
+        d = hd_sqrt(hd_mul(hd_mul(s, s), hd_inv(hd_dot3(n, n))));
+    }
+    if (!(d.a < dhat)) return hd_make(0.0, 0.0, 0.0);
+    hd t = hd_sub(d, hd_make(dhat, 0.0, 0.0));
+    hd lg = hd_log(hd_scale(d, 1.0 / dhat));
+    return hd_scale(hd_mul(hd_mul(t, t), lg), -kappa);
+}
+
+void oracle_vf_local(const double *p, const double *t0, const double *t1,
+                     const double *t2, double kappa, double dhat, double *E,
+                     double *g12, double *H144)
+{
+    const double *xs[4] = {p, t0, t1, t2};
+    const int type = oracle_vf_distance_type(p, t0, t1, t2);
+    hd X[12];
+    for (int a = 0; a < 12; ++a)
+        for (int b = a; b < 12; ++b) {
+            for (int i = 0; i < 12; ++i)
+                X[i] = hd_make(xs[i / 3][i % 3], i == a ? 1.0 : 0.0, i == b ? 1.0 : 0.0);
+            hd e = vf_energy_hd(X, type, kappa, dhat);
+            H144[12 * a + b] = e.d;
+            H144[12 * b + a] = e.d;
+            if (a == b) {
+                g12[a] = e.b;
+                *E = e.a;
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Assembly: g = sum_j S_j^T g_j,  H = sum_j S_j^T H_j S_j                  */
 /* ------------------------------------------------------------------------ */
 
@@ -375,8 +511,8 @@ int oracle_eval(const oracle_problem *p, const int32_t *row_ptr,
     memset(g, 0, 3 * (size_t)p->nv * sizeof(double));
     memset(hvals, 0, 9 * (size_t)nnzb * sizeof(double));
     double E = 0.0;
-    double e, gl[9], Hl[81];
-    int32_t vid[3];
+    double e, gl[12], Hl[144];
+    int32_t vid[4];
 
     for (int32_t s = 0; s < p->ns; ++s) {
         vid[0] = p->springs[2 * (int64_t)s];
@@ -413,6 +549,15 @@ int oracle_eval(const oracle_problem *p, const int32_t *row_ptr,
                              p->kappa, p->dhat, &e, gl, Hl);
         E += e;
         if (scatter(row_ptr, col_idx, 2, vid, gl, Hl, g, hvals)) return -3;
+    }
+    for (int32_t q = 0; q < p->nvf; ++q) {
+        vid[0] = p->vf[2 * (int64_t)q];
+        for (int i = 0; i < 3; ++i) vid[1 + i] = p->faces[3 * (int64_t)p->vf[2 * (int64_t)q + 1] + i];
+        oracle_vf_local(x + 3 * (int64_t)vid[0], x + 3 * (int64_t)vid[1],
+                        x + 3 * (int64_t)vid[2], x + 3 * (int64_t)vid[3], p->kappa, p->dhat,
+                        &e, gl, Hl);
+        E += e;
+        if (scatter(row_ptr, col_idx, 4, vid, gl, Hl, g, hvals)) return -3;
     }
     *energy = E;
     return 0;

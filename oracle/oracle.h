@@ -20,7 +20,8 @@
  *    always present, columns ascending within a row; block k holds
  *    d2F / dx_{row,r} dx_{col_idx[k],c} at vals[9k + 3r + c].
  *  - the pattern row of vertex a is {a} U {b : a, b share a face or a
- *    spring} U {pair partners of a}.
+ *    spring} U {pair partners of a} U {the face vertices of a's vertex-face
+ *    contacts} U {the vertices in contact with a face of a}.
  *  - the Hessian is exact (no projection or clamping).
  *
  * Every function returns 0 on success and a negative value on bad input.
@@ -50,6 +51,9 @@ typedef struct {
     int32_t np;                  /* vertex-vertex pairs; pairs[2*p + i] */
     const int32_t *pairs;
     double kappa, dhat;          /* barrier stiffness and support */
+    int32_t nvf;                 /* vertex-face contacts; vf[2*e] = vertex,
+                                    vf[2*e + 1] = face id (not one of its own) */
+    const int32_t *vf;
 } oracle_problem;
 
 /* Pattern: number of blocks, then the arrays (row_ptr[nv+1], col_idx[nnzb]). */
@@ -84,6 +88,17 @@ void oracle_inertia_local(const double *xv, const double *xt, double c,
 void oracle_face_local(const double *x0, const double *x1, const double *x2,
                        const double *dm_inv, double area, double *E,
                        double *g9, double *H81);
+/* Vertex-face contact: the barrier b(d) of the distance d from point p to
+ * the triangle (t0, t1, t2).  The closest point's region is decided at the
+ * given positions (type 0-2: vertex t_i; 3, 4, 5: the interior of edge
+ * (t0,t1), (t1,t2), (t2,t0); 6: the face interior) and d is that region's
+ * smooth formula; E, g12 and H144 (local DOF order p, t0, t1, t2) are its
+ * value and exact derivatives. */
+int oracle_vf_distance_type(const double *p, const double *t0, const double *t1,
+                            const double *t2);
+void oracle_vf_local(const double *p, const double *t0, const double *t1,
+                     const double *t2, double kappa, double dhat, double *E,
+                     double *g12, double *H144);
 /* Face gradient taken from the hyper-dual evaluator instead of the closed
  * form (for cross-checking the two). */
 void oracle_face_grad_hyperdual(const double *x0, const double *x1,

@@ -39,6 +39,7 @@ _MASK = (1 << 64) - 1
 SEED_POSITIONS = 1
 SEED_HVP_DIRECTION = 2
 SEED_CONTACT_BASE = 1000
+SEED_VF_BASE = 2000
 
 
 # ----------------------------------------------------------------------------
@@ -257,6 +258,84 @@ def contact_pairs(mesh: Mesh, x: np.ndarray, step: int, frac: float = 0.02,
         nrm = math.sqrt(g0 * g0 + g1 * g1 + g2 * g2)
         xn[b] = x[a] + (d / nrm) * np.array([g0, g1, g2])
     return pairs, xn
+
+
+def vf_contacts(mesh: Mesh, x: np.ndarray, step: int, frac: float = 0.02,
+                dhat: float | None = None):
+    """Seeded vertex-face contacts for one step on a grid mesh.
+
+    Q = round(frac * V) faces are drawn without replacement; each gets a
+    contact vertex drawn uniformly among the vertices that belong to no
+    drawn face and are not already used.  The vertex is then moved to
+    distance d ~ U(0.2*dhat, 0.9*dhat) from its face, cycling through three
+    placements so that every closest-point region occurs, each well inside
+    its region:
+      k % 3 == 0  above the face interior (barycentric weights >= 0.2),
+      k % 3 == 1  beside an edge (edge parameter in [0.3, 0.7], elevation
+                  20..70 degrees out of the face plane),
+      k % 3 == 2  beyond a vertex (along the outward bisector of its two
+                  edges, same elevation range).
+    The side of the face plane is random.  Returns (vf int32 (Q, 2) of
+    (vertex, face id), positions (V, 3) fp64).
+    """
+    V = mesh.nv
+    F = mesh.faces.shape[0]
+    if dhat is None:
+        dhat = 0.5 * mesh.h
+    Q = int(round(frac * V))
+    if 4 * Q > V or Q > F:
+        raise ValueError("too many vertex-face contacts for this grid")
+    rng = SplitMix64(SEED_VF_BASE + step)
+    fperm = list(range(F))
+    in_face = bytearray(V)
+    faces = []
+    for k in range(Q):
+        r = k + int(rng.uniform() * (F - k))
+        fperm[k], fperm[r] = fperm[r], fperm[k]
+        faces.append(fperm[k])
+        for t in mesh.faces[fperm[k]]:
+            in_face[int(t)] = 1
+    used = bytearray(V)
+    vf = np.empty((Q, 2), dtype=np.int32)
+    for k, f in enumerate(faces):
+        while True:
+            v = int(rng.uniform() * V)
+            if not in_face[v] and not used[v]:
+                break
+        used[v] = 1
+        vf[k] = (v, f)
+    xn = x.copy()
+    for k in range(Q):
+        v, f = int(vf[k, 0]), int(vf[k, 1])
+        t = [x[int(i)] for i in mesh.faces[f]]
+        nrm = np.cross(t[1] - t[0], t[2] - t[0])
+        nrm /= np.linalg.norm(nrm)
+        d = dhat * (0.2 + 0.7 * rng.uniform())
+        side = 1.0 if rng.uniform() < 0.5 else -1.0
+        theta = math.radians(20.0 + 50.0 * rng.uniform())
+        kind = k % 3
+        if kind == 0:
+            w = np.array([1.0 + rng.uniform(), 1.0 + rng.uniform(), 1.0 + rng.uniform()])
+            w /= w.sum()
+            xn[v] = w[0] * t[0] + w[1] * t[1] + w[2] * t[2] + side * d * nrm
+        elif kind == 1:
+            i = min(int(3 * rng.uniform()), 2)
+            j, o = (i + 1) % 3, (i + 2) % 3
+            lam = 0.3 + 0.4 * rng.uniform()
+            m = t[i] + lam * (t[j] - t[i])
+            a = (t[j] - t[i]) / np.linalg.norm(t[j] - t[i])
+            out = np.cross(a, nrm)
+            if np.dot(t[o] - m, out) > 0.0:
+                out = -out
+            xn[v] = m + d * (math.cos(theta) * out + side * math.sin(theta) * nrm)
+        else:
+            i = min(int(3 * rng.uniform()), 2)
+            a1 = (t[(i + 1) % 3] - t[i]) / np.linalg.norm(t[(i + 1) % 3] - t[i])
+            a2 = (t[(i + 2) % 3] - t[i]) / np.linalg.norm(t[(i + 2) % 3] - t[i])
+            w = -(a1 + a2)
+            w /= np.linalg.norm(w)
+            xn[v] = t[i] + d * (math.cos(theta) * w + side * math.sin(theta) * nrm)
+    return vf, xn
 
 
 # ----------------------------------------------------------------------------
