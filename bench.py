@@ -18,7 +18,8 @@ Prints ONE JSON line.  Besides the contract fields it carries
                 launch; ms_per_step includes the energy sum);
   cpu_baseline  the fp64 CPU oracle, single-threaded, on the same workload;
   secondary     the other workloads (face-energy grid eval and matrix-free
-                HVP, cloth plus contact-pair insertion, 100 x 100 cloth).
+                HVP, cloth plus contact-pair insertion, cloth plus
+                vertex-face contact insertion, 100 x 100 cloth).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--n 1000]
                     [--no-cpu-baseline] [--no-secondary] [--flush-mall]
@@ -316,6 +317,32 @@ def bench_secondary(torch, binding, inputs, args, timer):
         raise RuntimeError("pair insertion reported a device-side error")
     L.close()
     sec["pairs_per_step"] = P
+    # the same cloth + 2 % vertex-face contacts per step, fp32
+    L = binding.Lad(m.nv, dtype="f32",
+                    **binding.mesh_terms(m, vf_capacity=P, dhat=dhat, kappa=inputs.BARRIER_KAPPA))
+    sets = []
+    for step in range(3):
+        vf, xs = inputs.vf_contacts(m, m.x, step, dhat=dhat)
+        sets.append((torch.tensor(vf, dtype=torch.int32, device="cuda"), to_dev(torch, xs, "f32")))
+    out = L.alloc_outputs()
+    state = {"i": 0}
+
+    def vf_step():
+        c, xx = sets[state["i"] % len(sets)]
+        state["i"] += 1
+        L.insert_contacts(vf=c)
+        L.eval(xx, out=out)
+
+    r = timer.run(vf_step, steps, warm)
+    sec["cloth1000_vf_insert_eval_ms"] = round(r["median_ms"], 5)
+    rh = timer.run(lambda: L.hvp(sets[0][1], vdir, out=yv), steps, warm)
+    sec["cloth1000_vf_hvp_ms"] = round(rh["median_ms"], 5)
+    ri = timer.run(lambda: L.insert_contacts(vf=sets[0][0]), steps, warm)
+    sec["cloth1000_vf_insert_ms"] = round(ri["median_ms"], 5)
+    if L.device_status() != 0:
+        raise RuntimeError("contact insertion reported a device-side error")
+    L.close()
+    sec["vf_contacts_per_step"] = P
     return sec
 
 

@@ -99,6 +99,9 @@ typedef struct {
     double dhat;                /* pair barrier support, > 0 if pair_capacity>0 */
 
     int32_t eval_path;          /* LAD_PATH_AUTO, LAD_PATH_PATCH or LAD_PATH_ROWS */
+    int32_t vf_capacity;        /* max vertex-face contacts per
+                                   lad_insert_contacts, >= 0; > 0 needs faces
+                                   (nf > 0) and the row path                  */
 } lad_mesh_desc;
 
 /* Parallel decomposition of the evaluation and HVP kernels.
@@ -106,11 +109,11 @@ typedef struct {
  *                  every element touching an owned row is evaluated once per
  *                  such patch and scattered into the patch's rows, which are
  *                  accumulated in LDS and streamed out.  Any mix of terms.
- *  LAD_PATH_ROWS   row owner: one lane per block row evaluates every spring,
- *                  inertia and pair term of that row; each block is written
- *                  once, in a fixed order, without atomics.  Requires no face
- *                  term, rest lengths >= 0 and at most one spring per vertex
- *                  pair.
+ *  LAD_PATH_ROWS   row owner: one lane per block row evaluates every term of
+ *                  that row; each block is written once, in a fixed order,
+ *                  without atomics.  Requires rest lengths >= 0, at most one
+ *                  spring per vertex pair and, with face terms, rows shorter
+ *                  than 256 blocks.
  *  LAD_PATH_AUTO   LAD_PATH_ROWS when its requirements hold, else PATCH.  */
 enum { LAD_PATH_AUTO = 0, LAD_PATH_PATCH = 1, LAD_PATH_ROWS = 2 };
 
@@ -136,6 +139,8 @@ typedef struct {
                                    context, this lad_get_info call included;
                                    lad_eval_energy_grad_hess, lad_hvp and
                                    lad_insert_pairs never add to it          */
+    int32_t nvf_active;         /* vertex-face contacts of the active pattern  */
+    int32_t pad0;
 } lad_info;
 
 /*
@@ -184,7 +189,8 @@ lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
  *   d_energy device double, overwritten with F(x); or NULL, in which case the
  *            energy is not summed (one small kernel launch is saved: the
  *            evaluation itself is then a single launch on the row path,
- *            two with pair capacity).
+ *            two with pair capacity, three with vertex-face capacity: the
+ *            contact terms, the untouched rows, the rows contacts touch).
  *   d_grad   device [nv][3] dtype, fully overwritten.
  *   d_hvals  device [hvals_capacity][3][3] dtype; the first nnzb_active
  *            blocks are fully overwritten in the active pattern's order.
@@ -307,7 +313,28 @@ lad_status lad_newton_cg(lad_ctx *ctx, const void *d_x, const void *d_g, void *d
                          void *hip_stream);
 
 /*
- * Replace the runtime vertex-vertex pairs: the next pattern is
+ * Replace the runtime contacts: vertex-vertex pairs (barrier of |x_i - x_j|,
+ * as lad_insert_pairs) and vertex-face contacts (v, face f) with the same
+ * barrier applied to the distance from x_v to the triangle f; the region of
+ * the triangle's closest point (vertex, edge interior, face interior) is
+ * decided at the positions of each evaluation and d is that region's smooth
+ * formula.  The next pattern is topology U {(i,j),(j,i)} for every pair
+ * U {(v,t),(t,v) for t in f} for every contact, sorted and de-duplicated;
+ * the previous contacts are dropped.  Source: key design 4 (runtime
+ * vertex-vertex and vertex-face interactions, double-buffered CSR).
+ *   d_pairs  device int32 [npairs][2], 0 <= npairs <= pair_capacity.
+ *   d_vf     device int32 [nvf][2] of (vertex, face id), 0 <= nvf <=
+ *            vf_capacity; the vertex must not belong to the face.
+ * npairs = nvf = 0 restores the topology pattern.  Errors and device-side
+ * checks as lad_insert_pairs (LAD_ERR_CAPACITY for either count).
+ * Asynchronous.
+ */
+lad_status lad_insert_contacts(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs,
+                               const int32_t *d_vf, int32_t nvf, void *hip_stream);
+
+/*
+ * Replace the runtime vertex-vertex pairs (and drop any vertex-face
+ * contacts): the next pattern is
  * topology U {(i,j),(j,i) for every pair}, sorted and de-duplicated; the
  * previous pairs are dropped.  Built on the GPU into the inactive one of two
  * reserved pattern buffers, then made active by a device-side swap (no host

@@ -52,6 +52,7 @@ class lad_mesh_desc(ctypes.Structure):
         ("face_energy", ctypes.c_int32), ("dm_inv", _f64p), ("area", _f64p),
         ("kappa", ctypes.c_double), ("dhat", ctypes.c_double),
         ("eval_path", ctypes.c_int32),
+        ("vf_capacity", ctypes.c_int32),
     ]
 
 
@@ -65,6 +66,7 @@ class lad_info(ctypes.Structure):
         ("face_records", ctypes.c_int64), ("max_colors", ctypes.c_int32),
         ("active_buffer", ctypes.c_int32), ("eval_path", ctypes.c_int32),
         ("grid_eval", ctypes.c_int32), ("host_syncs", ctypes.c_int64),
+        ("nvf_active", ctypes.c_int32), ("pad0", ctypes.c_int32),
     ]
 
 
@@ -80,6 +82,7 @@ LAD_CG_CONVERGED, LAD_CG_NEG_CURVATURE, LAD_CG_MAX_ITERS = 0, 1, 2
 EXPORTS = [
     "lad_build_pattern", "lad_get_info", "lad_get_pattern", "lad_copy_pattern",
     "lad_eval_energy_grad_hess", "lad_hvp", "lad_newton_cg", "lad_insert_pairs",
+    "lad_insert_contacts",
     "lad_jacobian_pattern", "lad_copy_jacobian_pattern", "lad_residual_jacobian",
     "lad_gauss_newton_product",
     "lad_device_status", "lad_last_error", "lad_status_string", "lad_destroy",
@@ -116,6 +119,7 @@ def lib():
         L.lad_residual_jacobian.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.lad_gauss_newton_product.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.lad_insert_pairs.argtypes = [_vp, _vp, ctypes.c_int32, _vp]
+        L.lad_insert_contacts.argtypes = [_vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp]
         L.lad_device_status.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]
         L.lad_last_error.argtypes = [_vp]
         L.lad_last_error.restype = ctypes.c_char_p
@@ -211,6 +215,11 @@ def lad_gauss_newton_product(ctx, d_x, d_v, d_y, stream=None):
     _check(lib().lad_gauss_newton_product(ctx, _vp(d_x), _vp(d_v), _vp(d_y), _vp(stream)), ctx)
 
 
+def lad_insert_contacts(ctx, d_pairs, npairs, d_vf, nvf, stream=None):
+    _check(lib().lad_insert_contacts(ctx, _vp(d_pairs), int(npairs), _vp(d_vf), int(nvf),
+                                     _vp(stream)), ctx)
+
+
 def lad_insert_pairs(ctx, d_pairs, npairs, stream=None):
     _check(lib().lad_insert_pairs(ctx, _vp(d_pairs), int(npairs), _vp(stream)), ctx)
 
@@ -240,7 +249,8 @@ def _ptr(a, t):
 
 def make_desc(nv, faces=None, springs=None, rest_len=None, k=0.0, x_tilde=None, c=0.0,
               face_energy=False, dm_inv=None, area=None, pair_capacity=0, kappa=0.0,
-              dhat=0.0, dtype="f32", deterministic=False, patch_lds_bytes=0, path="auto"):
+              dhat=0.0, dtype="f32", deterministic=False, patch_lds_bytes=0, path="auto",
+              vf_capacity=0):
     """Fill a lad_mesh_desc from numpy arrays.  Returns (desc, keepalive)."""
     keep = {
         "faces": _i32(faces if faces is not None else np.zeros((0, 3))),
@@ -271,6 +281,7 @@ def make_desc(nv, faces=None, springs=None, rest_len=None, k=0.0, x_tilde=None, 
     d.kappa = float(kappa)
     d.dhat = float(dhat)
     d.eval_path = _PATHS[path] if isinstance(path, str) else int(path)
+    d.vf_capacity = int(vf_capacity)
     return d, keep
 
 
@@ -364,6 +375,18 @@ class Lad:
         lad_gauss_newton_product(self.ctx, x.data_ptr(), v.data_ptr(), y.data_ptr(), _stream())
         return y
 
+    def insert_contacts(self, pairs=None, vf=None):
+        """pairs: int32 cuda tensor (P, 2) or None; vf: int32 cuda tensor
+        (Q, 2) of (vertex, face id) or None.  Both empty restores the
+        topology pattern."""
+        np_ = 0 if pairs is None else pairs.shape[0]
+        nvf = 0 if vf is None else vf.shape[0]
+        for t in (pairs, vf):
+            if t is not None and t.numel():
+                assert t.dtype == self.torch.int32 and t.is_cuda and t.is_contiguous()
+        lad_insert_contacts(self.ctx, pairs.data_ptr() if np_ else None, np_,
+                            vf.data_ptr() if nvf else None, nvf, _stream())
+
     def insert_pairs(self, pairs):
         """pairs: int32 cuda tensor (P, 2), or None / empty for no pairs."""
         if pairs is None or pairs.numel() == 0:
@@ -387,7 +410,7 @@ class Lad:
 
 
 def mesh_terms(mesh, springs=True, inertia=True, faces=False, pair_capacity=0,
-               kappa=0.0, dhat=0.0):
+               kappa=0.0, dhat=0.0, vf_capacity=0):
     """Keyword arguments of Lad(...) for a generated grid bundle."""
     kw = {"faces": mesh.faces}
     if springs:
@@ -396,6 +419,6 @@ def mesh_terms(mesh, springs=True, inertia=True, faces=False, pair_capacity=0,
         kw.update(x_tilde=mesh.X, c=mesh.params.get("c", 0.0))
     if faces:
         kw.update(face_energy=True, dm_inv=mesh.dm_inv, area=mesh.area)
-    if pair_capacity:
-        kw.update(pair_capacity=pair_capacity, kappa=kappa, dhat=dhat)
+    if pair_capacity or vf_capacity:
+        kw.update(pair_capacity=pair_capacity, vf_capacity=vf_capacity, kappa=kappa, dhat=dhat)
     return kw

@@ -26,6 +26,8 @@ struct lad_ctx {
     hipStream_t stream = nullptr;
     int64_t nnzb_base = 0, hcap = 0;
     int32_t pair_cap = 0;
+    int32_t vf_cap = 0;              // vertex-face contact capacity
+    int32_t nf = 0;
     double k = 0, c = 0, kappa = 0, dhat = 0;
     int32_t springs_on = 0, faces_on = 0, inertia_on = 0;
     int32_t npatch = 0, lds_eval = 0, lds_hvp = 0, max_colors = 0;
@@ -59,6 +61,9 @@ struct lad_ctx {
     // and the Jacobian pattern (built by the first lad_jacobian_pattern call)
     int32_t ns = 0;
     int32_t *d_springs = nullptr;
+    int32_t *d_faces = nullptr;      // kept on the device for vertex-face contacts
+    void *d_vf_eval = nullptr;       // per-contact local terms (kVfEvalComps x vf_cap)
+    void *d_vf_hvp = nullptr;        // per-contact H_e u_e (kVfHvpComps x vf_cap)
     void *d_spring_rest = nullptr;
     int32_t *d_jrp = nullptr, *d_jci = nullptr;
     // Newton-CG work space, allocated by the first lad_newton_cg call
@@ -121,6 +126,10 @@ std::string check_desc(const lad_mesh_desc *d)
     if (d->nf < 0 || d->ns < 0) return "nf and ns must be >= 0";
     if (d->dtype != LAD_F32 && d->dtype != LAD_F64) return "dtype must be LAD_F32 or LAD_F64";
     if (d->pair_capacity < 0) return "pair_capacity must be >= 0";
+    if (d->vf_capacity < 0) return "vf_capacity must be >= 0";
+    if (d->vf_capacity > 0 && d->nf == 0) return "vertex-face contacts need faces";
+    if (d->vf_capacity > 0 && d->eval_path == LAD_PATH_PATCH)
+        return "vertex-face contacts need the row path";
     if (d->eval_path != LAD_PATH_AUTO && d->eval_path != LAD_PATH_PATCH &&
         d->eval_path != LAD_PATH_ROWS)
         return "eval_path must be LAD_PATH_AUTO, LAD_PATH_PATCH or LAD_PATH_ROWS";
@@ -148,10 +157,11 @@ std::string check_desc(const lad_mesh_desc *d)
         if (!std::isfinite(d->c)) return "non-finite c";
     }
     if (d->face_energy && d->nf > 0 && (!d->dm_inv || !d->area)) return "dm_inv or area is NULL";
-    if (d->pair_capacity > 0) {
-        if (!(d->dhat > 0) || !std::isfinite(d->dhat)) return "dhat must be > 0 with pairs";
+    if (d->pair_capacity > 0 || d->vf_capacity > 0) {
+        if (!(d->dhat > 0) || !std::isfinite(d->dhat)) return "dhat must be > 0 with contacts";
         if (!std::isfinite(d->kappa)) return "non-finite kappa";
-        if (int64_t(d->pair_capacity) * 2 >= (int64_t(1) << 30)) return "pair_capacity too large";
+        if (2 * int64_t(d->pair_capacity) + 4 * int64_t(d->vf_capacity) >= (int64_t(1) << 29))
+            return "pair_capacity / vf_capacity too large";
     }
     const int64_t raw = int64_t(d->nv) + 6 * int64_t(d->nf) + 2 * int64_t(d->ns);
     if (raw >= (int64_t(1) << 31)) return "mesh too large for int32 pattern indices";
@@ -266,10 +276,13 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.springs_on = ctx->springs_on;
     a.inertia_on = ctx->inertia_on;
     a.faces_on = ctx->faces_on;
-    a.pairs_on = ctx->pair_cap > 0 ? 1 : 0;
+    a.pairs_on = (ctx->pair_cap > 0 || ctx->vf_cap > 0) ? 1 : 0;
     a.lds_blocks = kRowLdsBlocks;
     a.state = ctx->d_state;
     a.pat = ctx->pat;
+    a.vf_eval = static_cast<T *>(ctx->d_vf_eval);
+    a.vf_hvp = static_cast<T *>(ctx->d_vf_hvp);
+    a.vf_stride = ctx->vf_cap;
     return a;
 }
 
@@ -282,10 +295,13 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
     hipError_t e = hipSuccess;
     int32_t nparts = 0;
     if (ctx->row_mode) {
-        // every row that no pair touches, then the touched rows
-        e = launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x), static_cast<T *>(g),
-                                static_cast<T *>(hv), EnergySink{ctx->d_epart, 0}, ctx->grid_eval,
-                                s);
+        // the vertex-face contact terms (one thread each), every row that no
+        // contact touches, then the touched rows, which add the contact terms
+        if (ctx->vf_cap > 0) e = launch_vf_eval<T>(row_args<T>(ctx), static_cast<const T *>(x), s);
+        if (e == hipSuccess)
+            e = launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
+                                    static_cast<T *>(g), static_cast<T *>(hv),
+                                    EnergySink{ctx->d_epart, 0}, ctx->grid_eval, s);
         nparts = ctx->grid_eval;
         // rows touched by pairs, one thread each
         if (e == hipSuccess && ctx->pair_blocks > 0) {
@@ -338,6 +354,12 @@ hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipS
         a.hvp_dot = dot_parts;
         a.hvp_skip = skip;
         if (dot_parts_used && dot_parts) *dot_parts_used = ctx->grid_hvp;
+        // the vertex-face contacts' H_e u_e first (the rows add them)
+        if (ctx->vf_cap > 0) {
+            const hipError_t e = launch_vf_hvp<T>(a, static_cast<const T *>(x),
+                                                  static_cast<const T *>(v), s, cg);
+            if (e != hipSuccess) return e;
+        }
         return launch_hvp_rows<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
                                   static_cast<T *>(y), ctx->grid_hvp, s, cg);
     }
@@ -452,6 +474,8 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     ctx->det = d->deterministic ? 1 : 0;
     ctx->stream = s;
     ctx->pair_cap = d->pair_capacity;
+    ctx->vf_cap = d->vf_capacity;
+    ctx->nf = d->nf;
     ctx->k = d->k;
     ctx->c = d->c;
     ctx->kappa = d->kappa;
@@ -478,7 +502,10 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     const int64_t raw = int64_t(nv) + 6 * int64_t(d->nf) + 2 * int64_t(d->ns);
     int32_t *d_faces = nullptr, *d_springs = nullptr;
     PatternScratch sc{};
-    e = tmp_alloc(&d_faces, size_t(d->nf) * 3);
+    // the faces stay on the device when vertex-face contacts may reference them
+    e = d->vf_capacity > 0 ? dev_alloc(ctx, &d_faces, size_t(d->nf) * 3)
+                           : tmp_alloc(&d_faces, size_t(d->nf) * 3);
+    if (d->vf_capacity > 0) ctx->d_faces = d_faces;
     // the springs stay on the device for the vector objective
     if (e == hipSuccess) e = dev_alloc(ctx, &d_springs, size_t(d->ns) * 2);
     ctx->d_springs = d_springs;
@@ -513,7 +540,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     }
     const int64_t nnzb = h_rp[nv];
     ctx->nnzb_base = nnzb;
-    ctx->hcap = nnzb + 2 * int64_t(d->pair_capacity);
+    ctx->hcap = nnzb + 2 * int64_t(d->pair_capacity) + 6 * int64_t(d->vf_capacity);
     if (ctx->hcap * 9 >= (int64_t(1) << 31)) {
         free_temps();
         return fail(ctx, LAD_ERR_ARG, "pattern too large for int32 value indices");
@@ -546,6 +573,8 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (d->eval_path == LAD_PATH_ROWS && !why.empty())
         return fail(ctx, LAD_ERR_ARG, "row path not applicable: " + why);
     ctx->row_mode = why.empty() ? 1 : 0;
+    if (!ctx->row_mode && d->vf_capacity > 0)
+        return fail(ctx, LAD_ERR_ARG, "vertex-face contacts need the row path: " + why);
     if (ctx->row_mode) {
         plan.hdr = rplan.chunk;
         ctx->lds_eval = ctx->es == 8 ? rows_lds_bytes<double>(kRowLdsBlocks)
@@ -575,7 +604,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     // (the pointer is stored in ctx->ins after that struct is reset below)
     std::vector<int32_t> row_chunk;
     int32_t *d_row_chunk = nullptr;
-    if (e == hipSuccess && ctx->row_mode && d->pair_capacity > 0) {
+    if (e == hipSuccess && ctx->row_mode && (d->pair_capacity > 0 || d->vf_capacity > 0)) {
         row_chunk.resize(size_t(nv));
         for (size_t c = 0; c < plan.hdr.size(); ++c)
             for (int32_t a = plan.hdr[c].v0; a < plan.hdr[c].v0 + plan.hdr[c].nown; ++a)
@@ -588,9 +617,11 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (st != LAD_OK) return st;
     if (ctx->row_mode) {
         e = ctx->dtype == LAD_F64
-                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, ctx->pair_cap > 0,
+                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, ctx->faces_on,
+                                    ctx->pair_cap > 0 || ctx->vf_cap > 0,
                                     &ctx->grid_eval, &ctx->grid_hvp)
-                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, ctx->faces_on, ctx->pair_cap > 0,
+                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, ctx->faces_on,
+                                   ctx->pair_cap > 0 || ctx->vf_cap > 0,
                                    &ctx->grid_eval, &ctx->grid_hvp);
         if (e != hipSuccess) return hip_fail(ctx, e, "occupancy query");
     } else {
@@ -611,17 +642,19 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     hs.nnzb[0] = int32_t(nnzb);
     if (e == hipSuccess)
         e = hipMemcpyAsync(ctx->d_state, &hs, sizeof(hs), hipMemcpyHostToDevice, s);
-    if (e == hipSuccess && d->pair_capacity > 0) {
-        const size_t cap2 = size_t(d->pair_capacity) * 2;
+    if (e == hipSuccess && (d->pair_capacity > 0 || d->vf_capacity > 0)) {
+        // incidence entries: 2 per pair, 4 per vertex-face contact
+        const size_t ninc = 2 * size_t(d->pair_capacity) + 4 * size_t(d->vf_capacity);
         for (int b = 1; b <= 2 && e == hipSuccess; ++b) {
             e = dev_alloc(ctx, &ctx->ins.rp[b], size_t(nv) + 1);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.ci[b], size_t(ctx->hcap));
-            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pairs[b], cap2);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pairs[b], 2 * size_t(d->pair_capacity));
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.vf[b], 2 * size_t(d->vf_capacity));
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_ptr[b], size_t(nv) + 1);
-            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc[b], cap2);
-            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_row[b], cap2);
-            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pnew[b], cap2);
-            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.trow[b], cap2);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc[b], ninc);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_row[b], ninc);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pnew[b], 3 * ninc);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.trow[b], ninc);
         }
         if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.cnt, size_t(nv));
         if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.cnt, 0, size_t(nv) * 4, s);
@@ -636,8 +669,19 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             ctx->pat.pinc[b] = ctx->ins.pinc[b];
             ctx->pat.pinc_row[b] = ctx->ins.pinc_row[b];
             ctx->pat.trow[b] = ctx->ins.trow[b];
+            ctx->pat.vf[b] = ctx->ins.vf[b];
         }
-        ctx->pair_blocks = int32_t((cap2 + kThreads - 1) / kThreads);
+        ctx->ins.faces = ctx->d_faces;
+        ctx->pat.faces = ctx->d_faces;
+        if (e == hipSuccess && d->vf_capacity > 0) {
+            char *ve = nullptr, *vh = nullptr;
+            const size_t cap = size_t(d->vf_capacity) * size_t(ctx->es);
+            e = dev_alloc(ctx, &ve, size_t(kVfEvalComps) * cap);
+            if (e == hipSuccess) e = dev_alloc(ctx, &vh, size_t(kVfHvpComps) * cap);
+            ctx->d_vf_eval = ve;
+            ctx->d_vf_hvp = vh;
+        }
+        ctx->pair_blocks = int32_t((ninc + kThreads - 1) / kThreads);
     }
     if (e == hipSuccess)
         e = dev_alloc(ctx, &ctx->d_epart,
@@ -651,7 +695,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
 
 lad_status check_vector_objective(lad_ctx *ctx)
 {
-    if (ctx->faces_on || ctx->pair_cap > 0)
+    if (ctx->faces_on || ctx->pair_cap > 0 || ctx->vf_cap > 0)
         return fail(ctx, LAD_ERR_STATE,
                     "the vector objective covers spring and inertia terms; this context has face "
                     "or pair terms");
@@ -721,6 +765,7 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     info->nnzb_active = hs.active == 0 ? ctx->nnzb_base : hs.nnzb[hs.active];
     info->hvals_capacity = ctx->hcap;
     info->npairs_active = hs.active == 0 ? 0 : hs.np[hs.active];
+    info->nvf_active = hs.active == 0 ? 0 : hs.nvf[hs.active];
     info->npatches = ctx->npatch;
     info->lds_bytes_eval = ctx->lds_eval;
     info->lds_bytes_hvp = ctx->lds_hvp;
@@ -905,24 +950,37 @@ lad_status lad_gauss_newton_product(lad_ctx *ctx, const void *d_x, const void *d
     return LAD_OK;
 }
 
-lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs, void *hip_stream)
+lad_status lad_insert_contacts(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs,
+                               const int32_t *d_vf, int32_t nvf, void *hip_stream)
 {
     if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
-    if (npairs < 0) return fail(ctx, LAD_ERR_ARG, "npairs must be >= 0");
+    if (npairs < 0 || nvf < 0) return fail(ctx, LAD_ERR_ARG, "npairs and nvf must be >= 0");
     if (npairs > ctx->pair_cap)
         return fail(ctx, LAD_ERR_CAPACITY,
                     "npairs " + std::to_string(npairs) + " exceeds pair_capacity " +
                         std::to_string(ctx->pair_cap));
+    if (nvf > ctx->vf_cap)
+        return fail(ctx, LAD_ERR_CAPACITY,
+                    "nvf " + std::to_string(nvf) + " exceeds vf_capacity " +
+                        std::to_string(ctx->vf_cap));
     if (npairs > 0 && !d_pairs) return fail(ctx, LAD_ERR_ARG, "d_pairs is NULL");
+    if (nvf > 0 && !d_vf) return fail(ctx, LAD_ERR_ARG, "d_vf is NULL");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = npairs == 0 ? launch_restore_topology(ctx->d_state, s)
-                               : launch_insert(ctx->d_state, d_pairs, npairs, ctx->nv, ctx->ins,
-                                               ctx->d_hdr, ctx->npatch, ctx->row_mode ? 0 : 1, s);
+    const bool none = npairs == 0 && nvf == 0;
+    hipError_t e = none ? launch_restore_topology(ctx->d_state, s)
+                        : launch_insert(ctx->d_state, d_pairs, npairs, d_vf, nvf, ctx->nv,
+                                        ctx->nf, ctx->ins, ctx->d_hdr, ctx->npatch,
+                                        ctx->row_mode ? 0 : 1, s);
     // the row path leaves the untouched rows' columns of the new buffer
     // unwritten until the pattern is read
-    if (ctx->row_mode && npairs > 0) ctx->cols_complete[1] = ctx->cols_complete[2] = false;
+    if (ctx->row_mode && !none) ctx->cols_complete[1] = ctx->cols_complete[2] = false;
     if (e != hipSuccess) return hip_fail(ctx, e, "insert launch");
     return LAD_OK;
+}
+
+lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs, void *hip_stream)
+{
+    return lad_insert_contacts(ctx, d_pairs, npairs, nullptr, 0, hip_stream);
 }
 
 lad_status lad_device_status(lad_ctx *ctx, void *hip_stream, int32_t *status)

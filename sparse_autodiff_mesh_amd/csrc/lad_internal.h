@@ -64,7 +64,8 @@ struct DevState {
                              // between inserts: the commit kernel clears it)
     int32_t np[3];           // pairs of each buffer
     int32_t nnzb[3];         // blocks of each buffer
-    int32_t pad[7];
+    int32_t nvf[3];          // vertex-face contacts of each buffer
+    int32_t pad[4];
 };
 
 // ---------------------------------------------------------------------------
@@ -146,6 +147,8 @@ struct PatternBufs {
     const int32_t *pinc_row[3];
     const int32_t *trow[3];      // per incidence entry: its row if the entry is
                                  // the row's first, else -1 (touched rows)
+    const int32_t *vf[3];        // vertex-face contacts: (vertex, face id)
+    const int32_t *faces;        // [nf][3] mesh faces (contacts on)
 };
 
 template <typename T>
@@ -212,7 +215,19 @@ struct RowArgs {
     // (null: none), and an early exit when *hvp_skip != 0 (null: never)
     double *hvp_dot;
     const int32_t *hvp_skip;
+    // vertex-face contacts: per-contact local terms formed by launch_vf_eval
+    // / launch_vf_hvp, component c of contact e at [c * vf_stride + e]
+    T *vf_eval;                  // kVfEvalComps components
+    T *vf_hvp;                   // kVfHvpComps components
+    int32_t vf_stride;           // vertex-face capacity (0: contacts off)
 };
+
+// Components of a contact's stored local term: energy, gradient (12), then
+// the 12 x 12 Hessian row-major, over (contact vertex, face vertex 0, 1, 2)
+// x coordinate; for the product, the 12-vector H_e u_e.
+constexpr int kVfHessOff = 13;
+constexpr int kVfEvalComps = kVfHessOff + 144;
+constexpr int kVfHvpComps = 12;
 
 template <typename T>
 int rows_lds_bytes(int lds_blocks);
@@ -239,6 +254,13 @@ struct CgDir {
 template <typename T>
 hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
                            hipStream_t s, const CgDir<T> &cg = CgDir<T>{});
+// Vertex-face contact terms of the active buffer, one thread per contact;
+// enqueued before the row kernels that add them (same stream).
+template <typename T>
+hipError_t launch_vf_eval(const RowArgs<T> &a, const T *x, hipStream_t s);
+template <typename T>
+hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, hipStream_t s,
+                         const CgDir<T> &cg = CgDir<T>{});
 template <typename T>
 hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x,
                              T *g, T *hvals, EnergySink es, int nblocks,
@@ -286,6 +308,8 @@ struct InsertBufs {
     int32_t *pinc_row[3];
     int32_t *pnew[3];            // distinct new partners per row (scratch)
     int32_t *trow[3];            // touched-row list, see PatternBufs::trow
+    int32_t *vf[3];              // vertex-face contacts: (vertex, face id)
+    const int32_t *faces;        // [nf][3] mesh faces (contacts on)
     const int32_t *row_chunk;    // [nv] chunk of each row (row path)
     int32_t *cnt;                // [nv], all zero between inserts
     int32_t *nnew;               // [nv] new blocks per row, all zero between inserts
@@ -294,8 +318,8 @@ struct InsertBufs {
 // complete_cols = 0 writes the columns of pair-touched rows only (row
 // path); launch_complete_cols then fills in the other rows of the active
 // buffer on demand.
-hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np,
-                         int32_t nv, InsertBufs b, const PatchHdr *hdr,
+hipError_t launch_insert(DevState *st, const int32_t *d_pairs, int32_t np, const int32_t *d_vf,
+                         int32_t nvf, int32_t nv, int32_t nf, InsertBufs b, const PatchHdr *hdr,
                          int32_t npatch, int complete_cols, hipStream_t s);
 hipError_t launch_complete_cols(DevState *st, InsertBufs b, const PatchHdr *hdr,
                                 int32_t npatch, hipStream_t s);

@@ -196,9 +196,12 @@ struct PairPre {
 
 // Every field is set whatever the row: with no (or fewer) pairs the unused
 // entries name the row's own vertex, so loads indexed by pp.b stay in range.
+// A row's incidence entries are sorted by element id, pairs (ids < npa)
+// before vertex-face contacts, so the prefetched pairs are the leading ones.
 template <typename T>
-__device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, const Row<T> &r,
-                                               const T *__restrict__ x, PairPre<T> &pp)
+__device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, int32_t npa,
+                                               const Row<T> &r, const T *__restrict__ x,
+                                               PairPre<T> &pp)
 {
     pp.n = 0;
 #pragma unroll
@@ -212,17 +215,20 @@ __device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, con
     if (act == 0 || r.p1 == r.p0) return;
     const int32_t *pl = A.pat.pinc[act];
     const int32_t *prs = A.pat.pairs[act];
-    pp.n = min(r.p1 - r.p0, kRowPairs);
     int32_t q[kRowPairs];
 #pragma unroll
-    for (int k = 0; k < kRowPairs; ++k) q[k] = pl[k < pp.n ? r.p0 + k : 0];
+    for (int k = 0; k < kRowPairs; ++k) q[k] = pl[min(r.p0 + k, r.p1 - 1)];
+    int32_t n = 0;
 #pragma unroll
-    for (int k = 0; k < kRowPairs; ++k) {
-        const int32_t i0 = prs[2 * q[k]], i1 = prs[2 * q[k] + 1];
-        pp.first[k] = i0 == r.a ? 1 : 0;
-        pp.b[k] = k < pp.n ? (i0 == r.a ? i1 : i0) : r.a;
-        pp.slot[k] = r.s0;
-    }
+    for (int k = 0; k < kRowPairs; ++k) n += (n == k && k < r.p1 - r.p0 && q[k] < npa) ? 1 : 0;
+    pp.n = n;
+#pragma unroll
+    for (int k = 0; k < kRowPairs; ++k)
+        if (k < n) {
+            const int32_t i0 = prs[2 * q[k]], i1 = prs[2 * q[k] + 1];
+            pp.first[k] = i0 == r.a ? 1 : 0;
+            pp.b[k] = i0 == r.a ? i1 : i0;
+        }
 #pragma unroll
     for (int k = 0; k < kRowPairs; ++k)
 #pragma unroll
@@ -337,8 +343,12 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     double E = 0.0;
     int32_t dslot = r.s0;
 
+    // pairs of the active buffer (element ids below npa are pairs); rows
+    // that no contact touches are evaluated with PAIRS = false, which
+    // compiles the contact code out
+    const int32_t npa = (PAIRS && act != 0) ? A.state->np[act] : 0;
     PairPre<T> pp;
-    prefetch_pairs(A, act, r, x, pp);
+    prefetch_pairs(A, PAIRS ? act : 0, npa, r, x, pp);
     int32_t jb = r.kb0;
     for (int32_t base = r.s0; base < r.s1; base += kBatch) {
         SlotBatch<T> q;
@@ -460,11 +470,44 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
 #pragma unroll
     for (int k = 0; k < kRowPairs; ++k)
         if (k < pp.n) pair_term(pp.xb[k], pp.slot[k], pp.first[k] != 0);
-    if (r.p1 - r.p0 > kRowPairs) {
+    // vertex-face contact e of the active buffer: its energy, gradient and
+    // Hessian over (p, t0, t1, t2) were formed once by k_vf_eval; the row
+    // adds its own 3-row strip (the energy in the contact vertex's row)
+    auto vf_term = [&](int32_t e) {
+        int32_t w[4];
+        w[0] = A.pat.vf[act][2 * int64_t(e)];
+        const int32_t f = A.pat.vf[act][2 * int64_t(e) + 1];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) w[1 + i] = A.pat.faces[3 * int64_t(f) + i];
+        const int li = w[0] == r.a ? 0 : (w[1] == r.a ? 1 : (w[2] == r.a ? 2 : 3));
+        const T *L = A.vf_eval + e;
+        const int64_t S = A.vf_stride;
+        if (li == 0) E += double(L[0]);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) G[c] += L[S * (1 + 3 * li + c)];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            T *Bm = Hs + 9 * ((m == li ? dslot : find_slot(cia, r.s0, r.s1, w[m])) - sb);
+#pragma unroll
+            for (int rr = 0; rr < 3; ++rr)
+#pragma unroll
+                for (int cc = 0; cc < 3; ++cc) {
+                    const T h = L[S * (kVfHessOff + 12 * (3 * li + rr) + 3 * m + cc)];
+                    if (m == li) D[3 * rr + cc] += h;
+                    else Bm[3 * rr + cc] += h;
+                }
+        }
+    };
+    // entries past the prefetched pairs: further pairs, then contacts
+    if (PAIRS && r.p1 - r.p0 > pp.n) {
         const int32_t *pl = A.pat.pinc[act];
         const int32_t *prs = A.pat.pairs[act];
-        for (int32_t k = r.p0 + kRowPairs; k < r.p1; ++k) {
+        for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
             const int32_t q = pl[k];
+            if (q >= npa) {
+                vf_term(q - npa);
+                continue;
+            }
             const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
             const int32_t b = i0 == r.a ? i1 : i0;
             T xb[3];
@@ -601,8 +644,9 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
 #pragma unroll
             for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
         }
+        const int32_t npa = act != 0 ? A.state->np[act] : 0;
         PairPre<T> pp;
-        prefetch_pairs(A, act, r, x, pp);
+        prefetch_pairs(A, act, npa, r, x, pp);
         // Every term is evaluated once in DualHv numbers seeded with the
         // term's variables and the matching components of v; the gradient's
         // directional derivative gt is the term's Hessian applied to v.
@@ -700,11 +744,24 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             for (int k = 0; k < kRowPairs; ++k)
                 if (k < pp.n) pair_hv(pp.xb[k], vp[k]);
         }
-        if (r.p1 - r.p0 > kRowPairs) {
+        // vertex-face contact e: the row's part of H_e u_e, formed by k_vf_hvp
+        auto vf_hv = [&](int32_t e) {
+            const int32_t pv = A.pat.vf[act][2 * int64_t(e)];
+            const int32_t f = A.pat.vf[act][2 * int64_t(e) + 1];
+            const int32_t t0 = A.pat.faces[3 * int64_t(f)], t1 = A.pat.faces[3 * int64_t(f) + 1];
+            const int li = pv == r.a ? 0 : (t0 == r.a ? 1 : (t1 == r.a ? 2 : 3));
+#pragma unroll
+            for (int c = 0; c < 3; ++c) Y[c] += A.vf_hvp[int64_t(A.vf_stride) * (3 * li + c) + e];
+        };
+        if (r.p1 - r.p0 > pp.n) {
             const int32_t *pl = A.pat.pinc[act];
             const int32_t *prs = A.pat.pairs[act];
-            for (int32_t k = r.p0 + kRowPairs; k < r.p1; ++k) {
+            for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
                 const int32_t qp = pl[k];
+                if (qp >= npa) {
+                    vf_hv(qp - npa);
+                    continue;
+                }
                 const int32_t i0 = prs[2 * qp], i1 = prs[2 * qp + 1];
                 const int32_t b = i0 == r.a ? i1 : i0;
                 T xb[3], vb[3];

@@ -1,0 +1,214 @@
+// lad_vf.hip -- vertex-face contact elements, one thread per contact.
+//
+// Page "Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+// Computations", section "Method" (element-level forward mode: each term is
+// evaluated once on seeded inputs, its local gradient and Hessian come out
+// of the same pass) and key design 4 (vertex-face interactions beside the
+// vertex-vertex ones).
+//
+// A point-triangle term couples four vertices, so its row-owner evaluation
+// would repeat the 9-variable second-order pass in each of the four rows
+// (and hold a 55-value dual number per intermediate in every row kernel).
+// Instead the term is evaluated once here, in its own thread, and the row
+// kernels add the strip that belongs to their row:
+//   k_vf_eval  energy, gradient and Hessian in the 12 vertex variables
+//              (contact vertex p, then the face's t0, t1, t2);
+//   k_vf_hvp   the 12-vector H_e u_e for the direction u.
+// Results are stored component-major (component c of contact e at
+// [c * stride + e]), so the lanes of a wave write consecutive addresses.
+// Contacts are read from the active pattern buffer; the grid walks
+// [0, nvf[active]) with a stride loop.
+#include <hip/hip_runtime.h>
+
+#include "contact_vf.h"
+#include "dual2.h"
+#include "lad_internal.h"
+
+namespace lad {
+
+namespace {
+
+constexpr int kVfThreads = 64;
+
+// Vertex ids (p, t0, t1, t2) and positions of contact e.
+template <typename T>
+__device__ __forceinline__ void vf_load(const RowArgs<T> &A, int act, int32_t e,
+                                        const T *__restrict__ x, int32_t w[4], T xp[3],
+                                        T xt[3][3])
+{
+    w[0] = A.pat.vf[act][2 * int64_t(e)];
+    const int32_t f = A.pat.vf[act][2 * int64_t(e) + 1];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) w[1 + i] = A.pat.faces[3 * int64_t(f) + i];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        xp[c] = x[int64_t(w[0]) * 3 + c];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) xt[i][c] = x[int64_t(w[1 + i]) * 3 + c];
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kVfThreads)
+k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
+{
+    const int act = A.state->active;
+    if (act == 0) return;
+    const int32_t n = A.state->nvf[act];
+    const int64_t S = A.vf_stride;
+    for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
+         e += int32_t(gridDim.x) * kVfThreads) {
+        int32_t w[4];
+        T xp[3], xt[3][3];
+        vf_load(A, act, e, x, w, xp, xt);
+        T *L = A.vf_eval + e;
+        const int region = vf_region(xp, xt[0], xt[1], xt[2]);
+        Dual2<T, 9> z[9];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) z[3 * i + c] = Dual2<T, 9>::var(xt[i][c] - xp[c], 3 * i + c);
+        const Dual2<T, 9> d = vf_distance(z, region);
+        if (!(d.v < A.dhat)) {  // outside the barrier's support: an all-zero term
+            for (int c = 0; c < kVfEvalComps; ++c) L[S * c] = T(0);
+            continue;
+        }
+        const Dual2<T, 9> en = barrier_of_distance(d, A.kappa, A.dhat);
+        L[0] = en.v;
+        // gradient: d/dt_i = d/dz_i, d/dp = -sum_i d/dz_i
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            T gp = T(0);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                gp -= en.g[3 * i + c];
+                L[S * (1 + 3 * (1 + i) + c)] = en.g[3 * i + c];
+            }
+            L[S * (1 + c)] = gp;
+        }
+        // Hessian, 12 x 12 row-major over (vertex, coordinate):
+        //   (t_i, t_j) = Hz_ij,  (p, t_j) = (t_j, p)^T = -sum_i Hz_ij,
+        //   (p, p) = sum_ij Hz_ij
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                T pp = T(0);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    T pj = T(0);  // (p r, t_j c)
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) {
+                        const T h = en.hess(3 * i + r, 3 * j + c);
+                        L[S * (kVfHessOff + 12 * (3 * (1 + i) + r) + 3 * (1 + j) + c)] = h;
+                        pj -= h;
+                    }
+                    L[S * (kVfHessOff + 12 * r + 3 * (1 + j) + c)] = pj;
+                    L[S * (kVfHessOff + 12 * (3 * (1 + j) + c) + r)] = pj;
+                    pp -= pj;
+                }
+                L[S * (kVfHessOff + 12 * r + c)] = pp;
+            }
+    }
+}
+
+// Direction component i: u[i], or the Newton-CG direction -r + beta d_old
+// (the same value the row HVP forms for its own rows).
+template <typename T, bool CG>
+__device__ __forceinline__ T vf_dir(const T *__restrict__ u, const CgDir<T> &cg, double beta,
+                                    int64_t i)
+{
+    if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
+    else return u[i];
+}
+
+template <typename T, bool CG>
+__global__ void __launch_bounds__(kVfThreads)
+k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T> cg)
+{
+    if (A.hvp_skip && *A.hvp_skip) return;
+    const int act = A.state->active;
+    if (act == 0) return;
+    const int32_t n = A.state->nvf[act];
+    const int64_t S = A.vf_stride;
+    const double beta = CG ? *cg.beta : 0.0;
+    for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
+         e += int32_t(gridDim.x) * kVfThreads) {
+        int32_t w[4];
+        T xp[3], xt[3][3], up[3], ut[3][3];
+        vf_load(A, act, e, x, w, xp, xt);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            up[c] = vf_dir<T, CG>(u, cg, beta, int64_t(w[0]) * 3 + c);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) ut[i][c] = vf_dir<T, CG>(u, cg, beta, int64_t(w[1 + i]) * 3 + c);
+        }
+        T *L = A.vf_hvp + e;
+        const int region = vf_region(xp, xt[0], xt[1], xt[2]);
+        // z_i = t_i - p seeded with the matching direction u_(t_i) - u_p
+        DualHv<T, 9> z[9];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                z[3 * i + c] = DualHv<T, 9>::var(xt[i][c] - xp[c], 3 * i + c, ut[i][c] - up[c]);
+        const DualHv<T, 9> d = vf_distance(z, region);
+        if (!(d.v < A.dhat)) {
+            for (int c = 0; c < kVfHvpComps; ++c) L[S * c] = T(0);
+            continue;
+        }
+        const DualHv<T, 9> en = barrier_of_distance(d, A.kappa, A.dhat);
+        // gt = Hz (u_t - u_p) in z; mapped as the gradient is
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            T yp = T(0);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                yp -= en.gt[3 * i + c];
+                L[S * (3 * (1 + i) + c)] = en.gt[3 * i + c];
+            }
+            L[S * c] = yp;
+        }
+    }
+}
+
+int vf_grid(int32_t cap)
+{
+    const int64_t g = (int64_t(cap) + kVfThreads - 1) / kVfThreads;
+    return int(g < 1 ? 1 : (g > 4096 ? 4096 : g));
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_vf_eval(const RowArgs<T> &a, const T *x, hipStream_t s)
+{
+    if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_eval || a.vf_stride <= 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_vf_eval<T>, dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0, s, a, x);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, hipStream_t s,
+                         const CgDir<T> &cg)
+{
+    if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_hvp || a.vf_stride <= 0)
+        return hipErrorInvalidValue;
+    if (cg.r)
+        hipLaunchKernelGGL((k_vf_hvp<T, true>), dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0,
+                           s, a, x, u, cg);
+    else
+        hipLaunchKernelGGL((k_vf_hvp<T, false>), dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0,
+                           s, a, x, u, cg);
+    return hipGetLastError();
+}
+
+template hipError_t launch_vf_eval<float>(const RowArgs<float> &, const float *, hipStream_t);
+template hipError_t launch_vf_eval<double>(const RowArgs<double> &, const double *, hipStream_t);
+template hipError_t launch_vf_hvp<float>(const RowArgs<float> &, const float *, const float *,
+                                         hipStream_t, const CgDir<float> &);
+template hipError_t launch_vf_hvp<double>(const RowArgs<double> &, const double *, const double *,
+                                          hipStream_t, const CgDir<double> &);
+
+}  // namespace lad
