@@ -65,6 +65,9 @@ def lib():
         L.oracle_face_local.argtypes = [_f64p, _f64p, _f64p, _f64p,
                                         ctypes.c_double, _f64p, _f64p, _f64p]
         L.oracle_face_local.restype = None
+        L.oracle_arap_local.argtypes = [_f64p, _f64p, _f64p, _f64p,
+                                        ctypes.c_double, _f64p, _f64p, _f64p]
+        L.oracle_arap_local.restype = None
         L.oracle_face_grad_hyperdual.argtypes = [_f64p, _f64p, _f64p, _f64p,
                                                  ctypes.c_double, _f64p]
         L.oracle_face_grad_hyperdual.restype = None
@@ -104,7 +107,9 @@ class Problem:
         self.inertia = x_tilde is not None
         self.x_tilde = _f64(x_tilde).reshape(-1, 3) if x_tilde is not None else None
         self.c = float(c)
-        self.face_energy = bool(face_energy)
+        # face term: False/None/0 none, True/1/"sd" symmetric Dirichlet, 2/"arap"
+        self.face_energy = {None: 0, False: 0, 0: 0, True: 1, 1: 1, "sd": 1, 2: 2,
+                            "arap": 2}[face_energy]
         self.dm_inv = _f64(dm_inv).reshape(-1, 4) if dm_inv is not None else None
         self.area = _f64(area) if area is not None else None
         self.pairs = _i32(pairs if pairs is not None else np.zeros((0, 2))).reshape(-1, 2)
@@ -134,7 +139,7 @@ class Problem:
         s.inertia = 1 if self.inertia else 0
         s.c = self.c
         s.x_tilde = _p(self.x_tilde, _f64p)
-        s.face_energy = 1 if self.face_energy else 0
+        s.face_energy = self.face_energy
         s.dm_inv = _p(self.dm_inv, _f64p)
         s.area = _p(self.area, _f64p)
         s.np = self.pairs.shape[0]
@@ -240,6 +245,12 @@ def inertia_local(xv, xt, c):
 def face_local(x0, x1, x2, dm_inv, area):
     x0, x1, x2, dm = _f64(x0), _f64(x1), _f64(x2), _f64(dm_inv)
     return _local(lib().oracle_face_local, 3, _p(x0, _f64p), _p(x1, _f64p),
+                  _p(x2, _f64p), _p(dm, _f64p), float(area))
+
+
+def arap_local(x0, x1, x2, dm_inv, area):
+    x0, x1, x2, dm = _f64(x0), _f64(x1), _f64(x2), _f64(dm_inv)
+    return _local(lib().oracle_arap_local, 3, _p(x0, _f64p), _p(x1, _f64p),
                   _p(x2, _f64p), _p(dm, _f64p), float(area))
 
 

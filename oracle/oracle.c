@@ -343,6 +343,55 @@ void oracle_face_grad_hyperdual(const double *x0, const double *x1,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Face: as-rigid-as-possible E = A sum_i (sigma_i - 1)^2 over the two      */
+/* singular values of the same F.  With C = F^T F:                          */
+/*   sigma_1^2 + sigma_2^2 = tr C,  sigma_1 sigma_2 = sqrt(det C),          */
+/*   so sigma_1 + sigma_2 = sqrt(tr C + 2 sqrt(det C)) and                  */
+/*   E = A (tr C - 2 (sigma_1 + sigma_2) + 2).                              */
+/* ------------------------------------------------------------------------ */
+
+static hd hd_sqrt(hd x);
+
+static hd arap_energy_hd(const hd *X, const double *Mi, double A)
+{
+    hd F[3][2];
+    for (int r = 0; r < 3; ++r) {
+        hd d0 = hd_sub(X[3 + r], X[r]);
+        hd d1 = hd_sub(X[6 + r], X[r]);
+        F[r][0] = hd_add(hd_scale(d0, Mi[0]), hd_scale(d1, Mi[2]));
+        F[r][1] = hd_add(hd_scale(d0, Mi[1]), hd_scale(d1, Mi[3]));
+    }
+    hd C00 = hd_make(0, 0, 0), C01 = hd_make(0, 0, 0), C11 = hd_make(0, 0, 0);
+    for (int r = 0; r < 3; ++r) {
+        C00 = hd_add(C00, hd_mul(F[r][0], F[r][0]));
+        C01 = hd_add(C01, hd_mul(F[r][0], F[r][1]));
+        C11 = hd_add(C11, hd_mul(F[r][1], F[r][1]));
+    }
+    hd tr = hd_add(C00, C11);
+    hd det = hd_sub(hd_mul(C00, C11), hd_mul(C01, C01));
+    hd ssum = hd_sqrt(hd_add(tr, hd_scale(hd_sqrt(det), 2.0)));
+    return hd_scale(hd_add(hd_sub(tr, hd_scale(ssum, 2.0)), hd_make(2.0, 0.0, 0.0)), A);
+}
+
+void oracle_arap_local(const double *x0, const double *x1, const double *x2,
+                       const double *dm_inv, double area, double *E,
+                       double *g9, double *H81)
+{
+    hd X[9];
+    for (int p = 0; p < 9; ++p)
+        for (int q = p; q < 9; ++q) {
+            face_seed(x0, x1, x2, p, q, X);
+            hd e = arap_energy_hd(X, dm_inv, area);
+            H81[9 * p + q] = e.d;
+            H81[9 * q + p] = e.d;
+            if (p == q) {
+                g9[p] = e.b;
+                *E = e.a;
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Vertex-face contact: barrier of the point-triangle distance              */
 /* ------------------------------------------------------------------------ */
 
@@ -534,9 +583,14 @@ int oracle_eval(const oracle_problem *p, const int32_t *row_ptr,
     if (p->face_energy) {
         for (int32_t f = 0; f < p->nf; ++f) {
             for (int i = 0; i < 3; ++i) vid[i] = p->faces[3 * (int64_t)f + i];
-            oracle_face_local(x + 3 * (int64_t)vid[0], x + 3 * (int64_t)vid[1],
-                              x + 3 * (int64_t)vid[2], p->dm_inv + 4 * (int64_t)f,
-                              p->area[f], &e, gl, Hl);
+            if (p->face_energy == 2)
+                oracle_arap_local(x + 3 * (int64_t)vid[0], x + 3 * (int64_t)vid[1],
+                                  x + 3 * (int64_t)vid[2], p->dm_inv + 4 * (int64_t)f,
+                                  p->area[f], &e, gl, Hl);
+            else
+                oracle_face_local(x + 3 * (int64_t)vid[0], x + 3 * (int64_t)vid[1],
+                                  x + 3 * (int64_t)vid[2], p->dm_inv + 4 * (int64_t)f,
+                                  p->area[f], &e, gl, Hl);
             E += e;
             if (scatter(row_ptr, col_idx, 3, vid, gl, Hl, g, hvals)) return -3;
         }

@@ -45,7 +45,8 @@ typedef struct {
     int32_t inertia;             /* 1 = add 0.5*c*|x_v - x_tilde_v|^2 per vertex */
     double c;
     const double *x_tilde;       /* [nv*3] */
-    int32_t face_energy;         /* 1 = symmetric Dirichlet per face */
+    int32_t face_energy;         /* per face: 0 = none, 1 = symmetric Dirichlet,
+                                    2 = as-rigid-as-possible */
     const double *dm_inv;        /* [nf*4] row-major inverse rest edge matrix */
     const double *area;          /* [nf] rest area */
     int32_t np;                  /* vertex-vertex pairs; pairs[2*p + i] */
@@ -86,6 +87,12 @@ void oracle_barrier_scalar(double d, double kappa, double dhat, double *b,
 void oracle_inertia_local(const double *xv, const double *xt, double c,
                           double *E, double *g3, double *H9);
 void oracle_face_local(const double *x0, const double *x1, const double *x2,
+                       const double *dm_inv, double area, double *E,
+                       double *g9, double *H81);
+/* As-rigid-as-possible face term A sum_i (sigma_i - 1)^2, sigma_i the
+ * singular values of F = [x1 - x0, x2 - x0] Dm^{-1}; value and exact
+ * derivatives from hyper-dual numbers. */
+void oracle_arap_local(const double *x0, const double *x1, const double *x2,
                        const double *dm_inv, double area, double *E,
                        double *g9, double *H81);
 /* Vertex-face contact: the barrier b(d) of the distance d from point p to
