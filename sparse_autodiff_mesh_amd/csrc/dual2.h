@@ -384,4 +384,36 @@ __device__ __forceinline__ DualHv<T, N> operator/(const DualHv<T, N> &a, const D
     return a * reciprocal(b);
 }
 
+// Mixed and unary forms, for generic term code written once for every
+// number type.
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator-(const DualHv<T, N> &a)
+{
+    return T(-1) * a;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator*(const DualHv<T, N> &a, T s)
+{
+    return s * a;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator+(T s, const DualHv<T, N> &a)
+{
+    return a + s;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator-(T s, const DualHv<T, N> &a)
+{
+    return (T(-1) * a) + s;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ DualHv<T, N> operator/(const DualHv<T, N> &a, T s)
+{
+    return (T(1) / s) * a;
+}
+
 }  // namespace lad

@@ -1,0 +1,73 @@
+// lad_terms_internal.h -- host-visible structures and launchers of the term
+// front end (kernels in terms_engine.h, sets in lad_terms.hip, the C ABI in
+// lad_terms_api.cpp).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lad_internal.h"
+
+namespace lad {
+namespace terms {
+
+constexpr int kMaxTerms = 4;   // term types of one set
+constexpr int kMaxVerts = 4;   // vertices per element (offsets pack into 24 bits)
+
+// Set ids (the values of LAD_TERMS_* in include/lad_terms.h).
+constexpr int kSetCloth = 1;
+constexpr int kSetArap = 2;
+constexpr int kSetSymDirichlet = 3;
+constexpr int kSetArapCloth = 4;
+
+// One element seen from the row of one of its vertices: e is the element
+// id; pk holds the row vertex's position i in the element (bits 0-1) and,
+// for b = 1 .. K-1, the block offset within the row of the element's
+// vertex (i + b) % K (bits 8b .. 8b+7).
+struct alignas(8) TermInc {
+    int32_t e;
+    uint32_t pk;
+};
+
+template <typename T>
+struct TermData {
+    const int32_t *inc_ptr;      // [nv+1] incidence offsets
+    const TermInc *inc;          // incident elements of each row, by element id
+    const int32_t *elems;        // [ne][K] vertex ids
+    const T *consts;             // [ne][kConsts]
+};
+
+template <typename T>
+struct TermsArgs {
+    const PatchHdr *chunk;       // v0, nown of each chunk of up to 64 rows
+    int32_t nchunk;
+    int32_t nv;
+    const int32_t *rp, *ci;      // pattern
+    const int32_t *diag;         // [nv] offset of the diagonal block in its row
+    int32_t lds_blocks;          // staging capacity per workgroup, in blocks
+    TermData<T> t[kMaxTerms];    // the launch's terms, in list order
+};
+
+struct TermInfo {
+    int arity;                   // vertices per element
+    int nconst;                  // constants per element
+    const char *name;
+};
+
+// Terms of a set (their number; 0 for an unknown set).
+int set_terms(int set, TermInfo out[kMaxTerms]);
+
+template <typename T>
+hipError_t terms_grid(int set, int lds, int nchunk, int nv, int *grid_eval, int *grid_hvp);
+// Fused: one launch, partial energies at es.part0 + [0, grid).  Unfused:
+// one launch per term t, partial energies at es.part0 + t * grid + [0, grid).
+template <typename T>
+hipError_t launch_terms_eval(int set, int fused, const TermsArgs<T> &a, const T *x, T *g, T *hv,
+                             EnergySink es, int grid, int lds, hipStream_t s);
+template <typename T>
+hipError_t launch_terms_hvp(int set, int fused, const TermsArgs<T> &a, const T *x, const T *v,
+                            T *y, int grid, hipStream_t s);
+
+}  // namespace terms
+}  // namespace lad

@@ -1,0 +1,258 @@
+// terms_engine.h -- the term front end's kernels: explicit gradient and
+// block-CSR Hessian, and the matrix-free Hessian-vector product, for any
+// compile-time list of user terms (user_terms.h), all of them fused into one
+// pass over the rows.
+//
+// Page "Locality-Aware Automatic Differentiation on the GPU for Mesh-Based
+// Computations", section "Method": from a user's local energy terms the
+// system analyses the stencil and derivative needs, preallocates the CSR
+// pattern from the topology, evaluates every term in forward mode with its
+// intermediates in registers, and assembles g = sum_j S_j^T g_j and
+// H = sum_j S_j^T H_j S_j.  Its stated limitation is one kernel per term
+// with no fusion across terms; here one launch evaluates every term of the
+// list (the unfused mode runs one launch per term and accumulates, for
+// comparison).
+//
+// Decomposition: row owner, as the fixed-function row kernels.  One lane
+// owns one block row; for each element incident to its vertex a (at
+// position i in the element) it evaluates the term on numbers that carry
+// only the Hessian rows of a's three variables (StripDual), seeding a's
+// coordinates as variables 0..2 and the element's vertex (i + b) % K as
+// variables 3b..3b+2.  The strip's block b is then exactly the row's block
+// for that vertex, at a column offset the incidence record holds, so a row
+// is written by one lane, in a fixed order, without atomics.  The energy of
+// an element is counted by the row of its vertex 0.  The product seeds
+// every variable with the direction's component and tracks derivatives in
+// a's three variables only (DualHv<T, 3>): every rule of those numbers acts
+// on one gradient component at a time, so this gives exactly a's part of
+// H_j v_j.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "dual2.h"
+#include "lad_device.h"
+#include "lad_internal.h"
+#include "lad_terms_internal.h"
+#include "strip_dual.h"
+
+namespace lad {
+namespace terms {
+
+constexpr int kTermBatch = 2;    // incident elements whose loads a lane issues together
+
+// LDS hand-off between the lanes of one wave: a wave's LDS operations run in
+// issue order, so only the compiler must be kept from moving memory
+// operations across this point (no workgroup barrier, which would also wait
+// for the chunk's outstanding HBM stores).
+__device__ __forceinline__ void terms_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The row's contributions from one term type: for each batch of incident
+// elements, every load first (records, vertex ids, positions, constants),
+// then the evaluations.  D is the row's diagonal block, G its gradient,
+// Hrow its slice of the staged blocks.
+template <typename Term, typename T>
+__device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
+                                             const T *__restrict__ x, T *Hrow, T D[9],
+                                             T G[3], double &E)
+{
+    constexpr int K = Term::kVerts, N = 3 * K, NC = Term::kConsts;
+    static_assert(K >= 1 && K <= kMaxVerts, "stencil of 1 to 4 vertices");
+    const int32_t p0 = td.inc_ptr[a], p1 = td.inc_ptr[a + 1];
+    for (int32_t base = p0; base < p1; base += kTermBatch) {
+        TermInc rec[kTermBatch];
+        int32_t vid[kTermBatch][K];
+        T xv[kTermBatch][K][3];
+        T cc[kTermBatch][NC > 0 ? NC : 1];
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j) rec[j] = td.inc[min(base + j, p1 - 1)];
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j) {
+#pragma unroll
+            for (int v = 0; v < K; ++v) vid[j][v] = td.elems[int64_t(rec[j].e) * K + v];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) cc[j][q] = td.consts[int64_t(rec[j].e) * NC + q];
+        }
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j)
+#pragma unroll
+            for (int v = 0; v < K; ++v)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) xv[j][v][c] = x[int64_t(vid[j][v]) * 3 + c];
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j) {
+            if (base + j >= p1) break;
+            const int i = int(rec[j].pk & 3u);
+            StripDual<T, N> z[K][3];
+#pragma unroll
+            for (int v = 0; v < K; ++v) {
+                const int b = (v - i + K) % K;  // the vertex's block in the strip
+#pragma unroll
+                for (int c = 0; c < 3; ++c) z[v][c] = StripDual<T, N>::var(xv[j][v][c], 3 * b + c);
+            }
+            const StripDual<T, N> en = Term::energy(z, cc[j]);
+            if (i == 0) E += double(en.v);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                G[r] += en.g[r];
+#pragma unroll
+                for (int c = 0; c < 3; ++c) D[3 * r + c] += en.h[r][c];
+            }
+#pragma unroll
+            for (int b = 1; b < K; ++b) {
+                T *B = Hrow + 9 * int32_t((rec[j].pk >> (8 * b)) & 255u);
+#pragma unroll
+                for (int r = 0; r < 3; ++r)
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) B[3 * r + c] += en.h[r][3 * b + c];
+            }
+        }
+    }
+}
+
+template <typename T, typename... Terms, size_t... I>
+__device__ __forceinline__ void row_eval_all(const TermsArgs<T> &A, int32_t a,
+                                             const T *__restrict__ x, T *Hrow, T D[9], T G[3],
+                                             double &E, std::index_sequence<I...>)
+{
+    (row_term_eval<Terms>(A.t[I], a, x, Hrow, D, G, E), ...);
+}
+
+// Energy, gradient and Hessian rows of the term list.  With ACC set the
+// launch adds into g and H as they are (the unfused mode's later terms);
+// otherwise it overwrites them.  Chunks of 64 rows are staged in LDS (a
+// single-wave workgroup, so the hand-off needs no barrier) and streamed out
+// with 16-byte non-temporal stores.
+template <typename T, bool ACC, typename... Terms>
+__global__ void __launch_bounds__(kRowThreads)
+k_terms_eval(TermsArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
+             EnergySink esink)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    T *stage = reinterpret_cast<T *>(smem);
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int c0 = int(int64_t(A.nchunk) * w / gridDim.x);
+    const int c1 = int(int64_t(A.nchunk) * (w + 1) / gridDim.x);
+    double eacc = 0.0;
+    for (int ch = c0; ch < c1; ++ch) {
+        const int32_t v0 = A.chunk[ch].v0, nrows = A.chunk[ch].nown;
+        const int32_t sb = A.rp[v0];
+        const int32_t nblk = A.rp[v0 + nrows] - sb;
+        const bool fits = nblk <= A.lds_blocks;  // checked at build; never false
+        const int pad = stage_pad<T>(int64_t(sb) * 9);
+        T *Hs = stage + pad;
+        if (fits) {
+            if constexpr (ACC)
+                for (int k = int(threadIdx.x); k < nblk * 9; k += kRowThreads)
+                    Hs[k] = hv[int64_t(sb) * 9 + k];
+            else
+                for (int k = int(threadIdx.x); k < nblk * 9; k += kRowThreads) Hs[k] = T(0);
+        }
+        terms_lds_sync();
+        if (fits && int(threadIdx.x) < nrows) {
+            const int32_t a = v0 + int32_t(threadIdx.x);
+            T *Hrow = Hs + 9 * (A.rp[a] - sb);
+            T D[9], G[3];
+#pragma unroll
+            for (int k = 0; k < 9; ++k) D[k] = T(0);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) G[k] = ACC ? g[int64_t(a) * 3 + k] : T(0);
+            row_eval_all<T, Terms...>(A, a, x, Hrow, D, G, eacc,
+                                      std::index_sequence_for<Terms...>{});
+            T *B = Hrow + 9 * A.diag[a];
+#pragma unroll
+            for (int k = 0; k < 9; ++k) B[k] += D[k];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) g[int64_t(a) * 3 + k] = G[k];
+        }
+        terms_lds_sync();
+        if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
+        terms_lds_sync();
+    }
+    store_energy(esink, block_sum<kRowThreads>(eacc, nullptr));
+}
+
+// The row's part of sum_j H_j v_j over one term type.
+template <typename Term, typename T>
+__device__ __forceinline__ void row_term_hvp(const TermData<T> &td, int32_t a,
+                                             const T *__restrict__ x, const T *__restrict__ v,
+                                             T Y[3])
+{
+    constexpr int K = Term::kVerts, NC = Term::kConsts;
+    const int32_t p0 = td.inc_ptr[a], p1 = td.inc_ptr[a + 1];
+    for (int32_t base = p0; base < p1; base += kTermBatch) {
+        TermInc rec[kTermBatch];
+        int32_t vid[kTermBatch][K];
+        T xv[kTermBatch][K][3], vv[kTermBatch][K][3];
+        T cc[kTermBatch][NC > 0 ? NC : 1];
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j) rec[j] = td.inc[min(base + j, p1 - 1)];
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j) {
+#pragma unroll
+            for (int u = 0; u < K; ++u) vid[j][u] = td.elems[int64_t(rec[j].e) * K + u];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) cc[j][q] = td.consts[int64_t(rec[j].e) * NC + q];
+        }
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j)
+#pragma unroll
+            for (int u = 0; u < K; ++u)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    xv[j][u][c] = x[int64_t(vid[j][u]) * 3 + c];
+                    vv[j][u][c] = v[int64_t(vid[j][u]) * 3 + c];
+                }
+#pragma unroll
+        for (int j = 0; j < kTermBatch; ++j) {
+            if (base + j >= p1) break;
+            const int i = int(rec[j].pk & 3u);
+            DualHv<T, 3> z[K][3];
+#pragma unroll
+            for (int u = 0; u < K; ++u)
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    z[u][c] = DualHv<T, 3>::var(xv[j][u][c], u == i ? c : -1, vv[j][u][c]);
+            const DualHv<T, 3> en = Term::energy(z, cc[j]);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) Y[c] += en.gt[c];
+        }
+    }
+}
+
+template <typename T, typename... Terms, size_t... I>
+__device__ __forceinline__ void row_hvp_all(const TermsArgs<T> &A, int32_t a,
+                                            const T *__restrict__ x, const T *__restrict__ v,
+                                            T Y[3], std::index_sequence<I...>)
+{
+    (row_term_hvp<Terms>(A.t[I], a, x, v, Y), ...);
+}
+
+// y = H v over the term list; with ACC set the launch adds into y.  Each
+// workgroup walks a contiguous range of rows (ranges grouped by XCD).
+template <typename T, bool ACC, typename... Terms>
+__global__ void __launch_bounds__(kRowThreads)
+k_terms_hvp(TermsArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
+{
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
+    const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
+    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kRowThreads) {
+        T Y[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) Y[k] = ACC ? y[int64_t(a) * 3 + k] : T(0);
+        row_hvp_all<T, Terms...>(A, a, x, v, Y, std::index_sequence_for<Terms...>{});
+#pragma unroll
+        for (int k = 0; k < 3; ++k) y[int64_t(a) * 3 + k] = Y[k];
+    }
+}
+
+}  // namespace terms
+}  // namespace lad

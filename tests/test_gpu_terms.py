@@ -1,0 +1,146 @@
+"""GPU parity of the term front end (lad_terms_* through the C ABI): each
+compiled term set against the oracle on identical inputs -- pattern bit for
+bit, E, g, H and H v within gpu_util.TOL -- in the fused and the unfused
+mode; the generic cloth set against the fixed-function cloth kernels; and
+the 512 x 512 ARAP face grid and 1000 x 1000 cloth at full size (fp32)."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_autodiff_mesh_amd import inputs, terms
+
+from gpu_util import TOL, dev, host_input, log_case, rel
+
+pytestmark = pytest.mark.gpu
+
+# oracle problem of each set: (springs, inertia, face term)
+ORACLE_TERMS = {"cloth": (True, True, False), "arap": (False, False, "arap"),
+                "symdir": (False, False, True), "arap_cloth": (True, True, "arap")}
+
+
+def oracle_problem(m, set_id, dtype):
+    sp, ine, face = ORACLE_TERMS[set_id]
+    return oracle.problem_from_mesh(m, springs=sp, inertia=ine, faces=face, f32=(dtype == "f32"))
+
+
+def run_set(m, set_id, dtype, fused=True, x=None):
+    import torch
+    T = terms.Terms(m.nv, set_id, terms.mesh_blocks(m, set_id), dtype=dtype, fused=fused)
+    x_h = host_input(m.x if x is None else x, dtype)
+    v_h = host_input(inputs.hvp_direction(m.nv), dtype)
+    E, g, H = T.eval(dev(x_h, dtype))
+    y = T.hvp(dev(x_h, dtype), dev(v_h, dtype))
+    rp, ci = T.pattern()
+    torch.cuda.synchronize()
+    out = dict(E=E.item(), g=g.cpu().numpy(), H=H.cpu().numpy(), y=y.cpu().numpy(),
+               rp=rp.cpu().numpy(), ci=ci.cpu().numpy())
+    T.close()
+    return out, x_h, v_h
+
+
+def check(m, set_id, dtype, out, x_h, v_h):
+    prob = oracle_problem(m, set_id, dtype)
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(out["rp"], orp) and np.array_equal(out["ci"], oci)
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    tol = TOL[dtype]
+    assert rel([out["E"]], [Eo]) <= tol, (out["E"], Eo)
+    assert rel(out["g"], go) <= tol, rel(out["g"], go)
+    assert rel(out["H"][: oci.size], Ho) <= tol, rel(out["H"][: oci.size], Ho)
+    yo = oracle.bsr_spmv(orp, oci, Ho, v_h)
+    assert rel(out["y"], yo) <= tol, rel(out["y"], yo)
+
+
+@pytest.mark.parametrize("set_id", ["cloth", "arap", "symdir", "arap_cloth"])
+@pytest.mark.parametrize("n,dtype,fused", [(3, "f64", True), (10, "f64", True),
+                                           (10, "f64", False), (37, "f32", True),
+                                           (37, "f32", False), (100, "f64", True)])
+def test_sets_match_oracle(lad, set_id, n, dtype, fused):
+    log_case(test="terms", set=set_id, n=n, dtype=dtype, fused=fused)
+    m = inputs.cloth(n)
+    out, x_h, v_h = run_set(m, set_id, dtype, fused)
+    check(m, set_id, dtype, out, x_h, v_h)
+
+
+@pytest.mark.parametrize("set_id", ["cloth", "arap_cloth"])
+def test_fused_and_unfused_agree(lad, set_id):
+    log_case(test="terms_fusion", set=set_id)
+    m = inputs.cloth(50)
+    a, _, _ = run_set(m, set_id, "f64", True)
+    b, _, _ = run_set(m, set_id, "f64", False)
+    assert abs(a["E"] - b["E"]) <= 1e-13 * abs(a["E"])
+    for k in ("g", "H", "y"):
+        assert rel(b[k], a[k]) <= 1e-14, (k, rel(b[k], a[k]))
+
+
+def test_generic_cloth_equals_fixed_function_kernels(lad):
+    # the same energy through the term front end and through lad_build_pattern
+    import torch
+    log_case(test="terms_vs_fixed")
+    m = inputs.cloth(60)
+    out, x_h, v_h = run_set(m, "cloth", "f64")
+    L = lad.Lad(m.nv, dtype="f64", path="rows", **lad.mesh_terms(m))
+    E, g, H = L.eval(dev(x_h, "f64"))
+    y = L.hvp(dev(x_h, "f64"), dev(v_h, "f64"))
+    torch.cuda.synchronize()
+    nnzb = out["ci"].size
+    assert abs(E.item() - out["E"]) <= 1e-13 * abs(E.item())
+    assert rel(out["g"], g.cpu().numpy()) <= 1e-13
+    assert rel(out["H"][:nnzb], H.cpu().numpy()[:nnzb]) <= 1e-13
+    assert rel(out["y"], y.cpu().numpy()) <= 1e-13
+    L.close()
+
+
+def test_bitwise_reproducible(lad):
+    log_case(test="terms_bitwise")
+    m = inputs.cloth(40)
+    a, _, _ = run_set(m, "arap_cloth", "f32")
+    b, _, _ = run_set(m, "arap_cloth", "f32")
+    for k in ("g", "H", "y"):
+        assert np.array_equal(a[k], b[k])
+    assert a["E"] == b["E"]
+
+
+def test_isolated_vertices_and_empty_blocks(lad):
+    # vertices that no element touches keep a zero row; a term with no
+    # elements contributes nothing
+    log_case(test="terms_isolated")
+    m = inputs.cloth(8)
+    faces = m.faces[: len(m.faces) // 3]
+    used = np.unique(faces)
+    blocks = [(faces, np.concatenate([m.dm_inv, m.area.reshape(-1, 1)], axis=1)[: len(faces)]),
+              (np.zeros((0, 2), np.int32), np.zeros((0, 2))),
+              (np.zeros((0, 1), np.int32), np.zeros((0, 4)))]
+    import torch
+    T = terms.Terms(m.nv, "arap_cloth", blocks, dtype="f64")
+    x_h = m.x
+    E, g, H = T.eval(dev(x_h, "f64"))
+    rp, ci = T.pattern()
+    torch.cuda.synchronize()
+    prob = oracle.Problem(nv=m.nv, faces=faces, face_energy="arap", dm_inv=m.dm_inv[: len(faces)],
+                          area=m.area[: len(faces)])
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    assert rel([E.item()], [Eo]) <= 1e-12
+    assert rel(g.cpu().numpy(), go) <= 1e-12
+    assert rel(H.cpu().numpy()[: oci.size], Ho) <= 1e-12
+    lonely = np.setdiff1d(np.arange(m.nv), used)
+    assert lonely.size > 0 and not g.cpu().numpy()[lonely].any()
+    T.close()
+
+
+def test_faces_512_arap_f32(lad):
+    log_case(test="terms_arap512")
+    m = inputs.face_grid(512)
+    out, x_h, v_h = run_set(m, "arap", "f32")
+    assert out["ci"].size == 1830914
+    check(m, "arap", "f32", out, x_h, v_h)
+
+
+def test_cloth_1000_generic_f32(lad):
+    log_case(test="terms_cloth1000")
+    m = inputs.cloth(1000)
+    out, x_h, v_h = run_set(m, "cloth", "f32")
+    assert out["ci"].size == 6992002
+    check(m, "cloth", "f32", out, x_h, v_h)
