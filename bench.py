@@ -19,7 +19,9 @@ Prints ONE JSON line.  Besides the contract fields it carries
   cpu_baseline  the fp64 CPU oracle, single-threaded, on the same workload;
   secondary     the other workloads (face-energy grid eval and matrix-free
                 HVP, cloth plus contact-pair insertion, cloth plus
-                vertex-face contact insertion, 100 x 100 cloth).
+                vertex-face contact insertion, 100 x 100 cloth, and the
+                term front end: ARAP faces, the generic cloth set, ARAP +
+                cloth fused and unfused).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--n 1000]
                     [--no-cpu-baseline] [--no-secondary] [--flush-mall]
@@ -61,6 +63,16 @@ def compulsory_bytes_eval(nv, ns, nf, nnzb, es, inertia=True, faces=False, npair
     b += npairs * 8                       # pair endpoints
     b += 3 * nv * es                      # g
     b += 9 * nnzb * es                    # H values
+    return b
+
+
+def compulsory_bytes_terms(nv, blocks, nnzb, es, hvp=False):
+    """Term front end: every element's vertex ids and constants once, x (and
+    v), g (or y), and for the explicit call the H blocks once."""
+    b = sum(el.shape[0] * (4 * el.shape[1] + es * cs.shape[1]) for el, cs in blocks)
+    b += nv * 3 * es * (3 if hvp else 2)
+    if not hvp:
+        b += nnzb * 9 * es
     return b
 
 
@@ -343,6 +355,51 @@ def bench_secondary(torch, binding, inputs, args, timer):
         raise RuntimeError("contact insertion reported a device-side error")
     L.close()
     sec["vf_contacts_per_step"] = P
+    sec.update(bench_terms(torch, inputs, args, timer, steps, warm))
+    return sec
+
+
+def bench_terms(torch, inputs, args, timer, steps, warm):
+    """The term front end: ARAP faces on the 512 x 512 grid, the generic
+    cloth set at 1000 x 1000 (the same energy as the headline kernel), and
+    ARAP + cloth fused into one launch against one launch per term."""
+    from sparse_autodiff_mesh_amd import terms
+    sec = {}
+    f = inputs.face_grid(512)
+    blocks = terms.mesh_blocks(f, "arap")
+    T = terms.Terms(f.nv, "arap", blocks, dtype="f32")
+    x = to_dev(torch, f.x, "f32")
+    v = to_dev(torch, inputs.hvp_direction(f.nv), "f32")
+    out = T.alloc_outputs()
+    r = timer.run(lambda: T.eval(x, out=out, energy=False), steps, warm)
+    b = compulsory_bytes_terms(f.nv, blocks, T.nnzb, 4)
+    sec["terms_arap512_eval_ms"] = round(r["median_ms"], 5)
+    sec["terms_arap512_eval_GBps"] = round(b / (r["median_ms"] * 1e-3) / 1e9, 1)
+    y = torch.empty_like(v)
+    r = timer.run(lambda: T.hvp(x, v, out=y), steps, warm)
+    sec["terms_arap512_hvp_ms"] = round(r["median_ms"], 5)
+    sec["terms_arap512_hvp_GBps"] = round(
+        compulsory_bytes_terms(f.nv, blocks, T.nnzb, 4, hvp=True) / (r["median_ms"] * 1e-3) / 1e9, 1)
+    T.close()
+    m = inputs.cloth(args.n)
+    x = to_dev(torch, m.x, "f32")
+    v = to_dev(torch, inputs.hvp_direction(m.nv), "f32")
+    y = torch.empty_like(v)
+    for set_id in ("cloth", "arap_cloth"):
+        blocks = terms.mesh_blocks(m, set_id)
+        for fused in (True, False):
+            if set_id == "cloth" and not fused:
+                continue
+            T = terms.Terms(m.nv, set_id, blocks, dtype="f32", fused=fused)
+            out = T.alloc_outputs()
+            r = timer.run(lambda: T.eval(x, out=out, energy=False), steps, warm)
+            tag = f"terms_{set_id}1000_{'fused' if fused else 'unfused'}"
+            sec[tag + "_eval_ms"] = round(r["median_ms"], 5)
+            sec[tag + "_eval_GBps"] = round(
+                compulsory_bytes_terms(m.nv, blocks, T.nnzb, 4) / (r["median_ms"] * 1e-3) / 1e9, 1)
+            r = timer.run(lambda: T.hvp(x, v, out=y), steps, warm)
+            sec[tag + "_hvp_ms"] = round(r["median_ms"], 5)
+            T.close()
     return sec
 
 

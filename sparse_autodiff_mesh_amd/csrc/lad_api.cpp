@@ -62,8 +62,10 @@ struct lad_ctx {
     int32_t ns = 0;
     int32_t *d_springs = nullptr;
     int32_t *d_faces = nullptr;      // kept on the device for vertex-face contacts
-    void *d_vf_eval = nullptr;       // per-contact local terms (kVfEvalComps x vf_cap)
-    void *d_vf_hvp = nullptr;        // per-contact H_e u_e (kVfHvpComps x vf_cap)
+    void *d_vf_eval = nullptr;       // per contact vertex: local term strips [4 vf_cap][kVfStrip]
+    void *d_vf_hvp = nullptr;        // per contact vertex: H_e u_e [4 vf_cap][kVfHvpStrip]
+    int32_t *d_vf_ids = nullptr;     // [vf_cap][4]
+    int32_t *d_vf_slots = nullptr;   // [4 vf_cap][4]
     void *d_spring_rest = nullptr;
     int32_t *d_jrp = nullptr, *d_jci = nullptr;
     // Newton-CG work space, allocated by the first lad_newton_cg call
@@ -282,6 +284,8 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.pat = ctx->pat;
     a.vf_eval = static_cast<T *>(ctx->d_vf_eval);
     a.vf_hvp = static_cast<T *>(ctx->d_vf_hvp);
+    a.vf_ids = ctx->d_vf_ids;
+    a.vf_slots = ctx->d_vf_slots;
     a.vf_stride = ctx->vf_cap;
     return a;
 }
@@ -675,9 +679,11 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         ctx->pat.faces = ctx->d_faces;
         if (e == hipSuccess && d->vf_capacity > 0) {
             char *ve = nullptr, *vh = nullptr;
-            const size_t cap = size_t(d->vf_capacity) * size_t(ctx->es);
-            e = dev_alloc(ctx, &ve, size_t(kVfEvalComps) * cap);
-            if (e == hipSuccess) e = dev_alloc(ctx, &vh, size_t(kVfHvpComps) * cap);
+            const size_t strips = 4 * size_t(d->vf_capacity);
+            e = dev_alloc(ctx, &ve, strips * size_t(kVfStrip) * size_t(ctx->es));
+            if (e == hipSuccess) e = dev_alloc(ctx, &vh, strips * size_t(kVfHvpStrip) * size_t(ctx->es));
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_vf_ids, strips);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->d_vf_slots, 4 * strips);
             ctx->d_vf_eval = ve;
             ctx->d_vf_hvp = vh;
         }

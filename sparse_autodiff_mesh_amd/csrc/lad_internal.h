@@ -216,18 +216,22 @@ struct RowArgs {
     double *hvp_dot;
     const int32_t *hvp_skip;
     // vertex-face contacts: per-contact local terms formed by launch_vf_eval
-    // / launch_vf_hvp, component c of contact e at [c * vf_stride + e]
-    T *vf_eval;                  // kVfEvalComps components
-    T *vf_hvp;                   // kVfHvpComps components
+    // / launch_vf_hvp (contact e's vertex m = 0..3 is the contact vertex, then
+    // the face's three; strip 4e + m holds what row "vertex m" needs)
+    T *vf_eval;                  // [4 cap][kVfStrip]
+    T *vf_hvp;                   // [4 cap][kVfHvpStrip]
+    int32_t *vf_ids;             // [cap][4] the contact's vertex ids
+    int32_t *vf_slots;           // [4 cap][4] block offset, in row m, of vertex 0..3
     int32_t vf_stride;           // vertex-face capacity (0: contacts off)
 };
 
-// Components of a contact's stored local term: energy, gradient (12), then
-// the 12 x 12 Hessian row-major, over (contact vertex, face vertex 0, 1, 2)
-// x coordinate; for the product, the 12-vector H_e u_e.
-constexpr int kVfHessOff = 13;
-constexpr int kVfEvalComps = kVfHessOff + 144;
-constexpr int kVfHvpComps = 12;
+// One contact seen from the row of its vertex m: the energy (kept in m = 0's
+// strip only, else 0), the gradient's 3 entries of vertex m, then the
+// Hessian's 3 rows of vertex m over the 12 columns (vertex, coordinate),
+// row-major; for the product, H_e u_e's 3 entries of vertex m (and one pad).
+constexpr int kVfHessOff = 4;
+constexpr int kVfStrip = kVfHessOff + 36;
+constexpr int kVfHvpStrip = 4;
 
 template <typename T>
 int rows_lds_bytes(int lds_blocks);

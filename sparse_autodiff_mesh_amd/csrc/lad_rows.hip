@@ -470,31 +470,35 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
 #pragma unroll
     for (int k = 0; k < kRowPairs; ++k)
         if (k < pp.n) pair_term(pp.xb[k], pp.slot[k], pp.first[k] != 0);
-    // vertex-face contact e of the active buffer: its energy, gradient and
-    // Hessian over (p, t0, t1, t2) were formed once by k_vf_eval; the row
-    // adds its own 3-row strip (the energy in the contact vertex's row)
+    // vertex-face contact e of the active buffer: k_vf_eval stored, for each
+    // of its four vertices, that row's strip (energy in the contact vertex's
+    // strip only, the gradient part, 3 Hessian rows over the contact's 12
+    // variables) and the four blocks' offsets in that row
     auto vf_term = [&](int32_t e) {
-        int32_t w[4];
-        w[0] = A.pat.vf[act][2 * int64_t(e)];
-        const int32_t f = A.pat.vf[act][2 * int64_t(e) + 1];
+        const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
+        const int li = w.x == r.a ? 0 : (w.y == r.a ? 1 : (w.z == r.a ? 2 : 3));
+        const int64_t strip = 4 * int64_t(e) + li;
+        const int4 so = *reinterpret_cast<const int4 *>(A.vf_slots + strip * 4);
+        const T *L = A.vf_eval + strip * kVfStrip;
+        T v[kVfStrip];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) w[1 + i] = A.pat.faces[3 * int64_t(f) + i];
-        const int li = w[0] == r.a ? 0 : (w[1] == r.a ? 1 : (w[2] == r.a ? 2 : 3));
-        const T *L = A.vf_eval + e;
-        const int64_t S = A.vf_stride;
-        if (li == 0) E += double(L[0]);
+        for (int k = 0; k < kVfStrip; ++k) v[k] = L[k];
+        E += double(v[0]);
 #pragma unroll
-        for (int c = 0; c < 3; ++c) G[c] += L[S * (1 + 3 * li + c)];
+        for (int c = 0; c < 3; ++c) G[c] += v[1 + c];
+        const int32_t off[4] = {so.x, so.y, so.z, so.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            T *Bm = Hs + 9 * ((m == li ? dslot : find_slot(cia, r.s0, r.s1, w[m])) - sb);
+            T *Bm = Hs + 9 * (r.s0 + off[m] - sb);
 #pragma unroll
             for (int rr = 0; rr < 3; ++rr)
 #pragma unroll
                 for (int cc = 0; cc < 3; ++cc) {
-                    const T h = L[S * (kVfHessOff + 12 * (3 * li + rr) + 3 * m + cc)];
-                    if (m == li) D[3 * rr + cc] += h;
-                    else Bm[3 * rr + cc] += h;
+                    // D is updated unconditionally (a select between D and
+                    // Bm would take D's address and move it to scratch)
+                    const T h = v[kVfHessOff + 12 * rr + 3 * m + cc];
+                    D[3 * rr + cc] += m == li ? h : T(0);
+                    if (m != li) Bm[3 * rr + cc] += h;
                 }
         }
     };
@@ -746,12 +750,11 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         }
         // vertex-face contact e: the row's part of H_e u_e, formed by k_vf_hvp
         auto vf_hv = [&](int32_t e) {
-            const int32_t pv = A.pat.vf[act][2 * int64_t(e)];
-            const int32_t f = A.pat.vf[act][2 * int64_t(e) + 1];
-            const int32_t t0 = A.pat.faces[3 * int64_t(f)], t1 = A.pat.faces[3 * int64_t(f) + 1];
-            const int li = pv == r.a ? 0 : (t0 == r.a ? 1 : (t1 == r.a ? 2 : 3));
+            const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
+            const int li = w.x == r.a ? 0 : (w.y == r.a ? 1 : (w.z == r.a ? 2 : 3));
+            const T *L = A.vf_hvp + (4 * int64_t(e) + li) * kVfHvpStrip;
 #pragma unroll
-            for (int c = 0; c < 3; ++c) Y[c] += A.vf_hvp[int64_t(A.vf_stride) * (3 * li + c) + e];
+            for (int c = 0; c < 3; ++c) Y[c] += L[c];
         };
         if (r.p1 - r.p0 > pp.n) {
             const int32_t *pl = A.pat.pinc[act];

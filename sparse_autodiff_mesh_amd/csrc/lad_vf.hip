@@ -14,9 +14,12 @@
 //   k_vf_eval  energy, gradient and Hessian in the 12 vertex variables
 //              (contact vertex p, then the face's t0, t1, t2);
 //   k_vf_hvp   the 12-vector H_e u_e for the direction u.
-// Results are stored component-major (component c of contact e at
-// [c * stride + e]), so the lanes of a wave write consecutive addresses.
-// Contacts are read from the active pattern buffer; the grid walks
+// Results are stored per contact vertex m as the strip its row reads
+// (contiguous, so a row takes it in a few 16-byte loads), together with the
+// contact's vertex ids and, for the explicit Hessian, the block offsets of
+// the contact's four vertices in each of the four rows: a touched row then
+// needs no search.  Contacts are read from the active pattern buffer (the
+// rows they touch have complete columns there); the grid walks
 // [0, nvf[active]) with a stride loop.
 #include <hip/hip_runtime.h>
 
@@ -29,6 +32,8 @@ namespace lad {
 namespace {
 
 constexpr int kVfThreads = 64;
+
+constexpr int kScan = 8;  // columns of a row matched per step
 
 // Vertex ids (p, t0, t1, t2) and positions of contact e.
 template <typename T>
@@ -55,13 +60,48 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
     const int act = A.state->active;
     if (act == 0) return;
     const int32_t n = A.state->nvf[act];
-    const int64_t S = A.vf_stride;
+    const int32_t *rp = A.pat.rp[act], *ci = A.pat.ci[act];
     for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
          e += int32_t(gridDim.x) * kVfThreads) {
         int32_t w[4];
         T xp[3], xt[3][3];
         vf_load(A, act, e, x, w, xp, xt);
-        T *L = A.vf_eval + e;
+        // the four rows' block offsets of the contact's four vertices: the
+        // rows are scanned kScan columns at a time, all four rows' loads of a
+        // window issued together and matched in registers
+        int32_t s0[4], len[4], off[4][4];
+#pragma unroll
+        for (int li = 0; li < 4; ++li) {
+            s0[li] = rp[w[li]];
+            len[li] = rp[w[li] + 1] - s0[li];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) off[li][m] = 0;
+        }
+        for (int32_t base = 0;; base += kScan) {
+            bool more = false;
+#pragma unroll
+            for (int li = 0; li < 4; ++li) {
+                int32_t col[kScan];
+#pragma unroll
+                for (int k = 0; k < kScan; ++k)
+                    col[k] = base + k < len[li] ? ci[s0[li] + base + k] : -1;
+#pragma unroll
+                for (int k = 0; k < kScan; ++k)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) off[li][m] = col[k] == w[m] ? base + k : off[li][m];
+                more |= base + kScan < len[li];
+            }
+            if (!more) break;
+        }
+#pragma unroll
+        for (int li = 0; li < 4; ++li) {
+            *reinterpret_cast<int4 *>(A.vf_slots + (4 * int64_t(e) + li) * 4) =
+                make_int4(off[li][0], off[li][1], off[li][2], off[li][3]);
+            A.vf_ids[4 * int64_t(e) + li] = w[li];
+        }
+        T *L[4];
+#pragma unroll
+        for (int li = 0; li < 4; ++li) L[li] = A.vf_eval + (4 * int64_t(e) + li) * kVfStrip;
         const int region = vf_region(xp, xt[0], xt[1], xt[2]);
         Dual2<T, 9> z[9];
 #pragma unroll
@@ -70,25 +110,30 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
             for (int c = 0; c < 3; ++c) z[3 * i + c] = Dual2<T, 9>::var(xt[i][c] - xp[c], 3 * i + c);
         const Dual2<T, 9> d = vf_distance(z, region);
         if (!(d.v < A.dhat)) {  // outside the barrier's support: an all-zero term
-            for (int c = 0; c < kVfEvalComps; ++c) L[S * c] = T(0);
+#pragma unroll
+            for (int li = 0; li < 4; ++li)
+                for (int c = 0; c < kVfStrip; ++c) L[li][c] = T(0);
             continue;
         }
         const Dual2<T, 9> en = barrier_of_distance(d, A.kappa, A.dhat);
-        L[0] = en.v;
-        // gradient: d/dt_i = d/dz_i, d/dp = -sum_i d/dz_i
+        // energy in the contact vertex's strip; gradient: d/dt_i = d/dz_i,
+        // d/dp = -sum_i d/dz_i
+        L[0][0] = en.v;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) L[1 + i][0] = T(0);
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
             T gp = T(0);
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 gp -= en.g[3 * i + c];
-                L[S * (1 + 3 * (1 + i) + c)] = en.g[3 * i + c];
+                L[1 + i][1 + c] = en.g[3 * i + c];
             }
-            L[S * (1 + c)] = gp;
+            L[0][1 + c] = gp;
         }
-        // Hessian, 12 x 12 row-major over (vertex, coordinate):
-        //   (t_i, t_j) = Hz_ij,  (p, t_j) = (t_j, p)^T = -sum_i Hz_ij,
-        //   (p, p) = sum_ij Hz_ij
+        // Hessian rows over the columns (p, t0, t1, t2) x coordinate:
+        //   (t_i, t_j) = Hz_ij,  (t_i, p) = -sum_j Hz_ij,
+        //   (p, t_j) = -sum_i Hz_ij,  (p, p) = sum_ij Hz_ij
 #pragma unroll
         for (int r = 0; r < 3; ++r)
 #pragma unroll
@@ -96,18 +141,24 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
                 T pp = T(0);
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
-                    T pj = T(0);  // (p r, t_j c)
+                    T pj = T(0);
 #pragma unroll
-                    for (int i = 0; i < 3; ++i) {
-                        const T h = en.hess(3 * i + r, 3 * j + c);
-                        L[S * (kVfHessOff + 12 * (3 * (1 + i) + r) + 3 * (1 + j) + c)] = h;
-                        pj -= h;
-                    }
-                    L[S * (kVfHessOff + 12 * r + 3 * (1 + j) + c)] = pj;
-                    L[S * (kVfHessOff + 12 * (3 * (1 + j) + c) + r)] = pj;
+                    for (int i = 0; i < 3; ++i) pj -= en.hess(3 * i + r, 3 * j + c);
+                    L[0][kVfHessOff + 12 * r + 3 * (1 + j) + c] = pj;
                     pp -= pj;
                 }
-                L[S * (kVfHessOff + 12 * r + c)] = pp;
+                L[0][kVfHessOff + 12 * r + c] = pp;
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    T ip = T(0);
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        const T h = en.hess(3 * i + r, 3 * j + c);
+                        L[1 + i][kVfHessOff + 12 * r + 3 * (1 + j) + c] = h;
+                        ip -= h;
+                    }
+                    L[1 + i][kVfHessOff + 12 * r + c] = ip;
+                }
             }
     }
 }
@@ -130,7 +181,6 @@ k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T
     const int act = A.state->active;
     if (act == 0) return;
     const int32_t n = A.state->nvf[act];
-    const int64_t S = A.vf_stride;
     const double beta = CG ? *cg.beta : 0.0;
     for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
          e += int32_t(gridDim.x) * kVfThreads) {
@@ -143,7 +193,9 @@ k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T
 #pragma unroll
             for (int i = 0; i < 3; ++i) ut[i][c] = vf_dir<T, CG>(u, cg, beta, int64_t(w[1 + i]) * 3 + c);
         }
-        T *L = A.vf_hvp + e;
+#pragma unroll
+        for (int li = 0; li < 4; ++li) A.vf_ids[4 * int64_t(e) + li] = w[li];
+        T *L = A.vf_hvp + 4 * int64_t(e) * kVfHvpStrip;
         const int region = vf_region(xp, xt[0], xt[1], xt[2]);
         // z_i = t_i - p seeded with the matching direction u_(t_i) - u_p
         DualHv<T, 9> z[9];
@@ -154,7 +206,7 @@ k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T
                 z[3 * i + c] = DualHv<T, 9>::var(xt[i][c] - xp[c], 3 * i + c, ut[i][c] - up[c]);
         const DualHv<T, 9> d = vf_distance(z, region);
         if (!(d.v < A.dhat)) {
-            for (int c = 0; c < kVfHvpComps; ++c) L[S * c] = T(0);
+            for (int c = 0; c < 4 * kVfHvpStrip; ++c) L[c] = T(0);
             continue;
         }
         const DualHv<T, 9> en = barrier_of_distance(d, A.kappa, A.dhat);
@@ -165,10 +217,12 @@ k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 yp -= en.gt[3 * i + c];
-                L[S * (3 * (1 + i) + c)] = en.gt[3 * i + c];
+                L[(1 + i) * kVfHvpStrip + c] = en.gt[3 * i + c];
             }
-            L[S * c] = yp;
+            L[c] = yp;
         }
+#pragma unroll
+        for (int li = 0; li < 4; ++li) L[li * kVfHvpStrip + 3] = T(0);
     }
 }
 
@@ -183,7 +237,9 @@ int vf_grid(int32_t cap)
 template <typename T>
 hipError_t launch_vf_eval(const RowArgs<T> &a, const T *x, hipStream_t s)
 {
-    if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_eval || a.vf_stride <= 0)
+    if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_eval || !a.vf_ids ||
+        !a.vf_slots || !a.pat.rp[1] || !a.pat.rp[2] || !a.pat.ci[1] || !a.pat.ci[2] ||
+        a.vf_stride <= 0)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_vf_eval<T>, dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0, s, a, x);
     return hipGetLastError();
@@ -193,7 +249,8 @@ template <typename T>
 hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, hipStream_t s,
                          const CgDir<T> &cg)
 {
-    if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_hvp || a.vf_stride <= 0)
+    if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_hvp || !a.vf_ids ||
+        a.vf_stride <= 0)
         return hipErrorInvalidValue;
     if (cg.r)
         hipLaunchKernelGGL((k_vf_hvp<T, true>), dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0,

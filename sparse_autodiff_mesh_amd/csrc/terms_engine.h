@@ -41,7 +41,13 @@
 namespace lad {
 namespace terms {
 
-constexpr int kTermBatch = 2;    // incident elements whose loads a lane issues together
+// Incident elements whose loads a lane issues together: more for small
+// stencils, whose per-element operands take few registers.
+template <int K>
+constexpr int term_batch()
+{
+    return K <= 2 ? 4 : 2;
+}
 
 // LDS hand-off between the lanes of one wave: a wave's LDS operations run in
 // issue order, so only the compiler must be kept from moving memory
@@ -54,6 +60,23 @@ __device__ __forceinline__ void terms_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The reverse of stream_out: n elements from global src into LDS dst, which
+// sits `pad` elements after a 16-byte boundary exactly where src is
+// misaligned, so the body moves in aligned 16-byte loads.
+template <int NT, typename T>
+__device__ __forceinline__ void stream_in(T *dst, const T *__restrict__ src, int n, int pad)
+{
+    constexpr int V = Vec<T>::n;
+    using VT = typename Vec<T>::type;
+    const int head = min(n, (V - pad) % V);
+    for (int i = threadIdx.x; i < head; i += NT) dst[i] = src[i];
+    const int nvec = (n - head) / V;
+    VT *dv = reinterpret_cast<VT *>(dst + head);
+    const VT *sv = reinterpret_cast<const VT *>(src + head);
+    for (int i = threadIdx.x; i < nvec; i += NT) dv[i] = __builtin_nontemporal_load(sv + i);
+    for (int i = head + nvec * V + threadIdx.x; i < n; i += NT) dst[i] = src[i];
+}
+
 // The row's contributions from one term type: for each batch of incident
 // elements, every load first (records, vertex ids, positions, constants),
 // then the evaluations.  D is the row's diagonal block, G its gradient,
@@ -64,6 +87,7 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
                                              T G[3], double &E)
 {
     constexpr int K = Term::kVerts, N = 3 * K, NC = Term::kConsts;
+    constexpr int kTermBatch = term_batch<K>();
     static_assert(K >= 1 && K <= kMaxVerts, "stencil of 1 to 4 vertices");
     const int32_t p0 = td.inc_ptr[a], p1 = td.inc_ptr[a + 1];
     for (int32_t base = p0; base < p1; base += kTermBatch) {
@@ -150,8 +174,7 @@ k_terms_eval(TermsArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
         T *Hs = stage + pad;
         if (fits) {
             if constexpr (ACC)
-                for (int k = int(threadIdx.x); k < nblk * 9; k += kRowThreads)
-                    Hs[k] = hv[int64_t(sb) * 9 + k];
+                stream_in<kRowThreads>(Hs, hv + int64_t(sb) * 9, nblk * 9, pad);
             else
                 for (int k = int(threadIdx.x); k < nblk * 9; k += kRowThreads) Hs[k] = T(0);
         }
@@ -186,6 +209,7 @@ __device__ __forceinline__ void row_term_hvp(const TermData<T> &td, int32_t a,
                                              T Y[3])
 {
     constexpr int K = Term::kVerts, NC = Term::kConsts;
+    constexpr int kTermBatch = term_batch<K>();
     const int32_t p0 = td.inc_ptr[a], p1 = td.inc_ptr[a + 1];
     for (int32_t base = p0; base < p1; base += kTermBatch) {
         TermInc rec[kTermBatch];
