@@ -33,6 +33,7 @@ class OracleProblem(ctypes.Structure):
         ("np", ctypes.c_int32), ("pairs", _i32p),
         ("kappa", ctypes.c_double), ("dhat", ctypes.c_double),
         ("nvf", ctypes.c_int32), ("vf", _i32p),
+        ("nq", ctypes.c_int32), ("quads", _i32p), ("kq", ctypes.c_double),
     ]
 
 
@@ -65,6 +66,9 @@ def lib():
         L.oracle_face_local.argtypes = [_f64p, _f64p, _f64p, _f64p,
                                         ctypes.c_double, _f64p, _f64p, _f64p]
         L.oracle_face_local.restype = None
+        L.oracle_quad_local.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_double,
+                                        _f64p, _f64p, _f64p]
+        L.oracle_quad_local.restype = None
         L.oracle_arap_local.argtypes = [_f64p, _f64p, _f64p, _f64p,
                                         ctypes.c_double, _f64p, _f64p, _f64p]
         L.oracle_arap_local.restype = None
@@ -98,7 +102,7 @@ class Problem:
 
     def __init__(self, nv, faces=None, springs=None, rest_len=None, k=0.0,
                  x_tilde=None, c=0.0, face_energy=False, dm_inv=None, area=None,
-                 pairs=None, kappa=0.0, dhat=0.0, vf=None):
+                 pairs=None, kappa=0.0, dhat=0.0, vf=None, quads=None, kq=0.0):
         self.nv = int(nv)
         self.faces = _i32(faces if faces is not None else np.zeros((0, 3))).reshape(-1, 3)
         self.springs = _i32(springs if springs is not None else np.zeros((0, 2))).reshape(-1, 2)
@@ -116,6 +120,8 @@ class Problem:
         self.kappa = float(kappa)
         self.dhat = float(dhat)
         self.vf = _i32(vf if vf is not None else np.zeros((0, 2))).reshape(-1, 2)
+        self.quads = _i32(quads if quads is not None else np.zeros((0, 4))).reshape(-1, 4)
+        self.kq = float(kq)
 
     def with_pairs(self, pairs, kappa=None, dhat=None):
         import copy
@@ -148,6 +154,9 @@ class Problem:
         s.dhat = self.dhat
         s.nvf = self.vf.shape[0]
         s.vf = _p(self.vf, _i32p)
+        s.nq = self.quads.shape[0]
+        s.quads = _p(self.quads, _i32p)
+        s.kq = self.kq
         return s
 
 
@@ -248,6 +257,12 @@ def face_local(x0, x1, x2, dm_inv, area):
                   _p(x2, _f64p), _p(dm, _f64p), float(area))
 
 
+def quad_local(x0, x1, x2, x3, kq):
+    x0, x1, x2, x3 = _f64(x0), _f64(x1), _f64(x2), _f64(x3)
+    return _local(lib().oracle_quad_local, 4, _p(x0, _f64p), _p(x1, _f64p), _p(x2, _f64p),
+                  _p(x3, _f64p), float(kq))
+
+
 def arap_local(x0, x1, x2, dm_inv, area):
     x0, x1, x2, dm = _f64(x0), _f64(x1), _f64(x2), _f64(dm_inv)
     return _local(lib().oracle_arap_local, 3, _p(x0, _f64p), _p(x1, _f64p),
@@ -280,7 +295,8 @@ def vf_distance_type(p, t0, t1, t2):
 
 
 def problem_from_mesh(mesh, springs=True, inertia=True, faces=False, pairs=None,
-                      kappa=0.0, dhat=0.0, k=None, c=None, f32=False, vf=None):
+                      kappa=0.0, dhat=0.0, k=None, c=None, f32=False, vf=None, quads=None,
+                      kq=0.0):
     """Build a Problem from a generated mesh bundle.  With f32=True every real
     input is rounded to fp32 first (the inputs an fp32 evaluation sees)."""
     r = (lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)) if f32 else (lambda a: a)
@@ -294,4 +310,4 @@ def problem_from_mesh(mesh, springs=True, inertia=True, faces=False, pairs=None,
         x_tilde=r(mesh.X) if inertia else None, c=rs(cc),
         face_energy=faces, dm_inv=r(mesh.dm_inv) if faces else None,
         area=r(mesh.area) if faces else None,
-        pairs=pairs, kappa=rs(kappa), dhat=rs(dhat), vf=vf)
+        pairs=pairs, kappa=rs(kappa), dhat=rs(dhat), vf=vf, quads=quads, kq=rs(kq))

@@ -34,7 +34,16 @@ static int cmp_rc(const void *a, const void *b)
 
 static int check_problem(const oracle_problem *p)
 {
-    if (!p || p->nv < 0 || p->nf < 0 || p->ns < 0 || p->np < 0 || p->nvf < 0) return -1;
+    if (!p || p->nv < 0 || p->nf < 0 || p->ns < 0 || p->np < 0 || p->nvf < 0 || p->nq < 0)
+        return -1;
+    if (p->nq > 0 && !p->quads) return -1;
+    for (int32_t q = 0; q < p->nq; ++q)
+        for (int i = 0; i < 4; ++i) {
+            int32_t v = p->quads[4 * (int64_t)q + i];
+            if (v < 0 || v >= p->nv) return -1;
+            for (int j = 0; j < i; ++j)
+                if (p->quads[4 * (int64_t)q + j] == v) return -1;
+        }
     if (p->nvf > 0 && !p->vf) return -1;
     if (p->nf > 0 && !p->faces) return -1;
     if (p->ns > 0 && (!p->springs || !p->rest_len)) return -1;
@@ -61,7 +70,7 @@ static int check_problem(const oracle_problem *p)
 static rc_pair *directed_pairs(const oracle_problem *p, int64_t *count)
 {
     int64_t n = (int64_t)p->nv + 6 * (int64_t)p->nf + 2 * (int64_t)p->ns +
-                2 * (int64_t)p->np + 6 * (int64_t)p->nvf;
+                2 * (int64_t)p->np + 6 * (int64_t)p->nvf + 12 * (int64_t)p->nq;
     rc_pair *e = (rc_pair *)malloc((size_t)(n > 0 ? n : 1) * sizeof(rc_pair));
     if (!e) return NULL;
     int64_t m = 0;
@@ -89,6 +98,12 @@ static rc_pair *directed_pairs(const oracle_problem *p, int64_t *count)
             e[m].r = v; e[m].c = t; ++m;
             e[m].r = t; e[m].c = v; ++m;
         }
+    }
+    for (int32_t q = 0; q < p->nq; ++q) {
+        const int32_t *t = p->quads + 4 * (int64_t)q;
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                if (i != j) { e[m].r = t[i]; e[m].c = t[j]; ++m; }
     }
     qsort(e, (size_t)m, sizeof(rc_pair), cmp_rc);
     *count = m;
@@ -392,6 +407,45 @@ void oracle_arap_local(const double *x0, const double *x1, const double *x2,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Quad planarity: 0.5 kq D^2, D = det[x1 - x0, x2 - x0, x3 - x0]            */
+/* (the triple product (x1 - x0) . ((x2 - x0) x (x3 - x0)))                 */
+/* ------------------------------------------------------------------------ */
+
+static hd quad_energy_hd(const hd *X, double kq)
+{
+    hd a[3], b[3], c[3];
+    for (int r = 0; r < 3; ++r) {
+        a[r] = hd_sub(X[3 + r], X[r]);
+        b[r] = hd_sub(X[6 + r], X[r]);
+        c[r] = hd_sub(X[9 + r], X[r]);
+    }
+    hd bxc0 = hd_sub(hd_mul(b[1], c[2]), hd_mul(b[2], c[1]));
+    hd bxc1 = hd_sub(hd_mul(b[2], c[0]), hd_mul(b[0], c[2]));
+    hd bxc2 = hd_sub(hd_mul(b[0], c[1]), hd_mul(b[1], c[0]));
+    hd D = hd_add(hd_add(hd_mul(a[0], bxc0), hd_mul(a[1], bxc1)), hd_mul(a[2], bxc2));
+    return hd_scale(hd_mul(D, D), 0.5 * kq);
+}
+
+void oracle_quad_local(const double *x0, const double *x1, const double *x2,
+                       const double *x3, double kq, double *E, double *g12, double *H144)
+{
+    const double *xs[4] = {x0, x1, x2, x3};
+    hd X[12];
+    for (int a = 0; a < 12; ++a)
+        for (int b = a; b < 12; ++b) {
+            for (int i = 0; i < 12; ++i)
+                X[i] = hd_make(xs[i / 3][i % 3], i == a ? 1.0 : 0.0, i == b ? 1.0 : 0.0);
+            hd e = quad_energy_hd(X, kq);
+            H144[12 * a + b] = e.d;
+            H144[12 * b + a] = e.d;
+            if (a == b) {
+                g12[a] = e.b;
+                *E = e.a;
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Vertex-face contact: barrier of the point-triangle distance              */
 /* ------------------------------------------------------------------------ */
 
@@ -610,6 +664,13 @@ int oracle_eval(const oracle_problem *p, const int32_t *row_ptr,
         oracle_vf_local(x + 3 * (int64_t)vid[0], x + 3 * (int64_t)vid[1],
                         x + 3 * (int64_t)vid[2], x + 3 * (int64_t)vid[3], p->kappa, p->dhat,
                         &e, gl, Hl);
+        E += e;
+        if (scatter(row_ptr, col_idx, 4, vid, gl, Hl, g, hvals)) return -3;
+    }
+    for (int32_t q = 0; q < p->nq; ++q) {
+        for (int i = 0; i < 4; ++i) vid[i] = p->quads[4 * (int64_t)q + i];
+        oracle_quad_local(x + 3 * (int64_t)vid[0], x + 3 * (int64_t)vid[1],
+                          x + 3 * (int64_t)vid[2], x + 3 * (int64_t)vid[3], p->kq, &e, gl, Hl);
         E += e;
         if (scatter(row_ptr, col_idx, 4, vid, gl, Hl, g, hvals)) return -3;
     }

@@ -21,7 +21,8 @@
  *    d2F / dx_{row,r} dx_{col_idx[k],c} at vals[9k + 3r + c].
  *  - the pattern row of vertex a is {a} U {b : a, b share a face or a
  *    spring} U {pair partners of a} U {the face vertices of a's vertex-face
- *    contacts} U {the vertices in contact with a face of a}.
+ *    contacts} U {the vertices in contact with a face of a} U {the other
+ *    vertices of a's planarity quads}.
  *  - the Hessian is exact (no projection or clamping).
  *
  * Every function returns 0 on success and a negative value on bad input.
@@ -55,6 +56,9 @@ typedef struct {
     int32_t nvf;                 /* vertex-face contacts; vf[2*e] = vertex,
                                     vf[2*e + 1] = face id (not one of its own) */
     const int32_t *vf;
+    int32_t nq;                  /* four-vertex planarity elements; quads[4*q + i] */
+    const int32_t *quads;
+    double kq;                   /* their stiffness */
 } oracle_problem;
 
 /* Pattern: number of blocks, then the arrays (row_ptr[nv+1], col_idx[nnzb]). */
@@ -95,6 +99,11 @@ void oracle_face_local(const double *x0, const double *x1, const double *x2,
 void oracle_arap_local(const double *x0, const double *x1, const double *x2,
                        const double *dm_inv, double area, double *E,
                        double *g9, double *H81);
+/* Quad planarity 0.5 kq det[x1 - x0, x2 - x0, x3 - x0]^2 (six times the
+ * signed volume of the tetrahedron on the four points, squared); value and
+ * exact derivatives from hyper-dual numbers, local DOF order x0..x3. */
+void oracle_quad_local(const double *x0, const double *x1, const double *x2,
+                       const double *x3, double kq, double *E, double *g12, double *H144);
 /* Vertex-face contact: the barrier b(d) of the distance d from point p to
  * the triangle (t0, t1, t2).  The closest point's region is decided at the
  * given positions (type 0-2: vertex t_i; 3, 4, 5: the interior of edge

@@ -133,6 +133,14 @@ def grid_faces(n: int) -> np.ndarray:
     return F
 
 
+def grid_quads(n: int) -> np.ndarray:
+    """The (n-1)^2 cells of the grid as four-vertex elements (v00, v10, v11,
+    v01), cells in row-major order; int32 (Q, 4)."""
+    j, i = np.meshgrid(np.arange(n - 1), np.arange(n - 1), indexing="ij")
+    v00 = (j * n + i).reshape(-1)
+    return np.stack([v00, v00 + 1, v00 + n + 1, v00 + n], axis=1).astype(np.int32)
+
+
 def unique_edges(faces: np.ndarray) -> np.ndarray:
     """Unique undirected edges (min, max) of a triangle list, sorted."""
     e = np.concatenate([faces[:, [0, 1]], faces[:, [1, 2]], faces[:, [2, 0]]])
