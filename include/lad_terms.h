@@ -29,6 +29,9 @@
  *   LAD_TERMS_SYMDIR      symmetric_dirichlet_face: 3 vertices,
  *                           A (tr C + tr C / det C), C = F^T F  [as arap_face]
  *   LAD_TERMS_ARAP_CLOTH  arap_face, spring, inertia
+ *   LAD_TERMS_CLOTH_QUAD  spring, inertia, and
+ *                         quad_planarity: 4 vertices,
+ *                           0.5 k det[x1 - x0, x2 - x0, x3 - x0]^2  [k]
  *
  * Layout and conventions are those of lad.h: x, v, g, y are [nv][3] of the
  * dtype; H values are [nnzb][3][3] row-major blocks in the pattern's
@@ -56,7 +59,8 @@ enum {
     LAD_TERMS_CLOTH = 1,
     LAD_TERMS_ARAP = 2,
     LAD_TERMS_SYMDIR = 3,
-    LAD_TERMS_ARAP_CLOTH = 4
+    LAD_TERMS_ARAP_CLOTH = 4,
+    LAD_TERMS_CLOTH_QUAD = 5
 };
 
 /* The elements of one term of a set. */

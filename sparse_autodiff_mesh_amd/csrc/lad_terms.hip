@@ -92,6 +92,7 @@ using SetCloth = TermList<Spring, Inertia>;
 using SetArap = TermList<ArapFace>;
 using SetSymDirichlet = TermList<SymDirichletFace>;
 using SetArapCloth = TermList<ArapFace, Spring, Inertia>;
+using SetClothQuad = TermList<Spring, Inertia, QuadPlanarity>;
 
 // Calls f(list) for the set's term list; false for an unknown set.
 template <typename F>
@@ -102,6 +103,7 @@ bool with_set(int set, F &&f)
     case kSetArap: f(SetArap{}); return true;
     case kSetSymDirichlet: f(SetSymDirichlet{}); return true;
     case kSetArapCloth: f(SetArapCloth{}); return true;
+    case kSetClothQuad: f(SetClothQuad{}); return true;
     default: return false;
     }
 }
@@ -114,11 +116,13 @@ int set_terms(int set, TermInfo out[kMaxTerms])
     const TermInfo inertia = info_of<Inertia>("inertia");
     const TermInfo arap = info_of<ArapFace>("arap_face");
     const TermInfo sd = info_of<SymDirichletFace>("symmetric_dirichlet_face");
+    const TermInfo quad = info_of<QuadPlanarity>("quad_planarity");
     switch (set) {
     case kSetCloth: out[0] = spring; out[1] = inertia; return 2;
     case kSetArap: out[0] = arap; return 1;
     case kSetSymDirichlet: out[0] = sd; return 1;
     case kSetArapCloth: out[0] = arap; out[1] = spring; out[2] = inertia; return 3;
+    case kSetClothQuad: out[0] = spring; out[1] = inertia; out[2] = quad; return 3;
     default: return 0;
     }
 }

@@ -20,6 +20,7 @@ constexpr int kSetCloth = 1;
 constexpr int kSetArap = 2;
 constexpr int kSetSymDirichlet = 3;
 constexpr int kSetArapCloth = 4;
+constexpr int kSetClothQuad = 5;
 
 // One element seen from the row of one of its vertices: e is the element
 // id; pk holds the row vertex's position i in the element (bits 0-1) and,

@@ -103,5 +103,27 @@ struct SymDirichletFace {
     }
 };
 
+// Quad planarity: 0.5 k det[x1 - x0, x2 - x0, x3 - x0]^2, the squared
+// (six-fold) volume of the tetrahedron on a quad's four vertices, zero
+// exactly when they are coplanar;  c = {k}
+struct QuadPlanarity {
+    static constexpr int kVerts = 4;
+    static constexpr int kConsts = 1;
+    template <class D, class T>
+    __device__ __forceinline__ static D energy(const D (&x)[4][3], const T *c)
+    {
+        D a[3], b[3], e[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            a[r] = x[1][r] - x[0][r];
+            b[r] = x[2][r] - x[0][r];
+            e[r] = x[3][r] - x[0][r];
+        }
+        const D det = a[0] * (b[1] * e[2] - b[2] * e[1]) + a[1] * (b[2] * e[0] - b[0] * e[2]) +
+                      a[2] * (b[0] * e[1] - b[1] * e[0]);
+        return (T(0.5) * c[0]) * sqr(det);
+    }
+};
+
 }  // namespace terms
 }  // namespace lad

@@ -11,7 +11,7 @@ import numpy as np
 from . import binding
 from .binding import LadError, _stream
 
-SETS = {"cloth": 1, "arap": 2, "symdir": 3, "arap_cloth": 4}
+SETS = {"cloth": 1, "arap": 2, "symdir": 3, "arap_cloth": 4, "cloth_quad": 5}
 
 TERMS_EXPORTS = [
     "lad_terms_describe", "lad_terms_build", "lad_terms_eval", "lad_terms_hvp",
@@ -169,10 +169,11 @@ class Terms:
         return rp, ci[: n.value]
 
 
-def mesh_blocks(mesh, set_id, k=None, c=None):
+def mesh_blocks(mesh, set_id, k=None, c=None, kq=1.0):
     """Term blocks of a generated grid bundle for one of the compiled sets:
     springs with (rest length, k), one inertia element per vertex with
-    (rest position, c), faces with (Dm^-1, rest area)."""
+    (rest position, c), faces with (Dm^-1, rest area), grid cells as
+    planarity quads with (kq)."""
     kk = mesh.params.get("k", 0.0) if k is None else k
     cc = mesh.params.get("c", 0.0) if c is None else c
     spring = (mesh.springs, np.stack([mesh.rest_len, np.full(len(mesh.rest_len), kk)], axis=1))
@@ -180,5 +181,9 @@ def mesh_blocks(mesh, set_id, k=None, c=None):
                np.concatenate([mesh.X, np.full((mesh.nv, 1), cc)], axis=1))
     face = (mesh.faces, np.concatenate([mesh.dm_inv, mesh.area.reshape(-1, 1)], axis=1))
     name = {v: k_ for k_, v in SETS.items()}.get(set_id, set_id)
+    if name == "cloth_quad":
+        from .inputs import grid_quads
+        q = grid_quads(mesh.n)
+        return [spring, inertia, (q, np.full((len(q), 1), float(kq)))]
     return {"cloth": [spring, inertia], "arap": [face], "symdir": [face],
             "arap_cloth": [face, spring, inertia]}[name]

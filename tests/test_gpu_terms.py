@@ -1,8 +1,9 @@
 """GPU parity of the term front end (lad_terms_* through the C ABI): each
-compiled term set against the oracle on identical inputs -- pattern bit for
-bit, E, g, H and H v within gpu_util.TOL -- in the fused and the unfused
-mode; the generic cloth set against the fixed-function cloth kernels; and
-the 512 x 512 ARAP face grid and 1000 x 1000 cloth at full size (fp32)."""
+compiled term set (stencils of 1 to 4 vertices) against the oracle on
+identical inputs -- pattern bit for bit, E, g, H and H v within
+gpu_util.TOL -- in the fused and the unfused mode; the generic cloth set
+against the fixed-function cloth kernels; and the 512 x 512 ARAP face grid
+and 1000 x 1000 cloth at full size (fp32)."""
 import numpy as np
 import pytest
 
@@ -15,17 +16,26 @@ pytestmark = pytest.mark.gpu
 
 # oracle problem of each set: (springs, inertia, face term)
 ORACLE_TERMS = {"cloth": (True, True, False), "arap": (False, False, "arap"),
-                "symdir": (False, False, True), "arap_cloth": (True, True, "arap")}
+                "symdir": (False, False, True), "arap_cloth": (True, True, "arap"),
+                "cloth_quad": (True, True, False)}
+def kq_of(m):
+    # planarity stiffness of the cloth_quad set, scaled as h^-4 so that the
+    # quad terms weigh about as much as the springs in E, g and H (the
+    # determinant is of order h^3, its gradient of order h^2)
+    return 1.0e3 / m.h ** 4
 
 
 def oracle_problem(m, set_id, dtype):
     sp, ine, face = ORACLE_TERMS[set_id]
-    return oracle.problem_from_mesh(m, springs=sp, inertia=ine, faces=face, f32=(dtype == "f32"))
+    quads = inputs.grid_quads(m.n) if set_id == "cloth_quad" else None
+    return oracle.problem_from_mesh(m, springs=sp, inertia=ine, faces=face, f32=(dtype == "f32"),
+                                    quads=quads, kq=kq_of(m) if quads is not None else 0.0)
 
 
 def run_set(m, set_id, dtype, fused=True, x=None):
     import torch
-    T = terms.Terms(m.nv, set_id, terms.mesh_blocks(m, set_id), dtype=dtype, fused=fused)
+    T = terms.Terms(m.nv, set_id, terms.mesh_blocks(m, set_id, kq=kq_of(m)), dtype=dtype,
+                    fused=fused)
     x_h = host_input(m.x if x is None else x, dtype)
     v_h = host_input(inputs.hvp_direction(m.nv), dtype)
     E, g, H = T.eval(dev(x_h, dtype))
@@ -51,7 +61,7 @@ def check(m, set_id, dtype, out, x_h, v_h):
     assert rel(out["y"], yo) <= tol, rel(out["y"], yo)
 
 
-@pytest.mark.parametrize("set_id", ["cloth", "arap", "symdir", "arap_cloth"])
+@pytest.mark.parametrize("set_id", ["cloth", "arap", "symdir", "arap_cloth", "cloth_quad"])
 @pytest.mark.parametrize("n,dtype,fused", [(3, "f64", True), (10, "f64", True),
                                            (10, "f64", False), (37, "f32", True),
                                            (37, "f32", False), (100, "f64", True)])
@@ -62,7 +72,7 @@ def test_sets_match_oracle(lad, set_id, n, dtype, fused):
     check(m, set_id, dtype, out, x_h, v_h)
 
 
-@pytest.mark.parametrize("set_id", ["cloth", "arap_cloth"])
+@pytest.mark.parametrize("set_id", ["cloth", "arap_cloth", "cloth_quad"])
 def test_fused_and_unfused_agree(lad, set_id):
     log_case(test="terms_fusion", set=set_id)
     m = inputs.cloth(50)

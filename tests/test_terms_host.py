@@ -37,6 +37,8 @@ def test_sets_describe_their_terms(L):
     assert terms.describe("symdir") == [("symmetric_dirichlet_face", 3, 5)]
     assert terms.describe("arap_cloth") == [("arap_face", 3, 5), ("spring", 2, 2),
                                             ("inertia", 1, 4)]
+    assert terms.describe("cloth_quad") == [("spring", 2, 2), ("inertia", 1, 4),
+                                            ("quad_planarity", 4, 1)]
     with pytest.raises(binding.LadError):
         terms.describe(99)
     n, ar = ctypes.c_int32(), ctypes.c_int32()
