@@ -267,8 +267,26 @@ def bench_secondary(torch, binding, inputs, args, timer):
     sec["cloth1000_newton_cg_ms_per_iter"] = round(r["median_ms"] / its, 5)
     sec["cloth1000_newton_cg_GBps"] = round(bcg * its / (r["median_ms"] * 1e-3) / 1e9, 1)
     sec["cloth1000_newton_cg_rel_residual"] = float(f"{stats['rel_residual']:.3e}")
-    # vector objective on the same context: residuals + explicit sparse
-    # Jacobian, and the matrix-free Gauss-Newton product
+    # the same solve on the 100 x 100 cloth, where every kernel is short and
+    # the launches per iteration dominate
+    m100 = inputs.cloth(100)
+    L100 = cloth_ctx(binding, m100, "f32")
+    z100 = inputs.gaussian_block(11, m100.X.size).reshape(m100.X.shape)
+    xs100 = to_dev(torch, m100.X + 0.002 * m100.h * z100, "f32")
+    _, gs100, _ = L100.eval(xs100)
+    ps100 = torch.empty_like(gs100)
+    st100 = {}
+
+    def cg100():
+        st100.update(L100.newton_cg(xs100, gs100, out=ps100, max_iters=its, eta=1e-12)[1])
+
+    r = timer.run(cg100, max(5, steps // 5), 2)
+    if st100["iterations"] != its:
+        raise RuntimeError(f"Newton-CG stopped early: {st100}")
+    sec["cloth100_newton_cg_ms_per_iter"] = round(r["median_ms"] / its, 5)
+    L100.close()
+    # vector objective on the 1000 x 1000 context: residuals + explicit
+    # sparse Jacobian, and the matrix-free Gauss-Newton product
     R, Jv = L.residual_jacobian(xc)
     r = timer.run(lambda: L.residual_jacobian(xc, out=(R, Jv)), steps, warm)
     bj = compulsory_bytes_residual_jacobian(mc.nv, mc.springs.shape[0], 4)

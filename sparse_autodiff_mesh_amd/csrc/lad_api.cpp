@@ -70,7 +70,8 @@ struct lad_ctx {
     int32_t *d_jrp = nullptr, *d_jci = nullptr;
     // Newton-CG work space, allocated by the first lad_newton_cg call
     void *cg_r = nullptr, *cg_d = nullptr, *cg_d2 = nullptr, *cg_y = nullptr;
-    double *cg_parts = nullptr;
+    double *cg_parts = nullptr;      // partial sums of d.Bd
+    double *cg_parts2 = nullptr;     // partial sums of r.r
     int32_t cg_nparts = 0;
     CgState *d_cg = nullptr;
     CgState *h_cg = nullptr;         // pinned host copy
@@ -345,18 +346,18 @@ hipError_t enqueue_hvp_patch(lad_ctx *ctx, const void *x, const void *v, void *y
 
 // y = H v.  The row path can also produce per-workgroup partial sums of
 // v.y (into dot_parts, returning their number in *dot_parts_used; 0 means
-// the caller must compute v.y itself), return at once while *skip != 0,
-// and form v itself as a Newton-CG direction (cg.r non-null).
+// the caller must compute v.y itself) and form v itself as a Newton-CG
+// direction (cg.r non-null), taking the step that closes the previous
+// update first.
 template <typename T>
 hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s,
                        double *dot_parts = nullptr, int32_t *dot_parts_used = nullptr,
-                       const int32_t *skip = nullptr, const CgDir<T> &cg = CgDir<T>{})
+                       const CgDir<T> &cg = CgDir<T>{})
 {
     if (dot_parts_used) *dot_parts_used = 0;
     if (ctx->row_mode) {
         RowArgs<T> a = row_args<T>(ctx);
         a.hvp_dot = dot_parts;
-        a.hvp_skip = skip;
         if (dot_parts_used && dot_parts) *dot_parts_used = ctx->grid_hvp;
         // the vertex-face contacts' H_e u_e first (the rows add them)
         if (ctx->vf_cap > 0) {
@@ -384,8 +385,9 @@ hipError_t cg_workspace(lad_ctx *ctx)
     if (e == hipSuccess && ctx->row_mode) e = dev_alloc(ctx, &d2, bytes);
     if (e == hipSuccess) e = dev_alloc(ctx, &y, bytes);
     const int32_t np = std::max<int32_t>(kCgMaxGrid, ctx->grid_hvp);
-    double *parts = nullptr;
+    double *parts = nullptr, *parts2 = nullptr;
     if (e == hipSuccess) e = dev_alloc(ctx, &parts, size_t(np));
+    if (e == hipSuccess) e = dev_alloc(ctx, &parts2, size_t(kCgMaxGrid));
     CgState *st = nullptr;
     if (e == hipSuccess) e = dev_alloc(ctx, &st, 1);
     CgState *h = nullptr;
@@ -396,6 +398,7 @@ hipError_t cg_workspace(lad_ctx *ctx)
     ctx->cg_d2 = d2;
     ctx->cg_y = y;
     ctx->cg_parts = parts;
+    ctx->cg_parts2 = parts2;
     ctx->cg_nparts = np;
     ctx->d_cg = st;
     ctx->h_cg = h;
@@ -403,13 +406,17 @@ hipError_t cg_workspace(lad_ctx *ctx)
 }
 
 // Truncated Newton-CG (line-search Newton-CG, Nocedal and Wright,
-// Algorithm 7.1): per iteration the new direction d = -r + beta d, y = H d
-// and the partial sums of d.y; alpha; p and r updates with the partial sums
-// of r.r; beta.  On the row path the direction update and the d.y sums are
-// fused into the HVP (d alternates between two buffers), so an iteration is
-// four launches; the patch path runs them as separate kernels.  All scalars
-// stay on the device; the host reads the stop flag every kCgCheck
-// iterations and the final state.
+// Algorithm 7.1).  Iteration j: the direction (after the step that closes
+// update j - 1: convergence or beta) d = -r + beta d, y = H d and the
+// partial sums of d.y; then update j (after its step: the negative-
+// curvature exit or alpha) p += alpha d, r += alpha y with the partial sums
+// of r.r.  Each step is taken by every workgroup of the kernel that needs
+// it, so the row path runs two launches per iteration (the direction and
+// the d.y sums are fused into the HVP, d alternating between two buffers);
+// the patch path runs the direction, its HVP, the d.y sums and the update.
+// One launch after the last iteration closes it.  All scalars stay on the
+// device; the host reads the stop flag every kCgCheck iterations and the
+// final state.
 template <typename T>
 hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *pv,
                              int32_t max_iters, double eta, hipStream_t s)
@@ -423,37 +430,38 @@ hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *
     T *r = static_cast<T *>(ctx->cg_r), *d = static_cast<T *>(ctx->cg_d),
       *y = static_cast<T *>(ctx->cg_y);
     CgState *st = ctx->d_cg;
-    const int32_t *stop = reinterpret_cast<const int32_t *>(reinterpret_cast<const char *>(st) +
-                                                            offsetof(CgState, stop));
-    e = launch_cg_init<T>(g, p, r, d, n, ctx->cg_parts, grid, s);
-    if (e == hipSuccess) e = launch_cg_start(ctx->cg_parts, grid, st, eta, max_iters, s);
-    const double *beta = reinterpret_cast<const double *>(reinterpret_cast<const char *>(st) +
-                                                          offsetof(CgState, beta));
-    for (int32_t done = 0; e == hipSuccess && done < max_iters;) {
+    e = launch_cg_init<T>(g, p, r, d, n, ctx->cg_parts2, grid, s);
+    if (e == hipSuccess) e = launch_cg_start(ctx->cg_parts2, grid, st, eta, max_iters, s);
+    int32_t done = 0;
+    while (e == hipSuccess && done < max_iters) {
         const int32_t nb = std::min(kCgCheck, max_iters - done);
         for (int32_t it = 0; it < nb && e == hipSuccess; ++it) {
+            const int32_t j = done + it;
             int32_t nparts = 0;
             T *dj = d;  // this iteration's direction
             if (ctx->row_mode) {
                 // d_j = -r + beta d_(j-1) inside the HVP; beta is 0 on the
                 // first iteration, where d_(-1) = -g from the init kernel
-                T *d_old = (done + it) % 2 == 0 ? d : static_cast<T *>(ctx->cg_d2);
-                dj = (done + it) % 2 == 0 ? static_cast<T *>(ctx->cg_d2) : d;
+                T *d_old = j % 2 == 0 ? d : static_cast<T *>(ctx->cg_d2);
+                dj = j % 2 == 0 ? static_cast<T *>(ctx->cg_d2) : d;
                 CgDir<T> cg;
                 cg.r = r;
                 cg.d_old = d_old;
                 cg.d_new = dj;
-                cg.beta = beta;
-                e = enqueue_hvp<T>(ctx, x, nullptr, y, s, ctx->cg_parts, &nparts, stop, cg);
+                cg.st = st;
+                cg.rr_parts = ctx->cg_parts2;
+                cg.n_rr = grid;
+                cg.iter = j;
+                e = enqueue_hvp<T>(ctx, x, nullptr, y, s, ctx->cg_parts, &nparts, cg);
             } else {
-                if (done + it > 0) e = launch_cg_dir<T>(r, d, n, grid, st, s);
+                if (j > 0) e = launch_cg_dir<T>(r, d, n, grid, ctx->cg_parts2, grid, st, j, s);
                 if (e == hipSuccess) e = enqueue_hvp<T>(ctx, x, d, y, s);
                 nparts = grid;
                 if (e == hipSuccess) e = launch_cg_dot<T>(d, y, n, ctx->cg_parts, grid, st, s);
             }
-            if (e == hipSuccess) e = launch_cg_alpha(ctx->cg_parts, nparts, st, s);
-            if (e == hipSuccess) e = launch_cg_update<T>(p, r, dj, y, n, ctx->cg_parts, grid, st, s);
-            if (e == hipSuccess) e = launch_cg_beta(ctx->cg_parts, grid, st, max_iters, s);
+            if (e == hipSuccess)
+                e = launch_cg_update<T>(p, r, dj, y, n, ctx->cg_parts, nparts, ctx->cg_parts2,
+                                        grid, st, j, s);
         }
         done += nb;
         if (e == hipSuccess && done < max_iters) {
@@ -462,6 +470,7 @@ hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *
             if (e == hipSuccess && ctx->h_cg->stop) break;
         }
     }
+    if (e == hipSuccess) e = launch_cg_close(ctx->cg_parts2, grid, st, done, s);
     if (e == hipSuccess) e = launch_cg_final<T>(g, p, n, grid, st, s);
     if (e == hipSuccess) e = hipMemcpyAsync(ctx->h_cg, st, sizeof(CgState), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = host_sync(ctx, s);
@@ -871,7 +880,7 @@ lad_status lad_newton_cg(lad_ctx *ctx, const void *d_x, const void *d_g, void *d
         stats->reason = h.reason;
         stats->grad_norm = h.gnorm;
         stats->rel_residual = (h.reason == LAD_CG_NEG_CURVATURE && h.iter == 0) ? 1.0
-                              : h.gnorm > 0.0 ? std::sqrt(h.rr) / h.gnorm
+                              : h.gnorm > 0.0 ? std::sqrt(h.rrv[h.iter & 1]) / h.gnorm
                                               : 0.0;
     }
     return LAD_OK;

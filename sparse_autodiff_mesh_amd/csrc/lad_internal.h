@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "lad.h"
+#include "lad_solve.h"
 
 namespace lad {
 
@@ -212,9 +213,8 @@ struct RowArgs {
     const DevState *state;
     PatternBufs pat;
     // HVP only: per-workgroup partial sums of v.y into hvp_dot[blockIdx]
-    // (null: none), and an early exit when *hvp_skip != 0 (null: never)
+    // (null: none)
     double *hvp_dot;
-    const int32_t *hvp_skip;
     // vertex-face contacts: per-contact local terms formed by launch_vf_eval
     // / launch_vf_hvp (contact e's vertex m = 0..3 is the contact vertex, then
     // the face's three; strip 4e + m holds what row "vertex m" needs)
@@ -245,15 +245,20 @@ hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, Energy
 template <typename T>
 hipError_t launch_eval_pair_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                                  int grid, hipStream_t s);
-// Newton-CG direction formed inside the row HVP: the operand is
-// v = -r + beta d_old (beta read from the device), and every row stores its
-// v into d_new.  With r null the HVP's operand is v itself.
+// Newton-CG direction formed inside the row HVP: every workgroup first
+// takes the step that closes the previous update (cg_device.h: convergence
+// or beta, from the partial sums of r.r; workgroup 0 records it in *st),
+// then uses v = -r + beta d_old, and every row stores its v into d_new.  At
+// iter 0 beta is 0 (d_old = -g).  With r null the HVP's operand is v itself.
 template <typename T>
 struct CgDir {
     const T *r = nullptr;
     const T *d_old = nullptr;
     T *d_new = nullptr;
-    const double *beta = nullptr;
+    CgState *st = nullptr;
+    const double *rr_parts = nullptr;  // partial sums of r.r after update iter - 1
+    int32_t n_rr = 0;
+    int32_t iter = 0;                  // updates completed before this direction
 };
 template <typename T>
 hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,

@@ -27,6 +27,7 @@
 #include "dual2.h"
 #include "energies.h"
 #include "lad_device.h"
+#include "cg_device.h"
 #include "lad_internal.h"
 #include "lad_jacobian.h"
 #include "residuals.h"
@@ -604,11 +605,8 @@ __global__ void __launch_bounds__(kRowThreads)
 k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y,
            CgDir<T> cg)
 {
-    // early exit once a Newton-CG solve has ended; the flag and beta are
-    // loaded together with the first row group's operands (below)
-    const int32_t skip = A.hvp_skip ? *A.hvp_skip : 0;
+    double beta = 0.0;
     // operand component i: v[i], or the next Newton-CG direction -r + beta d
-    const double beta = CG ? *cg.beta : 0.0;
     auto dir = [&](int64_t i) -> T {
         if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
         else return v[i];
@@ -628,12 +626,34 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     Row<T> rn;
     T vn[3];
     double vy = 0.0;  // this lane's part of v.y
-    if (an < r1) {
+    if constexpr (CG) {
+        // The first group's header and direction operands are loaded before
+        // the Newton-CG step below, so that their latency overlaps its sum.
+        T r_a[3], d_a[3];
+        if (an < r1) {
+            rn = load_row<T, false>(A, act, rpa, an, x);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                r_a[k] = cg.r[int64_t(an) * 3 + k];
+                d_a[k] = cg.d_old[int64_t(an) * 3 + k];
+            }
+        }
+        // Every workgroup takes the step that closes the previous update
+        // (convergence or beta) from the partial sums of r.r, the same way;
+        // none runs once the solve has ended.
+        int32_t stop = cg_stop<kRowThreads>(cg.st, nullptr);
+        if (!stop && cg.iter > 0)
+            beta = cg_beta_step<kRowThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, blockIdx.x == 0,
+                                             stop, nullptr, nullptr);
+        if (stop) return;  // workgroup-uniform
+        if (an < r1)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) vn[k] = T(-double(r_a[k]) + beta * double(d_a[k]));
+    } else if (an < r1) {
         rn = load_row<T, false>(A, act, rpa, an, x);
 #pragma unroll
         for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
     }
-    if (skip) return;  // workgroup-uniform
     for (; an < r1;) {
         const Row<T> r = rn;
         T va[3], Y[3] = {T(0), T(0), T(0)};

@@ -10,13 +10,17 @@
 namespace lad {
 
 // Scalars of one Newton-CG solve, kept on the device so that no iteration
-// needs the host: written only by the single-workgroup kernels
-// (launch_cg_start / _alpha / _beta), read by the rest.
+// needs the host.  Each scalar step of an iteration is computed by every
+// workgroup of the kernel that needs it, from the same partial sums in the
+// same order, so all take the same decision; workgroup 0 records it here.
+// r.r after k updates sits in rrv[k & 1]: a kernel that records the new
+// value reads the previous one from the other slot, so no workgroup reads a
+// field that workgroup 0 of the same kernel writes.
 struct CgState {
-    double rr;       // r.r of the current residual
+    double rrv[2];   // r.r after an even / odd number of updates
     double eps2;     // stop when r.r < eps2
-    double alpha;    // step of the current iteration
-    double beta;     // direction update of the current iteration
+    double alpha;    // step of the latest update
+    double beta;     // direction update of the latest direction
     double gnorm;    // |g|
     int32_t iter;    // completed CG updates
     int32_t stop;    // nonzero once the solve has ended
@@ -41,19 +45,24 @@ hipError_t launch_cg_start(const double *parts, int nparts, CgState *st, double 
 template <typename T>
 hipError_t launch_cg_dot(const T *a, const T *b, int64_t n, double *parts, int grid,
                          const CgState *st, hipStream_t s);
-// d.Bd from its partial sums: negative-curvature exit or the step alpha.
-hipError_t launch_cg_alpha(const double *parts, int nparts, CgState *st, hipStream_t s);
-// p += alpha d, r += alpha y; partial sums of the new r.r.
+// Update `iter` (0-based): its step from the partial sums of d.Bd
+// (dy_parts[0 .. n_dy)) -- the negative-curvature exit or alpha -- then
+// p += alpha d, r += alpha y, and the partial sums of the new r.r into
+// rr_parts[0 .. grid).
 template <typename T>
-hipError_t launch_cg_update(T *p, T *r, const T *d, const T *y, int64_t n, double *parts,
-                            int grid, const CgState *st, hipStream_t s);
-// New r.r from its partial sums: convergence, the iteration cap, or beta.
-hipError_t launch_cg_beta(const double *parts, int nparts, CgState *st, int32_t max_iters,
-                          hipStream_t s);
+hipError_t launch_cg_update(T *p, T *r, const T *d, const T *y, int64_t n, const double *dy_parts,
+                            int n_dy, double *rr_parts, int grid, CgState *st, int32_t iter,
+                            hipStream_t s);
+// Direction `iter` (>= 1) on the patch path: the step closing update
+// iter - 1 from the partial sums of r.r (convergence, or beta), then
 // d = -r + beta d.
 template <typename T>
-hipError_t launch_cg_dir(const T *r, T *d, int64_t n, int grid, const CgState *st,
-                         hipStream_t s);
+hipError_t launch_cg_dir(const T *r, T *d, int64_t n, int grid, const double *rr_parts,
+                         int n_rr, CgState *st, int32_t iter, hipStream_t s);
+// After the last update (`iters` in all): the step closing it, convergence
+// or the iteration cap.  One workgroup; nothing once the solve has ended.
+hipError_t launch_cg_close(const double *rr_parts, int n_rr, CgState *st, int32_t iters,
+                           hipStream_t s);
 // p = -g when the first direction already had non-positive curvature.
 template <typename T>
 hipError_t launch_cg_final(const T *g, T *p, int64_t n, int grid, const CgState *st,

@@ -23,6 +23,7 @@
 // [0, nvf[active]) with a stride loop.
 #include <hip/hip_runtime.h>
 
+#include "cg_device.h"
 #include "contact_vf.h"
 #include "dual2.h"
 #include "lad_internal.h"
@@ -32,6 +33,7 @@ namespace lad {
 namespace {
 
 constexpr int kVfThreads = 64;
+static_assert(kVfThreads == kRowThreads, "the Newton-CG step must be summed as the row HVP sums it");
 
 constexpr int kScan = 8;  // columns of a row matched per step
 
@@ -177,11 +179,20 @@ template <typename T, bool CG>
 __global__ void __launch_bounds__(kVfThreads)
 k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T> cg)
 {
-    if (A.hvp_skip && *A.hvp_skip) return;
+    // Newton-CG: the same step closing the previous update that the row HVP
+    // takes after this kernel (same partial sums, same order, same
+    // workgroup size), recorded there, not here
+    double beta = 0.0;
+    if constexpr (CG) {
+        int32_t stop = cg_stop<kVfThreads>(cg.st, nullptr);
+        if (!stop && cg.iter > 0)
+            beta = cg_beta_step<kVfThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, false, stop,
+                                            nullptr, nullptr);
+        if (stop) return;
+    }
     const int act = A.state->active;
     if (act == 0) return;
     const int32_t n = A.state->nvf[act];
-    const double beta = CG ? *cg.beta : 0.0;
     for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
          e += int32_t(gridDim.x) * kVfThreads) {
         int32_t w[4];
