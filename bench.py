@@ -374,6 +374,38 @@ def bench_secondary(torch, binding, inputs, args, timer):
     L.close()
     sec["vf_contacts_per_step"] = P
     sec.update(bench_terms(torch, inputs, args, timer, steps, warm))
+    sec.update(bench_patch_path(torch, binding, inputs, args, timer, steps, warm))
+    return sec
+
+
+def bench_patch_path(torch, binding, inputs, args, timer, steps, warm):
+    """The element-owner patch path (the pages' own decomposition: LDS
+    patches with ghost vertices, LDS accumulation, atomic flush of boundary
+    blocks; or colour phases in the deterministic mode) on the headline
+    cloth and the face grid, for comparison with the row path."""
+    sec = {}
+    m = inputs.cloth(args.n)
+    x = to_dev(torch, m.x, "f32")
+    for det in (False, True):
+        L = binding.Lad(m.nv, dtype="f32", path="patch", deterministic=det,
+                        **binding.mesh_terms(m))
+        out = L.alloc_outputs()
+        r = timer.run(lambda: L.eval(x, out=out, energy=False), steps, warm)
+        tag = "cloth1000_patch_det" if det else "cloth1000_patch"
+        nnzb = L.get_info()["nnzb_base"]
+        sec[tag + "_eval_ms"] = round(r["median_ms"], 5)
+        sec[tag + "_eval_GBps"] = round(
+            compulsory_bytes_eval(m.nv, m.springs.shape[0], 0, nnzb, 4) /
+            (r["median_ms"] * 1e-3) / 1e9, 1)
+        L.close()
+    f = inputs.face_grid(512)
+    L = binding.Lad(f.nv, dtype="f32", path="patch",
+                    **binding.mesh_terms(f, springs=False, inertia=False, faces=True))
+    x = to_dev(torch, f.x, "f32")
+    out = L.alloc_outputs()
+    r = timer.run(lambda: L.eval(x, out=out, energy=False), steps, warm)
+    sec["faces512_patch_eval_ms"] = round(r["median_ms"], 5)
+    L.close()
     return sec
 
 
