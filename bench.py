@@ -193,8 +193,8 @@ def to_dev(torch, a, dtype):
 
 def bench_headline(torch, binding, inputs, args, timer):
     m = inputs.cloth(args.n)
-    L = binding.Lad(m.nv, dtype="f32", patch_lds_bytes=args.patch_lds,
-                    **binding.mesh_terms(m))
+    L = binding.Lad(m.nv, dtype="f32", patch_lds_bytes=args.patch_lds, path=args.path,
+                    deterministic=args.deterministic, **binding.mesh_terms(m))
     info = L.get_info()
     x = to_dev(torch, m.x, "f32")
     E, g, H = L.alloc_outputs()
@@ -493,6 +493,10 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--flush-mall", action="store_true",
                     help="write a 512 MB scratch buffer before every timed call")
+    ap.add_argument("--path", default="auto", choices=["auto", "rows", "patch"],
+                    help="decomposition of the headline evaluation (auto picks rows)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="patch path: colour phases instead of LDS atomics")
     ap.add_argument("--patch-lds", type=int, default=0,
                     help="LDS bytes per patch (0 = library default)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -532,7 +536,7 @@ def main():
     kern_ms = tk["mean_ms"]
     melem = res["terms"] / (ms * 1e-3) / 1e6
     achieved = res["bytes"] / (kern_ms * 1e-3) / 1e9
-    traffic = read_traffic()
+    traffic = read_traffic() if res["info"]["eval_path"] == 2 else None
     line = {
         "metric": "grad+Hessian ms/eval & Melem/s on 1000² cloth (1 GPU); "
                   "achieved HBM GB/s vs peak",
@@ -564,7 +568,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "kernel": ("k_eval_rows<float>" if res["info"]["eval_path"] == 2
-                       else "k_eval_patch<float,false>"),
+                       else f"k_eval_patch<float,{'true' if args.deterministic else 'false'}>"),
             "kernel_ms_mean": round(kern_ms, 5),
             "kernel_ms_median": round(tk["median_ms"], 5),
             "call_ms_mean_with_energy": round(t["mean_ms"], 5),
