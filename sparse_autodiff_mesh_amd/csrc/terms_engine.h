@@ -77,6 +77,72 @@ __device__ __forceinline__ void stream_in(T *dst, const T *__restrict__ src, int
     for (int i = head + nvec * V + threadIdx.x; i < n; i += NT) dst[i] = src[i];
 }
 
+// Terms that depend only on differences of their vertices' positions say so
+// (kTranslationInvariant); the engine then differentiates them in the
+// positions of vertices 1 .. K-1 with vertex 0 held fixed, on one full
+// second-order number of 3(K-1) variables, and rebuilds the row's blocks
+// from the zero block-row sums of a translation-invariant Hessian:
+//   g_0 = -sum_j g_j,   H_jk as computed (j, k >= 1),
+//   H_0k = H_k0^T = -sum_j H_jk,   H_00 = sum_jk H_jk.
+// For K <= 3 that is fewer numbers per value than the strip (10 against 25
+// for two vertices, 28 against 37 for three).
+template <typename Term>
+constexpr bool use_relative()
+{
+    return Term::kTranslationInvariant && Term::kVerts >= 2 && Term::kVerts <= 3;
+}
+
+// Row i's blocks of element (e, vertices vid) by relative seeding; adds
+// into D (the row's diagonal), G and the row's blocks at the offsets in pk.
+template <typename Term, typename T>
+__device__ __forceinline__ void row_elem_relative(const T (&xv)[Term::kVerts][3], const T *cc,
+                                                  int i, uint32_t pk, T *Hrow, T D[9], T G[3],
+                                                  double &E)
+{
+    constexpr int K = Term::kVerts, NZ = 3 * (K - 1);
+    Dual2<T, NZ> z[K][3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) z[0][c] = Dual2<T, NZ>::constant(xv[0][c]);
+#pragma unroll
+    for (int v = 1; v < K; ++v)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) z[v][c] = Dual2<T, NZ>::var(xv[v][c], 3 * (v - 1) + c);
+    const Dual2<T, NZ> en = Term::energy(z, cc);
+    if (i == 0) E += double(en.v);
+    // Hessian block (a, b) of the full element, a, b = 0 .. K-1, entry (r, c)
+    auto hb = [&](int a, int b, int r, int c) -> T {
+        T s = T(0);
+#pragma unroll
+        for (int j = 1; j < K; ++j)
+#pragma unroll
+            for (int k = 1; k < K; ++k) {
+                const T h = en.hess(3 * (j - 1) + r, 3 * (k - 1) + c);
+                const T wa = a == 0 ? T(-1) : (a == j ? T(1) : T(0));
+                const T wb = b == 0 ? T(-1) : (b == k ? T(1) : T(0));
+                s += (wa * wb) * h;
+            }
+        return s;
+    };
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        T gi = T(0);
+#pragma unroll
+        for (int j = 1; j < K; ++j) gi += (i == 0 ? T(-1) : (i == j ? T(1) : T(0))) * en.g[3 * (j - 1) + r];
+        G[r] += gi;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) D[3 * r + c] += hb(i, i, r, c);
+    }
+#pragma unroll
+    for (int b = 1; b < K; ++b) {
+        const int v = (i + b) % K;
+        T *B = Hrow + 9 * int32_t((pk >> (8 * b)) & 255u);
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) B[3 * r + c] += hb(i, v, r, c);
+    }
+}
+
 // The row's contributions from one term type: for each batch of incident
 // elements, every load first (records, vertex ids, positions, constants),
 // then the evaluations.  D is the row's diagonal block, G its gradient,
@@ -114,6 +180,10 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
         for (int j = 0; j < kTermBatch; ++j) {
             if (base + j >= p1) break;
             const int i = int(rec[j].pk & 3u);
+            if constexpr (use_relative<Term>()) {
+                row_elem_relative<Term>(xv[j], cc[j], i, rec[j].pk, Hrow, D, G, E);
+                continue;
+            }
             StripDual<T, N> z[K][3];
 #pragma unroll
             for (int v = 0; v < K; ++v) {

@@ -6,6 +6,9 @@
 //   struct Term {
 //       static constexpr int kVerts;   // vertices per element (1 .. 4)
 //       static constexpr int kConsts;  // per-element constants (numbers)
+//       static constexpr bool kTranslationInvariant;  // depends on position
+//                                      // differences only (moving every
+//                                      // vertex by the same vector keeps it)
 //       template <class D, class T>
 //       __device__ static D energy(const D (&x)[kVerts][3], const T *c);
 //   };
@@ -31,6 +34,7 @@ namespace terms {
 struct Spring {
     static constexpr int kVerts = 2;
     static constexpr int kConsts = 2;
+    static constexpr bool kTranslationInvariant = true;
     template <class D, class T>
     __device__ __forceinline__ static D energy(const D (&x)[2][3], const T *c)
     {
@@ -44,6 +48,7 @@ struct Spring {
 struct Inertia {
     static constexpr int kVerts = 1;
     static constexpr int kConsts = 4;
+    static constexpr bool kTranslationInvariant = false;
     template <class D, class T>
     __device__ __forceinline__ static D energy(const D (&x)[1][3], const T *c)
     {
@@ -75,6 +80,7 @@ __device__ __forceinline__ void face_C(const D (&x)[3][3], const T *c, D &c00, D
 struct ArapFace {
     static constexpr int kVerts = 3;
     static constexpr int kConsts = 5;
+    static constexpr bool kTranslationInvariant = true;
     template <class D, class T>
     __device__ __forceinline__ static D energy(const D (&x)[3][3], const T *c)
     {
@@ -92,6 +98,7 @@ struct ArapFace {
 struct SymDirichletFace {
     static constexpr int kVerts = 3;
     static constexpr int kConsts = 5;
+    static constexpr bool kTranslationInvariant = true;
     template <class D, class T>
     __device__ __forceinline__ static D energy(const D (&x)[3][3], const T *c)
     {
@@ -109,6 +116,7 @@ struct SymDirichletFace {
 struct QuadPlanarity {
     static constexpr int kVerts = 4;
     static constexpr int kConsts = 1;
+    static constexpr bool kTranslationInvariant = true;
     template <class D, class T>
     __device__ __forceinline__ static D energy(const D (&x)[4][3], const T *c)
     {
