@@ -154,3 +154,52 @@ def test_cloth_1000_generic_f32(lad):
     out, x_h, v_h = run_set(m, "cloth", "f32")
     assert out["ci"].size == 6992002
     check(m, "cloth", "f32", out, x_h, v_h)
+
+
+def test_row_longer_than_256_blocks_is_rejected(lad):
+    # a star: vertex 0 joined by springs to 300 others (row of 301 blocks)
+    log_case(test="terms_long_row")
+    nv = 301
+    springs = np.stack([np.zeros(nv - 1, np.int32), np.arange(1, nv, dtype=np.int32)], axis=1)
+    blocks = [(springs, np.tile([1.0, 10.0], (nv - 1, 1))),
+              (np.arange(nv, dtype=np.int32).reshape(-1, 1), np.zeros((nv, 4)))]
+    with pytest.raises(lad.LadError) as ei:
+        terms.Terms(nv, "cloth", blocks, dtype="f32")
+    assert ei.value.status == lad.LAD_ERR_ARG and "256 blocks" in str(ei.value)
+    # 255 partners (a row of 256 blocks) is the longest row accepted
+    m = 256
+    T = terms.Terms(m, "cloth", [(springs[: m - 1], np.tile([1.0, 10.0], (m - 1, 1))),
+                                 (np.arange(m, dtype=np.int32).reshape(-1, 1),
+                                  np.zeros((m, 4)))], dtype="f64")
+    assert T.nnzb == m + 2 * (m - 1)
+    x = np.random.default_rng(3).normal(size=(m, 3))
+    v_h = inputs.hvp_direction(m)
+    E, g, H = T.eval(dev(x, "f64"))
+    y = T.hvp(dev(x, "f64"), dev(v_h, "f64"))
+    rp, ci = T.pattern()
+    prob = oracle.Problem(nv=m, springs=springs[: m - 1], rest_len=np.ones(m - 1), k=10.0,
+                          x_tilde=np.zeros((m, 3)), c=0.0)
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x)
+    assert rel([E.item()], [Eo]) <= 1e-12
+    assert rel(g.cpu().numpy(), go) <= 1e-12
+    assert rel(H.cpu().numpy()[: oci.size], Ho) <= 1e-12
+    assert rel(y.cpu().numpy(), oracle.bsr_spmv(orp, oci, Ho, v_h)) <= 1e-12
+    T.close()
+
+
+def test_single_vertex(lad):
+    log_case(test="terms_single_vertex")
+    blocks = [(np.zeros((0, 2), np.int32), np.zeros((0, 2))),
+              (np.zeros((1, 1), np.int32), np.array([[0.5, -1.0, 2.0, 3.0]]))]
+    T = terms.Terms(1, "cloth", blocks, dtype="f64")
+    x = np.array([[1.0, 1.0, 1.0]])
+    E, g, H = T.eval(dev(x, "f64"))
+    y = T.hvp(dev(x, "f64"), dev(np.array([[1.0, 2.0, 3.0]]), "f64"))
+    assert T.nnzb == 1
+    assert E.item() == pytest.approx(0.5 * 3.0 * (0.25 + 4.0 + 1.0), rel=1e-15)
+    assert np.allclose(g.cpu().numpy(), 3.0 * np.array([[0.5, 2.0, -1.0]]), rtol=1e-15)
+    assert np.allclose(H.cpu().numpy()[0], 3.0 * np.eye(3), rtol=1e-15)
+    assert np.allclose(y.cpu().numpy(), [[3.0, 6.0, 9.0]], rtol=1e-15)
+    T.close()
