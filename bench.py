@@ -504,8 +504,8 @@ def main():
                          "(reference kernel for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (the multi-GPU sharding is a design, not an implementation)",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not "
+              "supported (sharding over several GPUs is designed, not implemented)",
               file=sys.stderr)
         return 2
 
