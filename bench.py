@@ -453,10 +453,15 @@ def bench_terms(torch, inputs, args, timer, steps, warm):
     return sec
 
 
+CPU_SAMPLE_SECONDS = 10.0   # CPU work the baseline leg spends (bounded)
+
+
 def cpu_baseline(inputs, res):
     """The fp64 oracle, single-threaded, on the same 1000 x 1000 cloth (inputs
-    rounded to fp32 as the GPU sees them): one evaluation, the pattern built
-    beforehand and not timed."""
+    rounded to fp32 as the GPU sees them): full evaluations repeated until
+    about CPU_SAMPLE_SECONDS of work (at most 100), the median one reported;
+    the pattern is built beforehand and not timed."""
+    import statistics
     import oracle
     m = res["mesh"]
     prob = oracle.problem_from_mesh(m, f32=True)
@@ -464,18 +469,22 @@ def cpu_baseline(inputs, res):
     rp, ci = oracle.pattern(prob)
     t_pat = time.perf_counter() - t0
     x = inputs.round_f32(m.x)
-    t0 = time.perf_counter()
-    E, _, _ = oracle.evaluate(prob, rp, ci, x)
-    t_eval = time.perf_counter() - t0
+    times = []
+    E = None
+    while sum(times) < CPU_SAMPLE_SECONDS and len(times) < 100:
+        t0 = time.perf_counter()
+        E, _, _ = oracle.evaluate(prob, rp, ci, x)
+        times.append(time.perf_counter() - t0)
+    t_eval = statistics.median(times)
     rel_e = abs(E - res["energy"]) / abs(E)
     return {
         "value": round(res["terms"] / t_eval / 1e6, 4),
         "unit": "Melem/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one full evaluation of the {m.n}x{m.n} cloth "
-                   f"({res['terms']} terms), fp64, single thread; "
-                   f"pattern build {t_pat:.2f} s untimed"),
+        "sample": (f"{len(times)} full evaluations of the {m.n}x{m.n} cloth "
+                   f"({res['terms']} terms) in {sum(times):.1f} s, fp64, single thread, "
+                   f"median reported; pattern build {t_pat:.2f} s untimed"),
         "ms_per_eval": round(t_eval * 1e3, 1),
         "cpu_model": cpu_model(),
         "host_cpus": os.cpu_count(),
