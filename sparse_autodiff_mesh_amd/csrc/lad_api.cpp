@@ -344,6 +344,13 @@ hipError_t enqueue_hvp_patch(lad_ctx *ctx, const void *x, const void *v, void *y
     return e;
 }
 
+// Workgroups of the touched-row HVP kernel (a grid-stride loop over the
+// pattern's incidence entries); 0 without contact capacity.
+int pair_hvp_grid(const lad_ctx *ctx)
+{
+    return std::min<int32_t>(ctx->pair_blocks, kCgMaxGrid);
+}
+
 // y = H v.  The row path can also produce per-workgroup partial sums of
 // v.y (into dot_parts, returning their number in *dot_parts_used; 0 means
 // the caller must compute v.y itself) and form v itself as a Newton-CG
@@ -356,17 +363,23 @@ hipError_t enqueue_hvp(lad_ctx *ctx, const void *x, const void *v, void *y, hipS
 {
     if (dot_parts_used) *dot_parts_used = 0;
     if (ctx->row_mode) {
+        // every row's topology terms; then, with contacts possible, the
+        // vertex-face contacts' H_e u_e and the touched rows, which add their
+        // contact terms (and their part of v.y after the rows' own)
         RowArgs<T> a = row_args<T>(ctx);
         a.hvp_dot = dot_parts;
-        if (dot_parts_used && dot_parts) *dot_parts_used = ctx->grid_hvp;
-        // the vertex-face contacts' H_e u_e first (the rows add them)
-        if (ctx->vf_cap > 0) {
-            const hipError_t e = launch_vf_hvp<T>(a, static_cast<const T *>(x),
-                                                  static_cast<const T *>(v), s, cg);
-            if (e != hipSuccess) return e;
-        }
-        return launch_hvp_rows<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
-                                  static_cast<T *>(y), ctx->grid_hvp, s, cg);
+        const T *xt = static_cast<const T *>(x);
+        hipError_t e = launch_hvp_rows<T>(a, xt, static_cast<const T *>(v), static_cast<T *>(y),
+                                          ctx->grid_hvp, s, cg);
+        const T *u = cg.r ? cg.d_new : static_cast<const T *>(v);  // the direction as stored
+        if (e == hipSuccess && ctx->vf_cap > 0) e = launch_vf_hvp<T>(a, xt, u, cg.st, s);
+        const int pg = pair_hvp_grid(ctx);
+        if (e == hipSuccess && pg > 0)
+            e = launch_hvp_pair_rows<T>(a, xt, u, static_cast<T *>(y),
+                                        dot_parts ? dot_parts + ctx->grid_hvp : nullptr, pg,
+                                        cg.st, s);
+        if (dot_parts_used && dot_parts) *dot_parts_used = ctx->grid_hvp + pg;
+        return e;
     }
     return enqueue_hvp_patch<T>(ctx, x, v, y, s);
 }
@@ -384,7 +397,7 @@ hipError_t cg_workspace(lad_ctx *ctx)
     if (e == hipSuccess) e = dev_alloc(ctx, &d, bytes);
     if (e == hipSuccess && ctx->row_mode) e = dev_alloc(ctx, &d2, bytes);
     if (e == hipSuccess) e = dev_alloc(ctx, &y, bytes);
-    const int32_t np = std::max<int32_t>(kCgMaxGrid, ctx->grid_hvp);
+    const int32_t np = std::max<int32_t>(kCgMaxGrid, ctx->grid_hvp + pair_hvp_grid(ctx));
     double *parts = nullptr, *parts2 = nullptr;
     if (e == hipSuccess) e = dev_alloc(ctx, &parts, size_t(np));
     if (e == hipSuccess) e = dev_alloc(ctx, &parts2, size_t(kCgMaxGrid));

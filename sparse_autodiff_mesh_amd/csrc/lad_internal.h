@@ -267,9 +267,19 @@ hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, in
 // enqueued before the row kernels that add them (same stream).
 template <typename T>
 hipError_t launch_vf_eval(const RowArgs<T> &a, const T *x, hipStream_t s);
+// H_e u_e of every contact of the active buffer (before
+// launch_hvp_pair_rows, which adds them); with st set, nothing once the
+// Newton-CG solve has ended.
 template <typename T>
-hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, hipStream_t s,
-                         const CgDir<T> &cg = CgDir<T>{});
+hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, const CgState *st,
+                         hipStream_t s);
+// The runtime contacts' part of y = H v for the rows they touch, added to
+// what launch_hvp_rows stored (same stream, after it and launch_vf_hvp);
+// with dot set, workgroup b stores its partial sum of v.(the added part)
+// at dot[b].  grid = pair_rows_grid(the pattern's incidence capacity).
+template <typename T>
+hipError_t launch_hvp_pair_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, double *dot,
+                                int grid, const CgState *st, hipStream_t s);
 template <typename T>
 hipError_t launch_pairs_eval(const DevState *st, PatternBufs pat, const T *x,
                              T *g, T *hvals, EnergySink es, int nblocks,

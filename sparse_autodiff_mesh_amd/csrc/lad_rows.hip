@@ -600,7 +600,9 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
 // Matrix-free Hessian-vector product, y_a = sum over the row's terms of
 // H_ab v_b, with the local Hessians formed in registers and never stored.
 // ---------------------------------------------------------------------------
-template <typename T, bool FACES, bool PAIRS, bool CG>
+// Every row's topology terms (springs, faces, inertia); the runtime
+// contacts of the rows they touch are added afterwards by k_hvp_pair_rows.
+template <typename T, bool FACES, bool CG>
 __global__ void __launch_bounds__(kRowThreads)
 k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y,
            CgDir<T> cg)
@@ -611,9 +613,9 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
         else return v[i];
     };
-    const int act = PAIRS ? A.state->active : 0;
-    const int32_t *rpa = A.pat.rp[act];
-    const int32_t *cia = A.pat.ci[act];
+    constexpr int act = 0;  // the topology pattern
+    const int32_t *rpa = A.rp0;
+    const int32_t *cia = A.ci0;
     // Nothing is staged here, so a workgroup takes a contiguous row range
     // (ranges grouped by XCD) and walks it 64 rows at a time.  The row
     // header, position and direction of the next group are loaded while the
@@ -668,9 +670,6 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
 #pragma unroll
             for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
         }
-        const int32_t npa = act != 0 ? A.state->np[act] : 0;
-        PairPre<T> pp;
-        prefetch_pairs(A, act, npa, r, x, pp);
         // Every term is evaluated once in DualHv numbers seeded with the
         // term's variables and the matching components of v; the gradient's
         // directional derivative gt is the term's Hessian applied to v.
@@ -745,57 +744,6 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
 #pragma unroll
             for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
         }
-        auto pair_hv = [&](const T xb[3], const T vb[3]) {
-            T dz[3];
-#pragma unroll
-            for (int cc = 0; cc < 3; ++cc) dz[cc] = r.xa[cc] - xb[cc];
-            const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
-            if (!(l2 < A.dhat * A.dhat)) return;
-            DualHv<T, 3> d[3];
-#pragma unroll
-            for (int cc = 0; cc < 3; ++cc) d[cc] = DualHv<T, 3>::var(dz[cc], cc, va[cc] - vb[cc]);
-            const DualHv<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
-#pragma unroll
-            for (int cc = 0; cc < 3; ++cc) Y[cc] += e.gt[cc];
-        };
-        {
-            T vp[kRowPairs][3];
-#pragma unroll
-            for (int k = 0; k < kRowPairs; ++k)
-#pragma unroll
-                for (int cc = 0; cc < 3; ++cc) vp[k][cc] = dir(int64_t(pp.b[k]) * 3 + cc);
-#pragma unroll
-            for (int k = 0; k < kRowPairs; ++k)
-                if (k < pp.n) pair_hv(pp.xb[k], vp[k]);
-        }
-        // vertex-face contact e: the row's part of H_e u_e, formed by k_vf_hvp
-        auto vf_hv = [&](int32_t e) {
-            const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
-            const int li = w.x == r.a ? 0 : (w.y == r.a ? 1 : (w.z == r.a ? 2 : 3));
-            const T *L = A.vf_hvp + (4 * int64_t(e) + li) * kVfHvpStrip;
-#pragma unroll
-            for (int c = 0; c < 3; ++c) Y[c] += L[c];
-        };
-        if (r.p1 - r.p0 > pp.n) {
-            const int32_t *pl = A.pat.pinc[act];
-            const int32_t *prs = A.pat.pairs[act];
-            for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
-                const int32_t qp = pl[k];
-                if (qp >= npa) {
-                    vf_hv(qp - npa);
-                    continue;
-                }
-                const int32_t i0 = prs[2 * qp], i1 = prs[2 * qp + 1];
-                const int32_t b = i0 == r.a ? i1 : i0;
-                T xb[3], vb[3];
-#pragma unroll
-                for (int cc = 0; cc < 3; ++cc) {
-                    xb[cc] = x[int64_t(b) * 3 + cc];
-                    vb[cc] = dir(int64_t(b) * 3 + cc);
-                }
-                pair_hv(xb, vb);
-            }
-        }
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             y[int64_t(r.a) * 3 + k] = Y[k];
@@ -805,6 +753,79 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     if (A.hvp_dot) {
         const double sum = block_sum<kRowThreads>(vy, nullptr);
         if (threadIdx.x == 0) A.hvp_dot[blockIdx.x] = sum;
+    }
+}
+
+// The runtime contacts' part of y for the rows they touch, after
+// k_hvp_rows (topology terms of every row) and k_vf_hvp (the contacts'
+// H_e u_e strips): the grid strides over the incidence entries and the
+// thread at a row's first entry adds the row's pair terms, evaluated here
+// in DualHv numbers, and its contact strips, in element order.  With dot
+// set each workgroup stores its partial sum of v_a . (the added part),
+// which completes the Newton-CG d.Hd sums of k_hvp_rows; nothing is added
+// once the solve has ended.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+k_hvp_pair_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v,
+                T *__restrict__ y, double *__restrict__ dot, const CgState *st)
+{
+    __shared__ double red[kThreads / 64];
+    const int act = A.state->active;
+    const bool live = !(st && st->stop) && act != 0;
+    const int32_t ninc = live ? A.pat.pinc_ptr[act][A.nv] : 0;
+    double part = 0.0;
+    for (int32_t k = int32_t(blockIdx.x) * kThreads + int32_t(threadIdx.x); k < ninc;
+         k += int32_t(gridDim.x) * kThreads) {
+        const int32_t a = A.pat.trow[act][k];
+        if (a >= 0) {
+            const int32_t p0 = A.pat.pinc_ptr[act][a], p1 = A.pat.pinc_ptr[act][a + 1];
+            const int32_t npa = A.state->np[act];
+            const int32_t *pl = A.pat.pinc[act];
+            const int32_t *prs = A.pat.pairs[act];
+            T xa[3], va[3], Y[3] = {T(0), T(0), T(0)};
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                xa[c] = x[int64_t(a) * 3 + c];
+                va[c] = v[int64_t(a) * 3 + c];
+            }
+            for (int32_t q0 = p0; q0 < p1; ++q0) {
+                const int32_t q = pl[q0];
+                if (q >= npa) {  // vertex-face contact: the row's strip of H_e u_e
+                    const int32_t e = q - npa;
+                    const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
+                    const int li = w.x == a ? 0 : (w.y == a ? 1 : (w.z == a ? 2 : 3));
+                    const T *L = A.vf_hvp + (4 * int64_t(e) + li) * kVfHvpStrip;
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) Y[c] += L[c];
+                    continue;
+                }
+                const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
+                const int32_t b = i0 == a ? i1 : i0;
+                T dz[3], dv[3];
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    dz[c] = xa[c] - x[int64_t(b) * 3 + c];
+                    dv[c] = va[c] - v[int64_t(b) * 3 + c];
+                }
+                const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
+                if (!(l2 < A.dhat * A.dhat)) continue;  // outside the barrier's support
+                DualHv<T, 3> d[3];
+#pragma unroll
+                for (int c = 0; c < 3; ++c) d[c] = DualHv<T, 3>::var(dz[c], c, dv[c]);
+                const DualHv<T, 3> en = barrier_energy(d, A.kappa, A.dhat);
+#pragma unroll
+                for (int c = 0; c < 3; ++c) Y[c] += en.gt[c];
+            }
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                y[int64_t(a) * 3 + c] += Y[c];
+                part += double(va[c]) * double(Y[c]);
+            }
+        }
+    }
+    if (dot) {
+        const double sum = block_sum<kThreads>(part, red);
+        if (threadIdx.x == 0) dot[blockIdx.x] = sum;
     }
 }
 
@@ -892,7 +913,7 @@ static hipError_t rows_occupancy(int lds, int *occ_e, int *occ_h)
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_e, k_eval_rows<T, F, P>,
                                                                 kRowThreads, lds);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, P, false>,
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, false>,
                                                          kRowThreads, 0);
     return e;
 }
@@ -963,16 +984,16 @@ hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, Energy
     return hipGetLastError();
 }
 
-template <typename T, bool F, bool P>
+template <typename T, bool F>
 static void launch_hvp_rows_as(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
                                hipStream_t s, const CgDir<T> &cg)
 {
     if (cg.r)
-        hipLaunchKernelGGL((k_hvp_rows<T, F, P, true>), dim3(grid), dim3(kRowThreads), 0, s, a,
-                           x, v, y, cg);
+        hipLaunchKernelGGL((k_hvp_rows<T, F, true>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v,
+                           y, cg);
     else
-        hipLaunchKernelGGL((k_hvp_rows<T, F, P, false>), dim3(grid), dim3(kRowThreads), 0, s, a,
-                           x, v, y, cg);
+        hipLaunchKernelGGL((k_hvp_rows<T, F, false>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v,
+                           y, cg);
 }
 
 template <typename T>
@@ -980,11 +1001,21 @@ hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, in
                            hipStream_t s, const CgDir<T> &cg)
 {
     if (a.faces_on)
-        a.pairs_on ? launch_hvp_rows_as<T, true, true>(a, x, v, y, grid, s, cg)
-                   : launch_hvp_rows_as<T, true, false>(a, x, v, y, grid, s, cg);
+        launch_hvp_rows_as<T, true>(a, x, v, y, grid, s, cg);
     else
-        a.pairs_on ? launch_hvp_rows_as<T, false, true>(a, x, v, y, grid, s, cg)
-                   : launch_hvp_rows_as<T, false, false>(a, x, v, y, grid, s, cg);
+        launch_hvp_rows_as<T, false>(a, x, v, y, grid, s, cg);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_hvp_pair_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, double *dot,
+                                int grid, const CgState *st, hipStream_t s)
+{
+    for (int k = 1; k <= 2; ++k)  // the contact buffers the kernel may read
+        if (!a.pat.pairs[k] || !a.pat.pinc_ptr[k] || !a.pat.pinc[k] || !a.pat.trow[k])
+            return hipErrorInvalidValue;
+    if (a.vf_stride > 0 && (!a.vf_ids || !a.vf_hvp)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_hvp_pair_rows<T>, dim3(grid), dim3(kThreads), 0, s, a, x, v, y, dot, st);
     return hipGetLastError();
 }
 
@@ -996,7 +1027,9 @@ hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, in
     template hipError_t launch_eval_pair_rows<T>(const RowArgs<T> &, const T *, T *, T *,         \
                                                  EnergySink, int, hipStream_t);                   \
     template hipError_t launch_hvp_rows<T>(const RowArgs<T> &, const T *, const T *, T *, int,    \
-                                           hipStream_t, const CgDir<T> &);
+                                           hipStream_t, const CgDir<T> &);                        \
+    template hipError_t launch_hvp_pair_rows<T>(const RowArgs<T> &, const T *, const T *, T *,    \
+                                                double *, int, const CgState *, hipStream_t);
 LAD_ROWS_INST(float)
 LAD_ROWS_INST(double)
 

@@ -23,7 +23,6 @@
 // [0, nvf[active]) with a stride loop.
 #include <hip/hip_runtime.h>
 
-#include "cg_device.h"
 #include "contact_vf.h"
 #include "dual2.h"
 #include "lad_internal.h"
@@ -33,7 +32,6 @@ namespace lad {
 namespace {
 
 constexpr int kVfThreads = 64;
-static_assert(kVfThreads == kRowThreads, "the Newton-CG step must be summed as the row HVP sums it");
 
 constexpr int kScan = 8;  // columns of a row matched per step
 
@@ -165,31 +163,12 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
     }
 }
 
-// Direction component i: u[i], or the Newton-CG direction -r + beta d_old
-// (the same value the row HVP forms for its own rows).
-template <typename T, bool CG>
-__device__ __forceinline__ T vf_dir(const T *__restrict__ u, const CgDir<T> &cg, double beta,
-                                    int64_t i)
-{
-    if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
-    else return u[i];
-}
-
-template <typename T, bool CG>
+// With st set (Newton-CG), nothing is done once the solve has ended.
+template <typename T>
 __global__ void __launch_bounds__(kVfThreads)
-k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T> cg)
+k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, const CgState *st)
 {
-    // Newton-CG: the same step closing the previous update that the row HVP
-    // takes after this kernel (same partial sums, same order, same
-    // workgroup size), recorded there, not here
-    double beta = 0.0;
-    if constexpr (CG) {
-        int32_t stop = cg_stop<kVfThreads>(cg.st, nullptr);
-        if (!stop && cg.iter > 0)
-            beta = cg_beta_step<kVfThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, false, stop,
-                                            nullptr, nullptr);
-        if (stop) return;
-    }
+    if (st && st->stop) return;
     const int act = A.state->active;
     if (act == 0) return;
     const int32_t n = A.state->nvf[act];
@@ -200,9 +179,9 @@ k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, CgDir<T
         vf_load(A, act, e, x, w, xp, xt);
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
-            up[c] = vf_dir<T, CG>(u, cg, beta, int64_t(w[0]) * 3 + c);
+            up[c] = u[int64_t(w[0]) * 3 + c];
 #pragma unroll
-            for (int i = 0; i < 3; ++i) ut[i][c] = vf_dir<T, CG>(u, cg, beta, int64_t(w[1 + i]) * 3 + c);
+            for (int i = 0; i < 3; ++i) ut[i][c] = u[int64_t(w[1 + i]) * 3 + c];
         }
 #pragma unroll
         for (int li = 0; li < 4; ++li) A.vf_ids[4 * int64_t(e) + li] = w[li];
@@ -257,26 +236,22 @@ hipError_t launch_vf_eval(const RowArgs<T> &a, const T *x, hipStream_t s)
 }
 
 template <typename T>
-hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, hipStream_t s,
-                         const CgDir<T> &cg)
+hipError_t launch_vf_hvp(const RowArgs<T> &a, const T *x, const T *u, const CgState *st,
+                         hipStream_t s)
 {
     if (!a.pat.vf[1] || !a.pat.vf[2] || !a.pat.faces || !a.vf_hvp || !a.vf_ids ||
         a.vf_stride <= 0)
         return hipErrorInvalidValue;
-    if (cg.r)
-        hipLaunchKernelGGL((k_vf_hvp<T, true>), dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0,
-                           s, a, x, u, cg);
-    else
-        hipLaunchKernelGGL((k_vf_hvp<T, false>), dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0,
-                           s, a, x, u, cg);
+    hipLaunchKernelGGL(k_vf_hvp<T>, dim3(vf_grid(a.vf_stride)), dim3(kVfThreads), 0, s, a, x, u,
+                       st);
     return hipGetLastError();
 }
 
 template hipError_t launch_vf_eval<float>(const RowArgs<float> &, const float *, hipStream_t);
 template hipError_t launch_vf_eval<double>(const RowArgs<double> &, const double *, hipStream_t);
 template hipError_t launch_vf_hvp<float>(const RowArgs<float> &, const float *, const float *,
-                                         hipStream_t, const CgDir<float> &);
+                                         const CgState *, hipStream_t);
 template hipError_t launch_vf_hvp<double>(const RowArgs<double> &, const double *, const double *,
-                                          hipStream_t, const CgDir<double> &);
+                                          const CgState *, hipStream_t);
 
 }  // namespace lad
