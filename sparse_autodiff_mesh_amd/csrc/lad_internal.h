@@ -192,6 +192,10 @@ hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y,
 // vertex terms (inertia): one lane per block row, 64 rows per chunk.
 constexpr int kRowThreads = 64;
 constexpr int kRowsPerChunk = kRowThreads;
+// Threads per workgroup of the row product kernels (HVP, Gauss-Newton),
+// which share nothing between lanes: four waves, since the per-CU cap on
+// workgroups holds single-wave groups to 4 waves per SIMD.
+constexpr int kHvpThreads = 256;
 
 template <typename T>
 struct RowArgs {

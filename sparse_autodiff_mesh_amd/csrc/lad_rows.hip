@@ -603,10 +603,13 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
 // Every row's topology terms (springs, faces, inertia); the runtime
 // contacts of the rows they touch are added afterwards by k_hvp_pair_rows.
 template <typename T, bool FACES, bool CG>
-__global__ void __launch_bounds__(kRowThreads)
+__global__ void __launch_bounds__(kHvpThreads)
 k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y,
            CgDir<T> cg)
 {
+    __shared__ double red[kHvpThreads / 64];
+    __shared__ double sum_bc;
+    __shared__ int32_t stop_bc;
     double beta = 0.0;
     // operand component i: v[i], or the next Newton-CG direction -r + beta d
     auto dir = [&](int64_t i) -> T {
@@ -617,7 +620,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     const int32_t *rpa = A.rp0;
     const int32_t *cia = A.ci0;
     // Nothing is staged here, so a workgroup takes a contiguous row range
-    // (ranges grouped by XCD) and walks it 64 rows at a time.  The row
+    // (ranges grouped by XCD) and walks it kHvpThreads rows at a time.  The row
     // header, position and direction of the next group are loaded while the
     // current group is processed, which takes one dependent load level off
     // every group.
@@ -643,10 +646,10 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         // Every workgroup takes the step that closes the previous update
         // (convergence or beta) from the partial sums of r.r, the same way;
         // none runs once the solve has ended.
-        int32_t stop = cg_stop<kRowThreads>(cg.st, nullptr);
+        int32_t stop = cg_stop<kHvpThreads>(cg.st, &stop_bc);
         if (!stop && cg.iter > 0)
-            beta = cg_beta_step<kRowThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, blockIdx.x == 0,
-                                             stop, nullptr, nullptr);
+            beta = cg_beta_step<kHvpThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, blockIdx.x == 0,
+                                             stop, red, &sum_bc);
         if (stop) return;  // workgroup-uniform
         if (an < r1)
 #pragma unroll
@@ -664,7 +667,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             va[k] = vn[k];
             if constexpr (CG) cg.d_new[int64_t(r.a) * 3 + k] = va[k];
         }
-        an += kRowThreads;
+        an += kHvpThreads;
         if (an < r1) {
             rn = load_row<T, false>(A, act, rpa, an, x);
 #pragma unroll
@@ -751,7 +754,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         }
     }
     if (A.hvp_dot) {
-        const double sum = block_sum<kRowThreads>(vy, nullptr);
+        const double sum = block_sum<kHvpThreads>(vy, red);
         if (threadIdx.x == 0) A.hvp_dot[blockIdx.x] = sum;
     }
 }
@@ -837,7 +840,7 @@ k_hvp_pair_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v,
 // the inertia rows contribute sqrt(c) (sqrt(c) v_a).  J is never stored.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(kRowThreads)
+__global__ void __launch_bounds__(kHvpThreads)
 k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__restrict__ v,
           T *__restrict__ y)
 {
@@ -845,7 +848,7 @@ k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
     const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
-    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kRowThreads) {
+    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kHvpThreads) {
         const Row<T> r = load_row<T, false>(A, 0, rpa, a, x);
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
@@ -889,7 +892,7 @@ template <typename T>
 hipError_t launch_gauss_newton_rows(const RowArgs<T> &a, T sqrt_k, T sqrt_c, const T *x,
                                     const T *v, T *y, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_gn_rows<T>, dim3(grid), dim3(kRowThreads), 0, s, a, sqrt_k, sqrt_c, x, v,
+    hipLaunchKernelGGL(k_gn_rows<T>, dim3(grid), dim3(kHvpThreads), 0, s, a, sqrt_k, sqrt_c, x, v,
                        y);
     return hipGetLastError();
 }
@@ -914,7 +917,7 @@ static hipError_t rows_occupancy(int lds, int *occ_e, int *occ_h)
                                                                 kRowThreads, lds);
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, false>,
-                                                         kRowThreads, 0);
+                                                         kHvpThreads, 0);
     return e;
 }
 
@@ -935,13 +938,15 @@ hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int pairs, int *grid
                       : rows_occupancy<T, false, false>(lds, &occ_e, &occ_h);
     }
     if (e != hipSuccess) return e;
-    auto clamp = [&](int occ) {
+    auto clamp = [&](int occ, int64_t units) {
         const int64_t full = int64_t(cus > 0 ? cus : 1) * (occ > 0 ? occ : 1);
-        const int64_t g = nchunk < full ? nchunk : full;
+        const int64_t g = units < full ? units : full;
         return int(g < 1 ? 1 : g);
     };
-    *grid_eval = clamp(occ_e);
-    *grid_hvp = clamp(occ_h);
+    *grid_eval = clamp(occ_e, nchunk);
+    // the product kernels walk rows kHvpThreads at a time; chunks hold at
+    // most kRowsPerChunk rows
+    *grid_hvp = clamp(occ_h, (int64_t(nchunk) * kRowsPerChunk + kHvpThreads - 1) / kHvpThreads);
     return hipSuccess;
 }
 
@@ -989,10 +994,10 @@ static void launch_hvp_rows_as(const RowArgs<T> &a, const T *x, const T *v, T *y
                                hipStream_t s, const CgDir<T> &cg)
 {
     if (cg.r)
-        hipLaunchKernelGGL((k_hvp_rows<T, F, true>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v,
+        hipLaunchKernelGGL((k_hvp_rows<T, F, true>), dim3(grid), dim3(kHvpThreads), 0, s, a, x, v,
                            y, cg);
     else
-        hipLaunchKernelGGL((k_hvp_rows<T, F, false>), dim3(grid), dim3(kRowThreads), 0, s, a, x, v,
+        hipLaunchKernelGGL((k_hvp_rows<T, F, false>), dim3(grid), dim3(kHvpThreads), 0, s, a, x, v,
                            y, cg);
 }
 

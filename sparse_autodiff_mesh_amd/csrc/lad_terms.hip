@@ -55,8 +55,8 @@ template <typename T, typename... Ts>
 void launch_hvp_fused(TermList<Ts...>, const TermsArgs<T> &a, const T *x, const T *v, T *y,
                       int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_terms_hvp<T, false, Ts...>), dim3(grid), dim3(kRowThreads), 0, s, a, x,
-                       v, y);
+    hipLaunchKernelGGL((k_terms_hvp<T, false, Ts...>), dim3(grid), dim3(kTermsHvpThreads), 0, s, a,
+                       x, v, y);
 }
 
 template <typename T, bool ACC, typename Term>
@@ -65,8 +65,8 @@ void launch_hvp_one(const TermsArgs<T> &a, int idx, const T *x, const T *v, T *y
 {
     TermsArgs<T> b = a;
     b.t[0] = a.t[idx];
-    hipLaunchKernelGGL((k_terms_hvp<T, ACC, Term>), dim3(grid), dim3(kRowThreads), 0, s, b, x, v,
-                       y);
+    hipLaunchKernelGGL((k_terms_hvp<T, ACC, Term>), dim3(grid), dim3(kTermsHvpThreads), 0, s, b, x,
+                       v, y);
 }
 
 template <typename T, typename... Ts, size_t... I>
@@ -83,7 +83,7 @@ hipError_t occupancy(TermList<Ts...>, int lds, int *occ_e, int *occ_h)
         occ_e, k_terms_eval<T, false, Ts...>, kRowThreads, lds);
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_terms_hvp<T, false, Ts...>,
-                                                         kRowThreads, 0);
+                                                         kTermsHvpThreads, 0);
     return e;
 }
 
@@ -143,7 +143,7 @@ hipError_t terms_grid(int set, int lds, int nchunk, int nv, int *grid_eval, int 
         return int(g < 1 ? 1 : g);
     };
     *grid_eval = clamp(occ_e, nchunk);
-    *grid_hvp = clamp(occ_h, (int64_t(nv) + kRowThreads - 1) / kRowThreads);
+    *grid_hvp = clamp(occ_h, (int64_t(nv) + kTermsHvpThreads - 1) / kTermsHvpThreads);
     return hipSuccess;
 }
 

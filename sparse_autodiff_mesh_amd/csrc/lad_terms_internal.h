@@ -14,6 +14,7 @@ namespace terms {
 
 constexpr int kMaxTerms = 4;   // term types of one set
 constexpr int kMaxVerts = 4;   // vertices per element (offsets pack into 24 bits)
+constexpr int kTermsHvpThreads = 256;  // threads per workgroup of the product kernel
 
 // Set ids (the values of LAD_TERMS_* in include/lad_terms.h).
 constexpr int kSetCloth = 1;

@@ -330,15 +330,18 @@ __device__ __forceinline__ void row_hvp_all(const TermsArgs<T> &A, int32_t a,
 }
 
 // y = H v over the term list; with ACC set the launch adds into y.  Each
-// workgroup walks a contiguous range of rows (ranges grouped by XCD).
+// workgroup walks a contiguous range of rows (ranges grouped by XCD).  The
+// kernel shares nothing between lanes, so its workgroups are four waves:
+// the per-CU cap on workgroups would otherwise hold single-wave groups to
+// 4 waves per SIMD, though its registers allow 8.
 template <typename T, bool ACC, typename... Terms>
-__global__ void __launch_bounds__(kRowThreads)
+__global__ void __launch_bounds__(kTermsHvpThreads)
 k_terms_hvp(TermsArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
 {
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
     const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
-    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kRowThreads) {
+    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kTermsHvpThreads) {
         T Y[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) Y[k] = ACC ? y[int64_t(a) * 3 + k] : T(0);
