@@ -15,7 +15,11 @@ Prints ONE JSON line.  Besides the contract fields it carries
                 launch (one read of the mesh data, one write of g and H) over
                 the kernel's mean duration from HIP events on its stream
                 (calls made without the energy, so each call is that one
-                launch; ms_per_step includes the energy sum);
+                launch; ms_per_step includes the energy sum), plus the
+                kernel's mean with a 512 MB write before every call (inputs
+                evicted from the last-level cache) and the rate of a plain
+                256 MiB device copy (read + write bytes per second), both
+                measured with the secondary workloads;
   cpu_baseline  the fp64 CPU oracle, single-threaded, on the same workload;
   secondary     the other workloads (face-energy grid eval and matrix-free
                 HVP, cloth plus contact-pair insertion, cloth plus
@@ -146,15 +150,23 @@ class Timer:
         ends = [t.cuda.Event(enable_timing=True) for _ in range(steps)]
         total0 = t.cuda.Event(enable_timing=True)
         total1 = t.cuda.Event(enable_timing=True)
+        # the K-step region: the calls back to back, events only at its ends
+        # (without a flush; with one, the region includes it)
         t.cuda.synchronize()
         total0.record()
+        for _ in range(steps):
+            if flush is not None:
+                flush()
+            fn()
+        total1.record()
+        t.cuda.synchronize()
+        # per-call durations, an event pair around each call
         for i in range(steps):
             if flush is not None:
                 flush()
             starts[i].record()
             fn()
             ends[i].record()
-        total1.record()
         t.cuda.synchronize()
         per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
         return {
@@ -209,6 +221,23 @@ def bench_headline(torch, binding, inputs, args, timer):
     r = timer.run(fn, args.steps, args.warmup, flush=flush)
     # the evaluation kernel alone (energy not requested: one launch per call)
     rk = timer.run(fn_kernel, args.steps, args.warmup, flush=flush)
+    # With the secondary workloads: the kernel again with a 512 MB write
+    # before every call, which evicts its inputs from the last-level cache
+    # (MALL), and a plain device copy, the achievable HBM rate of a read +
+    # write stream.  (Left out of the profiled headline-only runs, whose
+    # kernel statistics must match the warm timing above.)
+    rkf, copy_gbps = None, None
+    if not args.no_secondary:
+        if not args.flush_mall:
+            scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+            rkf = timer.run(fn_kernel, min(args.steps, 50), 2, flush=lambda: scratch.fill_(1.0))
+            del scratch
+        nb = 256 * 1024 * 1024
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        rc = timer.run(lambda: dst.copy_(src), 20, 3)
+        copy_gbps = 2 * nb / (rc["mean_ms"] * 1e-3) / 1e9
+        del src, dst
     nv, ns = m.nv, m.springs.shape[0]
     nnzb = info["nnzb_base"]
     terms = ns + nv
@@ -216,7 +245,8 @@ def bench_headline(torch, binding, inputs, args, timer):
     torch.cuda.synchronize()
     energy = E.item()
     res = {
-        "mesh": m, "info": info, "timing": r, "timing_kernel": rk, "terms": terms, "bytes": bc,
+        "mesh": m, "info": info, "timing": r, "timing_kernel": rk, "timing_flushed": rkf,
+        "copy_gbps": copy_gbps, "terms": terms, "bytes": bc,
         "energy": energy, "nnzb": nnzb, "ns": ns, "nv": nv,
     }
     L.close()
@@ -583,6 +613,9 @@ def main():
             "call_ms_mean_with_energy": round(t["mean_ms"], 5),
             "algorithmic_bytes": res["bytes"],
             "flush_mall": bool(args.flush_mall),
+            "kernel_ms_mean_mall_flushed": (round(res["timing_flushed"]["mean_ms"], 5)
+                                            if res["timing_flushed"] else None),
+            "copy_GBps_measured": (round(res["copy_gbps"], 1) if res["copy_gbps"] else None),
         },
         "springs_per_s_M": round(res["ns"] / (ms * 1e-3) / 1e6, 2),
         "energy": res["energy"],

@@ -488,20 +488,30 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
 #pragma unroll
         for (int c = 0; c < 3; ++c) G[c] += v[1 + c];
         const int32_t off[4] = {so.x, so.y, so.z, so.w};
+        // The four blocks are distinct (distinct columns), so every load is
+        // issued before any store; block li is the diagonal, kept in D.
+        T cur[4][9];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            T *Bm = Hs + 9 * (r.s0 + off[m] - sb);
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int k = 0; k < 9; ++k) cur[m][k] = Hs[9 * (r.s0 + off[m] - sb) + k];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int rr = 0; rr < 3; ++rr)
 #pragma unroll
                 for (int cc = 0; cc < 3; ++cc) {
                     // D is updated unconditionally (a select between D and
-                    // Bm would take D's address and move it to scratch)
+                    // a block would take D's address and move it to scratch)
                     const T h = v[kVfHessOff + 12 * rr + 3 * m + cc];
                     D[3 * rr + cc] += m == li ? h : T(0);
-                    if (m != li) Bm[3 * rr + cc] += h;
+                    cur[m][3 * rr + cc] += h;
                 }
-        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (m != li)
+#pragma unroll
+                for (int k = 0; k < 9; ++k) Hs[9 * (r.s0 + off[m] - sb) + k] = cur[m][k];
     };
     // entries past the prefetched pairs: further pairs, then contacts
     if (PAIRS && r.p1 - r.p0 > pp.n) {
