@@ -49,6 +49,15 @@ constexpr int term_batch()
     return K <= 2 ? 4 : 2;
 }
 
+// The same for the explicit evaluation, whose occupancy is set by its LDS
+// staging (about two waves per SIMD), not by its registers: wider batches
+// put more of a row's loads in flight at once (a cloth row's springs in one).
+template <int K>
+constexpr int term_batch_eval()
+{
+    return K <= 2 ? 8 : (K == 3 ? 4 : 2);
+}
+
 // LDS hand-off between the lanes of one wave: a wave's LDS operations run in
 // issue order, so only the compiler must be kept from moving memory
 // operations across this point (no workgroup barrier, which would also wait
@@ -153,7 +162,7 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
                                              T G[3], double &E)
 {
     constexpr int K = Term::kVerts, N = 3 * K, NC = Term::kConsts;
-    constexpr int kTermBatch = term_batch<K>();
+    constexpr int kTermBatch = term_batch_eval<K>();
     static_assert(K >= 1 && K <= kMaxVerts, "stencil of 1 to 4 vertices");
     const int32_t p0 = td.inc_ptr[a], p1 = td.inc_ptr[a + 1];
     for (int32_t base = p0; base < p1; base += kTermBatch) {
@@ -166,7 +175,8 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
 #pragma unroll
         for (int j = 0; j < kTermBatch; ++j) {
 #pragma unroll
-            for (int v = 0; v < K; ++v) vid[j][v] = td.elems[int64_t(rec[j].e) * K + v];
+            for (int v = 0; v < K; ++v)  // a one-vertex element's vertex is the row's
+                vid[j][v] = K == 1 ? a : td.elems[int64_t(rec[j].e) * K + v];
 #pragma unroll
             for (int q = 0; q < NC; ++q) cc[j][q] = td.consts[int64_t(rec[j].e) * NC + q];
         }
@@ -291,7 +301,8 @@ __device__ __forceinline__ void row_term_hvp(const TermData<T> &td, int32_t a,
 #pragma unroll
         for (int j = 0; j < kTermBatch; ++j) {
 #pragma unroll
-            for (int u = 0; u < K; ++u) vid[j][u] = td.elems[int64_t(rec[j].e) * K + u];
+            for (int u = 0; u < K; ++u)  // a one-vertex element's vertex is the row's
+                vid[j][u] = K == 1 ? a : td.elems[int64_t(rec[j].e) * K + u];
 #pragma unroll
             for (int q = 0; q < NC; ++q) cc[j][q] = td.consts[int64_t(rec[j].e) * NC + q];
         }
