@@ -253,6 +253,23 @@ def bench_headline(torch, binding, inputs, args, timer):
     return res
 
 
+def bench_hvp_only(torch, binding, inputs, args, timer):
+    """The matrix-free HVP of the cloth alone (for counter runs): one line of
+    JSON with its event timing and compulsory bytes."""
+    m = inputs.cloth(args.n)
+    L = cloth_ctx(binding, m, "f32")
+    x = to_dev(torch, m.x, "f32")
+    v = to_dev(torch, inputs.hvp_direction(m.nv), "f32")
+    y = torch.empty_like(v)
+    r = timer.run(lambda: L.hvp(x, v, out=y), args.steps, args.warmup)
+    bc = compulsory_bytes_hvp(m.nv, m.springs.shape[0], 0, 4)
+    L.close()
+    return {"workload": f"matrix-free HVP, mass-spring cloth {args.n}x{args.n}, fp32",
+            "kernel": "k_hvp_rows<float, false, false>", "steps": args.steps,
+            "warmup": args.warmup, "ms_mean": round(r["mean_ms"], 5),
+            "algorithmic_bytes": bc, "GBps": round(bc / (r["mean_ms"] * 1e-3) / 1e9, 1)}
+
+
 def bench_secondary(torch, binding, inputs, args, timer):
     import numpy as np
     sec = {}
@@ -538,6 +555,8 @@ def main():
                     help="patch path: colour phases instead of LDS atomics")
     ap.add_argument("--patch-lds", type=int, default=0,
                     help="LDS bytes per patch (0 = library default)")
+    ap.add_argument("--hvp-only", action="store_true",
+                    help="only time the cloth HVP (prints its own JSON line; for counter runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device-to-device copy of 256 MiB five times "
                          "(reference kernel for the HBM byte counters)")
@@ -567,6 +586,9 @@ def main():
     binding.lib()  # fails loudly if liblad.so is missing
 
     timer = Timer(torch)
+    if args.hvp_only:
+        print(json.dumps(bench_hvp_only(torch, binding, inputs, args, timer)))
+        return 0
     log(f"bench: cloth {args.n}x{args.n} fp32, steps={args.steps} warmup={args.warmup}")
     res = bench_headline(torch, binding, inputs, args, timer)
     t = res["timing"]
