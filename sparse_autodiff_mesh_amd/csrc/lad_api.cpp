@@ -695,6 +695,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             ctx->pat.pinc[b] = ctx->ins.pinc[b];
             ctx->pat.pinc_row[b] = ctx->ins.pinc_row[b];
             ctx->pat.trow[b] = ctx->ins.trow[b];
+            ctx->pat.pnew[b] = ctx->ins.pnew[b];
             ctx->pat.vf[b] = ctx->ins.vf[b];
         }
         ctx->ins.faces = ctx->d_faces;

@@ -148,6 +148,9 @@ struct PatternBufs {
     const int32_t *pinc_row[3];
     const int32_t *trow[3];      // per incidence entry: its row if the entry is
                                  // the row's first, else -1 (touched rows)
+    const int32_t *pnew[3];      // per touched row, at 3 x its first incidence
+                                 // entry: its columns that the topology row
+                                 // lacks, ascending
     const int32_t *vf[3];        // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)
 };
@@ -329,7 +332,9 @@ struct InsertBufs {
     int32_t *pinc_ptr[3];
     int32_t *pinc[3];
     int32_t *pinc_row[3];
-    int32_t *pnew[3];            // distinct new partners per row (scratch)
+    int32_t *pnew[3];            // distinct new partners per row, kept until the
+                                 // buffer is next written (the row kernels
+                                 // read those of the active buffer)
     int32_t *trow[3];            // touched-row list, see PatternBufs::trow
     int32_t *vf[3];              // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)

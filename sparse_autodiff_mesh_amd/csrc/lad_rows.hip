@@ -78,6 +78,7 @@ struct Row {
     int32_t kb0, kb1;         // topology slot range
     int32_t f0, f1;           // incident-face range (when the face term is on)
     int32_t p0, p1;           // pair-incidence range (when pairs are active)
+    int32_t nn;               // columns the active row has beyond its topology row
     T xa[3];
     T xt[3];                  // inertial target (when the inertia term is on)
 };
@@ -99,6 +100,7 @@ __device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, int act, const i
     r.kb1 = A.rp0[a + 1];
     r.f0 = A.faces_on ? A.fptr[a] : 0;
     r.f1 = A.faces_on ? A.fptr[a + 1] : 0;
+    r.nn = act != 0 ? (r.s1 - r.s0) - (r.kb1 - r.kb0) : 0;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         r.xa[k] = x[int64_t(a) * 3 + k];
@@ -333,16 +335,154 @@ __device__ __forceinline__ void face_block(const Dual2<T, 6> &e, const T wa[2], 
 // ---------------------------------------------------------------------------
 // Energy, gradient and Hessian rows.
 // ---------------------------------------------------------------------------
-template <typename T, bool FACES, bool PAIRS>
+
+// A touched row whose active row has at most kMaxIns columns beyond its
+// topology row has its topology terms evaluated by the main kernel, each
+// block moved to its active slot; its contact terms are added afterwards.
+constexpr int kMaxIns = 4;
+
+// Inserted columns of a touched row (ascending; INT32_MAX past the count).
+template <typename T>
+__device__ __forceinline__ void load_inserted(const RowArgs<T> &A, int act, const Row<T> &r,
+                                              int32_t ins[kMaxIns])
+{
+#pragma unroll
+    for (int m = 0; m < kMaxIns; ++m)
+        ins[m] = (act != 0 && m < r.nn) ? A.pat.pnew[act][3 * int64_t(r.p0) + m] : INT32_MAX;
+}
+
+// Inserted columns before column b: topology slot kb0 + i of the row sits at
+// active slot s0 + i + shift_of(ins, its column).
+__device__ __forceinline__ int32_t shift_of(const int32_t ins[kMaxIns], int32_t b)
+{
+    int32_t n = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxIns; ++m) n += ins[m] < b ? 1 : 0;
+    return n;
+}
+
+// Slot of column b in the sorted active row [s0, s1) (b is present): the
+// row's columns are compared 16 at a time, all loads of a window issued
+// together.
+__device__ __forceinline__ int32_t slot_of(const int32_t *__restrict__ ci, int32_t s0,
+                                           int32_t s1, int32_t b)
+{
+    constexpr int W = 16;
+    for (int32_t base = s0; base < s1; base += W) {
+        int32_t c[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) c[k] = base + k < s1 ? ci[base + k] : -1;
+        int32_t f = -1;
+#pragma unroll
+        for (int k = 0; k < W; ++k) f = c[k] == b ? base + k : f;
+        if (f >= 0) return f;
+    }
+    return s0;
+}
+
+// Runtime pair (a, b) seen from row a: -K into block `slot` (a
+// read-modify-write), +K into the diagonal D, the gradient into G; the
+// energy counted by the pair's first vertex.
+template <typename T>
+__device__ __forceinline__ void pair_add(const RowArgs<T> &A, const Row<T> &r, const T xb[3],
+                                         T *B, bool first, T D[9], T G[3], double &E)
+{
+    T dz[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) dz[c] = r.xa[c] - xb[c];
+    const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
+    if (!(l2 < A.dhat * A.dhat)) return;  // outside the barrier's support
+    Dual2<T, 3> d[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(dz[c], c);
+    const Dual2<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
+    if (first) E += double(e.v);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        G[i] += e.g[i];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const T h = e.hess(i, j);
+            B[3 * i + j] -= h;
+            D[3 * i + j] += h;
+        }
+    }
+}
+
+// Vertex-face contact e of the active buffer seen from row a: k_vf_eval
+// stored, for each of its four vertices, that row's strip (energy in the
+// contact vertex's strip only, the gradient part, 3 Hessian rows over the
+// contact's 12 variables) and the four blocks' offsets in that row.  The
+// row's own block goes to D; the other three are added into the staged row
+// Hrow (block offsets from the row's first slot).
+template <typename T>
+__device__ __forceinline__ void vf_add(const RowArgs<T> &A, int32_t a, int32_t e, T *Hrow, T D[9],
+                                       T G[3], double &E)
+{
+    const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
+    const int li = w.x == a ? 0 : (w.y == a ? 1 : (w.z == a ? 2 : 3));
+    const int64_t strip = 4 * int64_t(e) + li;
+    const int4 so = *reinterpret_cast<const int4 *>(A.vf_slots + strip * 4);
+    const T *L = A.vf_eval + strip * kVfStrip;
+    T v[kVfStrip];
+#pragma unroll
+    for (int k = 0; k < kVfStrip; ++k) v[k] = L[k];
+    E += double(v[0]);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) G[c] += v[1 + c];
+    const int32_t off[4] = {so.x, so.y, so.z, so.w};
+    // The four blocks are distinct (distinct columns), so every load is
+    // issued before any store; block li is the diagonal, kept in D.
+    T cur[4][9];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int k = 0; k < 9; ++k) cur[m][k] = Hrow[9 * off[m] + k];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 3; ++rr)
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc) {
+                // D is updated unconditionally (a select between D and a
+                // block would take D's address and move it to scratch)
+                const T h = v[kVfHessOff + 12 * rr + 3 * m + cc];
+                D[3 * rr + cc] += m == li ? h : T(0);
+                cur[m][3 * rr + cc] += h;
+            }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        if (m != li)
+#pragma unroll
+            for (int k = 0; k < 9; ++k) Hrow[9 * off[m] + k] = cur[m][k];
+}
+
+// One row: energy part, gradient and every block, written into Hs (block
+// s - sb holds active slot s).  PAIRS: the full evaluation of a touched row
+// (column matching, pair and contact terms).  SHIFT (the main kernel of a
+// context with contact capacity): the topology terms of an untouched row,
+// or of a touched row with at most kMaxIns inserted columns, each block
+// placed at its active slot; k_eval_pair_rows then zeroes the inserted
+// blocks and adds the row's contact terms.
+template <typename T, bool FACES, bool PAIRS, bool SHIFT = false>
 __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const int32_t *cia,
                                            const Row<T> &r, int32_t sb,
                                            T *Hs, const T *__restrict__ x, T *__restrict__ g)
 {
+    static_assert(!(PAIRS && SHIFT), "one mode per row");
     T D[9], G[3] = {T(0), T(0), T(0)};
 #pragma unroll
     for (int i = 0; i < 9; ++i) D[i] = T(0);
     double E = 0.0;
     int32_t dslot = r.s0;
+
+    int32_t ins[kMaxIns];
+    Row<T> rt = r;  // the row as the slot loop walks it
+    if constexpr (SHIFT) {
+        load_inserted(A, A.state->active, r, ins);
+        rt.s1 = r.s0 + (r.kb1 - r.kb0);  // topology slots, in order
+        rt.p0 = rt.p1 = 0;
+    }
 
     // pairs of the active buffer (element ids below npa are pairs); rows
     // that no contact touches are evaluated with PAIRS = false, which
@@ -351,13 +491,14 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     PairPre<T> pp;
     prefetch_pairs(A, PAIRS ? act : 0, npa, r, x, pp);
     int32_t jb = r.kb0;
-    for (int32_t base = r.s0; base < r.s1; base += kBatch) {
+    for (int32_t base = rt.s0; base < rt.s1; base += kBatch) {
         SlotBatch<T> q;
-        load_batch(A, r, act, cia, base, jb, x, q);
+        load_batch(A, rt, act, cia, base, jb, x, q);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int32_t s = base + j;
-            if (s >= r.s1) break;
+            int32_t s = base + j;
+            if (s >= rt.s1) break;
+            if constexpr (SHIFT) s += shift_of(ins, q.b[j]);
 #pragma unroll
             for (int k = 0; k < kRowPairs; ++k) pp.slot[k] = q.b[j] == pp.b[k] ? s : pp.slot[k];
             T *B = Hs + 9 * (s - sb);
@@ -414,12 +555,15 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
 #pragma unroll
                     for (int k = 0; k < 9; ++k) D[k] += Bu[k];
                 } else {
-                    // block of face vertex u in this row: its topology slot,
-                    // or (a row that a pair touches) its column's position in the active row
+                    // block of face vertex u in this row: its topology slot
+                    // (moved past the inserted columns before it), or (a
+                    // touched row evaluated in full) its column's position
+                    // in the active row
                     const int32_t vu = u == (i + 1) % 3 ? fe.o1 : fe.o2;
                     const int32_t off = int32_t((fe.pk >> (8 * u + 8)) & 255u);
-                    const int32_t sl = (act == 0 || r.p1 == r.p0) ? r.s0 + off
-                                                                  : find_slot(cia, r.s0, r.s1, vu);
+                    int32_t sl = (act == 0 || r.p1 == r.p0) ? r.s0 + off
+                                                            : find_slot(cia, r.s0, r.s1, vu);
+                    if constexpr (SHIFT) sl += shift_of(ins, vu);
                     T *B = Hs + 9 * (sl - sb);
 #pragma unroll
                     for (int k = 0; k < 9; ++k) B[k] += Bu[k];
@@ -445,90 +589,28 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
 
     // runtime pairs of this row, in pair order: -K into the (a, b) block,
     // +K into the diagonal
-    auto pair_term = [&](const T xb[3], int32_t slot, bool first) {
-        T dz[3];
+    if constexpr (PAIRS) {
 #pragma unroll
-        for (int c = 0; c < 3; ++c) dz[c] = r.xa[c] - xb[c];
-        const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
-        if (!(l2 < A.dhat * A.dhat)) return;  // outside the barrier's support
-        Dual2<T, 3> d[3];
-#pragma unroll
-        for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(dz[c], c);
-        const Dual2<T, 3> e = barrier_energy(d, A.kappa, A.dhat);
-        if (first) E += double(e.v);
-        T *B = Hs + 9 * (slot - sb);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            G[i] += e.g[i];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const T h = e.hess(i, j);
-                B[3 * i + j] -= h;
-                D[3 * i + j] += h;
-            }
-        }
-    };
-#pragma unroll
-    for (int k = 0; k < kRowPairs; ++k)
-        if (k < pp.n) pair_term(pp.xb[k], pp.slot[k], pp.first[k] != 0);
-    // vertex-face contact e of the active buffer: k_vf_eval stored, for each
-    // of its four vertices, that row's strip (energy in the contact vertex's
-    // strip only, the gradient part, 3 Hessian rows over the contact's 12
-    // variables) and the four blocks' offsets in that row
-    auto vf_term = [&](int32_t e) {
-        const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
-        const int li = w.x == r.a ? 0 : (w.y == r.a ? 1 : (w.z == r.a ? 2 : 3));
-        const int64_t strip = 4 * int64_t(e) + li;
-        const int4 so = *reinterpret_cast<const int4 *>(A.vf_slots + strip * 4);
-        const T *L = A.vf_eval + strip * kVfStrip;
-        T v[kVfStrip];
-#pragma unroll
-        for (int k = 0; k < kVfStrip; ++k) v[k] = L[k];
-        E += double(v[0]);
-#pragma unroll
-        for (int c = 0; c < 3; ++c) G[c] += v[1 + c];
-        const int32_t off[4] = {so.x, so.y, so.z, so.w};
-        // The four blocks are distinct (distinct columns), so every load is
-        // issued before any store; block li is the diagonal, kept in D.
-        T cur[4][9];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int k = 0; k < 9; ++k) cur[m][k] = Hs[9 * (r.s0 + off[m] - sb) + k];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int rr = 0; rr < 3; ++rr)
-#pragma unroll
-                for (int cc = 0; cc < 3; ++cc) {
-                    // D is updated unconditionally (a select between D and
-                    // a block would take D's address and move it to scratch)
-                    const T h = v[kVfHessOff + 12 * rr + 3 * m + cc];
-                    D[3 * rr + cc] += m == li ? h : T(0);
-                    cur[m][3 * rr + cc] += h;
+        for (int k = 0; k < kRowPairs; ++k)
+            if (k < pp.n) pair_add(A, r, pp.xb[k], Hs + 9 * (pp.slot[k] - sb), pp.first[k] != 0, D, G, E);
+        // entries past the prefetched pairs: further pairs, then contacts
+        if (r.p1 - r.p0 > pp.n) {
+            const int32_t *pl = A.pat.pinc[act];
+            const int32_t *prs = A.pat.pairs[act];
+            for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
+                const int32_t q = pl[k];
+                if (q >= npa) {
+                    vf_add(A, r.a, q - npa, Hs + 9 * (r.s0 - sb), D, G, E);
+                    continue;
                 }
+                const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
+                const int32_t b = i0 == r.a ? i1 : i0;
+                T xb[3];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            if (m != li)
-#pragma unroll
-                for (int k = 0; k < 9; ++k) Hs[9 * (r.s0 + off[m] - sb) + k] = cur[m][k];
-    };
-    // entries past the prefetched pairs: further pairs, then contacts
-    if (PAIRS && r.p1 - r.p0 > pp.n) {
-        const int32_t *pl = A.pat.pinc[act];
-        const int32_t *prs = A.pat.pairs[act];
-        for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
-            const int32_t q = pl[k];
-            if (q >= npa) {
-                vf_term(q - npa);
-                continue;
+                for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
+                pair_add(A, r, xb, Hs + 9 * (find_slot(cia, r.s0, r.s1, b) - sb), i0 == r.a, D, G,
+                         E);
             }
-            const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
-            const int32_t b = i0 == r.a ? i1 : i0;
-            T xb[3];
-#pragma unroll
-            for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
-            pair_term(xb, find_slot(cia, r.s0, r.s1, b), i0 == r.a);
         }
     }
 
@@ -537,6 +619,67 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
     for (int i = 0; i < 9; ++i) B[i] = D[i];
 #pragma unroll
     for (int c = 0; c < 3; ++c) g[int64_t(r.a) * 3 + c] = G[c];
+    return E;
+}
+
+// The contact terms of a touched row whose topology terms the main kernel
+// evaluated (SHIFT mode): pairs and vertex-face contacts in element order,
+// added into the row's blocks, its diagonal block and its gradient in HBM.
+template <typename T>
+__device__ __forceinline__ double eval_row_contacts(const RowArgs<T> &A, int act, const Row<T> &r,
+                                                    const T *__restrict__ x, T *__restrict__ hv,
+                                                    T *__restrict__ g)
+{
+    const int32_t npa = A.state->np[act];
+    const int32_t *pl = A.pat.pinc[act];
+    const int32_t *prs = A.pat.pairs[act];
+    const int32_t *cia = A.pat.ci[act];
+    T D[9], G[3] = {T(0), T(0), T(0)};
+#pragma unroll
+    for (int i = 0; i < 9; ++i) D[i] = T(0);
+    double E = 0.0;
+    // slots of the diagonal and of the inserted columns, from one pass over
+    // the row's columns; the main kernel left the inserted blocks unwritten
+    int32_t tgt[1 + kMaxIns], pos[1 + kMaxIns];
+    load_inserted(A, act, r, tgt + 1);
+    tgt[0] = r.a;
+#pragma unroll
+    for (int t = 0; t <= kMaxIns; ++t) pos[t] = r.s0;
+    constexpr int W = 16;
+    for (int32_t base = r.s0; base < r.s1; base += W) {
+        int32_t c[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) c[k] = base + k < r.s1 ? cia[base + k] : -1;
+#pragma unroll
+        for (int k = 0; k < W; ++k)
+#pragma unroll
+            for (int t = 0; t <= kMaxIns; ++t) pos[t] = c[k] == tgt[t] ? base + k : pos[t];
+    }
+    const int32_t dslot = pos[0];
+#pragma unroll
+    for (int m = 0; m < kMaxIns; ++m)
+        if (m < r.nn)
+#pragma unroll
+            for (int i = 0; i < 9; ++i) hv[9 * int64_t(pos[1 + m]) + i] = T(0);
+    T *Hrow = hv + 9 * int64_t(r.s0);
+    for (int32_t k = r.p0; k < r.p1; ++k) {
+        const int32_t q = pl[k];
+        if (q >= npa) {
+            vf_add(A, r.a, q - npa, Hrow, D, G, E);
+            continue;
+        }
+        const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
+        const int32_t b = i0 == r.a ? i1 : i0;
+        T xb[3];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
+        pair_add(A, r, xb, hv + 9 * int64_t(slot_of(cia, r.s0, r.s1, b)), i0 == r.a, D, G, E);
+    }
+    T *B = hv + 9 * int64_t(dslot);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) B[i] += D[i];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g[int64_t(r.a) * 3 + c] += G[c];
     return E;
 }
 
@@ -565,12 +708,15 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         T *Hs = stage + pad;
         if (fits && int(threadIdx.x) < nrows) {
             const Row<T> r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
-            // A row that pairs touch is left to k_eval_pair_rows (its slice
-            // of the staging area is streamed out unwritten and overwritten
-            // there); every other row has its topology columns, so it is
-            // evaluated with act = 0, which compiles the pair code out.
-            if (!PAIRS || r.p1 == r.p0)
-                eacc += eval_row<T, FACES, false>(A, 0, cia, r, sb, Hs, x, g);
+            // Every row's topology terms, through the topology pattern
+            // (act = 0, no pair code); with contact capacity each block is
+            // moved to its active slot and the contact terms of touched rows
+            // follow in k_eval_pair_rows.  A row with more than kMaxIns
+            // inserted columns is left to that kernel whole (its slice of
+            // the staging area is streamed out unwritten and overwritten
+            // there).
+            if (!PAIRS || r.nn <= kMaxIns)
+                eacc += eval_row<T, FACES, false, PAIRS>(A, 0, cia, r, sb, Hs, x, g);
         }
         wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
@@ -579,14 +725,18 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
     store_energy(esink, block_sum<kRowThreads>(eacc, nullptr));
 }
 
-// Rows that current pairs touch: one thread per row (the thread of the row's
-// first pair-incidence entry, a fixed choice, so the energy sums keep their
-// order), which runs the full row evaluation -- column matching, pair terms
-// -- and writes the row's blocks and gradient straight to HBM.  It runs
-// after k_eval_rows on the same stream.  Only a few percent of the rows are
-// touched, but nearly every 64-row wave holds one, so handling them apart
-// keeps the divergent pair code out of the main kernel.  Every workgroup
-// stores a partial energy (zero when the topology pattern is active).
+// Rows that current contacts touch: one thread per row (the thread of the
+// row's first incidence entry, a fixed choice, so the energy sums keep their
+// order).  It runs after k_eval_rows on the same stream, which evaluated the
+// topology terms of every row with at most kMaxIns inserted columns; for
+// those the thread adds the row's contact terms (pairs, vertex-face
+// contacts) into its blocks, diagonal and gradient in HBM.  A row with more
+// inserted columns gets the full row evaluation here -- column matching,
+// topology and contact terms -- written straight to HBM.  Only a few
+// percent of the rows are touched, but nearly every 64-row wave holds one,
+// so handling them apart keeps the divergent contact code out of the main
+// kernel.  Every workgroup stores a partial energy (zero when the topology
+// pattern is active).
 template <typename T, bool FACES>
 __global__ void __launch_bounds__(kThreads)
 k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
@@ -600,7 +750,10 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
         const int32_t a = A.pat.trow[act][k];
         if (a >= 0) {
             const Row<T> r = load_row(A, act, A.pat.rp[act], a, x);
-            e = eval_row<T, FACES, true>(A, act, A.pat.ci[act], r, 0, hv, x, g);
+            if (r.nn <= kMaxIns)
+                e = eval_row_contacts(A, act, r, x, hv, g);
+            else
+                e = eval_row<T, FACES, true>(A, act, A.pat.ci[act], r, 0, hv, x, g);
         }
     }
     store_energy(esink, block_sum<kThreads>(e, red));
@@ -972,10 +1125,11 @@ template <typename T>
 hipError_t launch_eval_pair_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                                  int grid, hipStream_t s)
 {
-    for (int k = 1; k <= 2; ++k)  // the pair buffers the kernel may read
+    for (int k = 1; k <= 2; ++k)  // the contact buffers the kernel may read
         if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pairs[k] || !a.pat.pinc_ptr[k] ||
             !a.pat.pinc[k] || !a.pat.trow[k])
             return hipErrorInvalidValue;
+    if (a.vf_stride > 0 && (!a.vf_eval || !a.vf_ids || !a.vf_slots)) return hipErrorInvalidValue;
     if (a.faces_on)
         hipLaunchKernelGGL((k_eval_pair_rows<T, true>), dim3(grid), dim3(kThreads), 0, s, a, x, g,
                            hv, es);
@@ -990,6 +1144,10 @@ hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, Energy
                             int grid, hipStream_t s)
 {
     const int lds = rows_lds_bytes<T>(a.lds_blocks);
+    if (a.pairs_on)  // the buffers the contact-capacity variant reads
+        for (int k = 1; k <= 2; ++k)
+            if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pinc_ptr[k] || !a.pat.pnew[k])
+                return hipErrorInvalidValue;
     if (a.faces_on)
         a.pairs_on ? launch_eval_rows_as<T, true, true>(a, x, g, hv, es, grid, lds, s)
                    : launch_eval_rows_as<T, true, false>(a, x, g, hv, es, grid, lds, s);
