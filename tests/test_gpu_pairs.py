@@ -88,6 +88,43 @@ def test_duplicate_adjacent_and_shared_pairs(lad, path):
     L.close()
 
 
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_rows_with_many_inserted_columns(lad, dtype):
+    """Row path: hubs paired with 6, 5, 4 and 1 vertices that are not their
+    neighbours, so their active rows gain that many columns (the main kernel
+    places the topology blocks of rows with up to 4 inserted columns, the
+    touched-row kernel evaluates the longer ones in full), plus a repeated
+    pair; E, g, H and H v against the oracle."""
+    import torch
+    log_case(test="pairs_many_inserted", dtype=dtype)
+    m = inputs.cloth(20)
+    n = m.n
+    L, dhat = make(lad, m, dtype, 32, path="rows")
+    hubs = {5 * n + 5: [5 * n + 8, 5 * n + 11, 5 * n + 14, 8 * n + 5, 8 * n + 8, 8 * n + 11],
+            12 * n + 4: [12 * n + 7, 12 * n + 10, 15 * n + 4, 15 * n + 7, 15 * n + 10],
+            3 * n + 16: [6 * n + 16, 6 * n + 13, 9 * n + 16, 0 * n + 13],
+            17 * n + 17: [14 * n + 14]}
+    rng = np.random.default_rng(11)
+    x = m.x.copy()
+    pairs = []
+    for a, bs in hubs.items():
+        for b in bs:
+            pairs.append((a, b))
+            x[b] = x[a] + 0.4 * dhat * rng.normal(size=3) / np.sqrt(3)
+    pairs.append((3 * n + 16, 9 * n + 16))  # repeated: evaluated twice, one block
+    pairs = np.array(pairs, dtype=np.int32)
+    L.insert_pairs(pairs_dev(pairs))
+    assert L.device_status() == 0
+    prob, orp, oci, x_h = check_step(lad, L, m, dtype, pairs, x, dhat)
+    assert np.diff(orp)[5 * n + 5] - 7 == 6  # the hub's row: 7 topology blocks + 6
+    _, _, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    v_h = host_input(inputs.hvp_direction(m.nv), dtype)
+    y = L.hvp(dev(x_h, dtype), dev(v_h, dtype))
+    torch.cuda.synchronize()
+    assert rel(y.cpu().numpy(), oracle.bsr_spmv(orp, oci, Ho, v_h)) <= TOL[dtype]
+    L.close()
+
+
 @pytest.mark.parametrize("path", ["patch", "rows"])
 def test_pairs_with_faces_and_hvp(lad, path):
     """Faces plus pairs.  The barrier support is widened to 3h and each pair
