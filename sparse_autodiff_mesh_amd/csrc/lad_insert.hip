@@ -40,6 +40,11 @@ namespace {
 
 __device__ __forceinline__ int back_of(const DevState *st) { return st->active == 1 ? 2 : 1; }
 
+// Rows whose topology row has at most kRegCols columns (and at most kRegNew
+// new ones) are handled with their columns in registers.
+constexpr int kRegCols = 16;
+constexpr int kRegNew = 8;
+
 // The vertices of element q of the back buffer (2 for a pair, 4 for a
 // contact: the vertex, then its face's three); 0 if the element fails the
 // device-side check (an index out of range, a pair with i == j, a contact
@@ -156,6 +161,12 @@ k_ins_rows(const DevState *st, int32_t nent, int32_t np, int32_t nv, InsertBufs 
     const int32_t *prs = b.pairs[bk];
     int32_t *pn = b.pnew[bk] + 3 * int64_t(p0);
     int32_t nn = 0;
+    // the topology row in registers when it is short (membership tests
+    // then take no dependent loads), else binary search
+    const bool reg = rb1 - rb0 <= kRegCols;
+    int32_t topo[kRegCols];
+#pragma unroll
+    for (int i = 0; i < kRegCols; ++i) topo[i] = (reg && rb0 + i < rb1) ? b.ci[0][rb0 + i] : -1;
     for (int32_t q0 = p0; q0 < p1; ++q0) {
         const int32_t q = pl[q0];
         // this row's partners in element q: a pair's other vertex; for a
@@ -174,8 +185,15 @@ k_ins_rows(const DevState *st, int32_t nent, int32_t np, int32_t nv, InsertBufs 
         }
         for (int t = 0; t < npart; ++t) {
             const int32_t other = part[t];
-            const int32_t pos = lower_bound(b.ci[0], rb0, rb1, other);
-            if (pos < rb1 && b.ci[0][pos] == other) continue;
+            bool in_topo = false;
+            if (reg) {
+#pragma unroll
+                for (int i = 0; i < kRegCols; ++i) in_topo |= topo[i] == other;
+            } else {
+                const int32_t pos = lower_bound(b.ci[0], rb0, rb1, other);
+                in_topo = pos < rb1 && b.ci[0][pos] == other;
+            }
+            if (in_topo) continue;
             bool dup = false;
             for (int32_t m = 0; m < nn; ++m) dup |= pn[m] == other;
             if (!dup) pn[nn++] = other;
@@ -211,6 +229,10 @@ __device__ __forceinline__ void merge_row(const int32_t *cb, int32_t len, const 
 // with the row's new partners.  Each such row also checks the staging
 // capacity of the chunk that holds it (the only chunks whose size changed),
 // and re-zeroes its new-block count.
+// Rows of at most kRegCols topology columns and kRegNew new ones are merged
+// in registers: both lists are loaded at once and each column goes to its
+// index in its own list plus the number of smaller columns in the other
+// (the lists are sorted and disjoint).  Longer rows take the loop.
 __global__ void __launch_bounds__(kThreads)
 k_ins_merge_rows(DevState *st, int32_t nent, InsertBufs b, const PatchHdr *__restrict__ hdr)
 {
@@ -219,11 +241,36 @@ k_ins_merge_rows(DevState *st, int32_t nent, InsertBufs b, const PatchHdr *__res
     const int bk = back_of(st);
     const int32_t a = b.trow[bk][k];
     if (a < 0) return;
+    const PatchHdr h = hdr[b.row_chunk[a]];
     const int32_t rb0 = b.rp[0][a], len = b.rp[0][a + 1] - rb0;
     const int32_t o0 = b.rp[bk][a], nn = (b.rp[bk][a + 1] - o0) - len;
-    merge_row(b.ci[0] + rb0, len, b.pnew[bk] + 3 * int64_t(k), nn, b.ci[bk] + o0);
+    const int32_t *cb = b.ci[0] + rb0;
+    const int32_t *pn = b.pnew[bk] + 3 * int64_t(k);
+    int32_t *out = b.ci[bk] + o0;
+    if (len <= kRegCols && nn <= kRegNew) {
+        int32_t c[kRegCols], p[kRegNew];
+#pragma unroll
+        for (int i = 0; i < kRegCols; ++i) c[i] = i < len ? cb[i] : INT32_MAX;
+#pragma unroll
+        for (int m = 0; m < kRegNew; ++m) p[m] = m < nn ? pn[m] : INT32_MAX;
+#pragma unroll
+        for (int i = 0; i < kRegCols; ++i) {
+            int32_t before = 0;
+#pragma unroll
+            for (int m = 0; m < kRegNew; ++m) before += p[m] < c[i] ? 1 : 0;
+            if (i < len) out[i + before] = c[i];
+        }
+#pragma unroll
+        for (int m = 0; m < kRegNew; ++m) {
+            int32_t before = 0;
+#pragma unroll
+            for (int i = 0; i < kRegCols; ++i) before += c[i] < p[m] ? 1 : 0;
+            if (m < nn) out[m + before] = p[m];
+        }
+    } else {
+        merge_row(cb, len, pn, nn, out);
+    }
     if (nn > 0) b.nnew[a] = 0;
-    const PatchHdr h = hdr[b.row_chunk[a]];
     if (b.rp[bk][h.v0 + h.nown] - b.rp[bk][h.v0] > h.amap_cap) atomicOr(&st->err_cur, 2);
 }
 
