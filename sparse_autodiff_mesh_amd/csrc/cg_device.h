@@ -1,8 +1,8 @@
 // cg_device.h -- the scalar steps of the Newton-CG iteration as device
 // functions, computed redundantly by every workgroup of the kernel that
 // needs them (no single-workgroup launch between the vector kernels, no
-// device-wide fence).  Included by the solver, the row HVP and the contact
-// HVP, which form the direction themselves.  Not part of the public ABI.
+// device-wide fence).  Included by the solver and the row HVP, which forms
+// the direction itself.  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
