@@ -270,6 +270,30 @@ def bench_hvp_only(torch, binding, inputs, args, timer):
             "algorithmic_bytes": bc, "GBps": round(bc / (r["mean_ms"] * 1e-3) / 1e9, 1)}
 
 
+def bench_terms_cloth_only(torch, inputs, args, timer):
+    """The term front end's generic cloth set alone (for counter runs): its
+    fused explicit evaluation, then its product, with their event timings."""
+    from sparse_autodiff_mesh_amd import terms
+    m = inputs.cloth(args.n)
+    blocks = terms.mesh_blocks(m, "cloth")
+    T = terms.Terms(m.nv, "cloth", blocks, dtype="f32")
+    x = to_dev(torch, m.x, "f32")
+    v = to_dev(torch, inputs.hvp_direction(m.nv), "f32")
+    y = torch.empty_like(v)
+    out = T.alloc_outputs()
+    re = timer.run(lambda: T.eval(x, out=out, energy=False), args.steps, args.warmup)
+    rh = timer.run(lambda: T.hvp(x, v, out=y), args.steps, args.warmup)
+    be = compulsory_bytes_terms(m.nv, blocks, T.nnzb, 4)
+    bh = compulsory_bytes_terms(m.nv, blocks, T.nnzb, 4, hvp=True)
+    T.close()
+    return {"workload": f"term front end, cloth set (spring + inertia), {args.n}x{args.n}, fp32",
+            "kernels": ["k_terms_eval<float, false, Spring, Inertia>",
+                        "k_terms_hvp<float, false, Spring, Inertia>"],
+            "steps": args.steps, "warmup": args.warmup,
+            "eval_ms_mean": round(re["mean_ms"], 5), "eval_algorithmic_bytes": be,
+            "hvp_ms_mean": round(rh["mean_ms"], 5), "hvp_algorithmic_bytes": bh}
+
+
 def bench_secondary(torch, binding, inputs, args, timer):
     import numpy as np
     sec = {}
@@ -557,6 +581,9 @@ def main():
                     help="LDS bytes per patch (0 = library default)")
     ap.add_argument("--hvp-only", action="store_true",
                     help="only time the cloth HVP (prints its own JSON line; for counter runs)")
+    ap.add_argument("--terms-cloth-only", action="store_true",
+                    help="only time the term front end's cloth set, eval then HVP (prints "
+                         "its own JSON line; for counter runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device-to-device copy of 256 MiB five times "
                          "(reference kernel for the HBM byte counters)")
@@ -588,6 +615,9 @@ def main():
     timer = Timer(torch)
     if args.hvp_only:
         print(json.dumps(bench_hvp_only(torch, binding, inputs, args, timer)))
+        return 0
+    if args.terms_cloth_only:
+        print(json.dumps(bench_terms_cloth_only(torch, inputs, args, timer)))
         return 0
     log(f"bench: cloth {args.n}x{args.n} fp32, steps={args.steps} warmup={args.warmup}")
     res = bench_headline(torch, binding, inputs, args, timer)

@@ -143,7 +143,12 @@ hipError_t terms_grid(int set, int lds, int nchunk, int nv, int *grid_eval, int 
         return int(g < 1 ? 1 : g);
     };
     *grid_eval = clamp(occ_e, nchunk);
-    *grid_hvp = clamp(occ_h, (int64_t(nv) + kTermsHvpThreads - 1) / kTermsHvpThreads);
+    // The product's lanes each walk their own row's records, so a wave
+    // touches a wide strip of lines; more than kTermsHvpGroupsPerCU resident
+    // workgroups per CU overflow the L2 and refetch them (at 1000^2 cloth:
+    // 509 MB fetched and 78 us with 8 per CU, 314 MB and 55 us with 4).
+    *grid_hvp = clamp(occ_h < kTermsHvpGroupsPerCU ? occ_h : kTermsHvpGroupsPerCU,
+                      (int64_t(nv) + kTermsHvpThreads - 1) / kTermsHvpThreads);
     return hipSuccess;
 }
 

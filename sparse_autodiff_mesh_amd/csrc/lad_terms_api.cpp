@@ -31,6 +31,7 @@ struct lad_terms_ctx {
     PatchHdr *d_chunk = nullptr;
     int32_t *d_inc_ptr[kMaxTerms] = {};
     TermInc *d_inc[kMaxTerms] = {};
+    unsigned char *d_inl[kMaxTerms] = {};   // inline records (small stencils)
     int32_t *d_elems[kMaxTerms] = {};
     void *d_consts[kMaxTerms] = {};
     double *d_epart = nullptr;
@@ -258,15 +259,35 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
                 inc[size_t(cur[size_t(a)]++)] = r;
             }
         }
-        std::vector<int32_t> elems(b.elems, b.elems + int64_t(b.count) * K);
-        std::vector<T> consts(size_t(b.count) * size_t(NC));
-        for (size_t q = 0; q < consts.size(); ++q) consts[q] = T(b.consts[q]);
         e = upload(ctx, &ctx->d_inc_ptr[t], ptr, s);
-        if (e == hipSuccess) e = upload(ctx, &ctx->d_inc[t], inc, s);
-        if (e == hipSuccess) e = upload(ctx, &ctx->d_elems[t], elems, s);
-        T *dc = nullptr;
-        if (e == hipSuccess) e = upload(ctx, &dc, consts, s);
-        ctx->d_consts[t] = dc;
+        if (K <= kInlineVerts) {
+            // each record carries the element's other vertex and constants
+            // (InlineRec<T, NC>: pk, other, c[NC], padded to 8 bytes)
+            const size_t rb = inline_rec_bytes<T>(NC);
+            std::vector<unsigned char> recs(inc.size() * rb, 0);
+            for (size_t k = 0; k < inc.size(); ++k) {
+                unsigned char *r = recs.data() + k * rb;
+                const int64_t el = inc[k].e;
+                const int i = int(inc[k].pk & 3u);
+                const int32_t other = K == 2 ? b.elems[el * 2 + (1 - i)] : 0;
+                std::memcpy(r, &inc[k].pk, 4);
+                std::memcpy(r + 4, &other, 4);
+                for (int q = 0; q < NC; ++q) {
+                    const T c = T(b.consts[el * NC + q]);
+                    std::memcpy(r + 8 + size_t(q) * sizeof(T), &c, sizeof(T));
+                }
+            }
+            if (e == hipSuccess) e = upload(ctx, &ctx->d_inl[t], recs, s);
+        } else {
+            std::vector<int32_t> elems(b.elems, b.elems + int64_t(b.count) * K);
+            std::vector<T> consts(size_t(b.count) * size_t(NC));
+            for (size_t q = 0; q < consts.size(); ++q) consts[q] = T(b.consts[q]);
+            if (e == hipSuccess) e = upload(ctx, &ctx->d_inc[t], inc, s);
+            if (e == hipSuccess) e = upload(ctx, &ctx->d_elems[t], elems, s);
+            T *dc = nullptr;
+            if (e == hipSuccess) e = upload(ctx, &dc, consts, s);
+            ctx->d_consts[t] = dc;
+        }
     }
     if (e == hipSuccess)
         e = terms_grid<T>(ctx->set, ctx->lds_bytes, ctx->nchunk, nv, &ctx->grid_eval,
@@ -292,6 +313,7 @@ TermsArgs<T> args_of(const lad_terms_ctx *ctx)
     for (int t = 0; t < ctx->nterms; ++t) {
         a.t[t].inc_ptr = ctx->d_inc_ptr[t];
         a.t[t].inc = ctx->d_inc[t];
+        a.t[t].inl = ctx->d_inl[t];
         a.t[t].elems = ctx->d_elems[t];
         a.t[t].consts = static_cast<const T *>(ctx->d_consts[t]);
     }

@@ -15,6 +15,7 @@ namespace terms {
 constexpr int kMaxTerms = 4;   // term types of one set
 constexpr int kMaxVerts = 4;   // vertices per element (offsets pack into 24 bits)
 constexpr int kTermsHvpThreads = 256;  // threads per workgroup of the product kernel
+constexpr int kTermsHvpGroupsPerCU = 4;  // resident product workgroups per CU, at most
 
 // Set ids (the values of LAD_TERMS_* in include/lad_terms.h).
 constexpr int kSetCloth = 1;
@@ -32,12 +33,44 @@ struct alignas(8) TermInc {
     uint32_t pk;
 };
 
+// Terms of at most kInlineVerts vertices keep, in each row's incidence
+// record, the element's other vertex and its constants, so a row streams
+// its records instead of gathering the element's data by element id (each
+// element is stored once per vertex, twice at most).  Larger stencils keep
+// one copy of each element's data, which the rows of its vertices share
+// through the caches.
+constexpr int kInlineVerts = 2;
+
+// pk as in TermInc; other: the element's other vertex (two-vertex terms);
+// c: the element's constants.
+template <typename T, int NC>
+struct alignas(8) InlineRec {
+    uint32_t pk;
+    int32_t other;
+    T c[NC > 0 ? NC : 1];
+};
+
+template <typename T>
+constexpr size_t inline_rec_bytes(int nconst)
+{
+    return (8 + size_t(nconst > 0 ? nconst : 1) * sizeof(T) + 7) & ~size_t(7);
+}
+static_assert(sizeof(InlineRec<float, 2>) == inline_rec_bytes<float>(2), "record layout");
+static_assert(sizeof(InlineRec<float, 4>) == inline_rec_bytes<float>(4), "record layout");
+static_assert(sizeof(InlineRec<float, 1>) == inline_rec_bytes<float>(1), "record layout");
+static_assert(sizeof(InlineRec<double, 2>) == inline_rec_bytes<double>(2), "record layout");
+static_assert(sizeof(InlineRec<double, 4>) == inline_rec_bytes<double>(4), "record layout");
+static_assert(sizeof(InlineRec<double, 1>) == inline_rec_bytes<double>(1), "record layout");
+
 template <typename T>
 struct TermData {
     const int32_t *inc_ptr;      // [nv+1] incidence offsets
     const TermInc *inc;          // incident elements of each row, by element id
-    const int32_t *elems;        // [ne][K] vertex ids
-    const T *consts;             // [ne][kConsts]
+                                 // (terms of more than kInlineVerts vertices)
+    const void *inl;             // the same as InlineRec<T, kConsts> records
+                                 // (terms of at most kInlineVerts vertices)
+    const int32_t *elems;        // [ne][K] vertex ids (larger terms only)
+    const T *consts;             // [ne][kConsts] (larger terms only)
 };
 
 template <typename T>

@@ -86,6 +86,47 @@ __device__ __forceinline__ void stream_in(T *dst, const T *__restrict__ src, int
     for (int i = head + nvec * V + threadIdx.x; i < n; i += NT) dst[i] = src[i];
 }
 
+// The incidence records [base, base + B) of row a (indices clamped into the
+// row's range, so every load is valid): position and block offsets (pk),
+// vertex ids in element order and constants.  Small stencils read them from
+// the row's own records; larger ones gather the element's vertex ids and
+// constants by element id.
+template <typename Term, typename T, int B>
+__device__ __forceinline__ void load_records(const TermData<T> &td, int32_t a, int32_t base,
+                                             int32_t p1, TermInc (&rec)[B],
+                                             int32_t (&vid)[B][Term::kVerts],
+                                             T (&cc)[B][Term::kConsts > 0 ? Term::kConsts : 1])
+{
+    constexpr int K = Term::kVerts, NC = Term::kConsts;
+    if constexpr (K <= kInlineVerts) {
+        using R = InlineRec<T, NC>;
+        const R *ir = static_cast<const R *>(td.inl);
+        R q[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) q[j] = ir[min(base + j, p1 - 1)];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            rec[j].e = 0;  // not needed: the record holds the element's data
+            rec[j].pk = q[j].pk;
+            const int i = int(q[j].pk & 3u);
+#pragma unroll
+            for (int u = 0; u < K; ++u) vid[j][u] = u == i ? a : q[j].other;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) cc[j][k] = q[j].c[k];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < B; ++j) rec[j] = td.inc[min(base + j, p1 - 1)];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+#pragma unroll
+            for (int u = 0; u < K; ++u) vid[j][u] = td.elems[int64_t(rec[j].e) * K + u];
+#pragma unroll
+            for (int k = 0; k < NC; ++k) cc[j][k] = td.consts[int64_t(rec[j].e) * NC + k];
+        }
+    }
+}
+
 // Terms that depend only on differences of their vertices' positions say so
 // (kTranslationInvariant); the engine then differentiates them in the
 // positions of vertices 1 .. K-1 with vertex 0 held fixed, on one full
@@ -170,16 +211,7 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
         int32_t vid[kTermBatch][K];
         T xv[kTermBatch][K][3];
         T cc[kTermBatch][NC > 0 ? NC : 1];
-#pragma unroll
-        for (int j = 0; j < kTermBatch; ++j) rec[j] = td.inc[min(base + j, p1 - 1)];
-#pragma unroll
-        for (int j = 0; j < kTermBatch; ++j) {
-#pragma unroll
-            for (int v = 0; v < K; ++v)  // a one-vertex element's vertex is the row's
-                vid[j][v] = K == 1 ? a : td.elems[int64_t(rec[j].e) * K + v];
-#pragma unroll
-            for (int q = 0; q < NC; ++q) cc[j][q] = td.consts[int64_t(rec[j].e) * NC + q];
-        }
+        load_records<Term>(td, a, base, p1, rec, vid, cc);
 #pragma unroll
         for (int j = 0; j < kTermBatch; ++j)
 #pragma unroll
@@ -296,16 +328,7 @@ __device__ __forceinline__ void row_term_hvp(const TermData<T> &td, int32_t a,
         int32_t vid[kTermBatch][K];
         T xv[kTermBatch][K][3], vv[kTermBatch][K][3];
         T cc[kTermBatch][NC > 0 ? NC : 1];
-#pragma unroll
-        for (int j = 0; j < kTermBatch; ++j) rec[j] = td.inc[min(base + j, p1 - 1)];
-#pragma unroll
-        for (int j = 0; j < kTermBatch; ++j) {
-#pragma unroll
-            for (int u = 0; u < K; ++u)  // a one-vertex element's vertex is the row's
-                vid[j][u] = K == 1 ? a : td.elems[int64_t(rec[j].e) * K + u];
-#pragma unroll
-            for (int q = 0; q < NC; ++q) cc[j][q] = td.consts[int64_t(rec[j].e) * NC + q];
-        }
+        load_records<Term>(td, a, base, p1, rec, vid, cc);
 #pragma unroll
         for (int j = 0; j < kTermBatch; ++j)
 #pragma unroll
