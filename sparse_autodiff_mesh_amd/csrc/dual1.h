@@ -10,7 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "dual2.h"  // lad_sqrt
+#include "dual2.h"  // lad_sqrt_rcp
 
 namespace lad {
 
@@ -79,8 +79,9 @@ template <typename T, int N>
 __device__ __forceinline__ Dual1<T, N> sqrt(const Dual1<T, N> &a)
 {
     Dual1<T, N> r;
-    r.v = lad_sqrt(a.v);
-    const T d = T(0.5) / r.v;
+    T inv;
+    lad_sqrt_rcp(a.v, r.v, inv);
+    const T d = T(0.5) * inv;
 #pragma unroll
     for (int i = 0; i < N; ++i) r.g[i] = d * a.g[i];
     return r;

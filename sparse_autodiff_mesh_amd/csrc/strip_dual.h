@@ -20,7 +20,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "dual2.h"  // lad_sqrt, lad_log
+#include "dual2.h"  // lad_sqrt_rcp, lad_rcp, lad_log
 
 namespace lad {
 
@@ -196,22 +196,22 @@ __device__ __forceinline__ StripDual<T, N> chain(const StripDual<T, N> &a, T f0,
 template <typename T, int N>
 __device__ __forceinline__ StripDual<T, N> sqrt(const StripDual<T, N> &a)
 {
-    const T s = lad_sqrt(a.v);
-    const T inv = T(1) / s;
+    T s, inv;
+    lad_sqrt_rcp(a.v, s, inv);
     return chain(a, s, T(0.5) * inv, T(-0.25) * inv * inv * inv);
 }
 
 template <typename T, int N>
 __device__ __forceinline__ StripDual<T, N> log(const StripDual<T, N> &a)
 {
-    const T inv = T(1) / a.v;
+    const T inv = lad_rcp(a.v);
     return chain(a, lad_log(a.v), inv, -inv * inv);
 }
 
 template <typename T, int N>
 __device__ __forceinline__ StripDual<T, N> reciprocal(const StripDual<T, N> &a)
 {
-    const T inv = T(1) / a.v;
+    const T inv = lad_rcp(a.v);
     return chain(a, inv, -inv * inv, T(2) * inv * inv * inv);
 }
 
@@ -225,7 +225,7 @@ __device__ __forceinline__ StripDual<T, N> operator/(const StripDual<T, N> &a,
 template <typename T, int N>
 __device__ __forceinline__ StripDual<T, N> operator/(const StripDual<T, N> &a, T c)
 {
-    return (T(1) / c) * a;
+    return lad_rcp(c) * a;
 }
 
 }  // namespace lad
