@@ -39,6 +39,8 @@ struct lad_ctx {
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
     int32_t *d_fptr = nullptr;
+    int32_t *d_sl_ptr = nullptr, *d_sl_nb = nullptr;
+    void *d_sl_rest = nullptr;
     FaceInc *d_finc = nullptr;
     void *d_face_dm = nullptr, *d_face_area = nullptr;
 
@@ -218,6 +220,10 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
     if (e == hipSuccess && ctx->row_mode) {
         e = upload(ctx, &p, narrow<T>(rplan.slot_rest.data(), rplan.slot_rest.size()), s);
         ctx->d_slot_rest = p;
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_sl_ptr, rplan.sl_ptr, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_sl_nb, rplan.sl_nb, s);
+        if (e == hipSuccess) e = upload(ctx, &p, narrow<T>(rplan.sl_rest.data(), rplan.sl_rest.size()), s);
+        ctx->d_sl_rest = p;
     }
     if (e == hipSuccess && ctx->row_mode && ctx->faces_on) {
         e = upload(ctx, &p, narrow<T>(d->dm_inv, size_t(d->nf) * 4), s);
@@ -267,6 +273,9 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.rp0 = ctx->pat.rp[0];
     a.ci0 = ctx->pat.ci[0];
     a.slot_rest = static_cast<const T *>(ctx->d_slot_rest);
+    a.sl_ptr = ctx->d_sl_ptr;
+    a.sl_nb = ctx->d_sl_nb;
+    a.sl_rest = static_cast<const T *>(ctx->d_sl_rest);
     a.x_tilde = static_cast<const T *>(ctx->d_xt);
     a.fptr = ctx->d_fptr;
     a.finc = ctx->d_finc;

@@ -124,12 +124,23 @@ struct alignas(16) FaceInc {
     uint32_t pk;
 };
 constexpr int kMaxRowFaceSlots = 256;   // slot offsets fit 8 bits
+constexpr int kSliceRows = 64;          // rows per spring slice: one wave
 
 struct RowPlan {
     std::vector<PatchHdr> chunk;     // v0, nown (rows), blk0, nblk, amap_cap
     std::vector<double> slot_rest;   // [nnzb] rest length behind each block, -1: none
     std::vector<int32_t> fptr;       // [nv+1] face incidence offsets (face term on)
     std::vector<FaceInc> finc;       // incident faces of each row, by face id
+    // Spring slices for the product kernels: rows in slices of
+    // kSliceRows; slice t holds sl_ptr[t + 1] - sl_ptr[t] = kSliceRows * W_t
+    // entries, W_t the most springs any of its rows has.  Spring j of row
+    // kSliceRows * t + l (its j-th spring neighbour in ascending column
+    // order) is entry sl_ptr[t] + kSliceRows * j + l: a wave reads one
+    // spring of each of its rows with one coalesced load.  Padding entries
+    // name the row itself (or row 0 past the last row) with rest length -1.
+    std::vector<int32_t> sl_ptr;     // [nslice + 1]
+    std::vector<int32_t> sl_nb;      // neighbour vertex
+    std::vector<double> sl_rest;     // rest length
 };
 
 // Returns "" when the row path applies (rest lengths >= 0, at most one
@@ -208,6 +219,9 @@ struct RowArgs {
     const int32_t *rp0, *ci0;    // topology pattern
     const T *slot_rest;          // [nnzb_base] rest length of the spring behind
                                  // each block (< 0: no spring)
+    const int32_t *sl_ptr;       // spring slices (RowPlan): entry offsets,
+    const int32_t *sl_nb;        // neighbour vertices
+    const T *sl_rest;            // and rest lengths (< 0: padding)
     const T *x_tilde;            // null = no inertia
     const int32_t *fptr;         // [nv+1] face incidence offsets (faces on)
     const FaceInc *finc;         // incident faces of each row

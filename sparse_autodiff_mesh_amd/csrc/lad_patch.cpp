@@ -23,6 +23,7 @@
 //    summation order); the default mode uses LDS atomics and the same order
 //    keeps lanes of one wave off the same addresses.
 #include <algorithm>
+#include <climits>
 #include <cstring>
 
 #include "lad_internal.h"
@@ -340,6 +341,42 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         if (sab >= 0.0 || sba >= 0.0) return "two springs join the same vertex pair";
         sab = L;
         sba = L;
+    }
+    {
+        // spring slices: each row's spring neighbours in column order
+        const int64_t nsl = (int64_t(nv) + kSliceRows - 1) / kSliceRows;
+        out.sl_ptr.assign(size_t(nsl) + 1, 0);
+        int64_t tot = 0;
+        for (int64_t t = 0; t < nsl; ++t) {
+            int32_t w = 0;
+            for (int64_t a = t * kSliceRows; a < std::min<int64_t>(nv, (t + 1) * kSliceRows); ++a) {
+                int32_t n = 0;
+                for (int64_t k = rp[a]; k < rp[a + 1]; ++k)
+                    n += (ci[k] != a && out.slot_rest[size_t(k)] >= 0.0) ? 1 : 0;
+                w = std::max(w, n);
+            }
+            tot += int64_t(kSliceRows) * w;
+            if (tot > INT32_MAX) return "too many springs for the spring slices";
+            out.sl_ptr[size_t(t) + 1] = int32_t(tot);
+        }
+        out.sl_nb.assign(size_t(tot), 0);
+        out.sl_rest.assign(size_t(tot), -1.0);
+        for (int64_t t = 0; t < nsl; ++t) {
+            const int64_t w = (out.sl_ptr[size_t(t) + 1] - out.sl_ptr[size_t(t)]) / kSliceRows;
+            for (int64_t l = 0; l < kSliceRows; ++l) {
+                const int64_t a = t * kSliceRows + l;
+                const int64_t e0 = out.sl_ptr[size_t(t)] + l;
+                int64_t j = 0;
+                if (a < nv)
+                    for (int64_t k = rp[a]; k < rp[a + 1]; ++k)
+                        if (ci[k] != a && out.slot_rest[size_t(k)] >= 0.0) {
+                            out.sl_nb[size_t(e0 + kSliceRows * j)] = ci[k];
+                            out.sl_rest[size_t(e0 + kSliceRows * j)] = out.slot_rest[size_t(k)];
+                            ++j;
+                        }
+                for (; j < w; ++j) out.sl_nb[size_t(e0 + kSliceRows * j)] = a < nv ? int32_t(a) : 0;
+            }
+        }
     }
     if (in.face_energy && in.nf > 0) {
         // per-row incidence, rows in vertex order, faces by id within a row

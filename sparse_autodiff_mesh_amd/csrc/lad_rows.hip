@@ -763,6 +763,93 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
 // Matrix-free Hessian-vector product, y_a = sum over the row's terms of
 // H_ab v_b, with the local Hessians formed in registers and never stored.
 // ---------------------------------------------------------------------------
+// Spring neighbours a lane loads together in the product kernels.
+constexpr int kSliceBatch = 6;
+
+// What a lane of the product kernels loads for its row before the gathers:
+// the row's position, its operand (v, or r and the previous direction for
+// Newton-CG), its first kSliceBatch spring neighbours with their rest
+// lengths (without the face term only) or its incident-face range.  Every load depends only on the
+// slice index, so the next slice's are issued while the current slice is
+// processed.
+template <typename T>
+struct SliceRow {
+    T xa[3], o0[3], o1[3];
+    int32_t nb[kSliceBatch];
+    T L[kSliceBatch];
+    int32_t f0, f1;
+};
+
+// Issue the loads of slice t's head for lane `lane` (every index in bounds:
+// rows past the last are clamped to it, padding names a valid vertex).
+template <typename T, bool FACES, bool CG>
+__device__ __forceinline__ void slice_head(const RowArgs<T> &A, int32_t t, int lane,
+                                           const T *__restrict__ x, const T *__restrict__ v,
+                                           const CgDir<T> &cg, SliceRow<T> &h)
+{
+    const int32_t a = min(t * kSliceRows + lane, A.nv - 1);
+    const int32_t p = A.sl_ptr[t];
+    const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        h.xa[k] = x[int64_t(a) * 3 + k];
+        if constexpr (CG) {
+            h.o0[k] = cg.r[int64_t(a) * 3 + k];
+            h.o1[k] = cg.d_old[int64_t(a) * 3 + k];
+        } else {
+            h.o0[k] = v[int64_t(a) * 3 + k];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kSliceBatch; ++j) {
+        h.nb[j] = a;
+        h.L[j] = T(-1);
+        if (!FACES && j < ns) {  // wave-uniform; with faces the registers go to them
+            h.nb[j] = A.sl_nb[p + j * kSliceRows + lane];
+            h.L[j] = A.sl_rest[p + j * kSliceRows + lane];
+        }
+    }
+    h.f0 = FACES ? A.fptr[a] : 0;
+    h.f1 = FACES ? A.fptr[a + 1] : 0;
+}
+
+// Spring neighbours j0 .. j0 + kSliceBatch - 1 of row a (lane `lane` of
+// slice entries starting at p; ns springs in the slice's widest row): the
+// first batch from the prefetched head, later ones loaded here.
+template <typename T, bool FACES>
+__device__ __forceinline__ void slice_batch(const RowArgs<T> &A, const SliceRow<T> &h, int32_t p,
+                                            int32_t ns, int32_t j0, int lane, int32_t self,
+                                            int32_t nb[kSliceBatch], T L[kSliceBatch])
+{
+#pragma unroll
+    for (int j = 0; j < kSliceBatch; ++j) {
+        if (!FACES && j0 == 0) {
+            nb[j] = h.nb[j];
+            L[j] = h.L[j];
+        } else {
+            nb[j] = self;
+            L[j] = T(-1);
+            if (j0 + j < ns) {
+                nb[j] = A.sl_nb[p + (j0 + j) * kSliceRows + lane];
+                L[j] = A.sl_rest[p + (j0 + j) * kSliceRows + lane];
+            }
+        }
+    }
+}
+
+// This workgroup's slices [t0, t1) (contiguous ranges grouped by XCD) and
+// its wave's first slice; the waves walk the range kWaves slices apart.
+constexpr int32_t kSliceWaves = kHvpThreads / kSliceRows;
+__device__ __forceinline__ void slice_range(int32_t nv, int32_t &t0, int32_t &t1, int32_t &first)
+{
+    const int32_t wv = __builtin_amdgcn_readfirstlane(int32_t(threadIdx.x) / kSliceRows);
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t nsl = (nv + kSliceRows - 1) / kSliceRows;
+    t0 = int32_t(int64_t(nsl) * w / gridDim.x);
+    t1 = int32_t(int64_t(nsl) * (w + 1) / gridDim.x);
+    first = t0 + wv;
+}
+
 // Every row's topology terms (springs, faces, inertia); the runtime
 // contacts of the rows they touch are added afterwards by k_hvp_pair_rows.
 template <typename T, bool FACES, bool CG>
@@ -779,33 +866,19 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
         else return v[i];
     };
-    constexpr int act = 0;  // the topology pattern
-    const int32_t *rpa = A.rp0;
-    const int32_t *cia = A.ci0;
-    // Nothing is staged here, so a workgroup takes a contiguous row range
-    // (ranges grouped by XCD) and walks it kHvpThreads rows at a time.  The row
-    // header, position and direction of the next group are loaded while the
-    // current group is processed, which takes one dependent load level off
-    // every group.
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
-    const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
-    int32_t an = r0 + int32_t(threadIdx.x);
-    Row<T> rn;
-    T vn[3];
+    // Rows go in slices of kSliceRows, one wave per slice: lane l takes row
+    // kSliceRows * t + l, and spring j of the slice's rows is one coalesced
+    // load.  A workgroup takes a contiguous slice range (ranges grouped by
+    // XCD) and its waves walk it four slices apart.
+    const int lane = int(threadIdx.x) & (kSliceRows - 1);
+    int32_t t0, t1, tn;
+    slice_range(A.nv, t0, t1, tn);
+    SliceRow<T> hn;
     double vy = 0.0;  // this lane's part of v.y
+    // The first slice's loads are issued before the Newton-CG step below, so
+    // that their latency overlaps its sum.
+    if (tn < t1) slice_head<T, FACES, CG>(A, tn, lane, x, v, cg, hn);
     if constexpr (CG) {
-        // The first group's header and direction operands are loaded before
-        // the Newton-CG step below, so that their latency overlaps its sum.
-        T r_a[3], d_a[3];
-        if (an < r1) {
-            rn = load_row<T, false>(A, act, rpa, an, x);
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                r_a[k] = cg.r[int64_t(an) * 3 + k];
-                d_a[k] = cg.d_old[int64_t(an) * 3 + k];
-            }
-        }
         // Every workgroup takes the step that closes the previous update
         // (convergence or beta) from the partial sums of r.r, the same way;
         // none runs once the solve has ended.
@@ -814,107 +887,114 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             beta = cg_beta_step<kHvpThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, blockIdx.x == 0,
                                              stop, red, &sum_bc);
         if (stop) return;  // workgroup-uniform
-        if (an < r1)
-#pragma unroll
-            for (int k = 0; k < 3; ++k) vn[k] = T(-double(r_a[k]) + beta * double(d_a[k]));
-    } else if (an < r1) {
-        rn = load_row<T, false>(A, act, rpa, an, x);
-#pragma unroll
-        for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
     }
-    for (; an < r1;) {
-        const Row<T> r = rn;
+    for (; tn < t1;) {  // wave-uniform
+        const int32_t t = tn;
+        const SliceRow<T> h = hn;
+        tn += kSliceWaves;
+        if (tn < t1) slice_head<T, FACES, CG>(A, tn, lane, x, v, cg, hn);
+        const int32_t a = t * kSliceRows + lane;
+        const bool live = a < A.nv;
+        const int32_t p = A.sl_ptr[t];
+        const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            va[k] = vn[k];
-            if constexpr (CG) cg.d_new[int64_t(r.a) * 3 + k] = va[k];
-        }
-        an += kHvpThreads;
-        if (an < r1) {
-            rn = load_row<T, false>(A, act, rpa, an, x);
-#pragma unroll
-            for (int k = 0; k < 3; ++k) vn[k] = dir(int64_t(an) * 3 + k);
+            if constexpr (CG) va[k] = T(-double(h.o0[k]) + beta * double(h.o1[k]));
+            else va[k] = h.o0[k];
+            if (CG && live) cg.d_new[int64_t(a) * 3 + k] = va[k];
         }
         // Every term is evaluated once in DualHv numbers seeded with the
         // term's variables and the matching components of v; the gradient's
         // directional derivative gt is the term's Hessian applied to v.
-        int32_t jb = r.kb0;
-        for (int32_t base = r.s0; base < r.s1; base += kBatch) {
-            SlotBatch<T> q;
-            load_batch(A, r, act, cia, base, jb, x, q);
-            T vb[kBatch][3];
+        // Springs in the row's column order, kSliceBatch at a time.
+        for (int32_t j0 = 0; j0 < ns; j0 += kSliceBatch) {  // wave-uniform
+            int32_t nb[kSliceBatch];
+            T L[kSliceBatch];
+            slice_batch<T, FACES>(A, h, p, ns, j0, lane, live ? a : 0, nb, L);
+            T xb[kSliceBatch][3], vb[kSliceBatch][3];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
+            for (int j = 0; j < kSliceBatch; ++j)
 #pragma unroll
-                for (int k = 0; k < 3; ++k) vb[j][k] = dir(int64_t(bl) * 3 + k);
-            }
+                for (int k = 0; k < 3; ++k) {
+                    xb[j][k] = x[int64_t(nb[j]) * 3 + k];
+                    vb[j][k] = dir(int64_t(nb[j]) * 3 + k);
+                }
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (base + j >= r.s1) break;
-                if (q.b[j] == r.a || !(q.L[j] >= T(0))) continue;
+            for (int j = 0; j < kSliceBatch; ++j) {
+                if (j0 + j >= ns) break;
+                if (!(L[j] >= T(0))) continue;
                 DualHv<T, 3> d[3];
 #pragma unroll
                 for (int k = 0; k < 3; ++k)
-                    d[k] = DualHv<T, 3>::var(r.xa[k] - q.xb[j][k], k, va[k] - vb[j][k]);
-                const DualHv<T, 3> e = spring_energy(d, q.L[j], A.k);
+                    d[k] = DualHv<T, 3>::var(h.xa[k] - xb[j][k], k, va[k] - vb[j][k]);
+                const DualHv<T, 3> e = spring_energy(d, L[j], A.k);
 #pragma unroll
                 for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
             }
         }
-        if constexpr (FACES)
-        for (int32_t base = r.f0; base < r.f1; base += kFaceBatch) {
-            FaceBatch<T> q;
-            load_faces(A, r, base, x, q);
-            T vo[kFaceBatch][2][3];
+        if constexpr (FACES) {
+            Row<T> r{};
+            r.a = live ? a : A.nv - 1;
+            r.f0 = live ? h.f0 : 0;
+            r.f1 = live ? h.f1 : 0;
 #pragma unroll
-            for (int j = 0; j < kFaceBatch; ++j)
+            for (int k = 0; k < 3; ++k) r.xa[k] = h.xa[k];
+            for (int32_t base = r.f0; base < r.f1; base += kFaceBatch) {
+                FaceBatch<T> q;
+                load_faces(A, r, base, x, q);
+                T vo[kFaceBatch][2][3];
 #pragma unroll
-                for (int k = 0; k < 3; ++k) {
-                    vo[j][0][k] = dir(int64_t(q.e[j].o1) * 3 + k);
-                    vo[j][1][k] = dir(int64_t(q.e[j].o2) * 3 + k);
+                for (int j = 0; j < kFaceBatch; ++j)
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        vo[j][0][k] = dir(int64_t(q.e[j].o1) * 3 + k);
+                        vo[j][1][k] = dir(int64_t(q.e[j].o2) * 3 + k);
+                    }
+#pragma unroll
+                for (int j = 0; j < kFaceBatch; ++j) {
+                    if (base + j >= r.f1) break;
+                    const int i = int(q.e[j].pk & 3u);
+                    T Fv[6], w[3][2];
+                    face_F(r, q, j, i, Fv, w);
+                    // direction in F: dF = (dF/dp) v_face
+                    DualHv<T, 6> F[6];
+#pragma unroll
+                    for (int sp = 0; sp < 3; ++sp) {
+                        const T v0 = i == 0 ? va[sp] : (i == 1 ? vo[j][1][sp] : vo[j][0][sp]);
+                        const T v1 = i == 1 ? va[sp] : (i == 2 ? vo[j][1][sp] : vo[j][0][sp]);
+                        const T v2 = i == 2 ? va[sp] : (i == 0 ? vo[j][1][sp] : vo[j][0][sp]);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+                            F[2 * sp + c] = DualHv<T, 6>::var(
+                                Fv[2 * sp + c], 2 * sp + c,
+                                w[0][c] * v0 + w[1][c] * v1 + w[2][c] * v2);
+                    }
+                    const DualHv<T, 6> e = face_energy(F, q.area[j]);
+                    // y_a += (dF/dp_a)^T (d2E/dF2 dF)
+                    const T wa0 = i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]);
+                    const T wa1 = i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1]);
+#pragma unroll
+                    for (int sp = 0; sp < 3; ++sp)
+                        Y[sp] += wa0 * e.gt[2 * sp] + wa1 * e.gt[2 * sp + 1];
                 }
-#pragma unroll
-            for (int j = 0; j < kFaceBatch; ++j) {
-                if (base + j >= r.f1) break;
-                const int i = int(q.e[j].pk & 3u);
-                T Fv[6], w[3][2];
-                face_F(r, q, j, i, Fv, w);
-                // direction in F: dF = (dF/dp) v_face
-                DualHv<T, 6> F[6];
-#pragma unroll
-                for (int sp = 0; sp < 3; ++sp) {
-                    const T v0 = i == 0 ? va[sp] : (i == 1 ? vo[j][1][sp] : vo[j][0][sp]);
-                    const T v1 = i == 1 ? va[sp] : (i == 2 ? vo[j][1][sp] : vo[j][0][sp]);
-                    const T v2 = i == 2 ? va[sp] : (i == 0 ? vo[j][1][sp] : vo[j][0][sp]);
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        F[2 * sp + c] = DualHv<T, 6>::var(
-                            Fv[2 * sp + c], 2 * sp + c, w[0][c] * v0 + w[1][c] * v1 + w[2][c] * v2);
-                }
-                const DualHv<T, 6> e = face_energy(F, q.area[j]);
-                // y_a += (dF/dp_a)^T (d2E/dF2 dF)
-                const T wa0 = i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]);
-                const T wa1 = i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1]);
-#pragma unroll
-                for (int sp = 0; sp < 3; ++sp) Y[sp] += wa0 * e.gt[2 * sp] + wa1 * e.gt[2 * sp + 1];
             }
         }
         if (A.inertia_on) {
             // seeded at z = 0 (x_tilde not loaded): the Hessian c I is the same
             DualHv<T, 3> z[3];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) z[k] = DualHv<T, 3>::var(r.xa[k] - r.xt[k], k, va[k]);
+            for (int k = 0; k < 3; ++k) z[k] = DualHv<T, 3>::var(T(0), k, va[k]);
             const DualHv<T, 3> e = inertia_energy(z, A.c);
 #pragma unroll
             for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
         }
+        if (live)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            y[int64_t(r.a) * 3 + k] = Y[k];
-            vy += double(va[k]) * double(Y[k]);
-        }
+            for (int k = 0; k < 3; ++k) {
+                y[int64_t(a) * 3 + k] = Y[k];
+                vy += double(va[k]) * double(Y[k]);
+            }
     }
     if (A.hvp_dot) {
         const double sum = block_sum<kHvpThreads>(vy, red);
@@ -1007,34 +1087,45 @@ __global__ void __launch_bounds__(kHvpThreads)
 k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__restrict__ v,
           T *__restrict__ y)
 {
-    const int32_t *rpa = A.rp0;
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
-    const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
-    for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kHvpThreads) {
-        const Row<T> r = load_row<T, false>(A, 0, rpa, a, x);
-        T va[3], Y[3] = {T(0), T(0), T(0)};
+    // the walk of k_hvp_rows: slices of rows, the next slice's head loaded
+    // while the current one is processed
+    const int lane = int(threadIdx.x) & (kSliceRows - 1);
+    int32_t t0, t1, tn;
+    slice_range(A.nv, t0, t1, tn);
+    const CgDir<T> none{};
+    SliceRow<T> hn;
+    if (tn < t1) slice_head<T, false, false>(A, tn, lane, x, v, none, hn);
+    for (; tn < t1;) {  // wave-uniform
+        const int32_t t = tn;
+        const SliceRow<T> h = hn;
+        tn += kSliceWaves;
+        if (tn < t1) slice_head<T, false, false>(A, tn, lane, x, v, none, hn);
+        const int32_t a = t * kSliceRows + lane;
+        const bool live = a < A.nv;
+        const int32_t p = A.sl_ptr[t];
+        const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;
+        T Y[3] = {T(0), T(0), T(0)};
+        const T *va = h.o0;
+        for (int32_t j0 = 0; j0 < ns; j0 += kSliceBatch) {  // wave-uniform
+            int32_t nb[kSliceBatch];
+            T L[kSliceBatch];
+            slice_batch<T, false>(A, h, p, ns, j0, lane, live ? a : 0, nb, L);
+            T xb[kSliceBatch][3], vb[kSliceBatch][3];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) va[k] = v[int64_t(a) * 3 + k];
-        int32_t jb = r.kb0;
-        for (int32_t base = r.s0; base < r.s1; base += kBatch) {
-            SlotBatch<T> q;
-            load_batch(A, r, 0, A.ci0, base, jb, x, q);
-            T vb[kBatch][3];
+            for (int j = 0; j < kSliceBatch; ++j)
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int32_t bl = q.kb[j] >= 0 ? q.b[j] : r.a;
+                for (int k = 0; k < 3; ++k) {
+                    xb[j][k] = x[int64_t(nb[j]) * 3 + k];
+                    vb[j][k] = v[int64_t(nb[j]) * 3 + k];
+                }
 #pragma unroll
-                for (int k = 0; k < 3; ++k) vb[j][k] = v[int64_t(bl) * 3 + k];
-            }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (base + j >= r.s1) break;
-                if (q.b[j] == r.a || !(q.L[j] >= T(0))) continue;
+            for (int j = 0; j < kSliceBatch; ++j) {
+                if (j0 + j >= ns) break;
+                if (!(L[j] >= T(0))) continue;
                 Dual1<T, 3> z[3];
 #pragma unroll
-                for (int k = 0; k < 3; ++k) z[k] = Dual1<T, 3>::var(r.xa[k] - q.xb[j][k], k);
-                const Dual1<T, 3> e = spring_residual(z, q.L[j], sqrt_k);
+                for (int k = 0; k < 3; ++k) z[k] = Dual1<T, 3>::var(h.xa[k] - xb[j][k], k);
+                const Dual1<T, 3> e = spring_residual(z, L[j], sqrt_k);
                 const T u = e.g[0] * (va[0] - vb[j][0]) + e.g[1] * (va[1] - vb[j][1]) +
                             e.g[2] * (va[2] - vb[j][2]);
 #pragma unroll
@@ -1044,8 +1135,9 @@ k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__
         if (A.inertia_on)
 #pragma unroll
             for (int k = 0; k < 3; ++k) Y[k] += sqrt_c * (sqrt_c * va[k]);
+        if (live)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) y[int64_t(a) * 3 + k] = Y[k];
+            for (int k = 0; k < 3; ++k) y[int64_t(a) * 3 + k] = Y[k];
     }
 }
 

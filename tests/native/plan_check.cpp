@@ -263,6 +263,40 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
         want[size_t(slot_of(rp, ci, m.springs[2 * s + 1], m.springs[2 * s]))] = m.rest[s];
     }
     CHECK(plan.slot_rest == want, "%s: per-block rest lengths", tag);
+    // spring slices: every row's springs by ascending neighbour, from the
+    // spring list itself; widths are the slice maxima, padding marked
+    std::vector<std::vector<std::pair<int32_t, double>>> sp(m.nv);
+    for (size_t s = 0; s * 2 < m.springs.size(); ++s) {
+        sp[m.springs[2 * s]].push_back({m.springs[2 * s + 1], m.rest[s]});
+        sp[m.springs[2 * s + 1]].push_back({m.springs[2 * s], m.rest[s]});
+    }
+    for (auto &l : sp) std::sort(l.begin(), l.end());
+    const int32_t nsl = (m.nv + kSliceRows - 1) / kSliceRows;
+    CHECK(int32_t(plan.sl_ptr.size()) == nsl + 1 && plan.sl_ptr[0] == 0, "%s: slice offsets size", tag);
+    if (int32_t(plan.sl_ptr.size()) != nsl + 1) return;
+    CHECK(size_t(plan.sl_ptr[nsl]) == plan.sl_nb.size() && plan.sl_nb.size() == plan.sl_rest.size(),
+          "%s: slice entry count", tag);
+    for (int32_t t = 0; t < nsl; ++t) {
+        const int32_t len = plan.sl_ptr[t + 1] - plan.sl_ptr[t];
+        size_t wmax = 0;
+        for (int32_t a = t * kSliceRows; a < std::min(m.nv, (t + 1) * kSliceRows); ++a)
+            wmax = std::max(wmax, sp[a].size());
+        CHECK(len >= 0 && len % kSliceRows == 0 && size_t(len / kSliceRows) == wmax,
+              "%s: slice %d width", tag, t);
+        if (len < 0 || size_t(plan.sl_ptr[t + 1]) > plan.sl_nb.size()) continue;
+        for (int32_t l = 0; l < kSliceRows; ++l) {
+            const int32_t a = t * kSliceRows + l;
+            for (int32_t j = 0; j < len / kSliceRows; ++j) {
+                const size_t e = size_t(plan.sl_ptr[t] + j * kSliceRows + l);
+                if (a < m.nv && size_t(j) < sp[a].size())
+                    CHECK(plan.sl_nb[e] == sp[a][j].first && plan.sl_rest[e] == sp[a][j].second,
+                          "%s: row %d spring %d", tag, a, j);
+                else
+                    CHECK(plan.sl_nb[e] == (a < m.nv ? a : 0) && plan.sl_rest[e] == -1.0,
+                          "%s: row %d padding %d", tag, a, j);
+            }
+        }
+    }
     if (!faces_on) return;
     CHECK(int32_t(plan.fptr.size()) == m.nv + 1, "%s: face offsets size", tag);
     std::vector<std::vector<int32_t>> inc(m.nv);
