@@ -763,6 +763,16 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
 // Matrix-free Hessian-vector product, y_a = sum over the row's terms of
 // H_ab v_b, with the local Hessians formed in registers and never stored.
 // ---------------------------------------------------------------------------
+// Component of the Newton-CG direction -r + beta d_prev.
+__device__ __forceinline__ float cg_dir_comp(float r, float d, float beta)
+{
+    return __builtin_fmaf(beta, d, -r);
+}
+__device__ __forceinline__ double cg_dir_comp(double r, double d, double beta)
+{
+    return __builtin_fma(beta, d, -r);
+}
+
 // Spring neighbours a lane loads together in the product kernels.
 constexpr int kSliceBatch = 6;
 
@@ -861,9 +871,12 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     __shared__ double sum_bc;
     __shared__ int32_t stop_bc;
     double beta = 0.0;
-    // operand component i: v[i], or the next Newton-CG direction -r + beta d
+    T beta_t = T(0);  // beta in the working precision
+    // operand component i: v[i], or the next Newton-CG direction -r + beta d,
+    // one fused multiply-add in the working precision (the same formula for
+    // a row's own direction, which it stores, and for its neighbours')
     auto dir = [&](int64_t i) -> T {
-        if constexpr (CG) return T(-double(cg.r[i]) + beta * double(cg.d_old[i]));
+        if constexpr (CG) return cg_dir_comp(cg.r[i], cg.d_old[i], beta_t);
         else return v[i];
     };
     // Rows go in slices of kSliceRows, one wave per slice: lane l takes row
@@ -887,6 +900,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
             beta = cg_beta_step<kHvpThreads>(cg.st, cg.rr_parts, cg.n_rr, cg.iter, blockIdx.x == 0,
                                              stop, red, &sum_bc);
         if (stop) return;  // workgroup-uniform
+        beta_t = T(beta);
     }
     for (; tn < t1;) {  // wave-uniform
         const int32_t t = tn;
@@ -900,7 +914,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         T va[3], Y[3] = {T(0), T(0), T(0)};
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            if constexpr (CG) va[k] = T(-double(h.o0[k]) + beta * double(h.o1[k]));
+            if constexpr (CG) va[k] = cg_dir_comp(h.o0[k], h.o1[k], beta_t);
             else va[k] = h.o0[k];
             if (CG && live) cg.d_new[int64_t(a) * 3 + k] = va[k];
         }
