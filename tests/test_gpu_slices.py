@@ -126,3 +126,31 @@ def test_gauss_newton_irregular(lad, nv, extra, hubs, dtype):
     yo = ores.gauss_newton_product(Jo, v_h)
     assert rel(y.cpu().numpy(), yo) <= TOL[dtype]
     L.close()
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_hvp_tiny(lad, dtype):
+    """One vertex (inertia only: no spring slice entries at all) and two
+    vertices joined by one spring: one slice, 63 or 62 idle lanes."""
+    import torch
+    log_case(test="slices_tiny", dtype=dtype)
+    for nv, springs, rest in [(1, None, None),
+                              (2, np.array([[0, 1]], dtype=np.int32), np.array([0.9]))]:
+        x = np.array([[0.1, 0.2, 0.3], [1.0, 0.4, -0.2]])[:nv]
+        xt = x + 0.05
+        kw = {} if springs is None else dict(springs=springs, rest_len=rest, k=K)
+        L = lad.Lad(nv, dtype=dtype, x_tilde=xt, c=C, **kw)
+        prob = oracle.Problem(nv=nv, x_tilde=host_input(xt, dtype), c=C,
+                              **({} if springs is None else
+                                 dict(springs=springs, rest_len=host_input(rest, dtype), k=K)))
+        x_h = host_input(x, dtype)
+        v_h = host_input(inputs.hvp_direction(nv), dtype)
+        y = L.hvp(dev(x_h, dtype), dev(v_h, dtype))
+        yg = L.gauss_newton(dev(x_h, dtype), dev(v_h, dtype))
+        torch.cuda.synchronize()
+        rp, ci = oracle.pattern(prob)
+        yo = oracle.hvp(prob, rp, ci, x_h, v_h)
+        assert rel(y.cpu().numpy(), yo) <= TOL[dtype], (nv, rel(y.cpu().numpy(), yo))
+        if springs is None:
+            assert rel(yg.cpu().numpy(), C * v_h) <= TOL[dtype]
+        L.close()
