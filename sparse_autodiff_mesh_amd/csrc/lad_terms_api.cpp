@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -32,6 +33,8 @@ struct lad_terms_ctx {
     int32_t *d_inc_ptr[kMaxTerms] = {};
     TermInc *d_inc[kMaxTerms] = {};
     unsigned char *d_inl[kMaxTerms] = {};   // inline records (small stencils)
+    unsigned char *d_inl_sl[kMaxTerms] = {};  // the same, transposed per slice
+    int32_t *d_sl_ptr[kMaxTerms] = {};        // and the slices' offsets
     int32_t *d_elems[kMaxTerms] = {};
     void *d_consts[kMaxTerms] = {};
     double *d_epart = nullptr;
@@ -262,11 +265,32 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
         e = upload(ctx, &ctx->d_inc_ptr[t], ptr, s);
         if (K <= kInlineVerts) {
             // each record carries the element's other vertex and constants
-            // (InlineRec<T, NC>: pk, other, c[NC], padded to 8 bytes)
+            // (InlineRec<T, NC>: pk, other, c[NC], padded to 8 bytes); rows
+            // in order for the explicit pass, and for the product
+            // transposed per slice of kTermSliceRows rows: slice q holds
+            // kTermSliceRows x (its rows' largest count) records, record j
+            // of row a at sl_ptr[q] + kTermSliceRows j + a % kTermSliceRows
+            // (padding records are zero and never evaluated)
             const size_t rb = inline_rec_bytes<T>(NC);
-            std::vector<unsigned char> recs(inc.size() * rb, 0);
-            for (size_t k = 0; k < inc.size(); ++k) {
-                unsigned char *r = recs.data() + k * rb;
+            std::vector<unsigned char> rows(inc.size() * rb, 0);
+            const int64_t nsl = (int64_t(nv) + kTermSliceRows - 1) / kTermSliceRows;
+            std::vector<int32_t> slp(size_t(nsl) + 1, 0);
+            for (int64_t q = 0; q < nsl; ++q) {
+                int32_t w = 0;
+                for (int64_t a = q * kTermSliceRows;
+                     a < std::min<int64_t>(nv, (q + 1) * kTermSliceRows); ++a)
+                    w = std::max(w, ptr[size_t(a) + 1] - ptr[size_t(a)]);
+                const int64_t end = int64_t(slp[size_t(q)]) + int64_t(kTermSliceRows) * w;
+                if (end > INT32_MAX) return fail(nullptr, LAD_ERR_CAPACITY, "too many element records");
+                slp[size_t(q) + 1] = int32_t(end);
+            }
+            std::vector<unsigned char> recs(size_t(slp[size_t(nsl)]) * rb, 0);
+            for (int32_t a = 0; a < nv; ++a)
+            for (int32_t k = ptr[size_t(a)]; k < ptr[size_t(a) + 1]; ++k) {
+                const int64_t j = k - ptr[size_t(a)];  // the record's place in its row
+                const int64_t slot = slp[size_t(a / kTermSliceRows)] + j * kTermSliceRows +
+                                     a % kTermSliceRows;
+                unsigned char *r = rows.data() + size_t(k) * rb;
                 const int64_t el = inc[k].e;
                 const int i = int(inc[k].pk & 3u);
                 const int32_t other = K == 2 ? b.elems[el * 2 + (1 - i)] : 0;
@@ -276,8 +300,11 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
                     const T c = T(b.consts[el * NC + q]);
                     std::memcpy(r + 8 + size_t(q) * sizeof(T), &c, sizeof(T));
                 }
+                std::memcpy(recs.data() + size_t(slot) * rb, r, rb);
             }
-            if (e == hipSuccess) e = upload(ctx, &ctx->d_inl[t], recs, s);
+            if (e == hipSuccess) e = upload(ctx, &ctx->d_inl[t], rows, s);
+            if (e == hipSuccess) e = upload(ctx, &ctx->d_inl_sl[t], recs, s);
+            if (e == hipSuccess) e = upload(ctx, &ctx->d_sl_ptr[t], slp, s);
         } else {
             std::vector<int32_t> elems(b.elems, b.elems + int64_t(b.count) * K);
             std::vector<T> consts(size_t(b.count) * size_t(NC));
@@ -314,6 +341,8 @@ TermsArgs<T> args_of(const lad_terms_ctx *ctx)
         a.t[t].inc_ptr = ctx->d_inc_ptr[t];
         a.t[t].inc = ctx->d_inc[t];
         a.t[t].inl = ctx->d_inl[t];
+        a.t[t].inl_sl = ctx->d_inl_sl[t];
+        a.t[t].sl_ptr = ctx->d_sl_ptr[t];
         a.t[t].elems = ctx->d_elems[t];
         a.t[t].consts = static_cast<const T *>(ctx->d_consts[t]);
     }

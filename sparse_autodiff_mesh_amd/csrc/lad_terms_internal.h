@@ -40,6 +40,9 @@ struct alignas(8) TermInc {
 // one copy of each element's data, which the rows of its vertices share
 // through the caches.
 constexpr int kInlineVerts = 2;
+// Rows per slice of the transposed small-stencil records (one wave reads
+// record j of 64 consecutive rows with one coalesced load).
+constexpr int kTermSliceRows = 64;
 
 // pk as in TermInc; other: the element's other vertex (two-vertex terms);
 // c: the element's constants.
@@ -68,7 +71,13 @@ struct TermData {
     const TermInc *inc;          // incident elements of each row, by element id
                                  // (terms of more than kInlineVerts vertices)
     const void *inl;             // the same as InlineRec<T, kConsts> records
-                                 // (terms of at most kInlineVerts vertices)
+                                 // (terms of at most kInlineVerts vertices),
+                                 // rows in order (the explicit pass)
+    const void *inl_sl;          // the same records transposed per slice of
+                                 // kTermSliceRows rows (the product): record
+                                 // j of row a is inl_sl[sl_ptr[a / 64] +
+                                 // 64 j + a % 64]
+    const int32_t *sl_ptr;       // [nslice + 1] first record of each slice
     const int32_t *elems;        // [ne][K] vertex ids (larger terms only)
     const T *consts;             // [ne][kConsts] (larger terms only)
 };

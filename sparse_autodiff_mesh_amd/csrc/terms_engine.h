@@ -89,21 +89,32 @@ __device__ __forceinline__ void stream_in(T *dst, const T *__restrict__ src, int
 // The incidence records [base, base + B) of row a (indices clamped into the
 // row's range, so every load is valid): position and block offsets (pk),
 // vertex ids in element order and constants.  Small stencils read them from
-// the row's own records; larger ones gather the element's vertex ids and
-// constants by element id.
-template <typename Term, typename T, int B>
-__device__ __forceinline__ void load_records(const TermData<T> &td, int32_t a, int32_t base,
-                                             int32_t p1, TermInc (&rec)[B],
+// the row's own records: rows in order, or (SLICED, the product kernel,
+// whose waves walk whole slices) the copy transposed per slice, where a
+// wave reads record j of its 64 rows with one coalesced load; larger ones
+// gather the element's vertex ids and constants by element id.
+template <typename Term, bool SLICED, typename T, int B>
+__device__ __forceinline__ void load_records(const TermData<T> &td, int32_t a, int32_t p0,
+                                             int32_t base, int32_t p1, TermInc (&rec)[B],
                                              int32_t (&vid)[B][Term::kVerts],
                                              T (&cc)[B][Term::kConsts > 0 ? Term::kConsts : 1])
 {
     constexpr int K = Term::kVerts, NC = Term::kConsts;
     if constexpr (K <= kInlineVerts) {
         using R = InlineRec<T, NC>;
-        const R *ir = static_cast<const R *>(td.inl);
         R q[B];
+        if constexpr (SLICED) {
+            // the row's records in its slice, kTermSliceRows apart
+            const R *ir = static_cast<const R *>(td.inl_sl) + td.sl_ptr[a / kTermSliceRows] +
+                          a % kTermSliceRows;
 #pragma unroll
-        for (int j = 0; j < B; ++j) q[j] = ir[min(base + j, p1 - 1)];
+            for (int j = 0; j < B; ++j)
+                q[j] = ir[int64_t(min(base + j, p1 - 1) - p0) * kTermSliceRows];
+        } else {
+            const R *ir = static_cast<const R *>(td.inl);
+#pragma unroll
+            for (int j = 0; j < B; ++j) q[j] = ir[min(base + j, p1 - 1)];
+        }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
             rec[j].e = 0;  // not needed: the record holds the element's data
@@ -211,7 +222,7 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
         int32_t vid[kTermBatch][K];
         T xv[kTermBatch][K][3];
         T cc[kTermBatch][NC > 0 ? NC : 1];
-        load_records<Term>(td, a, base, p1, rec, vid, cc);
+        load_records<Term, false>(td, a, p0, base, p1, rec, vid, cc);
 #pragma unroll
         for (int j = 0; j < kTermBatch; ++j)
 #pragma unroll
@@ -328,7 +339,7 @@ __device__ __forceinline__ void row_term_hvp(const TermData<T> &td, int32_t a,
         int32_t vid[kTermBatch][K];
         T xv[kTermBatch][K][3], vv[kTermBatch][K][3];
         T cc[kTermBatch][NC > 0 ? NC : 1];
-        load_records<Term>(td, a, base, p1, rec, vid, cc);
+        load_records<Term, true>(td, a, p0, base, p1, rec, vid, cc);
 #pragma unroll
         for (int j = 0; j < kTermBatch; ++j)
 #pragma unroll
@@ -372,9 +383,12 @@ template <typename T, bool ACC, typename... Terms>
 __global__ void __launch_bounds__(kTermsHvpThreads)
 k_terms_hvp(TermsArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
 {
+    // ranges start on a slice boundary, so each wave's 64 rows read one
+    // slice of the small-stencil records
     const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t r0 = int32_t(int64_t(A.nv) * w / gridDim.x);
-    const int32_t r1 = int32_t(int64_t(A.nv) * (w + 1) / gridDim.x);
+    const int64_t nsl = (int64_t(A.nv) + kTermSliceRows - 1) / kTermSliceRows;
+    const int32_t r0 = int32_t(nsl * w / gridDim.x * kTermSliceRows);
+    const int32_t r1 = int32_t(min(int64_t(A.nv), nsl * (w + 1) / gridDim.x * kTermSliceRows));
     for (int32_t a = r0 + int32_t(threadIdx.x); a < r1; a += kTermsHvpThreads) {
         T Y[3];
 #pragma unroll
