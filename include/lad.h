@@ -164,8 +164,14 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info);
 /*
  * Active pattern: *nnzb gets its block count; *d_row_ptr and *d_col_idx get
  * library-owned DEVICE pointers, valid until the next lad_insert_pairs or
- * lad_destroy.  Synchronises `hip_stream` (which must be the stream the
- * context's calls run on, so that pending inserts are complete).
+ * lad_destroy.  This is the pattern the values of lad_eval_energy_grad_hess
+ * are laid out in: the block CSR preallocated from the topology (with the
+ * current contacts merged in), which a caller hands on to a solver.
+ * Source: key design 3 (sparsity pattern preallocated at initialisation,
+ * derivatives written straight into it) and key design 4 (the active one
+ * of the two pattern buffers).  Synchronises `hip_stream` (which must be
+ * the stream the context's calls run on, so that pending inserts are
+ * complete).  Errors: LAD_ERR_ARG (NULL argument), LAD_ERR_HIP.
  */
 lad_status lad_get_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nnzb,
                            const int32_t **d_row_ptr, const int32_t **d_col_idx);
@@ -173,9 +179,11 @@ lad_status lad_get_pattern(lad_ctx *ctx, void *hip_stream, int64_t *nnzb,
 /*
  * Copy the active pattern into caller-owned DEVICE buffers: d_row_ptr gets
  * nv+1 entries, d_col_idx gets nnzb entries (*nnzb, which must not exceed
- * col_capacity).  Synchronises `hip_stream` to read the active buffer, then
- * copies on it and synchronises again.  Errors: LAD_ERR_ARG (NULL pointer),
- * LAD_ERR_CAPACITY (col_capacity < nnzb; nothing copied).
+ * col_capacity).  Source: key design 3 (the preallocated block CSR handed
+ * to the caller) and key design 4 (the active pattern buffer).
+ * Synchronises `hip_stream` to read the active buffer, then copies on it
+ * and synchronises again.  Errors: LAD_ERR_ARG (NULL pointer),
+ * LAD_ERR_CAPACITY (col_capacity < nnzb; nothing copied), LAD_ERR_HIP.
  */
 lad_status lad_copy_pattern(lad_ctx *ctx, void *hip_stream, int32_t *d_row_ptr,
                             int32_t *d_col_idx, int64_t col_capacity, int64_t *nnzb);
@@ -344,8 +352,17 @@ lad_status lad_insert_contacts(lad_ctx *ctx, const int32_t *d_pairs, int32_t npa
  *   npairs   0 <= npairs <= pair_capacity (0 restores the topology pattern).
  * Host errors: LAD_ERR_ARG, LAD_ERR_CAPACITY (npairs > pair_capacity); the
  * pattern is then unchanged.  Device-side checks (index out of range, i == j,
- * a patch's reserved map exceeded) keep the previous pattern and pairs
- * active and latch an error readable with lad_device_status.
+ * staging capacity exceeded, see below) keep the previous pattern and pairs
+ * active and latch an error readable with lad_device_status
+ * (LAD_ERR_PAIRS for a bad index, LAD_ERR_CAPACITY for staging).
+ * Staging capacity: the evaluation stages a group of rows' blocks on chip,
+ * so inserted blocks are limited per group as well as in total.  Row path:
+ * each chunk of up to 64 consecutive rows (lad_info.npatches chunks) holds
+ * at most 512 blocks, topology and inserted together; a chunk of the grid
+ * cloths has at most 448 topology blocks, so it takes at least 64 inserted
+ * blocks (one per pair endpoint whose partner is new to its row, three for
+ * a contact vertex, one per face vertex of a contact).  Patch path: each
+ * patch takes max(32, 1/8 of its topology blocks) inserted blocks.
  * Asynchronous; hvals buffers sized to lad_info.hvals_capacity stay valid.
  */
 lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs,

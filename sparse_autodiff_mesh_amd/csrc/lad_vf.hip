@@ -21,6 +21,14 @@
 // needs no search.  Contacts are read from the active pattern buffer (the
 // rows they touch have complete columns there); the grid walks
 // [0, nvf[active]) with a stride loop.
+//
+// Both kernels work in fp64 whatever the storage type: the positions (and
+// the direction) are widened on load and only the stored strips are rounded
+// to the context's type.  A contact whose face has been squeezed into a
+// sliver (edges of very different lengths) loses most of its significant
+// digits in the face normal and in (t0 - p) . n, which fp32 cannot afford;
+// there are only a few contacts per step, so the wider arithmetic costs
+// little next to the row kernels.
 #include <hip/hip_runtime.h>
 
 #include "contact_vf.h"
@@ -38,8 +46,8 @@ constexpr int kScan = 8;  // columns of a row matched per step
 // Vertex ids (p, t0, t1, t2) and positions of contact e.
 template <typename T>
 __device__ __forceinline__ void vf_load(const RowArgs<T> &A, int act, int32_t e,
-                                        const T *__restrict__ x, int32_t w[4], T xp[3],
-                                        T xt[3][3])
+                                        const T *__restrict__ x, int32_t w[4], double xp[3],
+                                        double xt[3][3])
 {
     w[0] = A.pat.vf[act][2 * int64_t(e)];
     const int32_t f = A.pat.vf[act][2 * int64_t(e) + 1];
@@ -47,9 +55,9 @@ __device__ __forceinline__ void vf_load(const RowArgs<T> &A, int act, int32_t e,
     for (int i = 0; i < 3; ++i) w[1 + i] = A.pat.faces[3 * int64_t(f) + i];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-        xp[c] = x[int64_t(w[0]) * 3 + c];
+        xp[c] = double(x[int64_t(w[0]) * 3 + c]);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) xt[i][c] = x[int64_t(w[1 + i]) * 3 + c];
+        for (int i = 0; i < 3; ++i) xt[i][c] = double(x[int64_t(w[1 + i]) * 3 + c]);
     }
 }
 
@@ -64,7 +72,7 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
     for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
          e += int32_t(gridDim.x) * kVfThreads) {
         int32_t w[4];
-        T xp[3], xt[3][3];
+        double xp[3], xt[3][3];
         vf_load(A, act, e, x, w, xp, xt);
         // the four rows' block offsets of the contact's four vertices: the
         // rows are scanned kScan columns at a time, all four rows' loads of a
@@ -103,33 +111,35 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
 #pragma unroll
         for (int li = 0; li < 4; ++li) L[li] = A.vf_eval + (4 * int64_t(e) + li) * kVfStrip;
         const int region = vf_region(xp, xt[0], xt[1], xt[2]);
-        Dual2<T, 9> z[9];
+        Dual2<double, 9> z[9];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
-            for (int c = 0; c < 3; ++c) z[3 * i + c] = Dual2<T, 9>::var(xt[i][c] - xp[c], 3 * i + c);
-        const Dual2<T, 9> d = vf_distance(z, region);
-        if (!(d.v < A.dhat)) {  // outside the barrier's support: an all-zero term
+            for (int c = 0; c < 3; ++c)
+                z[3 * i + c] = Dual2<double, 9>::var(xt[i][c] - xp[c], 3 * i + c);
+        const Dual2<double, 9> d = vf_distance(z, region);
+        const double dhat = double(A.dhat);
+        if (!(d.v < dhat)) {  // outside the barrier's support: an all-zero term
 #pragma unroll
             for (int li = 0; li < 4; ++li)
                 for (int c = 0; c < kVfStrip; ++c) L[li][c] = T(0);
             continue;
         }
-        const Dual2<T, 9> en = barrier_of_distance(d, A.kappa, A.dhat);
+        const Dual2<double, 9> en = barrier_of_distance(d, double(A.kappa), dhat);
         // energy in the contact vertex's strip; gradient: d/dt_i = d/dz_i,
         // d/dp = -sum_i d/dz_i
-        L[0][0] = en.v;
+        L[0][0] = T(en.v);
 #pragma unroll
         for (int i = 0; i < 3; ++i) L[1 + i][0] = T(0);
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
-            T gp = T(0);
+            double gp = 0.0;
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 gp -= en.g[3 * i + c];
-                L[1 + i][1 + c] = en.g[3 * i + c];
+                L[1 + i][1 + c] = T(en.g[3 * i + c]);
             }
-            L[0][1 + c] = gp;
+            L[0][1 + c] = T(gp);
         }
         // Hessian rows over the columns (p, t0, t1, t2) x coordinate:
         //   (t_i, t_j) = Hz_ij,  (t_i, p) = -sum_j Hz_ij,
@@ -138,26 +148,26 @@ k_vf_eval(RowArgs<T> A, const T *__restrict__ x)
         for (int r = 0; r < 3; ++r)
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
-                T pp = T(0);
+                double pp = 0.0;
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
-                    T pj = T(0);
+                    double pj = 0.0;
 #pragma unroll
                     for (int i = 0; i < 3; ++i) pj -= en.hess(3 * i + r, 3 * j + c);
-                    L[0][kVfHessOff + 12 * r + 3 * (1 + j) + c] = pj;
+                    L[0][kVfHessOff + 12 * r + 3 * (1 + j) + c] = T(pj);
                     pp -= pj;
                 }
-                L[0][kVfHessOff + 12 * r + c] = pp;
+                L[0][kVfHessOff + 12 * r + c] = T(pp);
 #pragma unroll
                 for (int i = 0; i < 3; ++i) {
-                    T ip = T(0);
+                    double ip = 0.0;
 #pragma unroll
                     for (int j = 0; j < 3; ++j) {
-                        const T h = en.hess(3 * i + r, 3 * j + c);
-                        L[1 + i][kVfHessOff + 12 * r + 3 * (1 + j) + c] = h;
+                        const double h = en.hess(3 * i + r, 3 * j + c);
+                        L[1 + i][kVfHessOff + 12 * r + 3 * (1 + j) + c] = T(h);
                         ip -= h;
                     }
-                    L[1 + i][kVfHessOff + 12 * r + c] = ip;
+                    L[1 + i][kVfHessOff + 12 * r + c] = T(ip);
                 }
             }
     }
@@ -175,41 +185,43 @@ k_vf_hvp(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ u, const C
     for (int32_t e = int32_t(blockIdx.x * kVfThreads + threadIdx.x); e < n;
          e += int32_t(gridDim.x) * kVfThreads) {
         int32_t w[4];
-        T xp[3], xt[3][3], up[3], ut[3][3];
+        double xp[3], xt[3][3], up[3], ut[3][3];
         vf_load(A, act, e, x, w, xp, xt);
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
-            up[c] = u[int64_t(w[0]) * 3 + c];
+            up[c] = double(u[int64_t(w[0]) * 3 + c]);
 #pragma unroll
-            for (int i = 0; i < 3; ++i) ut[i][c] = u[int64_t(w[1 + i]) * 3 + c];
+            for (int i = 0; i < 3; ++i) ut[i][c] = double(u[int64_t(w[1 + i]) * 3 + c]);
         }
 #pragma unroll
         for (int li = 0; li < 4; ++li) A.vf_ids[4 * int64_t(e) + li] = w[li];
         T *L = A.vf_hvp + 4 * int64_t(e) * kVfHvpStrip;
         const int region = vf_region(xp, xt[0], xt[1], xt[2]);
         // z_i = t_i - p seeded with the matching direction u_(t_i) - u_p
-        DualHv<T, 9> z[9];
+        DualHv<double, 9> z[9];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int c = 0; c < 3; ++c)
-                z[3 * i + c] = DualHv<T, 9>::var(xt[i][c] - xp[c], 3 * i + c, ut[i][c] - up[c]);
-        const DualHv<T, 9> d = vf_distance(z, region);
-        if (!(d.v < A.dhat)) {
+                z[3 * i + c] =
+                    DualHv<double, 9>::var(xt[i][c] - xp[c], 3 * i + c, ut[i][c] - up[c]);
+        const DualHv<double, 9> d = vf_distance(z, region);
+        const double dhat = double(A.dhat);
+        if (!(d.v < dhat)) {
             for (int c = 0; c < 4 * kVfHvpStrip; ++c) L[c] = T(0);
             continue;
         }
-        const DualHv<T, 9> en = barrier_of_distance(d, A.kappa, A.dhat);
+        const DualHv<double, 9> en = barrier_of_distance(d, double(A.kappa), dhat);
         // gt = Hz (u_t - u_p) in z; mapped as the gradient is
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
-            T yp = T(0);
+            double yp = 0.0;
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 yp -= en.gt[3 * i + c];
-                L[(1 + i) * kVfHvpStrip + c] = en.gt[3 * i + c];
+                L[(1 + i) * kVfHvpStrip + c] = T(en.gt[3 * i + c]);
             }
-            L[c] = yp;
+            L[c] = T(yp);
         }
 #pragma unroll
         for (int li = 0; li < 4; ++li) L[li * kVfHvpStrip + 3] = T(0);

@@ -28,3 +28,14 @@ def host_input(a, dtype):
 
 def log_case(**kw):
     print("CASE " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def row_blocks(row_ptr, rows):
+    """Indices of every block of the given block rows of a CSR pattern (for
+    checking a subset of rows on its own)."""
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    starts = row_ptr[rows]
+    lens = row_ptr[rows + 1] - starts
+    first = np.cumsum(np.concatenate([[0], lens[:-1]]))
+    return np.repeat(starts - first, lens) + np.arange(int(lens.sum()))

@@ -1,7 +1,8 @@
 """Parity at the full benchmark sizes, in the configuration bench.py times
 (default library options; fp32): the 1000 x 1000 cloth, the 512 x 512
-symmetric-Dirichlet face grid (eval and HVP), and one step of the 1000 x
-1000 cloth with 20,000 contact pairs.  The oracle evaluates each whole
+symmetric-Dirichlet face grid (eval and HVP), and the 1000 x 1000 cloth
+with 20,000 fresh contact pairs per step over three steps and a final
+insert of nothing.  The oracle evaluates each whole
 problem on the host (fp32-rounded inputs, fp64 arithmetic); patterns must
 match bit for bit and values within the fp32 tolerance."""
 import numpy as np
@@ -10,7 +11,7 @@ import pytest
 import oracle
 from sparse_autodiff_mesh_amd import inputs
 
-from gpu_util import TOL, dev, host_input, log_case, rel
+from gpu_util import TOL, dev, host_input, log_case, rel, row_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -65,21 +66,59 @@ def test_faces_512_eval_and_hvp(lad):
     L.close()
 
 
-def test_cloth_1000_with_pairs(lad):
+def test_cloth_1000_pair_steps(lad):
+    """Contact steps at full size: fresh pairs at steps 0, 1 and 2 (the two
+    pattern buffers alternate: 1, 2, 1, so each is written over again and
+    the previous step's pairs must be gone), then an insert of nothing,
+    which restores the topology pattern.  Every step: the pattern bit for
+    bit, E, g, H and H v within the fp32 tolerance over the whole arrays,
+    and over the rows the pairs touch alone (their blocks, g and y), where
+    an error confined to the contact code would otherwise hide among the
+    seven million topology blocks."""
     import torch
-    log_case(test="full_pairs1000")
+    log_case(test="full_pairs1000_steps")
     m = inputs.cloth(1000)
     P = int(round(0.02 * m.nv))
     dhat = 0.5 * m.h
+    kappa = inputs.BARRIER_KAPPA
     L = lad.Lad(m.nv, dtype="f32",
-                **lad.mesh_terms(m, pair_capacity=P, kappa=inputs.BARRIER_KAPPA, dhat=dhat))
-    pairs, x = inputs.contact_pairs(m, m.x, step=0)
-    L.insert_pairs(torch.tensor(pairs, dtype=torch.int32, device="cuda"))
-    x_h = host_input(x, "f32")
+                **lad.mesh_terms(m, pair_capacity=P, kappa=kappa, dhat=dhat))
+    assert L.get_info()["eval_path"] == lad.LAD_PATH_ROWS
+    v_h = host_input(inputs.hvp_direction(m.nv), "f32")
+    tol = TOL["f32"]
+    for step in range(3):
+        log_case(test="full_pairs1000_steps", step=step)
+        pairs, x = inputs.contact_pairs(m, m.x, step=step)
+        L.insert_pairs(torch.tensor(pairs, dtype=torch.int32, device="cuda"))
+        x_h = host_input(x, "f32")
+        E, g, H, rp, ci = run(L, x_h)
+        y = L.hvp(dev(x_h, "f32"), dev(v_h, "f32"))
+        torch.cuda.synchronize()
+        assert L.device_status() == 0
+        info = L.get_info()
+        assert info["active_buffer"] == 1 + step % 2
+        assert info["nnzb_active"] == 7032002 and info["npairs_active"] == P
+        prob = oracle.problem_from_mesh(m, pairs=pairs, kappa=kappa, dhat=dhat, f32=True)
+        orp, oci = oracle.pattern(prob)
+        assert np.array_equal(rp, orp), "row_ptr differs"
+        assert np.array_equal(ci, oci), "col_idx differs"
+        Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+        yo = oracle.bsr_spmv(orp, oci, Ho, v_h)
+        Hg, yg = H[: oci.size], y.cpu().numpy()
+        assert rel([E], [Eo]) <= tol, (E, Eo)
+        assert rel(g, go) <= tol
+        assert rel(Hg, Ho) <= tol
+        assert rel(yg, yo) <= tol
+        rows = np.unique(pairs.reshape(-1))
+        blk = row_blocks(orp, rows)
+        assert rel(Hg[blk], Ho[blk]) <= tol, rel(Hg[blk], Ho[blk])
+        assert rel(g[rows], go[rows]) <= tol, rel(g[rows], go[rows])
+        assert rel(yg[rows], yo[rows]) <= tol, rel(yg[rows], yo[rows])
+        del H, Hg, Ho
+    L.insert_pairs(None)
+    x_h = host_input(m.x, "f32")
     res = run(L, x_h)
-    assert L.device_status() == 0
-    assert L.get_info()["nnzb_active"] == 7032002
-    prob = oracle.problem_from_mesh(m, pairs=pairs, kappa=inputs.BARRIER_KAPPA, dhat=dhat,
-                                    f32=True)
-    compare(L, prob, x_h, res)
+    assert L.get_info()["active_buffer"] == 0
+    assert res[3][-1] == 6992002
+    compare(L, oracle.problem_from_mesh(m, f32=True), x_h, res)
     L.close()

@@ -6,7 +6,7 @@ import pytest
 import oracle
 from sparse_autodiff_mesh_amd import inputs
 
-from gpu_util import TOL, dev, host_input, log_case, rel
+from gpu_util import TOL, dev, host_input, log_case, rel, row_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +122,81 @@ def test_rows_with_many_inserted_columns(lad, dtype):
     y = L.hvp(dev(x_h, dtype), dev(v_h, dtype))
     torch.cuda.synchronize()
     assert rel(y.cpu().numpy(), oracle.bsr_spmv(orp, oci, Ho, v_h)) <= TOL[dtype]
+    L.close()
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_rows_with_many_inserted_columns_and_faces(lad, dtype):
+    """Row path with the face term on: hubs paired with 7, 5, 4 and 1
+    vertices two or three grid steps away (the barrier support is 4h, so no
+    vertex moves and the faces stay regular).  A row with more than 4
+    inserted columns is evaluated whole by the touched-row kernel, which
+    then adds each face's off-diagonal blocks at slots found in the active
+    row; rows with fewer take the main kernel's shifted placement.  E, g, H
+    and H v against the oracle, also over the hubs' rows alone."""
+    import torch
+    log_case(test="pairs_many_inserted_faces", dtype=dtype)
+    m = inputs.cloth(20)
+    n = m.n
+    dhat = 4.0 * m.h
+    L = lad.Lad(m.nv, dtype=dtype, path="rows",
+                **lad.mesh_terms(m, faces=True, pair_capacity=32, kappa=KAPPA, dhat=dhat))
+    hubs = {5 * n + 5: [5 * n + 7, 5 * n + 8, 7 * n + 5, 8 * n + 5, 7 * n + 7, 3 * n + 5,
+                        5 * n + 2],
+            12 * n + 12: [12 * n + 14, 12 * n + 15, 14 * n + 12, 15 * n + 12, 14 * n + 14],
+            4 * n + 14: [4 * n + 16, 6 * n + 14, 6 * n + 16, 2 * n + 14],
+            16 * n + 4: [16 * n + 6]}
+    pairs = np.array([(a, b) for a, bs in hubs.items() for b in bs], dtype=np.int32)
+    assert len(np.unique(pairs[:, 1])) == len(pairs)
+    L.insert_pairs(pairs_dev(pairs))
+    assert L.device_status() == 0
+    prob, orp, oci, x_h = check_step(lad, L, m, dtype, pairs, m.x, dhat, faces=True)
+    for a, bs in hubs.items():
+        assert np.diff(orp)[a] == 7 + len(bs)   # 7 topology blocks + the new ones
+        d = np.linalg.norm(x_h[a] - x_h[np.array(bs)], axis=1)
+        assert np.all(d < dhat)
+    E, g, H = L.eval(dev(x_h, dtype))
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    v_h = host_input(inputs.hvp_direction(m.nv), dtype)
+    y = L.hvp(dev(x_h, dtype), dev(v_h, dtype))
+    torch.cuda.synchronize()
+    yo = oracle.bsr_spmv(orp, oci, Ho, v_h)
+    assert rel(y.cpu().numpy(), yo) <= TOL[dtype]
+    rows = np.array(list(hubs), dtype=np.int64)
+    blk = row_blocks(orp, rows)
+    Hg = H.cpu().numpy()[: oci.size]
+    assert rel(Hg[blk], Ho[blk]) <= TOL[dtype], rel(Hg[blk], Ho[blk])
+    assert rel(g.cpu().numpy()[rows], go[rows]) <= TOL[dtype]
+    assert rel(y.cpu().numpy()[rows], yo[rows]) <= TOL[dtype]
+    L.close()
+
+
+def test_chunk_staging_overflow_rejected(lad):
+    """Row path: the rows of one 64-row chunk share a fixed staging area of
+    512 blocks (topology and inserted).  An insert that puts 128 new blocks
+    into chunk 0 of a 20 x 20 cloth (rows 0..63 each paired with two far
+    vertices; the chunk's topology takes 395 blocks) is rejected on the device
+    with LAD_ERR_CAPACITY, the previous pairs stay active and evaluate as before,
+    and the next valid insert is taken."""
+    log_case(test="pairs_chunk_overflow")
+    m = inputs.cloth(20)
+    L, dhat = make(lad, m, "f64", 160, path="rows")
+    good, x = inputs.contact_pairs(m, m.x, step=1, frac=8 / m.nv)
+    L.insert_pairs(pairs_dev(good))
+    assert L.device_status() == 0
+    check_step(lad, L, m, "f64", good, x, dhat)
+    orp, _ = oracle.pattern(oracle.problem_from_mesh(m))
+    assert orp[64] - orp[0] + 128 > 512
+    over = np.array([(r, 200 + 2 * r + k) for r in range(64) for k in range(2)], dtype=np.int32)
+    L.insert_pairs(pairs_dev(over))
+    assert L.device_status() == lad.LAD_ERR_CAPACITY
+    assert L.get_info()["npairs_active"] == len(good)
+    check_step(lad, L, m, "f64", good, x, dhat)
+    # within the limit: 64 more blocks into chunk 0 at most
+    fits = over[::2][:40]
+    L.insert_pairs(pairs_dev(fits))
+    assert L.device_status() == 0
+    check_step(lad, L, m, "f64", fits, m.x, dhat)
     L.close()
 
 

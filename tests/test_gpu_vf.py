@@ -4,7 +4,10 @@ bit (topology U the contacts' (v, t) and (t, v) blocks U the pairs' blocks,
 sorted), E, g, H and H v within gpu_util.TOL.  Contacts come from
 inputs.vf_contacts (every closest-point region occurs) or, where the face
 energy is on, are chosen between a vertex and a face two grid steps away so
-that no vertex moves."""
+that no vertex moves.  Pairs are applied on top of the contacts' positions
+as generated, so they drag contact vertices and contact faces' vertices
+wherever their partners land; sliver_pairs drags face vertices on purpose
+so that active contacts sit on sliver triangles."""
 import numpy as np
 import pytest
 
@@ -12,7 +15,7 @@ import oracle
 from oracle import newton_cg as ncg
 from sparse_autodiff_mesh_amd import inputs
 
-from gpu_util import TOL, dev, host_input, log_case, rel
+from gpu_util import TOL, dev, host_input, log_case, rel, row_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -58,21 +61,56 @@ def check(L, m, dtype, x, dhat, vf, pairs=None, faces=False, hvp=True, mesh_term
     return prob, orp, oci, x_h
 
 
-def disjoint_pairs(m, x0, vf, step):
-    """Generated pairs that share no vertex with a contact (its vertex or its
-    face's), with their partners placed as the generator places them; the
-    other pairs are dropped, so no contact is reshaped.  (A face vertex
-    dragged across the grid leaves a sliver triangle whose face distance
-    cancels heavily in fp32.)"""
-    pairs, xp = inputs.contact_pairs(m, m.x, step=step)
+def sliver_pairs(m, x0, vf, dhat, stretch, seed, skip=()):
+    """Pairs that drag a vertex of contact faces so that the contact sits on a
+    sliver triangle.  For every second contact, one vertex t of its face is
+    paired with a far vertex a and placed next to it (distance U(0.1, 1)
+    dhat along a random direction, as the pair generator places partners):
+    "tall" contacts take a along the face's height through t, `stretch`
+    times the height out, so the face becomes a needle `stretch` times
+    taller than its base; "flat" contacts take a along the line of the
+    opposite edge, so the face becomes nearly degenerate (its three vertices
+    almost collinear).  Only drags after which the contact is still active
+    (the oracle's term is non-zero) are kept.  Vertices in `skip` and the
+    contact vertices never move or serve as a.  Returns (pairs, x, counts)."""
+    n = m.n
+    rng = np.random.default_rng(seed)
     used = np.zeros(m.nv, bool)
     used[vf[:, 0]] = True
-    used[m.faces[vf[:, 1]].reshape(-1)] = True
-    keep = ~(used[pairs[:, 0]] | used[pairs[:, 1]])
-    pairs = pairs[keep]
+    used[np.asarray(list(skip), dtype=np.int64)] = True
     x = x0.copy()
-    x[pairs[:, 1]] = xp[pairs[:, 1]]
-    return pairs, x
+    pairs = []
+    counts = {"tall": 0, "flat": 0}
+    for k, (v, f) in enumerate(vf[::2]):
+        tri = m.faces[f]
+        i = int(rng.integers(3))
+        t, o0, o1 = int(tri[i]), int(tri[(i + 1) % 3]), int(tri[(i + 2) % 3])
+        if used[t]:
+            continue
+        kind = "tall" if k % 2 == 0 else "flat"
+        gt, g0, g1 = (np.array([p % n, p // n], float) for p in (t, o0, o1))
+        if kind == "tall":
+            tgt = 0.5 * (g0 + g1) + stretch * (gt - 0.5 * (g0 + g1))
+        else:
+            tgt = g1 + stretch * (g1 - g0)
+        ia, ja = int(round(tgt[0])), int(round(tgt[1]))
+        if not (0 <= ia < n and 0 <= ja < n):
+            continue
+        a = ja * n + ia
+        if used[a] or a in tri or inputs.grid_adjacent(n, a, t):
+            continue
+        d = dhat * (0.1 + 0.9 * rng.random())
+        u = rng.normal(size=3)
+        keep_t = x[t].copy()
+        x[t] = x[a] + d * u / np.linalg.norm(u)
+        r = x[[v, *tri]].astype(np.float32).astype(np.float64)
+        if not oracle.vf_local(r[0], r[1], r[2], r[3], KAPPA, dhat)[0] > 0.0:
+            x[t] = keep_t
+            continue
+        used[a] = used[t] = True
+        pairs.append((a, t))
+        counts[kind] += 1
+    return np.array(pairs, dtype=np.int32).reshape(-1, 2), x, counts
 
 
 def contact_terms_only(m, x, vf, dhat, dtype):
@@ -116,7 +154,7 @@ def test_pairs_and_contacts_together(lad, dtype):
     m = inputs.cloth(40)
     dhat = 0.5 * m.h
     vf, x0 = inputs.vf_contacts(m, m.x, 1, dhat=dhat)
-    pairs, x = disjoint_pairs(m, x0, vf, 2)
+    pairs, x = inputs.contact_pairs(m, x0, step=2)
     # plus pairs that join a contact vertex to a neighbour, two vertices of
     # a contact face, and a contact vertex to another contact's face vertex
     # (at their current positions; those pair terms may be inactive)
@@ -257,33 +295,95 @@ def test_newton_cg_with_contacts(lad, dtype, iters):
     L.close()
 
 
+@pytest.mark.parametrize("dtype,mesh_terms", [("f32", False), ("f32", True), ("f64", True)])
+def test_contacts_on_sliver_faces(lad, dtype, mesh_terms):
+    """Contacts whose faces pairs have squeezed into slivers (needles 12
+    times taller than their base, and nearly collinear triangles), with the
+    generated pairs of the step on top; the contact terms are evaluated in
+    fp64 from the stored inputs whatever the dtype, so fp32 meets the same
+    tolerance as on regular faces.  Also checked over the touched rows
+    alone, where the contact terms are the largest share."""
+    log_case(test="vf_slivers", dtype=dtype, mesh_terms=mesh_terms)
+    m = inputs.cloth(48)
+    dhat = 0.5 * m.h
+    vf, x0 = inputs.vf_contacts(m, m.x, 3, dhat=dhat)
+    gen, x1 = inputs.contact_pairs(m, x0, step=4)
+    sl, x, counts = sliver_pairs(m, x1, vf, dhat, 12.0, seed=7, skip=gen.reshape(-1))
+    assert counts["tall"] >= 3 and counts["flat"] >= 1, counts
+    pairs = np.concatenate([gen, sl])
+    L, _ = make(lad, m, dtype, len(vf), pair_cap=len(pairs), dhat=dhat, mesh_terms=mesh_terms)
+    L.insert_contacts(pairs=idev(pairs), vf=idev(vf))
+    assert L.device_status() == 0
+    prob, orp, oci, x_h = check(L, m, dtype, x, dhat, vf, pairs=pairs, mesh_terms=mesh_terms)
+    E, g, H = L.eval(dev(x_h, dtype))
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    rows = np.unique(np.concatenate([vf[:, 0], m.faces[vf[:, 1]].reshape(-1), pairs.reshape(-1)]))
+    blk = row_blocks(orp, rows)
+    Hg = H.cpu().numpy()[: oci.size]
+    assert rel(Hg[blk], Ho[blk]) <= TOL[dtype], rel(Hg[blk], Ho[blk])
+    assert rel(g.cpu().numpy()[rows], go[rows]) <= TOL[dtype]
+    L.close()
+
+
 def test_cloth_1000_with_contacts(lad):
     """The 1000 x 1000 cloth in fp32 with 20,000 vertex-face contacts and
-    the generated pairs that share no vertex with them (about 17,000) in
-    one insert, checked against the whole oracle evaluation."""
+    20,000 generated pairs applied on top of the contacts' positions (they
+    drag contact vertices and face vertices where they land), plus pairs
+    that squeeze contact faces into slivers, over two steps (both pattern
+    buffers) and a final insert of nothing.  Every step: the pattern bit for
+    bit, E, g, H and H v over the whole arrays and over the touched rows
+    alone."""
     import torch
     log_case(test="vf_full1000")
     m = inputs.cloth(1000)
     Q = int(round(0.02 * m.nv))
     dhat = 0.5 * m.h
-    vf, x0 = inputs.vf_contacts(m, m.x, 0, dhat=dhat)
-    pairs, x1 = disjoint_pairs(m, x0, vf, 0)
-    L, _ = make(lad, m, "f32", Q, pair_cap=len(pairs), dhat=dhat)
-    L.insert_contacts(pairs=idev(pairs), vf=idev(vf))
-    assert L.device_status() == 0
-    x_h = host_input(x1, "f32")
-    E, g, H = L.eval(dev(x_h, "f32"))
+    tol = TOL["f32"]
     v_h = host_input(inputs.hvp_direction(m.nv), "f32")
-    y = L.hvp(dev(x_h, "f32"), dev(v_h, "f32"))
+    L = None
+    for step in range(2):
+        vf, x0 = inputs.vf_contacts(m, m.x, step, dhat=dhat)
+        gen, x1 = inputs.contact_pairs(m, x0, step=step)
+        sl, x, counts = sliver_pairs(m, x1, vf, dhat, 40.0, seed=step, skip=gen.reshape(-1))
+        assert counts["tall"] >= 100 and counts["flat"] >= 20, counts
+        pairs = np.concatenate([gen, sl])
+        if L is None:
+            L, _ = make(lad, m, "f32", Q, pair_cap=len(pairs) + 4096, dhat=dhat)
+        log_case(test="vf_full1000", step=step, pairs=len(pairs), slivers=counts)
+        L.insert_contacts(pairs=idev(pairs), vf=idev(vf))
+        x_h = host_input(x, "f32")
+        E, g, H = L.eval(dev(x_h, "f32"))
+        y = L.hvp(dev(x_h, "f32"), dev(v_h, "f32"))
+        torch.cuda.synchronize()
+        assert L.device_status() == 0
+        assert L.get_info()["active_buffer"] == 1 + step
+        prob = oracle.problem_from_mesh(m, pairs=pairs, vf=vf, kappa=KAPPA, dhat=dhat, f32=True)
+        orp, oci = oracle.pattern(prob)
+        rp, ci = L.pattern()
+        assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+        Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+        yo = oracle.bsr_spmv(orp, oci, Ho, v_h)
+        Hg, gg, yg = H.cpu().numpy()[: oci.size], g.cpu().numpy(), y.cpu().numpy()
+        assert rel([E.item()], [Eo]) <= tol
+        assert rel(gg, go) <= tol
+        assert rel(Hg, Ho) <= tol
+        assert rel(yg, yo) <= tol
+        rows = np.unique(np.concatenate([vf[:, 0], m.faces[vf[:, 1]].reshape(-1),
+                                         pairs.reshape(-1)]))
+        blk = row_blocks(orp, rows)
+        assert rel(Hg[blk], Ho[blk]) <= tol, rel(Hg[blk], Ho[blk])
+        assert rel(gg[rows], go[rows]) <= tol, rel(gg[rows], go[rows])
+        assert rel(yg[rows], yo[rows]) <= tol, rel(yg[rows], yo[rows])
+        del H, Hg, Ho
+    L.insert_contacts()
+    E, g, H = L.eval(dev(host_input(m.x, "f32"), "f32"))
     torch.cuda.synchronize()
-    prob = oracle.problem_from_mesh(m, pairs=pairs, vf=vf, kappa=KAPPA, dhat=dhat, f32=True)
+    assert L.get_info()["active_buffer"] == 0
+    prob = oracle.problem_from_mesh(m, kappa=KAPPA, dhat=dhat, f32=True)
     orp, oci = oracle.pattern(prob)
     rp, ci = L.pattern()
     assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
-    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
-    tol = TOL["f32"]
-    assert rel([E.item()], [Eo]) <= tol
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, host_input(m.x, "f32"))
     assert rel(g.cpu().numpy(), go) <= tol
     assert rel(H.cpu().numpy()[: oci.size], Ho) <= tol
-    assert rel(y.cpu().numpy(), oracle.bsr_spmv(orp, oci, Ho, v_h)) <= tol
     L.close()
