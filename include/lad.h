@@ -39,8 +39,9 @@
  * the previous pattern active and is reported by lad_device_status.
  *
  * Streams: every call enqueues on the caller's HIP stream (hipStream_t passed
- * as void*; NULL is the null stream).  lad_eval_energy_grad_hess, lad_hvp and
- * lad_insert_pairs never synchronise with the host.  lad_build_pattern,
+ * as void*; NULL is the null stream).  lad_eval_energy_grad_hess (and its
+ * _noalloc variant), lad_hvp and lad_insert_pairs never synchronise with
+ * the host.  lad_build_pattern,
  * lad_get_pattern, lad_get_info and lad_device_status synchronise that stream.
  *
  * Threading: one context must not be used by two host threads at once.
@@ -212,6 +213,35 @@ lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x,
                                      double *d_energy, void *d_grad,
                                      void *d_hvals, int64_t hvals_capacity_blocks,
                                      void *hip_stream);
+
+/*
+ * lad_eval_energy_grad_hess for callers that cannot allocate device memory:
+ * code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same kernels and the same results, bit for bit; the
+ * per-workgroup partial energies (the evaluation's only scratch) go to a
+ * static device array of the library instead of the context's buffer.  The
+ * call makes no hipMalloc, hipFree or other allocation; its first call on a
+ * device looks up that device's copy of the array.
+ *   Arguments, layout and ownership as lad_eval_energy_grad_hess.  The
+ *   context's device must be the current device.
+ *   Limit: at most 32768 partial energies (256 KiB): one per workgroup of
+ *   the evaluation's launches, about 2,100 for a row-path context on MI355X
+ *   (plus one per 256 contact incidence entries), one per patch on the patch
+ *   path.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (two streams, two host threads,
+ * two processes' contexts do not share it) race and may return a wrong
+ * energy.  Order them on one stream.  No slot is read before the call
+ * writes it, so nothing needs clearing between calls.
+ * Errors: as lad_eval_energy_grad_hess, plus LAD_ERR_CAPACITY (more partial
+ * energies than the array holds), LAD_ERR_STATE (vertex-face capacity, whose
+ * per-contact strips are context scratch; or another device current),
+ * LAD_ERR_HIP.  Nothing is enqueued on error.
+ */
+lad_status lad_eval_energy_grad_hess_noalloc(lad_ctx *ctx, const void *d_x,
+                                             double *d_energy, void *d_grad,
+                                             void *d_hvals, int64_t hvals_capacity_blocks,
+                                             void *hip_stream);
 
 /*
  * Matrix-free Hessian-vector product y = H(x) v, H never stored.

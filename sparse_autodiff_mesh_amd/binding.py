@@ -81,7 +81,7 @@ LAD_CG_CONVERGED, LAD_CG_NEG_CURVATURE, LAD_CG_MAX_ITERS = 0, 1, 2
 
 EXPORTS = [
     "lad_build_pattern", "lad_get_info", "lad_get_pattern", "lad_copy_pattern",
-    "lad_eval_energy_grad_hess", "lad_hvp", "lad_newton_cg", "lad_insert_pairs",
+    "lad_eval_energy_grad_hess", "lad_eval_energy_grad_hess_noalloc", "lad_hvp", "lad_newton_cg", "lad_insert_pairs",
     "lad_insert_contacts",
     "lad_jacobian_pattern", "lad_copy_jacobian_pattern", "lad_residual_jacobian",
     "lad_gauss_newton_product",
@@ -108,6 +108,8 @@ def lib():
                                        ctypes.POINTER(ctypes.c_int64)]
         L.lad_eval_energy_grad_hess.argtypes = [_vp, _vp, _vp, _vp, _vp,
                                                 ctypes.c_int64, _vp]
+        L.lad_eval_energy_grad_hess_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp,
+                                                        ctypes.c_int64, _vp]
         L.lad_hvp.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.lad_newton_cg.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_double,
                                     ctypes.POINTER(lad_cg_stats), _vp]
@@ -179,6 +181,13 @@ def lad_copy_pattern(ctx, stream, d_row_ptr, d_col_idx, col_capacity):
 def lad_eval_energy_grad_hess(ctx, d_x, d_energy, d_grad, d_hvals, capacity, stream=None):
     _check(lib().lad_eval_energy_grad_hess(ctx, _vp(d_x), _vp(d_energy), _vp(d_grad),
                                            _vp(d_hvals), int(capacity), _vp(stream)), ctx)
+
+
+def lad_eval_energy_grad_hess_noalloc(ctx, d_x, d_energy, d_grad, d_hvals, capacity,
+                                      stream=None):
+    _check(lib().lad_eval_energy_grad_hess_noalloc(ctx, _vp(d_x), _vp(d_energy), _vp(d_grad),
+                                                   _vp(d_hvals), int(capacity), _vp(stream)),
+           ctx)
 
 
 def lad_hvp(ctx, d_x, d_v, d_y, stream=None):

@@ -23,7 +23,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["lad_eval.hip", "lad_rows.hip", "lad_pattern.hip", "lad_insert.hip",
-               "lad_solve.hip", "lad_jacobian.hip", "lad_vf.hip", "lad_terms.hip"]
+               "lad_solve.hip", "lad_jacobian.hip", "lad_vf.hip", "lad_terms.hip",
+               "lad_noalloc.hip"]
 CXX_SOURCES = ["lad_api.cpp", "lad_patch.cpp", "lad_terms_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",

@@ -19,6 +19,7 @@
 using namespace lad;
 
 struct lad_ctx {
+    int32_t device = 0;              // HIP device the context was built on
     int32_t nv = 0;
     lad_dtype dtype = LAD_F32;
     int32_t es = 4;
@@ -300,11 +301,18 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     return a;
 }
 
+// Partial energies one evaluation writes: one per workgroup of its launches.
+int32_t eval_nparts(const lad_ctx *ctx)
+{
+    return (ctx->row_mode ? ctx->grid_eval : ctx->npatch) + ctx->pair_blocks;
+}
+
 template <typename T>
 hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, void *hv,
-                        hipStream_t s)
+                        double *parts, hipStream_t s)
 {
-    // Partial energies go to d_epart; one small launch sums them when the
+    // Every workgroup stores its partial energy at parts[...] (no slot is
+    // read before it is written); one small launch sums them when the
     // caller asked for the energy.
     hipError_t e = hipSuccess;
     int32_t nparts = 0;
@@ -315,28 +323,28 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
         if (e == hipSuccess)
             e = launch_eval_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
                                     static_cast<T *>(g), static_cast<T *>(hv),
-                                    EnergySink{ctx->d_epart, 0}, ctx->grid_eval, s);
+                                    EnergySink{parts, 0}, ctx->grid_eval, s);
         nparts = ctx->grid_eval;
         // rows touched by pairs, one thread each
         if (e == hipSuccess && ctx->pair_blocks > 0) {
             e = launch_eval_pair_rows<T>(row_args<T>(ctx), static_cast<const T *>(x),
                                          static_cast<T *>(g), static_cast<T *>(hv),
-                                         EnergySink{ctx->d_epart, ctx->grid_eval},
+                                         EnergySink{parts, ctx->grid_eval},
                                          ctx->pair_blocks, s);
             nparts += ctx->pair_blocks;
         }
     } else {
         const PatchArgs<T> a = patch_args<T>(ctx);
         e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g), static_cast<T *>(hv),
-                           EnergySink{ctx->d_epart, 0}, ctx->det, ctx->lds_eval, s);
+                           EnergySink{parts, 0}, ctx->det, ctx->lds_eval, s);
         if (e == hipSuccess && ctx->pair_blocks > 0)
             e = launch_pairs_eval<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
                                      static_cast<T *>(g), static_cast<T *>(hv),
-                                     EnergySink{ctx->d_epart, ctx->npatch}, ctx->pair_blocks,
+                                     EnergySink{parts, ctx->npatch}, ctx->pair_blocks,
                                      T(ctx->kappa), T(ctx->dhat), s);
         nparts = ctx->npatch + ctx->pair_blocks;
     }
-    if (e == hipSuccess && energy) e = launch_energy_reduce(ctx->d_epart, nparts, energy, s);
+    if (e == hipSuccess && energy) e = launch_energy_reduce(parts, nparts, energy, s);
     return e;
 }
 
@@ -501,7 +509,8 @@ hipError_t enqueue_newton_cg(lad_ctx *ctx, const void *x, const void *gv, void *
 
 lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
 {
-    hipError_t e;
+    hipError_t e = hipGetDevice(&ctx->device);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipGetDevice");
     const int32_t nv = d->nv;
     ctx->nv = nv;
     ctx->dtype = d->dtype;
@@ -766,6 +775,32 @@ hipError_t enqueue_gauss_newton(lad_ctx *ctx, const void *x, const void *v, void
 
 }  // namespace
 
+namespace lad {
+
+lad_status eval_with_parts(lad_ctx *ctx, const void *d_x, double *d_energy, void *d_grad,
+                           void *d_hvals, int64_t hvals_capacity_blocks, double *parts,
+                           hipStream_t s)
+{
+    if (!d_x || !d_grad || !d_hvals) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
+    if (hvals_capacity_blocks < ctx->hcap)
+        return fail(ctx, LAD_ERR_ARG, "hvals capacity below " + std::to_string(ctx->hcap) + " blocks");
+    hipError_t e = ctx->dtype == LAD_F64
+                       ? enqueue_eval<double>(ctx, d_x, d_energy, d_grad, d_hvals, parts, s)
+                       : enqueue_eval<float>(ctx, d_x, d_energy, d_grad, d_hvals, parts, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "eval launch");
+    return LAD_OK;
+}
+
+int32_t eval_scratch_doubles(const lad_ctx *ctx) { return eval_nparts(ctx); }
+
+int32_t ctx_device(const lad_ctx *ctx) { return ctx->device; }
+
+int32_t ctx_vf_capacity(const lad_ctx *ctx) { return ctx->vf_cap; }
+
+lad_status ctx_fail(lad_ctx *ctx, lad_status st, const char *msg) { return fail(ctx, st, msg); }
+
+}  // namespace lad
+
 extern "C" {
 
 lad_status lad_build_pattern(const lad_mesh_desc *desc, void *hip_stream, lad_ctx **out)
@@ -862,14 +897,8 @@ lad_status lad_eval_energy_grad_hess(lad_ctx *ctx, const void *d_x, double *d_en
                                      int64_t hvals_capacity_blocks, void *hip_stream)
 {
     if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
-    if (!d_x || !d_grad || !d_hvals) return fail(ctx, LAD_ERR_ARG, "NULL buffer");
-    if (hvals_capacity_blocks < ctx->hcap)
-        return fail(ctx, LAD_ERR_ARG, "hvals capacity below " + std::to_string(ctx->hcap) + " blocks");
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = ctx->dtype == LAD_F64 ? enqueue_eval<double>(ctx, d_x, d_energy, d_grad, d_hvals, s)
-                                         : enqueue_eval<float>(ctx, d_x, d_energy, d_grad, d_hvals, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "eval launch");
-    return LAD_OK;
+    return lad::eval_with_parts(ctx, d_x, d_energy, d_grad, d_hvals, hvals_capacity_blocks,
+                                ctx->d_epart, static_cast<hipStream_t>(hip_stream));
 }
 
 lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y, void *hip_stream)

@@ -367,4 +367,18 @@ hipError_t launch_complete_cols(DevState *st, InsertBufs b, const PatchHdr *hdr,
                                 int32_t npatch, hipStream_t s);
 hipError_t launch_restore_topology(DevState *st, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Context internals for entry points defined outside lad_api.cpp.
+// ---------------------------------------------------------------------------
+// lad_eval_energy_grad_hess with the per-workgroup partial energies in
+// `parts` (at least eval_scratch_doubles(ctx) doubles, every one written
+// before it is read); argument checks and errors as that entry point.
+lad_status eval_with_parts(lad_ctx *ctx, const void *d_x, double *d_energy, void *d_grad,
+                           void *d_hvals, int64_t hvals_capacity_blocks, double *parts,
+                           hipStream_t s);
+int32_t eval_scratch_doubles(const lad_ctx *ctx);
+int32_t ctx_device(const lad_ctx *ctx);        // device the context was built on
+int32_t ctx_vf_capacity(const lad_ctx *ctx);
+lad_status ctx_fail(lad_ctx *ctx, lad_status st, const char *msg);  // sets lad_last_error
+
 }  // namespace lad
