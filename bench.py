@@ -103,6 +103,31 @@ def compulsory_bytes_cg_iter(nv, ns, es):
     return compulsory_bytes_hvp(nv, ns, 0, es) + 8 * 3 * nv * es
 
 
+FACES_FILE = os.path.join(PROFILES, "counters_faces512_f32.txt")
+
+
+def read_valu_busy(path, kernel):
+    """VALU-busy share of `kernel` from a committed rocprofv3 counter summary
+    (SQ_INSTS_VALU x 4 cycles over 1024 SIMDs at 2.4 GHz, divided by the
+    traced average duration), if it was taken on the current kernel sources;
+    else None."""
+    if not os.path.exists(path):
+        return None
+    sha, cur, val = None, None, {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("[") and line.endswith("]"):
+                cur = line[1:-1]
+            elif line.startswith("kernel_source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith("valu_busy:") and cur:
+                val[cur] = float(line.split(":", 1)[1])
+    if sha != kernel_source_sha():
+        return None
+    return val.get(kernel)
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_autodiff_mesh_amd", "csrc")
@@ -270,6 +295,34 @@ def bench_hvp_only(torch, binding, inputs, args, timer):
             "algorithmic_bytes": bc, "GBps": round(bc / (r["mean_ms"] * 1e-3) / 1e9, 1)}
 
 
+def bench_faces_only(torch, binding, inputs, args, timer):
+    """The 512 x 512 symmetric-Dirichlet face grid alone (for counter runs):
+    the explicit evaluation kernel (no energy sum: one launch per call),
+    then the matrix-free HVP, with their event timings and compulsory
+    bytes."""
+    f = inputs.face_grid(512)
+    L = binding.Lad(f.nv, dtype="f32",
+                    **binding.mesh_terms(f, springs=False, inertia=False, faces=True))
+    info = L.get_info()
+    x = to_dev(torch, f.x, "f32")
+    v = to_dev(torch, inputs.hvp_direction(f.nv), "f32")
+    y = torch.empty_like(v)
+    out = L.alloc_outputs()
+    re = timer.run(lambda: L.eval(x, out=out, energy=False), args.steps, args.warmup)
+    rh = timer.run(lambda: L.hvp(x, v, out=y), args.steps, args.warmup)
+    nf = f.faces.shape[0]
+    be = compulsory_bytes_eval(f.nv, 0, nf, info["nnzb_base"], 4, inertia=False, faces=True)
+    bh = compulsory_bytes_hvp(f.nv, 0, nf, 4, faces=True)
+    L.close()
+    return {"workload": "symmetric-Dirichlet faces, 512x512 vertex grid, fp32",
+            "kernels": ["k_eval_rows<float, true, false>", "k_hvp_rows<float, true, false>"],
+            "faces": nf, "chunks": info["npatches"], "steps": args.steps, "warmup": args.warmup,
+            "eval_ms_mean": round(re["mean_ms"], 5), "eval_algorithmic_bytes": be,
+            "eval_GBps": round(be / (re["mean_ms"] * 1e-3) / 1e9, 1),
+            "hvp_ms_mean": round(rh["mean_ms"], 5), "hvp_algorithmic_bytes": bh,
+            "hvp_GBps": round(bh / (rh["mean_ms"] * 1e-3) / 1e9, 1)}
+
+
 def bench_terms_cloth_only(torch, inputs, args, timer):
     """The term front end's generic cloth set alone (for counter runs): its
     fused explicit evaluation, then its product, with their event timings."""
@@ -386,6 +439,12 @@ def bench_secondary(torch, binding, inputs, args, timer):
     bh = compulsory_bytes_hvp(f.nv, 0, nf, 4, faces=True)
     sec["faces512_hvp_ms"] = round(r["median_ms"], 5)
     sec["faces512_hvp_GBps"] = round(bh / (r["median_ms"] * 1e-3) / 1e9, 1)
+    sec["faces512_eval_hbm_frac"] = round(sec["faces512_eval_GBps"] / HBM_PEAK_GBPS, 4)
+    sec["faces512_hvp_hbm_frac"] = round(sec["faces512_hvp_GBps"] / HBM_PEAK_GBPS, 4)
+    # VALU-busy of the same kernels from the committed counter summary
+    # (null when the kernel sources changed since it was taken)
+    sec["faces512_eval_valu_busy"] = read_valu_busy(FACES_FILE, "k_eval_rows<float, true, false>")
+    sec["faces512_hvp_valu_busy"] = read_valu_busy(FACES_FILE, "k_hvp_rows<float, true, false>")
     L.close()
     # 1000 x 1000 cloth + 2 % contact pairs per step, fp32: insert + eval
     m = inputs.cloth(args.n)
@@ -581,6 +640,9 @@ def main():
                     help="LDS bytes per patch (0 = library default)")
     ap.add_argument("--hvp-only", action="store_true",
                     help="only time the cloth HVP (prints its own JSON line; for counter runs)")
+    ap.add_argument("--faces-only", action="store_true",
+                    help="only time the 512x512 face grid, eval kernel then HVP (prints its "
+                         "own JSON line; for counter runs)")
     ap.add_argument("--terms-cloth-only", action="store_true",
                     help="only time the term front end's cloth set, eval then HVP (prints "
                          "its own JSON line; for counter runs)")
@@ -615,6 +677,9 @@ def main():
     timer = Timer(torch)
     if args.hvp_only:
         print(json.dumps(bench_hvp_only(torch, binding, inputs, args, timer)))
+        return 0
+    if args.faces_only:
+        print(json.dumps(bench_faces_only(torch, binding, inputs, args, timer)))
         return 0
     if args.terms_cloth_only:
         print(json.dumps(bench_terms_cloth_only(torch, inputs, args, timer)))

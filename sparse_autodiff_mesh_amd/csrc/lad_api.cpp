@@ -43,6 +43,9 @@ struct lad_ctx {
     int32_t *d_sl_ptr = nullptr, *d_sl_nb = nullptr;
     void *d_sl_rest = nullptr;
     FaceInc *d_finc = nullptr;
+    RowFace *d_rfinc = nullptr;
+    int32_t *d_sf_ptr = nullptr;
+    SliceFace *d_sface = nullptr;
     void *d_face_dm = nullptr, *d_face_area = nullptr;
 
     std::vector<void *> allocs;
@@ -233,6 +236,9 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
         ctx->d_face_area = p;
         if (e == hipSuccess) e = upload(ctx, &ctx->d_fptr, rplan.fptr, s);
         if (e == hipSuccess) e = upload(ctx, &ctx->d_finc, rplan.finc, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_rfinc, rplan.rfinc, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_sf_ptr, rplan.sf_ptr, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_sface, rplan.sface, s);
     }
     // lifetime of the host vectors: synchronise before they go out of scope
     if (e == hipSuccess) e = host_sync(ctx, s);
@@ -280,6 +286,9 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.x_tilde = static_cast<const T *>(ctx->d_xt);
     a.fptr = ctx->d_fptr;
     a.finc = ctx->d_finc;
+    a.rfinc = ctx->d_rfinc;
+    a.sf_ptr = ctx->d_sf_ptr;
+    a.sface = ctx->d_sface;
     a.face_dm = static_cast<const T *>(ctx->d_face_dm);
     a.face_area = static_cast<const T *>(ctx->d_face_area);
     a.k = T(ctx->k);

@@ -115,22 +115,50 @@ constexpr int kRowLdsBlocks = 512;
 constexpr int kRowBaseBlocks = 456;
 
 // One triangle seen from the row of one of its vertices (row-owner face
-// terms).  f is the face id; with i the row vertex's position in the face,
-// o1 and o2 are the face's vertices at positions (i+1)%3 and (i+2)%3; pk
-// packs i (bits 0-1) and, for face position k = 0, 1, 2, the offset of that
-// vertex's block within the row's topology pattern (bits 8k+8 .. 8k+15).
+// terms, explicit kernel).  f is the face id; with i the row vertex's
+// position in the face, o1 and o2 are the face's vertices at positions
+// (i+1)%3 and (i+2)%3; pk packs i (bits 0-1) and, for face position k = 0,
+// 1, 2, the offset of that vertex's block within the row's topology pattern
+// (bits 8k+8 .. 8k+15).
 struct alignas(16) FaceInc {
     int32_t f, o1, o2;
     uint32_t pk;
 };
 constexpr int kMaxRowFaceSlots = 256;   // slot offsets fit 8 bits
-constexpr int kSliceRows = 64;          // rows per spring slice: one wave
+constexpr int kSliceRows = 64;          // rows per slice of the product kernels: one wave
+
+// Face terms in the product kernels.  Every slice lists the faces incident
+// to its rows once; the kernel evaluates each listed face once per slice,
+// in rounds of kFaceRound faces (one per lane, results in LDS), and every
+// row then gathers its part of the faces of the round.  A face whose
+// vertices lie in two slices is evaluated by both (each writes only its own
+// rows); on a grid numbered row by row that is every face, against three
+// evaluations (one per vertex row) when each row evaluates its faces
+// itself.  The list takes each row's first incident face, then each row's
+// second, and so on, so that every round holds about as many faces of
+// every row.
+constexpr int kFaceRound = 64;
+struct alignas(16) SliceFace {
+    int32_t v[3];   // the face's vertices, in face order
+    int32_t f;      // face id (rest data)
+};
+// One face seen from one of its rows in the product kernels: lf is its
+// position in the slice's list, i (bits 0-1 of pi) the row vertex's
+// position in the face.
+struct RowFace {
+    uint32_t lf;
+    uint32_t pi;
+};
 
 struct RowPlan {
     std::vector<PatchHdr> chunk;     // v0, nown (rows), blk0, nblk, amap_cap
     std::vector<double> slot_rest;   // [nnzb] rest length behind each block, -1: none
-    std::vector<int32_t> fptr;       // [nv+1] face incidence offsets (face term on)
-    std::vector<FaceInc> finc;       // incident faces of each row, by face id
+    // face term on:
+    std::vector<int32_t> fptr;       // [nv+1] offsets of each row's faces in finc and rfinc
+    std::vector<FaceInc> finc;       // each row's faces, by face id
+    std::vector<RowFace> rfinc;      // each row's faces, by position in its slice's list
+    std::vector<int32_t> sf_ptr;     // [nslice+1] offsets of each slice's face list
+    std::vector<SliceFace> sface;    // the slices' face lists
     // Spring slices for the product kernels: rows in slices of
     // kSliceRows; slice t holds sl_ptr[t + 1] - sl_ptr[t] = kSliceRows * W_t
     // entries, W_t the most springs any of its rows has.  Spring j of row
@@ -223,8 +251,11 @@ struct RowArgs {
     const int32_t *sl_nb;        // neighbour vertices
     const T *sl_rest;            // and rest lengths (< 0: padding)
     const T *x_tilde;            // null = no inertia
-    const int32_t *fptr;         // [nv+1] face incidence offsets (faces on)
-    const FaceInc *finc;         // incident faces of each row
+    const int32_t *fptr;         // [nv+1] offsets of each row's faces (faces on)
+    const FaceInc *finc;         // each row's faces, by id (explicit kernel)
+    const RowFace *rfinc;        // each row's faces, by slice list position (products)
+    const int32_t *sf_ptr;       // [nslice+1] offsets of each slice's face list
+    const SliceFace *sface;      // the slices' face lists
     const T *face_dm;            // [nf][4] row-major Dm^-1
     const T *face_area;          // [nf]
     T k, c, kappa, dhat;

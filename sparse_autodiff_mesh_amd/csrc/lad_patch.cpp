@@ -404,6 +404,45 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
                 out.finc[size_t(cur[a]++)] = e;
             }
         }
+        // each slice's face list: every row's first incident face (by id),
+        // then every row's second, ..., each face once; then every row's
+        // faces by their position in that list
+        const int64_t nsl = (int64_t(nv) + kSliceRows - 1) / kSliceRows;
+        out.sf_ptr.assign(size_t(nsl) + 1, 0);
+        out.rfinc.resize(out.finc.size());
+        std::vector<int32_t> where(size_t(in.nf), -1);   // position in the current list
+        std::vector<int64_t> owner(size_t(in.nf), -1);   // slice that listed the face
+        for (int64_t t = 0; t < nsl; ++t) {
+            const int32_t v0 = int32_t(t * kSliceRows);
+            const int32_t v1 = int32_t(std::min<int64_t>(nv, (t + 1) * kSliceRows));
+            int32_t maxdeg = 0;
+            for (int32_t a = v0; a < v1; ++a) maxdeg = std::max(maxdeg, out.fptr[a + 1] - out.fptr[a]);
+            int64_t nl = 0;
+            for (int32_t rank = 0; rank < maxdeg; ++rank)
+                for (int32_t a = v0; a < v1; ++a) {
+                    if (rank >= out.fptr[a + 1] - out.fptr[a]) continue;
+                    const int32_t f = out.finc[size_t(out.fptr[a] + rank)].f;
+                    if (owner[size_t(f)] == t) continue;
+                    owner[size_t(f)] = t;
+                    where[size_t(f)] = int32_t(nl++);
+                    SliceFace sf;
+                    for (int i = 0; i < 3; ++i) sf.v[i] = in.faces[3 * int64_t(f) + i];
+                    sf.f = f;
+                    out.sface.push_back(sf);
+                }
+            if (out.sf_ptr[size_t(t)] + nl > INT32_MAX) return "too many faces for the slice lists";
+            out.sf_ptr[size_t(t) + 1] = int32_t(out.sf_ptr[size_t(t)] + nl);
+            for (int32_t a = v0; a < v1; ++a) {
+                for (int32_t k = out.fptr[a]; k < out.fptr[a + 1]; ++k) {
+                    RowFace e;
+                    e.lf = uint32_t(where[size_t(out.finc[size_t(k)].f)]);
+                    e.pi = out.finc[size_t(k)].pk & 3u;
+                    out.rfinc[size_t(k)] = e;
+                }
+                std::sort(out.rfinc.begin() + out.fptr[a], out.rfinc.begin() + out.fptr[a + 1],
+                          [](const RowFace &p, const RowFace &q) { return p.lf < q.lf; });
+            }
+        }
     }
     for (int32_t v0 = 0; v0 < nv;) {
         int32_t n = 0, blk = 0;

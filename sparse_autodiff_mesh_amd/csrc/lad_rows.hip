@@ -146,7 +146,7 @@ __device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r,
         for (int j = 0; j < kBatch; ++j) {
             const int32_t kl = q.kb[j] >= 0 ? q.kb[j] : r.kb0;
             q.b[j] = A.ci0[kl];
-            q.L[j] = A.slot_rest[kl];
+            q.L[j] = A.springs_on ? A.slot_rest[kl] : T(-1);
         }
     } else {
         int32_t ca[kBatch], cb[kBatch];
@@ -168,13 +168,15 @@ __device__ __forceinline__ void load_batch(const RowArgs<T> &A, const Row<T> &r,
         }
         jb += nmatch;
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) q.L[j] = A.slot_rest[q.kb[j] >= 0 ? q.kb[j] : r.kb0];
+        for (int j = 0; j < kBatch; ++j)
+            q.L[j] = A.springs_on ? A.slot_rest[q.kb[j] >= 0 ? q.kb[j] : r.kb0] : T(-1);
     }
+    // neighbour positions only for the spring term (uniform)
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
         const int32_t bl = (base + j < r.s1) ? q.b[j] : r.a;
 #pragma unroll
-        for (int c = 0; c < 3; ++c) q.xb[j][c] = x[int64_t(bl) * 3 + c];
+        for (int c = 0; c < 3; ++c) q.xb[j][c] = A.springs_on ? x[int64_t(bl) * 3 + c] : T(0);
         if (q.kb[j] < 0 || !A.springs_on) q.L[j] = T(-1);
     }
 }
@@ -239,16 +241,51 @@ __device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, int
 }
 
 // ---------------------------------------------------------------------------
-// Face terms seen from one row.  The symmetric-Dirichlet energy is
-// differentiated in its natural variables F = [p1 - p0, p2 - p0] M
-// (M = Dm^-1, F stored row-major F[2s + c]), a constant linear image of the
-// face's vertex positions: dF[s][c] / dp_u[s] = w[u][c] with w1 = M row 0,
-// w2 = M row 1, w0 = -(w1 + w2).  Row vertex a at face position i then gets
-//   g_a[s]       += sum_c w[i][c] dE/dF[s][c]
+// Face terms.  The symmetric-Dirichlet energy is differentiated in its
+// natural variables F = [p1 - p0, p2 - p0] M (M = Dm^-1, F stored row-major
+// F[2s + c]), a constant linear image of the face's vertex positions:
+// dF[s][c] / dp_u[s] = w[u][c] with w1 = M row 0, w2 = M row 1,
+// w0 = -(w1 + w2).  The row of the face's vertex at position i then gets
+//   g_a[s]        += sum_c w[i][c] dE/dF[s][c]
 //   H_(a,u)[s][t] += sum_{c,c'} w[i][c] w[u][c'] d2E/dF[s][c] dF[t][c'].
+// The explicit kernel has every row evaluate its own faces (each face
+// three times, once per vertex row: the evaluation stays in registers and
+// the kernel keeps its occupancy); the product kernel evaluates every face
+// of a slice's list once per slice, one face per lane, and keeps its
+// per-vertex results in LDS for the rows of the slice to gather (fields of
+// one face are kFaceRound apart, so the lanes of a wave touch distinct
+// banks).
 // ---------------------------------------------------------------------------
-constexpr int kFaceBatch = 3;  // incident faces whose loads a lane issues together
+constexpr int kFaceHvpFields = 9;   // product kernel: w_u^T (d2E/dF2 dF) for u = 0, 1, 2
+constexpr int kRowFaceRegs = 8;     // a row's first faces, held in registers
+constexpr int kFaceBatch = 3;       // incident faces whose loads a lane issues together
 
+// Face positions (in face order), Dm^-1 and area of one face.
+template <typename T>
+struct FaceIn {
+    T p[3][3];
+    T m[4];
+    T area;
+};
+
+// One face of a slice's list, loaded by the lane that evaluates it.
+template <typename T>
+__device__ __forceinline__ void load_face(const RowArgs<T> &A, const SliceFace &sf,
+                                          const T *__restrict__ x, FaceIn<T> &q)
+{
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) q.p[u][c] = x[int64_t(sf.v[u]) * 3 + c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q.m[c] = A.face_dm[int64_t(sf.f) * 4 + c];
+    q.area = A.face_area[sf.f];
+}
+
+// The incident faces [base, base + kFaceBatch) of row r (explicit kernel),
+// with indices clamped into the row's range so that every load is valid:
+// each face's record, the positions of its other two vertices, Dm^-1 and
+// area, all issued together.
 template <typename T>
 struct FaceBatch {
     FaceInc e[kFaceBatch];
@@ -257,8 +294,6 @@ struct FaceBatch {
     T area[kFaceBatch];
 };
 
-// Loads of the incident faces [base, base + kFaceBatch) of row r, with
-// indices clamped into the row's range so that every load is valid.
 template <typename T>
 __device__ __forceinline__ void load_faces(const RowArgs<T> &A, const Row<T> &r, int32_t base,
                                            const T *__restrict__ x, FaceBatch<T> &q)
@@ -278,24 +313,39 @@ __device__ __forceinline__ void load_faces(const RowArgs<T> &A, const Row<T> &r,
     }
 }
 
-// Values of F = [p1 - p0, p2 - p0] M for face j of the batch (row vertex at
-// face position i) and the weights w[u][c] = dF[.][c] / dp_u.
+// Face j of a batch in face order: p_i = x_a, p_(i+1)%3 = o1, p_(i+2)%3 = o2.
 template <typename T>
-__device__ __forceinline__ void face_F(const Row<T> &r, const FaceBatch<T> &q, int j, int i,
-                                       T Fv[6], T w[3][2])
+__device__ __forceinline__ void batch_face(const Row<T> &r, const FaceBatch<T> &q, int j, int i,
+                                           FaceIn<T> &f)
 {
-    const T *o1 = q.xo[j][0], *o2 = q.xo[j][1];
-    const T *m = q.m[j];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-        // face positions: p_i = x_a, p_(i+1)%3 = o1, p_(i+2)%3 = o2
-        const T p0 = i == 0 ? r.xa[c] : (i == 1 ? o2[c] : o1[c]);
-        const T p1 = i == 1 ? r.xa[c] : (i == 2 ? o2[c] : o1[c]);
-        const T p2 = i == 2 ? r.xa[c] : (i == 0 ? o2[c] : o1[c]);
-        const T d0 = p1 - p0, d1 = p2 - p0;
-        Fv[2 * c + 0] = d0 * m[0] + d1 * m[2];
-        Fv[2 * c + 1] = d0 * m[1] + d1 * m[3];
+        const T *o1 = q.xo[j][0], *o2 = q.xo[j][1];
+        f.p[0][c] = i == 0 ? r.xa[c] : (i == 1 ? o2[c] : o1[c]);
+        f.p[1][c] = i == 1 ? r.xa[c] : (i == 2 ? o2[c] : o1[c]);
+        f.p[2][c] = i == 2 ? r.xa[c] : (i == 0 ? o2[c] : o1[c]);
     }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) f.m[c] = q.m[j][c];
+    f.area = q.area[j];
+}
+
+// F = [p1 - p0, p2 - p0] M.
+template <typename T>
+__device__ __forceinline__ void face_F(const FaceIn<T> &q, T Fv[6])
+{
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const T d0 = q.p[1][s] - q.p[0][s], d1 = q.p[2][s] - q.p[0][s];
+        Fv[2 * s + 0] = d0 * q.m[0] + d1 * q.m[2];
+        Fv[2 * s + 1] = d0 * q.m[1] + d1 * q.m[3];
+    }
+}
+
+// The weights w[u][c] = dF[.][c] / dp_u from M.
+template <typename T>
+__device__ __forceinline__ void face_w(const T m[4], T w[3][2])
+{
     w[1][0] = m[0];
     w[1][1] = m[1];
     w[2][0] = m[2];
@@ -304,32 +354,52 @@ __device__ __forceinline__ void face_F(const Row<T> &r, const FaceBatch<T> &q, i
     w[0][1] = -(m[1] + m[3]);
 }
 
-// Energy of face j of the batch as a Dual2 in F, and the weights w[u][c].
-template <typename T>
-__device__ __forceinline__ Dual2<T, 6> face_eval(const Row<T> &r, const FaceBatch<T> &q, int j,
-                                                 int i, T w[3][2])
+// The row's part of one face from its F-space derivatives gE (6) and the
+// packed d2E/dF2 h (21), the row vertex at face position i: the gradient
+// into G, the row's own block into D, and the blocks of the face vertices
+// at positions (i+1)%3 and (i+2)%3 to blk(position, block).  The row's
+// material weights are contracted first,
+//   P[s][t][c'] = sum_c w[i][c] d2E/dF[s][c] dF[t][c'],
+// then each block is P against the column vertex's weights.  (The weights
+// are picked by selects, not by indexing with i, which would put them in
+// scratch memory.)
+template <typename T, typename BlockAdd>
+__device__ __forceinline__ void face_row(const T gE[6], const T h[21], const T m[4], int i,
+                                         T D[9], T G[3], BlockAdd blk)
 {
-    T Fv[6];
-    face_F(r, q, j, i, Fv, w);
-    Dual2<T, 6> F[6];
+    // w[u][c] from M: w1 = M row 0, w2 = M row 1, w0 = -(w1 + w2)
+    auto pick = [&](int u, int c) __attribute__((always_inline)) {
+        const T a = m[c], b = m[2 + c];
+        return u == 1 ? a : (u == 2 ? b : -(a + b));
+    };
+    const int i1 = i == 2 ? 0 : i + 1, i2 = i == 0 ? 2 : i - 1;
+    const T wa[2] = {pick(i, 0), pick(i, 1)};
+    const T wb[2] = {pick(i1, 0), pick(i1, 1)};
+    const T wc[2] = {pick(i2, 0), pick(i2, 1)};
 #pragma unroll
-    for (int k = 0; k < 6; ++k) F[k] = Dual2<T, 6>::var(Fv[k], k);
-    return face_energy(F, q.area[j]);
-}
-
-// wa^T (d2E/dF[s][.] dF[t][.]) wu for all s, t.
-template <typename T>
-__device__ __forceinline__ void face_block(const Dual2<T, 6> &e, const T wa[2], const T wu[2],
-                                           T B[9])
-{
+    for (int s = 0; s < 3; ++s) G[s] += wa[0] * gE[2 * s] + wa[1] * gE[2 * s + 1];
+    auto H = [&](int p, int q) __attribute__((always_inline)) {
+        return p <= q ? h[Tri<6>::idx(p, q)] : h[Tri<6>::idx(q, p)];
+    };
+    T P[3][3][2];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                P[s][t][c] = wa[0] * H(2 * s, 2 * t + c) + wa[1] * H(2 * s + 1, 2 * t + c);
+    T B1[9], B2[9];
 #pragma unroll
     for (int s = 0; s < 3; ++s)
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
-            const T q0 = e.hess(2 * s, 2 * t) * wu[0] + e.hess(2 * s, 2 * t + 1) * wu[1];
-            const T q1 = e.hess(2 * s + 1, 2 * t) * wu[0] + e.hess(2 * s + 1, 2 * t + 1) * wu[1];
-            B[3 * s + t] = wa[0] * q0 + wa[1] * q1;
+            D[3 * s + t] += P[s][t][0] * wa[0] + P[s][t][1] * wa[1];
+            B1[3 * s + t] = P[s][t][0] * wb[0] + P[s][t][1] * wb[1];
+            B2[3 * s + t] = P[s][t][0] * wc[0] + P[s][t][1] * wc[1];
         }
+    blk(i1, B1);
+    blk(i2, B2);
 }
 
 // ---------------------------------------------------------------------------
@@ -457,39 +527,41 @@ __device__ __forceinline__ void vf_add(const RowArgs<T> &A, int32_t a, int32_t e
             for (int k = 0; k < 9; ++k) Hrow[9 * off[m] + k] = cur[m][k];
 }
 
-// One row: energy part, gradient and every block, written into Hs (block
-// s - sb holds active slot s).  PAIRS: the full evaluation of a touched row
-// (column matching, pair and contact terms).  SHIFT (the main kernel of a
-// context with contact capacity): the topology terms of an untouched row,
-// or of a touched row with at most kMaxIns inserted columns, each block
-// placed at its active slot; k_eval_pair_rows then zeroes the inserted
-// blocks and adds the row's contact terms.
-template <typename T, bool FACES, bool PAIRS, bool SHIFT = false>
-__device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const int32_t *cia,
-                                           const Row<T> &r, int32_t sb,
-                                           T *Hs, const T *__restrict__ x, T *__restrict__ g)
+// What a row accumulates in registers: its diagonal block, its gradient,
+// its part of the energy, and the active slot of its diagonal block.
+template <typename T>
+struct RowAcc {
+    T D[9];
+    T G[3];
+    double E;
+    int32_t dslot;
+};
+
+template <typename T>
+__device__ __forceinline__ void acc_init(RowAcc<T> &acc, int32_t s0)
 {
-    static_assert(!(PAIRS && SHIFT), "one mode per row");
-    T D[9], G[3] = {T(0), T(0), T(0)};
 #pragma unroll
-    for (int i = 0; i < 9; ++i) D[i] = T(0);
-    double E = 0.0;
-    int32_t dslot = r.s0;
+    for (int i = 0; i < 9; ++i) acc.D[i] = T(0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) acc.G[i] = T(0);
+    acc.E = 0.0;
+    acc.dslot = s0;
+}
 
-    int32_t ins[kMaxIns];
-    Row<T> rt = r;  // the row as the slot loop walks it
-    if constexpr (SHIFT) {
-        load_inserted(A, A.state->active, r, ins);
-        rt.s1 = r.s0 + (r.kb1 - r.kb0);  // topology slots, in order
-        rt.p0 = rt.p1 = 0;
-    }
-
-    // pairs of the active buffer (element ids below npa are pairs); rows
-    // that no contact touches are evaluated with PAIRS = false, which
-    // compiles the contact code out
-    const int32_t npa = (PAIRS && act != 0) ? A.state->np[act] : 0;
-    PairPre<T> pp;
-    prefetch_pairs(A, PAIRS ? act : 0, npa, r, x, pp);
+// The slot loop of one row over the active slots [rt.s0, rt.s1): every
+// slot gets its spring's block -K (+K into D), or zeros (no spring behind
+// it, or a block inserted by contacts); the diagonal slot is recorded.
+// PAIRS: slots found through the active row (column matching), and the
+// prefetched pairs' slots recorded in pp.  SHIFT: the topology slots in
+// order, each moved past the inserted columns before it.  Each spring's
+// energy is counted by its lower-numbered endpoint's row.
+template <typename T, bool PAIRS, bool SHIFT>
+__device__ __forceinline__ void row_slots(const RowArgs<T> &A, int act, const int32_t *cia,
+                                          const Row<T> &r, const Row<T> &rt,
+                                          const int32_t ins[kMaxIns], int32_t sb, T *Hs,
+                                          const T *__restrict__ x, RowAcc<T> &acc,
+                                          PairPre<T> &pp)
+{
     int32_t jb = r.kb0;
     for (int32_t base = rt.s0; base < rt.s1; base += kBatch) {
         SlotBatch<T> q;
@@ -499,14 +571,15 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
             int32_t s = base + j;
             if (s >= rt.s1) break;
             if constexpr (SHIFT) s += shift_of(ins, q.b[j]);
+            if constexpr (PAIRS)
 #pragma unroll
-            for (int k = 0; k < kRowPairs; ++k) pp.slot[k] = q.b[j] == pp.b[k] ? s : pp.slot[k];
+                for (int k = 0; k < kRowPairs; ++k) pp.slot[k] = q.b[j] == pp.b[k] ? s : pp.slot[k];
             T *B = Hs + 9 * (s - sb);
             if (q.kb[j] >= 0 && q.b[j] == r.a) {
-                dslot = s;
+                acc.dslot = s;
                 continue;
             }
-            if (!(q.L[j] >= T(0))) {  // inserted by a pair, or no spring behind the block
+            if (!(q.L[j] >= T(0))) {  // inserted by a contact, or no spring behind the block
 #pragma unroll
                 for (int i = 0; i < 9; ++i) B[i] = T(0);
                 continue;
@@ -517,21 +590,61 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
             const Dual2<T, 3> e = spring_energy(d, q.L[j], A.k);
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
-                G[i] += e.g[i];
+                acc.G[i] += e.g[i];
 #pragma unroll
                 for (int k = 0; k < 3; ++k) {
                     const T h = e.hess(i, k);
                     B[3 * i + k] = -h;
-                    D[3 * i + k] += h;
+                    acc.D[3 * i + k] += h;
                 }
             }
-            if (r.a < q.b[j]) E += double(e.v);
+            if (r.a < q.b[j]) acc.E += double(e.v);
         }
     }
+}
 
-    // faces: the diagonal block and g_a in registers; the two off-diagonal
-    // blocks of each face are added into this lane's own row slice in LDS
-    if constexpr (FACES)
+template <typename T>
+__device__ __forceinline__ void row_inertia(const RowArgs<T> &A, const Row<T> &r, RowAcc<T> &acc)
+{
+    if (!A.inertia_on) return;
+    Dual2<T, 3> z[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) z[c] = Dual2<T, 3>::var(r.xa[c] - r.xt[c], c);
+    const Dual2<T, 3> e = inertia_energy(z, A.c);
+    acc.E += double(e.v);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        acc.G[i] += e.g[i];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) acc.D[3 * i + j] += e.hess(i, j);
+    }
+}
+
+// The diagonal block into its slot, the gradient into g.
+template <typename T>
+__device__ __forceinline__ void row_store(const Row<T> &r, int32_t sb, T *Hs, T *__restrict__ g,
+                                          const RowAcc<T> &acc)
+{
+    T *B = Hs + 9 * (acc.dslot - sb);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) B[i] = acc.D[i];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g[int64_t(r.a) * 3 + c] = acc.G[c];
+}
+
+// The faces of one row, evaluated by the row itself in face-id order,
+// kFaceBatch at a time with all their loads issued together: the gradient
+// part and the diagonal block into acc, the blocks of the face's other two
+// vertices added into the staged row (block s - sb holds active slot s).
+// Block placement: the topology pattern active (act == 0) or a row no
+// contact touches, at the topology offset (SHIFT: moved past the inserted
+// columns before it); else at the column's position in the active row.
+// The energy of a face is counted by the row of its first vertex.
+template <typename T, bool SHIFT>
+__device__ __forceinline__ void row_faces(const RowArgs<T> &A, int act, const int32_t *cia,
+                                          const Row<T> &r, const int32_t ins[kMaxIns], int32_t sb,
+                                          T *Hs, const T *__restrict__ x, RowAcc<T> &acc)
+{
     for (int32_t base = r.f0; base < r.f1; base += kFaceBatch) {
         FaceBatch<T> q;
         load_faces(A, r, base, x, q);
@@ -540,86 +653,83 @@ __device__ __forceinline__ double eval_row(const RowArgs<T> &A, int act, const i
             if (base + j >= r.f1) break;
             const FaceInc fe = q.e[j];
             const int i = int(fe.pk & 3u);
-            T w[3][2];
-            const Dual2<T, 6> e = face_eval(r, q, j, i, w);
-            const T wa[2] = {i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]),
-                             i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1])};
-            if (i == 0) E += double(e.v);
+            FaceIn<T> f;
+            batch_face(r, q, j, i, f);
+            T Fv[6];
+            face_F(f, Fv);
+            Dual2<T, 6> F[6];
 #pragma unroll
-            for (int s = 0; s < 3; ++s) G[s] += wa[0] * e.g[2 * s] + wa[1] * e.g[2 * s + 1];
+            for (int c = 0; c < 6; ++c) F[c] = Dual2<T, 6>::var(Fv[c], c);
+            const Dual2<T, 6> en = face_energy(F, f.area);
+            if (i == 0) acc.E += double(en.v);
+            face_row(en.g, en.h, f.m, i, acc.D, acc.G,
+                     [&](int u, const T B[9]) __attribute__((always_inline)) {
+                         // u is the face position (i+1)%3 or (i+2)%3: o1 or o2
+                         const int32_t vu = u == (i == 2 ? 0 : i + 1) ? fe.o1 : fe.o2;
+                         int32_t sl;
+                         if (act == 0 || r.p1 == r.p0) {
+                             const int32_t off = int32_t((fe.pk >> (8 * u + 8)) & 255u);
+                             sl = r.s0 + off;
+                             if constexpr (SHIFT) sl += shift_of(ins, vu);
+                         } else {
+                             sl = find_slot(cia, r.s0, r.s1, vu);
+                         }
+                         T *Bp = Hs + 9 * (sl - sb);
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                T Bu[9];
-                face_block(e, wa, w[u], Bu);
-                if (u == i) {
-#pragma unroll
-                    for (int k = 0; k < 9; ++k) D[k] += Bu[k];
-                } else {
-                    // block of face vertex u in this row: its topology slot
-                    // (moved past the inserted columns before it), or (a
-                    // touched row evaluated in full) its column's position
-                    // in the active row
-                    const int32_t vu = u == (i + 1) % 3 ? fe.o1 : fe.o2;
-                    const int32_t off = int32_t((fe.pk >> (8 * u + 8)) & 255u);
-                    int32_t sl = (act == 0 || r.p1 == r.p0) ? r.s0 + off
-                                                            : find_slot(cia, r.s0, r.s1, vu);
-                    if constexpr (SHIFT) sl += shift_of(ins, vu);
-                    T *B = Hs + 9 * (sl - sb);
-#pragma unroll
-                    for (int k = 0; k < 9; ++k) B[k] += Bu[k];
-                }
-            }
+                         for (int k2 = 0; k2 < 9; ++k2) Bp[k2] += B[k2];
+                     });
         }
     }
+}
 
-    if (A.inertia_on) {
-        Dual2<T, 3> z[3];
+// The full evaluation of a row whose active row differs from its topology
+// row by more than kMaxIns columns (k_eval_pair_rows): column matching,
+// topology terms, its faces, inertia, then its
+// pairs and vertex-face contacts in element order; every block written
+// into Hs (block s - sb holds active slot s), g_a into g.
+template <typename T, bool FACES>
+__device__ __forceinline__ double eval_row_full(const RowArgs<T> &A, int act, const int32_t *cia,
+                                                const Row<T> &r, int32_t sb, T *Hs,
+                                                const T *__restrict__ x, T *__restrict__ g)
+{
+    RowAcc<T> acc;
+    acc_init(acc, r.s0);
+    int32_t ins[kMaxIns];
 #pragma unroll
-        for (int c = 0; c < 3; ++c)
-            z[c] = Dual2<T, 3>::var(r.xa[c] - r.xt[c], c);
-        const Dual2<T, 3> e = inertia_energy(z, A.c);
-        E += double(e.v);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            G[i] += e.g[i];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) D[3 * i + j] += e.hess(i, j);
-        }
-    }
-
+    for (int m = 0; m < kMaxIns; ++m) ins[m] = INT32_MAX;
+    const int32_t npa = act != 0 ? A.state->np[act] : 0;
+    PairPre<T> pp;
+    prefetch_pairs(A, act, npa, r, x, pp);
+    row_slots<T, true, false>(A, act, cia, r, r, ins, sb, Hs, x, acc, pp);
+    if constexpr (FACES) row_faces<T, false>(A, act, cia, r, ins, sb, Hs, x, acc);
+    row_inertia(A, r, acc);
     // runtime pairs of this row, in pair order: -K into the (a, b) block,
-    // +K into the diagonal
-    if constexpr (PAIRS) {
+    // +K into the diagonal; then further pairs and contacts
 #pragma unroll
-        for (int k = 0; k < kRowPairs; ++k)
-            if (k < pp.n) pair_add(A, r, pp.xb[k], Hs + 9 * (pp.slot[k] - sb), pp.first[k] != 0, D, G, E);
-        // entries past the prefetched pairs: further pairs, then contacts
-        if (r.p1 - r.p0 > pp.n) {
-            const int32_t *pl = A.pat.pinc[act];
-            const int32_t *prs = A.pat.pairs[act];
-            for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
-                const int32_t q = pl[k];
-                if (q >= npa) {
-                    vf_add(A, r.a, q - npa, Hs + 9 * (r.s0 - sb), D, G, E);
-                    continue;
-                }
-                const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
-                const int32_t b = i0 == r.a ? i1 : i0;
-                T xb[3];
-#pragma unroll
-                for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
-                pair_add(A, r, xb, Hs + 9 * (find_slot(cia, r.s0, r.s1, b) - sb), i0 == r.a, D, G,
-                         E);
+    for (int k = 0; k < kRowPairs; ++k)
+        if (k < pp.n)
+            pair_add(A, r, pp.xb[k], Hs + 9 * (pp.slot[k] - sb), pp.first[k] != 0, acc.D, acc.G,
+                     acc.E);
+    if (r.p1 - r.p0 > pp.n) {
+        const int32_t *pl = A.pat.pinc[act];
+        const int32_t *prs = A.pat.pairs[act];
+        for (int32_t k = r.p0 + pp.n; k < r.p1; ++k) {
+            const int32_t q = pl[k];
+            if (q >= npa) {
+                vf_add(A, r.a, q - npa, Hs + 9 * (r.s0 - sb), acc.D, acc.G, acc.E);
+                continue;
             }
+            const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
+            const int32_t b = i0 == r.a ? i1 : i0;
+            T xb[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
+            pair_add(A, r, xb, Hs + 9 * (find_slot(cia, r.s0, r.s1, b) - sb), i0 == r.a, acc.D,
+                     acc.G, acc.E);
         }
     }
-
-    T *B = Hs + 9 * (dslot - sb);
-#pragma unroll
-    for (int i = 0; i < 9; ++i) B[i] = D[i];
-#pragma unroll
-    for (int c = 0; c < 3; ++c) g[int64_t(r.a) * 3 + c] = G[c];
-    return E;
+    row_store(r, sb, Hs, g, acc);
+    return acc.E;
 }
 
 // The contact terms of a touched row whose topology terms the main kernel
@@ -706,17 +816,39 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         const bool fits = nblk <= A.lds_blocks;
         const int pad = stage_pad<T>(int64_t(sb) * 9);
         T *Hs = stage + pad;
+        // Every row's topology terms, through the topology pattern (act =
+        // 0, no pair code); with contact capacity each block is moved to its
+        // active slot and the contact terms of touched rows follow in
+        // k_eval_pair_rows.  A row with more than kMaxIns inserted columns
+        // is left to that kernel whole (its slice of the staging area is
+        // streamed out unwritten and overwritten there).
+        Row<T> r{};
+        bool own = false;
         if (fits && int(threadIdx.x) < nrows) {
-            const Row<T> r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
-            // Every row's topology terms, through the topology pattern
-            // (act = 0, no pair code); with contact capacity each block is
-            // moved to its active slot and the contact terms of touched rows
-            // follow in k_eval_pair_rows.  A row with more than kMaxIns
-            // inserted columns is left to that kernel whole (its slice of
-            // the staging area is streamed out unwritten and overwritten
-            // there).
-            if (!PAIRS || r.nn <= kMaxIns)
-                eacc += eval_row<T, FACES, false, PAIRS>(A, 0, cia, r, sb, Hs, x, g);
+            r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
+            own = !PAIRS || r.nn <= kMaxIns;
+        }
+        RowAcc<T> acc;
+        acc_init(acc, r.s0);
+        int32_t ins[kMaxIns];
+#pragma unroll
+        for (int m = 0; m < kMaxIns; ++m) ins[m] = INT32_MAX;
+        if (own) {
+            Row<T> rt = r;  // the row as the slot loop walks it
+            if constexpr (PAIRS) {
+                load_inserted(A, A.state->active, r, ins);
+                rt.s1 = r.s0 + (r.kb1 - r.kb0);  // topology slots, in order
+                rt.p0 = rt.p1 = 0;
+            }
+            PairPre<T> pp;
+            prefetch_pairs(A, 0, 0, r, x, pp);
+            row_slots<T, false, PAIRS>(A, 0, cia, r, rt, ins, sb, Hs, x, acc, pp);
+            if constexpr (FACES) row_faces<T, PAIRS>(A, 0, cia, r, ins, sb, Hs, x, acc);
+        }
+        if (own) {
+            row_inertia(A, r, acc);
+            row_store(r, sb, Hs, g, acc);
+            eacc += acc.E;
         }
         wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
@@ -753,7 +885,7 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
             if (r.nn <= kMaxIns)
                 e = eval_row_contacts(A, act, r, x, hv, g);
             else
-                e = eval_row<T, FACES, true>(A, act, A.pat.ci[act], r, 0, hv, x, g);
+                e = eval_row_full<T, FACES>(A, act, A.pat.ci[act], r, 0, hv, x, g);
         }
     }
     store_energy(esink, block_sum<kThreads>(e, red));
@@ -777,13 +909,16 @@ __device__ __forceinline__ double cg_dir_comp(double r, double d, double beta)
 constexpr int kSliceBatch = 6;
 
 // What a lane of the product kernels loads for its row before the gathers:
-// the row's position, its operand (v, or r and the previous direction for
+// the row (kSliceRows * t + lane, clamped to the last row for lanes past
+// it), its position, its operand (v, or r and the previous direction for
 // Newton-CG), its first kSliceBatch spring neighbours with their rest
-// lengths (without the face term only) or its incident-face range.  Every load depends only on the
-// slice index, so the next slice's are issued while the current slice is
-// processed.
+// lengths (without the face term only) or its face range.  Every load
+// depends only on the slice index, so the next slice's are issued while
+// the current slice is processed.
 template <typename T>
 struct SliceRow {
+    int32_t a;
+    int32_t live;
     T xa[3], o0[3], o1[3];
     int32_t nb[kSliceBatch];
     T L[kSliceBatch];
@@ -797,7 +932,9 @@ __device__ __forceinline__ void slice_head(const RowArgs<T> &A, int32_t t, int l
                                            const T *__restrict__ x, const T *__restrict__ v,
                                            const CgDir<T> &cg, SliceRow<T> &h)
 {
+    h.live = t * kSliceRows + lane < A.nv ? 1 : 0;
     const int32_t a = min(t * kSliceRows + lane, A.nv - 1);
+    h.a = a;
     const int32_t p = A.sl_ptr[t];
     const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;
 #pragma unroll
@@ -823,9 +960,9 @@ __device__ __forceinline__ void slice_head(const RowArgs<T> &A, int32_t t, int l
     h.f1 = FACES ? A.fptr[a + 1] : 0;
 }
 
-// Spring neighbours j0 .. j0 + kSliceBatch - 1 of row a (lane `lane` of
-// slice entries starting at p; ns springs in the slice's widest row): the
-// first batch from the prefetched head, later ones loaded here.
+// Spring neighbours j0 .. j0 + kSliceBatch - 1 of the lane's row (slice
+// entries starting at p; ns springs in the slice's widest row): the first
+// batch from the prefetched head, later ones loaded here.
 template <typename T, bool FACES>
 __device__ __forceinline__ void slice_batch(const RowArgs<T> &A, const SliceRow<T> &h, int32_t p,
                                             int32_t ns, int32_t j0, int lane, int32_t self,
@@ -848,7 +985,8 @@ __device__ __forceinline__ void slice_batch(const RowArgs<T> &A, const SliceRow<
 }
 
 // This workgroup's slices [t0, t1) (contiguous ranges grouped by XCD) and
-// its wave's first slice; the waves walk the range kWaves slices apart.
+// its wave's first slice; the waves walk the range kSliceWaves slices
+// apart.
 constexpr int32_t kSliceWaves = kHvpThreads / kSliceRows;
 __device__ __forceinline__ void slice_range(int32_t nv, int32_t &t0, int32_t &t1, int32_t &first)
 {
@@ -858,6 +996,89 @@ __device__ __forceinline__ void slice_range(int32_t nv, int32_t &t0, int32_t &t1
     t0 = int32_t(int64_t(nsl) * w / gridDim.x);
     t1 = int32_t(int64_t(nsl) * (w + 1) / gridDim.x);
     first = t0 + wv;
+}
+
+// The face terms of one slice (product kernel), all lanes of the wave
+// together: in rounds of kFaceRound listed faces, every lane evaluates one
+// face in numbers that carry the value, the gradient and the Hessian's
+// action on the face's direction dF = (dF/dp) u_face, and stores, for each
+// face vertex u, w_u^T (d2E/dF2 dF) in this wave's LDS records; every row
+// then adds the part of its position in the round's faces it belongs to,
+// in list order.  dir(i) gives component i of the direction.
+template <typename T, typename Dir>
+__device__ __forceinline__ void slice_faces(const RowArgs<T> &A, int32_t t, const SliceRow<T> &h,
+                                            T *rec, const T *__restrict__ x, Dir dir, T Y[3])
+{
+    const int lane = int(threadIdx.x) & (kSliceRows - 1);
+    const int32_t cf0 = A.sf_ptr[t], ncf = A.sf_ptr[t + 1] - cf0;
+    if (ncf == 0) return;  // wave-uniform: no faces in this slice
+    const int32_t nrf = h.live ? h.f1 - h.f0 : 0;
+    RowFace rf[kRowFaceRegs];
+#pragma unroll
+    for (int j = 0; j < kRowFaceRegs; ++j) rf[j] = A.rfinc[nrf > 0 ? h.f0 + min(j, nrf - 1) : 0];
+    auto gather = [&](const RowFace e, int32_t base) __attribute__((always_inline)) {
+        const int kk = int(e.lf) - base;
+        const int i = int(e.pi & 3u);
+#pragma unroll
+        for (int s = 0; s < 3; ++s) Y[s] += rec[(3 * i + s) * kFaceRound + kk];
+    };
+    // face inputs and the direction at its vertices, the next round's
+    // loaded while this round is evaluated (lanes past the list take its
+    // last face and store nothing)
+    struct In {
+        FaceIn<T> q;
+        T du[3][3];
+    };
+    auto load_in = [&](const SliceFace &cf, In &in) __attribute__((always_inline)) {
+        load_face(A, cf, x, in.q);
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) in.du[u][c] = dir(int64_t(cf.v[u]) * 3 + c);
+    };
+    auto face_at = [&](int32_t k) __attribute__((always_inline)) {
+        return A.sface[cf0 + min(k, ncf - 1)];
+    };
+    In cur;
+    load_in(face_at(lane), cur);
+    SliceFace cfn = face_at(kFaceRound + lane);
+    for (int32_t base = 0; base < ncf; base += kFaceRound) {  // wave-uniform
+        In nxt;
+        if (base + kFaceRound < ncf) load_in(cfn, nxt);  // wave-uniform
+        const SliceFace cfn2 = face_at(base + 2 * kFaceRound + lane);
+        T Fv[6], w[3][2];
+        face_F(cur.q, Fv);
+        face_w(cur.q.m, w);
+        DualHv<T, 6> F[6];
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                F[2 * sp + c] = DualHv<T, 6>::var(
+                    Fv[2 * sp + c], 2 * sp + c,
+                    w[0][c] * cur.du[0][sp] + w[1][c] * cur.du[1][sp] + w[2][c] * cur.du[2][sp]);
+        const DualHv<T, 6> en = face_energy(F, cur.q.area);
+        if (base + lane < ncf)
+#pragma unroll
+            for (int u = 0; u < 3; ++u)
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp)
+                    rec[(3 * u + sp) * kFaceRound + lane] =
+                        w[u][0] * en.gt[2 * sp] + w[u][1] * en.gt[2 * sp + 1];
+        wave_lds_sync();
+        // this round's faces of the row: each register copy checked in turn
+        const uint32_t lo = uint32_t(base), hi = uint32_t(base + kFaceRound);
+#pragma unroll
+        for (int j = 0; j < kRowFaceRegs; ++j)
+            if (j < nrf && rf[j].lf >= lo && rf[j].lf < hi) gather(rf[j], base);
+        for (int32_t kk = h.f0 + kRowFaceRegs; kk < h.f0 + nrf; ++kk) {  // long rows only
+            const RowFace e = A.rfinc[kk];
+            if (e.lf >= lo && e.lf < hi) gather(e, base);
+        }
+        wave_lds_sync();
+        cur = nxt;
+        cfn = cfn2;
+    }
 }
 
 // Every row's topology terms (springs, faces, inertia); the runtime
@@ -870,12 +1091,14 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     __shared__ double red[kHvpThreads / 64];
     __shared__ double sum_bc;
     __shared__ int32_t stop_bc;
+    // per wave: one round of face records (face term only)
+    __shared__ T frec[FACES ? kSliceWaves * kFaceHvpFields * kFaceRound : 1];
     double beta = 0.0;
     T beta_t = T(0);  // beta in the working precision
     // operand component i: v[i], or the next Newton-CG direction -r + beta d,
     // one fused multiply-add in the working precision (the same formula for
     // a row's own direction, which it stores, and for its neighbours')
-    auto dir = [&](int64_t i) -> T {
+    auto dir = [&](int64_t i) __attribute__((always_inline)) -> T {
         if constexpr (CG) return cg_dir_comp(cg.r[i], cg.d_old[i], beta_t);
         else return v[i];
     };
@@ -884,6 +1107,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     // load.  A workgroup takes a contiguous slice range (ranges grouped by
     // XCD) and its waves walk it four slices apart.
     const int lane = int(threadIdx.x) & (kSliceRows - 1);
+    T *rec = frec + (FACES ? (int(threadIdx.x) / kSliceRows) * kFaceHvpFields * kFaceRound : 0);
     int32_t t0, t1, tn;
     slice_range(A.nv, t0, t1, tn);
     SliceRow<T> hn;
@@ -907,8 +1131,8 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         const SliceRow<T> h = hn;
         tn += kSliceWaves;
         if (tn < t1) slice_head<T, FACES, CG>(A, tn, lane, x, v, cg, hn);
-        const int32_t a = t * kSliceRows + lane;
-        const bool live = a < A.nv;
+        const int32_t a = h.a;
+        const bool live = h.live != 0;
         const int32_t p = A.sl_ptr[t];
         const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;
         T va[3], Y[3] = {T(0), T(0), T(0)};
@@ -925,7 +1149,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         for (int32_t j0 = 0; j0 < ns; j0 += kSliceBatch) {  // wave-uniform
             int32_t nb[kSliceBatch];
             T L[kSliceBatch];
-            slice_batch<T, FACES>(A, h, p, ns, j0, lane, live ? a : 0, nb, L);
+            slice_batch<T, FACES>(A, h, p, ns, j0, lane, a, nb, L);
             T xb[kSliceBatch][3], vb[kSliceBatch][3];
 #pragma unroll
             for (int j = 0; j < kSliceBatch; ++j)
@@ -947,53 +1171,7 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
                 for (int k = 0; k < 3; ++k) Y[k] += e.gt[k];
             }
         }
-        if constexpr (FACES) {
-            Row<T> r{};
-            r.a = live ? a : A.nv - 1;
-            r.f0 = live ? h.f0 : 0;
-            r.f1 = live ? h.f1 : 0;
-#pragma unroll
-            for (int k = 0; k < 3; ++k) r.xa[k] = h.xa[k];
-            for (int32_t base = r.f0; base < r.f1; base += kFaceBatch) {
-                FaceBatch<T> q;
-                load_faces(A, r, base, x, q);
-                T vo[kFaceBatch][2][3];
-#pragma unroll
-                for (int j = 0; j < kFaceBatch; ++j)
-#pragma unroll
-                    for (int k = 0; k < 3; ++k) {
-                        vo[j][0][k] = dir(int64_t(q.e[j].o1) * 3 + k);
-                        vo[j][1][k] = dir(int64_t(q.e[j].o2) * 3 + k);
-                    }
-#pragma unroll
-                for (int j = 0; j < kFaceBatch; ++j) {
-                    if (base + j >= r.f1) break;
-                    const int i = int(q.e[j].pk & 3u);
-                    T Fv[6], w[3][2];
-                    face_F(r, q, j, i, Fv, w);
-                    // direction in F: dF = (dF/dp) v_face
-                    DualHv<T, 6> F[6];
-#pragma unroll
-                    for (int sp = 0; sp < 3; ++sp) {
-                        const T v0 = i == 0 ? va[sp] : (i == 1 ? vo[j][1][sp] : vo[j][0][sp]);
-                        const T v1 = i == 1 ? va[sp] : (i == 2 ? vo[j][1][sp] : vo[j][0][sp]);
-                        const T v2 = i == 2 ? va[sp] : (i == 0 ? vo[j][1][sp] : vo[j][0][sp]);
-#pragma unroll
-                        for (int c = 0; c < 2; ++c)
-                            F[2 * sp + c] = DualHv<T, 6>::var(
-                                Fv[2 * sp + c], 2 * sp + c,
-                                w[0][c] * v0 + w[1][c] * v1 + w[2][c] * v2);
-                    }
-                    const DualHv<T, 6> e = face_energy(F, q.area[j]);
-                    // y_a += (dF/dp_a)^T (d2E/dF2 dF)
-                    const T wa0 = i == 0 ? w[0][0] : (i == 1 ? w[1][0] : w[2][0]);
-                    const T wa1 = i == 0 ? w[0][1] : (i == 1 ? w[1][1] : w[2][1]);
-#pragma unroll
-                    for (int sp = 0; sp < 3; ++sp)
-                        Y[sp] += wa0 * e.gt[2 * sp] + wa1 * e.gt[2 * sp + 1];
-                }
-            }
-        }
+        if constexpr (FACES) slice_faces(A, t, h, rec, x, dir, Y);
         if (A.inertia_on) {
             // seeded at z = 0 (x_tilde not loaded): the Hessian c I is the same
             DualHv<T, 3> z[3];
@@ -1114,8 +1292,8 @@ k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__
         const SliceRow<T> h = hn;
         tn += kSliceWaves;
         if (tn < t1) slice_head<T, false, false>(A, tn, lane, x, v, none, hn);
-        const int32_t a = t * kSliceRows + lane;
-        const bool live = a < A.nv;
+        const int32_t a = h.a;
+        const bool live = h.live != 0;
         const int32_t p = A.sl_ptr[t];
         const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;
         T Y[3] = {T(0), T(0), T(0)};
@@ -1123,7 +1301,7 @@ k_gn_rows(RowArgs<T> A, T sqrt_k, T sqrt_c, const T *__restrict__ x, const T *__
         for (int32_t j0 = 0; j0 < ns; j0 += kSliceBatch) {  // wave-uniform
             int32_t nb[kSliceBatch];
             T L[kSliceBatch];
-            slice_batch<T, false>(A, h, p, ns, j0, lane, live ? a : 0, nb, L);
+            slice_batch<T, false>(A, h, p, ns, j0, lane, a, nb, L);
             T xb[kSliceBatch][3], vb[kSliceBatch][3];
 #pragma unroll
             for (int j = 0; j < kSliceBatch; ++j)
@@ -1227,10 +1405,19 @@ static void launch_eval_rows_as(const RowArgs<T> &a, const T *x, T *g, T *hv, En
                        es);
 }
 
+// The face tables the row kernels read when the face term is on.
+template <typename T>
+static bool face_tables_ok(const RowArgs<T> &a)
+{
+    return !a.faces_on ||
+           (a.fptr && a.finc && a.rfinc && a.sf_ptr && a.sface && a.face_dm && a.face_area);
+}
+
 template <typename T>
 hipError_t launch_eval_pair_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                                  int grid, hipStream_t s)
 {
+    if (!face_tables_ok(a)) return hipErrorInvalidValue;
     for (int k = 1; k <= 2; ++k)  // the contact buffers the kernel may read
         if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pairs[k] || !a.pat.pinc_ptr[k] ||
             !a.pat.pinc[k] || !a.pat.trow[k])
@@ -1250,6 +1437,7 @@ hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, Energy
                             int grid, hipStream_t s)
 {
     const int lds = rows_lds_bytes<T>(a.lds_blocks);
+    if (!face_tables_ok(a)) return hipErrorInvalidValue;
     if (a.pairs_on)  // the buffers the contact-capacity variant reads
         for (int k = 1; k <= 2; ++k)
             if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pinc_ptr[k] || !a.pat.pnew[k])
@@ -1279,6 +1467,7 @@ template <typename T>
 hipError_t launch_hvp_rows(const RowArgs<T> &a, const T *x, const T *v, T *y, int grid,
                            hipStream_t s, const CgDir<T> &cg)
 {
+    if (!face_tables_ok(a) || !a.sl_ptr) return hipErrorInvalidValue;
     if (a.faces_on)
         launch_hvp_rows_as<T, true>(a, x, v, y, grid, s, cg);
     else

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <map>
+#include <map>
 #include <random>
 #include <set>
 #include <string>
@@ -313,6 +314,50 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
             CHECK(i < 3 && t[i] == a && e.o1 == t[(i + 1) % 3] && e.o2 == t[(i + 2) % 3], "%s: row %d face %d vertices", tag, a, f);
             for (int u = 0; u < 3; ++u)
                 CHECK(int32_t((e.pk >> (8 * u + 8)) & 255u) == slot_of(rp, ci, a, t[u]) - rp[a], "%s: row %d face %d slot", tag, a, f);
+        }
+    }
+    // slice face lists of the product kernels: each face incident to a
+    // slice's rows exactly once, ordered by (its first position in an
+    // incident row's id-sorted face list, that row); every row's faces by
+    // their position in its slice's list, with the row's position in the face
+    CHECK(int32_t(plan.sf_ptr.size()) == nsl + 1 && plan.sf_ptr[0] == 0, "%s: slice face offsets", tag);
+    if (int32_t(plan.sf_ptr.size()) != nsl + 1) return;
+    CHECK(size_t(plan.sf_ptr[nsl]) == plan.sface.size(), "%s: slice face count", tag);
+    CHECK(plan.rfinc.size() == plan.finc.size(), "%s: row face records", tag);
+    for (int32_t t = 0; t < nsl; ++t) {
+        const int32_t v0 = t * kSliceRows, v1 = std::min(m.nv, (t + 1) * kSliceRows);
+        std::map<int32_t, std::pair<int32_t, int32_t>> key;  // face -> (rank, row)
+        for (int32_t a = v0; a < v1; ++a)
+            for (size_t r = 0; r < inc[a].size(); ++r) {
+                const auto k = std::make_pair(int32_t(r), a);
+                auto it = key.find(inc[a][r]);
+                if (it == key.end() || k < it->second) key[inc[a][r]] = k;
+            }
+        const int32_t n = plan.sf_ptr[t + 1] - plan.sf_ptr[t];
+        CHECK(n == int32_t(key.size()), "%s: slice %d lists %d faces, %zu incident", tag, t, n, key.size());
+        if (n != int32_t(key.size())) continue;
+        std::vector<std::pair<std::pair<int32_t, int32_t>, int32_t>> order;
+        for (const auto &kv : key) order.push_back({kv.second, kv.first});
+        std::sort(order.begin(), order.end());
+        for (int32_t k = 0; k < n; ++k) {
+            const SliceFace &sf = plan.sface[size_t(plan.sf_ptr[t] + k)];
+            const int32_t f = order[size_t(k)].second;
+            CHECK(sf.f == f, "%s: slice %d list position %d", tag, t, k);
+            for (int i = 0; i < 3; ++i) CHECK(sf.v[i] == m.faces[3 * size_t(f) + i], "%s: face %d vertices", tag, f);
+        }
+        for (int32_t a = v0; a < v1; ++a) {
+            std::vector<int32_t> got;
+            for (int32_t k = plan.fptr[a]; k < plan.fptr[a + 1] && size_t(k) < plan.rfinc.size(); ++k) {
+                const RowFace &e = plan.rfinc[size_t(k)];
+                CHECK(k == plan.fptr[a] || plan.rfinc[size_t(k - 1)].lf < e.lf, "%s: row %d faces not in list order", tag, a);
+                CHECK(int32_t(e.lf) < n, "%s: row %d face position", tag, a);
+                if (int32_t(e.lf) >= n) continue;
+                const int32_t f = plan.sface[size_t(plan.sf_ptr[t] + int32_t(e.lf))].f;
+                got.push_back(f);
+                CHECK(m.faces[3 * size_t(f) + (e.pi & 3u)] == a, "%s: row %d face %d position", tag, a, f);
+            }
+            std::sort(got.begin(), got.end());
+            CHECK(got == inc[a], "%s: row %d faces", tag, a);
         }
     }
 }
