@@ -151,7 +151,10 @@ struct RowFace {
 };
 
 struct RowPlan {
-    std::vector<PatchHdr> chunk;     // v0, nown (rows), blk0, nblk, amap_cap
+    std::vector<PatchHdr> chunk;     // v0, nown (rows), blk0, nblk, amap_cap, and spr_off:
+                                     // the spring slice whose rows the chunk is, when
+                                     // every off-diagonal block of its rows has a
+                                     // spring behind it, else -1
     std::vector<double> slot_rest;   // [nnzb] rest length behind each block, -1: none
     // face term on:
     std::vector<int32_t> fptr;       // [nv+1] offsets of each row's faces in finc and rfinc

@@ -374,7 +374,7 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
                             out.sl_rest[size_t(e0 + kSliceRows * j)] = out.slot_rest[size_t(k)];
                             ++j;
                         }
-                for (; j < w; ++j) out.sl_nb[size_t(e0 + kSliceRows * j)] = a < nv ? int32_t(a) : 0;
+                for (; j < w; ++j) out.sl_nb[size_t(e0 + kSliceRows * j)] = a < nv ? int32_t(a) : nv - 1;
             }
         }
     }
@@ -460,6 +460,17 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         h.blk0 = rp[v0];
         h.nblk = blk;
         h.amap_cap = kRowLdsBlocks;
+        // a chunk that is exactly one spring slice and whose rows hold only
+        // their diagonal and their springs' blocks reads its springs from the
+        // slice (spr_off = the slice), else from its rows (-1)
+        h.spr_off = -1;
+        if (v0 % kSliceRows == 0 && n == std::min(kSliceRows, nv - v0)) {
+            bool dense = true;
+            for (int32_t a = v0; a < v0 + n && dense; ++a)
+                for (int32_t k = rp[a]; k < rp[a + 1] && dense; ++k)
+                    dense = ci[k] == a || out.slot_rest[size_t(k)] >= 0.0;
+            if (dense) h.spr_off = v0 / kSliceRows;
+        }
         out.chunk.push_back(h);
         v0 += n;
     }

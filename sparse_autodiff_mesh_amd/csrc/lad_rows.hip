@@ -603,6 +603,62 @@ __device__ __forceinline__ void row_slots(const RowArgs<T> &A, int act, const in
     }
 }
 
+// The spring blocks of a row of a chunk that is exactly spring slice t and
+// whose rows hold only their diagonal and their springs' blocks (lane
+// `lane`, row r.a): spring j (its j-th neighbour in ascending column
+// order) comes from the slice with one coalesced load per j for the whole
+// wave and sits at slot s0 + j, moved one on past the diagonal when its
+// column is above the row; the diagonal's slot follows from the number of
+// neighbours below.  The same blocks, in the same order, as row_slots.
+constexpr int kDenseBatch = 6;  // springs whose loads a lane issues together
+
+template <typename T>
+__device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t, int lane,
+                                                  const Row<T> &r, int32_t sb, T *Hs,
+                                                  const T *__restrict__ x, RowAcc<T> &acc)
+{
+    const int32_t p = A.sl_ptr[t];
+    const int32_t ns = (A.sl_ptr[t + 1] - p) / kSliceRows;  // wave-uniform
+    int32_t below = 0;
+    for (int32_t j0 = 0; j0 < ns; j0 += kDenseBatch) {
+        int32_t nb[kDenseBatch];
+        T L[kDenseBatch], xb[kDenseBatch][3];
+#pragma unroll
+        for (int j = 0; j < kDenseBatch; ++j) {
+            const int64_t e = p + int64_t(min(j0 + j, ns - 1)) * kSliceRows + lane;
+            nb[j] = A.sl_nb[e];
+            L[j] = j0 + j < ns ? A.sl_rest[e] : T(-1);
+        }
+#pragma unroll
+        for (int j = 0; j < kDenseBatch; ++j)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) xb[j][c] = x[int64_t(nb[j]) * 3 + c];
+#pragma unroll
+        for (int j = 0; j < kDenseBatch; ++j) {
+            if (!(L[j] >= T(0))) continue;  // padding: the row has fewer springs
+            const bool above = nb[j] > r.a;
+            below += above ? 0 : 1;
+            T *B = Hs + 9 * (r.s0 + j0 + j + (above ? 1 : 0) - sb);
+            Dual2<T, 3> d[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(r.xa[c] - xb[j][c], c);
+            const Dual2<T, 3> e = spring_energy(d, L[j], A.k);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                acc.G[i] += e.g[i];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    const T h = e.hess(i, k);
+                    B[3 * i + k] = -h;
+                    acc.D[3 * i + k] += h;
+                }
+            }
+            if (above) acc.E += double(e.v);
+        }
+    }
+    acc.dslot = r.s0 + below;
+}
+
 template <typename T>
 __device__ __forceinline__ void row_inertia(const RowArgs<T> &A, const Row<T> &r, RowAcc<T> &acc)
 {
@@ -809,6 +865,7 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
     double eacc = 0.0;
     for (int c = c0; c < c1; ++c) {
         const int32_t v0 = A.chunk[c].v0, nrows = A.chunk[c].nown;
+        const int32_t dense_t = A.chunk[c].spr_off;  // its spring slice, or -1
         const int32_t sb = rpa[v0];
         const int32_t nblk = rpa[v0 + nrows] - sb;
         // The insertion check keeps every chunk within the staging capacity;
@@ -842,7 +899,10 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
             }
             PairPre<T> pp;
             prefetch_pairs(A, 0, 0, r, x, pp);
-            row_slots<T, false, PAIRS>(A, 0, cia, r, rt, ins, sb, Hs, x, acc, pp);
+            if (!PAIRS && A.springs_on && dense_t >= 0)  // wave-uniform
+                row_slice_springs(A, dense_t, int(threadIdx.x), r, sb, Hs, x, acc);
+            else
+                row_slots<T, false, PAIRS>(A, 0, cia, r, rt, ins, sb, Hs, x, acc, pp);
             if constexpr (FACES) row_faces<T, PAIRS>(A, 0, cia, r, ins, sb, Hs, x, acc);
         }
         if (own) {

@@ -241,6 +241,15 @@ void check_patch_plan(const Mesh &m, bool faces_on, int es, int budget, const ch
         }
 }
 
+bool has_spring(const Mesh &m, int32_t a, int32_t b)
+{
+    for (size_t s = 0; s * 2 < m.springs.size(); ++s)
+        if ((m.springs[2 * s] == a && m.springs[2 * s + 1] == b) ||
+            (m.springs[2 * s] == b && m.springs[2 * s + 1] == a))
+            return true;
+    return false;
+}
+
 void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
 {
     std::vector<int32_t> rp, ci;
@@ -255,6 +264,12 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
         CHECK(h.v0 == expect_v0 && h.nown > 0 && h.nown <= kRowsPerChunk, "%s: chunk rows", tag);
         CHECK(h.nblk == rp[h.v0 + h.nown] - rp[h.v0] && h.nblk <= kRowBaseBlocks, "%s: chunk blocks", tag);
         CHECK(h.amap_cap == kRowLdsBlocks, "%s: chunk capacity", tag);
+        // slice-aligned chunks whose off-diagonal blocks all carry springs
+        bool dense = h.v0 % kSliceRows == 0 && h.nown == std::min(kSliceRows, m.nv - h.v0);
+        for (int32_t a = h.v0; a < h.v0 + h.nown && dense; ++a)
+            for (int32_t k = rp[a]; k < rp[a + 1]; ++k)
+                if (ci[k] != a && !has_spring(m, a, ci[k])) dense = false;
+        CHECK(h.spr_off == (dense ? h.v0 / kSliceRows : -1), "%s: chunk %d slice flag", tag, h.v0);
         expect_v0 = h.v0 + h.nown;
     }
     CHECK(expect_v0 == m.nv, "%s: chunks do not cover the rows", tag);
@@ -293,7 +308,7 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
                     CHECK(plan.sl_nb[e] == sp[a][j].first && plan.sl_rest[e] == sp[a][j].second,
                           "%s: row %d spring %d", tag, a, j);
                 else
-                    CHECK(plan.sl_nb[e] == (a < m.nv ? a : 0) && plan.sl_rest[e] == -1.0,
+                    CHECK(plan.sl_nb[e] == (a < m.nv ? a : m.nv - 1) && plan.sl_rest[e] == -1.0,
                           "%s: row %d padding %d", tag, a, j);
             }
         }

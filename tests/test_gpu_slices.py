@@ -154,3 +154,60 @@ def test_hvp_tiny(lad, dtype):
         if springs is None:
             assert rel(yg.cpu().numpy(), C * v_h) <= TOL[dtype]
         L.close()
+
+
+def far_mesh(nv, extra, seed):
+    """A chain over nv vertices plus `extra` random pairs anywhere: springs
+    join vertices up to nv - 1 apart."""
+    u = inputs.uniform_block(seed, 3 * nv + 2 * extra + nv)
+    x = 0.5 * (u[:3 * nv].reshape(nv, 3) + 1.0)
+    pairs = {(a, a + 1) for a in range(nv - 1)}
+    r = u[3 * nv:3 * nv + 2 * extra]   # uniform in [0, 1)
+    for k in range(extra):
+        a = int(r[2 * k] * nv) % nv
+        b = int(r[2 * k + 1] * nv) % nv
+        if a != b:
+            pairs.add((min(a, b), max(a, b)))
+    springs = np.array(sorted(pairs), dtype=np.int32)
+    d = np.linalg.norm(x[springs[:, 0]] - x[springs[:, 1]], axis=1)
+    rest = d * (1.0 - 0.01 * np.abs(np.resize(u[3 * nv + 2 * extra:], len(springs))))
+    return x, springs, rest
+
+
+@pytest.mark.parametrize("case", ["hubs300_f64", "hubs300_f32", "hubs1000_f32", "far40000_f32",
+                                  "far40000_f64"])
+def test_eval_irregular(lad, case):
+    """The explicit evaluation on the irregular spring meshes: chunks that
+    are exactly one slice and hold only diagonal and spring blocks read
+    their springs from the slice, the other chunks (rows cut short by the
+    hubs' long rows) walk their rows; on the far mesh springs join vertices
+    up to 39,424 apart.  E, g, H and H v against the oracle."""
+    import torch
+    log_case(test="slices_eval", case=case)
+    dtype = case[-3:]
+    if case.startswith("far"):
+        nv = 40000
+        x, springs, rest = far_mesh(nv, 4000, seed=77)
+        assert np.abs(springs[:, 1] - springs[:, 0]).max() > 32767
+    else:
+        nv = int(case[4:case.index("_")])
+        x, springs, rest = spring_mesh(nv, 3 * nv, 2, seed=40 + nv)
+    xt = x + 0.01
+    L = lad.Lad(nv, dtype=dtype, springs=springs, rest_len=rest, k=K, x_tilde=xt, c=C)
+    assert L.get_info()["eval_path"] == lad.LAD_PATH_ROWS
+    prob = oracle.Problem(nv=nv, springs=springs, rest_len=host_input(rest, dtype), k=K,
+                          x_tilde=host_input(xt, dtype), c=C)
+    x_h = host_input(x, dtype)
+    E, g, H = L.eval(dev(x_h, dtype))
+    v_h = host_input(inputs.hvp_direction(nv), dtype)
+    y = L.hvp(dev(x_h, dtype), dev(v_h, dtype))
+    rp, ci = L.pattern()
+    torch.cuda.synchronize()
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    assert rel([E.item()], [Eo]) <= TOL[dtype]
+    assert rel(g.cpu().numpy(), go) <= TOL[dtype]
+    assert rel(H.cpu().numpy()[: oci.size], Ho) <= TOL[dtype]
+    assert rel(y.cpu().numpy(), oracle.bsr_spmv(orp, oci, Ho, v_h)) <= TOL[dtype]
+    L.close()
