@@ -70,6 +70,18 @@ def compulsory_bytes_eval(nv, ns, nf, nnzb, es, inertia=True, faces=False, npair
     return b
 
 
+def compulsory_bytes_pair_step(L, m, npairs):
+    """One contact step (insert the step's pairs, then evaluate): the pair
+    list read and the new row pointers written by the insertion, then the
+    evaluation's compulsory bytes on the active pattern (its nnzb includes
+    the pairs' new blocks)."""
+    info = L.get_info()
+    b = 8 * npairs + 4 * (m.nv + 1)
+    b += compulsory_bytes_eval(m.nv, m.springs.shape[0], 0, info["nnzb_active"], 4,
+                               npairs=npairs)
+    return b
+
+
 def compulsory_bytes_terms(nv, blocks, nnzb, es, hvp=False):
     """Term front end: every element's vertex ids and constants once, x (and
     v), g (or y), and for the explicit call the H blocks once."""
@@ -326,6 +338,49 @@ def bench_faces_only(torch, binding, inputs, args, timer):
             "hvp_GBps": round(bh / (rh["mean_ms"] * 1e-3) / 1e9, 1)}
 
 
+def bench_pairs_only(torch, binding, inputs, args, timer):
+    """The 1000 x 1000 cloth with 2 % contact pairs per step alone (for
+    kernel traces and counter runs): a step inserts the step's pairs, then
+    evaluates; one line of JSON with the step, insertion and evaluation
+    timings and the step's compulsory bytes."""
+    m = inputs.cloth(args.n)
+    dhat = 0.5 * m.h
+    P = int(round(0.02 * m.nv))
+    L = cloth_ctx(binding, m, "f32", pair_capacity=P, dhat=dhat, kappa=inputs.BARRIER_KAPPA)
+    sets = []
+    for step in range(3):
+        pairs, xs = inputs.contact_pairs(m, m.x, step=step)
+        sets.append((torch.tensor(pairs, dtype=torch.int32, device="cuda"),
+                     to_dev(torch, xs, "f32")))
+    out = L.alloc_outputs()
+    state = {"i": 0}
+
+    def step_fn():
+        p, xx = sets[state["i"] % len(sets)]
+        state["i"] += 1
+        L.insert_pairs(p)
+        L.eval(xx, out=out)
+
+    r = timer.run(step_fn, args.steps, args.warmup)
+    ri = timer.run(lambda: L.insert_pairs(sets[0][0]), args.steps, args.warmup)
+    L.insert_pairs(sets[0][0])
+    re = timer.run(lambda: L.eval(sets[0][1], out=out), args.steps, args.warmup)
+    bstep = compulsory_bytes_pair_step(L, m, P)
+    if L.device_status() != 0:
+        raise RuntimeError("pair insertion reported a device-side error")
+    L.close()
+    return {"workload": f"mass-spring cloth {args.n}x{args.n} + {P} contact pairs per step, "
+                        "fp32: insert, then gradient + block-CSR Hessian",
+            "kernels": ["k_ins_count", "k_ins_bucket", "k_ins_tiles",
+                        "k_eval_rows<float, false, true>", "k_eval_pair_rows<float, false>"],
+            "steps": args.steps, "warmup": args.warmup,
+            "step_ms_median": round(r["median_ms"], 5),
+            "insert_ms_median": round(ri["median_ms"], 5),
+            "eval_ms_median": round(re["median_ms"], 5),
+            "step_bytes": bstep,
+            "step_hbm_frac": round(bstep / (r["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def bench_terms_cloth_only(torch, inputs, args, timer):
     """The term front end's generic cloth set alone (for counter runs): its
     fused explicit evaluation, then its product, with their event timings."""
@@ -472,6 +527,10 @@ def bench_secondary(torch, binding, inputs, args, timer):
 
     r = timer.run(step_fn, steps, warm)
     sec["cloth1000_pairs_insert_eval_ms"] = round(r["median_ms"], 5)
+    bstep = compulsory_bytes_pair_step(L, m, P)
+    sec["cloth1000_pairs_step_bytes"] = bstep
+    sec["cloth1000_pairs_step_hbm_frac"] = round(
+        bstep / (r["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
     rh = timer.run(lambda: L.hvp(sets[0][1], vdir, out=yv), steps, warm)
     sec["cloth1000_pairs_hvp_ms"] = round(rh["median_ms"], 5)
     ri = timer.run(lambda: L.insert_pairs(sets[0][0]), steps, warm)
@@ -646,6 +705,8 @@ def main():
     ap.add_argument("--faces-only", action="store_true",
                     help="only time the 512x512 face grid, eval kernel then HVP (prints its "
                          "own JSON line; for counter runs)")
+    ap.add_argument("--pairs-only", action="store_true",
+                    help="time only the cloth step with contact pairs (for traces and counters)")
     ap.add_argument("--terms-cloth-only", action="store_true",
                     help="only time the term front end's cloth set, eval then HVP (prints "
                          "its own JSON line; for counter runs)")
@@ -686,6 +747,9 @@ def main():
         return 0
     if args.terms_cloth_only:
         print(json.dumps(bench_terms_cloth_only(torch, inputs, args, timer)))
+        return 0
+    if args.pairs_only:
+        print(json.dumps(bench_pairs_only(torch, binding, inputs, args, timer)))
         return 0
     log(f"bench: cloth {args.n}x{args.n} fp32, steps={args.steps} warmup={args.warmup}")
     res = bench_headline(torch, binding, inputs, args, timer)

@@ -136,6 +136,9 @@ std::string check_desc(const lad_mesh_desc *d)
     if (d->dtype != LAD_F32 && d->dtype != LAD_F64) return "dtype must be LAD_F32 or LAD_F64";
     if (d->pair_capacity < 0) return "pair_capacity must be >= 0";
     if (d->vf_capacity < 0) return "vf_capacity must be >= 0";
+    if (int64_t(d->pair_capacity) + d->vf_capacity > int64_t(kInsMaxWg) * kThreads)
+        return "pair_capacity + vf_capacity must be at most " +
+               std::to_string(int64_t(kInsMaxWg) * kThreads);
     if (d->vf_capacity > 0 && d->nf == 0) return "vertex-face contacts need faces";
     if (d->vf_capacity > 0 && d->eval_path == LAD_PATH_PATCH)
         return "vertex-face contacts need the row path";
@@ -652,17 +655,19 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (e == hipSuccess) e = upload(ctx, &ctx->d_fac, plan.fac, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_col_bounds, plan.col_bounds, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_diag_rel, plan.diag_rel, s);
-    // row path with pair capacity: the chunk of every row, for the
-    // insertion's capacity check (uploaded before the sync below)
-    // (the pointer is stored in ctx->ins after that struct is reset below)
-    std::vector<int32_t> row_chunk;
-    int32_t *d_row_chunk = nullptr;
-    if (e == hipSuccess && ctx->row_mode && (d->pair_capacity > 0 || d->vf_capacity > 0)) {
-        row_chunk.resize(size_t(nv));
-        for (size_t c = 0; c < plan.hdr.size(); ++c)
-            for (int32_t a = plan.hdr[c].v0; a < plan.hdr[c].v0 + plan.hdr[c].nown; ++a)
-                row_chunk[size_t(a)] = int32_t(c);
-        e = upload(ctx, &d_row_chunk, row_chunk, s);
+    // with pair capacity: the insertion's tiles (whole row chunks on the row
+    // path, for its capacity check; fixed row blocks on the patch path)
+    // (the pointers are stored in ctx->ins after that struct is reset below)
+    InsertTiles itiles;
+    int32_t *d_tile_row = nullptr, *d_tile_unit = nullptr, *d_row_tile = nullptr,
+            *d_row_unit = nullptr;
+    if (e == hipSuccess && (d->pair_capacity > 0 || d->vf_capacity > 0)) {
+        const std::string msg = build_insert_tiles(plan.hdr, nv, ctx->row_mode, itiles);
+        if (!msg.empty()) return fail(ctx, LAD_ERR_ARG, "insertion tiles: " + msg);
+        e = upload(ctx, &d_tile_row, itiles.tile_row, s);
+        if (e == hipSuccess) e = upload(ctx, &d_tile_unit, itiles.tile_unit, s);
+        if (e == hipSuccess) e = upload(ctx, &d_row_tile, itiles.row_tile, s);
+        if (e == hipSuccess && ctx->row_mode) e = upload(ctx, &d_row_unit, itiles.row_unit, s);
     }
     if (e != hipSuccess) return hip_fail(ctx, e, "upload of patch tables");
     lad_status st = ctx->dtype == LAD_F64 ? upload_constants<double>(ctx, d, plan, rplan, s)
@@ -685,7 +690,11 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     // ---- pattern buffers, device state, scratch
     std::memset(&ctx->pat, 0, sizeof(ctx->pat));
     std::memset(&ctx->ins, 0, sizeof(ctx->ins));
-    ctx->ins.row_chunk = d_row_chunk;
+    ctx->ins.tile_row = d_tile_row;
+    ctx->ins.tile_unit = d_tile_unit;
+    ctx->ins.row_tile = d_row_tile;
+    ctx->ins.row_unit = d_row_unit;
+    ctx->ins.ntiles = int32_t(itiles.tile_row.empty() ? 0 : itiles.tile_row.size() - 1);
     ctx->pat.rp[0] = d_rp0;
     ctx->pat.ci[0] = d_ci0;
     ctx->ins.rp[0] = d_rp0;
@@ -708,12 +717,19 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pinc_row[b], ninc);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pnew[b], 3 * ninc);
             if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.trow[b], ninc);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.pslot[b], ninc);
+            if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.rins1[b], size_t(nv));
         }
-        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.cnt, size_t(nv));
-        if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.cnt, 0, size_t(nv) * 4, s);
-        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.nnew, size_t(nv));
-        if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.nnew, 0, size_t(nv) * 4, s);
-        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.tmp, size_t(scan_tmp_size(nv)));
+        const size_t nt = size_t(ctx->ins.ntiles);
+        const size_t nel = size_t(d->pair_capacity) + size_t(d->vf_capacity);
+        ctx->ins.max_wg = int32_t((nel + kThreads - 1) / kThreads);
+        const size_t wg = size_t(ctx->ins.max_wg);
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.tstat, nt * kStatStride);
+        if (e == hipSuccess) e = hipMemsetAsync(ctx->ins.tstat, 0, nt * kStatStride * 8, s);
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.hist, nt * wg);
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.hoff, nt * wg);
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.seg, 2 * wg * size_t(kInsWgEnt));
+        if (e == hipSuccess) e = dev_alloc(ctx, &ctx->ins.erank, wg * size_t(kInsWgEnt));
         for (int b = 1; b <= 2; ++b) {
             ctx->pat.rp[b] = ctx->ins.rp[b];
             ctx->pat.ci[b] = ctx->ins.ci[b];
@@ -723,6 +739,8 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
             ctx->pat.pinc_row[b] = ctx->ins.pinc_row[b];
             ctx->pat.trow[b] = ctx->ins.trow[b];
             ctx->pat.pnew[b] = ctx->ins.pnew[b];
+            ctx->pat.pslot[b] = ctx->ins.pslot[b];
+            ctx->pat.rins1[b] = ctx->ins.rins1[b];
             ctx->pat.vf[b] = ctx->ins.vf[b];
         }
         ctx->ins.faces = ctx->d_faces;

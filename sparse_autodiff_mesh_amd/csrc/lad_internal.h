@@ -60,13 +60,18 @@ static_assert(sizeof(PatchHdr) == 64, "PatchHdr layout");
 // lad_insert_pairs writes it.
 struct DevState {
     int32_t active;
-    int32_t err_latched;     // sticky error bits: 1 = bad pair, 2 = capacity
+    int32_t err_latched;     // sticky error bits: 1 = bad pair, 2 = capacity,
+                             // 4 = the insertion's tile chain did not complete
     int32_t err_cur;         // error bits of the insert in flight (zero
-                             // between inserts: the commit kernel clears it)
+                             // between inserts: the commit clears it)
     int32_t np[3];           // pairs of each buffer
     int32_t nnzb[3];         // blocks of each buffer
     int32_t nvf[3];          // vertex-face contacts of each buffer
-    int32_t pad[4];
+    int32_t ins_back;        // buffer the insert in flight writes (set by its
+                             // first kernel, so the commit may flip `active`
+                             // while later workgroups still run)
+    uint32_t ins_seq;        // inserts so far: tags the tile chain's status
+    int32_t pad[2];
 };
 
 // ---------------------------------------------------------------------------
@@ -193,6 +198,12 @@ struct PatternBufs {
     const int32_t *pnew[3];      // per touched row, at 3 x its first incidence
                                  // entry: its columns that the topology row
                                  // lacks, ascending
+    const int32_t *rins1[3];     // per row: its smallest inserted column
+                                 // (INT32_MAX: none)
+    const int2 *pslot[3];        // per incidence entry (row path): slot, from
+                                 // the active row's start, of a pair's (row,
+                                 // partner) block (-1 for a vertex-face entry)
+                                 // and of the row's diagonal block
     const int32_t *vf[3];        // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)
 };
@@ -384,13 +395,44 @@ struct InsertBufs {
                                  // buffer is next written (the row kernels
                                  // read those of the active buffer)
     int32_t *trow[3];            // touched-row list, see PatternBufs::trow
+    int2 *pslot[3];              // see PatternBufs::pslot (row path)
+    int32_t *rins1[3];           // see PatternBufs::rins1
     int32_t *vf[3];              // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)
-    const int32_t *row_chunk;    // [nv] chunk of each row (row path)
-    int32_t *cnt;                // [nv], all zero between inserts
-    int32_t *nnew;               // [nv] new blocks per row, all zero between inserts
-    int32_t *tmp;                // scan scratch
+    // Insertion tiles: runs of whole units (row chunks on the row path, fixed
+    // row blocks on the patch path) of at most kInsTileRows rows.
+    int32_t ntiles;
+    const int32_t *tile_row;     // [ntiles+1] first row of each tile
+    const int32_t *tile_unit;    // [ntiles+1] first chunk of each tile (row path)
+    const int32_t *row_tile;     // [nv] tile of each row
+    const int32_t *row_unit;     // [nv] chunk of each row (row path)
+    unsigned long long *tstat;   // [ntiles * kStatStride] look-back status of each tile,
+                                 // one per 128-byte line (polled by many workgroups)
+    // The count kernel's output: per tile and count workgroup, the number of
+    // the workgroup's entries in the tile and their offset in its part of
+    // seg (tile-major); seg holds kInsWgEnt entries (two int4 each) per
+    // workgroup; erank is scratch beside seg.
+    int32_t max_wg;              // count workgroups at the contact capacity
+    int32_t *hist;               // [ntiles][max_wg]
+    int32_t *hoff;               // [ntiles][max_wg]
+    int4 *seg;                   // [max_wg * kInsWgEnt][2]
+    int32_t *erank;              // [max_wg * kInsWgEnt]
 };
+constexpr int kInsTileRows = 2048;   // rows per insertion tile, at most
+constexpr int kStatStride = 16;      // 8-byte words per tile status
+constexpr int kInsTileUnits = 256;   // row chunks per insertion tile, at most
+constexpr int kInsMaxTiles = 8192;   // tiles per pattern, at most (a count of each in LDS)
+constexpr int kInsMaxWg = 1024;      // count workgroups (of kThreads elements) per insert, at most
+constexpr int kInsWgEnt = 4 * kThreads;  // incidence entries of a count workgroup, at most
+// Tiles of the insertion over the row ranges `units` (contiguous, in row
+// order, covering 0 .. nv): whole units up to kInsTileRows rows and
+// kInsTileUnits units per tile when align_units, else kInsTileRows rows per
+// tile.  Empty string on success, else why the pattern cannot be tiled.
+struct InsertTiles {
+    std::vector<int32_t> tile_row, tile_unit, row_tile, row_unit;
+};
+std::string build_insert_tiles(const std::vector<PatchHdr> &units, int32_t nv, bool align_units,
+                               InsertTiles &out);
 // complete_cols = 0 writes the columns of pair-touched rows only (row
 // path); launch_complete_cols then fills in the other rows of the active
 // buffer on demand.

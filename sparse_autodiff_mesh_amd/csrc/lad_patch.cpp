@@ -477,4 +477,52 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
     return "";
 }
 
+std::string build_insert_tiles(const std::vector<PatchHdr> &units, int32_t nv, bool align_units,
+                               InsertTiles &out)
+{
+    out = InsertTiles();
+    if (nv <= 0) return "nv must be positive";
+    out.row_tile.assign(size_t(nv), 0);
+    out.tile_row.push_back(0);
+    out.tile_unit.push_back(0);
+    if (align_units) {
+        out.row_unit.assign(size_t(nv), 0);
+        int32_t next = 0;
+        for (size_t u = 0; u < units.size(); ++u) {
+            if (units[u].v0 != next || units[u].nown <= 0)
+                return "units must cover the rows in order";
+            if (units[u].nown > kInsTileRows) return "a row chunk exceeds the tile row limit";
+            next += units[u].nown;
+        }
+        if (next != nv) return "units must cover the rows in order";
+        int32_t rows = 0, nu = 0;
+        for (size_t u = 0; u < units.size(); ++u) {
+            if (nu > 0 && (rows + units[u].nown > kInsTileRows || nu == kInsTileUnits)) {
+                out.tile_row.push_back(units[u].v0);
+                out.tile_unit.push_back(int32_t(u));
+                rows = nu = 0;
+            }
+            rows += units[u].nown;
+            ++nu;
+            for (int32_t a = units[u].v0; a < units[u].v0 + units[u].nown; ++a)
+                out.row_unit[size_t(a)] = int32_t(u);
+        }
+        out.tile_row.push_back(nv);
+        out.tile_unit.push_back(int32_t(units.size()));
+    } else {
+        for (int32_t r = kInsTileRows; r < nv; r += kInsTileRows) {
+            out.tile_row.push_back(r);
+            out.tile_unit.push_back(0);
+        }
+        out.tile_row.push_back(nv);
+        out.tile_unit.push_back(0);
+    }
+    const size_t nt = out.tile_row.size() - 1;
+    if (nt > size_t(kInsMaxTiles)) return "too many rows for pair insertion";
+    for (size_t t = 0; t < nt; ++t)
+        for (int32_t a = out.tile_row[t]; a < out.tile_row[t + 1]; ++a)
+            out.row_tile[size_t(a)] = int32_t(t);
+    return "";
+}
+
 }  // namespace lad

@@ -208,22 +208,6 @@ hipError_t launch_scan(const int32_t *in, int32_t *out, int32_t n, int32_t *tmp,
     return scan_impl(in, DirectOut{out}, n, tmp, s);
 }
 
-// Scan whose output array is picked on the device (used by pair insertion),
-// optionally plus a per-element addend.
-struct BackOut {
-    int32_t *p[3];
-    const int32_t *addend;
-    const DevState *st;
-    __device__ int32_t *get() const { return p[st->active == 1 ? 2 : 1]; }
-    __device__ int32_t add(int64_t i) const { return addend ? addend[i] : 0; }
-};
-hipError_t launch_scan_back(const int32_t *in, int32_t *const out[3], const int32_t *add,
-                            const DevState *st, int32_t n, int32_t *tmp, hipStream_t s)
-{
-    BackOut o{{out[0], out[1], out[2]}, add, st};
-    return scan_impl(in, o, n, tmp, s);
-}
-
 hipError_t launch_pattern_count(int32_t nv, int32_t nf, const int32_t *faces, int32_t ns,
                                 const int32_t *springs, PatternScratch sc, hipStream_t s)
 {

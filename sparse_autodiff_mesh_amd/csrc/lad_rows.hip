@@ -86,13 +86,13 @@ struct Row {
 // Row header loads, all independent of each other.
 // With WITH_XT = false the inertial target is not loaded (the HVP needs
 // only the inertia term's Hessian, which does not depend on it).
-template <typename T, bool WITH_XT = true>
+template <typename T, bool WITH_XT = true, bool PINC = true>
 __device__ __forceinline__ Row<T> load_row(const RowArgs<T> &A, int act, const int32_t *rpa,
                                            int32_t a, const T *__restrict__ x)
 {
     Row<T> r;
-    r.p0 = act != 0 ? A.pat.pinc_ptr[act][a] : 0;
-    r.p1 = act != 0 ? A.pat.pinc_ptr[act][a + 1] : 0;
+    r.p0 = (PINC && act != 0) ? A.pat.pinc_ptr[act][a] : 0;
+    r.p1 = (PINC && act != 0) ? A.pat.pinc_ptr[act][a + 1] : 0;
     r.a = a;
     r.s0 = rpa[a];
     r.s1 = rpa[a + 1];
@@ -412,13 +412,22 @@ __device__ __forceinline__ void face_row(const T gE[6], const T h[21], const T m
 constexpr int kMaxIns = 4;
 
 // Inserted columns of a touched row (ascending; INT32_MAX past the count).
+// The first is stored per row (rins1, read with the row's header); the
+// others, for the few rows that gain more than one column, come from pnew
+// at the row's incidence offset.
 template <typename T>
 __device__ __forceinline__ void load_inserted(const RowArgs<T> &A, int act, const Row<T> &r,
-                                              int32_t ins[kMaxIns])
+                                              int32_t first, int32_t ins[kMaxIns])
 {
+    ins[0] = r.nn > 0 ? first : INT32_MAX;
 #pragma unroll
-    for (int m = 0; m < kMaxIns; ++m)
-        ins[m] = (act != 0 && m < r.nn) ? A.pat.pnew[act][3 * int64_t(r.p0) + m] : INT32_MAX;
+    for (int m = 1; m < kMaxIns; ++m) ins[m] = INT32_MAX;
+    if (r.nn > 1) {
+        const int32_t *pn = A.pat.pnew[act] + 3 * int64_t(A.pat.pinc_ptr[act][r.a]);
+#pragma unroll
+        for (int m = 1; m < kMaxIns; ++m)
+            if (m < r.nn) ins[m] = pn[m];
+    }
 }
 
 // Inserted columns before column b: topology slot kb0 + i of the row sits at
@@ -431,35 +440,17 @@ __device__ __forceinline__ int32_t shift_of(const int32_t ins[kMaxIns], int32_t 
     return n;
 }
 
-// Slot of column b in the sorted active row [s0, s1) (b is present): the
-// row's columns are compared 16 at a time, all loads of a window issued
-// together.
-__device__ __forceinline__ int32_t slot_of(const int32_t *__restrict__ ci, int32_t s0,
-                                           int32_t s1, int32_t b)
-{
-    constexpr int W = 16;
-    for (int32_t base = s0; base < s1; base += W) {
-        int32_t c[W];
-#pragma unroll
-        for (int k = 0; k < W; ++k) c[k] = base + k < s1 ? ci[base + k] : -1;
-        int32_t f = -1;
-#pragma unroll
-        for (int k = 0; k < W; ++k) f = c[k] == b ? base + k : f;
-        if (f >= 0) return f;
-    }
-    return s0;
-}
 
 // Runtime pair (a, b) seen from row a: -K into block `slot` (a
 // read-modify-write), +K into the diagonal D, the gradient into G; the
 // energy counted by the pair's first vertex.
 template <typename T>
-__device__ __forceinline__ void pair_add(const RowArgs<T> &A, const Row<T> &r, const T xb[3],
+__device__ __forceinline__ void pair_add(const RowArgs<T> &A, const T xa[3], const T xb[3],
                                          T *B, bool first, T D[9], T G[3], double &E)
 {
     T dz[3];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) dz[c] = r.xa[c] - xb[c];
+    for (int c = 0; c < 3; ++c) dz[c] = xa[c] - xb[c];
     const T l2 = dz[0] * dz[0] + dz[1] * dz[1] + dz[2] * dz[2];
     if (!(l2 < A.dhat * A.dhat)) return;  // outside the barrier's support
     Dual2<T, 3> d[3];
@@ -609,13 +600,15 @@ __device__ __forceinline__ void row_slots(const RowArgs<T> &A, int act, const in
 // order) comes from the slice with one coalesced load per j for the whole
 // wave and sits at slot s0 + j, moved one on past the diagonal when its
 // column is above the row; the diagonal's slot follows from the number of
-// neighbours below.  The same blocks, in the same order, as row_slots.
+// neighbours below.  SHIFT: every slot also moves past the row's inserted
+// columns below it.  The same blocks, in the same order, as row_slots.
 constexpr int kDenseBatch = 6;  // springs whose loads a lane issues together
 
-template <typename T>
+template <typename T, bool SHIFT>
 __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t, int lane,
-                                                  const Row<T> &r, int32_t sb, T *Hs,
-                                                  const T *__restrict__ x, RowAcc<T> &acc)
+                                                  const Row<T> &r, const int32_t ins[kMaxIns],
+                                                  int32_t sb, T *Hs, const T *__restrict__ x,
+                                                  RowAcc<T> &acc)
 {
     const int32_t p = A.sl_ptr[t];
     const int32_t ns = (A.sl_ptr[t + 1] - p) / kSliceRows;  // wave-uniform
@@ -638,7 +631,9 @@ __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t
             if (!(L[j] >= T(0))) continue;  // padding: the row has fewer springs
             const bool above = nb[j] > r.a;
             below += above ? 0 : 1;
-            T *B = Hs + 9 * (r.s0 + j0 + j + (above ? 1 : 0) - sb);
+            int32_t sl = r.s0 + j0 + j + (above ? 1 : 0);
+            if constexpr (SHIFT) sl += shift_of(ins, nb[j]);
+            T *B = Hs + 9 * (sl - sb);
             Dual2<T, 3> d[3];
 #pragma unroll
             for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(r.xa[c] - xb[j][c], c);
@@ -657,6 +652,7 @@ __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t
         }
     }
     acc.dslot = r.s0 + below;
+    if constexpr (SHIFT) acc.dslot += shift_of(ins, r.a);
 }
 
 template <typename T>
@@ -764,7 +760,7 @@ __device__ __forceinline__ double eval_row_full(const RowArgs<T> &A, int act, co
 #pragma unroll
     for (int k = 0; k < kRowPairs; ++k)
         if (k < pp.n)
-            pair_add(A, r, pp.xb[k], Hs + 9 * (pp.slot[k] - sb), pp.first[k] != 0, acc.D, acc.G,
+            pair_add(A, r.xa, pp.xb[k], Hs + 9 * (pp.slot[k] - sb), pp.first[k] != 0, acc.D, acc.G,
                      acc.E);
     if (r.p1 - r.p0 > pp.n) {
         const int32_t *pl = A.pat.pinc[act];
@@ -780,7 +776,7 @@ __device__ __forceinline__ double eval_row_full(const RowArgs<T> &A, int act, co
             T xb[3];
 #pragma unroll
             for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
-            pair_add(A, r, xb, Hs + 9 * (find_slot(cia, r.s0, r.s1, b) - sb), i0 == r.a, acc.D,
+            pair_add(A, r.xa, xb, Hs + 9 * (find_slot(cia, r.s0, r.s1, b) - sb), i0 == r.a, acc.D,
                      acc.G, acc.E);
         }
     }
@@ -788,64 +784,48 @@ __device__ __forceinline__ double eval_row_full(const RowArgs<T> &A, int act, co
     return acc.E;
 }
 
-// The contact terms of a touched row whose topology terms the main kernel
-// evaluated (SHIFT mode): pairs and vertex-face contacts in element order,
-// added into the row's blocks, its diagonal block and its gradient in HBM.
+// The contact terms of touched row a (incidence entries k0 .. k1, active row
+// from slot s0) whose topology terms the main kernel evaluated (SHIFT mode):
+// pairs and vertex-face contacts in element order, added into the row's
+// blocks, its diagonal block and its gradient in HBM.  The insertion stored
+// each pair entry's block slot and the row's diagonal slot (from the row's
+// start); the main kernel zeroed the row's inserted blocks.
 template <typename T>
-__device__ __forceinline__ double eval_row_contacts(const RowArgs<T> &A, int act, const Row<T> &r,
+__device__ __forceinline__ double eval_row_contacts(const RowArgs<T> &A, int act, int32_t a,
+                                                    int32_t k0, int32_t k1, int32_t s0,
                                                     const T *__restrict__ x, T *__restrict__ hv,
                                                     T *__restrict__ g)
 {
     const int32_t npa = A.state->np[act];
     const int32_t *pl = A.pat.pinc[act];
     const int32_t *prs = A.pat.pairs[act];
-    const int32_t *cia = A.pat.ci[act];
-    T D[9], G[3] = {T(0), T(0), T(0)};
+    const int2 *ps = A.pat.pslot[act];
+    T xa[3], D[9], G[3] = {T(0), T(0), T(0)};
+#pragma unroll
+    for (int c = 0; c < 3; ++c) xa[c] = x[int64_t(a) * 3 + c];
 #pragma unroll
     for (int i = 0; i < 9; ++i) D[i] = T(0);
     double E = 0.0;
-    // slots of the diagonal and of the inserted columns, from one pass over
-    // the row's columns; the main kernel left the inserted blocks unwritten
-    int32_t tgt[1 + kMaxIns], pos[1 + kMaxIns];
-    load_inserted(A, act, r, tgt + 1);
-    tgt[0] = r.a;
-#pragma unroll
-    for (int t = 0; t <= kMaxIns; ++t) pos[t] = r.s0;
-    constexpr int W = 16;
-    for (int32_t base = r.s0; base < r.s1; base += W) {
-        int32_t c[W];
-#pragma unroll
-        for (int k = 0; k < W; ++k) c[k] = base + k < r.s1 ? cia[base + k] : -1;
-#pragma unroll
-        for (int k = 0; k < W; ++k)
-#pragma unroll
-            for (int t = 0; t <= kMaxIns; ++t) pos[t] = c[k] == tgt[t] ? base + k : pos[t];
-    }
-    const int32_t dslot = pos[0];
-#pragma unroll
-    for (int m = 0; m < kMaxIns; ++m)
-        if (m < r.nn)
-#pragma unroll
-            for (int i = 0; i < 9; ++i) hv[9 * int64_t(pos[1 + m]) + i] = T(0);
-    T *Hrow = hv + 9 * int64_t(r.s0);
-    for (int32_t k = r.p0; k < r.p1; ++k) {
+    const int32_t dslot = s0 + ps[k0].y;
+    for (int32_t k = k0; k < k1; ++k) {
         const int32_t q = pl[k];
         if (q >= npa) {
-            vf_add(A, r.a, q - npa, Hrow, D, G, E);
+            vf_add(A, a, q - npa, hv + 9 * int64_t(s0), D, G, E);
             continue;
         }
+        const int32_t sl = s0 + ps[k].x;
         const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
-        const int32_t b = i0 == r.a ? i1 : i0;
+        const int32_t b = i0 == a ? i1 : i0;
         T xb[3];
 #pragma unroll
         for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
-        pair_add(A, r, xb, hv + 9 * int64_t(slot_of(cia, r.s0, r.s1, b)), i0 == r.a, D, G, E);
+        pair_add(A, xa, xb, hv + 9 * int64_t(sl), i0 == a, D, G, E);
     }
     T *B = hv + 9 * int64_t(dslot);
 #pragma unroll
     for (int i = 0; i < 9; ++i) B[i] += D[i];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) g[int64_t(r.a) * 3 + c] += G[c];
+    for (int c = 0; c < 3; ++c) g[int64_t(a) * 3 + c] += G[c];
     return E;
 }
 
@@ -881,8 +861,11 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         // streamed out unwritten and overwritten there).
         Row<T> r{};
         bool own = false;
+        int32_t first_ins = INT32_MAX;
         if (fits && int(threadIdx.x) < nrows) {
-            r = load_row(A, act, rpa, v0 + int32_t(threadIdx.x), x);
+            r = load_row<T, true, false>(A, act, rpa, v0 + int32_t(threadIdx.x), x);
+            if constexpr (PAIRS)
+                if (act != 0) first_ins = A.pat.rins1[act][r.a];
             own = !PAIRS || r.nn <= kMaxIns;
         }
         RowAcc<T> acc;
@@ -893,14 +876,18 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         if (own) {
             Row<T> rt = r;  // the row as the slot loop walks it
             if constexpr (PAIRS) {
-                load_inserted(A, A.state->active, r, ins);
+                load_inserted(A, act, r, first_ins, ins);
                 rt.s1 = r.s0 + (r.kb1 - r.kb0);  // topology slots, in order
                 rt.p0 = rt.p1 = 0;
+                // the blocks of inserted columns get contact terms only
+                // (k_eval_pair_rows adds them): zero the row first
+                if (r.nn > 0)
+                    for (int32_t i = 9 * (r.s0 - sb); i < 9 * (r.s1 - sb); ++i) Hs[i] = T(0);
             }
             PairPre<T> pp;
             prefetch_pairs(A, 0, 0, r, x, pp);
-            if (!PAIRS && A.springs_on && dense_t >= 0)  // wave-uniform
-                row_slice_springs(A, dense_t, int(threadIdx.x), r, sb, Hs, x, acc);
+            if (A.springs_on && dense_t >= 0)  // wave-uniform
+                row_slice_springs<T, PAIRS>(A, dense_t, int(threadIdx.x), r, ins, sb, Hs, x, acc);
             else
                 row_slots<T, false, PAIRS>(A, 0, cia, r, rt, ins, sb, Hs, x, acc, pp);
             if constexpr (FACES) row_faces<T, PAIRS>(A, 0, cia, r, ins, sb, Hs, x, acc);
@@ -941,11 +928,15 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
     if (act != 0 && k < A.pat.pinc_ptr[act][A.nv]) {
         const int32_t a = A.pat.trow[act][k];
         if (a >= 0) {
-            const Row<T> r = load_row(A, act, A.pat.rp[act], a, x);
-            if (r.nn <= kMaxIns)
-                e = eval_row_contacts(A, act, r, x, hv, g);
-            else
+            const int32_t *rpa = A.pat.rp[act];
+            const int32_t s0 = rpa[a], s1 = rpa[a + 1];
+            const int32_t nn = (s1 - s0) - (A.rp0[a + 1] - A.rp0[a]);
+            if (nn <= kMaxIns) {
+                e = eval_row_contacts(A, act, a, k, A.pat.pinc_ptr[act][a + 1], s0, x, hv, g);
+            } else {
+                const Row<T> r = load_row(A, act, rpa, a, x);
                 e = eval_row_full<T, FACES>(A, act, A.pat.ci[act], r, 0, hv, x, g);
+            }
         }
     }
     store_energy(esink, block_sum<kThreads>(e, red));
@@ -1480,7 +1471,7 @@ hipError_t launch_eval_pair_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, E
     if (!face_tables_ok(a)) return hipErrorInvalidValue;
     for (int k = 1; k <= 2; ++k)  // the contact buffers the kernel may read
         if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pairs[k] || !a.pat.pinc_ptr[k] ||
-            !a.pat.pinc[k] || !a.pat.trow[k])
+            !a.pat.pinc[k] || !a.pat.trow[k] || !a.pat.pslot[k])
             return hipErrorInvalidValue;
     if (a.vf_stride > 0 && (!a.vf_eval || !a.vf_ids || !a.vf_slots)) return hipErrorInvalidValue;
     if (a.faces_on)
@@ -1500,7 +1491,8 @@ hipError_t launch_eval_rows(const RowArgs<T> &a, const T *x, T *g, T *hv, Energy
     if (!face_tables_ok(a)) return hipErrorInvalidValue;
     if (a.pairs_on)  // the buffers the contact-capacity variant reads
         for (int k = 1; k <= 2; ++k)
-            if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pinc_ptr[k] || !a.pat.pnew[k])
+            if (!a.pat.rp[k] || !a.pat.ci[k] || !a.pat.pinc_ptr[k] || !a.pat.pnew[k] ||
+                !a.pat.rins1[k])
                 return hipErrorInvalidValue;
     if (a.faces_on)
         a.pairs_on ? launch_eval_rows_as<T, true, true>(a, x, g, hv, es, grid, lds, s)

@@ -394,6 +394,69 @@ void check_row_plan_rejects()
     CHECK(!build_row_plan(make_input(neg, rp, ci, false, 4, 0), neg.rest.data(), plan).empty(), "negative rest length accepted");
 }
 
+// Insertion tiles: consecutive runs of whole units (row chunks) within the
+// row and unit limits, or fixed row blocks; row_tile and row_unit agree.
+void check_insert_tiles(const std::vector<PatchHdr> &units, int32_t nv, bool align,
+                        const char *tag)
+{
+    InsertTiles t;
+    const std::string msg = build_insert_tiles(units, nv, align, t);
+    CHECK(msg.empty(), "%s: %s", tag, msg.c_str());
+    if (!msg.empty()) return;
+    const size_t nt = t.tile_row.size() - 1;
+    CHECK(t.tile_row.front() == 0 && t.tile_row.back() == nv, "%s: tiles cover the rows", tag);
+    CHECK(t.tile_unit.size() == nt + 1, "%s: tile_unit size", tag);
+    CHECK(t.row_tile.size() == size_t(nv), "%s: row_tile size", tag);
+    for (size_t k = 0; k < nt; ++k) {
+        const int32_t r0 = t.tile_row[k], r1 = t.tile_row[k + 1];
+        CHECK(r1 > r0 && r1 - r0 <= kInsTileRows, "%s: tile %zu rows %d..%d", tag, k, r0, r1);
+        for (int32_t a = r0; a < r1; ++a) CHECK(t.row_tile[size_t(a)] == int32_t(k), "%s: row_tile %d", tag, a);
+        if (align) {
+            const int32_t u0 = t.tile_unit[k], u1 = t.tile_unit[k + 1];
+            CHECK(u1 > u0 && u1 - u0 <= kInsTileUnits, "%s: tile %zu units", tag, k);
+            CHECK(units[size_t(u0)].v0 == r0, "%s: tile %zu starts a unit", tag, k);
+            CHECK(units[size_t(u1 - 1)].v0 + units[size_t(u1 - 1)].nown == r1, "%s: tile %zu ends a unit", tag, k);
+            for (int32_t u = u0; u < u1; ++u)
+                for (int32_t a = units[size_t(u)].v0; a < units[size_t(u)].v0 + units[size_t(u)].nown; ++a)
+                    CHECK(t.row_unit[size_t(a)] == u, "%s: row_unit %d", tag, a);
+            // greedy: the next unit would not have fitted
+            if (k + 1 < nt)
+                CHECK(u1 - u0 == kInsTileUnits ||
+                          r1 - r0 + units[size_t(u1)].nown > kInsTileRows,
+                      "%s: tile %zu closed early", tag, k);
+        } else {
+            CHECK(k + 1 == nt || r1 - r0 == kInsTileRows, "%s: fixed tile %zu", tag, k);
+        }
+    }
+    // rejected inputs
+    if (align && !units.empty()) {
+        std::vector<PatchHdr> gap = units;
+        gap.back().nown += 1;
+        CHECK(!build_insert_tiles(gap, nv, true, t).empty(), "%s: units past nv accepted", tag);
+    }
+}
+
+void check_insert_tiles_all()
+{
+    std::mt19937 rng(7);
+    for (int rep = 0; rep < 4; ++rep) {
+        std::vector<PatchHdr> units;
+        int32_t v0 = 0;
+        const int32_t nv = rep == 0 ? 9 : 1000 + 150000 * rep;
+        while (v0 < nv) {
+            PatchHdr h{};
+            h.v0 = v0;
+            h.nown = std::min<int32_t>(nv - v0, rep == 3 ? 1 + int32_t(rng() % 3) : 1 + int32_t(rng() % 64));
+            units.push_back(h);
+            v0 += h.nown;
+        }
+        char tag[64];
+        std::snprintf(tag, sizeof(tag), "tiles rep %d", rep);
+        check_insert_tiles(units, nv, true, tag);
+        check_insert_tiles(units, nv, false, tag);
+    }
+}
+
 }  // namespace
 
 int main()
@@ -411,6 +474,7 @@ int main()
     check_row_plan(r1, true, "random300 rows faces");
     check_row_plan(r2, false, "random2000 rows");
     check_row_plan_rejects();
+    check_insert_tiles_all();
     if (g_fail) {
         std::printf("%d checks failed\n", g_fail);
         return 1;
