@@ -118,7 +118,9 @@ __device__ __forceinline__ int64_t entry_of(int32_t q, int k, int32_t np)
 // entry holds (row, element, topology row start, topology row length) and
 // the row's partners in the element: a pair's other vertex; for a contact,
 // the face's three vertices (row = the contact vertex) or the contact
-// vertex (row = a face vertex); INT32_MAX past the last.
+// vertex (row = a face vertex); INT32_MAX past the last; then the row's
+// vertex's place in the element (0: the pair's first vertex or the
+// contact vertex).
 __global__ void __launch_bounds__(kThreads)
 k_ins_count(DevState *st, const int32_t *__restrict__ pairs_in, int32_t np,
             const int32_t *__restrict__ vf_in, int32_t nvf, int32_t nv, int32_t nf, int32_t nwg,
@@ -198,9 +200,9 @@ k_ins_count(DevState *st, const int32_t *__restrict__ pairs_in, int32_t np,
         if (k < m) {
             const int32_t pos = bins[tl[k]] + rank[k];
             seg[2 * pos] = make_int4(vert[k], q, rb[k], re[k] - rb[k]);
-            seg[2 * pos + 1] = m == 2   ? make_int4(vert[1 - k], INT32_MAX, INT32_MAX, 0)
+            seg[2 * pos + 1] = m == 2   ? make_int4(vert[1 - k], INT32_MAX, INT32_MAX, k)
                                : k == 0 ? make_int4(vert[1], vert[2], vert[3], 0)
-                                        : make_int4(vert[0], INT32_MAX, INT32_MAX, 0);
+                                        : make_int4(vert[0], INT32_MAX, INT32_MAX, k);
         }
 }
 
@@ -228,9 +230,10 @@ __device__ __forceinline__ void merge_row(const int32_t *cb, int32_t len, const 
 // topology row rb0 .. rb0+len): its entries (in pinc, in any order) sorted
 // by element id, its distinct partners that the topology row lacks,
 // ascending, into pnew at three slots per entry from p0, and per entry the
-// slot, from the row's start, of a pair's (row, partner) block (-1 for a
-// contact) and of the diagonal block into pslot.  Returns the number of new
-// partners.
+// slots, from the row's start, of a pair's (row, partner) block (-1 for a
+// contact) and of the diagonal block, and the pair's partner and orientation
+// (see PatternBufs::pslot), into pslot; the caller adds the row's start to
+// the slots.  Returns the number of new partners.
 __device__ int32_t order_row_global(const InsertBufs &b, int bk, int32_t np, int32_t a,
                                     int32_t p0, int32_t d, int32_t rb0, int32_t len)
 {
@@ -285,9 +288,14 @@ __device__ int32_t order_row_global(const InsertBufs &b, int bk, int32_t np, int
     const int32_t ds = below(a);
     for (int32_t k = p0; k < p1; ++k) {
         const int32_t q = pl[k];
-        int32_t sl = -1;
-        if (q < np) sl = below(prs[2 * q] == a ? prs[2 * q + 1] : prs[2 * q]);
-        b.pslot[bk][k] = make_int2(sl, ds);
+        int4 ps = make_int4(-1, ds, -1, 0);
+        if (q < np) {
+            const bool first = prs[2 * q] == a;
+            const int32_t other = first ? prs[2 * q + 1] : prs[2 * q];
+            ps.x = below(other);
+            ps.z = 2 * other + (first ? 1 : 0);
+        }
+        b.pslot[bk][k] = ps;
     }
     return nn;
 }
@@ -304,6 +312,7 @@ struct RegRow {
     int32_t part[kRegPart];
     int32_t q[kRegEnt];  // the entries' elements, ascending (INT32_MAX past the last)
     uint32_t keep;       // bit k: part[k] is new
+    uint32_t firstm;     // bit i: the row's vertex is entry i's pair's first vertex
 };
 
 __device__ __forceinline__ bool kept(const RegRow &w, int k) { return (w.keep >> k) & 1u; }
@@ -356,11 +365,13 @@ __device__ __forceinline__ int32_t row_reg(const int32_t ctop[kRegCols], int32_t
             pp[i] = pa;
             pp[i + 1] = pb;
         }
+    w.firstm = 0;
 #pragma unroll
     for (int i = 0; i < kRegEnt; ++i) {
         w.part[3 * i] = pp[i].x;
         w.part[3 * i + 1] = pp[i].y;
         w.part[3 * i + 2] = pp[i].z;
+        w.firstm |= pp[i].w == 0 ? (1u << i) : 0u;
     }
     int32_t nn = 0;
     w.keep = 0;
@@ -378,7 +389,7 @@ __device__ __forceinline__ int32_t row_reg(const int32_t ctop[kRegCols], int32_t
 }
 
 __device__ __forceinline__ void emit_row_reg(const InsertBufs &b, int bk, int32_t np, int32_t a,
-                                             int32_t p0, int32_t d, const RegRow &w)
+                                             int32_t p0, int32_t d, int32_t s0, const RegRow &w)
 {
     int32_t *pn = b.pnew[bk] + 3 * int64_t(p0);
     int32_t first = INT32_MAX;
@@ -393,14 +404,18 @@ __device__ __forceinline__ void emit_row_reg(const InsertBufs &b, int bk, int32_
             first = min(first, w.part[k]);
         }
     b.rins1[bk][a] = first;
-    const int32_t ds = reg_below(w, a);
+    const int32_t ds = s0 + reg_below(w, a);
+    const int32_t sw = __popc(w.keep) > kMaxIns ? -1 - s0 : s0;
 #pragma unroll
     for (int i = 0; i < kRegEnt; ++i)
         if (i < d) {
             b.trow[bk][p0 + i] = i == 0 ? a : -1;
             b.pinc_row[bk][p0 + i] = a;
             b.pinc[bk][p0 + i] = w.q[i];
-            b.pslot[bk][p0 + i] = make_int2(w.q[i] < np ? reg_below(w, w.part[3 * i]) : -1, ds);
+            const bool pair = w.q[i] < np;
+            b.pslot[bk][p0 + i] =
+                make_int4(pair ? s0 + reg_below(w, w.part[3 * i]) : -1, ds,
+                          pair ? 2 * w.part[3 * i] + int32_t((w.firstm >> i) & 1u) : -1, sw);
         }
 }
 
@@ -691,15 +706,7 @@ k_ins_tiles(DevState *st, int32_t np, int32_t nvf, int32_t nv, int32_t nwg,
         const int32_t i = b.seg[2 * si].x - r0;
         int32_t off, d;
         row_span(i, off, d);
-        if (ent_lds && d <= kRegEnt && s_len[i] <= kRegCols) {
-            RegRow v;
-            int32_t c2[kRegCols];
-            load_topo(b, s_rb[i], s_len[i], c2);
-            count_row(i, row_reg(c2, d, s_eq + off, s_ep + off, v));
-            emit_row_reg(b, bk, np, r0 + i, e0 + off, d, v);
-        } else {
-            count_row(i, slow_row(i, off, d));
-        }
+        count_row(i, slow_row(i, off, d));
     }
     lds_barrier();
 
@@ -734,7 +741,7 @@ k_ins_tiles(DevState *st, int32_t np, int32_t nvf, int32_t nv, int32_t nwg,
     // offsets, the first inserted column of untouched rows, the owned
     // register rows).  They go out after the look-back: a load issued
     // after them would wait for them too.
-    auto late_stores = [&]() __attribute__((always_inline)) {
+    auto late_stores = [&](int32_t X) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kTileSeg; ++j) {
             const int32_t i = tid + kThreads * j;
@@ -749,7 +756,7 @@ k_ins_tiles(DevState *st, int32_t np, int32_t nvf, int32_t nv, int32_t nwg,
             const int32_t i = my_h.x - r0;
             int32_t off, d;
             row_span(i, off, d);
-            emit_row_reg(b, bk, np, r0 + i, e0 + off, d, w);
+            emit_row_reg(b, bk, np, r0 + i, e0 + off, d, my_h.z + X + s_nn[i], w);
         }
     };
     constexpr int kLookPer = 4, kLook = kLookPer * kThreads;
@@ -846,7 +853,7 @@ k_ins_tiles(DevState *st, int32_t np, int32_t nvf, int32_t nv, int32_t nwg,
 
     // E. the stores: those above, then the active row pointers and the
     // touched rows' columns; the commit (last tile)
-    late_stores();
+    late_stores(X);
 #pragma unroll
     for (int j = 0; j < kTileSeg; ++j) {
         const int32_t i = tid + kThreads * j;
@@ -870,20 +877,31 @@ k_ins_tiles(DevState *st, int32_t np, int32_t nvf, int32_t nv, int32_t nwg,
             st->err_cur |= int32_t(eincl);  // the patch path's commit kernel reads it
         }
     }
-    auto merge = [&](int32_t i) __attribute__((always_inline)) {
+    // rows ordered in global memory: their columns, and their slots made
+    // absolute
+    auto finish_slow = [&](int32_t i) __attribute__((always_inline)) {
         const int32_t nn = (i + 1 < nr ? s_nn[i + 1] : agg) - s_nn[i];
-        merge_touched(b, bk, s_rb[i], s_len[i], e0 + s_cnt[i], s_rb[i] + X + s_nn[i], nn);
-    };
-    if (own && row_path) {
-        const int32_t i = my_h.x - r0;
-        if (w_ok) merge_reg(w, my_h.w, b.ci[bk] + my_h.z + X + s_nn[i]);
-        else merge(i);
-    }
-    if (row_path)
-        for (int32_t k = tid + kThreads; k < tcnt; k += kThreads) {
-            const int64_t si = seg_index(k);
-            if (b.erank[si] == 0) merge(b.seg[2 * si].x - r0);
+        const int32_t s0 = s_rb[i] + X + s_nn[i];
+        if (row_path) merge_touched(b, bk, s_rb[i], s_len[i], e0 + s_cnt[i], s0, nn);
+        int32_t off, d;
+        row_span(i, off, d);
+        for (int32_t k = e0 + off; k < e0 + off + d; ++k) {
+            int4 ps = b.pslot[bk][k];
+            ps.x = ps.x >= 0 ? s0 + ps.x : -1;
+            ps.y += s0;
+            ps.w = nn > kMaxIns ? -1 - s0 : s0;
+            b.pslot[bk][k] = ps;
         }
+    };
+    if (own) {
+        const int32_t i = my_h.x - r0;
+        if (!w_ok) finish_slow(i);
+        else if (row_path) merge_reg(w, my_h.w, b.ci[bk] + my_h.z + X + s_nn[i]);
+    }
+    for (int32_t k = tid + kThreads; k < tcnt; k += kThreads) {
+        const int64_t si = seg_index(k);
+        if (b.erank[si] == 0) finish_slow(b.seg[2 * si].x - r0);
+    }
 }
 
 constexpr int kMergeThreads = 64;

@@ -200,10 +200,14 @@ struct PatternBufs {
                                  // lacks, ascending
     const int32_t *rins1[3];     // per row: its smallest inserted column
                                  // (INT32_MAX: none)
-    const int2 *pslot[3];        // per incidence entry (row path): slot, from
-                                 // the active row's start, of a pair's (row,
-                                 // partner) block (-1 for a vertex-face entry)
-                                 // and of the row's diagonal block
+    const int4 *pslot[3];        // per incidence entry: the active slot of a
+                                 // pair's (row, partner) block (-1 for a
+                                 // vertex-face entry), of the row's diagonal
+                                 // block, the pair's partner p as 2 p + 1 when
+                                 // the row's vertex is the pair's first, 2 p
+                                 // when second (-1 for a vertex-face entry),
+                                 // and the row's first active slot s0 (-1 - s0
+                                 // when the row gains more than kMaxIns columns)
     const int32_t *vf[3];        // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)
 };
@@ -395,7 +399,7 @@ struct InsertBufs {
                                  // buffer is next written (the row kernels
                                  // read those of the active buffer)
     int32_t *trow[3];            // touched-row list, see PatternBufs::trow
-    int2 *pslot[3];              // see PatternBufs::pslot (row path)
+    int4 *pslot[3];              // see PatternBufs::pslot
     int32_t *rins1[3];           // see PatternBufs::rins1
     int32_t *vf[3];              // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)
@@ -418,6 +422,11 @@ struct InsertBufs {
     int4 *seg;                   // [max_wg * kInsWgEnt][2]
     int32_t *erank;              // [max_wg * kInsWgEnt]
 };
+// A touched row whose active row has at most kMaxIns columns beyond its
+// topology row has its topology terms evaluated by the main row kernel,
+// each block moved to its active slot; its contact terms are added
+// afterwards.  A row with more is evaluated whole by the touched-row kernel.
+constexpr int kMaxIns = 4;
 constexpr int kInsTileRows = 2048;   // rows per insertion tile, at most
 constexpr int kStatStride = 16;      // 8-byte words per tile status
 constexpr int kInsTileUnits = 256;   // row chunks per insertion tile, at most

@@ -406,11 +406,6 @@ __device__ __forceinline__ void face_row(const T gE[6], const T h[21], const T m
 // Energy, gradient and Hessian rows.
 // ---------------------------------------------------------------------------
 
-// A touched row whose active row has at most kMaxIns columns beyond its
-// topology row has its topology terms evaluated by the main kernel, each
-// block moved to its active slot; its contact terms are added afterwards.
-constexpr int kMaxIns = 4;
-
 // Inserted columns of a touched row (ascending; INT32_MAX past the count).
 // The first is stored per row (rins1, read with the row's header); the
 // others, for the few rows that gain more than one column, come from pnew
@@ -784,48 +779,48 @@ __device__ __forceinline__ double eval_row_full(const RowArgs<T> &A, int act, co
     return acc.E;
 }
 
-// The contact terms of touched row a (incidence entries k0 .. k1, active row
-// from slot s0) whose topology terms the main kernel evaluated (SHIFT mode):
-// pairs and vertex-face contacts in element order, added into the row's
-// blocks, its diagonal block and its gradient in HBM.  The insertion stored
-// each pair entry's block slot and the row's diagonal slot (from the row's
-// start); the main kernel zeroed the row's inserted blocks.
+// The contact terms of touched row a (incidence entries k0 .. k1; pi0 the
+// first entry's slots) whose topology terms the main kernel evaluated
+// (SHIFT mode): pairs and vertex-face contacts in element order, added into
+// the row's blocks, its diagonal block and its gradient in HBM.  The
+// insertion stored each entry's block slots, partner and orientation; the
+// main kernel zeroed the row's inserted blocks.  The first entry's loads
+// all go out at once.
 template <typename T>
 __device__ __forceinline__ double eval_row_contacts(const RowArgs<T> &A, int act, int32_t a,
-                                                    int32_t k0, int32_t k1, int32_t s0,
+                                                    int32_t k0, const int4 &pi0, int32_t q0,
                                                     const T *__restrict__ x, T *__restrict__ hv,
                                                     T *__restrict__ g)
 {
     const int32_t npa = A.state->np[act];
-    const int32_t *pl = A.pat.pinc[act];
-    const int32_t *prs = A.pat.pairs[act];
-    const int2 *ps = A.pat.pslot[act];
-    T xa[3], D[9], G[3] = {T(0), T(0), T(0)};
+    const int32_t k1 = A.pat.pinc_ptr[act][a + 1];
+    T xa[3], D[9], G[3];
+    T *Bd = hv + 9 * int64_t(pi0.y);
 #pragma unroll
-    for (int c = 0; c < 3; ++c) xa[c] = x[int64_t(a) * 3 + c];
+    for (int c = 0; c < 3; ++c) {
+        xa[c] = x[int64_t(a) * 3 + c];
+        G[c] = g[int64_t(a) * 3 + c];
+    }
 #pragma unroll
-    for (int i = 0; i < 9; ++i) D[i] = T(0);
+    for (int i = 0; i < 9; ++i) D[i] = Bd[i];
     double E = 0.0;
-    const int32_t dslot = s0 + ps[k0].y;
     for (int32_t k = k0; k < k1; ++k) {
-        const int32_t q = pl[k];
-        if (q >= npa) {
-            vf_add(A, a, q - npa, hv + 9 * int64_t(s0), D, G, E);
+        const int4 pi = k == k0 ? pi0 : A.pat.pslot[act][k];
+        if (pi.z < 0) {  // vertex-face contact
+            const int32_t q = k == k0 ? q0 : A.pat.pinc[act][k];
+            vf_add(A, a, q - npa, hv + 9 * int64_t(pi.w), D, G, E);
             continue;
         }
-        const int32_t sl = s0 + ps[k].x;
-        const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
-        const int32_t b = i0 == a ? i1 : i0;
+        const int32_t b = pi.z >> 1;
         T xb[3];
 #pragma unroll
         for (int c = 0; c < 3; ++c) xb[c] = x[int64_t(b) * 3 + c];
-        pair_add(A, xa, xb, hv + 9 * int64_t(sl), i0 == a, D, G, E);
+        pair_add(A, xa, xb, hv + 9 * int64_t(pi.x), (pi.z & 1) != 0, D, G, E);
     }
-    T *B = hv + 9 * int64_t(dslot);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) B[i] += D[i];
+    for (int i = 0; i < 9; ++i) Bd[i] = D[i];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) g[int64_t(a) * 3 + c] += G[c];
+    for (int c = 0; c < 3; ++c) g[int64_t(a) * 3 + c] = G[c];
     return E;
 }
 
@@ -927,14 +922,13 @@ k_eval_pair_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
     double e = 0.0;
     if (act != 0 && k < A.pat.pinc_ptr[act][A.nv]) {
         const int32_t a = A.pat.trow[act][k];
+        const int4 pi = A.pat.pslot[act][k];
+        const int32_t q = A.pat.pinc[act][k];
         if (a >= 0) {
-            const int32_t *rpa = A.pat.rp[act];
-            const int32_t s0 = rpa[a], s1 = rpa[a + 1];
-            const int32_t nn = (s1 - s0) - (A.rp0[a + 1] - A.rp0[a]);
-            if (nn <= kMaxIns) {
-                e = eval_row_contacts(A, act, a, k, A.pat.pinc_ptr[act][a + 1], s0, x, hv, g);
-            } else {
-                const Row<T> r = load_row(A, act, rpa, a, x);
+            if (pi.w >= 0) {
+                e = eval_row_contacts(A, act, a, k, pi, q, x, hv, g);
+            } else {  // more than kMaxIns new columns: the whole row here
+                const Row<T> r = load_row(A, act, A.pat.rp[act], a, x);
                 e = eval_row_full<T, FACES>(A, act, A.pat.ci[act], r, 0, hv, x, g);
             }
         }
