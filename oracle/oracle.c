@@ -56,6 +56,13 @@ static int check_problem(const oracle_problem *p)
         if (p->springs[i] < 0 || p->springs[i] >= p->nv) return -1;
     for (int64_t i = 0; i < 2 * (int64_t)p->np; ++i)
         if (p->pairs[i] < 0 || p->pairs[i] >= p->nv) return -1;
+    /* a spring and a vertex-vertex pair join two distinct vertices (a pair
+     * of one vertex would sit at distance zero, where the barrier is
+     * infinite) */
+    for (int32_t s = 0; s < p->ns; ++s)
+        if (p->springs[2 * (int64_t)s] == p->springs[2 * (int64_t)s + 1]) return -1;
+    for (int32_t q = 0; q < p->np; ++q)
+        if (p->pairs[2 * (int64_t)q] == p->pairs[2 * (int64_t)q + 1]) return -1;
     for (int32_t e = 0; e < p->nvf; ++e) {
         int32_t v = p->vf[2 * (int64_t)e], f = p->vf[2 * (int64_t)e + 1];
         if (v < 0 || v >= p->nv || f < 0 || f >= p->nf) return -1;
