@@ -64,7 +64,8 @@ typedef enum {
     LAD_ERR_OOM = -3,       /* device or host allocation failed             */
     LAD_ERR_HIP = -4,       /* a HIP runtime call failed                     */
     LAD_ERR_STATE = -5,     /* call not valid in the context's state        */
-    LAD_ERR_PAIRS = -6      /* device-side check rejected a pair set        */
+    LAD_ERR_PAIRS = -6,     /* device-side check rejected a pair set        */
+    LAD_ERR_NONFINITE = -7  /* debug check: an output held a NaN or an inf  */
 } lad_status;
 
 typedef enum { LAD_F32 = 0, LAD_F64 = 1 } lad_dtype;
@@ -399,11 +400,29 @@ lad_status lad_insert_pairs(lad_ctx *ctx, const int32_t *d_pairs, int32_t npairs
                             void *hip_stream);
 
 /*
- * Read and clear the device-side error latch set by lad_insert_pairs.
- * *status gets LAD_OK, LAD_ERR_PAIRS or LAD_ERR_CAPACITY.  Synchronises
+ * Read and clear the device-side error latch set by lad_insert_pairs and
+ * lad_insert_contacts and, in debug mode, by the output checks.  *status
+ * gets LAD_OK, LAD_ERR_PAIRS (a bad index), LAD_ERR_CAPACITY (staging),
+ * LAD_ERR_STATE (an insert whose workgroups did not complete their chain:
+ * an internal failure, the insert was not committed) or LAD_ERR_NONFINITE
+ * (debug mode), the first of these that applies.  Synchronises
  * `hip_stream`.
  */
 lad_status lad_device_status(lad_ctx *ctx, void *hip_stream, int32_t *status);
+
+/*
+ * Debug mode, for callers hunting a NaN or an inf.  flags = LAD_DEBUG_NONFINITE
+ * makes every later lad_eval_energy_grad_hess (and _noalloc) check its
+ * energy, gradient and the active pattern's Hessian blocks, and every
+ * lad_hvp its product, on the device after the call's kernels, on the same
+ * stream: a value that is not finite latches an error that
+ * lad_device_status reports as LAD_ERR_NONFINITE (the calls themselves stay
+ * asynchronous and make no host synchronisation; each check reads its
+ * outputs once more).  flags = 0 turns it off.  Errors: LAD_ERR_ARG (NULL
+ * ctx, unknown flag).  Makes no GPU call.
+ */
+#define LAD_DEBUG_NONFINITE 1
+lad_status lad_set_debug(lad_ctx *ctx, int32_t flags);
 
 /* Message for the last host-side error of this context ("" if none).  The
  * string is owned by the context.  With ctx == NULL: the last error of a

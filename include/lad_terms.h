@@ -150,6 +150,11 @@ lad_status lad_terms_copy_pattern(lad_terms_ctx *ctx, void *hip_stream, int32_t 
  * ctx == NULL, of the last failed lad_terms_build in this thread. */
 const char *lad_terms_last_error(const lad_terms_ctx *ctx);
 
+/* Host synchronisations this context has made so far (the build's, and one
+ * per lad_terms_copy_pattern; lad_terms_eval and lad_terms_hvp make none).
+ * Returns -1 for ctx == NULL.  Makes no GPU call. */
+int64_t lad_terms_host_syncs(const lad_terms_ctx *ctx);
+
 void lad_terms_destroy(lad_terms_ctx *ctx);
 
 #ifdef __cplusplus

@@ -23,6 +23,8 @@ LAD_ERR_OOM = -3
 LAD_ERR_HIP = -4
 LAD_ERR_STATE = -5
 LAD_ERR_PAIRS = -6
+LAD_ERR_NONFINITE = -7
+LAD_DEBUG_NONFINITE = 1
 LAD_F32 = 0
 LAD_F64 = 1
 LAD_PATH_AUTO = 0
@@ -85,7 +87,7 @@ EXPORTS = [
     "lad_insert_contacts",
     "lad_jacobian_pattern", "lad_copy_jacobian_pattern", "lad_residual_jacobian",
     "lad_gauss_newton_product",
-    "lad_device_status", "lad_last_error", "lad_status_string", "lad_destroy",
+    "lad_device_status", "lad_set_debug", "lad_last_error", "lad_status_string", "lad_destroy",
 ]
 
 _lib = None
@@ -123,6 +125,7 @@ def lib():
         L.lad_insert_pairs.argtypes = [_vp, _vp, ctypes.c_int32, _vp]
         L.lad_insert_contacts.argtypes = [_vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp]
         L.lad_device_status.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]
+        L.lad_set_debug.argtypes = [_vp, ctypes.c_int32]
         L.lad_last_error.argtypes = [_vp]
         L.lad_last_error.restype = ctypes.c_char_p
         L.lad_status_string.argtypes = [ctypes.c_int]
@@ -413,6 +416,9 @@ class Lad:
 
     def device_status(self) -> int:
         return lad_device_status(self.ctx, _stream())
+
+    def set_debug(self, flags: int) -> None:
+        _check(lib().lad_set_debug(self.ctx, int(flags)), self.ctx)
 
     def get_info(self) -> dict:
         return lad_get_info(self.ctx)

@@ -37,6 +37,7 @@ struct lad_ctx {
     int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
     bool cols_complete[3] = {true, true, true};  // column array of each pattern buffer complete
     int64_t host_syncs = 0;          // host synchronisations made for this context
+    int32_t debug_flags = 0;         // lad_set_debug
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
     int32_t *d_fptr = nullptr;
@@ -814,6 +815,9 @@ lad_status eval_with_parts(lad_ctx *ctx, const void *d_x, double *d_energy, void
     hipError_t e = ctx->dtype == LAD_F64
                        ? enqueue_eval<double>(ctx, d_x, d_energy, d_grad, d_hvals, parts, s)
                        : enqueue_eval<float>(ctx, d_x, d_energy, d_grad, d_hvals, parts, s);
+    if (e == hipSuccess && (ctx->debug_flags & LAD_DEBUG_NONFINITE))
+        e = launch_check_finite(ctx->d_state, d_energy, d_grad, 3 * int64_t(ctx->nv), d_hvals,
+                                ctx->es, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "eval launch");
     return LAD_OK;
 }
@@ -841,7 +845,7 @@ lad_status lad_build_pattern(const lad_mesh_desc *desc, void *hip_stream, lad_ct
     const lad_status s = build(desc, static_cast<hipStream_t>(hip_stream), ctx);
     if (s != LAD_OK) {
         g_build_error = ctx->err;
-        (void)hipStreamSynchronize(static_cast<hipStream_t>(hip_stream));
+        (void)host_sync(ctx, static_cast<hipStream_t>(hip_stream));
         free_all(ctx);
         delete ctx;
         return s;
@@ -935,6 +939,9 @@ lad_status lad_hvp(lad_ctx *ctx, const void *d_x, const void *d_v, void *d_y, vo
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = ctx->dtype == LAD_F64 ? enqueue_hvp<double>(ctx, d_x, d_v, d_y, s)
                                          : enqueue_hvp<float>(ctx, d_x, d_v, d_y, s);
+    if (e == hipSuccess && (ctx->debug_flags & LAD_DEBUG_NONFINITE))
+        e = launch_check_finite(ctx->d_state, nullptr, d_y, 3 * int64_t(ctx->nv), nullptr, ctx->es,
+                                s);
     if (e != hipSuccess) return hip_fail(ctx, e, "hvp launch");
     return LAD_OK;
 }
@@ -1090,7 +1097,20 @@ lad_status lad_device_status(lad_ctx *ctx, void *hip_stream, int32_t *status)
                            &zero, sizeof(zero), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lad_device_status");
-    *status = (hs.err_latched & 1) ? LAD_ERR_PAIRS : (hs.err_latched & 2) ? LAD_ERR_CAPACITY : LAD_OK;
+    const int32_t b = hs.err_latched;
+    *status = (b & 1)   ? LAD_ERR_PAIRS
+              : (b & 2) ? LAD_ERR_CAPACITY
+              : (b & 4) ? LAD_ERR_STATE
+              : (b & 8) ? LAD_ERR_NONFINITE
+                        : LAD_OK;
+    return LAD_OK;
+}
+
+lad_status lad_set_debug(lad_ctx *ctx, int32_t flags)
+{
+    if (!ctx) return fail(nullptr, LAD_ERR_ARG, "ctx is NULL");
+    if (flags & ~LAD_DEBUG_NONFINITE) return fail(ctx, LAD_ERR_ARG, "unknown debug flag");
+    ctx->debug_flags = flags;
     return LAD_OK;
 }
 
@@ -1106,6 +1126,7 @@ const char *lad_status_string(lad_status s)
     case LAD_ERR_HIP: return "LAD_ERR_HIP";
     case LAD_ERR_STATE: return "LAD_ERR_STATE";
     case LAD_ERR_PAIRS: return "LAD_ERR_PAIRS";
+    case LAD_ERR_NONFINITE: return "LAD_ERR_NONFINITE";
     }
     return "LAD_ERR_UNKNOWN";
 }
@@ -1113,7 +1134,7 @@ const char *lad_status_string(lad_status s)
 void lad_destroy(lad_ctx *ctx)
 {
     if (!ctx) return;
-    (void)hipStreamSynchronize(ctx->stream);
+    (void)host_sync(ctx, ctx->stream);
     free_all(ctx);
     delete ctx;
 }

@@ -508,6 +508,58 @@ k_energy_reduce(const double *__restrict__ parts, int32_t n, double *__restrict_
 
 }  // namespace
 
+namespace {
+
+// NaN or +-inf, from the exponent bits of the values read as integers (the
+// device code is compiled with finite-math assumptions, under which a test
+// on a floating-point value may be folded away)
+__device__ __forceinline__ bool nonfinite_bits(uint32_t u)
+{
+    return (u & 0x7f800000u) == 0x7f800000u;
+}
+
+__device__ __forceinline__ bool nonfinite_bits(unsigned long long u)
+{
+    const unsigned long long e = 0x7ff0000000000000ull;
+    return (u & e) == e;
+}
+
+// U: the unsigned integer of the values' width.  One flag per workgroup,
+// no ordering needed: the latch is an OR.
+template <typename U>
+__global__ void __launch_bounds__(kThreads)
+k_check_finite(DevState *st, const unsigned long long *__restrict__ energy,
+               const U *__restrict__ vec, int64_t nvec, const U *__restrict__ hv)
+{
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    const int64_t t0 = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    bool bad = t0 == 0 && energy && nonfinite_bits(*energy);
+    for (int64_t i = t0; i < nvec; i += stride) bad |= nonfinite_bits(vec[i]);
+    if (hv) {
+        const int64_t nh = 9 * int64_t(st->nnzb[st->active]);
+        for (int64_t i = t0; i < nh; i += stride) bad |= nonfinite_bits(hv[i]);
+    }
+    if (__syncthreads_or(bad) && threadIdx.x == 0) atomicOr(&st->err_latched, 8);
+}
+
+}  // namespace
+
+hipError_t launch_check_finite(DevState *st, const double *energy, const void *vec, int64_t nvec,
+                               const void *hv, int es, hipStream_t s)
+{
+    const unsigned grid = 1024;
+    const auto *e = reinterpret_cast<const unsigned long long *>(energy);
+    if (es == 8)
+        hipLaunchKernelGGL(k_check_finite<unsigned long long>, dim3(grid), dim3(kThreads), 0, s,
+                           st, e, static_cast<const unsigned long long *>(vec), nvec,
+                           static_cast<const unsigned long long *>(hv));
+    else
+        hipLaunchKernelGGL(k_check_finite<uint32_t>, dim3(grid), dim3(kThreads), 0, s, st, e,
+                           static_cast<const uint32_t *>(vec), nvec,
+                           static_cast<const uint32_t *>(hv));
+    return hipGetLastError();
+}
+
 hipError_t launch_energy_reduce(const double *parts, int32_t n, double *out, hipStream_t s)
 {
     hipLaunchKernelGGL(k_energy_reduce, dim3(1), dim3(kThreads), 0, s, parts, n, out);

@@ -240,6 +240,11 @@ struct EnergySink {
 };
 
 hipError_t launch_energy_reduce(const double *parts, int32_t n, double *out, hipStream_t s);
+// Debug check: bit 8 of st->err_latched if the energy (if given), any of
+// the nvec vector entries, or any value of the active pattern's blocks in
+// hv (if given) is not finite; es = 4 or 8 bytes per value.
+hipError_t launch_check_finite(DevState *st, const double *energy, const void *vec, int64_t nvec,
+                               const void *hv, int es, hipStream_t s);
 
 template <typename T>
 hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hvals,

@@ -40,6 +40,7 @@ struct lad_terms_ctx {
     double *d_epart = nullptr;
     std::vector<void *> allocs;
     std::string err;
+    int64_t host_syncs = 0;  // host synchronisations made for this context
 };
 
 namespace {
@@ -49,6 +50,14 @@ thread_local std::string g_terms_build_error;
 constexpr int32_t kChunkRows = kRowThreads;
 constexpr int32_t kChunkBlocks = 512;   // LDS staging per workgroup, in blocks
 constexpr int32_t kMaxRowBlocks = 256;  // column offsets are stored in 8 bits
+
+// Every host synchronisation of this front end goes through here and is
+// counted (lad_terms_host_syncs).
+hipError_t host_sync(lad_terms_ctx *ctx, hipStream_t s)
+{
+    if (ctx) ++ctx->host_syncs;
+    return hipStreamSynchronize(s);
+}
 
 lad_status fail(lad_terms_ctx *ctx, lad_status s, const std::string &msg)
 {
@@ -181,7 +190,7 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
     std::vector<int32_t> rp(static_cast<size_t>(nv) + 1);
     if (e == hipSuccess)
         e = hipMemcpyAsync(rp.data(), ctx->d_rp, rp.size() * 4, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) {
         free_temps();
         return fail(nullptr, LAD_ERR_HIP, std::string("pattern build: ") + hipGetErrorString(e));
@@ -196,7 +205,7 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
     std::vector<int32_t> ci(static_cast<size_t>(ctx->nnzb));
     if (e == hipSuccess && !ci.empty())
         e = hipMemcpyAsync(ci.data(), ctx->d_ci, ci.size() * 4, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     free_temps();
     if (e != hipSuccess)
         return fail(nullptr, LAD_ERR_HIP, std::string("pattern compaction: ") + hipGetErrorString(e));
@@ -321,7 +330,7 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
                           &ctx->grid_hvp);
     if (e == hipSuccess)
         e = dev_alloc(ctx, &ctx->d_epart, size_t(ctx->nterms) * size_t(ctx->grid_eval) * 8);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return fail(nullptr, LAD_ERR_HIP, std::string("upload: ") + hipGetErrorString(e));
     return LAD_OK;
 }
@@ -470,7 +479,7 @@ lad_status lad_terms_copy_pattern(lad_terms_ctx *ctx, void *hip_stream, int32_t 
                                   hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(d_col_idx, ctx->d_ci, size_t(ctx->nnzb) * 4, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) return fail(ctx, LAD_ERR_HIP, std::string("copy: ") + hipGetErrorString(e));
     return LAD_OK;
 }
@@ -479,6 +488,8 @@ const char *lad_terms_last_error(const lad_terms_ctx *ctx)
 {
     return ctx ? ctx->err.c_str() : g_terms_build_error.c_str();
 }
+
+int64_t lad_terms_host_syncs(const lad_terms_ctx *ctx) { return ctx ? ctx->host_syncs : -1; }
 
 void lad_terms_destroy(lad_terms_ctx *ctx)
 {

@@ -16,7 +16,7 @@ SETS = {"cloth": 1, "arap": 2, "symdir": 3, "arap_cloth": 4, "cloth_quad": 5}
 TERMS_EXPORTS = [
     "lad_terms_describe", "lad_terms_build", "lad_terms_eval", "lad_terms_hvp",
     "lad_terms_get_pattern", "lad_terms_copy_pattern", "lad_terms_last_error",
-    "lad_terms_destroy",
+    "lad_terms_host_syncs", "lad_terms_destroy",
 ]
 
 _vp = ctypes.c_void_p
@@ -54,6 +54,8 @@ def lib():
                                              ctypes.POINTER(ctypes.c_int64)]
         L.lad_terms_last_error.argtypes = [_vp]
         L.lad_terms_last_error.restype = ctypes.c_char_p
+        L.lad_terms_host_syncs.argtypes = [_vp]
+        L.lad_terms_host_syncs.restype = ctypes.c_int64
         L.lad_terms_destroy.argtypes = [_vp]
         L.lad_terms_destroy.restype = None
         _typed = True
@@ -158,6 +160,9 @@ class Terms:
         _check(lib().lad_terms_hvp(self.ctx, x.data_ptr(), v.data_ptr(), y.data_ptr(),
                                    _stream()), self.ctx)
         return y
+
+    def host_syncs(self) -> int:
+        return int(lib().lad_terms_host_syncs(self.ctx))
 
     def pattern(self):
         t = self.torch

@@ -38,8 +38,12 @@ def test_exports_match_header(L):
 def test_status_strings(L):
     for code, name in [(0, "LAD_OK"), (-1, "LAD_ERR_ARG"), (-2, "LAD_ERR_CAPACITY"),
                        (-3, "LAD_ERR_OOM"), (-4, "LAD_ERR_HIP"), (-5, "LAD_ERR_STATE"),
-                       (-6, "LAD_ERR_PAIRS")]:
+                       (-6, "LAD_ERR_PAIRS"), (-7, "LAD_ERR_NONFINITE")]:
         assert L.lad_status_string(code).decode() == name
+
+
+def test_set_debug_rejects_null_context(L):
+    assert L.lad_set_debug(None, binding.LAD_DEBUG_NONFINITE) == binding.LAD_ERR_ARG
 
 
 def build_status(desc):

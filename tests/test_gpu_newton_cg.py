@@ -12,9 +12,11 @@ systems (condition number about 90) they stay near the level of one HVP,
 so p is held to the HVP's own tolerances: 1e-12 relative in fp64 and 2e-5
 in fp32 (the largest differences seen, over up to 77 iterations, were about
 1.3e-15 and 6.5e-7).
-At the full 1000 x 1000 size the fp32 run is checked through properties
-the oracle computes independently: the true residual |H p + g| / |g| in
-fp64 matches the reported one, and p is a descent direction."""
+At the full 1000 x 1000 size the fp32 run is compared with the oracle
+over 8 iterations the same way, and a 16-iteration run is checked through
+properties the oracle computes independently: the true residual
+|H p + g| / |g| in fp64 matches the reported one, and p is a descent
+direction."""
 import numpy as np
 import pytest
 
@@ -161,11 +163,15 @@ def test_bitwise_reproducible(lad):
     L.close()
 
 
-def test_fullsize_cloth_f32_properties(lad):
-    # 1000 x 1000 cloth in fp32, 16 iterations, as timed by the benchmark
+def test_fullsize_cloth_f32_like_oracle_and_properties(lad):
+    # 1000 x 1000 cloth in fp32: 8 iterations against the oracle (the same
+    # stop, p to the fp32 tolerance), then 16 iterations, as timed by the
+    # benchmark, through the properties
     log_case(test="ncg_fullsize", n=1000, dtype="f32")
     m, x = near_rest(1000, 0.002)
     L, prob, rp, ci, x_h, g_h = setup(lad, m, x, "f32")
+    _, st8, _ = compare(lad, L, prob, rp, ci, x_h, g_h, "f32", max_iters=8, eta=1e-6)
+    assert st8["reason"] == lad.LAD_CG_MAX_ITERS and st8["iterations"] == 8
     p, st = L.newton_cg(dev(x_h, "f32"), dev(g_h, "f32"), max_iters=16, eta=1e-6)
     assert st["reason"] == lad.LAD_CG_MAX_ITERS and st["iterations"] == 16
     ph = p.cpu().numpy().astype(np.float64)

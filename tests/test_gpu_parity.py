@@ -277,3 +277,87 @@ def test_no_host_sync_in_step_calls(lad, path):
     assert s1 - s0 == 1
     torch.cuda.synchronize()
     L.close()
+
+
+def _spin_seconds(torch, cycles):
+    torch.cuda.synchronize()
+    import time
+    t0 = time.perf_counter()
+    torch.cuda._sleep(cycles)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+@pytest.mark.parametrize("path", ["rows", "patch"])
+def test_step_calls_return_while_stream_busy(lad, path):
+    """The same check as test_no_host_sync_in_step_calls, independent of
+    the library's own count: a spin kernel of at least a tenth of a second
+    is queued first on the stream, and the step calls (evaluation, HVP,
+    insertion, restore) must all return to the host well before it ends,
+    which they could not if any of them waited for the stream."""
+    import time
+    import torch
+    log_case(test="stream_busy", path=path)
+    m = inputs.cloth(30)
+    P = 18
+    L = lad.Lad(m.nv, dtype="f32", path=path,
+                **lad.mesh_terms(m, pair_capacity=P, kappa=inputs.BARRIER_KAPPA, dhat=0.5 * m.h))
+    x = dev(host_input(m.x, "f32"), "f32")
+    v = dev(host_input(inputs.hvp_direction(m.nv), "f32"), "f32")
+    pairs, _ = inputs.contact_pairs(m, m.x, step=0)
+    pd = torch.tensor(pairs, dtype=torch.int32, device="cuda")
+    out = L.alloc_outputs()
+    y = torch.empty_like(v)
+    L.eval(x, out=out)  # first calls (lazy set-up) outside the timed part
+    L.hvp(x, v, out=y)
+    cycles = 20_000_000
+    spin = _spin_seconds(torch, cycles)
+    while spin < 0.1:
+        cycles *= 2
+        spin = _spin_seconds(torch, cycles)
+    torch.cuda._sleep(cycles)
+    t0 = time.perf_counter()
+    for _ in range(3):
+        L.eval(x, out=out)
+        L.hvp(x, v, out=y)
+        L.insert_pairs(pd)
+        L.eval(x, out=out, energy=False)
+        L.insert_pairs(None)
+    host = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    assert host < 0.5 * spin, (host, spin)
+    L.close()
+
+
+def test_debug_mode_reports_nonfinite_outputs(lad):
+    """lad_set_debug(LAD_DEBUG_NONFINITE): an evaluation or product whose
+    output holds a NaN or an inf latches LAD_ERR_NONFINITE for
+    lad_device_status; finite outputs leave it clear; with the mode off no
+    check runs."""
+    import torch
+    log_case(test="debug_nonfinite")
+    m = inputs.cloth(20)
+    L = lad.Lad(m.nv, dtype="f32", **lad.mesh_terms(m))
+    x = dev(host_input(m.x, "f32"), "f32")
+    v = dev(host_input(inputs.hvp_direction(m.nv), "f32"), "f32")
+    out = L.alloc_outputs()
+    L.set_debug(lad.LAD_DEBUG_NONFINITE)
+    L.eval(x, out=out)
+    L.hvp(x, v)
+    assert L.device_status() == lad.LAD_OK
+    xbad = x.clone()
+    xbad[7, 1] = float("nan")
+    L.eval(xbad, out=out)
+    assert L.device_status() == lad.LAD_ERR_NONFINITE
+    assert L.device_status() == lad.LAD_OK  # read and cleared
+    vbad = v.clone()
+    vbad[3, 0] = float("inf")
+    L.hvp(x, vbad)
+    assert L.device_status() == lad.LAD_ERR_NONFINITE
+    L.set_debug(0)
+    L.eval(xbad, out=out)
+    assert L.device_status() == lad.LAD_OK
+    with pytest.raises(lad.LadError):
+        L.set_debug(2)
+    torch.cuda.synchronize()
+    L.close()

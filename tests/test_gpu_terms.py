@@ -203,3 +203,49 @@ def test_single_vertex(lad):
     assert np.allclose(H.cpu().numpy()[0], 3.0 * np.eye(3), rtol=1e-15)
     assert np.allclose(y.cpu().numpy(), [[3.0, 6.0, 9.0]], rtol=1e-15)
     T.close()
+
+
+def test_eval_and_hvp_make_no_host_sync(lad):
+    """lad_terms_eval and lad_terms_hvp never synchronise with the host: the
+    context's own count does not move, and the calls return while a spin
+    kernel of at least a tenth of a second still occupies the stream."""
+    import time
+    import torch
+    log_case(test="terms_no_host_sync")
+    m = inputs.cloth(30)
+    T = terms.Terms(m.nv, "arap_cloth", terms.mesh_blocks(m, "arap_cloth"), dtype="f32")
+    x = dev(host_input(m.x, "f32"), "f32")
+    v = dev(host_input(inputs.hvp_direction(m.nv), "f32"), "f32")
+    out = T.alloc_outputs()
+    y = torch.empty_like(v)
+    T.eval(x, out=out)
+    T.hvp(x, v, out=y)
+    torch.cuda.synchronize()
+    s0 = T.host_syncs()
+    assert s0 >= 1  # the build's
+    cycles = 20_000_000
+
+    def spin(c):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        torch.cuda._sleep(c)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    sp = spin(cycles)
+    while sp < 0.1:
+        cycles *= 2
+        sp = spin(cycles)
+    torch.cuda._sleep(cycles)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        T.eval(x, out=out)
+        T.eval(x, out=out, energy=False)
+        T.hvp(x, v, out=y)
+    host = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    assert host < 0.5 * sp, (host, sp)
+    assert T.host_syncs() == s0
+    T.pattern()
+    assert T.host_syncs() == s0 + 1
+    T.close()
