@@ -1229,7 +1229,9 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
         if (live)
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                y[int64_t(a) * 3 + k] = Y[k];
+                // non-temporal: y is not read again here, and its lines
+                // would evict neighbours' x and v from L2
+                __builtin_nontemporal_store(Y[k], y + int64_t(a) * 3 + k);
                 vy += double(va[k]) * double(Y[k]);
             }
     }
