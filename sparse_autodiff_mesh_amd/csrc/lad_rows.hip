@@ -1437,6 +1437,9 @@ hipError_t rows_grid(int lds_blocks, int nchunk, int faces, int pairs, int *grid
         const int64_t g = units < full ? units : full;
         return int(g < 1 ? 1 : g);
     };
+    // single-wave workgroups: a resident count per CU that is a multiple of
+    // its four SIMDs gives every SIMD the same number of waves
+    if (occ_e > 4) occ_e -= occ_e % 4;
     *grid_eval = clamp(occ_e, nchunk);
     // the product kernels walk rows kHvpThreads at a time; chunks hold at
     // most kRowsPerChunk rows

@@ -29,8 +29,8 @@ template <typename T, typename... Ts>
 void launch_eval_fused(TermList<Ts...>, const TermsArgs<T> &a, const T *x, T *g, T *hv,
                        EnergySink es, int grid, int lds, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_terms_eval<T, false, Ts...>), dim3(grid), dim3(kRowThreads), lds, s, a,
-                       x, g, hv, es);
+    hipLaunchKernelGGL((k_terms_eval<T, false, true, Ts...>), dim3(grid), dim3(kRowThreads), lds, s,
+                       a, x, g, hv, es);
 }
 
 template <typename T, bool ACC, typename Term>
@@ -39,8 +39,8 @@ void launch_eval_one(const TermsArgs<T> &a, int idx, const T *x, T *g, T *hv, En
 {
     TermsArgs<T> b = a;
     b.t[0] = a.t[idx];
-    hipLaunchKernelGGL((k_terms_eval<T, ACC, Term>), dim3(grid), dim3(kRowThreads), lds, s, b, x,
-                       g, hv, EnergySink{es.parts, es.part0 + idx * grid});
+    hipLaunchKernelGGL((k_terms_eval<T, ACC, false, Term>), dim3(grid), dim3(kRowThreads), lds, s,
+                       b, x, g, hv, EnergySink{es.parts, es.part0 + idx * grid});
 }
 
 // Unfused: one launch per term, the later ones adding into g and H.
@@ -80,7 +80,7 @@ template <typename T, typename... Ts>
 hipError_t occupancy(TermList<Ts...>, int lds, int *occ_e, int *occ_h)
 {
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        occ_e, k_terms_eval<T, false, Ts...>, kRowThreads, lds);
+        occ_e, k_terms_eval<T, false, true, Ts...>, kRowThreads, lds);
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_terms_hvp<T, false, Ts...>,
                                                          kTermsHvpThreads, 0);
@@ -142,6 +142,11 @@ hipError_t terms_grid(int set, int lds, int nchunk, int nv, int *grid_eval, int 
         const int64_t g = units < full ? units : full;
         return int(g < 1 ? 1 : g);
     };
+    // The explicit pass's workgroups are single waves: a resident count that
+    // is not a multiple of the CU's four SIMDs leaves some SIMDs a wave more
+    // work than others (10 per CU: 125 us for the cloth set at 1000^2, 8 per
+    // CU: 92 us).
+    if (occ_e > 4) occ_e -= occ_e % 4;
     *grid_eval = clamp(occ_e, nchunk);
     // The product's lanes each walk their own row's records, so a wave
     // touches a wide strip of lines; more than kTermsHvpGroupsPerCU resident

@@ -248,6 +248,9 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
     // ---- per term: incidence (rows in vertex order, elements by id), elements, constants
     e = upload(ctx, &ctx->d_diag, diag, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_chunk, chunks, s);
+    // first writer of every block of each row, in term order, then record
+    // order (records of a row are filled in element order)
+    std::vector<unsigned char> written(static_cast<size_t>(ctx->nnzb), 0);
     for (int t = 0; t < ctx->nterms && e == hipSuccess; ++t) {
         const lad_term_block &b = d->blocks[t];
         const int K = ctx->info[t].arity, NC = ctx->info[t].nconst;
@@ -267,6 +270,11 @@ lad_status build_typed(lad_terms_ctx *ctx, const lad_terms_desc *d, hipStream_t 
                     const int32_t pos = find_pos(rp, ci, a, v[(i + q) % K]);
                     if (pos < 0) return fail(nullptr, LAD_ERR_HIP, "element block missing from pattern");
                     r.pk |= uint32_t(pos) << (8 * q);
+                    unsigned char &wr = written[size_t(rp[size_t(a)] + pos)];
+                    if (!wr) {
+                        r.pk |= 1u << (1 + q);
+                        wr = 1;
+                    }
                 }
                 inc[size_t(cur[size_t(a)]++)] = r;
             }

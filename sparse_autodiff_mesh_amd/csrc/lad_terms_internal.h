@@ -25,9 +25,13 @@ constexpr int kSetArapCloth = 4;
 constexpr int kSetClothQuad = 5;
 
 // One element seen from the row of one of its vertices: e is the element
-// id; pk holds the row vertex's position i in the element (bits 0-1) and,
-// for b = 1 .. K-1, the block offset within the row of the element's
-// vertex (i + b) % K (bits 8b .. 8b+7).
+// id; pk holds the row vertex's position i in the element (bits 0-1), for
+// b = 1 .. K-1 the block offset within the row of the element's vertex
+// (i + b) % K (bits 8b .. 8b+7), and whether this record is that block's
+// first writer in the row (bit 1 + b): the first record, in the set's term
+// order and then the row's record order, whose element holds the column,
+// which stores its part instead of adding it (the fused explicit pass
+// starts from unwritten staging).
 struct alignas(8) TermInc {
     int32_t e;
     uint32_t pk;

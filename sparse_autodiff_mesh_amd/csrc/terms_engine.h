@@ -153,9 +153,19 @@ constexpr bool use_relative()
     return Term::kTranslationInvariant && Term::kVerts >= 2 && Term::kVerts <= 3;
 }
 
+// A block's part into the staged row: stored by the block's first writer
+// (FW: the fused pass, which starts from unwritten staging), else added.
+template <bool FW, typename T>
+__device__ __forceinline__ void put_block(T *B, uint32_t pk, int b, const T (&h)[9])
+{
+    const bool first = FW && ((pk >> (1 + b)) & 1u);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) B[k] = first ? h[k] : B[k] + h[k];
+}
+
 // Row i's blocks of element (e, vertices vid) by relative seeding; adds
 // into D (the row's diagonal), G and the row's blocks at the offsets in pk.
-template <typename Term, typename T>
+template <typename Term, bool FW, typename T>
 __device__ __forceinline__ void row_elem_relative(const T (&xv)[Term::kVerts][3], const T *cc,
                                                   int i, uint32_t pk, T *Hrow, T D[9], T G[3],
                                                   double &E)
@@ -196,11 +206,12 @@ __device__ __forceinline__ void row_elem_relative(const T (&xv)[Term::kVerts][3]
 #pragma unroll
     for (int b = 1; b < K; ++b) {
         const int v = (i + b) % K;
-        T *B = Hrow + 9 * int32_t((pk >> (8 * b)) & 255u);
+        T h[9];
 #pragma unroll
         for (int r = 0; r < 3; ++r)
 #pragma unroll
-            for (int c = 0; c < 3; ++c) B[3 * r + c] += hb(i, v, r, c);
+            for (int c = 0; c < 3; ++c) h[3 * r + c] = hb(i, v, r, c);
+        put_block<FW>(Hrow + 9 * int32_t((pk >> (8 * b)) & 255u), pk, b, h);
     }
 }
 
@@ -208,7 +219,7 @@ __device__ __forceinline__ void row_elem_relative(const T (&xv)[Term::kVerts][3]
 // elements, every load first (records, vertex ids, positions, constants),
 // then the evaluations.  D is the row's diagonal block, G its gradient,
 // Hrow its slice of the staged blocks.
-template <typename Term, typename T>
+template <typename Term, bool FW, typename T>
 __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
                                              const T *__restrict__ x, T *Hrow, T D[9],
                                              T G[3], double &E)
@@ -234,7 +245,7 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
             if (base + j >= p1) break;
             const int i = int(rec[j].pk & 3u);
             if constexpr (use_relative<Term>()) {
-                row_elem_relative<Term>(xv[j], cc[j], i, rec[j].pk, Hrow, D, G, E);
+                row_elem_relative<Term, FW>(xv[j], cc[j], i, rec[j].pk, Hrow, D, G, E);
                 continue;
             }
             StripDual<T, N> z[K][3];
@@ -254,30 +265,34 @@ __device__ __forceinline__ void row_term_eval(const TermData<T> &td, int32_t a,
             }
 #pragma unroll
             for (int b = 1; b < K; ++b) {
-                T *B = Hrow + 9 * int32_t((rec[j].pk >> (8 * b)) & 255u);
+                T h[9];
 #pragma unroll
                 for (int r = 0; r < 3; ++r)
 #pragma unroll
-                    for (int c = 0; c < 3; ++c) B[3 * r + c] += en.h[r][3 * b + c];
+                    for (int c = 0; c < 3; ++c) h[3 * r + c] = en.h[r][3 * b + c];
+                put_block<FW>(Hrow + 9 * int32_t((rec[j].pk >> (8 * b)) & 255u), rec[j].pk, b, h);
             }
         }
     }
 }
 
-template <typename T, typename... Terms, size_t... I>
+template <typename T, bool FW, typename... Terms, size_t... I>
 __device__ __forceinline__ void row_eval_all(const TermsArgs<T> &A, int32_t a,
                                              const T *__restrict__ x, T *Hrow, T D[9], T G[3],
                                              double &E, std::index_sequence<I...>)
 {
-    (row_term_eval<Terms>(A.t[I], a, x, Hrow, D, G, E), ...);
+    (row_term_eval<Terms, FW>(A.t[I], a, x, Hrow, D, G, E), ...);
 }
 
 // Energy, gradient and Hessian rows of the term list.  With ACC set the
 // launch adds into g and H as they are (the unfused mode's later terms);
-// otherwise it overwrites them.  Chunks of 64 rows are staged in LDS (a
-// single-wave workgroup, so the hand-off needs no barrier) and streamed out
-// with 16-byte non-temporal stores.
-template <typename T, bool ACC, typename... Terms>
+// otherwise it overwrites them.  FW (the fused launch of the whole list):
+// every block's first writer stores it and the diagonal is stored, so the
+// staging is not zeroed first; else it is zeroed (or read back, ACC) and
+// every part added.  Chunks of 64 rows are staged in LDS (a single-wave
+// workgroup, so the hand-off needs no barrier) and streamed out with
+// 16-byte non-temporal stores.
+template <typename T, bool ACC, bool FW, typename... Terms>
 __global__ void __launch_bounds__(kRowThreads)
 k_terms_eval(TermsArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
              EnergySink esink)
@@ -298,7 +313,7 @@ k_terms_eval(TermsArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
         if (fits) {
             if constexpr (ACC)
                 stream_in<kRowThreads>(Hs, hv + int64_t(sb) * 9, nblk * 9, pad);
-            else
+            else if constexpr (!FW)
                 for (int k = int(threadIdx.x); k < nblk * 9; k += kRowThreads) Hs[k] = T(0);
         }
         terms_lds_sync();
@@ -310,11 +325,11 @@ k_terms_eval(TermsArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
             for (int k = 0; k < 9; ++k) D[k] = T(0);
 #pragma unroll
             for (int k = 0; k < 3; ++k) G[k] = ACC ? g[int64_t(a) * 3 + k] : T(0);
-            row_eval_all<T, Terms...>(A, a, x, Hrow, D, G, eacc,
-                                      std::index_sequence_for<Terms...>{});
+            row_eval_all<T, FW, Terms...>(A, a, x, Hrow, D, G, eacc,
+                                          std::index_sequence_for<Terms...>{});
             T *B = Hrow + 9 * A.diag[a];
 #pragma unroll
-            for (int k = 0; k < 9; ++k) B[k] += D[k];
+            for (int k = 0; k < 9; ++k) B[k] = FW ? D[k] : B[k] + D[k];
 #pragma unroll
             for (int k = 0; k < 3; ++k) g[int64_t(a) * 3 + k] = G[k];
         }
