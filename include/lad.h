@@ -100,7 +100,8 @@ typedef struct {
     double kappa;               /* pair barrier stiffness                      */
     double dhat;                /* pair barrier support, > 0 if pair_capacity>0 */
 
-    int32_t eval_path;          /* LAD_PATH_AUTO, LAD_PATH_PATCH or LAD_PATH_ROWS */
+    int32_t eval_path;          /* LAD_PATH_AUTO, LAD_PATH_PATCH, LAD_PATH_ROWS
+                                   or LAD_PATH_PATCH_ATOMIC                   */
     int32_t vf_capacity;        /* max vertex-face contacts per
                                    lad_insert_contacts, >= 0; > 0 needs faces
                                    (nf > 0) and the row path                  */
@@ -116,8 +117,18 @@ typedef struct {
  *                  without atomics.  Requires rest lengths >= 0, at most one
  *                  spring per vertex pair and, with face terms, rows shorter
  *                  than 256 blocks.
- *  LAD_PATH_AUTO   LAD_PATH_ROWS when its requirements hold, else PATCH.  */
-enum { LAD_PATH_AUTO = 0, LAD_PATH_PATCH = 1, LAD_PATH_ROWS = 2 };
+ *  LAD_PATH_AUTO   LAD_PATH_ROWS when its requirements hold, else PATCH.
+ *  LAD_PATH_PATCH_ATOMIC  the page's own assembly: each element is evaluated
+ *                  once, by the patch owning its lowest vertex id; its
+ *                  blocks and gradient entries in other patches' rows are
+ *                  added with global float atomics into slots that a small
+ *                  launch zeroes first (Source: page "Locality-Aware
+ *                  Automatic Differentiation on the GPU for Mesh-Based
+ *                  Computations", key designs 3 and 4: atomic scatter-add
+ *                  into the preallocated pattern).  Results vary in the last
+ *                  bits from run to run.  Takes no deterministic mode and no
+ *                  contact capacity (LAD_ERR_ARG otherwise).  */
+enum { LAD_PATH_AUTO = 0, LAD_PATH_PATCH = 1, LAD_PATH_ROWS = 2, LAD_PATH_PATCH_ATOMIC = 3 };
 
 /* Summary of a context (lad_get_info synchronises the context's stream to
  * read the device-side active pattern size). */

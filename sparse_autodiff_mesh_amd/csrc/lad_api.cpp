@@ -24,6 +24,7 @@ struct lad_ctx {
     lad_dtype dtype = LAD_F32;
     int32_t es = 4;
     int32_t det = 0;
+    int32_t mode = kModeLdsAtomic;   // PatchMode of the patch kernels
     hipStream_t stream = nullptr;
     int64_t nnzb_base = 0, hcap = 0;
     int32_t pair_cap = 0;
@@ -59,6 +60,11 @@ struct lad_ctx {
     void *d_fac_area = nullptr;
     int32_t *d_col_bounds = nullptr;
     uint16_t *d_diag_rel = nullptr;
+    // element-once patches (LAD_PATH_PATCH_ATOMIC): see Plan
+    int32_t *d_spr_gblk = nullptr, *d_fac_gblk = nullptr;
+    uint8_t *d_blk_flag = nullptr, *d_vtx_flag = nullptr;
+    int32_t *d_bnd_blk = nullptr, *d_bnd_vtx = nullptr;
+    int32_t nbnd_blk = 0, nbnd_vtx = 0;
     void *d_xt = nullptr;
     DevState *d_state = nullptr;
     double *d_epart = nullptr;
@@ -144,8 +150,12 @@ std::string check_desc(const lad_mesh_desc *d)
     if (d->vf_capacity > 0 && d->eval_path == LAD_PATH_PATCH)
         return "vertex-face contacts need the row path";
     if (d->eval_path != LAD_PATH_AUTO && d->eval_path != LAD_PATH_PATCH &&
-        d->eval_path != LAD_PATH_ROWS)
-        return "eval_path must be LAD_PATH_AUTO, LAD_PATH_PATCH or LAD_PATH_ROWS";
+        d->eval_path != LAD_PATH_ROWS && d->eval_path != LAD_PATH_PATCH_ATOMIC)
+        return "eval_path must be LAD_PATH_AUTO, LAD_PATH_PATCH, LAD_PATH_ROWS or "
+               "LAD_PATH_PATCH_ATOMIC";
+    if (d->eval_path == LAD_PATH_PATCH_ATOMIC &&
+        (d->deterministic || d->pair_capacity > 0 || d->vf_capacity > 0))
+        return "LAD_PATH_PATCH_ATOMIC takes no deterministic mode and no contact capacity";
     if (d->patch_lds_bytes < 0 || d->patch_lds_bytes > kMaxPatchLds)
         return "patch_lds_bytes must be in [0, " + std::to_string(kMaxPatchLds) + "]";
     if (d->nf > 0 && !d->faces) return "faces is NULL";
@@ -271,6 +281,10 @@ PatchArgs<T> patch_args(const lad_ctx *ctx)
     a.inertia_on = ctx->inertia_on;
     a.state = ctx->d_state;
     a.pat = ctx->pat;
+    a.spr_gblk = ctx->d_spr_gblk;
+    a.fac_gblk = ctx->d_fac_gblk;
+    a.blk_flag = ctx->d_blk_flag;
+    a.vtx_flag = ctx->d_vtx_flag;
     return a;
 }
 
@@ -348,8 +362,15 @@ hipError_t enqueue_eval(lad_ctx *ctx, const void *x, double *energy, void *g, vo
         }
     } else {
         const PatchArgs<T> a = patch_args<T>(ctx);
-        e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g), static_cast<T *>(hv),
-                           EnergySink{parts, 0}, ctx->det, ctx->lds_eval, s);
+        // element-once patches add into the boundary slots: zero them first
+        if (ctx->mode == kModeBoundaryAtomic)
+            e = launch_zero_boundary<T>(ctx->d_bnd_blk, ctx->nbnd_blk, ctx->d_bnd_vtx,
+                                        ctx->nbnd_vtx, static_cast<T *>(hv), static_cast<T *>(g),
+                                        s);
+        if (e == hipSuccess)
+            e = launch_eval<T>(a, static_cast<const T *>(x), static_cast<T *>(g),
+                               static_cast<T *>(hv), EnergySink{parts, 0}, ctx->mode,
+                               ctx->lds_eval, s);
         if (e == hipSuccess && ctx->pair_blocks > 0)
             e = launch_pairs_eval<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
                                      static_cast<T *>(g), static_cast<T *>(hv),
@@ -365,8 +386,13 @@ template <typename T>
 hipError_t enqueue_hvp_patch(lad_ctx *ctx, const void *x, const void *v, void *y, hipStream_t s)
 {
     const PatchArgs<T> a = patch_args<T>(ctx);
-    hipError_t e = launch_hvp<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
-                                 static_cast<T *>(y), ctx->det, ctx->lds_hvp, s);
+    hipError_t e = hipSuccess;
+    if (ctx->mode == kModeBoundaryAtomic)
+        e = launch_zero_boundary<T>(nullptr, 0, ctx->d_bnd_vtx, ctx->nbnd_vtx, (T *)nullptr,
+                                    static_cast<T *>(y), s);
+    if (e == hipSuccess)
+        e = launch_hvp<T>(a, static_cast<const T *>(x), static_cast<const T *>(v),
+                          static_cast<T *>(y), ctx->mode, ctx->lds_hvp, s);
     if (e == hipSuccess && ctx->pair_blocks > 0)
         e = launch_pairs_hvp<T>(ctx->d_state, ctx->pat, static_cast<const T *>(x),
                                 static_cast<const T *>(v), static_cast<T *>(y), ctx->pair_blocks,
@@ -529,6 +555,9 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     ctx->dtype = d->dtype;
     ctx->es = d->dtype == LAD_F64 ? 8 : 4;
     ctx->det = d->deterministic ? 1 : 0;
+    ctx->mode = d->deterministic                          ? kModeColour
+                : d->eval_path == LAD_PATH_PATCH_ATOMIC ? kModeBoundaryAtomic
+                                                          : kModeLdsAtomic;
     ctx->stream = s;
     ctx->pair_cap = d->pair_capacity;
     ctx->vf_cap = d->vf_capacity;
@@ -623,10 +652,12 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     in.col_idx = h_ci.data();
     in.elem_size = ctx->es;
     in.lds_budget = d->patch_lds_bytes > 0 ? d->patch_lds_bytes : kDefaultPatchLds;
+    in.element_once = ctx->mode == kModeBoundaryAtomic ? 1 : 0;
     Plan plan;
     RowPlan rplan;
     std::string why = "patch path requested";
-    if (d->eval_path != LAD_PATH_PATCH) why = build_row_plan(in, d->rest_len, rplan);
+    if (d->eval_path != LAD_PATH_PATCH && d->eval_path != LAD_PATH_PATCH_ATOMIC)
+        why = build_row_plan(in, d->rest_len, rplan);
     if (d->eval_path == LAD_PATH_ROWS && !why.empty())
         return fail(ctx, LAD_ERR_ARG, "row path not applicable: " + why);
     ctx->row_mode = why.empty() ? 1 : 0;
@@ -656,6 +687,16 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (e == hipSuccess) e = upload(ctx, &ctx->d_fac, plan.fac, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_col_bounds, plan.col_bounds, s);
     if (e == hipSuccess) e = upload(ctx, &ctx->d_diag_rel, plan.diag_rel, s);
+    if (e == hipSuccess && ctx->mode == kModeBoundaryAtomic) {
+        e = upload(ctx, &ctx->d_spr_gblk, plan.spr_gblk, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_fac_gblk, plan.fac_gblk, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_blk_flag, plan.blk_flag, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_vtx_flag, plan.vtx_flag, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_bnd_blk, plan.bnd_blk, s);
+        if (e == hipSuccess) e = upload(ctx, &ctx->d_bnd_vtx, plan.bnd_vtx, s);
+        ctx->nbnd_blk = int32_t(plan.bnd_blk.size());
+        ctx->nbnd_vtx = int32_t(plan.bnd_vtx.size());
+    }
     // with pair capacity: the insertion's tiles (whole row chunks on the row
     // path, for its capacity check; fixed row blocks on the patch path)
     // (the pointers are stored in ctx->ins after that struct is reset below)
@@ -877,7 +918,9 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     info->face_records = ctx->nfac_rec;
     info->max_colors = ctx->max_colors;
     info->active_buffer = hs.active;
-    info->eval_path = ctx->row_mode ? LAD_PATH_ROWS : LAD_PATH_PATCH;
+    info->eval_path = ctx->row_mode                         ? LAD_PATH_ROWS
+                      : ctx->mode == kModeBoundaryAtomic ? LAD_PATH_PATCH_ATOMIC
+                                                         : LAD_PATH_PATCH;
     info->grid_eval = ctx->grid_eval;
     info->host_syncs = ctx->host_syncs;
     return LAD_OK;

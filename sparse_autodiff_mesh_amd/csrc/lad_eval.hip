@@ -46,24 +46,47 @@ __device__ __forceinline__ void add_block3(T *B, const Dual2<T, 3> &e, T s)
         for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(B + 3 * r + c, s * e.hess(r, c));
 }
 
+// Global float atomic add (the hardware instruction; relaxed, device scope).
+template <typename T>
+__device__ __forceinline__ void global_add(T *p, T v)
+{
+    (void)unsafeAtomicAdd(p, v);
+}
+
+// Element-once patches: where an element's contributions to the rows of
+// other patches go.  rib: the patch's ribbon list (local id nown + i is
+// vertex rib[i]); hv, g: the global value array and gradient.
+template <typename T>
+struct Foreign {
+    T *hv;
+    T *g;
+    const int32_t *rib;
+};
+
 // ---------------------------------------------------------------------------
 // Element bodies.  xs: staged positions (local ids); nown: owned count.
 // ---------------------------------------------------------------------------
 
 // Two-vertex spring, differentiated in z = x_a - x_b.  With K = d2f/dz2 and
 // q = df/dz the element blocks are g = [q, -q], H = [[K, -K], [-K, K]].
-template <bool ATOMIC, typename T>
+//
+// GA (element-once patches): the record is this element's only one, so its
+// energy always counts here, and a non-owned endpoint f gets its blocks
+// (f, f), (f, other) = gb[0], gb[1] and its gradient entries by global
+// atomics.
+template <bool ATOMIC, bool GA, typename T>
 __device__ __forceinline__ void spring_eval(const SpringRec rec, T rest, T k, const T *xs,
                                             T *H, T *gs, const uint16_t *dtab, int nown,
-                                            double &eacc)
+                                            double &eacc, const Foreign<T> &fo = {},
+                                            const int32_t *gb = nullptr)
 {
     const int la = rec.lab & 0xFFFF, lb = rec.lab >> 16;
     Dual2<T, 3> d[3];
 #pragma unroll
     for (int c = 0; c < 3; ++c) d[c] = Dual2<T, 3>::var(xs[3 * la + c] - xs[3 * lb + c], c);
     const Dual2<T, 3> e = spring_energy(d, rest, k);
+    if (GA || la < nown) eacc += double(e.v);
     if (la < nown) {
-        eacc += double(e.v);
 #pragma unroll
         for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(gs + 3 * la + c, e.g[c]);
         add_block3<ATOMIC>(H + 9 * dtab[la], e, T(1));
@@ -74,6 +97,24 @@ __device__ __forceinline__ void spring_eval(const SpringRec rec, T rest, T k, co
         for (int c = 0; c < 3; ++c) lds_add<ATOMIC>(gs + 3 * lb + c, -e.g[c]);
         add_block3<ATOMIC>(H + 9 * dtab[lb], e, T(1));
         add_block3<ATOMIC>(H + 9 * (rec.blk >> 16), e, T(-1));
+    }
+    if constexpr (GA) {
+        if (la >= nown || lb >= nown) {
+            const bool fa = la >= nown;
+            const int64_t f = fo.rib[(fa ? la : lb) - nown];
+            const T sg = fa ? T(1) : T(-1);
+            T *Bff = fo.hv + int64_t(gb[0]) * 9;
+            T *Bfo = fo.hv + int64_t(gb[1]) * 9;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) global_add(fo.g + 3 * f + c, sg * e.g[c]);
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    global_add(Bff + 3 * r + c, e.hess(r, c));
+                    global_add(Bfo + 3 * r + c, -e.hess(r, c));
+                }
+        }
     }
 }
 
@@ -110,24 +151,32 @@ __device__ __forceinline__ void face_local(const FaceRec &rec, const T *dm, T ar
     out.w[0][1] = -(m01 + m11);
 }
 
-template <bool ATOMIC, typename T>
+// GA (element-once patches): energy always counts; the rows of non-owned
+// vertices v get their blocks (v, u) = gb[3 v + u] and gradient entries by
+// global atomics.
+template <bool ATOMIC, bool GA, typename T>
 __device__ __forceinline__ void face_eval(const FaceRec rec, const T *dm, T area, const T *xs,
-                                          T *H, T *gs, int nown, double &eacc)
+                                          T *H, T *gs, int nown, double &eacc,
+                                          const Foreign<T> &fo = {}, const int32_t *gb = nullptr)
 {
     FaceLocal<T> fl;
     face_local(rec, dm, area, xs, fl);
     const Dual2<T, 6> &e = fl.e;
-    if (rec.l[0] < nown) eacc += double(e.v);
+    if (GA || rec.l[0] < nown) eacc += double(e.v);
 #pragma unroll
     for (int v = 0; v < 3; ++v) {
-        if (rec.l[v] >= nown) continue;
+        const bool own = rec.l[v] < nown;
+        if (!GA && !own) continue;
+        T *gv = own ? gs + 3 * rec.l[v] : fo.g + 3 * int64_t(fo.rib[rec.l[v] - nown]);
 #pragma unroll
-        for (int s = 0; s < 3; ++s)
-            lds_add<ATOMIC>(gs + 3 * rec.l[v] + s,
-                            fl.w[v][0] * e.g[2 * s] + fl.w[v][1] * e.g[2 * s + 1]);
+        for (int s = 0; s < 3; ++s) {
+            const T gsv = fl.w[v][0] * e.g[2 * s] + fl.w[v][1] * e.g[2 * s + 1];
+            if (own) lds_add<ATOMIC>(gv + s, gsv);
+            else global_add(gv + s, gsv);
+        }
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            T *B = H + 9 * rec.blk[3 * v + u];
+            T *B = own ? H + 9 * rec.blk[3 * v + u] : fo.hv + int64_t(gb[3 * v + u]) * 9;
 #pragma unroll
             for (int s = 0; s < 3; ++s)
 #pragma unroll
@@ -137,20 +186,69 @@ __device__ __forceinline__ void face_eval(const FaceRec rec, const T *dm, T area
                                  e.hess(2 * s, 2 * t + 1) * fl.w[u][1];
                     const T q1 = e.hess(2 * s + 1, 2 * t) * fl.w[u][0] +
                                  e.hess(2 * s + 1, 2 * t + 1) * fl.w[u][1];
-                    lds_add<ATOMIC>(B + 3 * s + t, fl.w[v][0] * q0 + fl.w[v][1] * q1);
+                    const T bv = fl.w[v][0] * q0 + fl.w[v][1] * q1;
+                    if (own) lds_add<ATOMIC>(B + 3 * s + t, bv);
+                    else global_add(B + 3 * s + t, bv);
                 }
         }
     }
 }
 
+// Flush of an element-once patch's LDS slice: entries of flagged units
+// (blocks of 9 values, or vertices of 3; flag[] in LDS, one byte per unit)
+// also receive other patches' atomics into slots zeroed beforehand, so they
+// are added atomically (and skipped when this patch's part is zero); the
+// rest are stored, in aligned 16-byte non-temporal vectors where no flagged
+// unit touches the vector.  Same alignment contract as stream_out.
+template <int NT, int UNIT, typename T>
+__device__ __forceinline__ void flush_flagged(T *__restrict__ dst, const T *src, int n, int pad,
+                                              const uint8_t *flag)
+{
+    constexpr int V = Vec<T>::n;
+    using VT = typename Vec<T>::type;
+    auto one = [&](int i) {
+        const T val = src[i];
+        if (flag[i / UNIT]) {
+            if (val != T(0)) global_add(dst + i, val);
+        } else {
+            dst[i] = val;
+        }
+    };
+    const int head = min(n, (V - pad) % V);
+    for (int i = threadIdx.x; i < head; i += NT) one(i);
+    const int nvec = (n - head) / V;
+    VT *dv = reinterpret_cast<VT *>(dst + head);
+    const VT *sv = reinterpret_cast<const VT *>(src + head);
+    for (int i = threadIdx.x; i < nvec; i += NT) {
+        const int e0 = head + V * i;
+        if (flag[e0 / UNIT] | flag[(e0 + V - 1) / UNIT]) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) one(e0 + j);
+        } else {
+            __builtin_nontemporal_store(sv[i], dv + i);
+        }
+    }
+    for (int i = head + nvec * V + threadIdx.x; i < n; i += NT) one(i);
+}
+
 // ---------------------------------------------------------------------------
 // Eval kernel: energy, gradient and Hessian block rows of one patch.
 // ---------------------------------------------------------------------------
-template <typename T, bool DET>
+//
+// MODE (PatchMode): kModeLdsAtomic and kModeColour evaluate every element
+// touching an owned row and store the owned slice.  kModeBoundaryAtomic runs
+// an element-once plan: elements are evaluated by one patch only, their
+// contributions to other patches' rows go out as global atomics, and the
+// owned entries that also receive such atomics (zeroed by a launch before
+// this one; flagged per block and per vertex) are added, not stored.  That
+// mode has no pairs, so the active pattern is the topology pattern.
+template <typename T, int MODE>
 __global__ void __launch_bounds__(kThreads)
 k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
              EnergySink esink)
 {
+    constexpr bool DET = MODE == kModeColour;
+    constexpr bool GA = MODE == kModeBoundaryAtomic;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int V = Vec<T>::n;
     const int p = xcd_remap(blockIdx.x, gridDim.x);
@@ -192,6 +290,16 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
         xs[3 * h.nown + i] = x[int64_t(A.rib[h.rib_off + r]) * 3 + c];
     }
     for (int i = tid; i < h.nown; i += kThreads) dtab[i] = A.diag_rel[h.v0 + i];
+    // element-once: boundary flags of the owned blocks, then of the owned
+    // vertices, in the (otherwise unused) active-block map region, which
+    // holds at least nblk + nown bytes
+    uint8_t *bflag = reinterpret_cast<uint8_t *>(amap);
+    uint8_t *vflag = bflag + h.nblk;
+    if constexpr (GA) {
+        for (int i = tid; i < h.nblk; i += kThreads) bflag[i] = A.blk_flag[h.blk0 + i];
+        for (int i = tid; i < h.nown; i += kThreads) vflag[i] = A.vtx_flag[h.v0 + i];
+    }
+    const Foreign<T> fo{hv, g, A.rib + h.rib_off};
     __syncthreads();
 
     double eacc = 0.0;
@@ -219,12 +327,14 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
             const int32_t *cb = A.col_bounds + h.col_off;
             for (int c = 0; c < h.nspr_col; ++c) {
                 for (int e = cb[c] + tid; e < cb[c + 1]; e += kThreads)
-                    spring_eval<false>(R[e], L[e], A.k, xs, H, gs, dtab, h.nown, eacc);
+                    spring_eval<false, false>(R[e], L[e], A.k, xs, H, gs, dtab, h.nown, eacc);
                 __syncthreads();
             }
         } else {
+            const int32_t *gb = GA ? A.spr_gblk + 2 * int64_t(h.spr_off) : nullptr;
             for (int e = tid; e < h.nspr; e += kThreads)
-                spring_eval<true>(R[e], L[e], A.k, xs, H, gs, dtab, h.nown, eacc);
+                spring_eval<true, GA>(R[e], L[e], A.k, xs, H, gs, dtab, h.nown, eacc, fo,
+                                      GA ? gb + 2 * e : nullptr);
         }
     }
 
@@ -237,18 +347,26 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
             const int32_t *cb = A.col_bounds + h.col_off + (h.nspr_col ? h.nspr_col + 1 : 0);
             for (int c = 0; c < h.nfac_col; ++c) {
                 for (int e = cb[c] + tid; e < cb[c + 1]; e += kThreads)
-                    face_eval<false>(R[e], dm + 4 * e, ar[e], xs, H, gs, h.nown, eacc);
+                    face_eval<false, false>(R[e], dm + 4 * e, ar[e], xs, H, gs, h.nown, eacc);
                 __syncthreads();
             }
         } else {
+            const int32_t *gb = GA ? A.fac_gblk + 9 * int64_t(h.fac_off) : nullptr;
             for (int e = tid; e < h.nfac; e += kThreads)
-                face_eval<true>(R[e], dm + 4 * e, ar[e], xs, H, gs, h.nown, eacc);
+                face_eval<true, GA>(R[e], dm + 4 * e, ar[e], xs, H, gs, h.nown, eacc, fo,
+                                    GA ? gb + 9 * e : nullptr);
         }
     }
     __syncthreads();
 
     // 5. write the owned slice of the active pattern's value array
     T *dst = hv + int64_t(ra0) * 9;
+    if constexpr (GA) {
+        flush_flagged<kThreads, 9>(dst, H, h.nblk * 9, hpad, bflag);
+        flush_flagged<kThreads, 3>(g + int64_t(h.v0) * 3, gs, h.nown * 3, gpad, vflag);
+        store_energy(esink, block_sum<kThreads>(eacc, red));
+        return;
+    }
     if (!mapped) {
         stream_out<kThreads>(dst, H, h.nblk * 9, hpad);
     } else if (nact <= h.amap_cap) {
@@ -283,10 +401,14 @@ k_eval_patch(PatchArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
 // ---------------------------------------------------------------------------
 // HVP kernel: y = H(x) v for the owned rows of one patch, H never formed.
 // ---------------------------------------------------------------------------
-template <typename T, bool DET>
+// MODE as for k_eval_patch; with kModeBoundaryAtomic the y entries of
+// flagged vertices are zeroed by an earlier launch and added to.
+template <typename T, int MODE>
 __global__ void __launch_bounds__(kThreads)
 k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__restrict__ y)
 {
+    constexpr bool DET = MODE == kModeColour;
+    constexpr bool GA = MODE == kModeBoundaryAtomic;
     extern __shared__ __align__(16) unsigned char smem[];
     const int p = xcd_remap(blockIdx.x, gridDim.x);
     const PatchHdr h = A.hdr[p];
@@ -319,8 +441,15 @@ k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T 
         __syncthreads();
     }
 
-    auto spring_hvp = [&](const SpringRec rec, T rest, auto atomic_tag) {
+    // y entries of a local vertex: LDS for owned ones, HBM (global atomics)
+    // for the ribbon vertices of an element-once patch
+    const int32_t *rib = A.rib + h.rib_off;
+    auto y_add = [&](int l, int r, T val, auto atomic_tag) {
         constexpr bool AT = decltype(atomic_tag)::value;
+        if (l < h.nown) lds_add<AT>(ys + 3 * l + r, val);
+        else if constexpr (GA) global_add(y + 3 * int64_t(rib[l - h.nown]) + r, val);
+    };
+    auto spring_hvp = [&](const SpringRec rec, T rest, auto atomic_tag) {
         const int la = rec.lab & 0xFFFF, lb = rec.lab >> 16;
         Dual2<T, 3> d[3];
         T dv[3];
@@ -333,12 +462,11 @@ k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T 
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
             const T kv = e.hess(r, 0) * dv[0] + e.hess(r, 1) * dv[1] + e.hess(r, 2) * dv[2];
-            if (la < h.nown) lds_add<AT>(ys + 3 * la + r, kv);
-            if (lb < h.nown) lds_add<AT>(ys + 3 * lb + r, -kv);
+            y_add(la, r, kv, atomic_tag);
+            y_add(lb, r, -kv, atomic_tag);
         }
     };
     auto face_hvp = [&](const FaceRec rec, const T *dm, T area, auto atomic_tag) {
-        constexpr bool AT = decltype(atomic_tag)::value;
         FaceLocal<T> fl;
         face_local(rec, dm, area, xs, fl);
         // dF = B v_j, yF = (d2E/dF2) dF, y_v = B_v^T yF
@@ -359,13 +487,11 @@ k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T 
             yF[i] = acc;
         }
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            if (rec.l[u] >= h.nown) continue;
+        for (int u = 0; u < 3; ++u)
 #pragma unroll
             for (int s = 0; s < 3; ++s)
-                lds_add<AT>(ys + 3 * rec.l[u] + s,
-                            fl.w[u][0] * yF[2 * s] + fl.w[u][1] * yF[2 * s + 1]);
-        }
+                y_add(rec.l[u], s, fl.w[u][0] * yF[2 * s] + fl.w[u][1] * yF[2 * s + 1],
+                      atomic_tag);
     };
     using AtomicTag = std::integral_constant<bool, !DET>;
 
@@ -401,7 +527,35 @@ k_hvp_patch(PatchArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T 
     }
     __syncthreads();
     T *yo = y + int64_t(h.v0) * 3;
-    for (int i = tid; i < h.nown * 3; i += kThreads) yo[i] = ys[i];
+    if constexpr (GA) {
+        const uint8_t *vflag = A.vtx_flag + h.v0;
+        for (int i = tid; i < h.nown * 3; i += kThreads) {
+            const T val = ys[i];
+            if (vflag[i / 3]) {
+                if (val != T(0)) global_add(yo + i, val);
+            } else {
+                yo[i] = val;
+            }
+        }
+    } else {
+        for (int i = tid; i < h.nown * 3; i += kThreads) yo[i] = ys[i];
+    }
+}
+
+// Zero the slots that element-once patches add into (one thread per value).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+k_zero_boundary(const int32_t *__restrict__ bnd_blk, int32_t nb, const int32_t *__restrict__ bnd_vtx,
+                int32_t nvb, T *__restrict__ hv, T *__restrict__ vec)
+{
+    const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t nh = hv ? 9 * int64_t(nb) : 0;
+    if (i < nh) {
+        hv[9 * int64_t(bnd_blk[i / 9]) + i % 9] = T(0);
+    } else if (i - nh < 3 * int64_t(nvb)) {
+        const int64_t j = i - nh;
+        vec[3 * int64_t(bnd_vtx[j / 3]) + j % 3] = T(0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -567,30 +721,49 @@ hipError_t launch_energy_reduce(const double *parts, int32_t n, double *out, hip
 }
 
 template <typename T>
-hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hv, EnergySink es, int det,
+hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hv, EnergySink es, int mode,
                        int lds_bytes, hipStream_t s)
 {
     if (a.npatch == 0) return hipSuccess;
-    if (det)
-        hipLaunchKernelGGL((k_eval_patch<T, true>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
-                           a, x, g, hv, es);
+    const dim3 grid(a.npatch), block(kThreads);
+    if (mode == kModeColour)
+        hipLaunchKernelGGL((k_eval_patch<T, kModeColour>), grid, block, lds_bytes, s, a, x, g, hv,
+                           es);
+    else if (mode == kModeBoundaryAtomic)
+        hipLaunchKernelGGL((k_eval_patch<T, kModeBoundaryAtomic>), grid, block, lds_bytes, s, a, x,
+                           g, hv, es);
     else
-        hipLaunchKernelGGL((k_eval_patch<T, false>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
-                           a, x, g, hv, es);
+        hipLaunchKernelGGL((k_eval_patch<T, kModeLdsAtomic>), grid, block, lds_bytes, s, a, x, g,
+                           hv, es);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y, int det, int lds_bytes,
-                      hipStream_t s)
+hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y, int mode,
+                      int lds_bytes, hipStream_t s)
 {
     if (a.npatch == 0) return hipSuccess;
-    if (det)
-        hipLaunchKernelGGL((k_hvp_patch<T, true>), dim3(a.npatch), dim3(kThreads), lds_bytes, s, a,
-                           x, v, y);
+    const dim3 grid(a.npatch), block(kThreads);
+    if (mode == kModeColour)
+        hipLaunchKernelGGL((k_hvp_patch<T, kModeColour>), grid, block, lds_bytes, s, a, x, v, y);
+    else if (mode == kModeBoundaryAtomic)
+        hipLaunchKernelGGL((k_hvp_patch<T, kModeBoundaryAtomic>), grid, block, lds_bytes, s, a, x,
+                           v, y);
     else
-        hipLaunchKernelGGL((k_hvp_patch<T, false>), dim3(a.npatch), dim3(kThreads), lds_bytes, s,
-                           a, x, v, y);
+        hipLaunchKernelGGL((k_hvp_patch<T, kModeLdsAtomic>), grid, block, lds_bytes, s, a, x, v,
+                           y);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_zero_boundary(const int32_t *bnd_blk, int32_t nb, const int32_t *bnd_vtx,
+                                int32_t nvb, T *hv, T *vec, hipStream_t s)
+{
+    const int64_t n = (hv ? 9 * int64_t(nb) : 0) + 3 * int64_t(nvb);
+    if (n == 0) return hipSuccess;
+    const int64_t grid = (n + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_zero_boundary<T>, dim3(unsigned(grid)), dim3(kThreads), 0, s, bnd_blk,
+                       nb, bnd_vtx, nvb, hv, vec);
     return hipGetLastError();
 }
 
@@ -617,8 +790,12 @@ hipError_t launch_pairs_hvp(const DevState *st, PatternBufs pat, const T *x, con
 template <typename T>
 static hipError_t raise_lds_limit(int bytes)
 {
-    const void *fns[] = {(const void *)k_eval_patch<T, false>, (const void *)k_eval_patch<T, true>,
-                         (const void *)k_hvp_patch<T, false>, (const void *)k_hvp_patch<T, true>};
+    const void *fns[] = {(const void *)k_eval_patch<T, kModeLdsAtomic>,
+                         (const void *)k_eval_patch<T, kModeColour>,
+                         (const void *)k_eval_patch<T, kModeBoundaryAtomic>,
+                         (const void *)k_hvp_patch<T, kModeLdsAtomic>,
+                         (const void *)k_hvp_patch<T, kModeColour>,
+                         (const void *)k_hvp_patch<T, kModeBoundaryAtomic>};
     for (const void *f : fns) {
         const hipError_t e =
             hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -638,6 +815,8 @@ hipError_t raise_lds_limits(int bytes)
                                        int, hipStream_t);                                          \
     template hipError_t launch_hvp<T>(const PatchArgs<T> &, const T *, const T *, T *, int, int,   \
                                       hipStream_t);                                                \
+    template hipError_t launch_zero_boundary<T>(const int32_t *, int32_t, const int32_t *,         \
+                                                int32_t, T *, T *, hipStream_t);                   \
     template hipError_t launch_pairs_eval<T>(const DevState *, PatternBufs, const T *, T *, T *,   \
                                              EnergySink, int, T, T, hipStream_t);                  \
     template hipError_t launch_pairs_hvp<T>(const DevState *, PatternBufs, const T *, const T *,   \

@@ -89,6 +89,17 @@ struct Plan {
     std::vector<uint16_t> diag_rel;        // [nv] patch-relative diagonal block
     std::vector<int32_t> vpatch;           // [nv] owning patch of each vertex
     int32_t lds_eval = 0, lds_hvp = 0, max_colors = 0;
+    // Element-once plans (boundary atomics) only.  Each element is kept by
+    // the patch that owns its lowest vertex id; its other vertices may lie
+    // in other patches ("foreign" rows).  spr_gblk[2 r + 0 / 1]: global
+    // blocks (f, f) and (f, o) of spring record r's foreign endpoint f (o the
+    // other endpoint), -1 when both are owned; fac_gblk[9 r + 3 v + u]:
+    // global block (v, u) of face record r when its vertex v is foreign,
+    // else -1.  bnd_blk / bnd_vtx: the blocks and vertices that receive a
+    // foreign contribution (ascending); blk_flag [nnzb] / vtx_flag [nv]: 1
+    // for those, else 0.
+    std::vector<int32_t> spr_gblk, fac_gblk, bnd_blk, bnd_vtx;
+    std::vector<uint8_t> blk_flag, vtx_flag;
 };
 
 struct PlanInput {
@@ -102,6 +113,7 @@ struct PlanInput {
     const int32_t *col_idx = nullptr;
     int32_t elem_size = 4;
     int32_t lds_budget = 0;
+    int32_t element_once = 0;              // 1: each element in one patch only
 };
 
 // LDS bytes of one patch in the eval and HVP kernels (same formula the
@@ -229,6 +241,11 @@ struct PatchArgs {
     int32_t springs_on, faces_on, inertia_on;
     const DevState *state;
     PatternBufs pat;
+    // element-once plans (boundary atomics): see Plan
+    const int32_t *spr_gblk;
+    const int32_t *fac_gblk;
+    const uint8_t *blk_flag;
+    const uint8_t *vtx_flag;
 };
 
 // Where a launch puts its partial energies: workgroup b stores its sum at
@@ -246,12 +263,23 @@ hipError_t launch_energy_reduce(const double *parts, int32_t n, double *out, hip
 hipError_t launch_check_finite(DevState *st, const double *energy, const void *vec, int64_t nvec,
                                const void *hv, int es, hipStream_t s);
 
+// Assembly of the patch kernels: LDS atomics, colour phases (fixed order),
+// or element-once patches whose contributions to other patches' rows are
+// added with global float atomics into slots zeroed beforehand.
+enum PatchMode { kModeLdsAtomic = 0, kModeColour = 1, kModeBoundaryAtomic = 2 };
+
 template <typename T>
 hipError_t launch_eval(const PatchArgs<T> &a, const T *x, T *g, T *hvals,
-                       EnergySink es, int det, int lds_bytes, hipStream_t s);
+                       EnergySink es, int mode, int lds_bytes, hipStream_t s);
 template <typename T>
 hipError_t launch_hvp(const PatchArgs<T> &a, const T *x, const T *v, T *y,
-                      int det, int lds_bytes, hipStream_t s);
+                      int mode, int lds_bytes, hipStream_t s);
+// Zero the nb blocks bnd_blk[] of hv (if hv is given) and the entries of
+// the nvb vertices bnd_vtx[] of vec: the slots that element-once patches
+// add into with global atomics.
+template <typename T>
+hipError_t launch_zero_boundary(const int32_t *bnd_blk, int32_t nb, const int32_t *bnd_vtx,
+                                int32_t nvb, T *hv, T *vec, hipStream_t s);
 
 // Row-owner kernels for two-vertex radial terms (springs, runtime pairs) and
 // vertex terms (inertia): one lane per block row, 64 rows per chunk.

@@ -22,6 +22,12 @@
 //    colours one after another with plain LDS read-add-write (a fixed
 //    summation order); the default mode uses LDS atomics and the same order
 //    keeps lanes of one wave off the same addresses.
+//  * Element-once plans (the page's own decomposition, key designs 3-4:
+//    assembly by atomic scatter-add into the preallocated pattern) keep
+//    each element in one patch only, the one owning its lowest vertex id.
+//    Its contributions to the rows of other patches go to HBM with global
+//    atomics; the plan lists those rows' blocks and vertices so they can be
+//    zeroed before the kernel and added to (not stored) by their owner.
 #include <algorithm>
 #include <climits>
 #include <cstring>
@@ -142,33 +148,39 @@ std::string build_plan(const PlanInput &in, Plan &out)
     for (int32_t p = 0; p < np; ++p)
         for (int32_t v = starts[p]; v < starts[p + 1]; ++v) out.vpatch[v] = p;
 
-    // ---- 2. element -> patch incidence (counting sort by patch)
+    // ---- 2. element -> patch incidence (counting sort by patch): every
+    // patch owning one of the element's vertices, or with element_once the
+    // patch of its lowest vertex id only (patches are ascending id ranges)
+    const bool once = in.element_once != 0;
+    auto patches_of = [&](const int32_t *ev, int m, int32_t *ps) {
+        int cnt = 0;
+        if (once) {
+            int32_t lo = ev[0];
+            for (int i = 1; i < m; ++i) lo = std::min(lo, ev[i]);
+            ps[cnt++] = out.vpatch[lo];
+            return cnt;
+        }
+        for (int i = 0; i < m; ++i) {
+            int32_t p = out.vpatch[ev[i]];
+            bool dup = false;
+            for (int j = 0; j < cnt; ++j) dup |= ps[j] == p;
+            if (!dup) ps[cnt++] = p;
+        }
+        return cnt;
+    };
     auto emit_lists = [&](int32_t ne, int m, const int32_t *ev, std::vector<int32_t> &off,
                           std::vector<int32_t> &lst) {
         off.assign(size_t(np) + 1, 0);
+        int32_t ps[3];
         for (int32_t e = 0; e < ne; ++e) {
-            int32_t ps[3];
-            int cnt = 0;
-            for (int i = 0; i < m; ++i) {
-                int32_t p = out.vpatch[ev[int64_t(e) * m + i]];
-                bool dup = false;
-                for (int j = 0; j < cnt; ++j) dup |= ps[j] == p;
-                if (!dup) ps[cnt++] = p;
-            }
+            const int cnt = patches_of(ev + int64_t(e) * m, m, ps);
             for (int j = 0; j < cnt; ++j) off[ps[j] + 1] += 1;
         }
         for (int32_t p = 0; p < np; ++p) off[p + 1] += off[p];
         lst.assign(off[np], 0);
         std::vector<int32_t> cur(off.begin(), off.end() - 1);
         for (int32_t e = 0; e < ne; ++e) {
-            int32_t ps[3];
-            int cnt = 0;
-            for (int i = 0; i < m; ++i) {
-                int32_t p = out.vpatch[ev[int64_t(e) * m + i]];
-                bool dup = false;
-                for (int j = 0; j < cnt; ++j) dup |= ps[j] == p;
-                if (!dup) ps[cnt++] = p;
-            }
+            const int cnt = patches_of(ev + int64_t(e) * m, m, ps);
             for (int j = 0; j < cnt; ++j) lst[cur[ps[j]]++] = e;
         }
     };
@@ -189,6 +201,20 @@ std::string build_plan(const PlanInput &in, Plan &out)
     out.fac_src.reserve(flst.size());
     std::vector<int> colour;
     std::vector<int32_t> order;
+    if (once) {
+        out.blk_flag.assign(size_t(rp[nv]), 0);
+        out.vtx_flag.assign(size_t(nv), 0);
+        out.spr_gblk.reserve(2 * slst.size());
+        out.fac_gblk.reserve(9 * flst.size());
+    }
+    // global block (a, b), flagged as receiving a foreign contribution
+    auto foreign_blk = [&](int32_t a, int32_t b) -> int32_t {
+        const int32_t pos = find_pos(rp, ci, a, b);
+        if (pos < 0) return -1;
+        out.blk_flag[size_t(rp[a] + pos)] = 1;
+        out.vtx_flag[size_t(a)] = 1;
+        return rp[a] + pos;
+    };
     for (int32_t p = 0; p < np; ++p) {
         PatchHdr &h = out.hdr[p];
         std::memset(&h, 0, sizeof(h));
@@ -203,12 +229,22 @@ std::string build_plan(const PlanInput &in, Plan &out)
             stamp[v] = p;
             local[v] = v - v0;
         }
-        for (int32_t v = v0; v < v1; ++v)
-            for (int32_t k = rp[v]; k < rp[v + 1]; ++k)
-                if (stamp[ci[k]] != p) {
-                    stamp[ci[k]] = p;
-                    rib.push_back(ci[k]);
-                }
+        auto add_rib = [&](int32_t u) {
+            if (stamp[u] != p) {
+                stamp[u] = p;
+                rib.push_back(u);
+            }
+        };
+        if (once) {
+            // the non-owned vertices of the patch's own elements
+            for (int32_t i = soff[p]; i < soff[p + 1]; ++i)
+                for (int j = 0; j < 2; ++j) add_rib(in.springs[2 * int64_t(slst[i]) + j]);
+            for (int32_t i = foff[p]; i < foff[p + 1]; ++i)
+                for (int j = 0; j < 3; ++j) add_rib(in.faces[3 * int64_t(flst[i]) + j]);
+        } else {
+            for (int32_t v = v0; v < v1; ++v)
+                for (int32_t k = rp[v]; k < rp[v + 1]; ++k) add_rib(ci[k]);
+        }
         std::sort(rib.begin(), rib.end());
         for (size_t i = 0; i < rib.size(); ++i) local[rib[i]] = nown + int32_t(i);
         h.rib_off = int32_t(out.rib.size());
@@ -264,6 +300,18 @@ std::string build_plan(const PlanInput &in, Plan &out)
                 rec.blk = uint32_t(sab) | (uint32_t(sba) << 16);
                 out.spr.push_back(rec);
                 out.spr_src.push_back(s);
+                if (once) {
+                    const bool fa = a < v0 || a >= v1, fb = b < v0 || b >= v1;
+                    int32_t g0 = -1, g1 = -1;
+                    if (fa || fb) {
+                        const int32_t f = fa ? a : b, o = fa ? b : a;
+                        g0 = foreign_blk(f, f);
+                        g1 = foreign_blk(f, o);
+                        if (g0 < 0 || g1 < 0) return "spring block missing from pattern";
+                    }
+                    out.spr_gblk.push_back(g0);
+                    out.spr_gblk.push_back(g1);
+                }
             }
             if (n > 0) out.col_bounds.push_back(n);
             else h.nspr_col = 0;
@@ -305,6 +353,14 @@ std::string build_plan(const PlanInput &in, Plan &out)
                         if (t[a] >= v0 && t[a] < v1 && s == kNone)
                             return "face block missing from pattern";
                         rec.blk[3 * a + b] = s;
+                        if (once) {
+                            int32_t gb = -1;
+                            if (t[a] < v0 || t[a] >= v1) {
+                                gb = foreign_blk(t[a], t[b]);
+                                if (gb < 0) return "face block missing from pattern";
+                            }
+                            out.fac_gblk.push_back(gb);
+                        }
                     }
                 }
                 out.fac.push_back(rec);
@@ -319,6 +375,12 @@ std::string build_plan(const PlanInput &in, Plan &out)
         h.lds_hvp = int32_t(lds_hvp_bytes(es, nown, nloc));
         out.lds_eval = std::max(out.lds_eval, h.lds_eval);
         out.lds_hvp = std::max(out.lds_hvp, h.lds_hvp);
+    }
+    if (once) {
+        for (int32_t b = 0; b < rp[nv]; ++b)
+            if (out.blk_flag[size_t(b)]) out.bnd_blk.push_back(b);
+        for (int32_t v = 0; v < nv; ++v)
+            if (out.vtx_flag[size_t(v)]) out.bnd_vtx.push_back(v);
     }
     return "";
 }

@@ -241,6 +241,158 @@ void check_patch_plan(const Mesh &m, bool faces_on, int es, int budget, const ch
         }
 }
 
+// Element-once plan: every element in exactly one patch (the owner of its
+// lowest vertex id), ribbons from the patch's own elements, foreign blocks
+// and flags as the kernels use them.  The kernels' data flow is replayed on
+// the host with one random scalar per element written into every block it
+// touches (and every gradient entry): LDS per patch, global adds for foreign
+// rows into zeroed boundary slots, then the flush (flagged entries added when
+// non-zero, the rest stored).  The result must equal the direct assembly.
+void check_element_once_plan(const Mesh &m, bool faces_on, int es, int budget, const char *tag)
+{
+    std::vector<int32_t> rp, ci;
+    pattern(m, rp, ci);
+    PlanInput in = make_input(m, rp, ci, faces_on, es, budget);
+    in.element_once = 1;
+    Plan plan;
+    const std::string err = build_plan(in, plan);
+    CHECK(err.empty(), "%s: build_plan failed: %s", tag, err.c_str());
+    if (!err.empty()) return;
+    const int32_t nv = m.nv, nnzb = rp[nv], nf = faces_on ? in.nf : 0;
+    CHECK(plan.spr_gblk.size() == 2 * plan.spr.size() && plan.fac_gblk.size() == 9 * plan.fac.size(),
+          "%s: foreign block tables sized", tag);
+    CHECK(int32_t(plan.blk_flag.size()) == nnzb && int32_t(plan.vtx_flag.size()) == nv, "%s: flag sizes", tag);
+    std::mt19937 rng(7);
+    std::uniform_real_distribution<double> U(0.5, 1.5);
+    std::vector<double> ws(in.ns), wf(nf);
+    for (auto &w : ws) w = U(rng);
+    for (auto &w : wf) w = U(rng);
+    // direct assembly
+    std::vector<double> H(nnzb, 0.0), G(nv, 0.0);
+    std::vector<int> foreign_blk(nnzb, 0), foreign_vtx(nv, 0);
+    auto direct = [&](const int32_t *vs, int k, double w) {
+        for (int i = 0; i < k; ++i) {
+            G[vs[i]] += w;
+            for (int j = 0; j < k; ++j) H[slot_of(rp, ci, vs[i], vs[j])] += w;
+        }
+    };
+    for (int32_t s = 0; s < in.ns; ++s) direct(&m.springs[2 * s], 2, ws[s]);
+    for (int32_t f = 0; f < nf; ++f) direct(&m.faces[3 * f], 3, wf[f]);
+    // replay of the kernels
+    std::vector<double> Hk(nnzb, -7.0), Gk(nv, -7.0);  // stale values everywhere
+    for (int32_t b : plan.bnd_blk) Hk[b] = 0.0;
+    for (int32_t v : plan.bnd_vtx) Gk[v] = 0.0;
+    std::vector<int> spr_seen(in.ns, 0), fac_seen(nf, 0);
+    std::vector<double> Hl, Gl;
+    std::vector<std::pair<int32_t, double>> hadd, gadd;  // global adds (any order)
+    for (size_t p = 0; p < plan.hdr.size(); ++p) {
+        const PatchHdr &h = plan.hdr[p];
+        auto owned = [&](int32_t v) { return v >= h.v0 && v < h.v0 + h.nown; };
+        std::vector<int32_t> rib(plan.rib.begin() + h.rib_off, plan.rib.begin() + h.rib_off + h.nrib);
+        std::set<int32_t> rib_expect;
+        auto global_of = [&](int l) { return l < h.nown ? h.v0 + l : rib[size_t(l - h.nown)]; };
+        Hl.assign(h.nblk, 0.0);
+        Gl.assign(h.nown, 0.0);
+        for (int32_t r = 0; r < h.nspr; ++r) {
+            const int32_t s = plan.spr_src[h.spr_off + r];
+            spr_seen[s] += 1;
+            const int32_t a = m.springs[2 * s], b = m.springs[2 * s + 1];
+            CHECK(owned(std::min(a, b)), "%s: spring %d not in its lowest vertex's patch", tag, s);
+            const SpringRec rec = plan.spr[h.spr_off + r];
+            const int la = rec.lab & 0xFFFF, lb = rec.lab >> 16;
+            CHECK(global_of(la) == a && global_of(lb) == b, "%s: spring %d local ids", tag, s);
+            for (int32_t v : {a, b})
+                if (!owned(v)) rib_expect.insert(v);
+            const int32_t *gb = &plan.spr_gblk[2 * size_t(h.spr_off + r)];
+            const double w = ws[s];
+            for (int e = 0; e < 2; ++e) {
+                const int32_t v = e ? b : a, o = e ? a : b;
+                const int l = e ? lb : la;
+                if (owned(v)) {
+                    Gl[l] += w;
+                    Hl[plan.diag_rel[v]] += w;
+                    Hl[(e ? rec.blk >> 16 : rec.blk & 0xFFFF)] += w;
+                } else {
+                    CHECK(gb[0] == slot_of(rp, ci, v, v) && gb[1] == slot_of(rp, ci, v, o),
+                          "%s: spring %d foreign blocks", tag, s);
+                    gadd.push_back({v, w});
+                    hadd.push_back({gb[0], w});
+                    hadd.push_back({gb[1], w});
+                    foreign_blk[gb[0]] = foreign_blk[gb[1]] = foreign_vtx[v] = 1;
+                }
+            }
+            if (owned(a) && owned(b)) CHECK(gb[0] == -1 && gb[1] == -1, "%s: spring %d owned, foreign blocks set", tag, s);
+        }
+        for (int32_t r = 0; r < h.nfac; ++r) {
+            const int32_t f = plan.fac_src[h.fac_off + r];
+            fac_seen[f] += 1;
+            const int32_t *t = &m.faces[3 * f];
+            CHECK(owned(std::min({t[0], t[1], t[2]})), "%s: face %d not in its lowest vertex's patch", tag, f);
+            const FaceRec &rec = plan.fac[h.fac_off + r];
+            const int32_t *gb = &plan.fac_gblk[9 * size_t(h.fac_off + r)];
+            for (int i = 0; i < 3; ++i) {
+                CHECK(global_of(rec.l[i]) == t[i], "%s: face %d local id", tag, f);
+                if (!owned(t[i])) rib_expect.insert(t[i]);
+                if (owned(t[i])) Gl[rec.l[i]] += wf[f];
+                else {
+                    gadd.push_back({t[i], wf[f]});
+                    foreign_vtx[t[i]] = 1;
+                }
+                for (int j = 0; j < 3; ++j) {
+                    if (owned(t[i])) {
+                        CHECK(gb[3 * i + j] == -1, "%s: face %d owned row with a foreign block", tag, f);
+                        Hl[rec.blk[3 * i + j]] += wf[f];
+                    } else {
+                        CHECK(gb[3 * i + j] == slot_of(rp, ci, t[i], t[j]), "%s: face %d foreign block", tag, f);
+                        hadd.push_back({gb[3 * i + j], wf[f]});
+                        foreign_blk[gb[3 * i + j]] = 1;
+                    }
+                }
+            }
+        }
+        CHECK(std::vector<int32_t>(rib_expect.begin(), rib_expect.end()) == rib, "%s: patch %zu ribbon", tag, p);
+        CHECK(h.lds_eval <= budget && 2 * h.amap_cap >= h.nblk + h.nown, "%s: patch %zu LDS", tag, p);
+        // flush of the owned slice
+        for (int32_t i = 0; i < h.nblk; ++i) {
+            const int32_t b = h.blk0 + i;
+            if (plan.blk_flag[b]) {
+                if (Hl[i] != 0.0) hadd.push_back({b, Hl[i]});
+            } else {
+                Hk[b] = Hl[i];
+            }
+        }
+        for (int32_t i = 0; i < h.nown; ++i) {
+            const int32_t v = h.v0 + i;
+            if (plan.vtx_flag[v]) {
+                if (Gl[i] != 0.0) gadd.push_back({v, Gl[i]});
+            } else {
+                Gk[v] = Gl[i];
+            }
+        }
+    }
+    for (auto &a : hadd) Hk[a.first] += a.second;
+    for (auto &a : gadd) Gk[a.first] += a.second;
+    for (int32_t s = 0; s < in.ns; ++s) CHECK(spr_seen[s] == 1, "%s: spring %d in %d patches", tag, s, spr_seen[s]);
+    for (int32_t f = 0; f < nf; ++f) CHECK(fac_seen[f] == 1, "%s: face %d in %d patches", tag, f, fac_seen[f]);
+    int nbad_flag = 0, nbad_val = 0;
+    for (int32_t b = 0; b < nnzb; ++b) {
+        nbad_flag += int(plan.blk_flag[b]) != foreign_blk[b];
+        nbad_val += std::abs(Hk[b] - H[b]) > 1e-12 * (1.0 + std::abs(H[b]));
+    }
+    for (int32_t v = 0; v < nv; ++v) {
+        nbad_flag += int(plan.vtx_flag[v]) != foreign_vtx[v];
+        nbad_val += std::abs(Gk[v] - G[v]) > 1e-12 * (1.0 + std::abs(G[v]));
+    }
+    CHECK(nbad_flag == 0, "%s: %d boundary flags differ from the foreign writes", tag, nbad_flag);
+    CHECK(nbad_val == 0, "%s: %d replayed values differ from the direct assembly", tag, nbad_val);
+    std::vector<int32_t> bb, bv;
+    for (int32_t b = 0; b < nnzb; ++b)
+        if (foreign_blk[b]) bb.push_back(b);
+    for (int32_t v = 0; v < nv; ++v)
+        if (foreign_vtx[v]) bv.push_back(v);
+    CHECK(bb == plan.bnd_blk && bv == plan.bnd_vtx, "%s: boundary lists", tag);
+}
+
 bool has_spring(const Mesh &m, int32_t a, int32_t b)
 {
     for (size_t s = 0; s * 2 < m.springs.size(); ++s)
@@ -469,6 +621,11 @@ int main()
     check_patch_plan(g64, true, 4, 40 * 1024, "grid64 faces");
     check_patch_plan(r1, true, 8, 8192, "random300 faces");
     check_patch_plan(r2, true, 4, 16384, "random2000 faces");
+    check_element_once_plan(g10, false, 8, 40 * 1024, "grid10 element-once");
+    check_element_once_plan(g37, true, 4, 6144, "grid37 faces element-once small patches");
+    check_element_once_plan(g64, true, 4, 40 * 1024, "grid64 faces element-once");
+    check_element_once_plan(r1, true, 8, 8192, "random300 faces element-once");
+    check_element_once_plan(r2, true, 4, 16384, "random2000 faces element-once");
     check_row_plan(g10, false, "grid10 rows");
     check_row_plan(g64, true, "grid64 rows faces");
     check_row_plan(r1, true, "random300 rows faces");

@@ -68,6 +68,10 @@ def tri_desc(**kw):
     (lambda d: setattr(d, "eval_path", 9), "eval_path"),
     (lambda d: setattr(d, "patch_lds_bytes", 1 << 20), "patch_lds_bytes"),
     (lambda d: setattr(d, "ns", -2), "ns"),
+    (lambda d: (setattr(d, "eval_path", binding.LAD_PATH_PATCH_ATOMIC),
+                setattr(d, "deterministic", 1)), "LAD_PATH_PATCH_ATOMIC"),
+    (lambda d: (setattr(d, "eval_path", binding.LAD_PATH_PATCH_ATOMIC),
+                setattr(d, "pair_capacity", 4), setattr(d, "dhat", 0.1)), "LAD_PATH_PATCH_ATOMIC"),
 ])
 def test_bad_descriptor_fields(L, mutate, msg):
     d, keep = tri_desc()
