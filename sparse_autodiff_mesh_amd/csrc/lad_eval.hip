@@ -653,9 +653,21 @@ k_pairs(const DevState *__restrict__ st, PatternBufs pat, const T *__restrict__ 
 __global__ void __launch_bounds__(kThreads)
 k_energy_reduce(const double *__restrict__ parts, int32_t n, double *__restrict__ out)
 {
+    // thread t adds parts t, t + kThreads, ... in that order; the loads of
+    // a round go out together (indices clamped, extras dropped), so a few
+    // thousand partials cost one or two memory round trips
+    constexpr int kRound = 8;
     __shared__ double red[kWaves];
     double s = 0.0;
-    for (int32_t i = threadIdx.x; i < n; i += kThreads) s += parts[i];
+    for (int32_t base = 0; base < n; base += kThreads * kRound) {
+        double v[kRound];
+#pragma unroll
+        for (int j = 0; j < kRound; ++j)
+            v[j] = parts[min(base + j * kThreads + int32_t(threadIdx.x), n - 1)];
+#pragma unroll
+        for (int j = 0; j < kRound; ++j)
+            if (base + j * kThreads + int32_t(threadIdx.x) < n) s += v[j];
+    }
     const double tot = block_sum<kThreads>(s, red);
     if (threadIdx.x == 0) *out = tot;
 }

@@ -189,6 +189,10 @@ struct RowPlan {
     std::vector<int32_t> sl_ptr;     // [nslice + 1]
     std::vector<int32_t> sl_nb;      // neighbour vertex
     std::vector<double> sl_rest;     // rest length
+    // The same neighbours as 16-bit differences from the entry's row
+    // (clamped to the last row past it): filled when every difference fits,
+    // which halves the neighbour bytes the kernels stream; else empty.
+    std::vector<int16_t> sl_d16;
 };
 
 // Returns "" when the row path applies (rest lengths >= 0, at most one
@@ -299,7 +303,8 @@ struct RowArgs {
     const T *slot_rest;          // [nnzb_base] rest length of the spring behind
                                  // each block (< 0: no spring)
     const int32_t *sl_ptr;       // spring slices (RowPlan): entry offsets,
-    const int32_t *sl_nb;        // neighbour vertices
+    const int32_t *sl_nb;        // neighbour vertices (null when sl_d16 is set)
+    const int16_t *sl_d16;       // or their differences from the row
     const T *sl_rest;            // and rest lengths (< 0: padding)
     const T *x_tilde;            // null = no inertia
     const int32_t *fptr;         // [nv+1] offsets of each row's faces (faces on)

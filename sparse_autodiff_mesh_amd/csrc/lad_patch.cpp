@@ -439,6 +439,25 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
                 for (; j < w; ++j) out.sl_nb[size_t(e0 + kSliceRows * j)] = a < nv ? int32_t(a) : nv - 1;
             }
         }
+        // 16-bit differences from the (clamped) row, when all fit
+        bool narrow = true;
+        for (int64_t t = 0; t < nsl && narrow; ++t)
+            for (int64_t e = out.sl_ptr[size_t(t)]; e < out.sl_ptr[size_t(t) + 1]; ++e) {
+                const int64_t a = std::min<int64_t>(t * kSliceRows + (e - out.sl_ptr[size_t(t)]) % kSliceRows, nv - 1);
+                const int64_t d = int64_t(out.sl_nb[size_t(e)]) - a;
+                if (d < INT16_MIN || d > INT16_MAX) {
+                    narrow = false;
+                    break;
+                }
+            }
+        if (narrow) {
+            out.sl_d16.resize(size_t(tot));
+            for (int64_t t = 0; t < nsl; ++t)
+                for (int64_t e = out.sl_ptr[size_t(t)]; e < out.sl_ptr[size_t(t) + 1]; ++e) {
+                    const int64_t a = std::min<int64_t>(t * kSliceRows + (e - out.sl_ptr[size_t(t)]) % kSliceRows, nv - 1);
+                    out.sl_d16[size_t(e)] = int16_t(int64_t(out.sl_nb[size_t(e)]) - a);
+                }
+        }
     }
     if (in.face_energy && in.nf > 0) {
         // per-row incidence, rows in vertex order, faces by id within a row

@@ -599,6 +599,27 @@ __device__ __forceinline__ void row_slots(const RowArgs<T> &A, int act, const in
 // columns below it.  The same blocks, in the same order, as row_slots.
 constexpr int kDenseBatch = 6;  // springs whose loads a lane issues together
 
+// Neighbour vertices of N spring slice entries e[j] of row a (clamped to
+// the last row): from their 16-bit differences when the slices store those,
+// else the stored vertex ids.  The test is uniform over the launch and taken
+// once for all N loads, which are issued before any of them is used.
+template <int N, typename T>
+__device__ __forceinline__ void slice_nbs(const RowArgs<T> &A, const int64_t (&e)[N], int32_t a,
+                                          int32_t (&nb)[N])
+{
+    int32_t raw[N];
+    const bool d16 = A.sl_d16 != nullptr;
+    if (d16) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) raw[j] = A.sl_d16[e[j]];
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) raw[j] = A.sl_nb[e[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) nb[j] = d16 ? a + raw[j] : raw[j];
+}
+
 template <typename T, bool SHIFT>
 __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t, int lane,
                                                   const Row<T> &r, const int32_t ins[kMaxIns],
@@ -611,12 +632,13 @@ __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t
     for (int32_t j0 = 0; j0 < ns; j0 += kDenseBatch) {
         int32_t nb[kDenseBatch];
         T L[kDenseBatch], xb[kDenseBatch][3];
+        int64_t e[kDenseBatch];
 #pragma unroll
-        for (int j = 0; j < kDenseBatch; ++j) {
-            const int64_t e = p + int64_t(min(j0 + j, ns - 1)) * kSliceRows + lane;
-            nb[j] = A.sl_nb[e];
-            L[j] = j0 + j < ns ? A.sl_rest[e] : T(-1);
-        }
+        for (int j = 0; j < kDenseBatch; ++j)
+            e[j] = p + int64_t(min(j0 + j, ns - 1)) * kSliceRows + lane;
+        slice_nbs(A, e, r.a, nb);
+#pragma unroll
+        for (int j = 0; j < kDenseBatch; ++j) L[j] = j0 + j < ns ? A.sl_rest[e[j]] : T(-1);
 #pragma unroll
         for (int j = 0; j < kDenseBatch; ++j)
 #pragma unroll
@@ -996,9 +1018,22 @@ __device__ __forceinline__ void slice_head(const RowArgs<T> &A, int32_t t, int l
     for (int j = 0; j < kSliceBatch; ++j) {
         h.nb[j] = a;
         h.L[j] = T(-1);
-        if (!FACES && j < ns) {  // wave-uniform; with faces the registers go to them
-            h.nb[j] = A.sl_nb[p + j * kSliceRows + lane];
-            h.L[j] = A.sl_rest[p + j * kSliceRows + lane];
+    }
+    if (!FACES && ns > 0) {  // wave-uniform; with faces the registers go to them
+        // entries past the widest row's springs re-read its last one and
+        // are dropped
+        int64_t e[kSliceBatch];
+        int32_t nb[kSliceBatch];
+#pragma unroll
+        for (int j = 0; j < kSliceBatch; ++j) e[j] = p + int64_t(min(j, ns - 1)) * kSliceRows + lane;
+        slice_nbs(A, e, a, nb);
+#pragma unroll
+        for (int j = 0; j < kSliceBatch; ++j) {
+            const T L = A.sl_rest[e[j]];
+            if (j < ns) {
+                h.nb[j] = nb[j];
+                h.L[j] = L;
+            }
         }
     }
     h.f0 = FACES ? A.fptr[a] : 0;
@@ -1013,19 +1048,27 @@ __device__ __forceinline__ void slice_batch(const RowArgs<T> &A, const SliceRow<
                                             int32_t ns, int32_t j0, int lane, int32_t self,
                                             int32_t nb[kSliceBatch], T L[kSliceBatch])
 {
+    if (!FACES && j0 == 0) {
 #pragma unroll
-    for (int j = 0; j < kSliceBatch; ++j) {
-        if (!FACES && j0 == 0) {
+        for (int j = 0; j < kSliceBatch; ++j) {
             nb[j] = h.nb[j];
             L[j] = h.L[j];
-        } else {
-            nb[j] = self;
-            L[j] = T(-1);
-            if (j0 + j < ns) {
-                nb[j] = A.sl_nb[p + (j0 + j) * kSliceRows + lane];
-                L[j] = A.sl_rest[p + (j0 + j) * kSliceRows + lane];
-            }
         }
+        return;
+    }
+    // j0 < ns: entries past the widest row's springs re-read its last one
+    // and are dropped
+    int64_t e[kSliceBatch];
+    int32_t nbv[kSliceBatch];
+#pragma unroll
+    for (int j = 0; j < kSliceBatch; ++j) e[j] = p + int64_t(min(j0 + j, ns - 1)) * kSliceRows + lane;
+    slice_nbs(A, e, self, nbv);
+#pragma unroll
+    for (int j = 0; j < kSliceBatch; ++j) {
+        const T Lj = A.sl_rest[e[j]];
+        const bool in = j0 + j < ns;
+        nb[j] = in ? nbv[j] : self;
+        L[j] = in ? Lj : T(-1);
     }
 }
 

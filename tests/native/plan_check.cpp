@@ -465,6 +465,18 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
             }
         }
     }
+    // 16-bit neighbour differences: present exactly when every one fits
+    bool fit = true;
+    for (int32_t t = 0; t < nsl; ++t)
+        for (int32_t e = plan.sl_ptr[t]; e < plan.sl_ptr[t + 1]; ++e) {
+            const int64_t a = std::min(t * kSliceRows + (e - plan.sl_ptr[t]) % kSliceRows, m.nv - 1);
+            const int64_t d = int64_t(plan.sl_nb[size_t(e)]) - a;
+            fit = fit && d >= INT16_MIN && d <= INT16_MAX;
+            if (!plan.sl_d16.empty() && size_t(e) < plan.sl_d16.size())
+                CHECK(a + plan.sl_d16[size_t(e)] == plan.sl_nb[size_t(e)], "%s: entry %d difference", tag, e);
+        }
+    CHECK(fit == (plan.sl_d16.size() == plan.sl_nb.size()) && (fit || plan.sl_d16.empty()),
+          "%s: 16-bit differences present %d, fit %d", tag, int(!plan.sl_d16.empty()), int(fit));
     if (!faces_on) return;
     CHECK(int32_t(plan.fptr.size()) == m.nv + 1, "%s: face offsets size", tag);
     std::vector<std::vector<int32_t>> inc(m.nv);
@@ -627,6 +639,34 @@ int main()
     check_element_once_plan(r1, true, 8, 8192, "random300 faces element-once");
     check_element_once_plan(r2, true, 4, 16384, "random2000 faces element-once");
     check_row_plan(g10, false, "grid10 rows");
+    {
+        // a chain of 40,000 vertices with one spring across it: differences
+        // beyond 16 bits, so the slices keep full vertex ids
+        Mesh chain;
+        chain.nv = 40000;
+        for (int32_t v = 0; v + 1 < chain.nv; ++v) {
+            chain.springs.push_back(v);
+            chain.springs.push_back(v + 1);
+            chain.rest.push_back(1.0);
+        }
+        chain.springs.push_back(3);
+        chain.springs.push_back(39990);
+        chain.rest.push_back(2.0);
+        auto narrow = [&](const Mesh &mm) {
+            std::vector<int32_t> rp, ci;
+            pattern(mm, rp, ci);
+            RowPlan rplan;
+            const std::string err = build_row_plan(make_input(mm, rp, ci, false, 4, 0), mm.rest.data(), rplan);
+            CHECK(err.empty(), "chain: %s", err.c_str());
+            return !rplan.sl_d16.empty();
+        };
+        check_row_plan(chain, false, "chain40000 rows wide");
+        CHECK(!narrow(chain), "chain40000 with a long spring: 16-bit differences kept");
+        chain.springs.resize(chain.springs.size() - 2);
+        chain.rest.pop_back();
+        check_row_plan(chain, false, "chain40000 rows narrow");
+        CHECK(narrow(chain), "chain40000: no 16-bit differences");
+    }
     check_row_plan(g64, true, "grid64 rows faces");
     check_row_plan(r1, true, "random300 rows faces");
     check_row_plan(r2, false, "random2000 rows");

@@ -89,6 +89,31 @@ def test_rows_bitwise_reproducible(lad):
     L.close()
 
 
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_rows_energy_over_changing_inputs(lad, dtype):
+    """Consecutive calls on different positions, with a call that skips the
+    energy in between, each give the oracle's energy (no partial energy of
+    an earlier call is summed), and no device error is latched."""
+    import torch
+    log_case(test="rows_energy_changing", dtype=dtype)
+    m = inputs.cloth(70)
+    L = lad.Lad(m.nv, dtype=dtype, **lad.mesh_terms(m))
+    prob = oracle.problem_from_mesh(m, f32=(dtype == "f32"))
+    orp, oci = oracle.pattern(prob)
+    out = L.alloc_outputs()
+    for k in range(4):
+        x_h = host_input(m.x + 0.01 * k * m.h * np.sin(np.arange(3 * m.nv)).reshape(m.nv, 3), dtype)
+        x = dev(x_h, dtype)
+        if k == 2:
+            L.eval(x, out=out, energy=False)
+        E, g, H = L.eval(x, out=out)
+        torch.cuda.synchronize()
+        Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+        assert rel([E.item()], [Eo]) <= TOL[dtype], (k, E.item(), Eo)
+    assert L.device_status() == 0
+    L.close()
+
+
 def test_springs_only_and_inertia_only_rows(lad):
     log_case(test="rows_single_terms")
     m = inputs.cloth(20)
