@@ -371,7 +371,7 @@ def bench_pairs_only(torch, binding, inputs, args, timer):
     L.close()
     return {"workload": f"mass-spring cloth {args.n}x{args.n} + {P} contact pairs per step, "
                         "fp32: insert, then gradient + block-CSR Hessian",
-            "kernels": ["k_ins_count", "k_ins_bucket", "k_ins_tiles",
+            "kernels": ["k_ins_count", "k_ins_tiles",
                         "k_eval_rows<float, false, true>", "k_eval_pair_rows<float, false>"],
             "steps": args.steps, "warmup": args.warmup,
             "step_ms_median": round(r["median_ms"], 5),

@@ -629,6 +629,7 @@ __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t
     const int32_t p = A.sl_ptr[t];
     const int32_t ns = (A.sl_ptr[t + 1] - p) / kSliceRows;  // wave-uniform
     int32_t below = 0;
+    int32_t ins_below[kMaxIns] = {};  // SHIFT: topology columns below each inserted one
     for (int32_t j0 = 0; j0 < ns; j0 += kDenseBatch) {
         int32_t nb[kDenseBatch];
         T L[kDenseBatch], xb[kDenseBatch][3];
@@ -649,7 +650,11 @@ __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t
             const bool above = nb[j] > r.a;
             below += above ? 0 : 1;
             int32_t sl = r.s0 + j0 + j + (above ? 1 : 0);
-            if constexpr (SHIFT) sl += shift_of(ins, nb[j]);
+            if constexpr (SHIFT) {
+                sl += shift_of(ins, nb[j]);
+#pragma unroll
+                for (int m = 0; m < kMaxIns; ++m) ins_below[m] += nb[j] < ins[m] ? 1 : 0;
+            }
             T *B = Hs + 9 * (sl - sb);
             Dual2<T, 3> d[3];
 #pragma unroll
@@ -669,7 +674,21 @@ __device__ __forceinline__ void row_slice_springs(const RowArgs<T> &A, int32_t t
         }
     }
     acc.dslot = r.s0 + below;
-    if constexpr (SHIFT) acc.dslot += shift_of(ins, r.a);
+    if constexpr (SHIFT) {
+        acc.dslot += shift_of(ins, r.a);
+        // the inserted columns' blocks get contact terms only (added by
+        // k_eval_pair_rows): zero them.  An inserted column follows the
+        // inserted columns and the topology columns (the diagonal, the
+        // springs) below it.
+#pragma unroll
+        for (int m = 0; m < kMaxIns; ++m)
+            if (ins[m] != INT32_MAX) {
+                const int32_t sl = r.s0 + shift_of(ins, ins[m]) + ins_below[m] + (r.a < ins[m] ? 1 : 0);
+                T *B = Hs + 9 * (sl - sb);
+#pragma unroll
+                for (int i = 0; i < 9; ++i) B[i] = T(0);
+            }
+    }
 }
 
 template <typename T>
@@ -897,8 +916,9 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
                 rt.s1 = r.s0 + (r.kb1 - r.kb0);  // topology slots, in order
                 rt.p0 = rt.p1 = 0;
                 // the blocks of inserted columns get contact terms only
-                // (k_eval_pair_rows adds them): zero the row first
-                if (r.nn > 0)
+                // (k_eval_pair_rows adds them): zero the row first (the
+                // spring-slice path zeroes just those blocks itself)
+                if (r.nn > 0 && !(A.springs_on && dense_t >= 0))
                     for (int32_t i = 9 * (r.s0 - sb); i < 9 * (r.s1 - sb); ++i) Hs[i] = T(0);
             }
             PairPre<T> pp;
