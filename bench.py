@@ -573,21 +573,21 @@ def bench_secondary(torch, binding, inputs, args, timer):
 def bench_patch_path(torch, binding, inputs, args, timer, steps, warm):
     """The element-owner patch path on the headline cloth and the face grid,
     for comparison with the row path: LDS patches with ghost vertices, the
-    owned rows accumulated in LDS with LDS atomics (cloth1000_patch), in
-    colour phases (_patch_det), or with each element evaluated once and its
-    blocks in other patches' rows added by global float atomics into slots
-    zeroed by a small launch first (_patch_atomic: the pages' own assembly).
-    Times are whole calls (the zeroing launch included)."""
+    owned rows accumulated in LDS in colour phases (cloth1000_patch, the
+    default assembly), with LDS atomics (_patch_lds_atomic), or with each
+    element evaluated once and its blocks in other patches' rows added by
+    global float atomics into slots zeroed by a small launch first
+    (_patch_atomic: the pages' own assembly).  Times are whole calls (the
+    zeroing launch included)."""
     sec = {}
     m = inputs.cloth(args.n)
     x = to_dev(torch, m.x, "f32")
     v = to_dev(torch, inputs.hvp_direction(m.nv), "f32")
     y = torch.empty_like(v)
-    for path, det, tag in (("patch", False, "cloth1000_patch"),
-                           ("patch", True, "cloth1000_patch_det"),
-                           ("patch_atomic", False, "cloth1000_patch_atomic")):
-        L = binding.Lad(m.nv, dtype="f32", path=path, deterministic=det,
-                        **binding.mesh_terms(m))
+    for path, tag in (("patch", "cloth1000_patch"),
+                      ("patch_lds_atomic", "cloth1000_patch_lds_atomic"),
+                      ("patch_atomic", "cloth1000_patch_atomic")):
+        L = binding.Lad(m.nv, dtype="f32", path=path, **binding.mesh_terms(m))
         out = L.alloc_outputs()
         r = timer.run(lambda: L.eval(x, out=out, energy=False), steps, warm)
         info = L.get_info()
@@ -597,13 +597,13 @@ def bench_patch_path(torch, binding, inputs, args, timer, steps, warm):
             compulsory_bytes_eval(m.nv, m.springs.shape[0], 0, nnzb, 4) /
             (r["median_ms"] * 1e-3) / 1e9, 1)
         sec[tag + "_spring_records"] = info["spring_records"]
-        if not det:
-            rh = timer.run(lambda: L.hvp(x, v, out=y), steps, warm)
-            sec[tag + "_hvp_ms"] = round(rh["median_ms"], 5)
+        rh = timer.run(lambda: L.hvp(x, v, out=y), steps, warm)
+        sec[tag + "_hvp_ms"] = round(rh["median_ms"], 5)
         L.close()
     f = inputs.face_grid(512)
     xf = to_dev(torch, f.x, "f32")
-    for path, tag in (("patch", "faces512_patch"), ("patch_atomic", "faces512_patch_atomic")):
+    for path, tag in (("patch", "faces512_patch"), ("patch_lds_atomic", "faces512_patch_lds_atomic"),
+                      ("patch_atomic", "faces512_patch_atomic")):
         L = binding.Lad(f.nv, dtype="f32", path=path,
                         **binding.mesh_terms(f, springs=False, inertia=False, faces=True))
         out = L.alloc_outputs()
@@ -707,10 +707,12 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--flush-mall", action="store_true",
                     help="write a 512 MB scratch buffer before every timed call")
-    ap.add_argument("--path", default="auto", choices=["auto", "rows", "patch", "patch_atomic"],
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "rows", "patch", "patch_atomic", "patch_lds_atomic"],
                     help="decomposition of the headline evaluation (auto picks rows)")
     ap.add_argument("--deterministic", action="store_true",
-                    help="patch path: colour phases instead of LDS atomics")
+                    help="ask the library for bitwise reproducible results (the atomic "
+                         "patch assemblies reject it)")
     ap.add_argument("--patch-lds", type=int, default=0,
                     help="LDS bytes per patch (0 = library default)")
     ap.add_argument("--hvp-only", action="store_true",
@@ -792,8 +794,8 @@ def main():
                         "springs k=1e3 + inertia m/dt^2=100, gradient + block-CSR Hessian",
             "vertices": res["nv"], "springs": res["ns"], "terms": res["terms"],
             "nnzb": res["nnzb"], "chunks_or_patches": res["info"]["npatches"],
-            "eval_path": {1: "patch", 2: "rows", 3: "patch_atomic"}.get(res["info"]["eval_path"],
-                                                                         "?"),
+            "eval_path": {1: "patch", 2: "rows", 3: "patch_atomic",
+                          4: "patch_lds_atomic"}.get(res["info"]["eval_path"], "?"),
             "workgroups": res["info"]["grid_eval"],
             "parallelism": "single GPU",
         },
@@ -804,10 +806,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": ("k_eval_rows<float>" if res["info"]["eval_path"] == 2
-                       else "k_zero_boundary<float> + k_eval_patch<float, 2>"
-                       if res["info"]["eval_path"] == 3
-                       else f"k_eval_patch<float, {1 if args.deterministic else 0}>"),
+            "kernel": {2: "k_eval_rows<float>",
+                       3: "k_zero_boundary<float> + k_eval_patch<float, 2>",
+                       4: "k_eval_patch<float, 0>"}.get(res["info"]["eval_path"],
+                                                        "k_eval_patch<float, 1>"),
             "kernel_ms_mean": round(kern_ms, 5),
             "kernel_ms_median": round(tk["median_ms"], 5),
             "call_ms_mean_with_energy": round(t["mean_ms"], 5),

@@ -79,8 +79,9 @@ typedef struct {
     const int32_t *faces;       /* [nf][3] vertex ids (counter-clockwise)      */
 
     lad_dtype dtype;            /* arithmetic and storage type of x, g, H, v, y */
-    int32_t deterministic;      /* 1: fixed-order (colour-phased) assembly,     */
-                                /*    bitwise reproducible run to run           */
+    int32_t deterministic;      /* 1: bitwise reproducible run to run required */
+                                /*    (every path but the two atomic patch      */
+                                /*    assemblies is; those reject it)           */
     int32_t patch_lds_bytes;    /* LDS budget per patch; 0 = library default    */
     int32_t pair_capacity;      /* max pairs per lad_insert_pairs, >= 0         */
 
@@ -100,8 +101,9 @@ typedef struct {
     double kappa;               /* pair barrier stiffness                      */
     double dhat;                /* pair barrier support, > 0 if pair_capacity>0 */
 
-    int32_t eval_path;          /* LAD_PATH_AUTO, LAD_PATH_PATCH, LAD_PATH_ROWS
-                                   or LAD_PATH_PATCH_ATOMIC                   */
+    int32_t eval_path;          /* LAD_PATH_AUTO, LAD_PATH_PATCH, LAD_PATH_ROWS,
+                                   LAD_PATH_PATCH_ATOMIC or
+                                   LAD_PATH_PATCH_LDS_ATOMIC                  */
     int32_t vf_capacity;        /* max vertex-face contacts per
                                    lad_insert_contacts, >= 0; > 0 needs faces
                                    (nf > 0) and the row path                  */
@@ -111,7 +113,10 @@ typedef struct {
  *  LAD_PATH_PATCH  element owner: one workgroup per patch of contiguous rows;
  *                  every element touching an owned row is evaluated once per
  *                  such patch and scattered into the patch's rows, which are
- *                  accumulated in LDS and streamed out.  Any mix of terms.
+ *                  accumulated in LDS and streamed out.  The scatter runs in
+ *                  colour phases (no two elements of a phase share an owned
+ *                  vertex): plain LDS adds in a fixed order, bitwise
+ *                  reproducible.  Any mix of terms.
  *  LAD_PATH_ROWS   row owner: one lane per block row evaluates every term of
  *                  that row; each block is written once, in a fixed order,
  *                  without atomics.  Requires rest lengths >= 0, at most one
@@ -127,8 +132,18 @@ typedef struct {
  *                  Computations", key designs 3 and 4: atomic scatter-add
  *                  into the preallocated pattern).  Results vary in the last
  *                  bits from run to run.  Takes no deterministic mode and no
- *                  contact capacity (LAD_ERR_ARG otherwise).  */
-enum { LAD_PATH_AUTO = 0, LAD_PATH_PATCH = 1, LAD_PATH_ROWS = 2, LAD_PATH_PATCH_ATOMIC = 3 };
+ *                  contact capacity (LAD_ERR_ARG otherwise).
+ *  LAD_PATH_PATCH_LDS_ATOMIC  LAD_PATH_PATCH with the scatter into LDS done
+ *                  by LDS float atomics instead of colour phases (the page's
+ *                  patch-local accumulation, key design 3); results vary in
+ *                  the last bits.  Takes no deterministic mode.  */
+enum {
+    LAD_PATH_AUTO = 0,
+    LAD_PATH_PATCH = 1,
+    LAD_PATH_ROWS = 2,
+    LAD_PATH_PATCH_ATOMIC = 3,
+    LAD_PATH_PATCH_LDS_ATOMIC = 4
+};
 
 /* Summary of a context (lad_get_info synchronises the context's stream to
  * read the device-side active pattern size). */
@@ -144,7 +159,7 @@ typedef struct {
     int32_t lds_bytes_hvp;
     int64_t spring_records;     /* element records incl. patch-boundary copies */
     int64_t face_records;
-    int32_t max_colors;         /* colour phases of the deterministic mode     */
+    int32_t max_colors;         /* colour phases of the patch path's assembly  */
     int32_t active_buffer;      /* 0 = topology pattern, 1/2 = pair buffers    */
     int32_t eval_path;          /* LAD_PATH_PATCH or LAD_PATH_ROWS in use      */
     int32_t grid_eval;          /* workgroups of one evaluation launch         */

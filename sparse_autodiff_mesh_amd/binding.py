@@ -31,8 +31,9 @@ LAD_PATH_AUTO = 0
 LAD_PATH_PATCH = 1
 LAD_PATH_ROWS = 2
 LAD_PATH_PATCH_ATOMIC = 3
+LAD_PATH_PATCH_LDS_ATOMIC = 4
 _PATHS = {"auto": LAD_PATH_AUTO, "patch": LAD_PATH_PATCH, "rows": LAD_PATH_ROWS,
-          "patch_atomic": LAD_PATH_PATCH_ATOMIC}
+          "patch_atomic": LAD_PATH_PATCH_ATOMIC, "patch_lds_atomic": LAD_PATH_PATCH_LDS_ATOMIC}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _f64p = ctypes.POINTER(ctypes.c_double)

@@ -23,7 +23,6 @@ struct lad_ctx {
     int32_t nv = 0;
     lad_dtype dtype = LAD_F32;
     int32_t es = 4;
-    int32_t det = 0;
     int32_t mode = kModeLdsAtomic;   // PatchMode of the patch kernels
     hipStream_t stream = nullptr;
     int64_t nnzb_base = 0, hcap = 0;
@@ -148,15 +147,19 @@ std::string check_desc(const lad_mesh_desc *d)
         return "pair_capacity + vf_capacity must be at most " +
                std::to_string(int64_t(kInsMaxWg) * kThreads);
     if (d->vf_capacity > 0 && d->nf == 0) return "vertex-face contacts need faces";
-    if (d->vf_capacity > 0 && d->eval_path == LAD_PATH_PATCH)
+    if (d->vf_capacity > 0 && (d->eval_path == LAD_PATH_PATCH ||
+                               d->eval_path == LAD_PATH_PATCH_LDS_ATOMIC))
         return "vertex-face contacts need the row path";
     if (d->eval_path != LAD_PATH_AUTO && d->eval_path != LAD_PATH_PATCH &&
-        d->eval_path != LAD_PATH_ROWS && d->eval_path != LAD_PATH_PATCH_ATOMIC)
-        return "eval_path must be LAD_PATH_AUTO, LAD_PATH_PATCH, LAD_PATH_ROWS or "
-               "LAD_PATH_PATCH_ATOMIC";
+        d->eval_path != LAD_PATH_ROWS && d->eval_path != LAD_PATH_PATCH_ATOMIC &&
+        d->eval_path != LAD_PATH_PATCH_LDS_ATOMIC)
+        return "eval_path must be LAD_PATH_AUTO, LAD_PATH_PATCH, LAD_PATH_ROWS, "
+               "LAD_PATH_PATCH_ATOMIC or LAD_PATH_PATCH_LDS_ATOMIC";
     if (d->eval_path == LAD_PATH_PATCH_ATOMIC &&
         (d->deterministic || d->pair_capacity > 0 || d->vf_capacity > 0))
         return "LAD_PATH_PATCH_ATOMIC takes no deterministic mode and no contact capacity";
+    if (d->eval_path == LAD_PATH_PATCH_LDS_ATOMIC && d->deterministic)
+        return "LAD_PATH_PATCH_LDS_ATOMIC takes no deterministic mode";
     if (d->patch_lds_bytes < 0 || d->patch_lds_bytes > kMaxPatchLds)
         return "patch_lds_bytes must be in [0, " + std::to_string(kMaxPatchLds) + "]";
     if (d->nf > 0 && !d->faces) return "faces is NULL";
@@ -557,10 +560,11 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     ctx->nv = nv;
     ctx->dtype = d->dtype;
     ctx->es = d->dtype == LAD_F64 ? 8 : 4;
-    ctx->det = d->deterministic ? 1 : 0;
-    ctx->mode = d->deterministic                          ? kModeColour
-                : d->eval_path == LAD_PATH_PATCH_ATOMIC ? kModeBoundaryAtomic
-                                                          : kModeLdsAtomic;
+    // the patch path's assembly: colour phases unless an atomic one is asked
+    // for (on gfx950 they are several times faster than LDS float atomics)
+    ctx->mode = d->eval_path == LAD_PATH_PATCH_ATOMIC       ? kModeBoundaryAtomic
+                : d->eval_path == LAD_PATH_PATCH_LDS_ATOMIC ? kModeLdsAtomic
+                                                            : kModeColour;
     ctx->stream = s;
     ctx->pair_cap = d->pair_capacity;
     ctx->vf_cap = d->vf_capacity;
@@ -659,7 +663,7 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     Plan plan;
     RowPlan rplan;
     std::string why = "patch path requested";
-    if (d->eval_path != LAD_PATH_PATCH && d->eval_path != LAD_PATH_PATCH_ATOMIC)
+    if (d->eval_path == LAD_PATH_AUTO || d->eval_path == LAD_PATH_ROWS)
         why = build_row_plan(in, d->rest_len, rplan);
     if (d->eval_path == LAD_PATH_ROWS && !why.empty())
         return fail(ctx, LAD_ERR_ARG, "row path not applicable: " + why);
@@ -923,6 +927,7 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     info->active_buffer = hs.active;
     info->eval_path = ctx->row_mode                         ? LAD_PATH_ROWS
                       : ctx->mode == kModeBoundaryAtomic ? LAD_PATH_PATCH_ATOMIC
+                      : ctx->mode == kModeLdsAtomic      ? LAD_PATH_PATCH_LDS_ATOMIC
                                                          : LAD_PATH_PATCH;
     info->grid_eval = ctx->grid_eval;
     info->host_syncs = ctx->host_syncs;

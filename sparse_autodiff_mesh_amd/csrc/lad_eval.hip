@@ -12,10 +12,12 @@
 //     matrix-free Hessian-vector product.
 //
 // gfx950 design: a patch owns a contiguous range of rows, so its whole slice
-// of the block-CSR value array is accumulated in LDS (LDS atomics, or plain
-// adds in colour phases for the deterministic mode) and then streamed to HBM
-// once with 16-byte stores.  Nothing in HBM is zero-filled, read back or
-// updated atomically; the only HBM writes are the final values.
+// of the block-CSR value array is accumulated in LDS (plain adds in colour
+// phases, or LDS atomics) and then streamed to HBM once with 16-byte stores:
+// nothing in HBM is zero-filled, read back or updated atomically, and the
+// only HBM writes are the final values.  The element-once assembly instead
+// sends each element's blocks in other patches' rows to HBM as global
+// atomics (the page's own scheme, kept for comparison).
 #include "dual2.h"
 #include "energies.h"
 #include "lad_device.h"

@@ -18,10 +18,10 @@
 //    boundary are evaluated once per patch that owns one of their vertices;
 //    ribbon vertices are the non-owned vertices of those elements.
 //  * Records inside a patch are greedily coloured so that no two elements of
-//    one colour share an owned vertex.  The deterministic mode runs the
+//    one colour share an owned vertex.  The default assembly runs the
 //    colours one after another with plain LDS read-add-write (a fixed
-//    summation order); the default mode uses LDS atomics and the same order
-//    keeps lanes of one wave off the same addresses.
+//    summation order); the LDS-atomic assembly uses LDS float atomics, and
+//    the same order keeps lanes of one wave off the same addresses.
 //  * Element-once plans (the page's own decomposition, key designs 3-4:
 //    assembly by atomic scatter-add into the preallocated pattern) keep
 //    each element in one patch only, the one owning its lowest vertex id.

@@ -72,6 +72,8 @@ def tri_desc(**kw):
                 setattr(d, "deterministic", 1)), "LAD_PATH_PATCH_ATOMIC"),
     (lambda d: (setattr(d, "eval_path", binding.LAD_PATH_PATCH_ATOMIC),
                 setattr(d, "pair_capacity", 4), setattr(d, "dhat", 0.1)), "LAD_PATH_PATCH_ATOMIC"),
+    (lambda d: (setattr(d, "eval_path", binding.LAD_PATH_PATCH_LDS_ATOMIC),
+                setattr(d, "deterministic", 1)), "LAD_PATH_PATCH_LDS_ATOMIC"),
 ])
 def test_bad_descriptor_fields(L, mutate, msg):
     d, keep = tri_desc()

@@ -1,5 +1,6 @@
 """Parity at the full benchmark sizes, in the configuration bench.py times
-(default library options; fp32): the 1000 x 1000 cloth, the 512 x 512
+(default library options; fp32): the 1000 x 1000 cloth (row path, and the
+patch path's assemblies the bench also times), the 512 x 512
 symmetric-Dirichlet face grid (eval and HVP), and the 1000 x 1000 cloth
 with 20,000 fresh contact pairs per step over three steps and a final
 insert of nothing.  The oracle evaluates each whole
@@ -44,6 +45,41 @@ def test_cloth_1000(lad):
     assert L.get_info()["nnzb_base"] == 6992002
     x_h = host_input(m.x, "f32")
     prob = oracle.problem_from_mesh(m, f32=True)
+    compare(L, prob, x_h, run(L, x_h))
+    L.close()
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_cloth_1000_patch_path(lad, det):
+    """The element-owner patch path at the full size the bench times it at
+    (LDS atomics, and colour phases with det): E, g, H and H v against the
+    oracle.  It is also the automatic fallback for meshes the row path does
+    not take."""
+    import torch
+    log_case(test="full_cloth1000_patch", det=det)
+    m = inputs.cloth(1000)
+    L = lad.Lad(m.nv, dtype="f32", path="patch", deterministic=det, **lad.mesh_terms(m))
+    assert L.get_info()["eval_path"] == lad.LAD_PATH_PATCH
+    x_h = host_input(m.x, "f32")
+    prob = oracle.problem_from_mesh(m, f32=True)
+    orp, oci = compare(L, prob, x_h, run(L, x_h))
+    v_h = host_input(inputs.hvp_direction(m.nv), "f32")
+    y = L.hvp(dev(x_h, "f32"), dev(v_h, "f32"))
+    torch.cuda.synchronize()
+    assert rel(y.cpu().numpy(), oracle.hvp(prob, orp, oci, x_h, v_h)) <= TOL["f32"]
+    L.close()
+
+
+@pytest.mark.parametrize("path", ["patch", "patch_atomic"])
+def test_faces_512_patch_paths(lad, path):
+    """The 512 x 512 face grid on the patch path's LDS-atomic and
+    global-atomic assemblies, at the size the bench times them."""
+    log_case(test="full_faces512_patch", path=path)
+    m = inputs.face_grid(512)
+    L = lad.Lad(m.nv, dtype="f32", path=path,
+                **lad.mesh_terms(m, springs=False, inertia=False, faces=True))
+    x_h = host_input(m.x, "f32")
+    prob = oracle.problem_from_mesh(m, springs=False, inertia=False, faces=True, f32=True)
     compare(L, prob, x_h, run(L, x_h))
     L.close()
 

@@ -45,7 +45,7 @@ def check_step(lad, L, m, dtype, pairs, x, dhat, faces=False):
 
 
 @pytest.mark.parametrize("n,dtype,det,lds,path", [
-    (24, "f64", False, 0, "patch"), (40, "f32", False, 6144, "patch"),
+    (24, "f64", False, 0, "patch_lds_atomic"), (40, "f32", False, 6144, "patch"),
     (40, "f64", True, 6144, "patch"), (100, "f32", False, 0, "patch"),
     (24, "f64", False, 0, "rows"), (40, "f32", False, 0, "rows"), (100, "f32", False, 0, "rows"),
     (100, "f64", False, 0, "rows"),

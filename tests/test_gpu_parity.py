@@ -46,11 +46,14 @@ def check_against_oracle(prob, x_h, res, dtype):
     (100, "f32", False, 0), (100, "f64", False, 0), (100, "f32", True, 0),
 ])
 def test_cloth_eval_patch(lad, n, dtype, det, lds):
+    """The patch path: colour phases (det, also the default assembly) and,
+    without det, the LDS-atomic assembly."""
     log_case(test="cloth_eval_patch", n=n, dtype=dtype, det=det, lds=lds)
     m = inputs.cloth(n)
-    L, prob, x_h, res = run_eval(lad, m, dtype, det, lds, path="patch")
+    path = "patch" if det else "patch_lds_atomic"
+    L, prob, x_h, res = run_eval(lad, m, dtype, det, lds, path=path)
     info = L.get_info()
-    assert info["eval_path"] == lad.LAD_PATH_PATCH
+    assert info["eval_path"] == (lad.LAD_PATH_PATCH if det else lad.LAD_PATH_PATCH_LDS_ATOMIC)
     if lds:
         assert info["npatches"] > 4  # several patches and ribbons
     check_against_oracle(prob, x_h, res, dtype)
@@ -125,8 +128,9 @@ def test_springs_only_and_inertia_only_rows(lad):
 
 
 @pytest.mark.parametrize("n,dtype,det,lds,path", [
-    (12, "f64", False, 0, "patch"), (33, "f32", False, 8192, "patch"),
+    (12, "f64", False, 0, "patch_lds_atomic"), (33, "f32", False, 8192, "patch"),
     (33, "f64", True, 8192, "patch"), (64, "f32", True, 0, "patch"),
+    (64, "f32", False, 0, "patch_lds_atomic"),
     (2, "f64", False, 0, "rows"), (12, "f64", False, 0, "rows"), (33, "f32", False, 0, "rows"),
     (64, "f32", False, 0, "rows"), (64, "f64", False, 0, "rows"), (129, "f32", False, 0, "rows"),
 ])
@@ -135,12 +139,14 @@ def test_face_eval(lad, n, dtype, det, lds, path):
     m = inputs.face_grid(n)
     L, prob, x_h, res = run_eval(lad, m, dtype, det, lds, springs=False, inertia=False,
                                  faces=True, path=path)
-    assert L.get_info()["eval_path"] == (lad.LAD_PATH_ROWS if path == "rows" else lad.LAD_PATH_PATCH)
+    assert L.get_info()["eval_path"] == {"rows": lad.LAD_PATH_ROWS, "patch": lad.LAD_PATH_PATCH,
+                                         "patch_lds_atomic": lad.LAD_PATH_PATCH_LDS_ATOMIC}[path]
     check_against_oracle(prob, x_h, res, dtype)
     L.close()
 
 
-@pytest.mark.parametrize("dtype,det,path", [("f64", False, "patch"), ("f32", True, "patch"),
+@pytest.mark.parametrize("dtype,det,path", [("f64", False, "patch_lds_atomic"),
+                                            ("f32", False, "patch"), ("f32", True, "patch"),
                                             ("f64", False, "rows"), ("f32", False, "rows")])
 def test_all_terms_eval(lad, dtype, det, path):
     log_case(test="all_terms", dtype=dtype, det=det, path=path)
@@ -152,7 +158,8 @@ def test_all_terms_eval(lad, dtype, det, path):
 
 
 @pytest.mark.parametrize("n,dtype,det,faces,lds,path", [
-    (20, "f64", False, True, 0, "patch"), (45, "f32", False, True, 8192, "patch"),
+    (20, "f64", False, True, 0, "patch_lds_atomic"), (45, "f32", False, True, 8192, "patch"),
+    (45, "f32", False, False, 8192, "patch_lds_atomic"),
     (45, "f64", True, False, 8192, "patch"), (64, "f32", True, True, 0, "patch"),
     (45, "f64", False, False, 0, "rows"), (100, "f32", False, False, 0, "rows"),
     (20, "f64", False, True, 0, "rows"), (45, "f32", False, True, 0, "rows"),
