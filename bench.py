@@ -242,8 +242,11 @@ def to_dev(torch, a, dtype):
 
 def bench_headline(torch, binding, inputs, args, timer):
     m = inputs.cloth(args.n)
+    t0 = time.perf_counter()
     L = binding.Lad(m.nv, dtype="f32", patch_lds_bytes=args.patch_lds, path=args.path,
                     deterministic=args.deterministic, **binding.mesh_terms(m))
+    torch.cuda.synchronize()
+    init_s = time.perf_counter() - t0
     info = L.get_info()
     x = to_dev(torch, m.x, "f32")
     E, g, H = L.alloc_outputs()
@@ -287,7 +290,7 @@ def bench_headline(torch, binding, inputs, args, timer):
     res = {
         "mesh": m, "info": info, "timing": r, "timing_kernel": rk, "timing_flushed": rkf,
         "copy_gbps": copy_gbps, "terms": terms, "bytes": bc,
-        "energy": energy, "nnzb": nnzb, "ns": ns, "nv": nv,
+        "energy": energy, "nnzb": nnzb, "ns": ns, "nv": nv, "init_s": init_s,
     }
     L.close()
     return res
@@ -824,6 +827,11 @@ def main():
                                   if res["timing_flushed"] else None),
             "copy_GBps_measured": (round(res["copy_gbps"], 1) if res["copy_gbps"] else None),
         },
+        # initialisation (untimed above): the GPU pattern build (HIP events
+        # around its launches) and the whole context build (host patching,
+        # uploads and the pattern, wall clock)
+        "init": {"pattern_gpu_ms": round(res["info"]["pattern_ms"], 3),
+                 "context_build_ms": round(res["init_s"] * 1e3, 1)},
         "springs_per_s_M": round(res["ns"] / (ms * 1e-3) / 1e6, 2),
         "energy": res["energy"],
     }

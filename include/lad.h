@@ -161,7 +161,7 @@ typedef struct {
     int64_t face_records;
     int32_t max_colors;         /* colour phases of the patch path's assembly  */
     int32_t active_buffer;      /* 0 = topology pattern, 1/2 = pair buffers    */
-    int32_t eval_path;          /* LAD_PATH_PATCH or LAD_PATH_ROWS in use      */
+    int32_t eval_path;          /* the LAD_PATH_* decomposition in use         */
     int32_t grid_eval;          /* workgroups of one evaluation launch         */
     int64_t host_syncs;         /* host synchronisations made so far for this
                                    context, this lad_get_info call included;
@@ -169,6 +169,10 @@ typedef struct {
                                    lad_insert_pairs never add to it          */
     int32_t nvf_active;         /* vertex-face contacts of the active pattern  */
     int32_t pad0;
+    double pattern_ms;          /* GPU time of the topology pattern's build in
+                                   lad_build_pattern (count, scan, fill, sort
+                                   and de-duplication, compaction), from HIP
+                                   events around those launches              */
 } lad_info;
 
 /*

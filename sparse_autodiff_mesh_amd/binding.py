@@ -72,6 +72,7 @@ class lad_info(ctypes.Structure):
         ("active_buffer", ctypes.c_int32), ("eval_path", ctypes.c_int32),
         ("grid_eval", ctypes.c_int32), ("host_syncs", ctypes.c_int64),
         ("nvf_active", ctypes.c_int32), ("pad0", ctypes.c_int32),
+        ("pattern_ms", ctypes.c_double),
     ]
 
 

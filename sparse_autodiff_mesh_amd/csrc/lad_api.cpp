@@ -37,6 +37,7 @@ struct lad_ctx {
     int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
     bool cols_complete[3] = {true, true, true};  // column array of each pattern buffer complete
     int64_t host_syncs = 0;          // host synchronisations made for this context
+    double pattern_ms = 0.0;         // GPU time of the topology pattern's build
     int32_t debug_flags = 0;         // lad_set_debug
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
@@ -619,16 +620,28 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         e = hipMemcpyAsync(d_faces, d->faces, size_t(d->nf) * 3 * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess && d->ns > 0)
         e = hipMemcpyAsync(d_springs, d->springs, size_t(d->ns) * 2 * 4, hipMemcpyHostToDevice, s);
+    // HIP events around the pattern launches (count .. scan here, the
+    // compaction below) time the build on the GPU
+    hipEvent_t ev[4] = {};
+    bool timed = true;
+    for (hipEvent_t &x : ev) timed = timed && hipEventCreate(&x) == hipSuccess;
+    auto drop_events = [&]() {
+        for (hipEvent_t &x : ev)
+            if (x) (void)hipEventDestroy(x);
+    };
+    if (timed && e == hipSuccess) (void)hipEventRecord(ev[0], s);
     if (e == hipSuccess) e = launch_pattern_count(nv, d->nf, d_faces, d->ns, d_springs, sc, s);
     if (e == hipSuccess) e = launch_pattern_fill(nv, d->nf, d_faces, d->ns, d_springs, sc, s);
     if (e == hipSuccess) e = launch_pattern_unique(nv, sc, s);
     if (e == hipSuccess) e = launch_scan(sc.ucnt, d_rp0, nv, sc.tmp, s);
+    if (timed && e == hipSuccess) (void)hipEventRecord(ev[1], s);
     std::vector<int32_t> h_rp(size_t(nv) + 1);
     if (e == hipSuccess)
         e = hipMemcpyAsync(h_rp.data(), d_rp0, h_rp.size() * 4, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = host_sync(ctx, s);
     if (e != hipSuccess) {
         free_temps();
+        drop_events();
         return hip_fail(ctx, e, "pattern build");
     }
     const int64_t nnzb = h_rp[nv];
@@ -636,15 +649,25 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     ctx->hcap = nnzb + 2 * int64_t(d->pair_capacity) + 6 * int64_t(d->vf_capacity);
     if (ctx->hcap * 9 >= (int64_t(1) << 31)) {
         free_temps();
+        drop_events();
         return fail(ctx, LAD_ERR_ARG, "pattern too large for int32 value indices");
     }
     e = dev_alloc(ctx, &d_ci0, size_t(nnzb));
+    if (timed && e == hipSuccess) (void)hipEventRecord(ev[2], s);
     if (e == hipSuccess) e = launch_pattern_compact(nv, sc, d_rp0, d_ci0, s);
+    if (timed && e == hipSuccess) (void)hipEventRecord(ev[3], s);
     std::vector<int32_t> h_ci(static_cast<size_t>(nnzb));
     if (e == hipSuccess && nnzb > 0)
         e = hipMemcpyAsync(h_ci.data(), d_ci0, h_ci.size() * 4, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = host_sync(ctx, s);
     free_temps();
+    if (e == hipSuccess && timed) {
+        float a = 0.f, b = 0.f;
+        if (hipEventElapsedTime(&a, ev[0], ev[1]) == hipSuccess &&
+            hipEventElapsedTime(&b, ev[2], ev[3]) == hipSuccess)
+            ctx->pattern_ms = double(a) + double(b);
+    }
+    drop_events();
     if (e != hipSuccess) return hip_fail(ctx, e, "pattern compaction");
 
     // ---- patches (host)
@@ -924,6 +947,7 @@ lad_status lad_get_info(lad_ctx *ctx, lad_info *info)
     info->spring_records = ctx->nspr_rec;
     info->face_records = ctx->nfac_rec;
     info->max_colors = ctx->max_colors;
+    info->pattern_ms = ctx->pattern_ms;
     info->active_buffer = hs.active;
     info->eval_path = ctx->row_mode                         ? LAD_PATH_ROWS
                       : ctx->mode == kModeBoundaryAtomic ? LAD_PATH_PATCH_ATOMIC

@@ -72,6 +72,7 @@ def test_cloth_eval_rows(lad, n, dtype):
     L, prob, x_h, res = run_eval(lad, m, dtype)
     info = L.get_info()
     assert info["eval_path"] == lad.LAD_PATH_ROWS
+    assert 0.0 < info["pattern_ms"] < 1e4  # the pattern build was timed on the GPU
     check_against_oracle(prob, x_h, res, dtype)
     L.close()
 
