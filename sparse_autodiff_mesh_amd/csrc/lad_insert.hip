@@ -313,6 +313,7 @@ struct RegRow {
     int32_t q[kRegEnt];  // the entries' elements, ascending (INT32_MAX past the last)
     uint32_t keep;       // bit k: part[k] is new
     uint32_t firstm;     // bit i: the row's vertex is entry i's pair's first vertex
+    uint32_t place;      // bits 2i, 2i + 1: the row's vertex's place in entry i's element
 };
 
 __device__ __forceinline__ bool kept(const RegRow &w, int k) { return (w.keep >> k) & 1u; }
@@ -366,12 +367,14 @@ __device__ __forceinline__ int32_t row_reg(const int32_t ctop[kRegCols], int32_t
             pp[i + 1] = pb;
         }
     w.firstm = 0;
+    w.place = 0;
 #pragma unroll
     for (int i = 0; i < kRegEnt; ++i) {
         w.part[3 * i] = pp[i].x;
         w.part[3 * i + 1] = pp[i].y;
         w.part[3 * i + 2] = pp[i].z;
         w.firstm |= pp[i].w == 0 ? (1u << i) : 0u;
+        w.place |= uint32_t(pp[i].w & 3) << (2 * i);
     }
     int32_t nn = 0;
     w.keep = 0;
@@ -415,7 +418,9 @@ __device__ __forceinline__ void emit_row_reg(const InsertBufs &b, int bk, int32_
             const bool pair = w.q[i] < np;
             b.pslot[bk][p0 + i] =
                 make_int4(pair ? s0 + reg_below(w, w.part[3 * i]) : -1, ds,
-                          pair ? 2 * w.part[3 * i] + int32_t((w.firstm >> i) & 1u) : -1, sw);
+                          pair ? 2 * w.part[3 * i] + int32_t((w.firstm >> i) & 1u)
+                               : -2 - int32_t((w.place >> (2 * i)) & 3u),
+                          sw);
         }
 }
 

@@ -221,9 +221,11 @@ struct PatternBufs {
                                  // vertex-face entry), of the row's diagonal
                                  // block, the pair's partner p as 2 p + 1 when
                                  // the row's vertex is the pair's first, 2 p
-                                 // when second (-1 for a vertex-face entry),
-                                 // and the row's first active slot s0 (-1 - s0
-                                 // when the row gains more than kMaxIns columns)
+                                 // when second (for a vertex-face entry -2 - i,
+                                 // i the row's vertex's place in the contact,
+                                 // or -1 when not recorded), and the row's
+                                 // first active slot s0 (-1 - s0 when the row
+                                 // gains more than kMaxIns columns)
     const int32_t *vf[3];        // vertex-face contacts: (vertex, face id)
     const int32_t *faces;        // [nf][3] mesh faces (contacts on)
 };

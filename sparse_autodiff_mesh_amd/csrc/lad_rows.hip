@@ -473,10 +473,12 @@ __device__ __forceinline__ void pair_add(const RowArgs<T> &A, const T xa[3], con
 // Hrow (block offsets from the row's first slot).
 template <typename T>
 __device__ __forceinline__ void vf_add(const RowArgs<T> &A, int32_t a, int32_t e, T *Hrow, T D[9],
-                                       T G[3], double &E)
+                                       T G[3], double &E, int li = -1)
 {
-    const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
-    const int li = w.x == a ? 0 : (w.y == a ? 1 : (w.z == a ? 2 : 3));
+    if (li < 0) {  // the row's vertex's place in the contact, when not given
+        const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
+        li = w.x == a ? 0 : (w.y == a ? 1 : (w.z == a ? 2 : 3));
+    }
     const int64_t strip = 4 * int64_t(e) + li;
     const int4 so = *reinterpret_cast<const int4 *>(A.vf_slots + strip * 4);
     const T *L = A.vf_eval + strip * kVfStrip;
@@ -849,7 +851,7 @@ __device__ __forceinline__ double eval_row_contacts(const RowArgs<T> &A, int act
         const int4 pi = k == k0 ? pi0 : A.pat.pslot[act][k];
         if (pi.z < 0) {  // vertex-face contact
             const int32_t q = k == k0 ? q0 : A.pat.pinc[act][k];
-            vf_add(A, a, q - npa, hv + 9 * int64_t(pi.w), D, G, E);
+            vf_add(A, a, q - npa, hv + 9 * int64_t(pi.w), D, G, E, pi.z <= -2 ? -2 - pi.z : -1);
             continue;
         }
         const int32_t b = pi.z >> 1;
@@ -1337,18 +1339,26 @@ k_hvp_pair_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v,
                 va[c] = v[int64_t(a) * 3 + c];
             }
             for (int32_t q0 = p0; q0 < p1; ++q0) {
+                // the entry's stored partner (pairs) or place in the contact
+                const int4 ps = A.pat.pslot[act][q0];
                 const int32_t q = pl[q0];
                 if (q >= npa) {  // vertex-face contact: the row's strip of H_e u_e
                     const int32_t e = q - npa;
-                    const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
-                    const int li = w.x == a ? 0 : (w.y == a ? 1 : (w.z == a ? 2 : 3));
+                    int li = ps.z <= -2 ? -2 - ps.z : -1;
+                    if (li < 0) {
+                        const int4 w = *reinterpret_cast<const int4 *>(A.vf_ids + 4 * int64_t(e));
+                        li = w.x == a ? 0 : (w.y == a ? 1 : (w.z == a ? 2 : 3));
+                    }
                     const T *L = A.vf_hvp + (4 * int64_t(e) + li) * kVfHvpStrip;
 #pragma unroll
                     for (int c = 0; c < 3; ++c) Y[c] += L[c];
                     continue;
                 }
-                const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
-                const int32_t b = i0 == a ? i1 : i0;
+                int32_t b = ps.z >> 1;
+                if (ps.z < 0) {  // not recorded: from the pair
+                    const int32_t i0 = prs[2 * q], i1 = prs[2 * q + 1];
+                    b = i0 == a ? i1 : i0;
+                }
                 T dz[3], dv[3];
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
@@ -1594,7 +1604,8 @@ hipError_t launch_hvp_pair_rows(const RowArgs<T> &a, const T *x, const T *v, T *
                                 int grid, const CgState *st, hipStream_t s)
 {
     for (int k = 1; k <= 2; ++k)  // the contact buffers the kernel may read
-        if (!a.pat.pairs[k] || !a.pat.pinc_ptr[k] || !a.pat.pinc[k] || !a.pat.trow[k])
+        if (!a.pat.pairs[k] || !a.pat.pinc_ptr[k] || !a.pat.pinc[k] || !a.pat.trow[k] ||
+            !a.pat.pslot[k])
             return hipErrorInvalidValue;
     if (a.vf_stride > 0 && (!a.vf_ids || !a.vf_hvp)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_hvp_pair_rows<T>, dim3(grid), dim3(kThreads), 0, s, a, x, v, y, dot, st);

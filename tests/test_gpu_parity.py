@@ -183,13 +183,14 @@ def test_hvp(lad, n, dtype, det, faces, lds, path):
     L.close()
 
 
-def test_single_vertex_and_isolated(lad):
-    """Degenerate meshes: one vertex with inertia only; a mesh with isolated
-    vertices (rows holding only the diagonal)."""
+@pytest.mark.parametrize("path", ["auto", "patch", "patch_lds_atomic", "patch_atomic"])
+def test_single_vertex_and_isolated(lad, path):
+    """Degenerate meshes, on every decomposition: one vertex with inertia
+    only; a mesh with isolated vertices (rows holding only the diagonal)."""
     import torch
-    log_case(test="degenerate")
+    log_case(test="degenerate", path=path)
     X = np.array([[0.1, 0.2, 0.3]])
-    L = lad.Lad(1, dtype="f64", x_tilde=np.zeros((1, 3)), c=4.0)
+    L = lad.Lad(1, dtype="f64", x_tilde=np.zeros((1, 3)), c=4.0, path=path)
     E, g, H = L.eval(dev(X, "f64"))
     torch.cuda.synchronize()
     assert abs(E.item() - 0.5 * 4.0 * 0.14) < 1e-15
@@ -201,7 +202,7 @@ def test_single_vertex_and_isolated(lad):
     springs = np.array([[0, 1], [1, 2], [0, 2], [4, 5]], dtype=np.int32)
     rest = np.array([1.0, 1.1, 0.9, 0.5])
     L = lad.Lad(6, dtype="f64", faces=faces, springs=springs, rest_len=rest, k=3.0,
-                x_tilde=np.zeros((6, 3)), c=2.0)
+                x_tilde=np.zeros((6, 3)), c=2.0, path=path)
     E, g, H = L.eval(dev(x, "f64"))
     rp, ci = L.pattern()
     torch.cuda.synchronize()
