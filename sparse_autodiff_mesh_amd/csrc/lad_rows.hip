@@ -1222,6 +1222,10 @@ k_hvp_rows(RowArgs<T> A, const T *__restrict__ x, const T *__restrict__ v, T *__
     slice_range(A.nv, t0, t1, tn);
     SliceRow<T> hn;
     double vy = 0.0;  // this lane's part of v.y
+    // A plain product inside a Newton-CG solve (cg.st set) does nothing once
+    // the solve has ended.
+    if constexpr (!CG)
+        if (cg.st && cg_stop<kHvpThreads>(cg.st, &stop_bc)) return;  // workgroup-uniform
     // The first slice's loads are issued before the Newton-CG step below, so
     // that their latency overlaps its sum.
     if (tn < t1) slice_head<T, FACES, CG>(A, tn, lane, x, v, cg, hn);

@@ -163,6 +163,24 @@ def test_bitwise_reproducible(lad):
     L.close()
 
 
+@pytest.mark.parametrize("n,dtype,iters", [(255, "f64", 300), (256, "f64", 300), (256, "f32", 12)])
+def test_both_row_path_iterations_like_oracle(lad, n, dtype, iters):
+    """Either side of the mesh size from which the row path forms each
+    direction in a launch of its own (65,536 vertices, 256 x 256): the solve
+    stops like the oracle's (fp64: converged; fp32: at a cap well before
+    convergence, so that the stop cannot hinge on rounding), with p to the
+    tolerance, and a second call is bitwise identical."""
+    log_case(test="ncg_split", n=n, dtype=dtype)
+    m, x = near_rest(n, 0.002)
+    L, prob, rp, ci, x_h, g_h = setup(lad, m, x, dtype)
+    p, st, _ = compare(lad, L, prob, rp, ci, x_h, g_h, dtype, max_iters=iters, eta=1e-3)
+    if dtype == "f64":
+        assert st["reason"] == lad.LAD_CG_CONVERGED
+    p2, st2 = L.newton_cg(dev(x_h, dtype), dev(g_h, dtype), max_iters=iters, eta=1e-3)
+    assert st2 == st and np.array_equal(p2.cpu().numpy(), p.cpu().numpy())
+    L.close()
+
+
 def test_fullsize_cloth_f32_like_oracle_and_properties(lad):
     # 1000 x 1000 cloth in fp32: 8 iterations against the oracle (the same
     # stop, p to the fp32 tolerance), then 16 iterations, as timed by the
