@@ -108,10 +108,12 @@ def compulsory_bytes_residual_jacobian(nv, ns, es):
 
 
 def compulsory_bytes_cg_iter(nv, ns, es):
-    """One Newton-CG iteration on the row path: the HVP, which forms its
-    operand d = -r + beta d_prev itself (reading r and d_prev, writing d:
-    two vectors more than a plain HVP), then p and r updated from d and y
-    (four vectors read, two written); the scalar kernels move a few KB."""
+    """One Newton-CG iteration: forming the direction d = -r + beta d_prev
+    (r and d_prev read, d written: two vectors more than a plain HVP, which
+    reads d as its operand), the HVP, then p and r updated from d and y (four
+    vectors read, two written); the scalar steps move a few KB.  The row
+    path on large meshes forms d in a launch of its own, which reads d once
+    more; that is charged to the implementation."""
     return compulsory_bytes_hvp(nv, ns, 0, es) + 8 * 3 * nv * es
 
 
