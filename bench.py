@@ -16,16 +16,22 @@ Prints ONE JSON line.  Besides the contract fields it carries
                 the kernel's mean duration from HIP events on its stream
                 (calls made without the energy, so each call is that one
                 launch; ms_per_step includes the energy sum), plus the
-                kernel's mean with a 512 MB write before every call (inputs
-                evicted from the last-level cache) and the rate of a plain
-                256 MiB device copy (read + write bytes per second), both
-                measured with the secondary workloads;
+                kernel's mean with a read-only 512 MB sweep before every call
+                (inputs evicted from the last-level cache), the rate of a
+                plain 256 MiB device copy (read + write bytes per second) and
+                of a plain 256 MiB fill (write-only), all measured with the
+                secondary workloads, and the counter-based HBM traffic of a
+                launch from the committed profile when the kernel sources
+                match it;
   cpu_baseline  the fp64 CPU oracle, single-threaded, on the same workload;
+  init          the GPU time of the pattern build and the wall-clock time
+                of the whole context build (not timed above);
   secondary     the other workloads (face-energy grid eval and matrix-free
-                HVP, cloth plus contact-pair insertion, cloth plus
-                vertex-face contact insertion, 100 x 100 cloth, and the
-                term front end: ARAP faces, the generic cloth set, ARAP +
-                cloth fused and unfused).
+                HVP, Newton-CG, the vector objective, cloth plus contact-pair
+                insertion, cloth plus vertex-face contact insertion, 100 x 100
+                cloth, the term front end: ARAP faces, the generic cloth set,
+                ARAP + cloth fused and unfused, and the patch path's three
+                assemblies).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--n 1000]
                     [--no-cpu-baseline] [--no-secondary] [--flush-mall]
@@ -271,7 +277,7 @@ def bench_headline(torch, binding, inputs, args, timer):
     # cache (MALL), and a plain device copy, the achievable HBM rate of a
     # read + write stream.  (Left out of the profiled headline-only runs,
     # whose kernel statistics must match the warm timing above.)
-    rkf, copy_gbps = None, None
+    rkf, copy_gbps, fill_gbps = None, None, None
     if not args.no_secondary:
         if not args.flush_mall:
             scratch = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
@@ -282,6 +288,11 @@ def bench_headline(torch, binding, inputs, args, timer):
         dst = torch.empty_like(src)
         rc = timer.run(lambda: dst.copy_(src), 20, 3)
         copy_gbps = 2 * nb / (rc["mean_ms"] * 1e-3) / 1e9
+        # a plain write-only stream (torch's fill): the ceiling of a
+        # write-dominated kernel such as this one (88 % of its bytes are H
+        # and g writes)
+        rf = timer.run(lambda: dst.fill_(1.0), 20, 3)
+        fill_gbps = nb / (rf["mean_ms"] * 1e-3) / 1e9
         del src, dst
     nv, ns = m.nv, m.springs.shape[0]
     nnzb = info["nnzb_base"]
@@ -291,7 +302,7 @@ def bench_headline(torch, binding, inputs, args, timer):
     energy = E.item()
     res = {
         "mesh": m, "info": info, "timing": r, "timing_kernel": rk, "timing_flushed": rkf,
-        "copy_gbps": copy_gbps, "terms": terms, "bytes": bc,
+        "copy_gbps": copy_gbps, "fill_gbps": fill_gbps, "terms": terms, "bytes": bc,
         "energy": energy, "nnzb": nnzb, "ns": ns, "nv": nv, "init_s": init_s,
     }
     L.close()
@@ -830,6 +841,7 @@ def main():
                                         / 1e9 / HBM_PEAK_GBPS, 4)
                                   if res["timing_flushed"] else None),
             "copy_GBps_measured": (round(res["copy_gbps"], 1) if res["copy_gbps"] else None),
+            "fill_GBps_measured": (round(res["fill_gbps"], 1) if res["fill_gbps"] else None),
         },
         # initialisation (untimed above): the GPU pattern build (HIP events
         # around its launches) and the whole context build (host patching,
