@@ -52,13 +52,6 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// This workgroup's contiguous range [c0, c1) of the n chunks.
-__device__ __forceinline__ void chunk_range(int n, int &c0, int &c1)
-{
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    c0 = int(int64_t(n) * w / gridDim.x);
-    c1 = int(int64_t(n) * (w + 1) / gridDim.x);
-}
 
 // Position of column b in the sorted active row [lo, hi); the caller knows
 // it is present.
@@ -878,10 +871,8 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
     const int act = PAIRS ? A.state->active : 0;
     const int32_t *rpa = A.pat.rp[act];
     const int32_t *cia = A.pat.ci[act];
-    int c0, c1;
-    chunk_range(A.nchunk, c0, c1);
     double eacc = 0.0;
-    for (int c = c0; c < c1; ++c) {
+    for (int c = first_chunk(); c < A.nchunk; c += int(gridDim.x)) {  // round robin
         const int32_t v0 = A.chunk[c].v0, nrows = A.chunk[c].nown;
         const int32_t dense_t = A.chunk[c].spr_off;  // its spring slice, or -1
         const int32_t sb = rpa[v0];

@@ -299,11 +299,8 @@ k_terms_eval(TermsArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__re
 {
     extern __shared__ __align__(16) unsigned char smem[];
     T *stage = reinterpret_cast<T *>(smem);
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int c0 = int(int64_t(A.nchunk) * w / gridDim.x);
-    const int c1 = int(int64_t(A.nchunk) * (w + 1) / gridDim.x);
     double eacc = 0.0;
-    for (int ch = c0; ch < c1; ++ch) {
+    for (int ch = first_chunk(); ch < A.nchunk; ch += int(gridDim.x)) {  // round robin
         const int32_t v0 = A.chunk[ch].v0, nrows = A.chunk[ch].nown;
         const int32_t sb = A.rp[v0];
         const int32_t nblk = A.rp[v0 + nrows] - sb;
