@@ -346,7 +346,7 @@ def bench_faces_only(torch, binding, inputs, args, timer):
     bh = compulsory_bytes_hvp(f.nv, 0, nf, 4, faces=True)
     L.close()
     return {"workload": "symmetric-Dirichlet faces, 512x512 vertex grid, fp32",
-            "kernels": ["k_eval_rows<float, true, false>", "k_hvp_rows<float, true, false>"],
+            "kernels": ["k_eval_face_rows<float>", "k_hvp_rows<float, true, false>"],
             "faces": nf, "chunks": info["npatches"], "steps": args.steps, "warmup": args.warmup,
             "eval_ms_mean": round(re["mean_ms"], 5), "eval_algorithmic_bytes": be,
             "eval_GBps": round(be / (re["mean_ms"] * 1e-3) / 1e9, 1),
@@ -519,7 +519,7 @@ def bench_secondary(torch, binding, inputs, args, timer):
     sec["faces512_hvp_hbm_frac"] = round(sec["faces512_hvp_GBps"] / HBM_PEAK_GBPS, 4)
     # VALU-busy of the same kernels from the committed counter summary
     # (null when the kernel sources changed since it was taken)
-    sec["faces512_eval_valu_busy"] = read_valu_busy(FACES_FILE, "k_eval_rows<float, true, false>")
+    sec["faces512_eval_valu_busy"] = read_valu_busy(FACES_FILE, "k_eval_face_rows<float>")
     sec["faces512_hvp_valu_busy"] = read_valu_busy(FACES_FILE, "k_hvp_rows<float, true, false>")
     L.close()
     # 1000 x 1000 cloth + 2 % contact pairs per step, fp32: insert + eval

@@ -28,6 +28,11 @@ struct Tri {
     }
 };
 
+// Fused multiply-add; the rules below are written as chains of them, one
+// rounding per product term.
+__device__ __forceinline__ float lad_fma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double lad_fma(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
 template <typename T, int N>
 struct Dual2 {
     static constexpr int NH = Tri<N>::size;
@@ -133,13 +138,14 @@ __device__ __forceinline__ Dual2<T, N> operator*(const Dual2<T, N> &a, const Dua
     Dual2<T, N> r;
     r.v = a.v * b.v;
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.g[i] = a.v * b.g[i] + b.v * a.g[i];
+    for (int i = 0; i < N; ++i) r.g[i] = lad_fma(a.v, b.g[i], b.v * a.g[i]);
 #pragma unroll
     for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int j = i; j < N; ++j) {
             const int k = Tri<N>::idx(i, j);
-            r.h[k] = a.v * b.h[k] + b.v * a.h[k] + (a.g[i] * b.g[j] + a.g[j] * b.g[i]);
+            r.h[k] = lad_fma(a.g[i], b.g[j],
+                             lad_fma(a.g[j], b.g[i], lad_fma(a.v, b.h[k], b.v * a.h[k])));
         }
     return r;
 }
@@ -150,14 +156,18 @@ __device__ __forceinline__ Dual2<T, N> sqr(const Dual2<T, N> &a)
     Dual2<T, N> r;
     r.v = a.v * a.v;
     const T two_v = T(2) * a.v;
+    T two_g[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.g[i] = two_v * a.g[i];
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = two_v * a.g[i];
+        two_g[i] = T(2) * a.g[i];
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int j = i; j < N; ++j) {
             const int k = Tri<N>::idx(i, j);
-            r.h[k] = two_v * a.h[k] + T(2) * (a.g[i] * a.g[j]);
+            r.h[k] = lad_fma(two_g[i], a.g[j], two_v * a.h[k]);
         }
     return r;
 }
@@ -168,14 +178,18 @@ __device__ __forceinline__ Dual2<T, N> chain(const Dual2<T, N> &a, T f0, T f1, T
 {
     Dual2<T, N> r;
     r.v = f0;
+    T f2g[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.g[i] = f1 * a.g[i];
+    for (int i = 0; i < N; ++i) {
+        r.g[i] = f1 * a.g[i];
+        f2g[i] = f2 * a.g[i];
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int j = i; j < N; ++j) {
             const int k = Tri<N>::idx(i, j);
-            r.h[k] = f1 * a.h[k] + f2 * (a.g[i] * a.g[j]);
+            r.h[k] = lad_fma(f2g[i], a.g[j], f1 * a.h[k]);
         }
     return r;
 }
@@ -332,11 +346,12 @@ __device__ __forceinline__ DualHv<T, N> operator*(const DualHv<T, N> &a, const D
 {
     DualHv<T, N> r;
     r.v = a.v * b.v;
-    r.t = a.v * b.t + b.v * a.t;
+    r.t = lad_fma(a.v, b.t, b.v * a.t);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        r.g[i] = a.v * b.g[i] + b.v * a.g[i];
-        r.gt[i] = a.v * b.gt[i] + b.v * a.gt[i] + (a.g[i] * b.t + b.g[i] * a.t);
+        r.g[i] = lad_fma(a.v, b.g[i], b.v * a.g[i]);
+        r.gt[i] = lad_fma(a.g[i], b.t,
+                          lad_fma(b.g[i], a.t, lad_fma(a.v, b.gt[i], b.v * a.gt[i])));
     }
     return r;
 }
@@ -348,10 +363,11 @@ __device__ __forceinline__ DualHv<T, N> sqr(const DualHv<T, N> &a)
     const T two_v = T(2) * a.v;
     r.v = a.v * a.v;
     r.t = two_v * a.t;
+    const T two_t = T(2) * a.t;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         r.g[i] = two_v * a.g[i];
-        r.gt[i] = two_v * a.gt[i] + T(2) * (a.g[i] * a.t);
+        r.gt[i] = lad_fma(two_t, a.g[i], two_v * a.gt[i]);
     }
     return r;
 }
@@ -367,7 +383,7 @@ __device__ __forceinline__ DualHv<T, N> chain(const DualHv<T, N> &a, T f0, T f1,
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         r.g[i] = f1 * a.g[i];
-        r.gt[i] = f1 * a.gt[i] + f2t * a.g[i];
+        r.gt[i] = lad_fma(f2t, a.g[i], f1 * a.gt[i]);
     }
     return r;
 }

@@ -53,7 +53,13 @@ __device__ __forceinline__ D face_energy(const D F[6], T area)
     D c11 = sqr(F[1]) + sqr(F[3]) + sqr(F[5]);
     D tr = c00 + c11;
     D det = c00 * c11 - sqr(c01);
-    return area * (tr + tr / det);
+    // A (tr + tr / det) = tr q with q = A (1 + 1 / det), a function of det
+    // alone: one chain-rule step and one product, where the quotient, the
+    // sum and the scaling by A would take three passes over the Hessian
+    const T inv = lad_rcp(det.v);
+    const T ai = area * inv;
+    const D q = chain(det, area + ai, -ai * inv, T(2) * ai * inv * inv);
+    return tr * q;
 }
 
 }  // namespace lad

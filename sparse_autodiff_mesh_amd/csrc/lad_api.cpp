@@ -32,6 +32,7 @@ struct lad_ctx {
     double k = 0, c = 0, kappa = 0, dhat = 0;
     int32_t springs_on = 0, faces_on = 0, inertia_on = 0;
     int32_t npatch = 0, lds_eval = 0, lds_hvp = 0, max_colors = 0;
+    int32_t row_lds_blocks = kRowLdsBlocks;  // row path: staging blocks per workgroup
     int64_t nspr_rec = 0, nfac_rec = 0;
     int32_t pair_blocks = 0;
     int32_t row_mode = 0;            // 1: row-owner kernels (LAD_PATH_ROWS)
@@ -324,7 +325,7 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.inertia_on = ctx->inertia_on;
     a.faces_on = ctx->faces_on;
     a.pairs_on = (ctx->pair_cap > 0 || ctx->vf_cap > 0) ? 1 : 0;
-    a.lds_blocks = kRowLdsBlocks;
+    a.lds_blocks = ctx->row_lds_blocks;
     a.state = ctx->d_state;
     a.pat = ctx->pat;
     a.vf_eval = static_cast<T *>(ctx->d_vf_eval);
@@ -714,8 +715,12 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
         return fail(ctx, LAD_ERR_ARG, "vertex-face contacts need the row path: " + why);
     if (ctx->row_mode) {
         plan.hdr = rplan.chunk;
-        ctx->lds_eval = ctx->es == 8 ? rows_lds_bytes<double>(kRowLdsBlocks)
-                                     : rows_lds_bytes<float>(kRowLdsBlocks);
+        // the face kernel without contact capacity stages half chunks
+        ctx->row_lds_blocks = (ctx->faces_on && d->pair_capacity == 0 && d->vf_capacity == 0)
+                                  ? half_chunk_blocks(rplan.chunk, h_rp.data())
+                                  : kRowLdsBlocks;
+        ctx->lds_eval = ctx->es == 8 ? rows_lds_bytes<double>(ctx->row_lds_blocks)
+                                     : rows_lds_bytes<float>(ctx->row_lds_blocks);
         ctx->lds_hvp = 0;
         ctx->nspr_rec = d->ns;
         ctx->nfac_rec = ctx->faces_on ? d->nf : 0;
@@ -766,10 +771,10 @@ lad_status build(const lad_mesh_desc *d, hipStream_t s, lad_ctx *ctx)
     if (st != LAD_OK) return st;
     if (ctx->row_mode) {
         e = ctx->dtype == LAD_F64
-                ? rows_grid<double>(kRowLdsBlocks, ctx->npatch, ctx->faces_on,
+                ? rows_grid<double>(ctx->row_lds_blocks, ctx->npatch, ctx->faces_on,
                                     ctx->pair_cap > 0 || ctx->vf_cap > 0,
                                     &ctx->grid_eval, &ctx->grid_hvp)
-                : rows_grid<float>(kRowLdsBlocks, ctx->npatch, ctx->faces_on,
+                : rows_grid<float>(ctx->row_lds_blocks, ctx->npatch, ctx->faces_on,
                                    ctx->pair_cap > 0 || ctx->vf_cap > 0,
                                    &ctx->grid_eval, &ctx->grid_hvp);
         if (e != hipSuccess) return hip_fail(ctx, e, "occupancy query");

@@ -199,6 +199,11 @@ struct RowPlan {
 // spring per vertex pair, rows short enough), else the reason.
 std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan &out);
 
+// The largest block count of a half chunk (its first kRowsPerChunk / 2 rows,
+// or the rest) over the chunks, with rp the topology row pointer: the
+// staging capacity of the face kernel, which stages one half at a time.
+int32_t half_chunk_blocks(const std::vector<PatchHdr> &chunks, const int32_t *rp);
+
 // ---------------------------------------------------------------------------
 // Kernel argument bundles and launchers (defined in the .hip files).
 // ---------------------------------------------------------------------------

@@ -385,6 +385,18 @@ std::string build_plan(const PlanInput &in, Plan &out)
     return "";
 }
 
+int32_t half_chunk_blocks(const std::vector<PatchHdr> &chunks, const int32_t *rp)
+{
+    const int32_t half = kRowsPerChunk / 2;
+    int32_t most = 1;
+    for (const PatchHdr &c : chunks)
+        for (int32_t h0 = 0; h0 < c.nown; h0 += half) {
+            const int32_t a = c.v0 + h0, b = c.v0 + std::min(c.nown, h0 + half);
+            most = std::max(most, rp[b] - rp[a]);
+        }
+    return most;
+}
+
 std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan &out)
 {
     const int32_t nv = in.nv;

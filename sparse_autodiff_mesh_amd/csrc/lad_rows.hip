@@ -252,6 +252,7 @@ __device__ __forceinline__ void prefetch_pairs(const RowArgs<T> &A, int act, int
 constexpr int kFaceHvpFields = 9;   // product kernel: w_u^T (d2E/dF2 dF) for u = 0, 1, 2
 constexpr int kRowFaceRegs = 8;     // a row's first faces, held in registers
 constexpr int kFaceBatch = 3;       // incident faces whose loads a lane issues together
+constexpr int kHalfFaceBatch = 2;   // the same for a lane that shares its row
 
 // Face positions (in face order), Dm^-1 and area of one face.
 template <typename T>
@@ -279,22 +280,24 @@ __device__ __forceinline__ void load_face(const RowArgs<T> &A, const SliceFace &
 // with indices clamped into the row's range so that every load is valid:
 // each face's record, the positions of its other two vertices, Dm^-1 and
 // area, all issued together.
-template <typename T>
+template <typename T, int NB = kFaceBatch>
 struct FaceBatch {
-    FaceInc e[kFaceBatch];
-    T xo[kFaceBatch][2][3];    // positions of o1, o2
-    T m[kFaceBatch][4];        // Dm^-1
-    T area[kFaceBatch];
+    static constexpr int n = NB;
+    FaceInc e[NB];
+    T xo[NB][2][3];    // positions of o1, o2
+    T m[NB][4];        // Dm^-1
+    T area[NB];
 };
 
-template <typename T>
+// STRIDE: every STRIDE-th face from base (a row shared by a pair of lanes).
+template <typename T, int STRIDE = 1, int NB = kFaceBatch>
 __device__ __forceinline__ void load_faces(const RowArgs<T> &A, const Row<T> &r, int32_t base,
-                                           const T *__restrict__ x, FaceBatch<T> &q)
+                                           const T *__restrict__ x, FaceBatch<T, NB> &q)
 {
 #pragma unroll
-    for (int j = 0; j < kFaceBatch; ++j) q.e[j] = A.finc[min(base + j, r.f1 - 1)];
+    for (int j = 0; j < NB; ++j) q.e[j] = A.finc[min(base + STRIDE * j, r.f1 - 1)];
 #pragma unroll
-    for (int j = 0; j < kFaceBatch; ++j) {
+    for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
             q.xo[j][0][c] = x[int64_t(q.e[j].o1) * 3 + c];
@@ -307,8 +310,8 @@ __device__ __forceinline__ void load_faces(const RowArgs<T> &A, const Row<T> &r,
 }
 
 // Face j of a batch in face order: p_i = x_a, p_(i+1)%3 = o1, p_(i+2)%3 = o2.
-template <typename T>
-__device__ __forceinline__ void batch_face(const Row<T> &r, const FaceBatch<T> &q, int j, int i,
+template <typename T, int NB>
+__device__ __forceinline__ void batch_face(const Row<T> &r, const FaceBatch<T, NB> &q, int j, int i,
                                            FaceIn<T> &f)
 {
 #pragma unroll
@@ -350,25 +353,24 @@ __device__ __forceinline__ void face_w(const T m[4], T w[3][2])
 // The row's part of one face from its F-space derivatives gE (6) and the
 // packed d2E/dF2 h (21), the row vertex at face position i: the gradient
 // into G, the row's own block into D, and the blocks of the face vertices
-// at positions (i+1)%3 and (i+2)%3 to blk(position, block).  The row's
-// material weights are contracted first,
+// at positions (i+1)%3 and (i+2)%3 into B1 and B2.  The row's material
+// weights are contracted first,
 //   P[s][t][c'] = sum_c w[i][c] d2E/dF[s][c] dF[t][c'],
 // then each block is P against the column vertex's weights.  (The weights
 // are picked by selects, not by indexing with i, which would put them in
 // scratch memory.)
-template <typename T, typename BlockAdd>
-__device__ __forceinline__ void face_row(const T gE[6], const T h[21], const T m[4], int i,
-                                         T D[9], T G[3], BlockAdd blk)
+template <typename T>
+__device__ __forceinline__ void face_row_blocks(const T gE[6], const T h[21], const T m[4], int i,
+                                                T D[9], T G[3], T B1[9], T B2[9])
 {
     // w[u][c] from M: w1 = M row 0, w2 = M row 1, w0 = -(w1 + w2)
     auto pick = [&](int u, int c) __attribute__((always_inline)) {
         const T a = m[c], b = m[2 + c];
         return u == 1 ? a : (u == 2 ? b : -(a + b));
     };
-    const int i1 = i == 2 ? 0 : i + 1, i2 = i == 0 ? 2 : i - 1;
+    const int i1 = i == 2 ? 0 : i + 1;
     const T wa[2] = {pick(i, 0), pick(i, 1)};
     const T wb[2] = {pick(i1, 0), pick(i1, 1)};
-    const T wc[2] = {pick(i2, 0), pick(i2, 1)};
 #pragma unroll
     for (int s = 0; s < 3; ++s) G[s] += wa[0] * gE[2 * s] + wa[1] * gE[2 * s + 1];
     auto H = [&](int p, int q) __attribute__((always_inline)) {
@@ -382,17 +384,27 @@ __device__ __forceinline__ void face_row(const T gE[6], const T h[21], const T m
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 P[s][t][c] = wa[0] * H(2 * s, 2 * t + c) + wa[1] * H(2 * s + 1, 2 * t + c);
-    T B1[9], B2[9];
+    // the three weights sum to zero, so the three blocks do too
 #pragma unroll
     for (int s = 0; s < 3; ++s)
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
-            D[3 * s + t] += P[s][t][0] * wa[0] + P[s][t][1] * wa[1];
+            const T own = P[s][t][0] * wa[0] + P[s][t][1] * wa[1];
+            D[3 * s + t] += own;
             B1[3 * s + t] = P[s][t][0] * wb[0] + P[s][t][1] * wb[1];
-            B2[3 * s + t] = P[s][t][0] * wc[0] + P[s][t][1] * wc[1];
+            B2[3 * s + t] = -(own + B1[3 * s + t]);
         }
-    blk(i1, B1);
-    blk(i2, B2);
+}
+
+// The same, with the two blocks handed to blk(position, block).
+template <typename T, typename BlockAdd>
+__device__ __forceinline__ void face_row(const T gE[6], const T h[21], const T m[4], int i,
+                                         T D[9], T G[3], BlockAdd blk)
+{
+    T B1[9], B2[9];
+    face_row_blocks(gE, h, m, i, D, G, B1, B2);
+    blk(i == 2 ? 0 : i + 1, B1);
+    blk(i == 0 ? 2 : i - 1, B2);
 }
 
 // ---------------------------------------------------------------------------
@@ -930,6 +942,135 @@ k_eval_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restr
         wave_lds_sync();
         if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
         wave_lds_sync();
+    }
+    store_energy(esink, block_sum<kRowThreads>(eacc, nullptr));
+}
+
+// The faces of row r taken by one lane of the pair that shares the row
+// (k_eval_face_rows): faces f0 + half, f0 + half + 2, ... in face-id order,
+// kFaceBatch at a time with all their loads issued together; the gradient
+// part and the diagonal block into acc.  The pair's two lanes add into the
+// same staged blocks (a neighbour's block gets a term from each face on
+// their shared edge), so every face step adds in two phases, first the
+// lanes of even half, then those of odd half, with a wave-level LDS
+// hand-off between them: no block is ever read and written by both lanes
+// of a pair in one instruction, and every block sums its terms in a fixed
+// order.  Topology pattern only.
+template <typename T>
+__device__ __forceinline__ void row_faces_half(const RowArgs<T> &A, const Row<T> &r, int half,
+                                               int32_t sb, T *Hs, const T *__restrict__ x,
+                                               RowAcc<T> &acc)
+{
+    for (int32_t base = r.f0 + half; base < r.f1; base += 2 * kHalfFaceBatch) {
+        FaceBatch<T, kHalfFaceBatch> q;
+        load_faces<T, 2, kHalfFaceBatch>(A, r, base, x, q);
+#pragma unroll
+        for (int j = 0; j < kHalfFaceBatch; ++j) {
+            if (base + 2 * j >= r.f1) break;
+            const FaceInc fe = q.e[j];
+            const int i = int(fe.pk & 3u);
+            FaceIn<T> f;
+            batch_face(r, q, j, i, f);
+            T Fv[6];
+            face_F(f, Fv);
+            Dual2<T, 6> F[6];
+#pragma unroll
+            for (int c = 0; c < 6; ++c) F[c] = Dual2<T, 6>::var(Fv[c], c);
+            const Dual2<T, 6> en = face_energy(F, f.area);
+            if (i == 0) acc.E += double(en.v);
+            T B1[9], B2[9];
+            face_row_blocks(en.g, en.h, f.m, i, acc.D, acc.G, B1, B2);
+            // B1 belongs to the vertex at face position (i+1)%3, which is
+            // o1; B2 to o2 (batch_face's order)
+            const int u1 = i == 2 ? 0 : i + 1, u2 = i == 0 ? 2 : i - 1;
+            T *P1 = Hs + 9 * (r.s0 + int32_t((fe.pk >> (8 * u1 + 8)) & 255u) - sb);
+            T *P2 = Hs + 9 * (r.s0 + int32_t((fe.pk >> (8 * u2 + 8)) & 255u) - sb);
+            if (half == 0) {
+#pragma unroll
+                for (int k = 0; k < 9; ++k) P1[k] += B1[k];
+#pragma unroll
+                for (int k = 0; k < 9; ++k) P2[k] += B2[k];
+            }
+            wave_lds_sync();
+            if (half == 1) {
+#pragma unroll
+                for (int k = 0; k < 9; ++k) P1[k] += B1[k];
+#pragma unroll
+                for (int k = 0; k < 9; ++k) P2[k] += B2[k];
+            }
+            wave_lds_sync();
+        }
+    }
+}
+
+// Explicit evaluation with the face term and no contact capacity.  The face
+// work (about 540 VALU instructions per face and row) makes this kernel
+// VALU-bound, and a wave's 64-row staging slice would hold it to two
+// resident waves per SIMD, too few to hide its loads.  So each row is shared
+// by a pair of lanes (lanes 2l and 2l + 1 own row l of 32), each taking
+// every other face of the row; a wave walks its 64-row chunk as two halves
+// of 32 rows and stages one half at a time (A.lds_blocks, set on the host
+// to the largest half's block count), which leaves registers, not LDS, to
+// limit the resident waves.  The lane of even half runs the row's slot loop
+// (springs, zero blocks) first; the pair's diagonal and gradient parts are
+// summed across the two lanes before that lane stores them.  The results
+// are bitwise reproducible, as every sum keeps a fixed order.
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads)
+k_eval_face_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__restrict__ hv,
+                 EnergySink esink)
+{
+    constexpr int kHalfRows = kRowThreads / 2;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T *stage = reinterpret_cast<T *>(smem);
+    const int32_t *rpa = A.pat.rp[0];
+    const int32_t *cia = A.pat.ci[0];
+    const int half = int(threadIdx.x) & 1;
+    const int rl = int(threadIdx.x) >> 1;  // the lane pair's row in the half chunk
+    double eacc = 0.0;
+    for (int c = first_chunk(); c < A.nchunk; c += int(gridDim.x)) {  // round robin
+        const int32_t cv0 = A.chunk[c].v0, cn = A.chunk[c].nown;
+        const int32_t dense_t = A.chunk[c].spr_off;  // its spring slice, or -1
+        for (int32_t h0 = 0; h0 < cn; h0 += kHalfRows) {
+            const int32_t v0 = cv0 + h0, nrows = min(kHalfRows, cn - h0);
+            const int32_t sb = rpa[v0];
+            const int32_t nblk = rpa[v0 + nrows] - sb;
+            // the host sizes the staging area for the largest half chunk
+            const bool fits = nblk <= A.lds_blocks;
+            const int pad = stage_pad<T>(int64_t(sb) * 9);
+            T *Hs = stage + pad;
+            const bool own = fits && rl < nrows;
+            Row<T> r{};
+            if (own) r = load_row<T, true, false>(A, 0, rpa, v0 + rl, x);
+            RowAcc<T> acc;
+            acc_init(acc, r.s0);
+            if (own && half == 0) {
+                const int32_t ins[kMaxIns] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
+                static_assert(kMaxIns == 4, "ins initialiser");
+                PairPre<T> pp;
+                prefetch_pairs(A, 0, 0, r, x, pp);
+                if (A.springs_on && dense_t >= 0)  // wave-uniform
+                    row_slice_springs<T, false>(A, dense_t, h0 + rl, r, ins, sb, Hs, x, acc);
+                else
+                    row_slots<T, false, false>(A, 0, cia, r, r, ins, sb, Hs, x, acc, pp);
+            }
+            wave_lds_sync();  // every block is written before the faces add into it
+            if (own) row_faces_half(A, r, half, sb, Hs, x, acc);
+            // the pair's parts of the diagonal block and the gradient (the
+            // same sum in both lanes: addition is commutative)
+#pragma unroll
+            for (int i = 0; i < 9; ++i) acc.D[i] += __shfl_xor(acc.D[i], 1);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) acc.G[i] += __shfl_xor(acc.G[i], 1);
+            if (own && half == 0) {
+                row_inertia(A, r, acc);
+                row_store(r, sb, Hs, g, acc);
+            }
+            if (own) eacc += acc.E;
+            wave_lds_sync();
+            if (fits) stream_out<kRowThreads>(hv + int64_t(sb) * 9, Hs, nblk * 9, pad);
+            wave_lds_sync();
+        }
     }
     store_energy(esink, block_sum<kRowThreads>(eacc, nullptr));
 }
@@ -1475,8 +1616,13 @@ int rows_lds_bytes(int lds_blocks)
 template <typename T, bool F, bool P>
 static hipError_t rows_occupancy(int lds, int *occ_e, int *occ_h)
 {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_e, k_eval_rows<T, F, P>,
-                                                                kRowThreads, lds);
+    hipError_t e;
+    if constexpr (F && !P)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_e, k_eval_face_rows<T>, kRowThreads,
+                                                         lds);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_e, k_eval_rows<T, F, P>, kRowThreads,
+                                                         lds);
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ_h, k_hvp_rows<T, F, false>,
                                                          kHvpThreads, 0);
@@ -1519,8 +1665,12 @@ template <typename T, bool F, bool P>
 static void launch_eval_rows_as(const RowArgs<T> &a, const T *x, T *g, T *hv, EnergySink es,
                                 int grid, int lds, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_eval_rows<T, F, P>), dim3(grid), dim3(kRowThreads), lds, s, a, x, g, hv,
-                       es);
+    if constexpr (F && !P)
+        hipLaunchKernelGGL((k_eval_face_rows<T>), dim3(grid), dim3(kRowThreads), lds, s, a, x, g,
+                           hv, es);
+    else
+        hipLaunchKernelGGL((k_eval_rows<T, F, P>), dim3(grid), dim3(kRowThreads), lds, s, a, x, g,
+                           hv, es);
 }
 
 // The face tables the row kernels read when the face term is on.
