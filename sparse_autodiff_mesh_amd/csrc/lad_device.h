@@ -105,4 +105,16 @@ __device__ __forceinline__ void stream_out(T *__restrict__ dst, const T *src, in
     for (int i = head + nvec * V + threadIdx.x; i < n; i += NT) dst[i] = src[i];
 }
 
+// Zero the first n elements of the 16-byte aligned LDS area p with NT
+// threads in 16-byte stores (n is rounded up to a whole vector, which the
+// caller's allocation must hold).
+template <int NT, typename T>
+__device__ __forceinline__ void zero_lds(T *p, int n)
+{
+    using VT = typename Vec<T>::type;
+    const int nvec = (n + Vec<T>::n - 1) / Vec<T>::n;
+    const VT z = {};
+    for (int i = threadIdx.x; i < nvec; i += NT) reinterpret_cast<VT *>(p)[i] = z;
+}
+
 }  // namespace lad

@@ -969,6 +969,8 @@ __device__ __forceinline__ void row_faces_half(const RowArgs<T> &A, const Row<T>
             if (base + 2 * j >= r.f1) break;
             const FaceInc fe = q.e[j];
             const int i = int(fe.pk & 3u);
+            // the row's own block (every face of the row names it)
+            acc.dslot = r.s0 + int32_t((fe.pk >> (8 * i + 8)) & 255u);
             FaceIn<T> f;
             batch_face(r, q, j, i, f);
             T Fv[6];
@@ -1011,9 +1013,10 @@ __device__ __forceinline__ void row_faces_half(const RowArgs<T> &A, const Row<T>
 // every other face of the row; a wave walks its 64-row chunk as two halves
 // of 32 rows and stages one half at a time (A.lds_blocks, set on the host
 // to the largest half's block count), which leaves registers, not LDS, to
-// limit the resident waves.  The lane of even half runs the row's slot loop
-// (springs, zero blocks) first; the pair's diagonal and gradient parts are
-// summed across the two lanes before that lane stores them.  The results
+// limit the resident waves.  With springs, the lane of even half runs the
+// row's slot loop (spring blocks, zero blocks) first; without, the wave
+// zeroes the staged half chunk.  The pair's diagonal and gradient parts are
+// summed across the two lanes before the lane of even half stores them.  The results
 // are bitwise reproducible, as every sum keeps a fixed order.
 template <typename T>
 __global__ void __launch_bounds__(kRowThreads)
@@ -1044,12 +1047,18 @@ k_eval_face_rows(RowArgs<T> A, const T *__restrict__ x, T *__restrict__ g, T *__
             if (own) r = load_row<T, true, false>(A, 0, rpa, v0 + rl, x);
             RowAcc<T> acc;
             acc_init(acc, r.s0);
-            if (own && half == 0) {
+            if (!A.springs_on) {  // uniform
+                // a row's blocks are then its diagonal (slot s0 for a row
+                // without faces; else named by each face record) and its
+                // face neighbours', which the faces add into: zero the half
+                // chunk's staging with the whole wave
+                if (fits) zero_lds<kRowThreads>(stage, pad + 9 * nblk);
+            } else if (own && half == 0) {
                 const int32_t ins[kMaxIns] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
                 static_assert(kMaxIns == 4, "ins initialiser");
                 PairPre<T> pp;
                 prefetch_pairs(A, 0, 0, r, x, pp);
-                if (A.springs_on && dense_t >= 0)  // wave-uniform
+                if (dense_t >= 0)  // wave-uniform
                     row_slice_springs<T, false>(A, dense_t, h0 + rl, r, ins, sb, Hs, x, acc);
                 else
                     row_slots<T, false, false>(A, 0, cia, r, r, ins, sb, Hs, x, acc, pp);
