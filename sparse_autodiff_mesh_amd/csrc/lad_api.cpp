@@ -43,7 +43,7 @@ struct lad_ctx {
     int32_t grid_eval = 0, grid_hvp = 0;
     void *d_slot_rest = nullptr;
     int32_t *d_fptr = nullptr;
-    int32_t *d_sl_ptr = nullptr, *d_sl_nb = nullptr;
+    int32_t *d_sl_ptr = nullptr, *d_sl_nb = nullptr, *d_sl_rows = nullptr;
     int16_t *d_sl_d16 = nullptr;
     void *d_sl_rest = nullptr;
     FaceInc *d_finc = nullptr;
@@ -245,6 +245,7 @@ lad_status upload_constants(lad_ctx *ctx, const lad_mesh_desc *d, const Plan &pl
         e = upload(ctx, &p, narrow<T>(rplan.slot_rest.data(), rplan.slot_rest.size()), s);
         ctx->d_slot_rest = p;
         if (e == hipSuccess) e = upload(ctx, &ctx->d_sl_ptr, rplan.sl_ptr, s);
+        if (e == hipSuccess && !rplan.sl_rows.empty()) e = upload(ctx, &ctx->d_sl_rows, rplan.sl_rows, s);
         if (e == hipSuccess && !rplan.sl_d16.empty()) e = upload(ctx, &ctx->d_sl_d16, rplan.sl_d16, s);
         else if (e == hipSuccess) e = upload(ctx, &ctx->d_sl_nb, rplan.sl_nb, s);
         if (e == hipSuccess) e = upload(ctx, &p, narrow<T>(rplan.sl_rest.data(), rplan.sl_rest.size()), s);
@@ -305,6 +306,7 @@ RowArgs<T> row_args(const lad_ctx *ctx)
     a.rp0 = ctx->pat.rp[0];
     a.ci0 = ctx->pat.ci[0];
     a.slot_rest = static_cast<const T *>(ctx->d_slot_rest);
+    a.sl_rows = ctx->d_sl_rows;
     a.sl_ptr = ctx->d_sl_ptr;
     a.sl_nb = ctx->d_sl_nb;
     a.sl_d16 = ctx->d_sl_d16;

@@ -179,18 +179,22 @@ struct RowPlan {
     std::vector<RowFace> rfinc;      // each row's faces, by position in its slice's list
     std::vector<int32_t> sf_ptr;     // [nslice+1] offsets of each slice's face list
     std::vector<SliceFace> sface;    // the slices' face lists
-    // Spring slices for the product kernels: rows in slices of
-    // kSliceRows; slice t holds sl_ptr[t + 1] - sl_ptr[t] = kSliceRows * W_t
-    // entries, W_t the most springs any of its rows has.  Spring j of row
-    // kSliceRows * t + l (its j-th spring neighbour in ascending column
-    // order) is entry sl_ptr[t] + kSliceRows * j + l: a wave reads one
-    // spring of each of its rows with one coalesced load.  Padding entries
-    // name the row itself (or row 0 past the last row) with rest length -1.
+    // Slices of the product kernels: slice t's lane l takes row
+    // kSliceRows * t + l, or, with the face term on, sl_rows[kSliceRows * t
+    // + l] (breadth-first patches of the mesh, -1 for padding; every row in
+    // exactly one slice).  Spring slices: slice t holds sl_ptr[t + 1] -
+    // sl_ptr[t] = kSliceRows * W_t entries, W_t the most springs any of its
+    // rows has.  Spring j of lane l's row (its j-th spring neighbour in
+    // ascending column order) is entry sl_ptr[t] + kSliceRows * j + l: a
+    // wave reads one spring of each of its rows with one coalesced load.
+    // Padding entries name the row itself (the last row for a padding lane)
+    // with rest length -1.
+    std::vector<int32_t> sl_rows;
     std::vector<int32_t> sl_ptr;     // [nslice + 1]
     std::vector<int32_t> sl_nb;      // neighbour vertex
     std::vector<double> sl_rest;     // rest length
     // The same neighbours as 16-bit differences from the entry's row
-    // (clamped to the last row past it): filled when every difference fits,
+    // (the last row for a padding lane): filled when every difference fits,
     // which halves the neighbour bytes the kernels stream; else empty.
     std::vector<int16_t> sl_d16;
 };
@@ -309,6 +313,7 @@ struct RowArgs {
     const int32_t *rp0, *ci0;    // topology pattern
     const T *slot_rest;          // [nnzb_base] rest length of the spring behind
                                  // each block (< 0: no spring)
+    const int32_t *sl_rows;      // product slices' rows (RowPlan; null: contiguous)
     const int32_t *sl_ptr;       // spring slices (RowPlan): entry offsets,
     const int32_t *sl_nb;        // neighbour vertices (null when sl_d16 is set)
     const int16_t *sl_d16;       // or their differences from the row

@@ -397,6 +397,48 @@ int32_t half_chunk_blocks(const std::vector<PatchHdr> &chunks, const int32_t *rp
     return most;
 }
 
+// The rows of the product kernels' slices when the face term is on:
+// patches of kSliceRows vertices grown breadth first over the pattern's
+// adjacency (each patch seeded at the lowest vertex no patch holds yet,
+// neighbours taken in column order, a new seed whenever the search runs
+// dry, so every slice but the last is full).  A slice lists every face
+// incident to its rows once, and a compact patch touches about 2.5 faces
+// per row where 64 consecutive rows of a mesh numbered line by line touch
+// 4 (512 x 512 grid: 159 against 257 faces per slice).  Padding: -1.
+static void bfs_slice_rows(int32_t nv, const int32_t *rp, const int32_t *ci,
+                           std::vector<int32_t> &rows)
+{
+    const int64_t nsl = (int64_t(nv) + kSliceRows - 1) / kSliceRows;
+    rows.assign(size_t(nsl * kSliceRows), -1);
+    std::vector<uint8_t> taken(size_t(nv), 0);
+    std::vector<int32_t> queue;
+    queue.reserve(kSliceRows);
+    int32_t cursor = 0;
+    for (int64_t t = 0; t < nsl; ++t) {
+        int32_t n = 0;
+        size_t head = 0;
+        queue.clear();
+        while (n < kSliceRows) {
+            if (head == queue.size()) {  // the search ran dry: a new seed
+                while (cursor < nv && taken[size_t(cursor)]) ++cursor;
+                if (cursor == nv) break;
+                taken[size_t(cursor)] = 1;
+                queue.push_back(cursor);
+            }
+            const int32_t v = queue[head++];
+            rows[size_t(t * kSliceRows + n++)] = v;
+            // take a neighbour only while the patch has room for it, so
+            // every vertex taken is placed
+            for (int32_t k = rp[v]; k < rp[v + 1]; ++k) {
+                const int32_t w = ci[k];
+                if (taken[size_t(w)] || n + int32_t(queue.size() - head) >= kSliceRows) continue;
+                taken[size_t(w)] = 1;
+                queue.push_back(w);
+            }
+        }
+    }
+}
+
 std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan &out)
 {
     const int32_t nv = in.nv;
@@ -416,6 +458,14 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         sab = L;
         sba = L;
     }
+    const bool faces = in.face_energy && in.nf > 0;
+    if (faces) bfs_slice_rows(nv, rp, ci, out.sl_rows);
+    // row of lane l of product slice t, -1 for padding
+    auto slice_row = [&](int64_t t, int64_t l) -> int32_t {
+        if (!out.sl_rows.empty()) return out.sl_rows[size_t(t * kSliceRows + l)];
+        const int64_t a = t * kSliceRows + l;
+        return a < nv ? int32_t(a) : -1;
+    };
     {
         // spring slices: each row's spring neighbours in column order
         const int64_t nsl = (int64_t(nv) + kSliceRows - 1) / kSliceRows;
@@ -423,7 +473,9 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         int64_t tot = 0;
         for (int64_t t = 0; t < nsl; ++t) {
             int32_t w = 0;
-            for (int64_t a = t * kSliceRows; a < std::min<int64_t>(nv, (t + 1) * kSliceRows); ++a) {
+            for (int64_t l = 0; l < kSliceRows; ++l) {
+                const int32_t a = slice_row(t, l);
+                if (a < 0) continue;
                 int32_t n = 0;
                 for (int64_t k = rp[a]; k < rp[a + 1]; ++k)
                     n += (ci[k] != a && out.slot_rest[size_t(k)] >= 0.0) ? 1 : 0;
@@ -438,24 +490,29 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         for (int64_t t = 0; t < nsl; ++t) {
             const int64_t w = (out.sl_ptr[size_t(t) + 1] - out.sl_ptr[size_t(t)]) / kSliceRows;
             for (int64_t l = 0; l < kSliceRows; ++l) {
-                const int64_t a = t * kSliceRows + l;
+                const int32_t a = slice_row(t, l);
                 const int64_t e0 = out.sl_ptr[size_t(t)] + l;
                 int64_t j = 0;
-                if (a < nv)
+                if (a >= 0)
                     for (int64_t k = rp[a]; k < rp[a + 1]; ++k)
                         if (ci[k] != a && out.slot_rest[size_t(k)] >= 0.0) {
                             out.sl_nb[size_t(e0 + kSliceRows * j)] = ci[k];
                             out.sl_rest[size_t(e0 + kSliceRows * j)] = out.slot_rest[size_t(k)];
                             ++j;
                         }
-                for (; j < w; ++j) out.sl_nb[size_t(e0 + kSliceRows * j)] = a < nv ? int32_t(a) : nv - 1;
+                for (; j < w; ++j) out.sl_nb[size_t(e0 + kSliceRows * j)] = a >= 0 ? a : nv - 1;
             }
         }
-        // 16-bit differences from the (clamped) row, when all fit
+        // 16-bit differences from the row (the last row for padding), when
+        // all fit
+        auto entry_row = [&](int64_t t, int64_t e) -> int64_t {
+            const int32_t a = slice_row(t, (e - out.sl_ptr[size_t(t)]) % kSliceRows);
+            return a >= 0 ? a : nv - 1;
+        };
         bool narrow = true;
         for (int64_t t = 0; t < nsl && narrow; ++t)
             for (int64_t e = out.sl_ptr[size_t(t)]; e < out.sl_ptr[size_t(t) + 1]; ++e) {
-                const int64_t a = std::min<int64_t>(t * kSliceRows + (e - out.sl_ptr[size_t(t)]) % kSliceRows, nv - 1);
+                const int64_t a = entry_row(t, e);
                 const int64_t d = int64_t(out.sl_nb[size_t(e)]) - a;
                 if (d < INT16_MIN || d > INT16_MAX) {
                     narrow = false;
@@ -466,12 +523,12 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
             out.sl_d16.resize(size_t(tot));
             for (int64_t t = 0; t < nsl; ++t)
                 for (int64_t e = out.sl_ptr[size_t(t)]; e < out.sl_ptr[size_t(t) + 1]; ++e) {
-                    const int64_t a = std::min<int64_t>(t * kSliceRows + (e - out.sl_ptr[size_t(t)]) % kSliceRows, nv - 1);
+                    const int64_t a = entry_row(t, e);
                     out.sl_d16[size_t(e)] = int16_t(int64_t(out.sl_nb[size_t(e)]) - a);
                 }
         }
     }
-    if (in.face_energy && in.nf > 0) {
+    if (faces) {
         // per-row incidence, rows in vertex order, faces by id within a row
         out.fptr.assign(size_t(nv) + 1, 0);
         for (int64_t f = 0; f < in.nf; ++f)
@@ -506,14 +563,16 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         std::vector<int32_t> where(size_t(in.nf), -1);   // position in the current list
         std::vector<int64_t> owner(size_t(in.nf), -1);   // slice that listed the face
         for (int64_t t = 0; t < nsl; ++t) {
-            const int32_t v0 = int32_t(t * kSliceRows);
-            const int32_t v1 = int32_t(std::min<int64_t>(nv, (t + 1) * kSliceRows));
             int32_t maxdeg = 0;
-            for (int32_t a = v0; a < v1; ++a) maxdeg = std::max(maxdeg, out.fptr[a + 1] - out.fptr[a]);
+            for (int64_t l = 0; l < kSliceRows; ++l) {
+                const int32_t a = slice_row(t, l);
+                if (a >= 0) maxdeg = std::max(maxdeg, out.fptr[a + 1] - out.fptr[a]);
+            }
             int64_t nl = 0;
             for (int32_t rank = 0; rank < maxdeg; ++rank)
-                for (int32_t a = v0; a < v1; ++a) {
-                    if (rank >= out.fptr[a + 1] - out.fptr[a]) continue;
+                for (int64_t l = 0; l < kSliceRows; ++l) {
+                    const int32_t a = slice_row(t, l);
+                    if (a < 0 || rank >= out.fptr[a + 1] - out.fptr[a]) continue;
                     const int32_t f = out.finc[size_t(out.fptr[a] + rank)].f;
                     if (owner[size_t(f)] == t) continue;
                     owner[size_t(f)] = t;
@@ -525,7 +584,9 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
                 }
             if (out.sf_ptr[size_t(t)] + nl > INT32_MAX) return "too many faces for the slice lists";
             out.sf_ptr[size_t(t) + 1] = int32_t(out.sf_ptr[size_t(t)] + nl);
-            for (int32_t a = v0; a < v1; ++a) {
+            for (int64_t l = 0; l < kSliceRows; ++l) {
+                const int32_t a = slice_row(t, l);
+                if (a < 0) continue;
                 for (int32_t k = out.fptr[a]; k < out.fptr[a + 1]; ++k) {
                     RowFace e;
                     e.lf = uint32_t(where[size_t(out.finc[size_t(k)].f)]);
@@ -557,7 +618,7 @@ std::string build_row_plan(const PlanInput &in, const double *rest_len, RowPlan 
         // their diagonal and their springs' blocks reads its springs from the
         // slice (spr_off = the slice), else from its rows (-1)
         h.spr_off = -1;
-        if (v0 % kSliceRows == 0 && n == std::min(kSliceRows, nv - v0)) {
+        if (out.sl_rows.empty() && v0 % kSliceRows == 0 && n == std::min(kSliceRows, nv - v0)) {
             bool dense = true;
             for (int32_t a = v0; a < v0 + n && dense; ++a)
                 for (int32_t k = rp[a]; k < rp[a + 1] && dense; ++k)

@@ -1139,8 +1139,8 @@ __device__ __forceinline__ double cg_dir_comp(double r, double d, double beta)
 constexpr int kSliceBatch = 6;
 
 // What a lane of the product kernels loads for its row before the gathers:
-// the row (kSliceRows * t + lane, clamped to the last row for lanes past
-// it), its position, its operand (v, or r and the previous direction for
+// the row (kSliceRows * t + lane, or the slice's listed row; the last row
+// for lanes past the rows, which store nothing), its position, its operand (v, or r and the previous direction for
 // Newton-CG), its first kSliceBatch spring neighbours with their rest
 // lengths (without the face term only) or its face range.  Every load
 // depends only on the slice index, so the next slice's are issued while
@@ -1162,8 +1162,15 @@ __device__ __forceinline__ void slice_head(const RowArgs<T> &A, int32_t t, int l
                                            const T *__restrict__ x, const T *__restrict__ v,
                                            const CgDir<T> &cg, SliceRow<T> &h)
 {
-    h.live = t * kSliceRows + lane < A.nv ? 1 : 0;
-    const int32_t a = min(t * kSliceRows + lane, A.nv - 1);
+    int32_t a;
+    if (A.sl_rows) {  // patches of the mesh (face term on)
+        const int32_t r = A.sl_rows[int64_t(t) * kSliceRows + lane];
+        h.live = r >= 0 ? 1 : 0;
+        a = r >= 0 ? r : A.nv - 1;
+    } else {
+        h.live = t * kSliceRows + lane < A.nv ? 1 : 0;
+        a = min(t * kSliceRows + lane, A.nv - 1);
+    }
     h.a = a;
     const int32_t p = A.sl_ptr[t];
     const int32_t ns = A.springs_on ? (A.sl_ptr[t + 1] - p) / kSliceRows : 0;

@@ -411,13 +411,38 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
     const std::string err = build_row_plan(in, m.rest.data(), plan);
     CHECK(err.empty(), "%s: build_row_plan failed: %s", tag, err.c_str());
     if (!err.empty()) return;
+    const int32_t nsl = (m.nv + kSliceRows - 1) / kSliceRows;
+    // product slices: contiguous rows, or with the face term on a partition
+    // of the rows into full slices (the last may be short) listed in
+    // sl_rows, padded with -1 at the end
+    CHECK(plan.sl_rows.empty() != faces_on, "%s: slice rows present %d", tag, int(!plan.sl_rows.empty()));
+    if (!plan.sl_rows.empty()) {
+        CHECK(plan.sl_rows.size() == size_t(nsl) * kSliceRows, "%s: slice rows size", tag);
+        if (plan.sl_rows.size() != size_t(nsl) * kSliceRows) return;
+        std::vector<int32_t> seen(size_t(m.nv), 0);
+        for (size_t k = 0; k < plan.sl_rows.size(); ++k) {
+            const int32_t a = plan.sl_rows[k];
+            if (k < size_t(m.nv)) {
+                CHECK(a >= 0 && a < m.nv, "%s: slice entry %zu row %d", tag, k, a);
+                if (a >= 0 && a < m.nv) seen[size_t(a)] += 1;
+            } else {
+                CHECK(a == -1, "%s: slice padding %zu", tag, k);
+            }
+        }
+        for (int32_t a = 0; a < m.nv; ++a) CHECK(seen[size_t(a)] == 1, "%s: row %d in %d slices", tag, a, seen[size_t(a)]);
+    }
+    auto row_of = [&](int32_t t, int32_t l) -> int32_t {
+        if (!plan.sl_rows.empty()) return plan.sl_rows[size_t(t) * kSliceRows + size_t(l)];
+        return t * kSliceRows + l < m.nv ? t * kSliceRows + l : -1;
+    };
     int32_t expect_v0 = 0;
     for (const PatchHdr &h : plan.chunk) {
         CHECK(h.v0 == expect_v0 && h.nown > 0 && h.nown <= kRowsPerChunk, "%s: chunk rows", tag);
         CHECK(h.nblk == rp[h.v0 + h.nown] - rp[h.v0] && h.nblk <= kRowBaseBlocks, "%s: chunk blocks", tag);
         CHECK(h.amap_cap == kRowLdsBlocks, "%s: chunk capacity", tag);
         // slice-aligned chunks whose off-diagonal blocks all carry springs
-        bool dense = h.v0 % kSliceRows == 0 && h.nown == std::min(kSliceRows, m.nv - h.v0);
+        bool dense = plan.sl_rows.empty() && h.v0 % kSliceRows == 0 &&
+                     h.nown == std::min(kSliceRows, m.nv - h.v0);
         for (int32_t a = h.v0; a < h.v0 + h.nown && dense; ++a)
             for (int32_t k = rp[a]; k < rp[a + 1]; ++k)
                 if (ci[k] != a && !has_spring(m, a, ci[k])) dense = false;
@@ -439,7 +464,6 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
         sp[m.springs[2 * s + 1]].push_back({m.springs[2 * s], m.rest[s]});
     }
     for (auto &l : sp) std::sort(l.begin(), l.end());
-    const int32_t nsl = (m.nv + kSliceRows - 1) / kSliceRows;
     CHECK(int32_t(plan.sl_ptr.size()) == nsl + 1 && plan.sl_ptr[0] == 0, "%s: slice offsets size", tag);
     if (int32_t(plan.sl_ptr.size()) != nsl + 1) return;
     CHECK(size_t(plan.sl_ptr[nsl]) == plan.sl_nb.size() && plan.sl_nb.size() == plan.sl_rest.size(),
@@ -447,20 +471,20 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
     for (int32_t t = 0; t < nsl; ++t) {
         const int32_t len = plan.sl_ptr[t + 1] - plan.sl_ptr[t];
         size_t wmax = 0;
-        for (int32_t a = t * kSliceRows; a < std::min(m.nv, (t + 1) * kSliceRows); ++a)
-            wmax = std::max(wmax, sp[a].size());
+        for (int32_t l = 0; l < kSliceRows; ++l)
+            if (row_of(t, l) >= 0) wmax = std::max(wmax, sp[size_t(row_of(t, l))].size());
         CHECK(len >= 0 && len % kSliceRows == 0 && size_t(len / kSliceRows) == wmax,
               "%s: slice %d width", tag, t);
         if (len < 0 || size_t(plan.sl_ptr[t + 1]) > plan.sl_nb.size()) continue;
         for (int32_t l = 0; l < kSliceRows; ++l) {
-            const int32_t a = t * kSliceRows + l;
+            const int32_t a = row_of(t, l);
             for (int32_t j = 0; j < len / kSliceRows; ++j) {
                 const size_t e = size_t(plan.sl_ptr[t] + j * kSliceRows + l);
-                if (a < m.nv && size_t(j) < sp[a].size())
+                if (a >= 0 && size_t(j) < sp[a].size())
                     CHECK(plan.sl_nb[e] == sp[a][j].first && plan.sl_rest[e] == sp[a][j].second,
                           "%s: row %d spring %d", tag, a, j);
                 else
-                    CHECK(plan.sl_nb[e] == (a < m.nv ? a : m.nv - 1) && plan.sl_rest[e] == -1.0,
+                    CHECK(plan.sl_nb[e] == (a >= 0 ? a : m.nv - 1) && plan.sl_rest[e] == -1.0,
                           "%s: row %d padding %d", tag, a, j);
             }
         }
@@ -469,7 +493,8 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
     bool fit = true;
     for (int32_t t = 0; t < nsl; ++t)
         for (int32_t e = plan.sl_ptr[t]; e < plan.sl_ptr[t + 1]; ++e) {
-            const int64_t a = std::min(t * kSliceRows + (e - plan.sl_ptr[t]) % kSliceRows, m.nv - 1);
+            const int32_t r = row_of(t, (e - plan.sl_ptr[t]) % kSliceRows);
+            const int64_t a = r >= 0 ? r : m.nv - 1;
             const int64_t d = int64_t(plan.sl_nb[size_t(e)]) - a;
             fit = fit && d >= INT16_MIN && d <= INT16_MAX;
             if (!plan.sl_d16.empty() && size_t(e) < plan.sl_d16.size())
@@ -497,21 +522,24 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
     }
     // slice face lists of the product kernels: each face incident to a
     // slice's rows exactly once, ordered by (its first position in an
-    // incident row's id-sorted face list, that row); every row's faces by
-    // their position in its slice's list, with the row's position in the face
+    // incident row's id-sorted face list, that row's lane); every row's
+    // faces by their position in its slice's list, with the row's position
+    // in the face
     CHECK(int32_t(plan.sf_ptr.size()) == nsl + 1 && plan.sf_ptr[0] == 0, "%s: slice face offsets", tag);
     if (int32_t(plan.sf_ptr.size()) != nsl + 1) return;
     CHECK(size_t(plan.sf_ptr[nsl]) == plan.sface.size(), "%s: slice face count", tag);
     CHECK(plan.rfinc.size() == plan.finc.size(), "%s: row face records", tag);
     for (int32_t t = 0; t < nsl; ++t) {
-        const int32_t v0 = t * kSliceRows, v1 = std::min(m.nv, (t + 1) * kSliceRows);
-        std::map<int32_t, std::pair<int32_t, int32_t>> key;  // face -> (rank, row)
-        for (int32_t a = v0; a < v1; ++a)
+        std::map<int32_t, std::pair<int32_t, int32_t>> key;  // face -> (rank, lane)
+        for (int32_t l = 0; l < kSliceRows; ++l) {
+            const int32_t a = row_of(t, l);
+            if (a < 0) continue;
             for (size_t r = 0; r < inc[a].size(); ++r) {
-                const auto k = std::make_pair(int32_t(r), a);
+                const auto k = std::make_pair(int32_t(r), l);
                 auto it = key.find(inc[a][r]);
                 if (it == key.end() || k < it->second) key[inc[a][r]] = k;
             }
+        }
         const int32_t n = plan.sf_ptr[t + 1] - plan.sf_ptr[t];
         CHECK(n == int32_t(key.size()), "%s: slice %d lists %d faces, %zu incident", tag, t, n, key.size());
         if (n != int32_t(key.size())) continue;
@@ -524,7 +552,9 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
             CHECK(sf.f == f, "%s: slice %d list position %d", tag, t, k);
             for (int i = 0; i < 3; ++i) CHECK(sf.v[i] == m.faces[3 * size_t(f) + i], "%s: face %d vertices", tag, f);
         }
-        for (int32_t a = v0; a < v1; ++a) {
+        for (int32_t l = 0; l < kSliceRows; ++l) {
+            const int32_t a = row_of(t, l);
+            if (a < 0) continue;
             std::vector<int32_t> got;
             for (int32_t k = plan.fptr[a]; k < plan.fptr[a + 1] && size_t(k) < plan.rfinc.size(); ++k) {
                 const RowFace &e = plan.rfinc[size_t(k)];
