@@ -450,6 +450,19 @@ void check_row_plan(const Mesh &m, bool faces_on, const char *tag)
         expect_v0 = h.v0 + h.nown;
     }
     CHECK(expect_v0 == m.nv, "%s: chunks do not cover the rows", tag);
+    // the face kernel's staging capacity: the largest block count of the
+    // first kRowsPerChunk / 2 rows of a chunk or of the rest
+    {
+        int32_t most = 1;
+        for (const PatchHdr &h : plan.chunk)
+            for (int32_t part = 0; part < 2; ++part) {
+                const int32_t a = h.v0 + std::min(h.nown, part * (kRowsPerChunk / 2));
+                const int32_t b = part == 0 ? h.v0 + std::min(h.nown, kRowsPerChunk / 2) : h.v0 + h.nown;
+                most = std::max(most, rp[b] - rp[a]);
+            }
+        CHECK(half_chunk_blocks(plan.chunk, rp.data()) == most, "%s: half-chunk staging %d, want %d",
+              tag, half_chunk_blocks(plan.chunk, rp.data()), most);
+    }
     std::vector<double> want(ci.size(), -1.0);
     for (size_t s = 0; s * 2 < m.springs.size(); ++s) {
         want[size_t(slot_of(rp, ci, m.springs[2 * s], m.springs[2 * s + 1]))] = m.rest[s];

@@ -211,3 +211,56 @@ def test_eval_irregular(lad, case):
     assert rel(H.cpu().numpy()[: oci.size], Ho) <= TOL[dtype]
     assert rel(y.cpu().numpy(), oracle.bsr_spmv(orp, oci, Ho, v_h)) <= TOL[dtype]
     L.close()
+
+
+def face_mesh_irregular(n, drop, seed):
+    """An n x n face grid with its vertices renumbered by a seeded
+    permutation and about `drop` of its faces removed (seeded): rows of
+    every valence from 0 (isolated vertices) to 6, a numbering with no grid
+    order (the product kernels' breadth-first slices and the explicit
+    kernel's half chunks see uneven rows), and faces that keep their rest
+    data (Dm^-1, area from the unpermuted grid)."""
+    m = inputs.face_grid(n)
+    u = inputs.uniform_block(seed, m.nv + m.faces.shape[0])
+    perm = np.argsort(u[:m.nv], kind="stable").astype(np.int32)  # new id of old vertex v
+    keep = u[m.nv:] >= drop
+    faces = perm[m.faces[keep]]
+    x = np.empty_like(m.x)
+    x[perm] = m.x
+    return m.nv, x, faces.astype(np.int32), m.dm_inv[keep], m.area[keep]
+
+
+@pytest.mark.parametrize("n,drop,dtype", [(40, 0.1, "f64"), (40, 0.1, "f32"), (97, 0.03, "f32")])
+def test_faces_irregular(lad, n, drop, dtype):
+    """The face kernels on a renumbered grid with faces removed: E, g, H
+    and H v against the oracle, the block pattern bit-exact, and repeated
+    evaluations and products bitwise identical."""
+    import torch
+    log_case(test="faces_irregular", n=n, drop=drop, dtype=dtype)
+    nv, x, faces, dm, area = face_mesh_irregular(n, drop, seed=300 + n)
+    L = lad.Lad(nv, dtype=dtype, faces=faces, face_energy=True, dm_inv=dm, area=area)
+    assert L.get_info()["eval_path"] == lad.LAD_PATH_ROWS
+    prob = oracle.Problem(nv=nv, faces=faces, face_energy=True, dm_inv=host_input(dm, dtype),
+                          area=host_input(area, dtype))
+    x_h = host_input(x, dtype)
+    v_h = host_input(inputs.hvp_direction(nv), dtype)
+    xd, vd = dev(x_h, dtype), dev(v_h, dtype)
+    E, g, H = L.eval(xd)
+    y = L.hvp(xd, vd)
+    rp, ci = L.pattern()
+    torch.cuda.synchronize()
+    E, g, H, y = E.clone(), g.clone(), H.clone(), y.clone()
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    assert rel([E.item()], [Eo]) <= TOL[dtype]
+    assert rel(g.cpu().numpy(), go) <= TOL[dtype]
+    assert rel(H.cpu().numpy()[: oci.size], Ho) <= TOL[dtype]
+    assert rel(y.cpu().numpy(), oracle.hvp(prob, orp, oci, x_h, v_h)) <= TOL[dtype]
+    for _ in range(3):
+        E2, g2, H2 = L.eval(xd)
+        y2 = L.hvp(xd, vd)
+        torch.cuda.synchronize()
+        assert torch.equal(E2, E) and torch.equal(g2, g) and torch.equal(H2, H)
+        assert torch.equal(y2, y)
+    L.close()
