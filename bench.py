@@ -148,12 +148,46 @@ def read_valu_busy(path, kernel):
     return val.get(kernel)
 
 
+def code_only(text):
+    """C++ source text without its comments, whitespace runs collapsed: what
+    the compiler sees, so that a comment edit keeps the fingerprint."""
+    out, i, n, quote = [], 0, len(text), None
+    while i < n:
+        c = text[i]
+        if quote:
+            out.append(c)
+            if c == "\\" and i + 1 < n:
+                out.append(text[i + 1])
+                i += 2
+                continue
+            if c == quote:
+                quote = None
+            i += 1
+        elif c in "\"'":
+            quote = c
+            out.append(c)
+            i += 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha():
+    """Fingerprint of the kernel sources the committed counter summaries were
+    taken on (their code, not their comments)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_autodiff_mesh_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_only(f.read()).encode() + b"\0")
     return h.hexdigest()
 
 

@@ -17,13 +17,14 @@
 // z = x_a - x_b as seed variables the local Hessian is the same 3x3 block K
 // both times, bit for bit), writes the off-diagonal block -K of every slot
 // of its row exactly once, and accumulates the diagonal block and g_a in
-// registers.  No block is written twice, nothing is zero-filled, there are no
-// atomics, and every sum is taken in a fixed order: the result is bitwise
-// reproducible.  A wave's 64 consecutive rows form one contiguous slice of
-// the value array; it is staged in LDS and streamed to HBM with 16-byte
-// nontemporal stores.  Workgroups are persistent: each walks a contiguous
-// range of row chunks, and the ranges are grouped by XCD so that vertex
-// positions shared by neighbouring rows stay in one L2.
+// registers.  Spring blocks are written once, there are no atomics, and
+// every sum is taken in a fixed order: the result is bitwise reproducible.
+// A wave's 64 consecutive rows form one contiguous slice of the value array;
+// it is staged in LDS and streamed to HBM with 16-byte nontemporal stores.
+// Workgroups are persistent: the explicit kernels take row chunks round
+// robin in an XCD-grouped numbering, the product kernels contiguous slice
+// ranges grouped by XCD, so that vertex positions shared by neighbouring
+// rows stay in one L2.
 #include "dual2.h"
 #include "energies.h"
 #include "lad_device.h"
