@@ -264,3 +264,75 @@ def test_faces_irregular(lad, n, drop, dtype):
         assert torch.equal(E2, E) and torch.equal(g2, g) and torch.equal(H2, H)
         assert torch.equal(y2, y)
     L.close()
+
+
+def fan_mesh(k, seed):
+    """A disc: vertex 0 at the centre, a ring of k vertices around it and a
+    second ring of k further out; faces (0, i, i+1) around the centre (so
+    its row holds k faces and k + 1 blocks) and two per quad between the
+    rings.  Rest positions in the xy plane, positions perturbed by up to
+    0.05 of the ring spacing (seeded)."""
+    ang = 2.0 * np.pi * np.arange(k) / k
+    X = np.zeros((1 + 2 * k, 3))
+    X[1:k + 1, 0], X[1:k + 1, 1] = np.cos(ang), np.sin(ang)
+    X[k + 1:, 0], X[k + 1:, 1] = 2.0 * np.cos(ang), 2.0 * np.sin(ang)
+    faces = []
+    for i in range(k):
+        a, b = 1 + i, 1 + (i + 1) % k          # inner ring
+        c, d = k + 1 + i, k + 1 + (i + 1) % k  # outer ring
+        faces += [(0, a, b), (a, c, d), (a, d, b)]
+    faces = np.array(faces, dtype=np.int32)
+    dm, area = inputs.face_rest_data(X, faces)
+    u = 2.0 * inputs.uniform_block(seed, 3 * X.shape[0]) - 1.0
+    x = X + 0.05 * u.reshape(-1, 3)
+    springs = inputs.unique_edges(faces)
+    rest = np.linalg.norm(X[springs[:, 0]] - X[springs[:, 1]], axis=1)
+    return X, x, faces, dm, area, springs, rest
+
+
+@pytest.mark.parametrize("k,dtype,with_springs", [(40, "f64", False), (40, "f32", False),
+                                                  (40, "f32", True), (100, "f64", True)])
+def test_faces_fan(lad, k, dtype, with_springs):
+    """A row with many more faces than the product kernel keeps in
+    registers (the centre's k faces; the rest are read from the row's
+    records) and whose consecutive faces share a neighbour's block (the
+    explicit kernel's two lanes of a row add into shared blocks in
+    phases): E, g, H, H v and the pattern against the oracle, repeated
+    calls bitwise identical; with springs on every edge, the faces add into
+    the blocks the slot loop wrote."""
+    import torch
+    log_case(test="faces_fan", k=k, dtype=dtype, springs=with_springs)
+    X, x, faces, dm, area, springs, rest = fan_mesh(k, seed=500 + k)
+    nv = X.shape[0]
+    kw = dict(faces=faces, face_energy=True, dm_inv=dm, area=area)
+    pkw = dict(faces=faces, face_energy=True, dm_inv=host_input(dm, dtype),
+               area=host_input(area, dtype))
+    if with_springs:
+        kw.update(springs=springs, rest_len=rest, k=K)
+        pkw.update(springs=springs, rest_len=host_input(rest, dtype), k=K)
+    L = lad.Lad(nv, dtype=dtype, **kw)
+    assert L.get_info()["eval_path"] == lad.LAD_PATH_ROWS
+    prob = oracle.Problem(nv=nv, **pkw)
+    x_h = host_input(x, dtype)
+    v_h = host_input(inputs.hvp_direction(nv), dtype)
+    xd, vd = dev(x_h, dtype), dev(v_h, dtype)
+    E, g, H = L.eval(xd)
+    y = L.hvp(xd, vd)
+    rp, ci = L.pattern()
+    torch.cuda.synchronize()
+    E, g, H, y = E.clone(), g.clone(), H.clone(), y.clone()
+    orp, oci = oracle.pattern(prob)
+    assert np.array_equal(rp.cpu().numpy(), orp) and np.array_equal(ci.cpu().numpy(), oci)
+    assert orp[1] - orp[0] == k + 1  # the centre's row
+    Eo, go, Ho = oracle.evaluate(prob, orp, oci, x_h)
+    assert rel([E.item()], [Eo]) <= TOL[dtype]
+    assert rel(g.cpu().numpy(), go) <= TOL[dtype]
+    assert rel(H.cpu().numpy()[: oci.size], Ho) <= TOL[dtype]
+    assert rel(y.cpu().numpy(), oracle.hvp(prob, orp, oci, x_h, v_h)) <= TOL[dtype]
+    for _ in range(3):
+        E2, g2, H2 = L.eval(xd)
+        y2 = L.hvp(xd, vd)
+        torch.cuda.synchronize()
+        assert torch.equal(E2, E) and torch.equal(g2, g) and torch.equal(H2, H)
+        assert torch.equal(y2, y)
+    L.close()
