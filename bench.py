@@ -215,16 +215,27 @@ def read_traffic():
 # ---------------------------------------------------------------------------
 class Timer:
     """HIP events on torch's current stream, which is the stream every lad_*
-    call is enqueued on (the binding passes it explicitly)."""
+    call is enqueued on (the binding passes it explicitly).
 
-    def __init__(self, torch):
+    Warm-up: at least `warmup` untimed calls, and (unless warmup is 0) calls
+    until `min_warm_s` of wall time has passed, so that a GPU left idle
+    during a context's host-side set-up is back at its running clocks when
+    the timed calls start."""
+
+    def __init__(self, torch, min_warm_s=0.05):
         self.torch = torch
+        self.min_warm_s = min_warm_s
 
     def run(self, fn, steps, warmup, flush=None):
         t = self.torch
+        t0 = time.perf_counter()
         for _ in range(warmup):
             fn()
         t.cuda.synchronize()
+        while warmup > 0 and time.perf_counter() - t0 < self.min_warm_s:
+            for _ in range(warmup):
+                fn()
+            t.cuda.synchronize()
         starts = [t.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [t.cuda.Event(enable_timing=True) for _ in range(steps)]
         total0 = t.cuda.Event(enable_timing=True)
